@@ -1,0 +1,198 @@
+"""Plain fp64 CPU oracle for fused linear cross-entropy.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: it is used by ``tests/``, by the package entry point's
+smoke check and by the benchmark's CPU-baseline leg.  It shares no code with
+the GPU library and imports nothing from it.
+
+What it computes is the plain definition of the loss that the trl-lib
+"fused-linear-ce" kernel card describes (sections "Full signature", "Metrics
+for free" and "Algorithm"): cross-entropy of ``hidden @ weight.T (+ bias)``
+against integer targets, with an ignore index, a logit scale, an optional
+soft cap, mean / sum / none reductions, the two forward-only metrics (mean
+token accuracy over non-ignored positions, mean softmax entropy in nats), and
+the gradients of the loss with respect to hidden, weight and bias.
+
+Unlike the fused method it DOES materialise logits, one block of rows at a
+time (the row block only bounds memory; every row is independent), and does
+all arithmetic in fp64 after an exact upcast of the inputs.  Library
+primitives used as steps: numpy matmul (BLAS), exp, log, tanh, argmax.
+
+Readings of points the card leaves open (each is stated where it is used):
+  * transform order: bias, then scale, then soft cap:
+        z = c * tanh(s * (raw + b) / c)      (c = softcap; identity if None)
+  * soft cap form c*tanh(x/c); logit_scale multiplies;
+  * mean divides by the number of non-ignored rows; with none of them the
+    mean loss and both metrics are NaN and every gradient is zero;
+  * ignored rows have per-row loss 0 under reduction "none";
+  * argmax ties resolve to the smallest vocabulary index (numpy's argmax);
+  * metrics average over non-ignored rows;
+  * a non-ignored target outside [0, V) raises ValueError.
+
+Every function here is pinned by CPU tests against library routines
+(torch cross_entropy and autograd, scipy logsumexp / softmax / entropy),
+closed forms (zero weight, zero scale, two classes), invariants and central
+finite differences.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def _f64(a):
+    """Exact upcast to fp64 (inputs are fp32, or bf16/f16 already widened to fp32)."""
+    return None if a is None else np.asarray(a, dtype=np.float64)
+
+
+def transform_logits(raw, bias, logit_scale, softcap):
+    """Bias, then logit scale, then soft cap (card: "Algorithm" -- the tile
+    "applies bias / logit_scale / softcap"; the order as listed)."""
+    y = raw + bias[None, :] if bias is not None else raw
+    y = logit_scale * y
+    if softcap is not None:
+        y = softcap * np.tanh(y / softcap)
+    return y
+
+
+def transform_derivative(z, logit_scale, softcap):
+    """d z / d raw for the transform above, written in terms of the final z:
+    s for no cap; s * (1 - (z/c)^2) with the cap (derivative of c*tanh(x/c))."""
+    if softcap is None:
+        return np.full_like(z, logit_scale)
+    return logit_scale * (1.0 - (z / softcap) ** 2)
+
+
+def row_statistics(z):
+    """Per-row log-sum-exp, softmax, entropy, argmax and top-1/top-2 gap.
+
+    lse_i = m_i + log sum_j exp(z_ij - m_i) with m_i = max_j z_ij; the softmax
+    p = exp(z - lse); entropy H_i = -sum_j p_ij log p_ij = lse_i - sum_j p_ij z_ij
+    in nats (card: "Metrics for free"); argmax is the smallest index attaining
+    the row maximum; gap = top-1 minus top-2 value (inf when V == 1).
+    """
+    m = z.max(axis=1)
+    lse = m + np.log(np.exp(z - m[:, None]).sum(axis=1))
+    p = np.exp(z - lse[:, None])
+    entropy = lse - (p * z).sum(axis=1)
+    argmax = z.argmax(axis=1)
+    if z.shape[1] >= 2:
+        top2 = np.partition(z, z.shape[1] - 2, axis=1)[:, -2:]
+        gap = top2[:, 1] - top2[:, 0]
+    else:
+        gap = np.full(z.shape[0], np.inf)
+    return lse, p, entropy, argmax, gap
+
+
+def flce_reference(hidden, weight, targets, bias=None, ignore_index=-100,
+                   logit_scale=1.0, softcap=None, reduction="mean",
+                   grad_output=None, compute_grads=True, row_block=256):
+    """Forward and backward of the loss, by its definition, in fp64.
+
+    Arguments follow the card's "Full signature": hidden (N,H), weight (V,H),
+    targets (N,) integer ids, bias (V,) or None, ignore_index, logit_scale,
+    softcap (None or > 0), reduction "mean" | "sum" | "none".  ``grad_output``
+    is the upstream gradient of the returned loss: a scalar for mean/sum, an
+    (N,) vector for none; None means 1.
+
+    Returns a dict with
+      loss            scalar (mean/sum) or (N,) (none)
+      row_loss        (N,)  lse_i - z_{i,t_i}, 0 on ignored rows
+      lse             (N,)  log-sum-exp of the final logits
+      argmax, gap     (N,)  first-index argmax and top-1/top-2 gap of z
+      hit             (N,)  valid and argmax == target
+      row_entropy     (N,)  softmax entropy of the row (nats)
+      n_valid         number of non-ignored rows
+      accuracy, entropy   the two metrics (card: "Metrics for free")
+      grad_hidden (N,H), grad_weight (V,H), grad_bias (V,) or None  (if compute_grads)
+    """
+    if reduction not in ("mean", "sum", "none"):
+        raise ValueError(f"unknown reduction {reduction!r}")
+    if softcap is not None and not softcap > 0:
+        raise ValueError("softcap must be None or > 0")
+    h = _f64(hidden)
+    w = _f64(weight)
+    b = _f64(bias)
+    t = np.asarray(targets, dtype=np.int64)
+    n, hd = h.shape
+    v = w.shape[0]
+    valid = t != ignore_index
+    if np.any(valid & ((t < 0) | (t >= v))):
+        raise ValueError("target id outside [0, V) on a non-ignored row")
+    n_valid = int(valid.sum())
+
+    # Per-row coefficient of the gradient of the reduced loss w.r.t. row_loss_i.
+    if reduction == "none":
+        g = np.ones(n) if grad_output is None else np.asarray(grad_output, np.float64).reshape(n)
+        coef = np.where(valid, g, 0.0)
+    else:
+        g = 1.0 if grad_output is None else float(np.asarray(grad_output, np.float64).reshape(()))
+        scale = g / n_valid if (reduction == "mean" and n_valid > 0) else (g if reduction == "sum" else 0.0)
+        coef = np.where(valid, scale, 0.0)
+
+    row_loss = np.zeros(n)
+    lse = np.zeros(n)
+    argmax = np.zeros(n, dtype=np.int64)
+    gap = np.zeros(n)
+    row_entropy = np.zeros(n)
+    if compute_grads:
+        grad_h = np.zeros((n, hd))
+        grad_w = np.zeros((v, hd))
+        grad_b = np.zeros(v) if b is not None else None
+
+    for r0 in range(0, n, row_block):
+        r1 = min(n, r0 + row_block)
+        hr = h[r0:r1]
+        raw = hr @ w.T                                    # (R, V) logits before transforms
+        z = transform_logits(raw, b, logit_scale, softcap)
+        lse_r, p, ent_r, am_r, gap_r = row_statistics(z)
+        tr = t[r0:r1]
+        vr = valid[r0:r1]
+        rows = np.arange(r1 - r0)
+        zt = np.where(vr, z[rows, np.where(vr, tr, 0)], 0.0)
+        row_loss[r0:r1] = np.where(vr, lse_r - zt, 0.0)
+        lse[r0:r1] = lse_r
+        argmax[r0:r1] = am_r
+        gap[r0:r1] = gap_r
+        row_entropy[r0:r1] = ent_r
+        if compute_grads:
+            # d loss_i / d z_ij = p_ij - [j == t_i]  (card: "Algorithm", p - onehot)
+            gz = p.copy()
+            gz[rows[vr], tr[vr]] -= 1.0
+            gz[~vr] = 0.0
+            graw = coef[r0:r1, None] * gz * transform_derivative(z, logit_scale, softcap)
+            if b is not None:
+                # the bias enters before the scale: d raw / d b_j = 1
+                grad_b += graw.sum(axis=0)
+            grad_h[r0:r1] = graw @ w                       # (p - onehot) @ weight
+            grad_w += graw.T @ hr                          # (p - onehot).T @ hidden
+
+    hit = valid & (argmax == t)
+    if reduction == "none":
+        loss = row_loss.copy()
+    elif reduction == "sum":
+        loss = float(row_loss[valid].sum())
+    else:
+        loss = float(row_loss[valid].sum() / n_valid) if n_valid > 0 else math.nan
+    accuracy = float(hit.sum() / n_valid) if n_valid > 0 else math.nan
+    entropy = float(row_entropy[valid].sum() / n_valid) if n_valid > 0 else math.nan
+
+    out = dict(loss=loss, row_loss=row_loss, lse=lse, argmax=argmax, gap=gap, hit=hit,
+               row_entropy=row_entropy, n_valid=n_valid, accuracy=accuracy, entropy=entropy)
+    if compute_grads:
+        out.update(grad_hidden=grad_h, grad_weight=grad_w, grad_bias=grad_b)
+    return out
+
+
+def row_argmax_ids(hidden, weight, bias=None, logit_scale=1.0, softcap=None, row_block=256):
+    """First-index argmax of each row's final logits (used to build targets
+    that equal the row argmax)."""
+    h = _f64(hidden)
+    w = _f64(weight)
+    b = _f64(bias)
+    out = np.zeros(h.shape[0], dtype=np.int64)
+    for r0 in range(0, h.shape[0], row_block):
+        z = transform_logits(h[r0:r0 + row_block] @ w.T, b, logit_scale, softcap)
+        out[r0:r0 + row_block] = z.argmax(axis=1)
+    return out
