@@ -1,0 +1,131 @@
+/*
+ * flce.h -- C ABI of the MI355X (gfx950) fused linear cross-entropy library.
+ *
+ * The operation is the one the trl-lib "fused-linear-ce" kernel card
+ * defines ("Full signature", "Metrics for free", "Algorithm"):
+ *
+ *   raw  = hidden @ weight^T                  (N x V, never stored)
+ *   z    = c * tanh(s * (raw + bias) / c)     (bias optional; cap only if softcap > 0)
+ *   lse  = log sum_j exp(z_ij)
+ *   loss_i = lse_i - z_{i,t_i}   for rows whose target t_i != ignore_index, else 0
+ *   loss = mean over non-ignored rows | sum | per-row vector   (reduction)
+ *   metrics = { mean token accuracy (first-index argmax of z == target, over
+ *               non-ignored rows), mean softmax entropy in nats (same rows) }
+ *
+ * and its gradients (card: "Algorithm"): with G = (softmax(z) - onehot(t))
+ * scaled by the reduction and the upstream gradient and by dz/draw,
+ *   grad_hidden = G @ weight,  grad_weight = G^T @ hidden,  grad_bias = sum_i G_i.
+ *
+ * Readings of points the card leaves open: the transform applies bias, then
+ * logit_scale (a multiplier), then the soft cap c*tanh(x/c); "mean" divides
+ * by the number of non-ignored rows; with no such row the mean loss and both
+ * metrics are NaN and every gradient is 0; ignored rows have per-row loss 0.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers, row-major and dense:
+ *     hidden (N,H), weight (V,H), bias (V), targets (N) int64, grad_hidden
+ *     (N,H), grad_weight (V,H), grad_bias (V).  hidden, weight, grad_hidden,
+ *     grad_weight must be 16-byte aligned.  hidden/weight/bias and the
+ *     gradient outputs share the problem's dtype; loss, lse, metrics and
+ *     grad_loss are fp32.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
+ *     default stream) and never synchronises the host.
+ *   - The library never allocates, frees or retains device memory.  The
+ *     caller owns every buffer, including `workspace`, which must hold at
+ *     least the byte count the matching *_workspace_size function returns
+ *     and must not be used by anything else until the call's work on
+ *     `stream` has finished.  Calls that share a workspace must be ordered.
+ *   - Host-detectable errors return a status before anything is launched;
+ *     flce_last_error() then gives a thread-local message.  FLCE_ERR_HIP
+ *     reports a HIP runtime failure (including "no device").
+ *   - Out-of-range targets (not ignore_index, outside [0,V)) cannot be seen
+ *     without a sync: such a row's loss and gradient rows are NaN and bit 0
+ *     of the device status word is set (read it with flce_forward_status).
+ */
+#ifndef FLCE_H
+#define FLCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FLCE_F32 = 0, FLCE_F16 = 1, FLCE_BF16 = 2 } flce_dtype_t;
+
+typedef enum { FLCE_MEAN = 0, FLCE_SUM = 1, FLCE_NONE = 2 } flce_reduction_t;
+
+typedef enum {
+  FLCE_OK = 0,
+  FLCE_ERR_INVALID_ARGUMENT = 1, /* null / misaligned pointer, bad size or option   */
+  FLCE_ERR_UNSUPPORTED = 2,      /* valid but not handled (e.g. H not a multiple of 16 bytes) */
+  FLCE_ERR_WORKSPACE = 3,        /* workspace missing or smaller than required     */
+  FLCE_ERR_HIP = 4               /* HIP runtime error (launch failure, no device)  */
+} flce_status_t;
+
+/* Problem description (card: "Full signature").  Plain data; the library
+ * keeps no pointer to it after a call returns. */
+typedef struct flce_problem {
+  int64_t n_tokens;      /* N >= 0 rows of hidden / targets                         */
+  int64_t hidden;        /* H >= 1; H * sizeof(dtype) must be a multiple of 16      */
+  int64_t vocab;         /* V >= 1 rows of weight; N, V < 2^31                      */
+  int64_t ignore_index;  /* rows with this target are ignored (default -100)        */
+  int32_t dtype;         /* flce_dtype_t of hidden, weight, bias and gradients      */
+  int32_t reduction;     /* flce_reduction_t                                        */
+  float logit_scale;     /* s, finite (default 1.0)                                 */
+  float softcap;         /* c: 0 = no cap; > 0 enables c*tanh(x/c); < 0, inf, NaN invalid */
+  int32_t return_metrics;/* 0 / 1: also compute {accuracy, entropy}                 */
+  int32_t has_bias;      /* 0 / 1: bias (V) present                                 */
+  /* Plan overrides (0 = automatic).  They change the partition of the work,
+   * not the result beyond fp32 summation order. */
+  int32_t fwd_tiles_per_split; /* vocabulary tiles (256 ids) per forward split      */
+  int32_t bwd_vocab_chunk;     /* vocabulary ids per backward chunk (multiple of 256) */
+} flce_problem_t;
+
+/* Bytes of workspace flce_forward / flce_backward need for problem *p
+ * (0 if *p is invalid; never fails otherwise).  Pure host function. */
+size_t flce_forward_workspace_size(const flce_problem_t* p);
+size_t flce_backward_workspace_size(const flce_problem_t* p);
+
+/* Forward pass (card: "Algorithm", forward; "Metrics for free").
+ *   hidden, weight, targets, bias (NULL iff !has_bias): inputs as above.
+ *   loss:    out, [1] for MEAN/SUM, [N] for NONE.
+ *   lse:     out, [N] per-row log-sum-exp of z, the state the backward pass
+ *            consumes; may be NULL when no backward follows.
+ *   metrics: out, [2] = {mean_token_accuracy, entropy}; NULL iff !return_metrics.
+ * The loss and lse are bit-identical whether or not metrics are requested. */
+flce_status_t flce_forward(const flce_problem_t* p, const void* hidden, const void* weight,
+                           const int64_t* targets, const void* bias, float* loss, float* lse,
+                           float* metrics, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* Backward pass (card: "Algorithm", backward: recompute each logit tile,
+ * form p - onehot, accumulate the three gradients).
+ *   lse:        in, [N] from flce_forward with the same problem and inputs.
+ *   grad_loss:  in, device fp32 upstream gradient of the loss, [1] for
+ *               MEAN/SUM, [N] for NONE; NULL means 1.
+ *   grad_hidden (N,H), grad_weight (V,H), grad_bias (V): outputs, each may
+ *               be NULL when not wanted (grad_bias requires has_bias).  They
+ *               are overwritten, not accumulated into. */
+flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const void* weight,
+                            const int64_t* targets, const void* bias, const float* lse,
+                            const float* grad_loss, void* grad_hidden, void* grad_weight,
+                            void* grad_bias, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* Synchronously reads the device status word the last flce_forward call
+ * left in `workspace` (bit 0: a non-ignored target outside [0,V)).
+ * Waits for `stream`.  Debug helper, not for hot loops. */
+flce_status_t flce_forward_status(const flce_problem_t* p, const void* workspace,
+                                  uint32_t* status_out, void* stream);
+
+const char* flce_status_str(flce_status_t s);
+const char* flce_last_error(void);
+const char* flce_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLCE_H */

@@ -1,0 +1,158 @@
+"""Fused linear cross-entropy on MI355X (gfx950).
+
+``fused_linear_cross_entropy`` has the signature of the trl-lib
+"fused-linear-ce" kernel card ("Full signature"): the cross-entropy of
+``hidden @ weight.T (+ bias)`` against int64 targets, with ignore_index,
+logit_scale, softcap, mean / sum / none reductions and optional metrics
+(mean token accuracy, mean softmax entropy), differentiable with respect to
+hidden, weight and bias.  The N x V logit matrix is never materialised.
+
+Every step runs in the hand-written HIP kernels of ``libflce.so`` through
+its C ABI (include/flce.h); this module only allocates tensors with
+PyTorch's caching allocator and passes device pointers and the current
+stream.  There is no CPU or PyTorch fallback.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _abi
+from ._abi import FlceError, Problem, library, make_problem  # noqa: F401
+
+__all__ = ["fused_linear_cross_entropy", "flce_forward", "flce_backward", "FlceError",
+           "Problem", "make_problem", "library"]
+
+_DTYPES = {torch.float32: _abi.F32, torch.float16: _abi.F16, torch.bfloat16: _abi.BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _check_inputs(hidden, weight, targets, bias):
+    if not hidden.is_cuda:
+        raise ValueError("hidden must be a GPU tensor (there is no CPU path)")
+    if hidden.dim() != 2 or weight.dim() != 2 or targets.dim() != 1:
+        raise ValueError("expected hidden (N,H), weight (V,H), targets (N,)")
+    if weight.shape[1] != hidden.shape[1] or targets.shape[0] != hidden.shape[0]:
+        raise ValueError(f"shape mismatch: hidden {tuple(hidden.shape)}, weight {tuple(weight.shape)}, "
+                         f"targets {tuple(targets.shape)}")
+    if hidden.dtype not in _DTYPES or weight.dtype != hidden.dtype:
+        raise ValueError("hidden and weight must share one of float32 / float16 / bfloat16")
+    if targets.dtype != torch.int64:
+        raise ValueError("targets must be int64")
+    if bias is not None and (bias.shape != (weight.shape[0],) or bias.dtype != hidden.dtype):
+        raise ValueError("bias must be (V,) in the dtype of hidden")
+    for t in (hidden, weight, targets) + ((bias,) if bias is not None else ()):
+        if t.device != hidden.device:
+            raise ValueError("all tensors must be on one device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def problem_for(hidden, weight, bias, ignore_index=-100, logit_scale=1.0, softcap=None,
+                reduction="mean", return_metrics=False, fwd_tiles_per_split=0,
+                bwd_vocab_chunk=0) -> Problem:
+    return make_problem(hidden.shape[0], hidden.shape[1], weight.shape[0], _DTYPES[hidden.dtype],
+                        reduction, ignore_index, logit_scale, softcap, return_metrics,
+                        bias is not None, fwd_tiles_per_split, bwd_vocab_chunk)
+
+
+def flce_forward(hidden, weight, targets, bias=None, *, ignore_index=-100, logit_scale=1.0,
+                 softcap=None, reduction="mean", return_metrics=False, want_lse=True,
+                 workspace: Optional[torch.Tensor] = None, fwd_tiles_per_split=0):
+    """Tensor-level ``flce_forward``: returns (loss, lse or None, metrics or None)."""
+    _check_inputs(hidden, weight, targets, bias)
+    p = problem_for(hidden, weight, bias, ignore_index, logit_scale, softcap, reduction,
+                    return_metrics, fwd_tiles_per_split=fwd_tiles_per_split)
+    n = hidden.shape[0]
+    dev = hidden.device
+    loss = torch.empty(n if reduction == "none" else 1, dtype=torch.float32, device=dev)
+    lse = torch.empty(n, dtype=torch.float32, device=dev) if want_lse else None
+    metrics = torch.empty(2, dtype=torch.float32, device=dev) if return_metrics else None
+    need = _abi.flce_forward_workspace_size(p)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream().cuda_stream
+    _abi.check(_abi.flce_forward(p, _ptr(hidden), _ptr(weight), _ptr(targets), _ptr(bias),
+                                 _ptr(loss), _ptr(lse), _ptr(metrics), _ptr(workspace),
+                                 workspace.numel(), stream))
+    if reduction != "none":
+        loss = loss.view(())
+    return loss, lse, metrics
+
+
+def flce_backward(hidden, weight, targets, bias, lse, grad_loss=None, *, ignore_index=-100,
+                  logit_scale=1.0, softcap=None, reduction="mean", need_hidden=True,
+                  need_weight=True, need_bias=True, workspace: Optional[torch.Tensor] = None,
+                  bwd_vocab_chunk=0):
+    """Tensor-level ``flce_backward``: returns (grad_hidden, grad_weight, grad_bias)."""
+    _check_inputs(hidden, weight, targets, bias)
+    p = problem_for(hidden, weight, bias, ignore_index, logit_scale, softcap, reduction,
+                    False, bwd_vocab_chunk=bwd_vocab_chunk)
+    dev = hidden.device
+    if grad_loss is not None:
+        grad_loss = grad_loss.to(device=dev, dtype=torch.float32).contiguous()
+        expect = hidden.shape[0] if reduction == "none" else 1
+        if grad_loss.numel() != expect:
+            raise ValueError(f"grad_loss must have {expect} elements")
+    gh = torch.empty_like(hidden) if need_hidden else None
+    gw = torch.empty_like(weight) if need_weight else None
+    gb = torch.empty_like(bias) if (need_bias and bias is not None) else None
+    need = _abi.flce_backward_workspace_size(p)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream().cuda_stream
+    _abi.check(_abi.flce_backward(p, _ptr(hidden), _ptr(weight), _ptr(targets), _ptr(bias),
+                                  _ptr(lse), _ptr(grad_loss), _ptr(gh), _ptr(gw), _ptr(gb),
+                                  _ptr(workspace), workspace.numel(), stream))
+    return gh, gw, gb
+
+
+class _FusedLinearCrossEntropy(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, hidden, weight, targets, bias, ignore_index, logit_scale, softcap,
+                reduction, return_metrics):
+        loss, lse, metrics = flce_forward(hidden, weight, targets, bias, ignore_index=ignore_index,
+                                          logit_scale=logit_scale, softcap=softcap,
+                                          reduction=reduction, return_metrics=return_metrics)
+        ctx.save_for_backward(hidden, weight, targets, bias, lse)
+        ctx.opts = (ignore_index, logit_scale, softcap, reduction)
+        if metrics is None:
+            metrics = torch.empty(0, device=hidden.device)
+        ctx.mark_non_differentiable(metrics)
+        return loss, metrics
+
+    @staticmethod
+    def backward(ctx, grad_loss, _grad_metrics):
+        hidden, weight, targets, bias, lse = ctx.saved_tensors
+        ignore_index, logit_scale, softcap, reduction = ctx.opts
+        nh, nw, _, nb = ctx.needs_input_grad[:4]
+        gh, gw, gb = flce_backward(hidden, weight, targets, bias, lse, grad_loss,
+                                   ignore_index=ignore_index, logit_scale=logit_scale,
+                                   softcap=softcap, reduction=reduction, need_hidden=nh,
+                                   need_weight=nw, need_bias=nb and bias is not None)
+        return gh, gw, None, gb, None, None, None, None, None
+
+
+def fused_linear_cross_entropy(hidden, weight, targets, bias=None, ignore_index=-100,
+                               logit_scale=1.0, softcap=None, reduction="mean",
+                               return_metrics=False):
+    """Cross-entropy of ``hidden @ weight.T (+ bias)`` without materialising logits.
+
+    Returns ``loss`` (fp32; scalar for mean/sum, (N,) for none), or
+    ``(loss, {"mean_token_accuracy": ..., "entropy": ...})`` with
+    ``return_metrics=True``.  hidden, weight and bias receive gradients.
+    """
+    if reduction not in ("mean", "sum", "none"):
+        raise ValueError(f"unknown reduction {reduction!r}")
+    loss, metrics = _FusedLinearCrossEntropy.apply(hidden, weight, targets, bias, ignore_index,
+                                                   logit_scale, softcap, reduction,
+                                                   return_metrics)
+    if not return_metrics:
+        return loss
+    return loss, {"mean_token_accuracy": metrics[0], "entropy": metrics[1]}

@@ -1,0 +1,134 @@
+"""ctypes view of the C ABI in include/flce.h (argument marshalling only).
+
+Every function here forwards to the gfx950 library ``libflce.so`` built
+in-tree by ``linear_cross_entropy_fwd_amd.build``.  There is no fallback: if
+the library is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+from . import build as _build
+
+LIB_PATH = _build.LIB
+
+F32, F16, BF16 = 0, 1, 2
+MEAN, SUM, NONE = 0, 1, 2
+REDUCTIONS = {"mean": MEAN, "sum": SUM, "none": NONE}
+
+STATUS = {0: "FLCE_OK", 1: "FLCE_ERR_INVALID_ARGUMENT", 2: "FLCE_ERR_UNSUPPORTED",
+          3: "FLCE_ERR_WORKSPACE", 4: "FLCE_ERR_HIP"}
+
+
+class Problem(ctypes.Structure):
+    """Mirror of ``flce_problem_t``."""
+    _fields_ = [
+        ("n_tokens", ctypes.c_int64),
+        ("hidden", ctypes.c_int64),
+        ("vocab", ctypes.c_int64),
+        ("ignore_index", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+        ("reduction", ctypes.c_int32),
+        ("logit_scale", ctypes.c_float),
+        ("softcap", ctypes.c_float),
+        ("return_metrics", ctypes.c_int32),
+        ("has_bias", ctypes.c_int32),
+        ("fwd_tiles_per_split", ctypes.c_int32),
+        ("bwd_vocab_chunk", ctypes.c_int32),
+    ]
+
+
+class FlceError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+_lock = threading.Lock()
+
+_VP = ctypes.c_void_p
+_PP = ctypes.POINTER(Problem)
+
+_SIGNATURES = {
+    "flce_forward_workspace_size": (ctypes.c_size_t, [_PP]),
+    "flce_backward_workspace_size": (ctypes.c_size_t, [_PP]),
+    "flce_forward": (ctypes.c_int, [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
+    "flce_backward": (ctypes.c_int, [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                     ctypes.c_size_t, _VP]),
+    "flce_forward_status": (ctypes.c_int, [_PP, _VP, ctypes.POINTER(ctypes.c_uint32), _VP]),
+    "flce_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "flce_last_error": (ctypes.c_char_p, []),
+    "flce_version": (ctypes.c_char_p, []),
+}
+
+
+def library() -> ctypes.CDLL:
+    """The loaded gfx950 library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise RuntimeError(
+                        f"{LIB_PATH} is missing: build it with `python -m linear_cross_entropy_fwd_amd.build`")
+                lib = ctypes.CDLL(LIB_PATH)
+                for name, (res, args) in _SIGNATURES.items():
+                    fn = getattr(lib, name)
+                    fn.restype = res
+                    fn.argtypes = args
+                _lib = lib
+    return _lib
+
+
+def last_error() -> str:
+    return library().flce_last_error().decode()
+
+
+def check(status: int) -> None:
+    if status != 0:
+        raise FlceError(status, last_error())
+
+
+def make_problem(n, h, v, dtype, reduction="mean", ignore_index=-100, logit_scale=1.0,
+                 softcap=None, return_metrics=False, has_bias=False, fwd_tiles_per_split=0,
+                 bwd_vocab_chunk=0) -> Problem:
+    return Problem(int(n), int(h), int(v), int(ignore_index), int(dtype),
+                   REDUCTIONS[reduction] if isinstance(reduction, str) else int(reduction),
+                   float(logit_scale), 0.0 if softcap is None else float(softcap),
+                   int(bool(return_metrics)), int(bool(has_bias)), int(fwd_tiles_per_split),
+                   int(bwd_vocab_chunk))
+
+
+def flce_forward_workspace_size(p: Problem) -> int:
+    return int(library().flce_forward_workspace_size(ctypes.byref(p)))
+
+
+def flce_backward_workspace_size(p: Problem) -> int:
+    return int(library().flce_backward_workspace_size(ctypes.byref(p)))
+
+
+def flce_forward(p: Problem, hidden, weight, targets, bias, loss, lse, metrics, workspace,
+                 workspace_bytes, stream) -> int:
+    """Raw call with integer device addresses (0 = NULL); returns the status."""
+    return library().flce_forward(ctypes.byref(p), hidden, weight, targets, bias, loss, lse,
+                                  metrics, workspace, workspace_bytes, stream)
+
+
+def flce_backward(p: Problem, hidden, weight, targets, bias, lse, grad_loss, grad_hidden,
+                  grad_weight, grad_bias, workspace, workspace_bytes, stream) -> int:
+    return library().flce_backward(ctypes.byref(p), hidden, weight, targets, bias, lse,
+                                   grad_loss, grad_hidden, grad_weight, grad_bias, workspace,
+                                   workspace_bytes, stream)
+
+
+def flce_forward_status(p: Problem, workspace, stream) -> int:
+    out = ctypes.c_uint32(0)
+    check(library().flce_forward_status(ctypes.byref(p), workspace, ctypes.byref(out), stream))
+    return int(out.value)
+
+
+def flce_version() -> str:
+    return library().flce_version().decode()

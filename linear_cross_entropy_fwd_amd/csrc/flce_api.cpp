@@ -1,0 +1,392 @@
+// flce_api.cpp -- the C ABI (include/flce.h): argument validation, the
+// launch plan, workspace layout and the launch sequence of each pass.
+// Host code only; kernels live in flce_kernels.hip.
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+
+#include "../../include/flce.h"
+#include "flce_plan.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+flce_status_t fail(flce_status_t s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+flce_status_t fail(flce_status_t s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+flce_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(FLCE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kTile = 256;
+constexpr int64_t kAlign = 256;
+constexpr int64_t kDefaultChunk = 8192;
+constexpr int kMaxSplits = 64;
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+int64_t cdiv(int64_t x, int64_t m) { return (x + m - 1) / m; }
+int elem_bytes(int dtype) { return dtype == FLCE_F32 ? 4 : 2; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+flce_status_t check_problem(const flce_problem_t* p) {
+  if (!p) return fail(FLCE_ERR_INVALID_ARGUMENT, "problem is NULL");
+  if (p->dtype != FLCE_F32 && p->dtype != FLCE_F16 && p->dtype != FLCE_BF16)
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "unknown dtype %d", p->dtype);
+  if (p->reduction != FLCE_MEAN && p->reduction != FLCE_SUM && p->reduction != FLCE_NONE)
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "unknown reduction %d", p->reduction);
+  if (p->n_tokens < 0) return fail(FLCE_ERR_INVALID_ARGUMENT, "n_tokens < 0");
+  if (p->hidden < 1) return fail(FLCE_ERR_INVALID_ARGUMENT, "hidden < 1");
+  if (p->vocab < 1) return fail(FLCE_ERR_INVALID_ARGUMENT, "vocab < 1");
+  if (p->n_tokens >= (int64_t(1) << 31) || p->vocab >= (int64_t(1) << 31))
+    return fail(FLCE_ERR_UNSUPPORTED, "n_tokens and vocab must be < 2^31");
+  if (p->hidden > (int64_t(1) << 20)) return fail(FLCE_ERR_UNSUPPORTED, "hidden > 2^20");
+  if ((p->hidden * elem_bytes(p->dtype)) % 16 != 0)
+    return fail(FLCE_ERR_UNSUPPORTED, "hidden * sizeof(dtype) must be a multiple of 16 bytes (H=%lld)",
+                (long long)p->hidden);
+  if (!isfinite(p->logit_scale)) return fail(FLCE_ERR_INVALID_ARGUMENT, "logit_scale is not finite");
+  if (!(p->softcap >= 0.f) || isinf(p->softcap))
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "softcap must be 0 (none) or a finite value > 0");
+  if (p->return_metrics != 0 && p->return_metrics != 1)
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "return_metrics must be 0 or 1");
+  if (p->has_bias != 0 && p->has_bias != 1) return fail(FLCE_ERR_INVALID_ARGUMENT, "has_bias must be 0 or 1");
+  if (p->fwd_tiles_per_split < 0) return fail(FLCE_ERR_INVALID_ARGUMENT, "fwd_tiles_per_split < 0");
+  if (p->bwd_vocab_chunk < 0 || p->bwd_vocab_chunk % kTile != 0)
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "bwd_vocab_chunk must be 0 or a positive multiple of 256");
+  return FLCE_OK;
+}
+
+// ---------------------------------------------------------------- forward plan
+
+struct FwdLayout {
+  int n_tok_tiles, n_voc_tiles, tiles_per_split, n_splits;
+  size_t off_status, off_part, off_rowloss, off_rowent, off_rowflag, total;
+};
+
+FwdLayout fwd_layout(const flce_problem_t& p) {
+  FwdLayout L{};
+  const int64_t N = p.n_tokens, V = p.vocab;
+  L.n_tok_tiles = (int)cdiv(N, kTile);
+  L.n_voc_tiles = (int)cdiv(V, kTile);
+  // Depends on V only (not N): a row's result must not depend on the batch.
+  L.tiles_per_split = p.fwd_tiles_per_split > 0
+                          ? std::min(p.fwd_tiles_per_split, L.n_voc_tiles)
+                          : (int)std::max<int64_t>(1, cdiv(L.n_voc_tiles, kMaxSplits));
+  L.n_splits = (int)cdiv(L.n_voc_tiles, L.tiles_per_split);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = (size_t)round_up((int64_t)(off + bytes), kAlign);
+    return o;
+  };
+  L.off_status = take(16);
+  L.off_part = take((size_t)6 * L.n_splits * N * 4);
+  L.off_rowloss = take((size_t)N * 4);
+  L.off_rowent = take((size_t)N * 4);
+  L.off_rowflag = take((size_t)N * 4);
+  L.total = off;
+  return L;
+}
+
+// ---------------------------------------------------------------- backward plan
+
+struct BwdLayout {
+  int64_t chunk, npad, cvpad_max;
+  int n_chunks, n_tok_tiles, n_h_tiles;
+  size_t off_scale, off_ht, off_wct, off_g, off_gt, off_dh, off_db, total;
+};
+
+BwdLayout bwd_layout(const flce_problem_t& p) {
+  BwdLayout L{};
+  const int64_t N = p.n_tokens, H = p.hidden, V = p.vocab;
+  const int eb = elem_bytes(p.dtype);
+  L.chunk = std::min<int64_t>(p.bwd_vocab_chunk > 0 ? p.bwd_vocab_chunk : kDefaultChunk, round_up(V, kTile));
+  L.n_chunks = (int)cdiv(V, L.chunk);
+  L.npad = round_up(std::max<int64_t>(N, 1), 64);
+  L.cvpad_max = round_up(std::min(L.chunk, V), 64);
+  L.n_tok_tiles = (int)cdiv(N, kTile);
+  L.n_h_tiles = (int)cdiv(H, kTile);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = (size_t)round_up((int64_t)(off + bytes), kAlign);
+    return o;
+  };
+  L.off_scale = take(16);
+  L.off_ht = take((size_t)H * L.npad * eb);
+  L.off_wct = take((size_t)H * L.cvpad_max * eb);
+  L.off_g = take((size_t)L.npad * L.cvpad_max * eb);
+  L.off_gt = take((size_t)L.cvpad_max * L.npad * eb);
+  L.off_dh = take(L.n_chunks > 1 ? (size_t)N * H * 4 : 0);
+  L.off_db = take(p.has_bias ? (size_t)2 * L.n_tok_tiles * V * 4 : 0);
+  L.total = off;
+  return L;
+}
+
+flce_status_t check_workspace(const void* ws, size_t bytes, size_t need) {
+  if (need == 0) return FLCE_OK;
+  if (!ws) return fail(FLCE_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (bytes < need) return fail(FLCE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", bytes, need);
+  if (!aligned(ws, 256)) return fail(FLCE_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  return FLCE_OK;
+}
+
+float cap_of(const flce_problem_t& p) { return p.softcap > 0.f ? p.softcap : 1.f; }
+
+}  // namespace
+
+extern "C" {
+
+size_t flce_forward_workspace_size(const flce_problem_t* p) {
+  if (check_problem(p) != FLCE_OK) return 0;
+  return fwd_layout(*p).total;
+}
+
+size_t flce_backward_workspace_size(const flce_problem_t* p) {
+  if (check_problem(p) != FLCE_OK) return 0;
+  return bwd_layout(*p).total;
+}
+
+flce_status_t flce_forward(const flce_problem_t* p, const void* hidden, const void* weight,
+                           const int64_t* targets, const void* bias, float* loss, float* lse,
+                           float* metrics, void* workspace, size_t workspace_bytes, void* stream) {
+  flce_status_t s = check_problem(p);
+  if (s != FLCE_OK) return s;
+  const int64_t N = p->n_tokens;
+  if (N > 0 && (!hidden || !weight || !targets))
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "hidden, weight and targets must be non-NULL");
+  if (p->has_bias && !bias) return fail(FLCE_ERR_INVALID_ARGUMENT, "has_bias=1 but bias is NULL");
+  if (!p->has_bias && bias) return fail(FLCE_ERR_INVALID_ARGUMENT, "bias given but has_bias=0");
+  if (!loss && !(p->reduction == FLCE_NONE && N == 0)) return fail(FLCE_ERR_INVALID_ARGUMENT, "loss is NULL");
+  if (p->return_metrics && !metrics) return fail(FLCE_ERR_INVALID_ARGUMENT, "return_metrics=1 but metrics is NULL");
+  if (!p->return_metrics && metrics) return fail(FLCE_ERR_INVALID_ARGUMENT, "metrics given but return_metrics=0");
+  if (!aligned(hidden, 16) || !aligned(weight, 16))
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "hidden and weight must be 16-byte aligned");
+  if (!aligned(targets, 8)) return fail(FLCE_ERR_INVALID_ARGUMENT, "targets must be 8-byte aligned");
+  if (bias && !aligned(bias, (uintptr_t)elem_bytes(p->dtype)))
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "bias is misaligned");
+  const FwdLayout L = fwd_layout(*p);
+  s = check_workspace(workspace, workspace_bytes, L.total);
+  if (s != FLCE_OK) return s;
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  const bool metrics_on = p->return_metrics != 0;
+  hipError_t e;
+  if (N > 0) {
+    flce::FwdArgs fa{};
+    fa.hidden = reinterpret_cast<const char*>(hidden);
+    fa.weight = reinterpret_cast<const char*>(weight);
+    fa.bias = reinterpret_cast<const char*>(bias);
+    fa.targets = targets;
+    fa.part = reinterpret_cast<float*>(ws + L.off_part);
+    fa.N = N;
+    fa.H = p->hidden;
+    fa.V = p->vocab;
+    fa.ignore_index = p->ignore_index;
+    fa.n_tok_tiles = L.n_tok_tiles;
+    fa.n_voc_tiles = L.n_voc_tiles;
+    fa.tiles_per_split = L.tiles_per_split;
+    fa.n_splits = L.n_splits;
+    fa.s = p->logit_scale;
+    fa.cap = cap_of(*p);
+    fa.inv_cap = 1.f / fa.cap;
+    e = flce::launch_forward_tiles(p->dtype, metrics_on, p->has_bias != 0, p->softcap > 0.f, fa, st);
+    if (e != hipSuccess) return hip_fail(e, "forward tile kernel");
+
+    flce::CombineArgs ca{};
+    ca.targets = targets;
+    ca.part = fa.part;
+    ca.lse_out = lse;
+    ca.loss_rows = p->reduction == FLCE_NONE ? loss : nullptr;
+    ca.row_loss = reinterpret_cast<float*>(ws + L.off_rowloss);
+    ca.row_ent = reinterpret_cast<float*>(ws + L.off_rowent);
+    ca.row_flag = reinterpret_cast<int*>(ws + L.off_rowflag);
+    ca.N = N;
+    ca.V = p->vocab;
+    ca.ignore_index = p->ignore_index;
+    ca.tiles_per_split = L.tiles_per_split;
+    ca.n_splits = L.n_splits;
+    e = flce::launch_forward_combine(metrics_on, ca, st);
+    if (e != hipSuccess) return hip_fail(e, "forward combine kernel");
+  }
+  flce::ReduceArgs ra{};
+  ra.row_loss = reinterpret_cast<const float*>(ws + L.off_rowloss);
+  ra.row_ent = reinterpret_cast<const float*>(ws + L.off_rowent);
+  ra.row_flag = reinterpret_cast<const int*>(ws + L.off_rowflag);
+  ra.loss = loss;
+  ra.metrics = metrics;
+  ra.status = reinterpret_cast<uint32_t*>(ws + L.off_status);
+  ra.N = N;
+  ra.reduction = p->reduction;
+  e = flce::launch_forward_reduce(metrics_on, ra, st);
+  if (e != hipSuccess) return hip_fail(e, "forward reduce kernel");
+  return FLCE_OK;
+}
+
+flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const void* weight,
+                            const int64_t* targets, const void* bias, const float* lse,
+                            const float* grad_loss, void* grad_hidden, void* grad_weight,
+                            void* grad_bias, void* workspace, size_t workspace_bytes, void* stream) {
+  flce_status_t s = check_problem(p);
+  if (s != FLCE_OK) return s;
+  const int64_t N = p->n_tokens, H = p->hidden, V = p->vocab;
+  const int eb = elem_bytes(p->dtype);
+  if (grad_bias && !p->has_bias) return fail(FLCE_ERR_INVALID_ARGUMENT, "grad_bias given but has_bias=0");
+  if (p->has_bias && !bias) return fail(FLCE_ERR_INVALID_ARGUMENT, "has_bias=1 but bias is NULL");
+  if (!p->has_bias && bias) return fail(FLCE_ERR_INVALID_ARGUMENT, "bias given but has_bias=0");
+  const bool want_dh = grad_hidden != nullptr && N > 0;
+  const bool want_dw = grad_weight != nullptr;
+  const bool want_db = grad_bias != nullptr;
+  if (!want_dh && !want_dw && !want_db) return FLCE_OK;
+  if (N > 0 && (!hidden || !weight || !targets || !lse))
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "hidden, weight, targets and lse must be non-NULL");
+  if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(grad_hidden, 16) || !aligned(grad_weight, 16))
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "hidden, weight, grad_hidden and grad_weight must be 16-byte aligned");
+  if (!aligned(targets, 8) || !aligned(lse, 4) || !aligned(grad_loss, 4))
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "targets / lse / grad_loss misaligned");
+  if ((bias && !aligned(bias, (uintptr_t)eb)) || (grad_bias && !aligned(grad_bias, (uintptr_t)eb)))
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "bias / grad_bias misaligned");
+  const BwdLayout L = bwd_layout(*p);
+  s = check_workspace(workspace, workspace_bytes, L.total);
+  if (s != FLCE_OK) return s;
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  hipError_t e;
+  if (N == 0) {  // every gradient is zero
+    if (want_dw && (e = flce::launch_fill_zero(grad_weight, (size_t)V * H * eb, st)) != hipSuccess)
+      return hip_fail(e, "zero fill");
+    if (want_db && (e = flce::launch_fill_zero(grad_bias, (size_t)V * eb, st)) != hipSuccess)
+      return hip_fail(e, "zero fill");
+    return FLCE_OK;
+  }
+
+  float* scale = reinterpret_cast<float*>(ws + L.off_scale);
+  flce::PrepArgs pa{targets, grad_loss, scale, N, p->ignore_index, p->reduction, p->logit_scale};
+  if ((e = flce::launch_backward_prep(pa, st)) != hipSuccess) return hip_fail(e, "backward prep kernel");
+
+  char* ht = ws + L.off_ht;
+  char* wct = ws + L.off_wct;
+  char* g = ws + L.off_g;
+  char* gt = ws + L.off_gt;
+  float* dh = reinterpret_cast<float*>(ws + L.off_dh);
+  float* db = reinterpret_cast<float*>(ws + L.off_db);
+  if (want_dw) {
+    flce::TransposeArgs ta{reinterpret_cast<const char*>(hidden), ht, N, H, H, L.npad};
+    if ((e = flce::launch_transpose(p->dtype, ta, st)) != hipSuccess) return hip_fail(e, "transpose kernel");
+  }
+  for (int c = 0; c < L.n_chunks; ++c) {
+    const int64_t c0 = (int64_t)c * L.chunk;
+    const int cv = (int)std::min<int64_t>(L.chunk, V - c0);
+    const int cvpad = (int)round_up(cv, 64);
+    if (want_dh) {
+      flce::TransposeArgs ta{reinterpret_cast<const char*>(weight) + c0 * H * eb, wct, cv, H, H, cvpad};
+      if ((e = flce::launch_transpose(p->dtype, ta, st)) != hipSuccess) return hip_fail(e, "transpose kernel");
+    }
+    flce::GArgs ga{};
+    ga.hidden = reinterpret_cast<const char*>(hidden);
+    ga.weight = reinterpret_cast<const char*>(weight);
+    ga.bias = reinterpret_cast<const char*>(bias);
+    ga.targets = targets;
+    ga.lse = lse;
+    ga.grad_rows = p->reduction == FLCE_NONE ? grad_loss : nullptr;
+    ga.G = want_dh ? g : nullptr;
+    ga.GT = want_dw ? gt : nullptr;
+    ga.dbpart = want_db ? db : nullptr;
+    ga.N = N;
+    ga.H = H;
+    ga.V = V;
+    ga.ignore_index = p->ignore_index;
+    ga.c0 = c0;
+    ga.cv = cv;
+    ga.cvpad = cvpad;
+    ga.npad = (int)L.npad;
+    ga.n_tok_tiles = L.n_tok_tiles;
+    ga.n_voc_tiles = (int)cdiv(cv, kTile);
+    ga.none_reduction = p->reduction == FLCE_NONE;
+    ga.s = p->logit_scale;
+    ga.cap = cap_of(*p);
+    ga.inv_cap = 1.f / ga.cap;
+    if ((e = flce::launch_backward_g(p->dtype, p->has_bias != 0, p->softcap > 0.f, ga, st)) != hipSuccess)
+      return hip_fail(e, "backward G kernel");
+    if (want_dh) {
+      flce::DhArgs da{};
+      da.G = g;
+      da.WcT = wct;
+      da.acc = dh;
+      da.out = reinterpret_cast<char*>(grad_hidden);
+      da.scale = scale;
+      da.N = N;
+      da.H = H;
+      da.cvpad = cvpad;
+      da.n_tok_tiles = L.n_tok_tiles;
+      da.n_h_tiles = L.n_h_tiles;
+      da.first = c == 0;
+      da.last = c == L.n_chunks - 1;
+      if ((e = flce::launch_backward_dh(p->dtype, da, st)) != hipSuccess) return hip_fail(e, "grad_hidden kernel");
+    }
+    if (want_dw) {
+      flce::DwArgs wa{};
+      wa.GT = gt;
+      wa.HT = ht;
+      wa.out = reinterpret_cast<char*>(grad_weight) + c0 * H * eb;
+      wa.scale = scale;
+      wa.H = H;
+      wa.cv = cv;
+      wa.npad = (int)L.npad;
+      wa.n_voc_tiles = (int)cdiv(cv, kTile);
+      wa.n_h_tiles = L.n_h_tiles;
+      if ((e = flce::launch_backward_dw(p->dtype, wa, st)) != hipSuccess) return hip_fail(e, "grad_weight kernel");
+    }
+  }
+  if (want_db) {
+    flce::DbArgs ba{db, reinterpret_cast<char*>(grad_bias), scale, V, 2 * L.n_tok_tiles};
+    if ((e = flce::launch_backward_db(p->dtype, ba, st)) != hipSuccess) return hip_fail(e, "grad_bias kernel");
+  }
+  return FLCE_OK;
+}
+
+flce_status_t flce_forward_status(const flce_problem_t* p, const void* workspace, uint32_t* status_out,
+                                  void* stream) {
+  flce_status_t s = check_problem(p);
+  if (s != FLCE_OK) return s;
+  if (!workspace || !status_out) return fail(FLCE_ERR_INVALID_ARGUMENT, "workspace and status_out must be non-NULL");
+  const FwdLayout L = fwd_layout(*p);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(status_out, reinterpret_cast<const char*>(workspace) + L.off_status,
+                                sizeof(uint32_t), hipMemcpyDeviceToHost, st);
+  if (e != hipSuccess) return hip_fail(e, "status copy");
+  if ((e = hipStreamSynchronize(st)) != hipSuccess) return hip_fail(e, "status sync");
+  return FLCE_OK;
+}
+
+const char* flce_status_str(flce_status_t s) {
+  switch (s) {
+    case FLCE_OK: return "FLCE_OK";
+    case FLCE_ERR_INVALID_ARGUMENT: return "FLCE_ERR_INVALID_ARGUMENT";
+    case FLCE_ERR_UNSUPPORTED: return "FLCE_ERR_UNSUPPORTED";
+    case FLCE_ERR_WORKSPACE: return "FLCE_ERR_WORKSPACE";
+    case FLCE_ERR_HIP: return "FLCE_ERR_HIP";
+  }
+  return "FLCE_ERR_UNKNOWN";
+}
+
+const char* flce_last_error(void) { return g_last_error.c_str(); }
+
+const char* flce_version(void) { return "flce-gfx950 0.1.0"; }
+
+}  // extern "C"

@@ -1,0 +1,720 @@
+// flce_kernels.hip -- gfx950 kernels of fused linear cross-entropy.
+//
+// Forward (trl-lib "fused-linear-ce" card, "Algorithm" and "Metrics for
+// free"): each workgroup computes 256 x 256 logit tiles z^T = W . hidden^T
+// with bf16/f16 (or fp32) MFMA into fp32 registers, applies bias / scale /
+// soft cap, and folds every tile into per-row online log-sum-exp state
+// (running max m and rescaled sum S), together with the target-logit gather,
+// the running argmax and the entropy sum U = sum e^{z-m} (z-m).  Vocabulary
+// ids run along the MFMA row axis, so each lane owns 4 token columns and
+// reduces its 64 logits per column in registers; the two half-waves and the
+// two waves that share a token merge once per split.  Nothing of size N x V
+// is written: only 6 words per (row, split).
+//
+// Backward (card: "Algorithm", backward): per vocabulary chunk of Cv ids,
+// recompute the logit tiles, form G = (p - onehot) * coef * dz/draw in the
+// input dtype (both G and G^T), then contract
+//   grad_hidden += G . W_c        (fp32 accumulator across chunks)
+//   grad_weight[c] = G^T . hidden (complete per chunk, written once)
+// with the same NT GEMM tile (W_c and hidden are transposed into the
+// workspace first so that both operands of every contraction are
+// K-contiguous).  grad_bias sums G over rows per tile, then over tiles in a
+// fixed order.  No atomics: results are deterministic.
+#include <math.h>
+
+#include <type_traits>
+
+#include "flce_device.h"
+#include "flce_plan.h"
+
+namespace flce {
+
+// ------------------------------------------------------------------ helpers
+
+__device__ __forceinline__ float soft_cap(float y, float cap, float inv_cap) {
+  return cap * tanhf(y * inv_cap);
+}
+
+// Merge online-softmax state (m2,S2,U2) into (m,S,U).  Symmetric in its two
+// operands (fp add / mul commute), so the merge order of a pair never
+// changes the bits.  U = sum e^{z-m}(z-m) rescales as e^{m-M}(U + (m-M) S).
+template <bool METRICS>
+__device__ __forceinline__ void lse_merge(float& m, float& S, float& U, float m2, float S2, float U2) {
+  const float M = fmaxf(m, m2);
+  if (M == -INFINITY) return;
+  float s1 = 0.f, s2 = 0.f, u1 = 0.f, u2 = 0.f;
+  if (m != -INFINITY) {
+    const float d = m - M;
+    const float al = fast_exp2(d * LOG2E);
+    s1 = S * al;
+    if (METRICS) u1 = al * fmaf(d, S, U);
+  }
+  if (m2 != -INFINITY) {
+    const float d = m2 - M;
+    const float al = fast_exp2(d * LOG2E);
+    s2 = S2 * al;
+    if (METRICS) u2 = al * fmaf(d, S2, U2);
+  }
+  m = M;
+  S = s1 + s2;
+  if (METRICS) U = u1 + u2;
+}
+
+// First-index argmax merge: larger value wins, ties go to the smaller id.
+__device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {
+  if (v2 > v || (v2 == v && i2 < i)) {
+    v = v2;
+    i = i2;
+  }
+}
+
+template <int D, bool BIAS>
+__device__ __forceinline__ void load_bias_rows(float (&bv)[4][16], const char* bias, int vbase,
+                                               int64_t V, int half) {
+  typedef typename Elem<D>::T T;
+  const T* b = reinterpret_cast<const T*>(bias);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if (BIAS) {
+        int64_t v = (int64_t)vbase + 32 * i + acc_row(r, half);
+        v = v < V ? v : V - 1;
+        bv[i][r] = to_f32<D>(b[v]);
+      } else {
+        bv[i][r] = 0.f;
+      }
+    }
+}
+
+// ------------------------------------------------------------------ forward tiles
+
+template <int D, bool METRICS, bool BIAS, bool CAP>
+__global__ __launch_bounds__(NTHREADS) void fwd_tiles_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  constexpr int EB = Elem<D>::bytes;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave >> 1, wn = wave & 1, r32 = lane & 31, half = lane >> 5;
+
+  const int L = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int tt = L % a.n_tok_tiles, split = L / a.n_tok_tiles;
+  const int64_t n0 = (int64_t)tt * TILE;
+  const int vt_begin = split * a.tiles_per_split;
+  const int vt_end = min(vt_begin + a.tiles_per_split, a.n_voc_tiles);
+  const int64_t rowb = a.H * EB;
+
+  Panel B{a.hidden + n0 * rowb, rowb, (int)min<int64_t>(TILE, a.N - n0), rowb};
+
+  int tgt[4];
+  float m[4], S[4], U[4], zt[4], av[4];
+  int ai[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t n = n0 + wn * 128 + 32 * j + r32;
+    const int64_t tv = n < a.N ? a.targets[n] : a.ignore_index;
+    tgt[j] = (tv != a.ignore_index && tv >= 0 && tv < a.V) ? (int)tv : -1;
+    m[j] = -INFINITY;
+    S[j] = 0.f;
+    U[j] = 0.f;
+    zt[j] = 0.f;
+    av[j] = -INFINITY;
+    ai[j] = 0x7fffffff;
+  }
+
+  f32x16_t acc[4][4];
+  for (int vt = vt_begin; vt < vt_end; ++vt) {
+    const int64_t v0 = (int64_t)vt * TILE;
+    Panel A{a.weight + v0 * rowb, rowb, (int)min<int64_t>(TILE, a.V - v0), rowb};
+    gemm_nt_tile<D>(acc, A, B, lds);
+
+    const int vbase = (int)v0 + wm * 128;
+    const bool ragged = v0 + TILE > a.V;
+    float bv[4][16];
+    load_bias_rows<D, BIAS>(bv, a.bias, vbase, a.V, half);
+
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float z[4][16];
+      float zmax = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float y = acc[i][j][r];
+          if (BIAS) y = y + bv[i][r];
+          y = a.s * y;
+          if (CAP) y = soft_cap(y, a.cap, a.inv_cap);
+          if (ragged && vbase + 32 * i + acc_row(r, half) >= a.V) y = -INFINITY;
+          z[i][r] = y;
+          zmax = fmaxf(zmax, y);
+        }
+      const float mold = m[j];
+      const float mnew = fmaxf(mold, zmax);
+      if (mnew != -INFINITY) {
+        float sum = 0.f, usum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float d = z[i][r] - mnew;
+            const float e = fast_exp2(d * LOG2E);
+            sum = sum + e;
+            if (METRICS) usum = fmaf(e, fmaxf(d, -1e30f), usum);
+          }
+        if (mold == -INFINITY) {
+          S[j] = sum;
+          if (METRICS) U[j] = usum;
+        } else {
+          const float dm = mold - mnew;
+          const float al = fast_exp2(dm * LOG2E);
+          if (METRICS) U[j] = fmaf(al, fmaf(dm, S[j], U[j]), usum);
+          S[j] = fmaf(S[j], al, sum);
+        }
+        m[j] = mnew;
+      }
+      if (METRICS && zmax > av[j]) {
+        int idx = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int v = vbase + 32 * i + acc_row(r, half);
+            if (z[i][r] == zmax && v < idx) idx = v;
+          }
+        av[j] = zmax;
+        ai[j] = idx;
+      }
+      const int local = tgt[j] - vbase;
+      if (local >= 0 && local < 128 && ((local >> 2) & 1) == half) {
+        const int ti = local >> 5, tr = ((local & 31) >> 3) * 4 + (local & 3);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (i == ti && r == tr) zt[j] = z[i][r];
+      }
+    }
+  }
+
+  // Lanes l and l^32 hold the same token columns over disjoint vocab rows.
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float m2 = __shfl_xor(m[j], 32), S2 = __shfl_xor(S[j], 32);
+    const float U2 = __shfl_xor(U[j], 32), z2 = __shfl_xor(zt[j], 32);
+    const float av2 = __shfl_xor(av[j], 32);
+    const int ai2 = __shfl_xor(ai[j], 32);
+    lse_merge<METRICS>(m[j], S[j], U[j], m2, S2, U2);
+    zt[j] = zt[j] + z2;  // the non-owner holds +0
+    if (METRICS) argmax_merge(av[j], ai[j], av2, ai2);
+  }
+
+  // Waves wm=0 and wm=1 hold the same tokens over disjoint vocab rows.
+  float* xs = reinterpret_cast<float*>(lds);
+  if (wm == 1 && half == 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tok = wn * 128 + 32 * j + r32;
+      xs[0 * TILE + tok] = m[j];
+      xs[1 * TILE + tok] = S[j];
+      xs[2 * TILE + tok] = U[j];
+      xs[3 * TILE + tok] = zt[j];
+      xs[4 * TILE + tok] = av[j];
+      xs[5 * TILE + tok] = __int_as_float(ai[j]);
+    }
+  }
+  __syncthreads();
+  if (wm == 0 && half == 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tok = wn * 128 + 32 * j + r32;
+      lse_merge<METRICS>(m[j], S[j], U[j], xs[0 * TILE + tok], xs[1 * TILE + tok], xs[2 * TILE + tok]);
+      zt[j] = zt[j] + xs[3 * TILE + tok];
+      if (METRICS) argmax_merge(av[j], ai[j], xs[4 * TILE + tok], __float_as_int(xs[5 * TILE + tok]));
+      const int64_t n = n0 + tok;
+      if (n < a.N) {
+        const int64_t stride = (int64_t)a.n_splits * a.N;
+        float* p = a.part + (int64_t)split * a.N + n;
+        p[0 * stride] = m[j];
+        p[1 * stride] = S[j];
+        p[2 * stride] = U[j];
+        p[3 * stride] = zt[j];
+        p[4 * stride] = av[j];
+        p[5 * stride] = __int_as_float(ai[j]);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ forward combine / reduce
+
+template <bool METRICS>
+__global__ __launch_bounds__(256) void fwd_combine_kernel(CombineArgs a) {
+  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (n >= a.N) return;
+  const int64_t tv = a.targets[n];
+  const bool valid = tv != a.ignore_index;
+  const bool bad = valid && (tv < 0 || tv >= a.V);
+  const int64_t stride = (int64_t)a.n_splits * a.N;
+  const float* pm = a.part + n;
+  float M = -INFINITY;
+  for (int k = 0; k < a.n_splits; ++k) M = fmaxf(M, pm[(int64_t)k * a.N]);
+  float S = 0.f, U = 0.f;
+  float av = -INFINITY;
+  int ai = 0x7fffffff;
+  for (int k = 0; k < a.n_splits; ++k) {
+    const float mk = pm[(int64_t)k * a.N];
+    if (mk != -INFINITY) {
+      const float d = mk - M;
+      const float al = fast_exp2(d * LOG2E);
+      S = S + pm[stride + (int64_t)k * a.N] * al;
+      if (METRICS) U = U + al * fmaf(d, pm[stride + (int64_t)k * a.N], pm[2 * stride + (int64_t)k * a.N]);
+    }
+    if (METRICS)
+      argmax_merge(av, ai, pm[4 * stride + (int64_t)k * a.N], __float_as_int(pm[5 * stride + (int64_t)k * a.N]));
+  }
+  const float logS = logf(S);
+  const float lse = M + logS;
+  float row = 0.f;
+  if (valid) {
+    if (bad) {
+      row = NAN;
+    } else {
+      const int owner = (int)((tv / TILE) / a.tiles_per_split);
+      row = lse - pm[3 * stride + (int64_t)owner * a.N];
+    }
+  }
+  if (a.lse_out) a.lse_out[n] = lse;
+  if (a.loss_rows) a.loss_rows[n] = row;
+  a.row_loss[n] = row;
+  int flag = (valid ? 1 : 0) | (bad ? 4 : 0);
+  if (METRICS) {
+    if (valid && !bad && ai == tv) flag |= 2;
+    a.row_ent[n] = valid ? logS - U / S : 0.f;
+  }
+  a.row_flag[n] = flag;
+}
+
+template <bool METRICS>
+__global__ __launch_bounds__(1024) void fwd_reduce_kernel(ReduceArgs a) {
+  __shared__ double sh_l[1024], sh_e[1024];
+  __shared__ int sh_v[1024], sh_h[1024], sh_b[1024];
+  const int t = threadIdx.x;
+  double sl = 0.0, se = 0.0;
+  int nv = 0, nh = 0, nb = 0;
+  for (int64_t n = t; n < a.N; n += 1024) {
+    const int f = a.row_flag[n];
+    sl += (double)a.row_loss[n];
+    nv += f & 1;
+    nh += (f >> 1) & 1;
+    nb |= (f >> 2) & 1;
+    if (METRICS) se += (double)a.row_ent[n];
+  }
+  sh_l[t] = sl;
+  sh_e[t] = se;
+  sh_v[t] = nv;
+  sh_h[t] = nh;
+  sh_b[t] = nb;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if (t < w) {
+      sh_l[t] += sh_l[t + w];
+      sh_e[t] += sh_e[t + w];
+      sh_v[t] += sh_v[t + w];
+      sh_h[t] += sh_h[t + w];
+      sh_b[t] |= sh_b[t + w];
+    }
+    __syncthreads();
+  }
+  if (t == 0) {
+    const int64_t nvalid = sh_v[0];
+    if (a.reduction == 0) a.loss[0] = nvalid > 0 ? (float)(sh_l[0] / (double)nvalid) : NAN;
+    if (a.reduction == 1) a.loss[0] = (float)sh_l[0];
+    if (METRICS && a.metrics) {
+      a.metrics[0] = nvalid > 0 ? (float)((double)sh_h[0] / (double)nvalid) : NAN;
+      a.metrics[1] = nvalid > 0 ? (float)(sh_e[0] / (double)nvalid) : NAN;
+    }
+    a.status[0] = (uint32_t)sh_b[0];
+  }
+}
+
+// ------------------------------------------------------------------ backward helpers
+
+__global__ __launch_bounds__(1024) void bwd_prep_kernel(PrepArgs a) {
+  __shared__ int sh[1024];
+  const int t = threadIdx.x;
+  int nv = 0;
+  for (int64_t n = t; n < a.N; n += 1024) nv += a.targets[n] != a.ignore_index ? 1 : 0;
+  sh[t] = nv;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if (t < w) sh[t] += sh[t + w];
+    __syncthreads();
+  }
+  if (t == 0) {
+    float scale = 1.f;
+    if (a.reduction != 2) {
+      const float g = a.grad_loss ? a.grad_loss[0] : 1.f;
+      if (a.reduction == 0) scale = sh[0] > 0 ? g / (float)sh[0] : 0.f;
+      else scale = g;
+    }
+    a.scale[0] = scale * a.s;
+  }
+}
+
+// dst[c][r] = src[r][c] for r < rows, 0 for rows <= r < rpad.  64x64 tiles.
+template <int EB>
+__global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
+  typedef typename std::conditional<EB == 4, uint32_t, uint16_t>::type U;
+  __shared__ U tile[64][65];
+  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+  const U* src = reinterpret_cast<const U*>(a.src);
+  U* dst = reinterpret_cast<U*>(a.dst);
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int k = ty; k < 64; k += 4) {
+    const int64_t r = r0 + k, c = c0 + tx;
+    tile[k][tx] = (r < a.rows && c < a.cols) ? src[r * a.src_ld + c] : (U)0;
+  }
+  __syncthreads();
+  for (int k = ty; k < 64; k += 4) {
+    const int64_t c = c0 + k, r = r0 + tx;
+    if (c < a.cols && r < a.rpad) dst[c * a.rpad + r] = tile[tx][k];
+  }
+}
+
+__global__ void fill_zero_kernel(uint8_t* p, int64_t bytes) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < bytes;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+// ------------------------------------------------------------------ backward G (recompute)
+
+template <int D, bool BIAS, bool CAP>
+__global__ __launch_bounds__(NTHREADS) void bwd_g_kernel(GArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  typedef typename Elem<D>::T T;
+  constexpr int EB = Elem<D>::bytes;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave >> 1, wn = wave & 1, r32 = lane & 31, half = lane >> 5;
+
+  const int L = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int tt = L % a.n_tok_tiles, vt = L / a.n_tok_tiles;
+  const int64_t n0 = (int64_t)tt * TILE;
+  const int vl0 = vt * TILE;              // chunk-local first id of the tile
+  const int64_t v0 = a.c0 + vl0;          // global first id
+  const int64_t rowb = a.H * EB;
+
+  Panel A{a.weight + v0 * rowb, rowb, (int)min<int64_t>(TILE, a.V - v0), rowb};
+  Panel B{a.hidden + n0 * rowb, rowb, (int)min<int64_t>(TILE, a.N - n0), rowb};
+  f32x16_t acc[4][4];
+  gemm_nt_tile<D>(acc, A, B, lds);
+
+  float lse[4], coef[4];
+  int tgt[4];
+  bool live[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t n = n0 + wn * 128 + 32 * j + r32;
+    live[j] = false;
+    tgt[j] = -1;
+    lse[j] = 0.f;
+    coef[j] = 0.f;
+    if (n < a.N) {
+      const int64_t tv = a.targets[n];
+      if (tv != a.ignore_index) {
+        live[j] = true;
+        lse[j] = a.lse[n];
+        if (tv < 0 || tv >= a.V) {
+          coef[j] = NAN;
+        } else {
+          tgt[j] = (int)tv;
+          coef[j] = (a.none_reduction && a.grad_rows) ? a.grad_rows[n] : 1.f;
+        }
+      }
+    }
+  }
+
+  const int vbase = (int)v0 + wm * 128;
+  float bv[4][16];
+  load_bias_rows<D, BIAS>(bv, a.bias, vbase, a.V, half);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int v = vbase + 32 * i + acc_row(r, half);
+      const int vl = v - (int)a.c0;
+      const bool vin = v < a.V && vl < a.cv;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float y = acc[i][j][r];
+        if (BIAS) y = y + bv[i][r];
+        y = a.s * y;
+        if (CAP) y = soft_cap(y, a.cap, a.inv_cap);
+        const float p = fast_exp2((y - lse[j]) * LOG2E);
+        float g = v == tgt[j] ? p - 1.f : p;
+        if (CAP) {
+          const float q = y * a.inv_cap;
+          g = g * fmaf(-q, q, 1.f);
+        }
+        g = g * coef[j];
+        acc[i][j][r] = (vin && live[j]) ? g : 0.f;
+      }
+    }
+
+  // G[n][vl] (row pitch cvpad): 4 consecutive ids per lane -> one vector store.
+  if (a.G) {
+    T* G = reinterpret_cast<T*>(a.G);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t n = n0 + wn * 128 + 32 * j + r32;
+      if (n >= a.npad) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int vl = vl0 + wm * 128 + 32 * i + 8 * g4 + 4 * half;
+          if (vl >= a.cvpad) continue;
+          T* dst = G + n * a.cvpad + vl;
+          if constexpr (EB == 2) {
+            typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+            u16x4 pk;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pk[e] = __builtin_bit_cast(uint16_t, from_f32<D>(acc[i][j][4 * g4 + e]));
+            *reinterpret_cast<u16x4*>(dst) = pk;
+          } else {
+            *reinterpret_cast<float4*>(dst) =
+                make_float4(acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2], acc[i][j][4 * g4 + 3]);
+          }
+        }
+    }
+  }
+  // G^T[vl][n] (row pitch npad): lanes of a half-wave cover 32 consecutive tokens.
+  if (a.GT) {
+    T* GT = reinterpret_cast<T*>(a.GT);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int vl = vl0 + wm * 128 + 32 * i + acc_row(r, half);
+        if (vl >= a.cvpad) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t n = n0 + wn * 128 + 32 * j + r32;
+          if (n < a.npad) GT[(int64_t)vl * a.npad + n] = from_f32<D>(acc[i][j][r]);
+        }
+      }
+  }
+  // grad_bias partials: sum over this wave's 128 tokens, per vocabulary id.
+  if (a.dbpart) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float s = (acc[i][0][r] + acc[i][1][r]) + (acc[i][2][r] + acc[i][3][r]);
+        s += __shfl_xor(s, 1);
+        s += __shfl_xor(s, 2);
+        s += __shfl_xor(s, 4);
+        s += __shfl_xor(s, 8);
+        s += __shfl_xor(s, 16);
+        const int v = vbase + 32 * i + acc_row(r, half);
+        const int vl = v - (int)a.c0;
+        if (r32 == 0 && v < a.V && vl < a.cv) a.dbpart[(int64_t)(2 * tt + wn) * a.V + v] = s;
+      }
+  }
+}
+
+// ------------------------------------------------------------------ backward contractions
+
+template <int D>
+__global__ __launch_bounds__(NTHREADS) void bwd_dh_kernel(DhArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  typedef typename Elem<D>::T T;
+  constexpr int EB = Elem<D>::bytes;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave >> 1, wn = wave & 1, r32 = lane & 31, half = lane >> 5;
+  const int L = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int tt = L % a.n_tok_tiles, ht = L / a.n_tok_tiles;
+  const int64_t n0 = (int64_t)tt * TILE, h0 = (int64_t)ht * TILE;
+  const int64_t kb = (int64_t)a.cvpad * EB;
+  Panel A{a.G + n0 * kb, kb, (int)min<int64_t>(TILE, a.N - n0), kb};
+  Panel B{a.WcT + h0 * kb, kb, (int)min<int64_t>(TILE, a.H - h0), kb};
+  f32x16_t acc[4][4];
+  gemm_nt_tile<D>(acc, A, B, lds);
+  const float scale = a.scale[0];
+  T* out = reinterpret_cast<T*>(a.out);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t n = n0 + wm * 128 + 32 * i + acc_row(r, half);
+      if (n >= a.N) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t h = h0 + wn * 128 + 32 * j + r32;
+        if (h >= a.H) continue;
+        const int64_t idx = n * a.H + h;
+        const float val = acc[i][j][r] * scale;
+        if (a.first && a.last) out[idx] = from_f32<D>(val);
+        else if (a.first) a.acc[idx] = val;
+        else if (a.last) out[idx] = from_f32<D>(a.acc[idx] + val);
+        else a.acc[idx] = a.acc[idx] + val;
+      }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(NTHREADS) void bwd_dw_kernel(DwArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  typedef typename Elem<D>::T T;
+  constexpr int EB = Elem<D>::bytes;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave >> 1, wn = wave & 1, r32 = lane & 31, half = lane >> 5;
+  const int L = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int ht = L % a.n_h_tiles, vt = L / a.n_h_tiles;
+  const int64_t v0 = (int64_t)vt * TILE, h0 = (int64_t)ht * TILE;
+  const int64_t kb = (int64_t)a.npad * EB;
+  Panel A{a.GT + v0 * kb, kb, (int)min<int64_t>(TILE, a.cv - v0), kb};
+  Panel B{a.HT + h0 * kb, kb, (int)min<int64_t>(TILE, a.H - h0), kb};
+  f32x16_t acc[4][4];
+  gemm_nt_tile<D>(acc, A, B, lds);
+  const float scale = a.scale[0];
+  T* out = reinterpret_cast<T*>(a.out);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t v = v0 + wm * 128 + 32 * i + acc_row(r, half);
+      if (v >= a.cv) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t h = h0 + wn * 128 + 32 * j + r32;
+        if (h < a.H) out[v * a.H + h] = from_f32<D>(acc[i][j][r] * scale);
+      }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_db_kernel(DbArgs a) {
+  typedef typename Elem<D>::T T;
+  const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (v >= a.V) return;
+  float s = 0.f;
+  for (int p = 0; p < a.n_parts; ++p) s = s + a.dbpart[(int64_t)p * a.V + v];
+  reinterpret_cast<T*>(a.out)[v] = from_f32<D>(s * a.scale[0]);
+}
+
+// ------------------------------------------------------------------ launchers
+
+static inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+template <int D>
+static hipError_t fwd_tiles_dispatch(bool metrics, bool bias, bool cap, const FwdArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)(a.n_tok_tiles * a.n_splits)), block(NTHREADS);
+#define FLCE_FWD(M, B, C)                                                         \
+  if (metrics == M && bias == B && cap == C) {                                    \
+    hipLaunchKernelGGL((fwd_tiles_kernel<D, M, B, C>), grid, block, 0, st, a);    \
+    return hipGetLastError();                                                     \
+  }
+  FLCE_FWD(false, false, false) FLCE_FWD(false, false, true) FLCE_FWD(false, true, false)
+  FLCE_FWD(false, true, true) FLCE_FWD(true, false, false) FLCE_FWD(true, false, true)
+  FLCE_FWD(true, true, false) FLCE_FWD(true, true, true)
+#undef FLCE_FWD
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_forward_tiles(int dtype, bool metrics, bool bias, bool cap, const FwdArgs& a,
+                                hipStream_t st) {
+  switch (dtype) {
+    case DT_F32: return fwd_tiles_dispatch<DT_F32>(metrics, bias, cap, a, st);
+    case DT_F16: return fwd_tiles_dispatch<DT_F16>(metrics, bias, cap, a, st);
+    case DT_BF16: return fwd_tiles_dispatch<DT_BF16>(metrics, bias, cap, a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_forward_combine(bool metrics, const CombineArgs& a, hipStream_t st) {
+  const dim3 grid(blocks_for(a.N, 256)), block(256);
+  if (metrics) hipLaunchKernelGGL(fwd_combine_kernel<true>, grid, block, 0, st, a);
+  else hipLaunchKernelGGL(fwd_combine_kernel<false>, grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_forward_reduce(bool metrics, const ReduceArgs& a, hipStream_t st) {
+  if (metrics) hipLaunchKernelGGL(fwd_reduce_kernel<true>, dim3(1), dim3(1024), 0, st, a);
+  else hipLaunchKernelGGL(fwd_reduce_kernel<false>, dim3(1), dim3(1024), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_backward_prep(const PrepArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3(1), dim3(1024), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(int dtype, const TransposeArgs& a, hipStream_t st) {
+  const dim3 grid(blocks_for(a.rpad, 64), blocks_for(a.cols, 64)), block(256);
+  if (dtype == DT_F32) hipLaunchKernelGGL(transpose_kernel<4>, grid, block, 0, st, a);
+  else hipLaunchKernelGGL(transpose_kernel<2>, grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t g_dispatch(bool bias, bool cap, const GArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)(a.n_tok_tiles * a.n_voc_tiles)), block(NTHREADS);
+  if (!bias && !cap) hipLaunchKernelGGL((bwd_g_kernel<D, false, false>), grid, block, 0, st, a);
+  else if (!bias && cap) hipLaunchKernelGGL((bwd_g_kernel<D, false, true>), grid, block, 0, st, a);
+  else if (bias && !cap) hipLaunchKernelGGL((bwd_g_kernel<D, true, false>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((bwd_g_kernel<D, true, true>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_backward_g(int dtype, bool bias, bool cap, const GArgs& a, hipStream_t st) {
+  switch (dtype) {
+    case DT_F32: return g_dispatch<DT_F32>(bias, cap, a, st);
+    case DT_F16: return g_dispatch<DT_F16>(bias, cap, a, st);
+    case DT_BF16: return g_dispatch<DT_BF16>(bias, cap, a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_backward_dh(int dtype, const DhArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)(a.n_tok_tiles * a.n_h_tiles)), block(NTHREADS);
+  switch (dtype) {
+    case DT_F32: hipLaunchKernelGGL(bwd_dh_kernel<DT_F32>, grid, block, 0, st, a); break;
+    case DT_F16: hipLaunchKernelGGL(bwd_dh_kernel<DT_F16>, grid, block, 0, st, a); break;
+    case DT_BF16: hipLaunchKernelGGL(bwd_dh_kernel<DT_BF16>, grid, block, 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_backward_dw(int dtype, const DwArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)(a.n_voc_tiles * a.n_h_tiles)), block(NTHREADS);
+  switch (dtype) {
+    case DT_F32: hipLaunchKernelGGL(bwd_dw_kernel<DT_F32>, grid, block, 0, st, a); break;
+    case DT_F16: hipLaunchKernelGGL(bwd_dw_kernel<DT_F16>, grid, block, 0, st, a); break;
+    case DT_BF16: hipLaunchKernelGGL(bwd_dw_kernel<DT_BF16>, grid, block, 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_backward_db(int dtype, const DbArgs& a, hipStream_t st) {
+  const dim3 grid(blocks_for(a.V, 256)), block(256);
+  switch (dtype) {
+    case DT_F32: hipLaunchKernelGGL(bwd_db_kernel<DT_F32>, grid, block, 0, st, a); break;
+    case DT_F16: hipLaunchKernelGGL(bwd_db_kernel<DT_F16>, grid, block, 0, st, a); break;
+    case DT_BF16: hipLaunchKernelGGL(bwd_db_kernel<DT_BF16>, grid, block, 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t st) {
+  if (bytes == 0) return hipSuccess;
+  const unsigned grid = (unsigned)std::min<int64_t>(4096, ((int64_t)bytes + 255) / 256);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid), dim3(256), 0, st, reinterpret_cast<uint8_t*>(dst),
+                     (int64_t)bytes);
+  return hipGetLastError();
+}
+
+}  // namespace flce

@@ -1,0 +1,120 @@
+// flce_plan.h -- host/device shared argument blocks and the launch plan.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace flce {
+
+// Forward: one workgroup per (token tile, vocabulary split); a split is a run
+// of consecutive 256-id vocabulary tiles whose per-row online state the
+// workgroup carries in registers.  The split size depends on V only, so a
+// row's result does not depend on how many rows share the call.
+struct FwdArgs {
+  const char* hidden;
+  const char* weight;
+  const char* bias;
+  const int64_t* targets;
+  float* part;  // [6][n_splits][N]: m, S, U, z_target, argmax value, argmax id
+  int64_t N, H, V, ignore_index;
+  int n_tok_tiles, n_voc_tiles, tiles_per_split, n_splits;
+  float s, cap, inv_cap;
+};
+
+struct CombineArgs {
+  const int64_t* targets;
+  const float* part;
+  float* lse_out;   // may be null
+  float* loss_rows; // [N] output for reduction "none", else null
+  float* row_loss;  // workspace [N]
+  float* row_ent;   // workspace [N]
+  int* row_flag;    // workspace [N]: bit0 valid, bit1 hit, bit2 bad target
+  int64_t N, V, ignore_index;
+  int tiles_per_split, n_splits;
+};
+
+struct ReduceArgs {
+  const float* row_loss;
+  const float* row_ent;
+  const int* row_flag;
+  float* loss;      // [1] (mean/sum), unused for none
+  float* metrics;   // [2] or null
+  uint32_t* status;
+  int64_t N;
+  int reduction;
+};
+
+struct PrepArgs {
+  const int64_t* targets;
+  const float* grad_loss;  // null = 1
+  float* scale;            // out [1]: uniform gradient factor (reduction * upstream * s)
+  int64_t N, ignore_index;
+  int reduction;
+  float s;
+};
+
+struct TransposeArgs {
+  const char* src;   // rows x cols, leading dim src_ld elements
+  char* dst;         // cols x rpad, leading dim rpad elements; zeros for rows >= rows
+  int64_t rows, cols, src_ld, rpad;
+};
+
+struct GArgs {
+  const char* hidden;
+  const char* weight;   // full (V,H)
+  const char* bias;
+  const int64_t* targets;
+  const float* lse;
+  const float* grad_rows;  // reduction "none": per-row upstream gradient (null = 1)
+  char* G;                 // [npad][cvpad] or null
+  char* GT;                // [cvpad][npad] or null
+  float* dbpart;           // [2*n_tok_tiles][V] or null
+  int64_t N, H, V, ignore_index, c0;
+  int cv, cvpad, npad, n_tok_tiles, n_voc_tiles;
+  int none_reduction;
+  float s, cap, inv_cap;
+};
+
+struct DhArgs {
+  const char* G;     // [npad][cvpad]
+  const char* WcT;   // [H][cvpad]
+  float* acc;        // [N][H] fp32 accumulator across chunks
+  char* out;         // grad_hidden (N,H)
+  const float* scale;
+  int64_t N, H;
+  int cvpad, n_tok_tiles, n_h_tiles, first, last;
+};
+
+struct DwArgs {
+  const char* GT;    // [cvpad][npad]
+  const char* HT;    // [H][npad]
+  char* out;         // grad_weight rows [c0, c0+cv)
+  const float* scale;
+  int64_t H;
+  int cv, npad, n_voc_tiles, n_h_tiles;
+};
+
+struct DbArgs {
+  const float* dbpart;
+  char* out;
+  const float* scale;
+  int64_t V;
+  int n_parts;
+};
+
+// Launchers (flce_kernels.hip).  All asynchronous on `st`.
+hipError_t launch_forward_tiles(int dtype, bool metrics, bool bias, bool cap, const FwdArgs& a,
+                                hipStream_t st);
+hipError_t launch_forward_combine(bool metrics, const CombineArgs& a, hipStream_t st);
+hipError_t launch_forward_reduce(bool metrics, const ReduceArgs& a, hipStream_t st);
+hipError_t launch_backward_prep(const PrepArgs& a, hipStream_t st);
+hipError_t launch_transpose(int dtype, const TransposeArgs& a, hipStream_t st);
+hipError_t launch_backward_g(int dtype, bool bias, bool cap, const GArgs& a, hipStream_t st);
+hipError_t launch_backward_dh(int dtype, const DhArgs& a, hipStream_t st);
+hipError_t launch_backward_dw(int dtype, const DwArgs& a, hipStream_t st);
+hipError_t launch_backward_db(int dtype, const DbArgs& a, hipStream_t st);
+hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t st);
+
+}  // namespace flce

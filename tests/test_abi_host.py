@@ -1,0 +1,148 @@
+"""CPU tests of the C ABI: the library loads, exports every function the
+header declares, sizes workspaces, and rejects invalid arguments with the
+documented status before anything is launched.  No compute call here reaches
+a GPU: every call is invalid, and the one valid call runs only when no GPU
+is present (where it must report FLCE_ERR_HIP)."""
+import os
+import re
+
+import pytest
+
+from linear_cross_entropy_fwd_amd import _abi
+from linear_cross_entropy_fwd_amd._abi import BF16, F16, F32, make_problem
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "flce.h")
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIP = 0, 1, 2, 3, 4
+FAKE = 0x100000  # a 1 MiB-aligned non-null address; never dereferenced by these tests
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(flce_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = _abi.library()
+    names = declared_functions()
+    assert len(names) >= 8
+    for name in names:
+        assert hasattr(lib, name), name
+    assert _abi.flce_version().startswith("flce-gfx950")
+
+
+def test_status_strings():
+    lib = _abi.library()
+    for code, name in _abi.STATUS.items():
+        assert lib.flce_status_str(code).decode() == name
+
+
+def base(**kw):
+    args = dict(n=64, h=128, v=1000, dtype=F32)
+    args.update(kw)
+    return make_problem(args.pop("n"), args.pop("h"), args.pop("v"), args.pop("dtype"), **args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), INVALID),
+    (dict(reduction=5), INVALID),
+    (dict(n=-1), INVALID),
+    (dict(h=0), INVALID),
+    (dict(v=0), INVALID),
+    (dict(v=1 << 31), UNSUPPORTED),
+    (dict(h=30, dtype=F32), UNSUPPORTED),      # 120 bytes per row
+    (dict(h=12, dtype=BF16), UNSUPPORTED),     # 24 bytes per row
+    (dict(logit_scale=float("inf")), INVALID),
+    (dict(logit_scale=float("nan")), INVALID),
+    (dict(softcap=-1.0), INVALID),
+    (dict(softcap=float("nan")), INVALID),
+    (dict(softcap=float("inf")), INVALID),
+    (dict(fwd_tiles_per_split=-2), INVALID),
+    (dict(bwd_vocab_chunk=1000), INVALID),
+])
+def test_invalid_problems(kw, status):
+    p = base(**kw)
+    assert _abi.flce_forward_workspace_size(p) == 0
+    assert _abi.flce_backward_workspace_size(p) == 0
+    st = _abi.flce_forward(p, FAKE, FAKE, FAKE, 0, FAKE, FAKE, 0, FAKE, 1 << 30, 0)
+    assert st == status, _abi.last_error()
+    assert _abi.last_error()
+
+
+def test_problem_null():
+    import ctypes
+    lib = _abi.library()
+    assert lib.flce_forward_workspace_size(None) == 0
+    assert lib.flce_forward(None, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, 1 << 30, None) == INVALID
+
+
+def test_forward_pointer_and_workspace_validation():
+    p = base()
+    need = _abi.flce_forward_workspace_size(p)
+    assert need > 0
+    call = lambda **kw: _abi.flce_forward(
+        p, kw.get("h", FAKE), kw.get("w", FAKE), kw.get("t", FAKE), kw.get("b", 0), kw.get("loss", FAKE),
+        kw.get("lse", FAKE), kw.get("m", 0), kw.get("ws", FAKE), kw.get("wsb", need), 0)
+    assert call(h=0) == INVALID
+    assert call(t=0) == INVALID
+    assert call(loss=0) == INVALID
+    assert call(b=FAKE) == INVALID              # bias without has_bias
+    assert call(m=FAKE) == INVALID              # metrics without return_metrics
+    assert call(h=FAKE + 4) == INVALID          # misaligned hidden
+    assert call(t=FAKE + 4) == INVALID          # misaligned targets
+    assert call(ws=0) == WORKSPACE
+    assert call(wsb=need - 1) == WORKSPACE
+    assert call(ws=FAKE + 64) == INVALID        # misaligned workspace
+    pb = base(has_bias=True, return_metrics=True)
+    assert _abi.flce_forward(pb, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, 1 << 30, 0) == INVALID
+    assert _abi.flce_forward(pb, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 1 << 30, 0) == INVALID
+
+
+def test_backward_pointer_and_workspace_validation():
+    p = base()
+    need = _abi.flce_backward_workspace_size(p)
+    assert need > 0
+    call = lambda **kw: _abi.flce_backward(
+        p, kw.get("h", FAKE), kw.get("w", FAKE), kw.get("t", FAKE), kw.get("b", 0), kw.get("lse", FAKE),
+        0, kw.get("gh", FAKE), kw.get("gw", FAKE), kw.get("gb", 0), kw.get("ws", FAKE), kw.get("wsb", need), 0)
+    assert call(lse=0) == INVALID
+    assert call(gb=FAKE) == INVALID             # grad_bias without has_bias
+    assert call(gh=FAKE + 8) == INVALID         # misaligned grad_hidden
+    assert call(ws=0) == WORKSPACE
+    assert call(wsb=need - 1) == WORKSPACE
+    # nothing requested: a no-op that succeeds without touching anything
+    assert call(gh=0, gw=0, ws=0, wsb=0) == OK
+
+
+def test_workspace_sizes_scale_and_never_hold_n_by_v():
+    for n, h, v, dt in [(64, 128, 1000, F32), (2048, 2048, 32000, BF16), (4096, 4096, 128256, BF16),
+                        (8192, 3584, 152064, BF16), (16384, 2048, 262144, BF16)]:
+        for bias in (False, True):
+            p = make_problem(n, h, v, dt, has_bias=bias)
+            fwd = _abi.flce_forward_workspace_size(p)
+            bwd = _abi.flce_backward_workspace_size(p)
+            nv_bytes = n * v * (4 if dt == F32 else 2)
+            assert 0 < fwd < nv_bytes or n * v < 1 << 20
+            # the largest single backward buffer is a (N x chunk) gradient slab, far below N x V
+            assert bwd < nv_bytes or n * v < 1 << 20
+    big = make_problem(4096, 4096, 128256, BF16)
+    assert _abi.flce_backward_workspace_size(big) < 400e6
+
+
+def test_plan_overrides_change_workspace():
+    a = _abi.flce_forward_workspace_size(make_problem(512, 256, 50000, BF16))
+    b = _abi.flce_forward_workspace_size(make_problem(512, 256, 50000, BF16, fwd_tiles_per_split=1))
+    assert b > a                                  # more splits -> more partial state
+    c = _abi.flce_backward_workspace_size(make_problem(512, 256, 50000, BF16, bwd_vocab_chunk=1024))
+    d = _abi.flce_backward_workspace_size(make_problem(512, 256, 50000, BF16))
+    assert c < d
+
+
+def test_valid_call_without_gpu_reports_hip_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; this test covers the no-device path only")
+    p = base(n=0)
+    st = _abi.flce_forward(p, 0, 0, 0, 0, FAKE, 0, 0, FAKE, 1 << 20, 0)
+    assert st == HIP
+    assert "device" in _abi.last_error().lower() or _abi.last_error()

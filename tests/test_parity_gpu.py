@@ -1,0 +1,132 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs, element by element, at sizes the oracle finishes in
+seconds that still span several 256-wide tiles and ragged tails."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import flce_inputs as fi
+from flce_testutil import (TOL, check_against_oracle, fill_argmax_targets, gpu_inputs, log_case,
+                           oracle_inputs, to_np)
+from oracle import flce_reference
+
+pytestmark = pytest.mark.gpu
+
+
+def run_case(w: fi.Workload, *, backward=True, bwd_vocab_chunk=0, fwd_tiles_per_split=0,
+             grad_output=None, d=None):
+    import linear_cross_entropy_fwd_amd as flce
+    log_case(f"{w.name} n={w.n} h={w.h} v={w.v} dtype={w.dtype} red={w.reduction} "
+             f"chunk={bwd_vocab_chunk} tps={fwd_tiles_per_split}")
+    if d is None:
+        d = fill_argmax_targets(w, fi.generate(w))
+    g = gpu_inputs(d)
+    loss, lse, metrics = flce.flce_forward(
+        g["hidden"], g["weight"], g["targets"], g["bias"], ignore_index=w.ignore_index,
+        logit_scale=w.logit_scale, softcap=w.softcap, reduction=w.reduction,
+        return_metrics=w.return_metrics, fwd_tiles_per_split=fwd_tiles_per_split)
+    grads = None
+    if backward:
+        go = None if grad_output is None else torch.as_tensor(grad_output, dtype=torch.float32)
+        grads = flce.flce_backward(
+            g["hidden"], g["weight"], g["targets"], g["bias"], lse, go, ignore_index=w.ignore_index,
+            logit_scale=w.logit_scale, softcap=w.softcap, reduction=w.reduction,
+            bwd_vocab_chunk=bwd_vocab_chunk)
+    torch.cuda.synchronize()
+    h, wt, t, b = oracle_inputs(d)
+    ref = flce_reference(h, wt, t, b, ignore_index=w.ignore_index, logit_scale=w.logit_scale,
+                         softcap=w.softcap, reduction=w.reduction, grad_output=grad_output,
+                         compute_grads=backward)
+    out = check_against_oracle(w, d, ref, loss=loss, lse=lse, metrics=metrics, grads=grads,
+                               what=w.name)
+    print("  errors:", out, flush=True)
+    return loss, lse, metrics, grads, ref, d
+
+
+W = fi.WORKLOADS
+
+
+def test_tiny_f32_full_config():
+    run_case(W["tiny_f32"])
+
+
+def test_midvocab_shape_ragged_bf16():
+    run_case(W["midvocab_bf16"].resized(n=300, h=256, v=3000))
+
+
+def test_headvocab_shape_multichunk_bf16():
+    run_case(W["headvocab_bf16"].resized(n=512, h=512, v=8200), bwd_vocab_chunk=2048)
+
+
+def test_transforms_shape_bias_scale_cap_sum_metrics():
+    run_case(W["transforms_bf16"].resized(n=384, h=384, v=5000), bwd_vocab_chunk=1024)
+
+
+def test_peaked_shape_none_forward_and_mean_backward():
+    w = W["peaked_bf16"].resized(n=512, h=1024, v=4096)
+    d = fill_argmax_targets(w, fi.generate(w))
+    run_case(w.resized(reduction="none"), backward=False, d=d)
+    run_case(w, d=d)
+
+
+def test_f16_replica_of_midvocab():
+    run_case(W["midvocab_bf16"].resized(n=320, h=256, v=2500, dtype="f16"))
+
+
+def test_none_reduction_backward_with_row_gradients():
+    w = W["transforms_bf16"].resized(n=200, h=128, v=1500, reduction="none", return_metrics=False)
+    go = np.random.default_rng(0).standard_normal(200).astype(np.float32)
+    run_case(w, grad_output=go)
+
+
+@pytest.mark.parametrize("n", [1, 63, 65, 257])
+def test_token_tails(n):
+    run_case(W["tiny_f32"].resized(n=n, h=64, v=700))
+    run_case(W["midvocab_bf16"].resized(n=n, h=128, v=1000))
+
+
+@pytest.mark.parametrize("v", [1, 7, 255, 257, 32001])
+def test_vocab_tails(v):
+    run_case(W["headvocab_bf16"].resized(n=96, h=128, v=v, targets="uniform"))
+
+
+@pytest.mark.parametrize("h,dtype", [(36, "f32"), (72, "bf16"), (200, "f16")])
+def test_hidden_not_multiple_of_stage(h, dtype):
+    run_case(W["midvocab_bf16"].resized(n=100, h=h, v=600, dtype=dtype))
+
+
+@pytest.mark.parametrize("tps,chunk", [(1, 256), (3, 768), (100, 0)])
+def test_plan_overrides(tps, chunk):
+    run_case(W["transforms_bf16"].resized(n=300, h=256, v=2600), fwd_tiles_per_split=tps,
+             bwd_vocab_chunk=chunk)
+
+
+def test_ignore_index_edge_cases():
+    base = W["tiny_f32"].resized(n=130, h=64, v=500)
+    d = fi.generate(base)
+    d_all = dict(d, targets=torch.full_like(d["targets"], -100))
+    for red in ("mean", "sum", "none"):
+        run_case(base.resized(reduction=red), d=d_all)
+    d_none = dict(d, targets=d["targets"].clamp(min=0))
+    run_case(base, d=d_none)
+    # an ignore index that is also a valid id: rows whose target is 0 are ignored
+    w0 = base.resized(ignore_index=0)
+    d0 = dict(d, targets=torch.where(d["targets"] < 0, torch.zeros_like(d["targets"]), d["targets"]))
+    run_case(w0, d=d0)
+
+
+def test_empty_batch():
+    import linear_cross_entropy_fwd_amd as flce
+    log_case("N=0")
+    h = torch.empty(0, 64, device="cuda")
+    w = torch.randn(50, 64, device="cuda")
+    t = torch.empty(0, dtype=torch.int64, device="cuda")
+    b = torch.randn(50, device="cuda")
+    loss, lse, m = flce.flce_forward(h, w, t, b, return_metrics=True)
+    assert math.isnan(loss.item()) and torch.isnan(m).all()
+    loss, _, _ = flce.flce_forward(h, w, t, b, reduction="sum")
+    assert loss.item() == 0.0
+    gh, gw, gb = flce.flce_backward(h, w, t, b, lse)
+    assert gh.numel() == 0 and torch.all(gw == 0) and torch.all(gb == 0)
