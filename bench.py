@@ -1,0 +1,215 @@
+"""Benchmark: fused linear cross-entropy forward + backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step is one full pass of the hot path over one batch: flce_forward
+(logit tiles with online log-sum-exp, split combine, reduction) followed by
+flce_backward (recompute, grad_hidden, grad_weight) on the head-vocabulary
+workload N=4096 tokens, H=4096, V=128256, bf16, mean reduction, Zipf(1.1)
+targets with 5% ignored rows.  Inputs are synthetic (seeded), generated on
+the GPU and resident in HBM before the timed region; outputs and workspaces
+are allocated once and reused.
+
+Prints one JSON line: throughput as TFLOP/s counting 8*N*H*V flops per step,
+the fraction of the dense bf16 MFMA peak, peak device memory above the
+inputs, a roofline entry for the forward logit-tile kernel, and the fp64
+CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fwd+bwd TFLOP/s (8*N*H*V) and MFMA util at N=4096,H=4096,V=128256 bf16"
+PEAK_BF16_TFLOPS = 2516.6          # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_tiles_headvocab_traffic.json")
+KERNEL_SOURCES = ["linear_cross_entropy_fwd_amd/csrc/flce_kernels.hip",
+                  "linear_cross_entropy_fwd_amd/csrc/flce_device.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic():
+    """HBM bytes per forward-tile launch from the committed counter runs, or
+    None when the kernel sources changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(d, w, rows: int):
+    """fp64 oracle (as it stands) on the first `rows` rows of the same inputs."""
+    import numpy as np
+    import threadpoolctl
+    from oracle import flce_reference
+
+    h = d["hidden"][:rows].float().cpu().numpy()
+    t = d["targets"][:rows].cpu().numpy()
+    wt = d["weight"].float().cpu().numpy()
+    np.dot(np.ones((2, 2)), np.ones((2, 2)))   # load BLAS so its thread pool is visible
+    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] + [1])
+    t0 = time.perf_counter()
+    flce_reference(h, wt, t, None, ignore_index=w.ignore_index, logit_scale=w.logit_scale,
+                   softcap=w.softcap, reduction=w.reduction)
+    dt = time.perf_counter() - t0
+    flops = 8.0 * rows * w.h * w.v
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {rows} of {w.n} rows (full H={w.h}, V={w.v}), fwd+bwd in fp64, "
+                      f"{dt:.2f} s wall, 8*rows*H*V flops"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=64)
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="run one device-to-device copy of this size first (HBM counter calibration)")
+    ap.add_argument("--workload", default="headvocab_bf16")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+              f"multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import flce_inputs as fi
+    import linear_cross_entropy_fwd_amd as flce
+    from linear_cross_entropy_fwd_amd import _abi
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = fi.WORKLOADS[args.workload]
+    d = fi.generate(w, device=dev)
+    hidden, weight, targets, bias = d["hidden"], d["weight"], d["targets"], d["bias"]
+    torch.cuda.synchronize()
+    base_mem = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+
+    p = flce.problem_for(hidden, weight, bias, w.ignore_index, w.logit_scale, w.softcap,
+                         w.reduction, w.return_metrics)
+    fws = torch.empty(_abi.flce_forward_workspace_size(p), dtype=torch.uint8, device=dev)
+    bws = torch.empty(_abi.flce_backward_workspace_size(p), dtype=torch.uint8, device=dev)
+    loss = torch.empty(w.n if w.reduction == "none" else 1, dtype=torch.float32, device=dev)
+    lse = torch.empty(w.n, dtype=torch.float32, device=dev)
+    metrics = torch.empty(2, dtype=torch.float32, device=dev) if w.return_metrics else None
+    gh = torch.empty_like(hidden)
+    gw = torch.empty_like(weight)
+    gb = torch.empty_like(bias) if bias is not None else None
+    ptr = lambda t: 0 if t is None else t.data_ptr()
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def forward():
+        _abi.check(_abi.flce_forward(p, ptr(hidden), ptr(weight), ptr(targets), ptr(bias), ptr(loss),
+                                     ptr(lse), ptr(metrics), ptr(fws), fws.numel(), sh))
+
+    def backward():
+        _abi.check(_abi.flce_backward(p, ptr(hidden), ptr(weight), ptr(targets), ptr(bias), ptr(lse), 0,
+                                      ptr(gh), ptr(gw), ptr(gb), ptr(bws), bws.numel(), sh))
+
+    if args.copy_calibration_mb > 0:
+        src = torch.ones(args.copy_calibration_mb << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(args.warmup):
+        forward()
+        backward()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for e0, e1, e2 in ev:
+        e0.record(stream)
+        forward()
+        e1.record(stream)
+        backward()
+        e2.record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / args.steps
+    fwd_ms = sum(e0.elapsed_time(e1) for e0, e1, _ in ev) / args.steps
+    bwd_ms = sum(e1.elapsed_time(e2) for _, e1, e2 in ev) / args.steps
+    peak_incr = torch.cuda.max_memory_allocated() - base_mem
+    if not torch.isfinite(loss).all() or not torch.isfinite(gw.float().abs().max()):
+        print("non-finite result", file=sys.stderr)
+        sys.exit(3)
+
+    flops = 8.0 * w.n * w.h * w.v
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    fwd_tflops = 2.0 * w.n * w.h * w.v / (fwd_ms * 1e-3) / 1e12
+    traffic = stored_traffic()
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded counter-hash inputs generated on the GPU)",
+        "config": {"workload": w.name, "n_tokens": w.n, "hidden": w.h, "vocab": w.v,
+                   "reduction": w.reduction, "targets": f"{w.targets}, {w.ignore_frac:.0%} ignored",
+                   "global_batch": w.n, "parallelism": "none (1 GPU)"},
+        "mfma_util": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "fwd_ms": round(fwd_ms, 4),
+        "bwd_ms": round(bwd_ms, 4),
+        "peak_mem_incr_mb": round(peak_incr / 2**20, 1),
+        "n_by_v_bytes_mb": round(w.n * w.v * 2 / 2**20, 1),
+        "wall_s_timed": round(t_wall, 3),
+        "roofline": {"kernel": "fwd_tiles_kernel (forward logit tiles + online LSE)",
+                     "bound": "mfma", "achieved": round(fwd_tflops, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic,
+                     "flops_per_launch": 2 * w.n * w.h * w.v,
+                     "window": "HIP events around flce_forward (tile kernel + combine + reduce)"},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(d, w, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
