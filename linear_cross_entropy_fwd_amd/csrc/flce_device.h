@@ -5,11 +5,9 @@
 //
 // Tile geometry: a workgroup of 256 threads (4 wave64s, one per SIMD) owns a
 // 256 x 256 fp32 output tile; wave w covers rows [128*(w>>1), +128) and
-// columns [128*(w&1), +128) as 4 x 4 blocks of the 32x32 MFMA.  K advances
-// 128 bytes per stage (64 bf16/f16 or 32 fp32 values); two LDS stages of
-// 256 rows x 144 bytes per operand (16 bytes of padding per row keep the
-// 16-byte fragment reads bank-conflict free), refilled from registers that
-// were loaded from global memory one stage ahead.
+// columns [128*(w&1), +128) as 4 x 4 blocks of the 32x32 MFMA; operands
+// stream through a four-stage LDS ring fed by direct global-to-LDS copies
+// (see gemm_nt_tile below).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -35,11 +33,6 @@ template <int D> __device__ __forceinline__ typename Elem<D>::T from_f32(float x
 
 constexpr int TILE = 256;          // output tile edge (rows and columns)
 constexpr int NTHREADS = 256;      // 4 waves
-constexpr int KBYTES = 128;        // K bytes per stage
-constexpr int PITCH = 144;         // LDS row pitch (bytes)
-constexpr int OP_BYTES = TILE * PITCH;           // one operand, one stage
-constexpr int STAGE_BYTES = 2 * OP_BYTES;        // A + B
-constexpr int LDS_BYTES = 2 * STAGE_BYTES;       // double buffered: 147456
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -79,67 +72,210 @@ struct Panel {
   int64_t kbytes;
 };
 
-template <bool MASKED>
-__device__ __forceinline__ void panel_load(uint4 (&r)[8], const Panel& p, int64_t k0, int t) {
-  const int seg = t & 7, rb = t >> 3;
-  const int64_t koff = k0 + seg * 16;
-  const bool kin = !MASKED || koff < p.kbytes;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int row = rb + 32 * i;
-    row = row < p.rows ? row : p.rows - 1;
-    const uint4* src = reinterpret_cast<const uint4*>(p.base + (int64_t)row * p.ld + koff);
-    if (MASKED) r[i] = kin ? *src : make_uint4(0u, 0u, 0u, 0u);
-    else r[i] = *src;
-  }
+// ---------------------------------------------------------------------------
+// Multi-stage operand pipeline.  Global memory is copied straight into LDS
+// (global_load_lds_dwordx4, 16 bytes per lane) three K-stages ahead of use,
+// into a ring of NSTAGES buffers.  A stage is 64 bytes of K for all 256 rows
+// of A and of B (32 KB).  Rows are stored 64 bytes apart with the four 16-byte
+// chunks of a row XOR-swizzled by (row>>2)&3, so that the 16 lanes that read
+// one chunk of 16 consecutive rows hit all 64 LDS banks once.  Each stage has
+// two 32-byte slabs; the fragments of the next slab are read while the MFMAs
+// of the current one run, and the single barrier per stage sits between the
+// two slabs' MFMAs.
+
+constexpr int ROWB = 64;                 // K bytes per row per stage
+constexpr int OPB = TILE * ROWB;         // one operand, one stage: 16 KB
+constexpr int STB = 2 * OPB;             // A + B: 32 KB
+constexpr int NSTAGES = 4;               // 128 KB of LDS
+
+__shared__ __attribute__((aligned(1024))) char g_stage0[STB];
+__shared__ __attribute__((aligned(1024))) char g_stage1[STB];
+__shared__ __attribute__((aligned(1024))) char g_stage2[STB];
+__shared__ __attribute__((aligned(1024))) char g_stage3[STB];
+
+// Separate arrays per stage (not one array with offsets) so that no access
+// to one stage's buffer is mistaken for an access to another's.
+template <int S> __device__ __forceinline__ char* stage_buf() {
+  if constexpr (S == 0) return g_stage0;
+  else if constexpr (S == 1) return g_stage1;
+  else if constexpr (S == 2) return g_stage2;
+  else return g_stage3;
 }
 
-// Loads K-stage `kt`; only a ragged last stage (K not a multiple of 128
-// bytes) takes the masked path.
-__device__ __forceinline__ void stage_load(uint4 (&ra)[8], uint4 (&rb)[8], const Panel& A,
-                                           const Panel& B, int kt, int nfull, int t) {
-  const int64_t k0 = (int64_t)kt * KBYTES;
-  if (kt < nfull) {
-    panel_load<false>(ra, A, k0, t);
-    panel_load<false>(rb, B, k0, t);
-  } else {
-    panel_load<true>(ra, A, k0, t);
-    panel_load<true>(rb, B, k0, t);
-  }
-}
-
-__device__ __forceinline__ void panel_store_lds(char* lds_op, const uint4 (&r)[8], int t) {
-  const int seg = t & 7, rb = t >> 3;
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    *reinterpret_cast<uint4*>(lds_op + (rb + 32 * i) * PITCH + seg * 16) = r[i];
-}
+struct Frags {
+  uint4 a[4], b[4];
+};
 
 template <int D>
-__device__ __forceinline__ void stage_mfma(f32x16_t (&acc)[4][4], const char* la, const char* lb,
-                                           int wm, int wn, int lane) {
-  const int r32 = lane & 31, half = lane >> 5;
+__device__ __forceinline__ void frag_mfma(f32x16_t (&acc)[4][4], const Frags& f) {
 #pragma unroll
-  for (int kc = 0; kc < 4; ++kc) {
-    uint4 a[4], b[4];
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      a[i] = *reinterpret_cast<const uint4*>(la + (wm * 128 + i * 32 + r32) * PITCH + kc * 32 + half * 16);
+    for (int j = 0; j < 4; ++j) mfma_frag<D>(acc[i][j], f.a[i], f.b[j]);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// One wave-wide copy of 16 bytes per lane from global memory into LDS: lane l
+// writes LDS bytes [lds + 16*l, +16).  Issued through inline asm so that only
+// the pipeline's explicit vmcnt waits order it (the compiler would otherwise
+// wait for every outstanding copy before any LDS read of a stage buffer).
+// `gbase` and `lds` are wave-uniform; `voff` is the lane's byte offset.
+__device__ __forceinline__ void lds_copy16(const char* gbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(gbase), "s"(lds)
+               : "memory");
+}
+
+// s_waitcnt vmcnt(N) only (gfx9 encoding: expcnt and lgkmcnt left at max).
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Wait until at most `n` stages (8 copies each) of this wave are in flight.
+__device__ __forceinline__ void wait_stages(int n) {
+  if (n >= 2) wait_vmcnt<16>();
+  else if (n == 1) wait_vmcnt<8>();
+  else wait_vmcnt<0>();
+}
+
+// Workgroup barrier that waits for this wave's LDS accesses (lgkmcnt(0)) but
+// not for its in-flight global copies; the signal fences keep the compiler
+// from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Per-thread global byte offsets of its 8 copies per stage.  Copy i (0..7):
+// operand i>>2, 16-row block blk = (i&3)*4 + wave; lane L covers row
+// blk*16 + L/4 (clamped to the panel), LDS chunk position L&3, which holds
+// global chunk (L&3) ^ ((row>>2)&3) of that row.
+struct CopyPlan {
+  uint32_t off[8];
+};
+
+__device__ __forceinline__ void copy_plan(CopyPlan& cp, const Panel& A, const Panel& B, int t) {
+  const int wave = t >> 6, L = t & 63;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      b[j] = *reinterpret_cast<const uint4*>(lb + (wn * 128 + j * 32 + r32) * PITCH + kc * 32 + half * 16);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) mfma_frag<D>(acc[i][j], a[i], b[j]);
+  for (int i = 0; i < 8; ++i) {
+    const Panel& p = i < 4 ? A : B;
+    const int blk = (i & 3) * 4 + wave;
+    int row = blk * 16 + (L >> 2);
+    const int c = (L & 3) ^ ((row >> 2) & 3);
+    row = row < p.rows ? row : p.rows - 1;
+    cp.off[i] = (uint32_t)(row * p.ld) + (uint32_t)(c * 16);
   }
+}
+
+// Copies stage kt into buffer S.  MASKED (ragged last stage only): a chunk
+// past K is read from the row's last valid 16 bytes instead (the offset stays
+// non-negative, so the address stays inside the row) and zeroed after it lands.
+template <int S, bool MASKED>
+__device__ __forceinline__ void copy_stage(const CopyPlan& cp, const Panel& A, const Panel& B, int kt,
+                                           int t) {
+  const int wave = t >> 6, L = t & 63;
+  const int64_t k0 = (int64_t)kt * ROWB;
+  char* base = stage_buf<S>();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const Panel& p = i < 4 ? A : B;
+    const int blk = (i & 3) * 4 + wave;
+    uint32_t off = cp.off[i];
+    if (MASKED) {
+      const int c = (((blk * 16 + (L >> 2)) >> 2) & 3) ^ (L & 3);
+      if (k0 + c * 16 >= p.kbytes) off = off - (uint32_t)(c * 16) + (uint32_t)(p.kbytes - 16 - k0);
+    }
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(base + (i >> 2) * OPB + blk * 1024));
+    lds_copy16(p.base + k0, off, dst);
+  }
+}
+
+template <int S>
+__device__ __forceinline__ void copy_any(const CopyPlan& cp, const Panel& A, const Panel& B, int kt,
+                                         int nk, bool ragged, int t) {
+  if (ragged && kt == nk - 1) copy_stage<S, true>(cp, A, B, kt, t);
+  else copy_stage<S, false>(cp, A, B, kt, t);
+}
+
+// Zeroes this thread's LDS chunks of ragged stage kt that lie past K.
+template <int S>
+__device__ __forceinline__ void zero_tail(const Panel& A, int kt, int t) {
+  const int wave = t >> 6, L = t & 63;
+  const int64_t k0 = (int64_t)kt * ROWB;
+  char* base = stage_buf<S>();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int blk = (i & 3) * 4 + wave;
+    const int c = (((blk * 16 + (L >> 2)) >> 2) & 3) ^ (L & 3);
+    if (k0 + c * 16 >= A.kbytes)
+      *reinterpret_cast<uint4*>(base + (i >> 2) * OPB + blk * 1024 + L * 16) = make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+// Byte offsets, inside a stage buffer, of this lane's fragment chunk for
+// slab 0 and slab 1, for its first A and first B row block.  The lane reads
+// rows wm*128 + 32*i + (l&31): they differ by multiples of 32, so the swizzle
+// term (row>>2)&3 = ((l&31)>>2)&3 is the same for all four blocks, which then
+// sit 32*ROWB bytes apart (an immediate offset).
+struct FragBase {
+  uint32_t a[2], b[2];
+};
+
+__device__ __forceinline__ void frag_base(FragBase& fb, int wm, int wn, int lane) {
+  const int r32 = lane & 31, half = lane >> 5, x = (r32 >> 2) & 3;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const uint32_t coff = (uint32_t)(((2 * s + half) ^ x) << 4);
+    fb.a[s] = (uint32_t)((wm * 128 + r32) * ROWB) + coff;
+    fb.b[s] = (uint32_t)(OPB + (wn * 128 + r32) * ROWB) + coff;
+  }
+}
+
+// Fragments of slab `slab` (32 bytes of K) of buffer S for this wave's 4 A
+// and 4 B row blocks: lane (l&31, l>>5) reads chunk 2*slab + (l>>5) of its row.
+template <int S>
+__device__ __forceinline__ void frag_read(Frags& f, const FragBase& fb, int slab) {
+  const char* base = stage_buf<S>();
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    f.a[i] = *reinterpret_cast<const uint4*>(base + fb.a[slab] + i * 32 * ROWB);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    f.b[j] = *reinterpret_cast<const uint4*>(base + fb.b[slab] + j * 32 * ROWB);
+}
+
+// Stage kt from buffer S (f0 holds its slab 0): copy stage kt+3 into buffer
+// (S+3)%4, slab-0 MFMAs, wait for stage kt+1 and barrier, read its slab 0,
+// slab-1 MFMAs.
+template <int D, int S>
+__device__ __forceinline__ void kstage(f32x16_t (&acc)[4][4], Frags& f0, Frags& f1, const CopyPlan& cp,
+                                       const FragBase& fb, const Panel& A, const Panel& B, int kt,
+                                       int nk, bool ragged, int t) {
+  frag_read<S>(f1, fb, 1);
+  if (kt + NSTAGES - 1 < nk) copy_any<(S + NSTAGES - 1) % NSTAGES>(cp, A, B, kt + NSTAGES - 1, nk, ragged, t);
+  frag_mfma<D>(acc, f0);
+  if (kt + 1 < nk) {
+    wait_stages(min(NSTAGES - 2, nk - kt - 2));
+    if (ragged && kt + 1 == nk - 1) zero_tail<(S + 1) % NSTAGES>(A, kt + 1, t);
+    lds_barrier();
+    frag_read<(S + 1) % NSTAGES>(f0, fb, 0);
+  }
+  frag_mfma<D>(acc, f1);
 }
 
 // acc[i][j] (this wave's 4x4 blocks) = A_panel . B_panel^T over all of K.
-// Ends with a barrier, so the caller may reuse `lds` right away.
+// Uses the stage buffers; returns after a barrier, so the caller may reuse
+// them (e.g. g_stage0) right away.
 template <int D>
-__device__ __forceinline__ void gemm_nt_tile(f32x16_t (&acc)[4][4], const Panel& A, const Panel& B,
-                                             char* lds) {
+__device__ __forceinline__ void gemm_nt_tile(f32x16_t (&acc)[4][4], const Panel& A, const Panel& B) {
+  static_assert(NSTAGES == 4, "the unrolled loop below assumes four stages");
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
@@ -148,26 +284,28 @@ __device__ __forceinline__ void gemm_nt_tile(f32x16_t (&acc)[4][4], const Panel&
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  const int nfull = (int)(A.kbytes / KBYTES);
-  const int nk = (int)((A.kbytes + KBYTES - 1) / KBYTES);
-  uint4 ra[8], rb[8];
-  stage_load(ra, rb, A, B, 0, nfull, t);
-  panel_store_lds(lds, ra, t);
-  panel_store_lds(lds + OP_BYTES, rb, t);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const char* cur = lds + (kt & 1) * STAGE_BYTES;
-    char* nxt = lds + ((kt + 1) & 1) * STAGE_BYTES;
-    const bool more = kt + 1 < nk;
-    if (more) stage_load(ra, rb, A, B, kt + 1, nfull, t);
-    stage_mfma<D>(acc, cur, cur + OP_BYTES, wm, wn, lane);
-    if (more) {
-      panel_store_lds(nxt, ra, t);
-      panel_store_lds(nxt + OP_BYTES, rb, t);
-    }
-    __syncthreads();
+  const int nk = (int)((A.kbytes + ROWB - 1) / ROWB);
+  const bool ragged = (A.kbytes % ROWB) != 0;
+  CopyPlan cp;
+  copy_plan(cp, A, B, t);
+  lds_barrier();  // every wave is done with the buffers of any previous use
+  copy_any<0>(cp, A, B, 0, nk, ragged, t);
+  if (1 < nk) copy_any<1>(cp, A, B, 1, nk, ragged, t);
+  if (2 < nk) copy_any<2>(cp, A, B, 2, nk, ragged, t);
+  wait_stages(min(NSTAGES - 2, nk - 1));
+  if (ragged && nk == 1) zero_tail<0>(A, 0, t);
+  lds_barrier();
+  FragBase fb;
+  frag_base(fb, wm, wn, lane);
+  Frags f0, f1;
+  frag_read<0>(f0, fb, 0);
+  for (int kt = 0; kt < nk; kt += 4) {
+    kstage<D, 0>(acc, f0, f1, cp, fb, A, B, kt, nk, ragged, t);
+    if (kt + 1 < nk) kstage<D, 1>(acc, f0, f1, cp, fb, A, B, kt + 1, nk, ragged, t);
+    if (kt + 2 < nk) kstage<D, 2>(acc, f0, f1, cp, fb, A, B, kt + 2, nk, ragged, t);
+    if (kt + 3 < nk) kstage<D, 3>(acc, f0, f1, cp, fb, A, B, kt + 3, nk, ragged, t);
   }
+  lds_barrier();
 }
 
 // Bijective remap of a 1-D workgroup id so that consecutive logical ids land

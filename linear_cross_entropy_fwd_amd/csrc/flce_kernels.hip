@@ -31,6 +31,14 @@ namespace flce {
 
 // ------------------------------------------------------------------ helpers
 
+// An int the compiler cannot see through: per-tile epilogue indices derived
+// from it are recomputed after each tile's GEMM instead of being hoisted out
+// of the tile loop and kept live (in registers the K-loop needs) across it.
+__device__ __forceinline__ int opaque_int(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 __device__ __forceinline__ float soft_cap(float y, float cap, float inv_cap) {
   return cap * tanhf(y * inv_cap);
 }
@@ -89,9 +97,10 @@ __device__ __forceinline__ void load_bias_rows(float (&bv)[4][16], const char* b
 
 // ------------------------------------------------------------------ forward tiles
 
+__shared__ float g_fwd_state[7 * 4 * NTHREADS];  // 28 KB next to the 128 KB stage ring
+
 template <int D, bool METRICS, bool BIAS, bool CAP>
 __global__ __launch_bounds__(NTHREADS) void fwd_tiles_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   constexpr int EB = Elem<D>::bytes;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1, r32 = lane & 31, half = lane >> 5;
@@ -105,29 +114,34 @@ __global__ __launch_bounds__(NTHREADS) void fwd_tiles_kernel(FwdArgs a) {
 
   Panel B{a.hidden + n0 * rowb, rowb, (int)min<int64_t>(TILE, a.N - n0), rowb};
 
-  int tgt[4];
-  float m[4], S[4], U[4], zt[4], av[4];
-  int ai[4];
+  // Per-row online state, kept in this thread's own LDS slots between vocab
+  // tiles so that it does not occupy registers across the GEMM.  Slot k of
+  // token column j: 0 m, 1 S, 2 U, 3 z_target, 4 argmax value, 5 argmax id,
+  // 6 target id (-1 when the row is ignored or its target is out of range).
+  float* st = g_fwd_state + t;
+#define FST(k, j) st[((k) * 4 + (j)) * NTHREADS]
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int64_t n = n0 + wn * 128 + 32 * j + r32;
     const int64_t tv = n < a.N ? a.targets[n] : a.ignore_index;
-    tgt[j] = (tv != a.ignore_index && tv >= 0 && tv < a.V) ? (int)tv : -1;
-    m[j] = -INFINITY;
-    S[j] = 0.f;
-    U[j] = 0.f;
-    zt[j] = 0.f;
-    av[j] = -INFINITY;
-    ai[j] = 0x7fffffff;
+    FST(0, j) = -INFINITY;
+    FST(1, j) = 0.f;
+    FST(2, j) = 0.f;
+    FST(3, j) = 0.f;
+    FST(4, j) = -INFINITY;
+    FST(5, j) = __int_as_float(0x7fffffff);
+    FST(6, j) = __int_as_float((tv != a.ignore_index && tv >= 0 && tv < a.V) ? (int)tv : -1);
   }
 
   f32x16_t acc[4][4];
   for (int vt = vt_begin; vt < vt_end; ++vt) {
     const int64_t v0 = (int64_t)vt * TILE;
     Panel A{a.weight + v0 * rowb, rowb, (int)min<int64_t>(TILE, a.V - v0), rowb};
-    gemm_nt_tile<D>(acc, A, B, lds);
+    gemm_nt_tile<D>(acc, A, B);
 
-    const int vbase = (int)v0 + wm * 128;
+    const int to = opaque_int(t);
+    const int half = (to >> 5) & 1;
+    const int vbase = (int)v0 + (to >> 7) * 128;
     const bool ragged = v0 + TILE > a.V;
     float bv[4][16];
     load_bias_rows<D, BIAS>(bv, a.bias, vbase, a.V, half);
@@ -148,7 +162,7 @@ __global__ __launch_bounds__(NTHREADS) void fwd_tiles_kernel(FwdArgs a) {
           z[i][r] = y;
           zmax = fmaxf(zmax, y);
         }
-      const float mold = m[j];
+      const float mold = FST(0, j);
       const float mnew = fmaxf(mold, zmax);
       if (mnew != -INFINITY) {
         float sum = 0.f, usum = 0.f;
@@ -162,17 +176,18 @@ __global__ __launch_bounds__(NTHREADS) void fwd_tiles_kernel(FwdArgs a) {
             if (METRICS) usum = fmaf(e, fmaxf(d, -1e30f), usum);
           }
         if (mold == -INFINITY) {
-          S[j] = sum;
-          if (METRICS) U[j] = usum;
+          FST(1, j) = sum;
+          if (METRICS) FST(2, j) = usum;
         } else {
           const float dm = mold - mnew;
           const float al = fast_exp2(dm * LOG2E);
-          if (METRICS) U[j] = fmaf(al, fmaf(dm, S[j], U[j]), usum);
-          S[j] = fmaf(S[j], al, sum);
+          const float Sold = FST(1, j);
+          if (METRICS) FST(2, j) = fmaf(al, fmaf(dm, Sold, FST(2, j)), usum);
+          FST(1, j) = fmaf(Sold, al, sum);
         }
-        m[j] = mnew;
+        FST(0, j) = mnew;
       }
-      if (METRICS && zmax > av[j]) {
+      if (METRICS && zmax > FST(4, j)) {
         int idx = 0x7fffffff;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -181,20 +196,35 @@ __global__ __launch_bounds__(NTHREADS) void fwd_tiles_kernel(FwdArgs a) {
             const int v = vbase + 32 * i + acc_row(r, half);
             if (z[i][r] == zmax && v < idx) idx = v;
           }
-        av[j] = zmax;
-        ai[j] = idx;
+        FST(4, j) = zmax;
+        FST(5, j) = __int_as_float(idx);
       }
-      const int local = tgt[j] - vbase;
+      const int local = __float_as_int(FST(6, j)) - vbase;
       if (local >= 0 && local < 128 && ((local >> 2) & 1) == half) {
         const int ti = local >> 5, tr = ((local & 31) >> 3) * 4 + (local & 3);
+        float zv = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (i == ti && r == tr) zt[j] = z[i][r];
+            if (i == ti && r == tr) zv = z[i][r];
+        FST(3, j) = zv;
       }
     }
   }
+
+  float m[4], S[4], U[4], zt[4], av[4];
+  int ai[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    m[j] = FST(0, j);
+    S[j] = FST(1, j);
+    U[j] = FST(2, j);
+    zt[j] = FST(3, j);
+    av[j] = FST(4, j);
+    ai[j] = __float_as_int(FST(5, j));
+  }
+#undef FST
 
   // Lanes l and l^32 hold the same token columns over disjoint vocab rows.
 #pragma unroll
@@ -209,7 +239,7 @@ __global__ __launch_bounds__(NTHREADS) void fwd_tiles_kernel(FwdArgs a) {
   }
 
   // Waves wm=0 and wm=1 hold the same tokens over disjoint vocab rows.
-  float* xs = reinterpret_cast<float*>(lds);
+  float* xs = reinterpret_cast<float*>(g_stage0);  // free after gemm_nt_tile returns
   if (wm == 1 && half == 0) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -391,7 +421,6 @@ __global__ void fill_zero_kernel(uint8_t* p, int64_t bytes) {
 
 template <int D, bool BIAS, bool CAP>
 __global__ __launch_bounds__(NTHREADS) void bwd_g_kernel(GArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   typedef typename Elem<D>::T T;
   constexpr int EB = Elem<D>::bytes;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -407,7 +436,7 @@ __global__ __launch_bounds__(NTHREADS) void bwd_g_kernel(GArgs a) {
   Panel A{a.weight + v0 * rowb, rowb, (int)min<int64_t>(TILE, a.V - v0), rowb};
   Panel B{a.hidden + n0 * rowb, rowb, (int)min<int64_t>(TILE, a.N - n0), rowb};
   f32x16_t acc[4][4];
-  gemm_nt_tile<D>(acc, A, B, lds);
+  gemm_nt_tile<D>(acc, A, B);
 
   float lse[4], coef[4];
   int tgt[4];
@@ -527,7 +556,6 @@ __global__ __launch_bounds__(NTHREADS) void bwd_g_kernel(GArgs a) {
 
 template <int D>
 __global__ __launch_bounds__(NTHREADS) void bwd_dh_kernel(DhArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   typedef typename Elem<D>::T T;
   constexpr int EB = Elem<D>::bytes;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -539,7 +567,7 @@ __global__ __launch_bounds__(NTHREADS) void bwd_dh_kernel(DhArgs a) {
   Panel A{a.G + n0 * kb, kb, (int)min<int64_t>(TILE, a.N - n0), kb};
   Panel B{a.WcT + h0 * kb, kb, (int)min<int64_t>(TILE, a.H - h0), kb};
   f32x16_t acc[4][4];
-  gemm_nt_tile<D>(acc, A, B, lds);
+  gemm_nt_tile<D>(acc, A, B);
   const float scale = a.scale[0];
   T* out = reinterpret_cast<T*>(a.out);
 #pragma unroll
@@ -564,7 +592,6 @@ __global__ __launch_bounds__(NTHREADS) void bwd_dh_kernel(DhArgs a) {
 
 template <int D>
 __global__ __launch_bounds__(NTHREADS) void bwd_dw_kernel(DwArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   typedef typename Elem<D>::T T;
   constexpr int EB = Elem<D>::bytes;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -576,7 +603,7 @@ __global__ __launch_bounds__(NTHREADS) void bwd_dw_kernel(DwArgs a) {
   Panel A{a.GT + v0 * kb, kb, (int)min<int64_t>(TILE, a.cv - v0), kb};
   Panel B{a.HT + h0 * kb, kb, (int)min<int64_t>(TILE, a.H - h0), kb};
   f32x16_t acc[4][4];
-  gemm_nt_tile<D>(acc, A, B, lds);
+  gemm_nt_tile<D>(acc, A, B);
   const float scale = a.scale[0];
   T* out = reinterpret_cast<T*>(a.out);
 #pragma unroll
