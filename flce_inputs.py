@@ -74,6 +74,19 @@ def _indices(n: int, device, start: int = 0) -> torch.Tensor:
     return torch.arange(start, start + n, dtype=torch.int64, device=device)
 
 
+def normal_range(start: int, count: int, std: float, key: int, dtype: torch.dtype,
+                 device="cpu") -> torch.Tensor:
+    """Elements [start, start+count) of the flattened N(0, std) stream ``key``."""
+    idx = _indices(count, device, start)
+    acc = torch.zeros(count, dtype=torch.int64, device=device)
+    for w in range(6):
+        h = hash_words(key, w, idx)
+        acc += (h >> 16) + (h & 0xFFFF)
+    x = (acc - 393210).to(torch.float32) * (1.0 / 65536.0)  # exact
+    x = x * torch.tensor(std, dtype=torch.float32)          # one fp32 rounding
+    return x.to(dtype)
+
+
 def normal_(shape, std: float, key: int, dtype: torch.dtype, device="cpu",
             block: Optional[int] = None) -> torch.Tensor:
     """N(0, std) draws (Irwin-Hall of 12 16-bit uniforms), rounded to dtype.
@@ -89,15 +102,15 @@ def normal_(shape, std: float, key: int, dtype: torch.dtype, device="cpu",
     out = torch.empty(numel, dtype=dtype, device=device)
     for b0 in range(0, numel, block):
         n = min(block, numel - b0)
-        idx = _indices(n, device, b0)
-        acc = torch.zeros(n, dtype=torch.int64, device=device)
-        for w in range(6):
-            h = hash_words(key, w, idx)
-            acc += (h >> 16) + (h & 0xFFFF)
-        x = (acc - 393210).to(torch.float32) * (1.0 / 65536.0)  # exact
-        x = x * torch.tensor(std, dtype=torch.float32)          # one fp32 rounding
-        out[b0:b0 + n] = x.to(dtype)
+        out[b0:b0 + n] = normal_range(b0, n, std, key, dtype, device)
     return out.view(*shape)
+
+
+def weight_rows(w: "Workload", r0: int, r1: int, device="cpu") -> torch.Tensor:
+    """Rows [r0, r1) of workload w's weight, drawn alone (same values as generate)."""
+    wstd = 1.0 / w.h if w.weight_std_is_inv_h else w.weight_std
+    return normal_range(r0 * w.h, (r1 - r0) * w.h, wstd, w.seed * 16 + _S_WEIGHT,
+                        w.torch_dtype, device).view(r1 - r0, w.h)
 
 
 def uniform_ids(n: int, v: int, key: int, device="cpu") -> torch.Tensor:

@@ -196,3 +196,57 @@ def row_argmax_ids(hidden, weight, bias=None, logit_scale=1.0, softcap=None, row
         z = transform_logits(h[r0:r0 + row_block] @ w.T, b, logit_scale, softcap)
         out[r0:r0 + row_block] = z.argmax(axis=1)
     return out
+
+
+def gradient_samples(hidden, weight, targets, lse, rows, vocab_ids, bias=None, ignore_index=-100,
+                     logit_scale=1.0, softcap=None, reduction="mean", grad_output=None):
+    """Selected gradient entries by the definition, given each row's lse.
+
+    grad_hidden[rows] needs the whole logit row of each selected token;
+    grad_weight[vocab_ids] and grad_bias[vocab_ids] need the selected logit
+    column for every token.  ``lse`` must be the oracle's own per-row
+    log-sum-exp (``flce_reference(..., compute_grads=False)["lse"]``).  The
+    coefficient of each row is the same as in ``flce_reference``: p - onehot
+    (card: "Algorithm"), times the reduction's upstream factor, times
+    d z / d raw.
+    """
+    h = _f64(hidden)
+    w = _f64(weight)
+    b = _f64(bias)
+    t = np.asarray(targets, dtype=np.int64)
+    lse = np.asarray(lse, dtype=np.float64)
+    n = h.shape[0]
+    valid = t != ignore_index
+    if np.any(valid & ((t < 0) | (t >= w.shape[0]))):
+        raise ValueError("target id outside [0, V) on a non-ignored row")
+    n_valid = int(valid.sum())
+    if reduction == "none":
+        g = np.ones(n) if grad_output is None else np.asarray(grad_output, np.float64).reshape(n)
+        coef = np.where(valid, g, 0.0)
+    else:
+        g = 1.0 if grad_output is None else float(np.asarray(grad_output, np.float64).reshape(()))
+        scale = g / n_valid if (reduction == "mean" and n_valid > 0) else (g if reduction == "sum" else 0.0)
+        coef = np.where(valid, scale, 0.0)
+
+    rows = np.asarray(rows, dtype=np.int64)
+    vocab_ids = np.asarray(vocab_ids, dtype=np.int64)
+    # grad_hidden rows: whole logit rows
+    z = transform_logits(h[rows] @ w.T, b, logit_scale, softcap)
+    gz = np.exp(z - lse[rows, None])
+    for k, i in enumerate(rows):
+        if valid[i]:
+            gz[k, t[i]] -= 1.0
+        else:
+            gz[k] = 0.0
+    graw = coef[rows, None] * gz * transform_derivative(z, logit_scale, softcap)
+    grad_h = graw @ w
+    # grad_weight / grad_bias entries: selected logit columns for all rows
+    zc = transform_logits(h @ w[vocab_ids].T, None if b is None else b[vocab_ids],
+                          logit_scale, softcap)
+    gzc = np.exp(zc - lse[:, None])
+    gzc -= (t[:, None] == vocab_ids[None, :]) & valid[:, None]
+    gzc[~valid] = 0.0
+    grawc = coef[:, None] * gzc * transform_derivative(zc, logit_scale, softcap)
+    grad_w = grawc.T @ h
+    grad_b = grawc.sum(axis=0)
+    return dict(grad_hidden=grad_h, grad_weight=grad_w, grad_bias=grad_b)

@@ -339,3 +339,22 @@ def test_mutation_last_index_argmax_is_caught(monkeypatch):
     monkeypatch.setattr(orc, "row_statistics", wrong)
     _pins_fail(lambda: test_zero_weight_closed_form(7, "mean"))
     _pins_fail(test_argmax_and_gap_brute_force)
+
+
+# --------------------------------------------------------------------------- sampled gradients
+
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+def test_gradient_samples_match_autograd(reduction):
+    h, w, b, t = problem(23, 41, 12, 70, bias=True, ignore_frac=0.25, wstd=1.5)
+    g = np.random.default_rng(9).standard_normal(41) if reduction == "none" else 0.6
+    for s, cap in [(1.0, None), (0.5, 2.5)]:
+        fwd = flce_reference(h, w, t, b, logit_scale=s, softcap=cap, reduction=reduction,
+                             compute_grads=False)
+        rows = [0, 3, 17, 40] + list(np.nonzero(t == -100)[0][:1])
+        vids = [0, 5, int(t[t >= 0][0]), 69]
+        smp = orc.gradient_samples(h, w, t, fwd["lse"], rows, vids, b, logit_scale=s, softcap=cap,
+                                   reduction=reduction, grad_output=g)
+        _, gh, gw, gb = torch_loss(h, w, b, t, -100, s, cap, reduction, g)
+        np.testing.assert_allclose(smp["grad_hidden"], gh[rows], rtol=1e-10, atol=1e-13)
+        np.testing.assert_allclose(smp["grad_weight"], gw[vids], rtol=1e-10, atol=1e-13)
+        np.testing.assert_allclose(smp["grad_bias"], gb[vids], rtol=1e-10, atol=1e-13)
