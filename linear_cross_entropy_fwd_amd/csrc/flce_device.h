@@ -264,9 +264,11 @@ __device__ __forceinline__ void kstage(f32x16_t (&acc)[4][4], Frags& f0, Frags& 
   if (kt + 1 < nk) {
     wait_stages(min(NSTAGES - 2, nk - kt - 2));
     if (ragged && kt + 1 == nk - 1) zero_tail<(S + 1) % NSTAGES>(A, kt + 1, t);
-    lds_barrier();
-    frag_read<(S + 1) % NSTAGES>(f0, fb, 0);
   }
+  // Unconditional (after the last stage the fragments read are unused), so
+  // that the slab-1 MFMAs below follow a single path and wait for nothing.
+  lds_barrier();
+  frag_read<(S + 1) % NSTAGES>(f0, fb, 0);
   frag_mfma<D>(acc, f1);
 }
 
