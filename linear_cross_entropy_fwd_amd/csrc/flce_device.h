@@ -130,6 +130,16 @@ __device__ __forceinline__ void lds_copy16(const char* gbase, uint32_t voff, uin
                : "memory");
 }
 
+// A wave-uniform pointer forced into scalar registers (a uniform value the
+// compiler computed in vector registers, e.g. after an integer division,
+// would otherwise be handed to the "s" operand of lds_copy16).
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t u = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 // s_waitcnt vmcnt(N) only (gfx9 encoding: expcnt and lgkmcnt left at max).
 template <int N> __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -174,34 +184,37 @@ __device__ __forceinline__ void copy_plan(CopyPlan& cp, const Panel& A, const Pa
   }
 }
 
-// Copies stage kt into buffer S.  MASKED (ragged last stage only): a chunk
-// past K is read from the row's last valid 16 bytes instead (the offset stays
-// non-negative, so the address stays inside the row) and zeroed after it lands.
-template <int S, bool MASKED>
-__device__ __forceinline__ void copy_stage(const CopyPlan& cp, const Panel& A, const Panel& B, int kt,
-                                           int t) {
+// Copy I (0..7) of stage kc into buffer S.  `masked` (ragged last stage
+// only): a chunk past K is read from the row's last valid 16 bytes instead
+// (the offset stays non-negative, so the address stays inside the row) and
+// zeroed after it lands.  The choice is a select, not a branch.
+template <int S, int I>
+__device__ __forceinline__ void copy_one_any(const CopyPlan& cp, const Panel& A, const Panel& B, int kc,
+                                            bool masked, int t) {
   const int wave = t >> 6, L = t & 63;
-  const int64_t k0 = (int64_t)kt * ROWB;
-  char* base = stage_buf<S>();
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const Panel& p = i < 4 ? A : B;
-    const int blk = (i & 3) * 4 + wave;
-    uint32_t off = cp.off[i];
-    if (MASKED) {
-      const int c = (((blk * 16 + (L >> 2)) >> 2) & 3) ^ (L & 3);
-      if (k0 + c * 16 >= p.kbytes) off = off - (uint32_t)(c * 16) + (uint32_t)(p.kbytes - 16 - k0);
-    }
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(base + (i >> 2) * OPB + blk * 1024));
-    lds_copy16(p.base + k0, off, dst);
-  }
+  const int64_t k0 = (int64_t)kc * ROWB;
+  const Panel& p = I < 4 ? A : B;
+  const int blk = (I & 3) * 4 + wave;
+  const int c = (((blk * 16 + (L >> 2)) >> 2) & 3) ^ (L & 3);
+  const uint32_t off = (masked && k0 + c * 16 >= p.kbytes)
+                           ? cp.off[I] - (uint32_t)(c * 16) + (uint32_t)(p.kbytes - 16 - k0)
+                           : cp.off[I];
+  const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(stage_buf<S>() + (I >> 2) * OPB + blk * 1024));
+  lds_copy16(uniform_ptr(p.base + k0), off, dst);
 }
 
 template <int S>
 __device__ __forceinline__ void copy_any(const CopyPlan& cp, const Panel& A, const Panel& B, int kt,
                                          int nk, bool ragged, int t) {
-  if (ragged && kt == nk - 1) copy_stage<S, true>(cp, A, B, kt, t);
-  else copy_stage<S, false>(cp, A, B, kt, t);
+  const bool masked = ragged && kt == nk - 1;
+  copy_one_any<S, 0>(cp, A, B, kt, masked, t);
+  copy_one_any<S, 1>(cp, A, B, kt, masked, t);
+  copy_one_any<S, 2>(cp, A, B, kt, masked, t);
+  copy_one_any<S, 3>(cp, A, B, kt, masked, t);
+  copy_one_any<S, 4>(cp, A, B, kt, masked, t);
+  copy_one_any<S, 5>(cp, A, B, kt, masked, t);
+  copy_one_any<S, 6>(cp, A, B, kt, masked, t);
+  copy_one_any<S, 7>(cp, A, B, kt, masked, t);
 }
 
 // Zeroes this thread's LDS chunks of ragged stage kt that lie past K.
@@ -238,43 +251,94 @@ __device__ __forceinline__ void frag_base(FragBase& fb, int wm, int wn, int lane
   }
 }
 
-// Fragments of slab `slab` (32 bytes of K) of buffer S for this wave's 4 A
-// and 4 B row blocks: lane (l&31, l>>5) reads chunk 2*slab + (l>>5) of its row.
-template <int S>
-__device__ __forceinline__ void frag_read(Frags& f, const FragBase& fb, int slab) {
+// Fragment P (0..3: A row block P, 4..7: B row block P-4) of slab `slab` of
+// buffer S: lane (l&31, l>>5) reads chunk 2*slab + (l>>5) of its row.
+template <int S, int P>
+__device__ __forceinline__ void frag_read_one(Frags& f, const FragBase& fb, int slab) {
   const char* base = stage_buf<S>();
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    f.a[i] = *reinterpret_cast<const uint4*>(base + fb.a[slab] + i * 32 * ROWB);
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    f.b[j] = *reinterpret_cast<const uint4*>(base + fb.b[slab] + j * 32 * ROWB);
+  if constexpr (P < 4)
+    f.a[P] = *reinterpret_cast<const uint4*>(base + fb.a[slab] + P * 32 * ROWB);
+  else
+    f.b[P - 4] = *reinterpret_cast<const uint4*>(base + fb.b[slab] + (P - 4) * 32 * ROWB);
 }
 
-// Stage kt from buffer S (f0 holds its slab 0): copy stage kt+3 into buffer
-// (S+3)%4, slab-0 MFMAs, wait for stage kt+1 and barrier, read its slab 0,
-// slab-1 MFMAs.
+// All eight, in the order slab_phase issues them, so that every path into a
+// stage has the same reads pending.
+template <int S>
+__device__ __forceinline__ void frag_read(Frags& f, const FragBase& fb, int slab) {
+  frag_read_one<S, 0>(f, fb, slab);
+  frag_read_one<S, 4>(f, fb, slab);
+  frag_read_one<S, 5>(f, fb, slab);
+  frag_read_one<S, 6>(f, fb, slab);
+  frag_read_one<S, 7>(f, fb, slab);
+  frag_read_one<S, 1>(f, fb, slab);
+  frag_read_one<S, 2>(f, fb, slab);
+  frag_read_one<S, 3>(f, fb, slab);
+}
+
+// Keeps the instruction scheduler from moving anything across this point,
+// so that the source order below is the issue order.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// One slab's 16 MFMAs on `fm`, with the eight fragment reads of the next slab
+// (buffer RS, slab RSLAB, into `fr`) and four copies (C0..C0+3 of stage kc
+// into buffer CS) spread between them: a wave has one SIMD to itself, issues
+// in order, and would otherwise stall its MFMAs behind a burst of copies
+// waiting for the address unit.
+template <int D, int RS, int CS, int C0>
+__device__ __forceinline__ void slab_phase(f32x16_t (&acc)[4][4], const Frags& fm, Frags& fr, const FragBase& fb,
+                                           int rslab, const CopyPlan& cp, const Panel& A, const Panel& B,
+                                           int kc, bool masked, int t) {
+  // The MFMAs run row block by row block (A0 with B0..B3, then A1, ...), so
+  // the reads go A0 B0 B1 B2 B3 A1 A2 A3: each lands at least ten MFMAs
+  // before its first use in the next slab.
+#define FLCE_STEP(I, J) mfma_frag<D>(acc[I][J], fm.a[I], fm.b[J])
+  FLCE_STEP(0, 0); frag_read_one<RS, 0>(fr, fb, rslab); sched_fence();
+  FLCE_STEP(0, 1); copy_one_any<CS, C0 + 0>(cp, A, B, kc, masked, t); sched_fence();
+  FLCE_STEP(0, 2); frag_read_one<RS, 4>(fr, fb, rslab); sched_fence();
+  FLCE_STEP(0, 3); sched_fence();
+  FLCE_STEP(1, 0); frag_read_one<RS, 5>(fr, fb, rslab); sched_fence();
+  FLCE_STEP(1, 1); copy_one_any<CS, C0 + 1>(cp, A, B, kc, masked, t); sched_fence();
+  FLCE_STEP(1, 2); frag_read_one<RS, 6>(fr, fb, rslab); sched_fence();
+  FLCE_STEP(1, 3); sched_fence();
+  FLCE_STEP(2, 0); frag_read_one<RS, 7>(fr, fb, rslab); sched_fence();
+  FLCE_STEP(2, 1); copy_one_any<CS, C0 + 2>(cp, A, B, kc, masked, t); sched_fence();
+  FLCE_STEP(2, 2); frag_read_one<RS, 1>(fr, fb, rslab); sched_fence();
+  FLCE_STEP(2, 3); sched_fence();
+  FLCE_STEP(3, 0); frag_read_one<RS, 2>(fr, fb, rslab); sched_fence();
+  FLCE_STEP(3, 1); copy_one_any<CS, C0 + 3>(cp, A, B, kc, masked, t); sched_fence();
+  FLCE_STEP(3, 2); frag_read_one<RS, 3>(fr, fb, rslab); sched_fence();
+  FLCE_STEP(3, 3); sched_fence();
+#undef FLCE_STEP
+}
+
+// Stage kt from buffer S (f0 holds its slab 0).  Every stage copies stage
+// kc = kt+3 into buffer (S+3)%4 (that buffer was last read in stage kt-1,
+// before that stage's barrier); past the end of K the copy re-reads the last
+// stage (never used) so that the schedule has no branches.
+//   phase A: slab-0 MFMAs | slab-1 reads of buffer S | copies 0..3 (operand A)
+//   wait for stage kt+1's copies, zero its ragged tail, barrier
+//   phase B: slab-1 MFMAs | slab-0 reads of buffer S+1 | copies 4..7 (operand B)
+// Copies issued after stage kt+1's when the wait runs: stage kt+2's eight and
+// stage kt+3's first four.
 template <int D, int S>
 __device__ __forceinline__ void kstage(f32x16_t (&acc)[4][4], Frags& f0, Frags& f1, const CopyPlan& cp,
                                        const FragBase& fb, const Panel& A, const Panel& B, int kt,
                                        int nk, bool ragged, int t) {
-  frag_read<S>(f1, fb, 1);
-  if (kt + NSTAGES - 1 < nk) copy_any<(S + NSTAGES - 1) % NSTAGES>(cp, A, B, kt + NSTAGES - 1, nk, ragged, t);
-  frag_mfma<D>(acc, f0);
-  if (kt + 1 < nk) {
-    wait_stages(min(NSTAGES - 2, nk - kt - 2));
-    if (ragged && kt + 1 == nk - 1) zero_tail<(S + 1) % NSTAGES>(A, kt + 1, t);
-  }
-  // Unconditional (after the last stage the fragments read are unused), so
-  // that the slab-1 MFMAs below follow a single path and wait for nothing.
+  constexpr int SN = (S + 1) % NSTAGES, SC = (S + NSTAGES - 1) % NSTAGES;
+  const int kc = min(kt + NSTAGES - 1, nk - 1);
+  const bool masked = ragged && kc == nk - 1;
+  sched_fence();
+  slab_phase<D, S, SC, 0>(acc, f0, f1, fb, 1, cp, A, B, kc, masked, t);
+  wait_vmcnt<12>();
+  if (ragged && kt + 1 == nk - 1) zero_tail<SN>(A, kt + 1, t);
   lds_barrier();
-  frag_read<(S + 1) % NSTAGES>(f0, fb, 0);
-  frag_mfma<D>(acc, f1);
+  slab_phase<D, SN, SC, 4>(acc, f1, f0, fb, 0, cp, A, B, kc, masked, t);
 }
 
 // acc[i][j] (this wave's 4x4 blocks) = A_panel . B_panel^T over all of K.
-// Uses the stage buffers; returns after a barrier, so the caller may reuse
-// them (e.g. g_stage0) right away.
+// Uses the stage buffers; returns after a barrier with no copy in flight, so
+// the caller may reuse them (e.g. g_stage0) right away.
 template <int D>
 __device__ __forceinline__ void gemm_nt_tile(f32x16_t (&acc)[4][4], const Panel& A, const Panel& B) {
   static_assert(NSTAGES == 4, "the unrolled loop below assumes four stages");
@@ -291,22 +355,35 @@ __device__ __forceinline__ void gemm_nt_tile(f32x16_t (&acc)[4][4], const Panel&
   CopyPlan cp;
   copy_plan(cp, A, B, t);
   lds_barrier();  // every wave is done with the buffers of any previous use
+  // stages 0..2 (clamped to the last stage, as in kstage)
   copy_any<0>(cp, A, B, 0, nk, ragged, t);
-  if (1 < nk) copy_any<1>(cp, A, B, 1, nk, ragged, t);
-  if (2 < nk) copy_any<2>(cp, A, B, 2, nk, ragged, t);
-  wait_stages(min(NSTAGES - 2, nk - 1));
+  copy_any<1>(cp, A, B, min(1, nk - 1), nk, ragged, t);
+  copy_any<2>(cp, A, B, min(2, nk - 1), nk, ragged, t);
+  wait_vmcnt<16>();
   if (ragged && nk == 1) zero_tail<0>(A, 0, t);
   lds_barrier();
   FragBase fb;
   frag_base(fb, wm, wn, lane);
   Frags f0, f1;
   frag_read<0>(f0, fb, 0);
-  for (int kt = 0; kt < nk; kt += 4) {
+  // Whole rounds of four stages, then the remaining 0..3 stages outside the
+  // loop (a loop header with only two predecessors keeps the waitcnt pass
+  // from falling back to a full wait at the top of every round).
+  int kt = 0;
+  for (; kt + 4 <= nk; kt += 4) {
     kstage<D, 0>(acc, f0, f1, cp, fb, A, B, kt, nk, ragged, t);
-    if (kt + 1 < nk) kstage<D, 1>(acc, f0, f1, cp, fb, A, B, kt + 1, nk, ragged, t);
-    if (kt + 2 < nk) kstage<D, 2>(acc, f0, f1, cp, fb, A, B, kt + 2, nk, ragged, t);
-    if (kt + 3 < nk) kstage<D, 3>(acc, f0, f1, cp, fb, A, B, kt + 3, nk, ragged, t);
+    kstage<D, 1>(acc, f0, f1, cp, fb, A, B, kt + 1, nk, ragged, t);
+    kstage<D, 2>(acc, f0, f1, cp, fb, A, B, kt + 2, nk, ragged, t);
+    kstage<D, 3>(acc, f0, f1, cp, fb, A, B, kt + 3, nk, ragged, t);
   }
+  if (kt < nk) {
+    kstage<D, 0>(acc, f0, f1, cp, fb, A, B, kt, nk, ragged, t);
+    if (kt + 1 < nk) {
+      kstage<D, 1>(acc, f0, f1, cp, fb, A, B, kt + 1, nk, ragged, t);
+      if (kt + 2 < nk) kstage<D, 2>(acc, f0, f1, cp, fb, A, B, kt + 2, nk, ragged, t);
+    }
+  }
+  wait_vmcnt<0>();
   lds_barrier();
 }
 
