@@ -106,14 +106,6 @@ struct Frags {
   uint4 a[4], b[4];
 };
 
-template <int D>
-__device__ __forceinline__ void frag_mfma(f32x16_t (&acc)[4][4], const Frags& f) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) mfma_frag<D>(acc[i][j], f.a[i], f.b[j]);
-}
-
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
@@ -144,13 +136,6 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
 template <int N> __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// Wait until at most `n` stages (8 copies each) of this wave are in flight.
-__device__ __forceinline__ void wait_stages(int n) {
-  if (n >= 2) wait_vmcnt<16>();
-  else if (n == 1) wait_vmcnt<8>();
-  else wait_vmcnt<0>();
 }
 
 // Workgroup barrier that waits for this wave's LDS accesses (lgkmcnt(0)) but
@@ -280,60 +265,102 @@ __device__ __forceinline__ void frag_read(Frags& f, const FragBase& fb, int slab
 // so that the source order below is the issue order.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// Copy issuers for slab_phase.  PlainCopy: a stage that lies wholly inside K
+// (no clamp, no mask); everything but the lane's fixed offset cp.off[I] is
+// scalar (the stage's global base and the LDS destination in m0).
+struct PlainCopy {
+  const CopyPlan& cp;
+  const char* base;   // operand base + this stage's K offset (wave-uniform)
+  uint32_t wave_lds;  // wave * 1024 (wave-uniform)
+  template <int S, int I> __device__ __forceinline__ void issue() const {
+    lds_copy16(base, cp.off[I], lds_addr(stage_buf<S>() + (I >> 2) * OPB + (I & 3) * 4096) + wave_lds);
+  }
+};
+
+// EdgeCopy: a stage at the end of K -- clamped to the last stage and masked
+// when that one is ragged (copy_one_any).
+struct EdgeCopy {
+  const CopyPlan& cp;
+  const Panel& A;
+  const Panel& B;
+  int kc;
+  bool masked;
+  int t;
+  template <int S, int I> __device__ __forceinline__ void issue() const {
+    copy_one_any<S, I>(cp, A, B, kc, masked, t);
+  }
+};
+
 // One slab's 16 MFMAs on `fm`, with the eight fragment reads of the next slab
-// (buffer RS, slab RSLAB, into `fr`) and four copies (C0..C0+3 of stage kc
-// into buffer CS) spread between them: a wave has one SIMD to itself, issues
-// in order, and would otherwise stall its MFMAs behind a burst of copies
-// waiting for the address unit.
-template <int D, int RS, int CS, int C0>
+// (buffer RS, slab `rslab`, into `fr`) and four copies (C0..C0+3 into buffer
+// CS) spread between them: a wave has one SIMD to itself, issues in order,
+// and would otherwise stall its MFMAs behind a burst of copies.
+template <int D, int RS, int CS, int C0, class Copy>
 __device__ __forceinline__ void slab_phase(f32x16_t (&acc)[4][4], const Frags& fm, Frags& fr, const FragBase& fb,
-                                           int rslab, const CopyPlan& cp, const Panel& A, const Panel& B,
-                                           int kc, bool masked, int t) {
+                                           int rslab, const Copy& cp) {
   // The MFMAs run row block by row block (A0 with B0..B3, then A1, ...), so
   // the reads go A0 B0 B1 B2 B3 A1 A2 A3: each lands at least ten MFMAs
   // before its first use in the next slab.
 #define FLCE_STEP(I, J) mfma_frag<D>(acc[I][J], fm.a[I], fm.b[J])
   FLCE_STEP(0, 0); frag_read_one<RS, 0>(fr, fb, rslab); sched_fence();
-  FLCE_STEP(0, 1); copy_one_any<CS, C0 + 0>(cp, A, B, kc, masked, t); sched_fence();
+  FLCE_STEP(0, 1); cp.template issue<CS, C0 + 0>(); sched_fence();
   FLCE_STEP(0, 2); frag_read_one<RS, 4>(fr, fb, rslab); sched_fence();
   FLCE_STEP(0, 3); sched_fence();
   FLCE_STEP(1, 0); frag_read_one<RS, 5>(fr, fb, rslab); sched_fence();
-  FLCE_STEP(1, 1); copy_one_any<CS, C0 + 1>(cp, A, B, kc, masked, t); sched_fence();
+  FLCE_STEP(1, 1); cp.template issue<CS, C0 + 1>(); sched_fence();
   FLCE_STEP(1, 2); frag_read_one<RS, 6>(fr, fb, rslab); sched_fence();
   FLCE_STEP(1, 3); sched_fence();
   FLCE_STEP(2, 0); frag_read_one<RS, 7>(fr, fb, rslab); sched_fence();
-  FLCE_STEP(2, 1); copy_one_any<CS, C0 + 2>(cp, A, B, kc, masked, t); sched_fence();
+  FLCE_STEP(2, 1); cp.template issue<CS, C0 + 2>(); sched_fence();
   FLCE_STEP(2, 2); frag_read_one<RS, 1>(fr, fb, rslab); sched_fence();
   FLCE_STEP(2, 3); sched_fence();
   FLCE_STEP(3, 0); frag_read_one<RS, 2>(fr, fb, rslab); sched_fence();
-  FLCE_STEP(3, 1); copy_one_any<CS, C0 + 3>(cp, A, B, kc, masked, t); sched_fence();
+  FLCE_STEP(3, 1); cp.template issue<CS, C0 + 3>(); sched_fence();
   FLCE_STEP(3, 2); frag_read_one<RS, 3>(fr, fb, rslab); sched_fence();
   FLCE_STEP(3, 3); sched_fence();
 #undef FLCE_STEP
 }
 
 // Stage kt from buffer S (f0 holds its slab 0).  Every stage copies stage
-// kc = kt+3 into buffer (S+3)%4 (that buffer was last read in stage kt-1,
-// before that stage's barrier); past the end of K the copy re-reads the last
-// stage (never used) so that the schedule has no branches.
+// kt+3 into buffer (S+3)%4 (that buffer was last read in stage kt-1, before
+// that stage's barrier):
 //   phase A: slab-0 MFMAs | slab-1 reads of buffer S | copies 0..3 (operand A)
 //   wait for stage kt+1's copies, zero its ragged tail, barrier
 //   phase B: slab-1 MFMAs | slab-0 reads of buffer S+1 | copies 4..7 (operand B)
 // Copies issued after stage kt+1's when the wait runs: stage kt+2's eight and
 // stage kt+3's first four.
+//
+// kstage_plain: stage kt+3 lies wholly inside K.
 template <int D, int S>
-__device__ __forceinline__ void kstage(f32x16_t (&acc)[4][4], Frags& f0, Frags& f1, const CopyPlan& cp,
-                                       const FragBase& fb, const Panel& A, const Panel& B, int kt,
-                                       int nk, bool ragged, int t) {
+__device__ __forceinline__ void kstage_plain(f32x16_t (&acc)[4][4], Frags& f0, Frags& f1, const CopyPlan& cp,
+                                             const FragBase& fb, const Panel& A, const Panel& B, int kt,
+                                             uint32_t wave_lds) {
+  constexpr int SN = (S + 1) % NSTAGES, SC = (S + NSTAGES - 1) % NSTAGES;
+  const int64_t k0 = (int64_t)(kt + NSTAGES - 1) * ROWB;
+  const PlainCopy ca{cp, uniform_ptr(A.base + k0), wave_lds};
+  const PlainCopy cb{cp, uniform_ptr(B.base + k0), wave_lds};
+  sched_fence();
+  slab_phase<D, S, SC, 0>(acc, f0, f1, fb, 1, ca);
+  wait_vmcnt<12>();
+  lds_barrier();
+  slab_phase<D, SN, SC, 4>(acc, f1, f0, fb, 0, cb);
+}
+
+// kstage_edge: any stage; past the end of K the copy re-reads the last stage
+// (never used), so the schedule still has no branches.
+template <int D, int S>
+__device__ __forceinline__ void kstage_edge(f32x16_t (&acc)[4][4], Frags& f0, Frags& f1, const CopyPlan& cp,
+                                            const FragBase& fb, const Panel& A, const Panel& B, int kt,
+                                            int nk, bool ragged, int t) {
   constexpr int SN = (S + 1) % NSTAGES, SC = (S + NSTAGES - 1) % NSTAGES;
   const int kc = min(kt + NSTAGES - 1, nk - 1);
-  const bool masked = ragged && kc == nk - 1;
+  const EdgeCopy c{cp, A, B, kc, ragged && kc == nk - 1, t};
   sched_fence();
-  slab_phase<D, S, SC, 0>(acc, f0, f1, fb, 1, cp, A, B, kc, masked, t);
+  slab_phase<D, S, SC, 0>(acc, f0, f1, fb, 1, c);
   wait_vmcnt<12>();
   if (ragged && kt + 1 == nk - 1) zero_tail<SN>(A, kt + 1, t);
   lds_barrier();
-  slab_phase<D, SN, SC, 4>(acc, f1, f0, fb, 0, cp, A, B, kc, masked, t);
+  slab_phase<D, SN, SC, 4>(acc, f1, f0, fb, 0, c);
 }
 
 // acc[i][j] (this wave's 4x4 blocks) = A_panel . B_panel^T over all of K.
@@ -341,7 +368,7 @@ __device__ __forceinline__ void kstage(f32x16_t (&acc)[4][4], Frags& f0, Frags& 
 // the caller may reuse them (e.g. g_stage0) right away.
 template <int D>
 __device__ __forceinline__ void gemm_nt_tile(f32x16_t (&acc)[4][4], const Panel& A, const Panel& B) {
-  static_assert(NSTAGES == 4, "the unrolled loop below assumes four stages");
+  static_assert(NSTAGES == 4, "the unrolled loops below assume four stages");
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
@@ -352,10 +379,11 @@ __device__ __forceinline__ void gemm_nt_tile(f32x16_t (&acc)[4][4], const Panel&
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   const int nk = (int)((A.kbytes + ROWB - 1) / ROWB);
   const bool ragged = (A.kbytes % ROWB) != 0;
+  const uint32_t wave_lds = (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024u;
   CopyPlan cp;
   copy_plan(cp, A, B, t);
   lds_barrier();  // every wave is done with the buffers of any previous use
-  // stages 0..2 (clamped to the last stage, as in kstage)
+  // stages 0..2 (clamped to the last stage, as in kstage_edge)
   copy_any<0>(cp, A, B, 0, nk, ragged, t);
   copy_any<1>(cp, A, B, min(1, nk - 1), nk, ragged, t);
   copy_any<2>(cp, A, B, min(2, nk - 1), nk, ragged, t);
@@ -366,21 +394,26 @@ __device__ __forceinline__ void gemm_nt_tile(f32x16_t (&acc)[4][4], const Panel&
   frag_base(fb, wm, wn, lane);
   Frags f0, f1;
   frag_read<0>(f0, fb, 0);
-  // Whole rounds of four stages, then the remaining 0..3 stages outside the
-  // loop (a loop header with only two predecessors keeps the waitcnt pass
-  // from falling back to a full wait at the top of every round).
+  // Whole rounds of four plain stages (each copies a stage that is neither
+  // past K nor ragged: kt+3+3 <= last_plain), then rounds of edge stages.
+  // A loop header with only two predecessors keeps the waitcnt pass from
+  // falling back to a full wait at the top of every round.
+  const int last_plain = ragged ? nk - 2 : nk - 1;
   int kt = 0;
-  for (; kt + 4 <= nk; kt += 4) {
-    kstage<D, 0>(acc, f0, f1, cp, fb, A, B, kt, nk, ragged, t);
-    kstage<D, 1>(acc, f0, f1, cp, fb, A, B, kt + 1, nk, ragged, t);
-    kstage<D, 2>(acc, f0, f1, cp, fb, A, B, kt + 2, nk, ragged, t);
-    kstage<D, 3>(acc, f0, f1, cp, fb, A, B, kt + 3, nk, ragged, t);
+  for (; kt + 6 <= last_plain; kt += 4) {
+    kstage_plain<D, 0>(acc, f0, f1, cp, fb, A, B, kt, wave_lds);
+    kstage_plain<D, 1>(acc, f0, f1, cp, fb, A, B, kt + 1, wave_lds);
+    kstage_plain<D, 2>(acc, f0, f1, cp, fb, A, B, kt + 2, wave_lds);
+    kstage_plain<D, 3>(acc, f0, f1, cp, fb, A, B, kt + 3, wave_lds);
   }
-  if (kt < nk) {
-    kstage<D, 0>(acc, f0, f1, cp, fb, A, B, kt, nk, ragged, t);
+  for (; kt < nk; kt += 4) {
+    kstage_edge<D, 0>(acc, f0, f1, cp, fb, A, B, kt, nk, ragged, t);
     if (kt + 1 < nk) {
-      kstage<D, 1>(acc, f0, f1, cp, fb, A, B, kt + 1, nk, ragged, t);
-      if (kt + 2 < nk) kstage<D, 2>(acc, f0, f1, cp, fb, A, B, kt + 2, nk, ragged, t);
+      kstage_edge<D, 1>(acc, f0, f1, cp, fb, A, B, kt + 1, nk, ragged, t);
+      if (kt + 2 < nk) {
+        kstage_edge<D, 2>(acc, f0, f1, cp, fb, A, B, kt + 2, nk, ragged, t);
+        if (kt + 3 < nk) kstage_edge<D, 3>(acc, f0, f1, cp, fb, A, B, kt + 3, nk, ragged, t);
+      }
     }
   }
   wait_vmcnt<0>();
