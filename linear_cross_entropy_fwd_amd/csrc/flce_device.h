@@ -102,10 +102,6 @@ template <int S> __device__ __forceinline__ char* stage_buf() {
   else return g_stage3;
 }
 
-struct Frags {
-  uint4 a[4], b[4];
-};
-
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
@@ -148,252 +144,284 @@ __device__ __forceinline__ void lds_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Per-thread global byte offsets of its 8 copies per stage.  Copy i (0..7):
-// operand i>>2, 16-row block blk = (i&3)*4 + wave; lane L covers row
-// blk*16 + L/4 (clamped to the panel), LDS chunk position L&3, which holds
-// global chunk (L&3) ^ ((row>>2)&3) of that row.
-struct CopyPlan {
-  uint32_t off[8];
+// Keeps the instruction scheduler from moving anything across this point,
+// so that the source order is the issue order.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Wave layout of a workgroup of W waves over the 256 x 256 tile: a GM x GN
+// grid of wave tiles of WI x WJ 32x32 blocks.
+//   W = 4: one wave per SIMD, 128 x 128 per wave (256 accumulator registers).
+//   W = 8: two waves per SIMD, 128 x 64 per wave (128 accumulator registers);
+//          while one wave of a SIMD waits (a copy being issued, a barrier),
+//          the other keeps the MFMA unit busy.
+template <int W> struct Geo;
+template <> struct Geo<4> { static constexpr int WI = 4, WJ = 4; };
+template <> struct Geo<8> { static constexpr int WI = 4, WJ = 2; };
+template <int W> struct Gemm {
+  static constexpr int WI = Geo<W>::WI, WJ = Geo<W>::WJ;
+  static constexpr int GN = TILE / (32 * WJ);   // wave columns
+  static constexpr int NCOP = 2 * TILE / 16 / W;  // 16-row copies per thread per stage
+  static constexpr int NREAD = WI + WJ;         // fragment reads per slab
+  __device__ static int wm(int wave) { return wave / GN; }
+  __device__ static int wn(int wave) { return wave % GN; }
 };
 
-__device__ __forceinline__ void copy_plan(CopyPlan& cp, const Panel& A, const Panel& B, int t) {
+template <int W> struct Frags {
+  uint4 a[Gemm<W>::WI], b[Gemm<W>::WJ];
+};
+
+// Per-thread global byte offsets of its copies.  A stage is 32 copies of 16
+// rows x 64 bytes (1 KB): block b = 0..31 is operand b>>4, rows (b&15)*16 ..
+// +16.  Copy i of wave w is block w + W*i (so copies 0 .. NCOP/2-1 are of
+// operand A, the rest of B).  Lane L covers row (b&15)*16 + L/4 (clamped to
+// the panel) and LDS chunk position L&3, which holds global chunk
+// (L&3) ^ ((row>>2)&3) of that row.
+template <int W> struct CopyPlan {
+  uint32_t off[Gemm<W>::NCOP];
+};
+
+template <int W> __device__ __forceinline__ constexpr int copy_block(int i, int wave) { return wave + W * i; }
+
+template <int W>
+__device__ __forceinline__ void copy_plan(CopyPlan<W>& cp, const Panel& A, const Panel& B, int t) {
   const int wave = t >> 6, L = t & 63;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const Panel& p = i < 4 ? A : B;
-    const int blk = (i & 3) * 4 + wave;
-    int row = blk * 16 + (L >> 2);
+  for (int i = 0; i < Gemm<W>::NCOP; ++i) {
+    const int blk = copy_block<W>(i, wave);
+    const Panel& p = blk < 16 ? A : B;
+    int row = (blk & 15) * 16 + (L >> 2);
     const int c = (L & 3) ^ ((row >> 2) & 3);
     row = row < p.rows ? row : p.rows - 1;
     cp.off[i] = (uint32_t)(row * p.ld) + (uint32_t)(c * 16);
   }
 }
 
-// Copy I (0..7) of stage kc into buffer S.  `masked` (ragged last stage
-// only): a chunk past K is read from the row's last valid 16 bytes instead
-// (the offset stays non-negative, so the address stays inside the row) and
-// zeroed after it lands.  The choice is a select, not a branch.
-template <int S, int I>
-__device__ __forceinline__ void copy_one_any(const CopyPlan& cp, const Panel& A, const Panel& B, int kc,
+// Copy I of stage kc into buffer S.  `masked` (ragged last stage only): a
+// chunk past K is read from the row's last valid 16 bytes instead (the offset
+// stays non-negative, so the address stays inside the row) and zeroed after
+// it lands.  The choice is a select, not a branch.
+template <int W, int S, int I>
+__device__ __forceinline__ void copy_one_any(const CopyPlan<W>& cp, const Panel& A, const Panel& B, int kc,
                                             bool masked, int t) {
   const int wave = t >> 6, L = t & 63;
   const int64_t k0 = (int64_t)kc * ROWB;
-  const Panel& p = I < 4 ? A : B;
-  const int blk = (I & 3) * 4 + wave;
-  const int c = (((blk * 16 + (L >> 2)) >> 2) & 3) ^ (L & 3);
+  constexpr bool OPA = I < Gemm<W>::NCOP / 2;
+  const Panel& p = OPA ? A : B;
+  const int blk = copy_block<W>(I, wave);
+  const int c = ((((blk & 15) * 16 + (L >> 2)) >> 2) & 3) ^ (L & 3);
   const uint32_t off = (masked && k0 + c * 16 >= p.kbytes)
                            ? cp.off[I] - (uint32_t)(c * 16) + (uint32_t)(p.kbytes - 16 - k0)
                            : cp.off[I];
-  const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(stage_buf<S>() + (I >> 2) * OPB + blk * 1024));
+  const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(stage_buf<S>() + blk * 1024));
   lds_copy16(uniform_ptr(p.base + k0), off, dst);
 }
 
-template <int S>
-__device__ __forceinline__ void copy_any(const CopyPlan& cp, const Panel& A, const Panel& B, int kt,
+template <int W, int S, int I = 0>
+__device__ __forceinline__ void copy_any(const CopyPlan<W>& cp, const Panel& A, const Panel& B, int kt,
                                          int nk, bool ragged, int t) {
-  const bool masked = ragged && kt == nk - 1;
-  copy_one_any<S, 0>(cp, A, B, kt, masked, t);
-  copy_one_any<S, 1>(cp, A, B, kt, masked, t);
-  copy_one_any<S, 2>(cp, A, B, kt, masked, t);
-  copy_one_any<S, 3>(cp, A, B, kt, masked, t);
-  copy_one_any<S, 4>(cp, A, B, kt, masked, t);
-  copy_one_any<S, 5>(cp, A, B, kt, masked, t);
-  copy_one_any<S, 6>(cp, A, B, kt, masked, t);
-  copy_one_any<S, 7>(cp, A, B, kt, masked, t);
+  if constexpr (I < Gemm<W>::NCOP) {
+    copy_one_any<W, S, I>(cp, A, B, kt, ragged && kt == nk - 1, t);
+    copy_any<W, S, I + 1>(cp, A, B, kt, nk, ragged, t);
+  }
 }
 
 // Zeroes this thread's LDS chunks of ragged stage kt that lie past K.
-template <int S>
+template <int W, int S>
 __device__ __forceinline__ void zero_tail(const Panel& A, int kt, int t) {
   const int wave = t >> 6, L = t & 63;
   const int64_t k0 = (int64_t)kt * ROWB;
   char* base = stage_buf<S>();
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int blk = (i & 3) * 4 + wave;
-    const int c = (((blk * 16 + (L >> 2)) >> 2) & 3) ^ (L & 3);
-    if (k0 + c * 16 >= A.kbytes)
-      *reinterpret_cast<uint4*>(base + (i >> 2) * OPB + blk * 1024 + L * 16) = make_uint4(0u, 0u, 0u, 0u);
+  for (int i = 0; i < Gemm<W>::NCOP; ++i) {
+    const int blk = copy_block<W>(i, wave);
+    const int c = ((((blk & 15) * 16 + (L >> 2)) >> 2) & 3) ^ (L & 3);
+    if (k0 + c * 16 >= A.kbytes) *reinterpret_cast<uint4*>(base + blk * 1024 + L * 16) = make_uint4(0u, 0u, 0u, 0u);
   }
 }
 
 // Byte offsets, inside a stage buffer, of this lane's fragment chunk for
 // slab 0 and slab 1, for its first A and first B row block.  The lane reads
-// rows wm*128 + 32*i + (l&31): they differ by multiples of 32, so the swizzle
-// term (row>>2)&3 = ((l&31)>>2)&3 is the same for all four blocks, which then
+// rows r0 + 32*i + (l&31): they differ by multiples of 32, so the swizzle
+// term (row>>2)&3 = ((l&31)>>2)&3 is the same for all its blocks, which then
 // sit 32*ROWB bytes apart (an immediate offset).
 struct FragBase {
   uint32_t a[2], b[2];
 };
 
-__device__ __forceinline__ void frag_base(FragBase& fb, int wm, int wn, int lane) {
+template <int W>
+__device__ __forceinline__ void frag_base(FragBase& fb, int wave, int lane) {
   const int r32 = lane & 31, half = lane >> 5, x = (r32 >> 2) & 3;
+  const int ra = Gemm<W>::wm(wave) * 32 * Gemm<W>::WI, rb = Gemm<W>::wn(wave) * 32 * Gemm<W>::WJ;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const uint32_t coff = (uint32_t)(((2 * s + half) ^ x) << 4);
-    fb.a[s] = (uint32_t)((wm * 128 + r32) * ROWB) + coff;
-    fb.b[s] = (uint32_t)(OPB + (wn * 128 + r32) * ROWB) + coff;
+    fb.a[s] = (uint32_t)((ra + r32) * ROWB) + coff;
+    fb.b[s] = (uint32_t)(OPB + (rb + r32) * ROWB) + coff;
   }
 }
 
-// Fragment P (0..3: A row block P, 4..7: B row block P-4) of slab `slab` of
-// buffer S: lane (l&31, l>>5) reads chunk 2*slab + (l>>5) of its row.
-template <int S, int P>
-__device__ __forceinline__ void frag_read_one(Frags& f, const FragBase& fb, int slab) {
+// Fragment P (0..WI-1: A row block P; WI..: B row block P-WI) of slab `slab`
+// of buffer S: lane (l&31, l>>5) reads chunk 2*slab + (l>>5) of its row.
+template <int W, int S, int P>
+__device__ __forceinline__ void frag_read_one(Frags<W>& f, const FragBase& fb, int slab) {
+  constexpr int WI = Gemm<W>::WI;
   const char* base = stage_buf<S>();
-  if constexpr (P < 4)
+  if constexpr (P < WI)
     f.a[P] = *reinterpret_cast<const uint4*>(base + fb.a[slab] + P * 32 * ROWB);
   else
-    f.b[P - 4] = *reinterpret_cast<const uint4*>(base + fb.b[slab] + (P - 4) * 32 * ROWB);
+    f.b[P - WI] = *reinterpret_cast<const uint4*>(base + fb.b[slab] + (P - WI) * 32 * ROWB);
 }
 
-// All eight, in the order slab_phase issues them, so that every path into a
-// stage has the same reads pending.
-template <int S>
-__device__ __forceinline__ void frag_read(Frags& f, const FragBase& fb, int slab) {
-  frag_read_one<S, 0>(f, fb, slab);
-  frag_read_one<S, 4>(f, fb, slab);
-  frag_read_one<S, 5>(f, fb, slab);
-  frag_read_one<S, 6>(f, fb, slab);
-  frag_read_one<S, 7>(f, fb, slab);
-  frag_read_one<S, 1>(f, fb, slab);
-  frag_read_one<S, 2>(f, fb, slab);
-  frag_read_one<S, 3>(f, fb, slab);
+// The order in which a slab's fragments are read: A0, B0 .. B(WJ-1), A1 ..
+// A(WI-1) -- the MFMAs run row block by row block (A0 with every B, then
+// A1, ...), so each fragment is read in the order it is first needed.
+template <int W> __device__ __forceinline__ constexpr int read_order(int k) {
+  constexpr int WI = Gemm<W>::WI, WJ = Gemm<W>::WJ;
+  return k == 0 ? 0 : (k <= WJ ? WI + k - 1 : k - WJ);
 }
 
-// Keeps the instruction scheduler from moving anything across this point,
-// so that the source order below is the issue order.
-__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+// What follows MFMA step s of a slab: read k (0..NREAD-1), copy c (100 + c)
+// or nothing (-1).  W = 4: 16 MFMAs | a read after every even step, a copy
+// after every fourth (1, 5, 9, 13).  W = 8: 8 MFMAs | reads after steps
+// 0 1 3 4 6 7, copies after 2 and 5.
+template <int W> __device__ __forceinline__ constexpr int slab_action(int s) {
+  if constexpr (W == 4) {
+    return (s & 1) == 0 ? s / 2 : ((s & 3) == 1 ? 100 + s / 4 : -1);
+  } else {
+    return s == 2 ? 100 : (s == 5 ? 101 : (s < 2 ? s : (s < 5 ? s - 1 : s - 2)));
+  }
+}
 
 // Copy issuers for slab_phase.  PlainCopy: a stage that lies wholly inside K
 // (no clamp, no mask); everything but the lane's fixed offset cp.off[I] is
 // scalar (the stage's global base and the LDS destination in m0).
-struct PlainCopy {
-  const CopyPlan& cp;
+template <int W> struct PlainCopy {
+  const CopyPlan<W>& cp;
   const char* base;   // operand base + this stage's K offset (wave-uniform)
   uint32_t wave_lds;  // wave * 1024 (wave-uniform)
   template <int S, int I> __device__ __forceinline__ void issue() const {
-    lds_copy16(base, cp.off[I], lds_addr(stage_buf<S>() + (I >> 2) * OPB + (I & 3) * 4096) + wave_lds);
+    lds_copy16(base, cp.off[I], lds_addr(stage_buf<S>() + W * I * 1024) + wave_lds);
   }
 };
 
 // EdgeCopy: a stage at the end of K -- clamped to the last stage and masked
 // when that one is ragged (copy_one_any).
-struct EdgeCopy {
-  const CopyPlan& cp;
+template <int W> struct EdgeCopy {
+  const CopyPlan<W>& cp;
   const Panel& A;
   const Panel& B;
   int kc;
   bool masked;
   int t;
   template <int S, int I> __device__ __forceinline__ void issue() const {
-    copy_one_any<S, I>(cp, A, B, kc, masked, t);
+    copy_one_any<W, S, I>(cp, A, B, kc, masked, t);
   }
 };
 
-// One slab's 16 MFMAs on `fm`, with the eight fragment reads of the next slab
-// (buffer RS, slab `rslab`, into `fr`) and four copies (C0..C0+3 into buffer
-// CS) spread between them: a wave has one SIMD to itself, issues in order,
-// and would otherwise stall its MFMAs behind a burst of copies.
-template <int D, int RS, int CS, int C0, class Copy>
-__device__ __forceinline__ void slab_phase(f32x16_t (&acc)[4][4], const Frags& fm, Frags& fr, const FragBase& fb,
-                                           int rslab, const Copy& cp) {
-  // The MFMAs run row block by row block (A0 with B0..B3, then A1, ...), so
-  // the reads go A0 B0 B1 B2 B3 A1 A2 A3: each lands at least ten MFMAs
-  // before its first use in the next slab.
-#define FLCE_STEP(I, J) mfma_frag<D>(acc[I][J], fm.a[I], fm.b[J])
-  FLCE_STEP(0, 0); frag_read_one<RS, 0>(fr, fb, rslab); sched_fence();
-  FLCE_STEP(0, 1); cp.template issue<CS, C0 + 0>(); sched_fence();
-  FLCE_STEP(0, 2); frag_read_one<RS, 4>(fr, fb, rslab); sched_fence();
-  FLCE_STEP(0, 3); sched_fence();
-  FLCE_STEP(1, 0); frag_read_one<RS, 5>(fr, fb, rslab); sched_fence();
-  FLCE_STEP(1, 1); cp.template issue<CS, C0 + 1>(); sched_fence();
-  FLCE_STEP(1, 2); frag_read_one<RS, 6>(fr, fb, rslab); sched_fence();
-  FLCE_STEP(1, 3); sched_fence();
-  FLCE_STEP(2, 0); frag_read_one<RS, 7>(fr, fb, rslab); sched_fence();
-  FLCE_STEP(2, 1); cp.template issue<CS, C0 + 2>(); sched_fence();
-  FLCE_STEP(2, 2); frag_read_one<RS, 1>(fr, fb, rslab); sched_fence();
-  FLCE_STEP(2, 3); sched_fence();
-  FLCE_STEP(3, 0); frag_read_one<RS, 2>(fr, fb, rslab); sched_fence();
-  FLCE_STEP(3, 1); cp.template issue<CS, C0 + 3>(); sched_fence();
-  FLCE_STEP(3, 2); frag_read_one<RS, 3>(fr, fb, rslab); sched_fence();
-  FLCE_STEP(3, 3); sched_fence();
-#undef FLCE_STEP
+// One slab's WI x WJ MFMAs on `fm`, with the NREAD fragment reads of the next
+// slab (buffer RS, slab `rslab`, into `fr`) and NCOP/2 copies (C0.. into
+// buffer CS) placed between them as slab_action says: a wave issues in order
+// and would otherwise stall its MFMAs behind a burst of copies or reads.
+template <int D, int W, int RS, int CS, int C0, int STEP = 0, class Copy>
+__device__ __forceinline__ void slab_phase(f32x16_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], const Frags<W>& fm,
+                                           Frags<W>& fr, const FragBase& fb, int rslab, const Copy& cp) {
+  constexpr int WJ = Gemm<W>::WJ;
+  if constexpr (STEP < Gemm<W>::WI * WJ) {
+    constexpr int I = STEP / WJ, J = STEP % WJ;
+    mfma_frag<D>(acc[I][J], fm.a[I], fm.b[J]);
+    constexpr int act = slab_action<W>(STEP);
+    if constexpr (act >= 100) cp.template issue<CS, C0 + act - 100>();
+    else if constexpr (act >= 0) frag_read_one<W, RS, read_order<W>(act)>(fr, fb, rslab);
+    sched_fence();
+    slab_phase<D, W, RS, CS, C0, STEP + 1>(acc, fm, fr, fb, rslab, cp);
+  }
+}
+
+// All NREAD fragments of a slab, in read_order (so that every path into a
+// stage has the same reads pending).
+template <int W, int S, int K = 0>
+__device__ __forceinline__ void frag_read(Frags<W>& f, const FragBase& fb, int slab) {
+  if constexpr (K < Gemm<W>::NREAD) {
+    frag_read_one<W, S, read_order<W>(K)>(f, fb, slab);
+    frag_read<W, S, K + 1>(f, fb, slab);
+  }
 }
 
 // Stage kt from buffer S (f0 holds its slab 0).  Every stage copies stage
 // kt+3 into buffer (S+3)%4 (that buffer was last read in stage kt-1, before
 // that stage's barrier):
-//   phase A: slab-0 MFMAs | slab-1 reads of buffer S | copies 0..3 (operand A)
+//   phase A: slab-0 MFMAs | slab-1 reads of buffer S | operand-A copies
 //   wait for stage kt+1's copies, zero its ragged tail, barrier
-//   phase B: slab-1 MFMAs | slab-0 reads of buffer S+1 | copies 4..7 (operand B)
-// Copies issued after stage kt+1's when the wait runs: stage kt+2's eight and
-// stage kt+3's first four.
-//
+//   phase B: slab-1 MFMAs | slab-0 reads of buffer S+1 | operand-B copies
+// Copies issued after stage kt+1's when the wait runs: stage kt+2's NCOP and
+// stage kt+3's first NCOP/2.
+template <int W> constexpr int kStageWait = Gemm<W>::NCOP + Gemm<W>::NCOP / 2;
+
 // kstage_plain: stage kt+3 lies wholly inside K.
-template <int D, int S>
-__device__ __forceinline__ void kstage_plain(f32x16_t (&acc)[4][4], Frags& f0, Frags& f1, const CopyPlan& cp,
-                                             const FragBase& fb, const Panel& A, const Panel& B, int kt,
-                                             uint32_t wave_lds) {
-  constexpr int SN = (S + 1) % NSTAGES, SC = (S + NSTAGES - 1) % NSTAGES;
+template <int D, int W, int S>
+__device__ __forceinline__ void kstage_plain(f32x16_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], Frags<W>& f0,
+                                             Frags<W>& f1, const CopyPlan<W>& cp, const FragBase& fb,
+                                             const Panel& A, const Panel& B, int kt, uint32_t wave_lds) {
+  constexpr int SN = (S + 1) % NSTAGES, SC = (S + NSTAGES - 1) % NSTAGES, H = Gemm<W>::NCOP / 2;
   const int64_t k0 = (int64_t)(kt + NSTAGES - 1) * ROWB;
-  const PlainCopy ca{cp, uniform_ptr(A.base + k0), wave_lds};
-  const PlainCopy cb{cp, uniform_ptr(B.base + k0), wave_lds};
+  const PlainCopy<W> ca{cp, uniform_ptr(A.base + k0), wave_lds};
+  const PlainCopy<W> cb{cp, uniform_ptr(B.base + k0), wave_lds};
   sched_fence();
-  slab_phase<D, S, SC, 0>(acc, f0, f1, fb, 1, ca);
-  wait_vmcnt<12>();
+  slab_phase<D, W, S, SC, 0>(acc, f0, f1, fb, 1, ca);
+  wait_vmcnt<kStageWait<W>>();
   lds_barrier();
-  slab_phase<D, SN, SC, 4>(acc, f1, f0, fb, 0, cb);
+  slab_phase<D, W, SN, SC, H>(acc, f1, f0, fb, 0, cb);
 }
 
 // kstage_edge: any stage; past the end of K the copy re-reads the last stage
 // (never used), so the schedule still has no branches.
-template <int D, int S>
-__device__ __forceinline__ void kstage_edge(f32x16_t (&acc)[4][4], Frags& f0, Frags& f1, const CopyPlan& cp,
-                                            const FragBase& fb, const Panel& A, const Panel& B, int kt,
-                                            int nk, bool ragged, int t) {
-  constexpr int SN = (S + 1) % NSTAGES, SC = (S + NSTAGES - 1) % NSTAGES;
+template <int D, int W, int S>
+__device__ __forceinline__ void kstage_edge(f32x16_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], Frags<W>& f0,
+                                            Frags<W>& f1, const CopyPlan<W>& cp, const FragBase& fb,
+                                            const Panel& A, const Panel& B, int kt, int nk, bool ragged,
+                                            int t) {
+  constexpr int SN = (S + 1) % NSTAGES, SC = (S + NSTAGES - 1) % NSTAGES, H = Gemm<W>::NCOP / 2;
   const int kc = min(kt + NSTAGES - 1, nk - 1);
-  const EdgeCopy c{cp, A, B, kc, ragged && kc == nk - 1, t};
+  const EdgeCopy<W> c{cp, A, B, kc, ragged && kc == nk - 1, t};
   sched_fence();
-  slab_phase<D, S, SC, 0>(acc, f0, f1, fb, 1, c);
-  wait_vmcnt<12>();
-  if (ragged && kt + 1 == nk - 1) zero_tail<SN>(A, kt + 1, t);
+  slab_phase<D, W, S, SC, 0>(acc, f0, f1, fb, 1, c);
+  wait_vmcnt<kStageWait<W>>();
+  if (ragged && kt + 1 == nk - 1) zero_tail<W, SN>(A, kt + 1, t);
   lds_barrier();
-  slab_phase<D, SN, SC, 4>(acc, f1, f0, fb, 0, c);
+  slab_phase<D, W, SN, SC, H>(acc, f1, f0, fb, 0, c);
 }
 
-// acc[i][j] (this wave's 4x4 blocks) = A_panel . B_panel^T over all of K.
+// acc[i][j] (this wave's WI x WJ blocks) = A_panel . B_panel^T over all of K.
 // Uses the stage buffers; returns after a barrier with no copy in flight, so
 // the caller may reuse them (e.g. g_stage0) right away.
-template <int D>
-__device__ __forceinline__ void gemm_nt_tile(f32x16_t (&acc)[4][4], const Panel& A, const Panel& B) {
+template <int D, int W>
+__device__ __forceinline__ void gemm_nt_tile(f32x16_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], const Panel& A,
+                                             const Panel& B) {
   static_assert(NSTAGES == 4, "the unrolled loops below assume four stages");
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < Gemm<W>::WI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < Gemm<W>::WJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   const int nk = (int)((A.kbytes + ROWB - 1) / ROWB);
   const bool ragged = (A.kbytes % ROWB) != 0;
   const uint32_t wave_lds = (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024u;
-  CopyPlan cp;
-  copy_plan(cp, A, B, t);
+  CopyPlan<W> cp;
+  copy_plan<W>(cp, A, B, t);
   lds_barrier();  // every wave is done with the buffers of any previous use
   // stages 0..2 (clamped to the last stage, as in kstage_edge)
-  copy_any<0>(cp, A, B, 0, nk, ragged, t);
-  copy_any<1>(cp, A, B, min(1, nk - 1), nk, ragged, t);
-  copy_any<2>(cp, A, B, min(2, nk - 1), nk, ragged, t);
-  wait_vmcnt<16>();
-  if (ragged && nk == 1) zero_tail<0>(A, 0, t);
+  copy_any<W, 0>(cp, A, B, 0, nk, ragged, t);
+  copy_any<W, 1>(cp, A, B, min(1, nk - 1), nk, ragged, t);
+  copy_any<W, 2>(cp, A, B, min(2, nk - 1), nk, ragged, t);
+  wait_vmcnt<2 * Gemm<W>::NCOP>();
+  if (ragged && nk == 1) zero_tail<W, 0>(A, 0, t);
   lds_barrier();
   FragBase fb;
-  frag_base(fb, wm, wn, lane);
-  Frags f0, f1;
-  frag_read<0>(f0, fb, 0);
+  frag_base<W>(fb, wave, lane);
+  Frags<W> f0, f1;
+  frag_read<W, 0>(f0, fb, 0);
   // Whole rounds of four plain stages (each copies a stage that is neither
   // past K nor ragged: kt+3+3 <= last_plain), then rounds of edge stages.
   // A loop header with only two predecessors keeps the waitcnt pass from
@@ -401,18 +429,18 @@ __device__ __forceinline__ void gemm_nt_tile(f32x16_t (&acc)[4][4], const Panel&
   const int last_plain = ragged ? nk - 2 : nk - 1;
   int kt = 0;
   for (; kt + 6 <= last_plain; kt += 4) {
-    kstage_plain<D, 0>(acc, f0, f1, cp, fb, A, B, kt, wave_lds);
-    kstage_plain<D, 1>(acc, f0, f1, cp, fb, A, B, kt + 1, wave_lds);
-    kstage_plain<D, 2>(acc, f0, f1, cp, fb, A, B, kt + 2, wave_lds);
-    kstage_plain<D, 3>(acc, f0, f1, cp, fb, A, B, kt + 3, wave_lds);
+    kstage_plain<D, W, 0>(acc, f0, f1, cp, fb, A, B, kt, wave_lds);
+    kstage_plain<D, W, 1>(acc, f0, f1, cp, fb, A, B, kt + 1, wave_lds);
+    kstage_plain<D, W, 2>(acc, f0, f1, cp, fb, A, B, kt + 2, wave_lds);
+    kstage_plain<D, W, 3>(acc, f0, f1, cp, fb, A, B, kt + 3, wave_lds);
   }
   for (; kt < nk; kt += 4) {
-    kstage_edge<D, 0>(acc, f0, f1, cp, fb, A, B, kt, nk, ragged, t);
+    kstage_edge<D, W, 0>(acc, f0, f1, cp, fb, A, B, kt, nk, ragged, t);
     if (kt + 1 < nk) {
-      kstage_edge<D, 1>(acc, f0, f1, cp, fb, A, B, kt + 1, nk, ragged, t);
+      kstage_edge<D, W, 1>(acc, f0, f1, cp, fb, A, B, kt + 1, nk, ragged, t);
       if (kt + 2 < nk) {
-        kstage_edge<D, 2>(acc, f0, f1, cp, fb, A, B, kt + 2, nk, ragged, t);
-        if (kt + 3 < nk) kstage_edge<D, 3>(acc, f0, f1, cp, fb, A, B, kt + 3, nk, ragged, t);
+        kstage_edge<D, W, 2>(acc, f0, f1, cp, fb, A, B, kt + 2, nk, ragged, t);
+        if (kt + 3 < nk) kstage_edge<D, W, 3>(acc, f0, f1, cp, fb, A, B, kt + 3, nk, ragged, t);
       }
     }
   }

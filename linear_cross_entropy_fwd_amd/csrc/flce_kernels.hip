@@ -137,7 +137,7 @@ __global__ __launch_bounds__(NTHREADS) void fwd_tiles_kernel(FwdArgs a) {
   for (int vt = vt_begin; vt < vt_end; ++vt) {
     const int64_t v0 = (int64_t)vt * TILE;
     Panel A{a.weight + v0 * rowb, rowb, (int)min<int64_t>(TILE, a.V - v0), rowb};
-    gemm_nt_tile<D>(acc, A, B);
+    gemm_nt_tile<D, 4>(acc, A, B);
 
     const int to = opaque_int(t);
     const int half = (to >> 5) & 1;
@@ -436,7 +436,7 @@ __global__ __launch_bounds__(NTHREADS) void bwd_g_kernel(GArgs a) {
   Panel A{a.weight + v0 * rowb, rowb, (int)min<int64_t>(TILE, a.V - v0), rowb};
   Panel B{a.hidden + n0 * rowb, rowb, (int)min<int64_t>(TILE, a.N - n0), rowb};
   f32x16_t acc[4][4];
-  gemm_nt_tile<D>(acc, A, B);
+  gemm_nt_tile<D, 4>(acc, A, B);
 
   float lse[4], coef[4];
   int tgt[4];
@@ -554,31 +554,34 @@ __global__ __launch_bounds__(NTHREADS) void bwd_g_kernel(GArgs a) {
 
 // ------------------------------------------------------------------ backward contractions
 
-template <int D>
-__global__ __launch_bounds__(NTHREADS) void bwd_dh_kernel(DhArgs a) {
+// Waves per workgroup of the two plain contractions (see Gemm<W>).
+constexpr int kContractWaves = 8;
+
+template <int D, int W>
+__global__ __launch_bounds__(W * 64) void bwd_dh_kernel(DhArgs a) {
   typedef typename Elem<D>::T T;
-  constexpr int EB = Elem<D>::bytes;
+  constexpr int EB = Elem<D>::bytes, WI = Gemm<W>::WI, WJ = Gemm<W>::WJ;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = wave >> 1, wn = wave & 1, r32 = lane & 31, half = lane >> 5;
+  const int wm = Gemm<W>::wm(wave), wn = Gemm<W>::wn(wave), r32 = lane & 31, half = lane >> 5;
   const int L = xcd_logical_id(blockIdx.x, gridDim.x);
   const int tt = L % a.n_tok_tiles, ht = L / a.n_tok_tiles;
   const int64_t n0 = (int64_t)tt * TILE, h0 = (int64_t)ht * TILE;
   const int64_t kb = (int64_t)a.cvpad * EB;
   Panel A{a.G + n0 * kb, kb, (int)min<int64_t>(TILE, a.N - n0), kb};
   Panel B{a.WcT + h0 * kb, kb, (int)min<int64_t>(TILE, a.H - h0), kb};
-  f32x16_t acc[4][4];
-  gemm_nt_tile<D>(acc, A, B);
+  f32x16_t acc[WI][WJ];
+  gemm_nt_tile<D, W>(acc, A, B);
   const float scale = a.scale[0];
   T* out = reinterpret_cast<T*>(a.out);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < WI; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int64_t n = n0 + wm * 128 + 32 * i + acc_row(r, half);
+      const int64_t n = n0 + wm * 32 * WI + 32 * i + acc_row(r, half);
       if (n >= a.N) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t h = h0 + wn * 128 + 32 * j + r32;
+      for (int j = 0; j < WJ; ++j) {
+        const int64_t h = h0 + wn * 32 * WJ + 32 * j + r32;
         if (h >= a.H) continue;
         const int64_t idx = n * a.H + h;
         const float val = acc[i][j][r] * scale;
@@ -590,31 +593,31 @@ __global__ __launch_bounds__(NTHREADS) void bwd_dh_kernel(DhArgs a) {
     }
 }
 
-template <int D>
-__global__ __launch_bounds__(NTHREADS) void bwd_dw_kernel(DwArgs a) {
+template <int D, int W>
+__global__ __launch_bounds__(W * 64) void bwd_dw_kernel(DwArgs a) {
   typedef typename Elem<D>::T T;
-  constexpr int EB = Elem<D>::bytes;
+  constexpr int EB = Elem<D>::bytes, WI = Gemm<W>::WI, WJ = Gemm<W>::WJ;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = wave >> 1, wn = wave & 1, r32 = lane & 31, half = lane >> 5;
+  const int wm = Gemm<W>::wm(wave), wn = Gemm<W>::wn(wave), r32 = lane & 31, half = lane >> 5;
   const int L = xcd_logical_id(blockIdx.x, gridDim.x);
   const int ht = L % a.n_h_tiles, vt = L / a.n_h_tiles;
   const int64_t v0 = (int64_t)vt * TILE, h0 = (int64_t)ht * TILE;
   const int64_t kb = (int64_t)a.npad * EB;
   Panel A{a.GT + v0 * kb, kb, (int)min<int64_t>(TILE, a.cv - v0), kb};
   Panel B{a.HT + h0 * kb, kb, (int)min<int64_t>(TILE, a.H - h0), kb};
-  f32x16_t acc[4][4];
-  gemm_nt_tile<D>(acc, A, B);
+  f32x16_t acc[WI][WJ];
+  gemm_nt_tile<D, W>(acc, A, B);
   const float scale = a.scale[0];
   T* out = reinterpret_cast<T*>(a.out);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < WI; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int64_t v = v0 + wm * 128 + 32 * i + acc_row(r, half);
+      const int64_t v = v0 + wm * 32 * WI + 32 * i + acc_row(r, half);
       if (v >= a.cv) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t h = h0 + wn * 128 + 32 * j + r32;
+      for (int j = 0; j < WJ; ++j) {
+        const int64_t h = h0 + wn * 32 * WJ + 32 * j + r32;
         if (h < a.H) out[v * a.H + h] = from_f32<D>(acc[i][j][r] * scale);
       }
     }
@@ -704,22 +707,22 @@ hipError_t launch_backward_g(int dtype, bool bias, bool cap, const GArgs& a, hip
 }
 
 hipError_t launch_backward_dh(int dtype, const DhArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)(a.n_tok_tiles * a.n_h_tiles)), block(NTHREADS);
+  const dim3 grid((unsigned)(a.n_tok_tiles * a.n_h_tiles)), block(kContractWaves * 64);
   switch (dtype) {
-    case DT_F32: hipLaunchKernelGGL(bwd_dh_kernel<DT_F32>, grid, block, 0, st, a); break;
-    case DT_F16: hipLaunchKernelGGL(bwd_dh_kernel<DT_F16>, grid, block, 0, st, a); break;
-    case DT_BF16: hipLaunchKernelGGL(bwd_dh_kernel<DT_BF16>, grid, block, 0, st, a); break;
+    case DT_F32: hipLaunchKernelGGL((bwd_dh_kernel<DT_F32, kContractWaves>), grid, block, 0, st, a); break;
+    case DT_F16: hipLaunchKernelGGL((bwd_dh_kernel<DT_F16, kContractWaves>), grid, block, 0, st, a); break;
+    case DT_BF16: hipLaunchKernelGGL((bwd_dh_kernel<DT_BF16, kContractWaves>), grid, block, 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_backward_dw(int dtype, const DwArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)(a.n_voc_tiles * a.n_h_tiles)), block(NTHREADS);
+  const dim3 grid((unsigned)(a.n_voc_tiles * a.n_h_tiles)), block(kContractWaves * 64);
   switch (dtype) {
-    case DT_F32: hipLaunchKernelGGL(bwd_dw_kernel<DT_F32>, grid, block, 0, st, a); break;
-    case DT_F16: hipLaunchKernelGGL(bwd_dw_kernel<DT_F16>, grid, block, 0, st, a); break;
-    case DT_BF16: hipLaunchKernelGGL(bwd_dw_kernel<DT_BF16>, grid, block, 0, st, a); break;
+    case DT_F32: hipLaunchKernelGGL((bwd_dw_kernel<DT_F32, kContractWaves>), grid, block, 0, st, a); break;
+    case DT_F16: hipLaunchKernelGGL((bwd_dw_kernel<DT_F16, kContractWaves>), grid, block, 0, st, a); break;
+    case DT_BF16: hipLaunchKernelGGL((bwd_dw_kernel<DT_BF16, kContractWaves>), grid, block, 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
