@@ -131,7 +131,7 @@ BwdLayout bwd_layout(const flce_problem_t& p) {
   L.off_g = take((size_t)L.npad * L.cvpad_max * eb);
   L.off_gt = take((size_t)L.cvpad_max * L.npad * eb);
   L.off_dh = take(L.n_chunks > 1 ? (size_t)N * H * 4 : 0);
-  L.off_db = take(p.has_bias ? (size_t)2 * L.n_tok_tiles * V * 4 : 0);
+  L.off_db = take(p.has_bias ? (size_t)flce::kBiasParts * L.n_tok_tiles * V * 4 : 0);
   L.total = off;
   return L;
 }
@@ -354,7 +354,7 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
     }
   }
   if (want_db) {
-    flce::DbArgs ba{db, reinterpret_cast<char*>(grad_bias), scale, V, 2 * L.n_tok_tiles};
+    flce::DbArgs ba{db, reinterpret_cast<char*>(grad_bias), scale, V, flce::kBiasParts * L.n_tok_tiles};
     if ((e = flce::launch_backward_db(p->dtype, ba, st)) != hipSuccess) return hip_fail(e, "grad_bias kernel");
   }
   return FLCE_OK;

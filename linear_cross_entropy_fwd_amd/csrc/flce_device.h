@@ -3,9 +3,8 @@
 // K-contiguous) that the forward logit pass, the backward recompute pass and
 // the two gradient contractions share.
 //
-// Tile geometry: a workgroup of 256 threads (4 wave64s, one per SIMD) owns a
-// 256 x 256 fp32 output tile; wave w covers rows [128*(w>>1), +128) and
-// columns [128*(w&1), +128) as 4 x 4 blocks of the 32x32 MFMA; operands
+// Tile geometry: a workgroup owns a 256 x 256 fp32 output tile, split over
+// its 4 or 8 wave64s as blocks of the 32x32 MFMA (Gemm<W> below); operands
 // stream through a four-stage LDS ring fed by direct global-to-LDS copies
 // (see gemm_nt_tile below).
 #pragma once
@@ -32,7 +31,6 @@ template <int D> __device__ __forceinline__ typename Elem<D>::T from_f32(float x
 }
 
 constexpr int TILE = 256;          // output tile edge (rows and columns)
-constexpr int NTHREADS = 256;      // 4 waves
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;

@@ -76,13 +76,13 @@ __device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2)
   }
 }
 
-template <int D, bool BIAS>
-__device__ __forceinline__ void load_bias_rows(float (&bv)[4][16], const char* bias, int vbase,
+template <int D, bool BIAS, int WI>
+__device__ __forceinline__ void load_bias_rows(float (&bv)[WI][16], const char* bias, int vbase,
                                                int64_t V, int half) {
   typedef typename Elem<D>::T T;
   const T* b = reinterpret_cast<const T*>(bias);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < WI; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       if (BIAS) {
@@ -97,13 +97,15 @@ __device__ __forceinline__ void load_bias_rows(float (&bv)[4][16], const char* b
 
 // ------------------------------------------------------------------ forward tiles
 
-__shared__ float g_fwd_state[7 * 4 * NTHREADS];  // 28 KB next to the 128 KB stage ring
+// 28 KB next to the 128 KB stage ring: 7 values x WJ token columns per thread.
+__shared__ float g_fwd_state[7 * 4 * 256];
 
-template <int D, bool METRICS, bool BIAS, bool CAP>
-__global__ __launch_bounds__(NTHREADS) void fwd_tiles_kernel(FwdArgs a) {
-  constexpr int EB = Elem<D>::bytes;
+template <int D, bool METRICS, bool BIAS, bool CAP, int W>
+__global__ __launch_bounds__(W * 64) void fwd_tiles_kernel(FwdArgs a) {
+  constexpr int EB = Elem<D>::bytes, WI = Gemm<W>::WI, WJ = Gemm<W>::WJ, NT = W * 64;
+  static_assert(7 * WJ * NT <= 7 * 4 * 256, "online state does not fit g_fwd_state");
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = wave >> 1, wn = wave & 1, r32 = lane & 31, half = lane >> 5;
+  const int wm = Gemm<W>::wm(wave), wn = Gemm<W>::wn(wave), r32 = lane & 31, half = lane >> 5;
 
   const int L = xcd_logical_id(blockIdx.x, gridDim.x);
   const int tt = L % a.n_tok_tiles, split = L / a.n_tok_tiles;
@@ -119,10 +121,10 @@ __global__ __launch_bounds__(NTHREADS) void fwd_tiles_kernel(FwdArgs a) {
   // token column j: 0 m, 1 S, 2 U, 3 z_target, 4 argmax value, 5 argmax id,
   // 6 target id (-1 when the row is ignored or its target is out of range).
   float* st = g_fwd_state + t;
-#define FST(k, j) st[((k) * 4 + (j)) * NTHREADS]
+#define FST(k, j) st[((k) * WJ + (j)) * NT]
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t n = n0 + wn * 128 + 32 * j + r32;
+  for (int j = 0; j < WJ; ++j) {
+    const int64_t n = n0 + wn * 32 * WJ + 32 * j + r32;
     const int64_t tv = n < a.N ? a.targets[n] : a.ignore_index;
     FST(0, j) = -INFINITY;
     FST(1, j) = 0.f;
@@ -133,25 +135,25 @@ __global__ __launch_bounds__(NTHREADS) void fwd_tiles_kernel(FwdArgs a) {
     FST(6, j) = __int_as_float((tv != a.ignore_index && tv >= 0 && tv < a.V) ? (int)tv : -1);
   }
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[WI][WJ];
   for (int vt = vt_begin; vt < vt_end; ++vt) {
     const int64_t v0 = (int64_t)vt * TILE;
     Panel A{a.weight + v0 * rowb, rowb, (int)min<int64_t>(TILE, a.V - v0), rowb};
-    gemm_nt_tile<D, 4>(acc, A, B);
+    gemm_nt_tile<D, W>(acc, A, B);
 
     const int to = opaque_int(t);
     const int half = (to >> 5) & 1;
-    const int vbase = (int)v0 + (to >> 7) * 128;
+    const int vbase = (int)v0 + Gemm<W>::wm(to >> 6) * 32 * WI;
     const bool ragged = v0 + TILE > a.V;
-    float bv[4][16];
-    load_bias_rows<D, BIAS>(bv, a.bias, vbase, a.V, half);
+    float bv[WI][16];
+    load_bias_rows<D, BIAS, WI>(bv, a.bias, vbase, a.V, half);
 
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float z[4][16];
+    for (int j = 0; j < WJ; ++j) {
+      float z[WI][16];
       float zmax = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < WI; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float y = acc[i][j][r];
@@ -167,7 +169,7 @@ __global__ __launch_bounds__(NTHREADS) void fwd_tiles_kernel(FwdArgs a) {
       if (mnew != -INFINITY) {
         float sum = 0.f, usum = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < WI; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const float d = z[i][r] - mnew;
@@ -190,7 +192,7 @@ __global__ __launch_bounds__(NTHREADS) void fwd_tiles_kernel(FwdArgs a) {
       if (METRICS && zmax > FST(4, j)) {
         int idx = 0x7fffffff;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < WI; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int v = vbase + 32 * i + acc_row(r, half);
@@ -200,11 +202,11 @@ __global__ __launch_bounds__(NTHREADS) void fwd_tiles_kernel(FwdArgs a) {
         FST(5, j) = __int_as_float(idx);
       }
       const int local = __float_as_int(FST(6, j)) - vbase;
-      if (local >= 0 && local < 128 && ((local >> 2) & 1) == half) {
+      if (local >= 0 && local < 32 * WI && ((local >> 2) & 1) == half) {
         const int ti = local >> 5, tr = ((local & 31) >> 3) * 4 + (local & 3);
         float zv = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < WI; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             if (i == ti && r == tr) zv = z[i][r];
@@ -213,10 +215,10 @@ __global__ __launch_bounds__(NTHREADS) void fwd_tiles_kernel(FwdArgs a) {
     }
   }
 
-  float m[4], S[4], U[4], zt[4], av[4];
-  int ai[4];
+  float m[WJ], S[WJ], U[WJ], zt[WJ], av[WJ];
+  int ai[WJ];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < WJ; ++j) {
     m[j] = FST(0, j);
     S[j] = FST(1, j);
     U[j] = FST(2, j);
@@ -228,7 +230,7 @@ __global__ __launch_bounds__(NTHREADS) void fwd_tiles_kernel(FwdArgs a) {
 
   // Lanes l and l^32 hold the same token columns over disjoint vocab rows.
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < WJ; ++j) {
     const float m2 = __shfl_xor(m[j], 32), S2 = __shfl_xor(S[j], 32);
     const float U2 = __shfl_xor(U[j], 32), z2 = __shfl_xor(zt[j], 32);
     const float av2 = __shfl_xor(av[j], 32);
@@ -240,10 +242,11 @@ __global__ __launch_bounds__(NTHREADS) void fwd_tiles_kernel(FwdArgs a) {
 
   // Waves wm=0 and wm=1 hold the same tokens over disjoint vocab rows.
   float* xs = reinterpret_cast<float*>(g_stage0);  // free after gemm_nt_tile returns
+  static_assert(TILE / (32 * WI) == 2, "two wave rows share each token column");
   if (wm == 1 && half == 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tok = wn * 128 + 32 * j + r32;
+    for (int j = 0; j < WJ; ++j) {
+      const int tok = wn * 32 * WJ + 32 * j + r32;
       xs[0 * TILE + tok] = m[j];
       xs[1 * TILE + tok] = S[j];
       xs[2 * TILE + tok] = U[j];
@@ -255,8 +258,8 @@ __global__ __launch_bounds__(NTHREADS) void fwd_tiles_kernel(FwdArgs a) {
   __syncthreads();
   if (wm == 0 && half == 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tok = wn * 128 + 32 * j + r32;
+    for (int j = 0; j < WJ; ++j) {
+      const int tok = wn * 32 * WJ + 32 * j + r32;
       lse_merge<METRICS>(m[j], S[j], U[j], xs[0 * TILE + tok], xs[1 * TILE + tok], xs[2 * TILE + tok]);
       zt[j] = zt[j] + xs[3 * TILE + tok];
       if (METRICS) argmax_merge(av[j], ai[j], xs[4 * TILE + tok], __float_as_int(xs[5 * TILE + tok]));
@@ -419,12 +422,13 @@ __global__ void fill_zero_kernel(uint8_t* p, int64_t bytes) {
 
 // ------------------------------------------------------------------ backward G (recompute)
 
-template <int D, bool BIAS, bool CAP>
-__global__ __launch_bounds__(NTHREADS) void bwd_g_kernel(GArgs a) {
+template <int D, bool BIAS, bool CAP, int W>
+__global__ __launch_bounds__(W * 64) void bwd_g_kernel(GArgs a) {
   typedef typename Elem<D>::T T;
-  constexpr int EB = Elem<D>::bytes;
+  constexpr int EB = Elem<D>::bytes, WI = Gemm<W>::WI, WJ = Gemm<W>::WJ;
+  static_assert(Gemm<W>::GN == kBiasParts || W != kRecomputeWaves, "grad_bias partials per token tile");
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = wave >> 1, wn = wave & 1, r32 = lane & 31, half = lane >> 5;
+  const int wm = Gemm<W>::wm(wave), wn = Gemm<W>::wn(wave), r32 = lane & 31, half = lane >> 5;
 
   const int L = xcd_logical_id(blockIdx.x, gridDim.x);
   const int tt = L % a.n_tok_tiles, vt = L / a.n_tok_tiles;
@@ -435,15 +439,15 @@ __global__ __launch_bounds__(NTHREADS) void bwd_g_kernel(GArgs a) {
 
   Panel A{a.weight + v0 * rowb, rowb, (int)min<int64_t>(TILE, a.V - v0), rowb};
   Panel B{a.hidden + n0 * rowb, rowb, (int)min<int64_t>(TILE, a.N - n0), rowb};
-  f32x16_t acc[4][4];
-  gemm_nt_tile<D, 4>(acc, A, B);
+  f32x16_t acc[WI][WJ];
+  gemm_nt_tile<D, W>(acc, A, B);
 
-  float lse[4], coef[4];
-  int tgt[4];
-  bool live[4];
+  float lse[WJ], coef[WJ];
+  int tgt[WJ];
+  bool live[WJ];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t n = n0 + wn * 128 + 32 * j + r32;
+  for (int j = 0; j < WJ; ++j) {
+    const int64_t n = n0 + wn * 32 * WJ + 32 * j + r32;
     live[j] = false;
     tgt[j] = -1;
     lse[j] = 0.f;
@@ -463,18 +467,18 @@ __global__ __launch_bounds__(NTHREADS) void bwd_g_kernel(GArgs a) {
     }
   }
 
-  const int vbase = (int)v0 + wm * 128;
-  float bv[4][16];
-  load_bias_rows<D, BIAS>(bv, a.bias, vbase, a.V, half);
+  const int vbase = (int)v0 + wm * 32 * WI;
+  float bv[WI][16];
+  load_bias_rows<D, BIAS, WI>(bv, a.bias, vbase, a.V, half);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < WI; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int v = vbase + 32 * i + acc_row(r, half);
       const int vl = v - (int)a.c0;
       const bool vin = v < a.V && vl < a.cv;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < WJ; ++j) {
         float y = acc[i][j][r];
         if (BIAS) y = y + bv[i][r];
         y = a.s * y;
@@ -494,14 +498,14 @@ __global__ __launch_bounds__(NTHREADS) void bwd_g_kernel(GArgs a) {
   if (a.G) {
     T* G = reinterpret_cast<T*>(a.G);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t n = n0 + wn * 128 + 32 * j + r32;
+    for (int j = 0; j < WJ; ++j) {
+      const int64_t n = n0 + wn * 32 * WJ + 32 * j + r32;
       if (n >= a.npad) continue;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < WI; ++i)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const int vl = vl0 + wm * 128 + 32 * i + 8 * g4 + 4 * half;
+          const int vl = vl0 + wm * 32 * WI + 32 * i + 8 * g4 + 4 * half;
           if (vl >= a.cvpad) continue;
           T* dst = G + n * a.cvpad + vl;
           if constexpr (EB == 2) {
@@ -521,25 +525,27 @@ __global__ __launch_bounds__(NTHREADS) void bwd_g_kernel(GArgs a) {
   if (a.GT) {
     T* GT = reinterpret_cast<T*>(a.GT);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < WI; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int vl = vl0 + wm * 128 + 32 * i + acc_row(r, half);
+        const int vl = vl0 + wm * 32 * WI + 32 * i + acc_row(r, half);
         if (vl >= a.cvpad) continue;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t n = n0 + wn * 128 + 32 * j + r32;
+        for (int j = 0; j < WJ; ++j) {
+          const int64_t n = n0 + wn * 32 * WJ + 32 * j + r32;
           if (n < a.npad) GT[(int64_t)vl * a.npad + n] = from_f32<D>(acc[i][j][r]);
         }
       }
   }
-  // grad_bias partials: sum over this wave's 128 tokens, per vocabulary id.
+  // grad_bias partials: sum over this wave's 32*WJ tokens, per vocabulary id.
   if (a.dbpart) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < WI; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float s = (acc[i][0][r] + acc[i][1][r]) + (acc[i][2][r] + acc[i][3][r]);
+        float s = acc[i][0][r];
+#pragma unroll
+        for (int j = 1; j < WJ; ++j) s = s + acc[i][j][r];
         s += __shfl_xor(s, 1);
         s += __shfl_xor(s, 2);
         s += __shfl_xor(s, 4);
@@ -547,15 +553,12 @@ __global__ __launch_bounds__(NTHREADS) void bwd_g_kernel(GArgs a) {
         s += __shfl_xor(s, 16);
         const int v = vbase + 32 * i + acc_row(r, half);
         const int vl = v - (int)a.c0;
-        if (r32 == 0 && v < a.V && vl < a.cv) a.dbpart[(int64_t)(2 * tt + wn) * a.V + v] = s;
+        if (r32 == 0 && v < a.V && vl < a.cv) a.dbpart[(int64_t)(Gemm<W>::GN * tt + wn) * a.V + v] = s;
       }
   }
 }
 
 // ------------------------------------------------------------------ backward contractions
-
-// Waves per workgroup of the two plain contractions (see Gemm<W>).
-constexpr int kContractWaves = 8;
 
 template <int D, int W>
 __global__ __launch_bounds__(W * 64) void bwd_dh_kernel(DhArgs a) {
@@ -639,10 +642,10 @@ static inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + p
 
 template <int D>
 static hipError_t fwd_tiles_dispatch(bool metrics, bool bias, bool cap, const FwdArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)(a.n_tok_tiles * a.n_splits)), block(NTHREADS);
-#define FLCE_FWD(M, B, C)                                                         \
-  if (metrics == M && bias == B && cap == C) {                                    \
-    hipLaunchKernelGGL((fwd_tiles_kernel<D, M, B, C>), grid, block, 0, st, a);    \
+  const dim3 grid((unsigned)(a.n_tok_tiles * a.n_splits)), block(kFwdWaves * 64);
+#define FLCE_FWD(M, B, C)                                                                \
+  if (metrics == M && bias == B && cap == C) {                                           \
+    hipLaunchKernelGGL((fwd_tiles_kernel<D, M, B, C, kFwdWaves>), grid, block, 0, st, a); \
     return hipGetLastError();                                                     \
   }
   FLCE_FWD(false, false, false) FLCE_FWD(false, false, true) FLCE_FWD(false, true, false)
@@ -689,11 +692,12 @@ hipError_t launch_transpose(int dtype, const TransposeArgs& a, hipStream_t st) {
 
 template <int D>
 static hipError_t g_dispatch(bool bias, bool cap, const GArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)(a.n_tok_tiles * a.n_voc_tiles)), block(NTHREADS);
-  if (!bias && !cap) hipLaunchKernelGGL((bwd_g_kernel<D, false, false>), grid, block, 0, st, a);
-  else if (!bias && cap) hipLaunchKernelGGL((bwd_g_kernel<D, false, true>), grid, block, 0, st, a);
-  else if (bias && !cap) hipLaunchKernelGGL((bwd_g_kernel<D, true, false>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((bwd_g_kernel<D, true, true>), grid, block, 0, st, a);
+  constexpr int W = kRecomputeWaves;
+  const dim3 grid((unsigned)(a.n_tok_tiles * a.n_voc_tiles)), block(W * 64);
+  if (!bias && !cap) hipLaunchKernelGGL((bwd_g_kernel<D, false, false, W>), grid, block, 0, st, a);
+  else if (!bias && cap) hipLaunchKernelGGL((bwd_g_kernel<D, false, true, W>), grid, block, 0, st, a);
+  else if (bias && !cap) hipLaunchKernelGGL((bwd_g_kernel<D, true, false, W>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((bwd_g_kernel<D, true, true, W>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 

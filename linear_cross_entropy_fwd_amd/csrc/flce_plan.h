@@ -8,6 +8,16 @@
 
 namespace flce {
 
+// Waves per workgroup of the GEMM-shaped kernels (each 256 x 256 output
+// tile; 4 = one wave per SIMD with 128 x 128 per wave, 8 = two per SIMD with
+// 128 x 64 per wave).
+constexpr int kFwdWaves = 8;        // forward logit tiles
+constexpr int kRecomputeWaves = 8;  // backward recompute (G, G^T, grad_bias partials)
+constexpr int kContractWaves = 8;   // grad_hidden and grad_weight contractions
+// grad_bias partial sums per 256-token tile: one per wave column (64 tokens
+// each with 8 waves, 128 with 4).
+constexpr int kBiasParts = kRecomputeWaves == 8 ? 4 : 2;
+
 // Forward: one workgroup per (token tile, vocabulary split); a split is a run
 // of consecutive 256-id vocabulary tiles whose per-row online state the
 // workgroup carries in registers.  The split size depends on V only, so a
