@@ -71,33 +71,31 @@ struct Panel {
 };
 
 // ---------------------------------------------------------------------------
-// Multi-stage operand pipeline.  Global memory is copied straight into LDS
-// (global_load_lds_dwordx4, 16 bytes per lane) three K-stages ahead of use,
-// into a ring of NSTAGES buffers.  A stage is 64 bytes of K for all 256 rows
-// of A and of B (32 KB).  Rows are stored 64 bytes apart with the four 16-byte
-// chunks of a row XOR-swizzled by (row>>2)&3, so that the 16 lanes that read
-// one chunk of 16 consecutive rows hit all 64 LDS banks once.  Each stage has
-// two 32-byte slabs; the fragments of the next slab are read while the MFMAs
-// of the current one run, and the single barrier per stage sits between the
-// two slabs' MFMAs.
+// Two-stage operand pipeline.  Global memory is copied straight into LDS
+// (global_load_lds_dwordx4, 16 bytes per lane) one K-stage ahead of use into
+// two buffers.  A stage is 128 bytes of K (one cache line per row) for all
+// 256 rows of A and of B (64 KB); one copy instruction moves 8 whole rows
+// (1 KB).  Rows are stored 128 bytes apart with the eight 16-byte chunks of
+// row r at positions c ^ ((r>>1)&7), so that the 16 lanes that read one
+// chunk of 16 consecutive rows hit all 64 LDS banks once.  A stage has four
+// 32-byte slabs; the fragments of the next slab are read while the MFMAs of
+// the current one run, and the one barrier per stage sits before the last
+// slab's MFMAs.
 
-constexpr int ROWB = 64;                 // K bytes per row per stage
-constexpr int OPB = TILE * ROWB;         // one operand, one stage: 16 KB
-constexpr int STB = 2 * OPB;             // A + B: 32 KB
-constexpr int NSTAGES = 4;               // 128 KB of LDS
+constexpr int ROWB = 128;                // K bytes per row per stage
+constexpr int OPB = TILE * ROWB;         // one operand, one stage: 32 KB
+constexpr int STB = 2 * OPB;             // A + B: 64 KB
+constexpr int NSTAGES = 2;               // 128 KB of LDS
+constexpr int NSLABS = ROWB / 32;        // 32-byte MFMA slabs per stage
 
 __shared__ __attribute__((aligned(1024))) char g_stage0[STB];
 __shared__ __attribute__((aligned(1024))) char g_stage1[STB];
-__shared__ __attribute__((aligned(1024))) char g_stage2[STB];
-__shared__ __attribute__((aligned(1024))) char g_stage3[STB];
 
 // Separate arrays per stage (not one array with offsets) so that no access
 // to one stage's buffer is mistaken for an access to another's.
 template <int S> __device__ __forceinline__ char* stage_buf() {
   if constexpr (S == 0) return g_stage0;
-  else if constexpr (S == 1) return g_stage1;
-  else if constexpr (S == 2) return g_stage2;
-  else return g_stage3;
+  else return g_stage1;
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -157,9 +155,11 @@ template <> struct Geo<4> { static constexpr int WI = 4, WJ = 4; };
 template <> struct Geo<8> { static constexpr int WI = 4, WJ = 2; };
 template <int W> struct Gemm {
   static constexpr int WI = Geo<W>::WI, WJ = Geo<W>::WJ;
-  static constexpr int GN = TILE / (32 * WJ);   // wave columns
-  static constexpr int NCOP = 2 * TILE / 16 / W;  // 16-row copies per thread per stage
-  static constexpr int NREAD = WI + WJ;         // fragment reads per slab
+  static constexpr int GN = TILE / (32 * WJ);       // wave columns
+  static constexpr int NBLK = 2 * TILE / 8;         // 8-row copy blocks per stage (64)
+  static constexpr int NCOP = NBLK / W;             // copies per thread per stage
+  static constexpr int NREAD = WI + WJ;             // fragment reads per slab
+  static constexpr int NSTEP = WI * WJ;             // MFMAs per slab
   __device__ static int wm(int wave) { return wave / GN; }
   __device__ static int wn(int wave) { return wave % GN; }
 };
@@ -168,17 +168,18 @@ template <int W> struct Frags {
   uint4 a[Gemm<W>::WI], b[Gemm<W>::WJ];
 };
 
-// Per-thread global byte offsets of its copies.  A stage is 32 copies of 16
-// rows x 64 bytes (1 KB): block b = 0..31 is operand b>>4, rows (b&15)*16 ..
-// +16.  Copy i of wave w is block w + W*i (so copies 0 .. NCOP/2-1 are of
-// operand A, the rest of B).  Lane L covers row (b&15)*16 + L/4 (clamped to
-// the panel) and LDS chunk position L&3, which holds global chunk
-// (L&3) ^ ((row>>2)&3) of that row.
+// Per-thread global byte offsets of its copies.  Block b = 0..63 of a stage
+// is operand b>>5, rows (b&31)*8 .. +8.  Copy i of wave w is block w + W*i
+// (copies 0 .. NCOP/2-1 are of operand A, the rest of B).  Lane L covers row
+// (b&31)*8 + L/8 (clamped to the panel) and LDS chunk position L&7, which
+// holds global chunk (L&7) ^ ((row>>1)&7) of that row.
 template <int W> struct CopyPlan {
   uint32_t off[Gemm<W>::NCOP];
 };
 
 template <int W> __device__ __forceinline__ constexpr int copy_block(int i, int wave) { return wave + W * i; }
+__device__ __forceinline__ int copy_row(int blk, int L) { return (blk & 31) * 8 + (L >> 3); }
+__device__ __forceinline__ int copy_chunk(int row, int L) { return (L & 7) ^ ((row >> 1) & 7); }
 
 template <int W>
 __device__ __forceinline__ void copy_plan(CopyPlan<W>& cp, const Panel& A, const Panel& B, int t) {
@@ -186,9 +187,9 @@ __device__ __forceinline__ void copy_plan(CopyPlan<W>& cp, const Panel& A, const
 #pragma unroll
   for (int i = 0; i < Gemm<W>::NCOP; ++i) {
     const int blk = copy_block<W>(i, wave);
-    const Panel& p = blk < 16 ? A : B;
-    int row = (blk & 15) * 16 + (L >> 2);
-    const int c = (L & 3) ^ ((row >> 2) & 3);
+    const Panel& p = blk < 32 ? A : B;
+    int row = copy_row(blk, L);
+    const int c = copy_chunk(row, L);
     row = row < p.rows ? row : p.rows - 1;
     cp.off[i] = (uint32_t)(row * p.ld) + (uint32_t)(c * 16);
   }
@@ -206,7 +207,7 @@ __device__ __forceinline__ void copy_one_any(const CopyPlan<W>& cp, const Panel&
   constexpr bool OPA = I < Gemm<W>::NCOP / 2;
   const Panel& p = OPA ? A : B;
   const int blk = copy_block<W>(I, wave);
-  const int c = ((((blk & 15) * 16 + (L >> 2)) >> 2) & 3) ^ (L & 3);
+  const int c = copy_chunk(copy_row(blk, L), L);
   const uint32_t off = (masked && k0 + c * 16 >= p.kbytes)
                            ? cp.off[I] - (uint32_t)(c * 16) + (uint32_t)(p.kbytes - 16 - k0)
                            : cp.off[I];
@@ -214,12 +215,12 @@ __device__ __forceinline__ void copy_one_any(const CopyPlan<W>& cp, const Panel&
   lds_copy16(uniform_ptr(p.base + k0), off, dst);
 }
 
-template <int W, int S, int I = 0>
-__device__ __forceinline__ void copy_any(const CopyPlan<W>& cp, const Panel& A, const Panel& B, int kt,
-                                         int nk, bool ragged, int t) {
-  if constexpr (I < Gemm<W>::NCOP) {
-    copy_one_any<W, S, I>(cp, A, B, kt, ragged && kt == nk - 1, t);
-    copy_any<W, S, I + 1>(cp, A, B, kt, nk, ragged, t);
+template <int W, int S, int I0, int I1>
+__device__ __forceinline__ void copy_range(const CopyPlan<W>& cp, const Panel& A, const Panel& B, int kt,
+                                           int nk, bool ragged, int t) {
+  if constexpr (I0 < I1) {
+    copy_one_any<W, S, I0>(cp, A, B, kt, ragged && kt == nk - 1, t);
+    copy_range<W, S, I0 + 1, I1>(cp, A, B, kt, nk, ragged, t);
   }
 }
 
@@ -232,42 +233,42 @@ __device__ __forceinline__ void zero_tail(const Panel& A, int kt, int t) {
 #pragma unroll
   for (int i = 0; i < Gemm<W>::NCOP; ++i) {
     const int blk = copy_block<W>(i, wave);
-    const int c = ((((blk & 15) * 16 + (L >> 2)) >> 2) & 3) ^ (L & 3);
+    const int c = copy_chunk(copy_row(blk, L), L);
     if (k0 + c * 16 >= A.kbytes) *reinterpret_cast<uint4*>(base + blk * 1024 + L * 16) = make_uint4(0u, 0u, 0u, 0u);
   }
 }
 
-// Byte offsets, inside a stage buffer, of this lane's fragment chunk for
-// slab 0 and slab 1, for its first A and first B row block.  The lane reads
-// rows r0 + 32*i + (l&31): they differ by multiples of 32, so the swizzle
-// term (row>>2)&3 = ((l&31)>>2)&3 is the same for all its blocks, which then
-// sit 32*ROWB bytes apart (an immediate offset).
+// Byte offsets, inside a stage buffer, of this lane's fragment chunk of each
+// slab for its first A and first B row block.  The lane reads rows
+// r0 + 32*i + (l&31): they differ by multiples of 32, so the swizzle term
+// ((row>>1)&7) = ((l&31)>>1)&7 is the same for all its blocks, which then sit
+// 32*ROWB bytes apart (an immediate offset).
 struct FragBase {
-  uint32_t a[2], b[2];
+  uint32_t a[NSLABS], b[NSLABS];
 };
 
 template <int W>
 __device__ __forceinline__ void frag_base(FragBase& fb, int wave, int lane) {
-  const int r32 = lane & 31, half = lane >> 5, x = (r32 >> 2) & 3;
+  const int r32 = lane & 31, half = lane >> 5, x = (r32 >> 1) & 7;
   const int ra = Gemm<W>::wm(wave) * 32 * Gemm<W>::WI, rb = Gemm<W>::wn(wave) * 32 * Gemm<W>::WJ;
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < NSLABS; ++s) {
     const uint32_t coff = (uint32_t)(((2 * s + half) ^ x) << 4);
     fb.a[s] = (uint32_t)((ra + r32) * ROWB) + coff;
     fb.b[s] = (uint32_t)(OPB + (rb + r32) * ROWB) + coff;
   }
 }
 
-// Fragment P (0..WI-1: A row block P; WI..: B row block P-WI) of slab `slab`
-// of buffer S: lane (l&31, l>>5) reads chunk 2*slab + (l>>5) of its row.
-template <int W, int S, int P>
-__device__ __forceinline__ void frag_read_one(Frags<W>& f, const FragBase& fb, int slab) {
+// Fragment P (0..WI-1: A row block P; WI..: B row block P-WI) of slab SL of
+// buffer S: lane (l&31, l>>5) reads chunk 2*SL + (l>>5) of its row.
+template <int W, int S, int SL, int P>
+__device__ __forceinline__ void frag_read_one(Frags<W>& f, const FragBase& fb) {
   constexpr int WI = Gemm<W>::WI;
   const char* base = stage_buf<S>();
   if constexpr (P < WI)
-    f.a[P] = *reinterpret_cast<const uint4*>(base + fb.a[slab] + P * 32 * ROWB);
+    f.a[P] = *reinterpret_cast<const uint4*>(base + fb.a[SL] + P * 32 * ROWB);
   else
-    f.b[P - WI] = *reinterpret_cast<const uint4*>(base + fb.b[slab] + (P - WI) * 32 * ROWB);
+    f.b[P - WI] = *reinterpret_cast<const uint4*>(base + fb.b[SL] + (P - WI) * 32 * ROWB);
 }
 
 // The order in which a slab's fragments are read: A0, B0 .. B(WJ-1), A1 ..
@@ -278,16 +279,19 @@ template <int W> __device__ __forceinline__ constexpr int read_order(int k) {
   return k == 0 ? 0 : (k <= WJ ? WI + k - 1 : k - WJ);
 }
 
-// What follows MFMA step s of a slab: read k (0..NREAD-1), copy c (100 + c)
-// or nothing (-1).  W = 4: 16 MFMAs | a read after every even step, a copy
-// after every fourth (1, 5, 9, 13).  W = 8: 8 MFMAs | reads after steps
-// 0 1 3 4 6 7, copies after 2 and 5.
-template <int W> __device__ __forceinline__ constexpr int slab_action(int s) {
-  if constexpr (W == 4) {
-    return (s & 1) == 0 ? s / 2 : ((s & 3) == 1 ? 100 + s / 4 : -1);
-  } else {
-    return s == 2 ? 100 : (s == 5 ? 101 : (s < 2 ? s : (s < 5 ? s - 1 : s - 2)));
-  }
+// Which read (0..NREAD-1) and which of the phase's copies (0..NCOP/2-1)
+// follow MFMA step s of a slab; -1 for none.  With copies (COPIES):
+//   W = 4: 16 steps, a read after every even step, a copy after every odd one;
+//   W = 8: 8 steps, reads after steps 0..5, copies after 1, 3, 5, 7.
+// Without: W = 4 reads after even steps; W = 8 after 0 1 3 4 6 7.
+template <int W, bool COPIES> __device__ __forceinline__ constexpr int step_read(int s) {
+  if constexpr (W == 4) return (s & 1) == 0 ? s / 2 : -1;
+  else if constexpr (COPIES) return s < 6 ? s : -1;
+  else return s == 2 || s == 5 ? -1 : (s < 2 ? s : (s < 5 ? s - 1 : s - 2));
+}
+template <int W, bool COPIES> __device__ __forceinline__ constexpr int step_copy(int s) {
+  if constexpr (!COPIES) return -1;
+  else return (s & 1) == 1 ? s / 2 : -1;
 }
 
 // Copy issuers for slab_phase.  PlainCopy: a stage that lies wholly inside K
@@ -295,7 +299,7 @@ template <int W> __device__ __forceinline__ constexpr int slab_action(int s) {
 // scalar (the stage's global base and the LDS destination in m0).
 template <int W> struct PlainCopy {
   const CopyPlan<W>& cp;
-  const char* base;   // operand base + this stage's K offset (wave-uniform)
+  const char* base;   // operand base + the copied stage's K offset (wave-uniform)
   uint32_t wave_lds;  // wave * 1024 (wave-uniform)
   template <int S, int I> __device__ __forceinline__ void issue() const {
     lds_copy16(base, cp.off[I], lds_addr(stage_buf<S>() + W * I * 1024) + wave_lds);
@@ -315,78 +319,88 @@ template <int W> struct EdgeCopy {
     copy_one_any<W, S, I>(cp, A, B, kc, masked, t);
   }
 };
+struct NoCopy {
+  template <int S, int I> __device__ __forceinline__ void issue() const {}
+};
 
-// One slab's WI x WJ MFMAs on `fm`, with the NREAD fragment reads of the next
-// slab (buffer RS, slab `rslab`, into `fr`) and NCOP/2 copies (C0.. into
-// buffer CS) placed between them as slab_action says: a wave issues in order
-// and would otherwise stall its MFMAs behind a burst of copies or reads.
-template <int D, int W, int RS, int CS, int C0, int STEP = 0, class Copy>
+// One slab's WI x WJ MFMAs on `fm`, with the NREAD fragment reads of slab RSL
+// of buffer RS (into `fr`) and, if COPIES, the phase's NCOP/2 copies (C0 ..
+// into buffer CS) placed between them as step_read / step_copy say: a wave
+// issues in order and would otherwise stall its MFMAs behind a burst of
+// copies or reads.
+template <int D, int W, int RS, int RSL, int CS, int C0, bool COPIES, int STEP = 0, class Copy>
 __device__ __forceinline__ void slab_phase(f32x16_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], const Frags<W>& fm,
-                                           Frags<W>& fr, const FragBase& fb, int rslab, const Copy& cp) {
+                                           Frags<W>& fr, const FragBase& fb, const Copy& cp) {
   constexpr int WJ = Gemm<W>::WJ;
-  if constexpr (STEP < Gemm<W>::WI * WJ) {
+  if constexpr (STEP < Gemm<W>::NSTEP) {
     constexpr int I = STEP / WJ, J = STEP % WJ;
     mfma_frag<D>(acc[I][J], fm.a[I], fm.b[J]);
-    constexpr int act = slab_action<W>(STEP);
-    if constexpr (act >= 100) cp.template issue<CS, C0 + act - 100>();
-    else if constexpr (act >= 0) frag_read_one<W, RS, read_order<W>(act)>(fr, fb, rslab);
+    constexpr int rd = step_read<W, COPIES>(STEP), cpy = step_copy<W, COPIES>(STEP);
+    if constexpr (rd >= 0) frag_read_one<W, RS, RSL, read_order<W>(rd)>(fr, fb);
+    if constexpr (cpy >= 0) cp.template issue<CS, C0 + cpy>();
     sched_fence();
-    slab_phase<D, W, RS, CS, C0, STEP + 1>(acc, fm, fr, fb, rslab, cp);
+    slab_phase<D, W, RS, RSL, CS, C0, COPIES, STEP + 1>(acc, fm, fr, fb, cp);
   }
 }
 
-// All NREAD fragments of a slab, in read_order (so that every path into a
-// stage has the same reads pending).
-template <int W, int S, int K = 0>
-__device__ __forceinline__ void frag_read(Frags<W>& f, const FragBase& fb, int slab) {
+// All NREAD fragments of slab SL of buffer S, in read_order (so that every
+// path into a stage has the same reads pending).
+template <int W, int S, int SL, int K = 0>
+__device__ __forceinline__ void frag_read(Frags<W>& f, const FragBase& fb) {
   if constexpr (K < Gemm<W>::NREAD) {
-    frag_read_one<W, S, read_order<W>(K)>(f, fb, slab);
-    frag_read<W, S, K + 1>(f, fb, slab);
+    frag_read_one<W, S, SL, read_order<W>(K)>(f, fb);
+    frag_read<W, S, SL, K + 1>(f, fb);
   }
 }
 
-// Stage kt from buffer S (f0 holds its slab 0).  Every stage copies stage
-// kt+3 into buffer (S+3)%4 (that buffer was last read in stage kt-1, before
-// that stage's barrier):
-//   phase A: slab-0 MFMAs | slab-1 reads of buffer S | operand-A copies
-//   wait for stage kt+1's copies, zero its ragged tail, barrier
-//   phase B: slab-1 MFMAs | slab-0 reads of buffer S+1 | operand-B copies
-// Copies issued after stage kt+1's when the wait runs: stage kt+2's NCOP and
-// stage kt+3's first NCOP/2.
-template <int W> constexpr int kStageWait = Gemm<W>::NCOP + Gemm<W>::NCOP / 2;
+// Stage kt from buffer S (f0 holds its slab 0; stage kt+1's operand-A copies
+// are in flight):
+//   slab 0: MFMAs | reads of slab 1 | operand-B copies of stage kt+1 (into S^1)
+//   slab 1: MFMAs | reads of slab 2
+//   slab 2: MFMAs | reads of slab 3
+//   wait for every copy (stage kt+1), zero its ragged tail, barrier: every
+//   wave is done reading buffer S and stage kt+1 is visible
+//   slab 3: MFMAs | reads of slab 0 of stage kt+1 (S^1) | operand-A copies of
+//   stage kt+2 (into S)
+// CB and CA issue the two halves of copies.
+template <int D, int W, int S, class CB, class CA>
+__device__ __forceinline__ void kstage(f32x16_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], Frags<W>& f0, Frags<W>& f1,
+                                       const FragBase& fb, const CB& cb, const CA& ca, bool zero_next,
+                                       const Panel& A, int kt, int t) {
+  static_assert(NSLABS == 4, "the schedule below assumes four slabs");
+  constexpr int SN = S ^ 1, H = Gemm<W>::NCOP / 2;
+  const NoCopy nc;
+  sched_fence();
+  slab_phase<D, W, S, 1, SN, H, true>(acc, f0, f1, fb, cb);
+  slab_phase<D, W, S, 2, SN, 0, false>(acc, f1, f0, fb, nc);
+  slab_phase<D, W, S, 3, SN, 0, false>(acc, f0, f1, fb, nc);
+  wait_vmcnt<0>();
+  if (zero_next) zero_tail<W, SN>(A, kt + 1, t);
+  lds_barrier();
+  slab_phase<D, W, SN, 0, S, 0, true>(acc, f1, f0, fb, ca);
+}
 
-// kstage_plain: stage kt+3 lies wholly inside K.
 template <int D, int W, int S>
 __device__ __forceinline__ void kstage_plain(f32x16_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], Frags<W>& f0,
                                              Frags<W>& f1, const CopyPlan<W>& cp, const FragBase& fb,
-                                             const Panel& A, const Panel& B, int kt, uint32_t wave_lds) {
-  constexpr int SN = (S + 1) % NSTAGES, SC = (S + NSTAGES - 1) % NSTAGES, H = Gemm<W>::NCOP / 2;
-  const int64_t k0 = (int64_t)(kt + NSTAGES - 1) * ROWB;
-  const PlainCopy<W> ca{cp, uniform_ptr(A.base + k0), wave_lds};
-  const PlainCopy<W> cb{cp, uniform_ptr(B.base + k0), wave_lds};
-  sched_fence();
-  slab_phase<D, W, S, SC, 0>(acc, f0, f1, fb, 1, ca);
-  wait_vmcnt<kStageWait<W>>();
-  lds_barrier();
-  slab_phase<D, W, SN, SC, H>(acc, f1, f0, fb, 0, cb);
+                                             const Panel& A, const Panel& B, int kt, uint32_t wave_lds,
+                                             int t) {
+  const PlainCopy<W> cb{cp, uniform_ptr(B.base + (int64_t)(kt + 1) * ROWB), wave_lds};
+  const PlainCopy<W> ca{cp, uniform_ptr(A.base + (int64_t)(kt + 2) * ROWB), wave_lds};
+  kstage<D, W, S>(acc, f0, f1, fb, cb, ca, false, A, kt, t);
 }
 
-// kstage_edge: any stage; past the end of K the copy re-reads the last stage
-// (never used), so the schedule still has no branches.
+// Past the end of K a copy re-reads the last stage (never used), so the
+// schedule still has no branches.
 template <int D, int W, int S>
 __device__ __forceinline__ void kstage_edge(f32x16_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], Frags<W>& f0,
                                             Frags<W>& f1, const CopyPlan<W>& cp, const FragBase& fb,
                                             const Panel& A, const Panel& B, int kt, int nk, bool ragged,
                                             int t) {
-  constexpr int SN = (S + 1) % NSTAGES, SC = (S + NSTAGES - 1) % NSTAGES, H = Gemm<W>::NCOP / 2;
-  const int kc = min(kt + NSTAGES - 1, nk - 1);
-  const EdgeCopy<W> c{cp, A, B, kc, ragged && kc == nk - 1, t};
-  sched_fence();
-  slab_phase<D, W, S, SC, 0>(acc, f0, f1, fb, 1, c);
-  wait_vmcnt<kStageWait<W>>();
-  if (ragged && kt + 1 == nk - 1) zero_tail<W, SN>(A, kt + 1, t);
-  lds_barrier();
-  slab_phase<D, W, SN, SC, H>(acc, f1, f0, fb, 0, c);
+  const int k1 = min(kt + 1, nk - 1), k2 = min(kt + 2, nk - 1);
+  const EdgeCopy<W> cb{cp, A, B, k1, ragged && k1 == nk - 1, t};
+  const EdgeCopy<W> ca{cp, A, B, k2, ragged && k2 == nk - 1, t};
+  kstage<D, W, S>(acc, f0, f1, fb, cb, ca, ragged && kt + 1 == nk - 1, A, kt, t);
 }
 
 // acc[i][j] (this wave's WI x WJ blocks) = A_panel . B_panel^T over all of K.
@@ -395,7 +409,8 @@ __device__ __forceinline__ void kstage_edge(f32x16_t (&acc)[Gemm<W>::WI][Gemm<W>
 template <int D, int W>
 __device__ __forceinline__ void gemm_nt_tile(f32x16_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], const Panel& A,
                                              const Panel& B) {
-  static_assert(NSTAGES == 4, "the unrolled loops below assume four stages");
+  static_assert(NSTAGES == 2, "the loops below alternate two buffers");
+  constexpr int H = Gemm<W>::NCOP / 2;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
 #pragma unroll
   for (int i = 0; i < Gemm<W>::WI; ++i)
@@ -409,38 +424,29 @@ __device__ __forceinline__ void gemm_nt_tile(f32x16_t (&acc)[Gemm<W>::WI][Gemm<W
   CopyPlan<W> cp;
   copy_plan<W>(cp, A, B, t);
   lds_barrier();  // every wave is done with the buffers of any previous use
-  // stages 0..2 (clamped to the last stage, as in kstage_edge)
-  copy_any<W, 0>(cp, A, B, 0, nk, ragged, t);
-  copy_any<W, 1>(cp, A, B, min(1, nk - 1), nk, ragged, t);
-  copy_any<W, 2>(cp, A, B, min(2, nk - 1), nk, ragged, t);
-  wait_vmcnt<2 * Gemm<W>::NCOP>();
+  // stage 0 whole, stage 1's operand-A half (clamped as in kstage_edge)
+  copy_range<W, 0, 0, 2 * H>(cp, A, B, 0, nk, ragged, t);
+  copy_range<W, 1, 0, H>(cp, A, B, min(1, nk - 1), nk, ragged, t);
+  wait_vmcnt<H>();
   if (ragged && nk == 1) zero_tail<W, 0>(A, 0, t);
   lds_barrier();
   FragBase fb;
   frag_base<W>(fb, wave, lane);
   Frags<W> f0, f1;
-  frag_read<W, 0>(f0, fb, 0);
-  // Whole rounds of four plain stages (each copies a stage that is neither
-  // past K nor ragged: kt+3+3 <= last_plain), then rounds of edge stages.
-  // A loop header with only two predecessors keeps the waitcnt pass from
-  // falling back to a full wait at the top of every round.
+  frag_read<W, 0, 0>(f0, fb);
+  // Pairs of plain stages (every copy they issue lies inside K and is not
+  // ragged: kt+1+2 <= last_plain), then pairs of edge stages.  A loop header
+  // with only two predecessors keeps the waitcnt pass from falling back to a
+  // full wait at the top of every round.
   const int last_plain = ragged ? nk - 2 : nk - 1;
   int kt = 0;
-  for (; kt + 6 <= last_plain; kt += 4) {
-    kstage_plain<D, W, 0>(acc, f0, f1, cp, fb, A, B, kt, wave_lds);
-    kstage_plain<D, W, 1>(acc, f0, f1, cp, fb, A, B, kt + 1, wave_lds);
-    kstage_plain<D, W, 2>(acc, f0, f1, cp, fb, A, B, kt + 2, wave_lds);
-    kstage_plain<D, W, 3>(acc, f0, f1, cp, fb, A, B, kt + 3, wave_lds);
+  for (; kt + 3 <= last_plain; kt += 2) {
+    kstage_plain<D, W, 0>(acc, f0, f1, cp, fb, A, B, kt, wave_lds, t);
+    kstage_plain<D, W, 1>(acc, f0, f1, cp, fb, A, B, kt + 1, wave_lds, t);
   }
-  for (; kt < nk; kt += 4) {
+  for (; kt < nk; kt += 2) {
     kstage_edge<D, W, 0>(acc, f0, f1, cp, fb, A, B, kt, nk, ragged, t);
-    if (kt + 1 < nk) {
-      kstage_edge<D, W, 1>(acc, f0, f1, cp, fb, A, B, kt + 1, nk, ragged, t);
-      if (kt + 2 < nk) {
-        kstage_edge<D, W, 2>(acc, f0, f1, cp, fb, A, B, kt + 2, nk, ragged, t);
-        if (kt + 3 < nk) kstage_edge<D, W, 3>(acc, f0, f1, cp, fb, A, B, kt + 3, nk, ragged, t);
-      }
-    }
+    if (kt + 1 < nk) kstage_edge<D, W, 1>(acc, f0, f1, cp, fb, A, B, kt + 1, nk, ragged, t);
   }
   wait_vmcnt<0>();
   lds_barrier();
