@@ -279,19 +279,18 @@ template <int W> __device__ __forceinline__ constexpr int read_order(int k) {
   return k == 0 ? 0 : (k <= WJ ? WI + k - 1 : k - WJ);
 }
 
-// Which read (0..NREAD-1) and which of the phase's copies (0..NCOP/2-1)
-// follow MFMA step s of a slab; -1 for none.  With copies (COPIES):
-//   W = 4: 16 steps, a read after every even step, a copy after every odd one;
-//   W = 8: 8 steps, reads after steps 0..5, copies after 1, 3, 5, 7.
-// Without: W = 4 reads after even steps; W = 8 after 0 1 3 4 6 7.
+// Which read (0..NREAD-1) and which copy (0..NCOP-1) follow MFMA step s of
+// a slab; -1 for none.  With copies (COPIES, every copy of a stage in one
+// slab): W = 4: 16 steps, a copy after each, a read after every even one;
+// W = 8: 8 steps, a copy after each, reads after steps 0..5.  Without:
+// W = 4 reads after even steps; W = 8 after 0 1 3 4 6 7.
 template <int W, bool COPIES> __device__ __forceinline__ constexpr int step_read(int s) {
   if constexpr (W == 4) return (s & 1) == 0 ? s / 2 : -1;
   else if constexpr (COPIES) return s < 6 ? s : -1;
   else return s == 2 || s == 5 ? -1 : (s < 2 ? s : (s < 5 ? s - 1 : s - 2));
 }
 template <int W, bool COPIES> __device__ __forceinline__ constexpr int step_copy(int s) {
-  if constexpr (!COPIES) return -1;
-  else return (s & 1) == 1 ? s / 2 : -1;
+  return COPIES ? s : -1;
 }
 
 // Copy issuers for slab_phase.  PlainCopy: a stage that lies wholly inside K
@@ -353,41 +352,50 @@ __device__ __forceinline__ void frag_read(Frags<W>& f, const FragBase& fb) {
   }
 }
 
-// Stage kt from buffer S (f0 holds its slab 0; stage kt+1's operand-A copies
-// are in flight):
-//   slab 0: MFMAs | reads of slab 1 | operand-B copies of stage kt+1 (into S^1)
+// Stage kt from buffer S (f0 holds its slab 0; stage kt+1's copies are in
+// flight into S^1):
+//   slab 0: MFMAs | reads of slab 1
 //   slab 1: MFMAs | reads of slab 2
 //   slab 2: MFMAs | reads of slab 3
 //   wait for every copy (stage kt+1), zero its ragged tail, barrier: every
 //   wave is done reading buffer S and stage kt+1 is visible
-//   slab 3: MFMAs | reads of slab 0 of stage kt+1 (S^1) | operand-A copies of
-//   stage kt+2 (into S)
-// CB and CA issue the two halves of copies.
-template <int D, int W, int S, class CB, class CA>
+//   slab 3: MFMAs | reads of slab 0 of stage kt+1 (S^1) | every copy of
+//   stage kt+2 (into S), as early as the buffer allows, so that each copy
+//   has at least three slabs of MFMAs to land
+template <int D, int W, int S, class C>
 __device__ __forceinline__ void kstage(f32x16_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], Frags<W>& f0, Frags<W>& f1,
-                                       const FragBase& fb, const CB& cb, const CA& ca, bool zero_next,
-                                       const Panel& A, int kt, int t) {
+                                       const FragBase& fb, const C& c, bool zero_next, const Panel& A, int kt,
+                                       int t) {
   static_assert(NSLABS == 4, "the schedule below assumes four slabs");
-  constexpr int SN = S ^ 1, H = Gemm<W>::NCOP / 2;
+  constexpr int SN = S ^ 1;
   const NoCopy nc;
   sched_fence();
-  slab_phase<D, W, S, 1, SN, H, true>(acc, f0, f1, fb, cb);
+  slab_phase<D, W, S, 1, SN, 0, false>(acc, f0, f1, fb, nc);
   slab_phase<D, W, S, 2, SN, 0, false>(acc, f1, f0, fb, nc);
   slab_phase<D, W, S, 3, SN, 0, false>(acc, f0, f1, fb, nc);
   wait_vmcnt<0>();
   if (zero_next) zero_tail<W, SN>(A, kt + 1, t);
   lds_barrier();
-  slab_phase<D, W, SN, 0, S, 0, true>(acc, f1, f0, fb, ca);
+  slab_phase<D, W, SN, 0, S, 0, true>(acc, f1, f0, fb, c);
 }
+
+// Both operands' copies of one stage: copy I < NCOP/2 is of A, the rest of B.
+template <int W> struct PlainCopy2 {
+  PlainCopy<W> a, b;
+  template <int S, int I> __device__ __forceinline__ void issue() const {
+    if constexpr (I < Gemm<W>::NCOP / 2) a.template issue<S, I>();
+    else b.template issue<S, I>();
+  }
+};
 
 template <int D, int W, int S>
 __device__ __forceinline__ void kstage_plain(f32x16_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], Frags<W>& f0,
                                              Frags<W>& f1, const CopyPlan<W>& cp, const FragBase& fb,
                                              const Panel& A, const Panel& B, int kt, uint32_t wave_lds,
                                              int t) {
-  const PlainCopy<W> cb{cp, uniform_ptr(B.base + (int64_t)(kt + 1) * ROWB), wave_lds};
-  const PlainCopy<W> ca{cp, uniform_ptr(A.base + (int64_t)(kt + 2) * ROWB), wave_lds};
-  kstage<D, W, S>(acc, f0, f1, fb, cb, ca, false, A, kt, t);
+  const int64_t k0 = (int64_t)(kt + 2) * ROWB;
+  const PlainCopy2<W> c{{cp, uniform_ptr(A.base + k0), wave_lds}, {cp, uniform_ptr(B.base + k0), wave_lds}};
+  kstage<D, W, S>(acc, f0, f1, fb, c, false, A, kt, t);
 }
 
 // Past the end of K a copy re-reads the last stage (never used), so the
@@ -397,10 +405,9 @@ __device__ __forceinline__ void kstage_edge(f32x16_t (&acc)[Gemm<W>::WI][Gemm<W>
                                             Frags<W>& f1, const CopyPlan<W>& cp, const FragBase& fb,
                                             const Panel& A, const Panel& B, int kt, int nk, bool ragged,
                                             int t) {
-  const int k1 = min(kt + 1, nk - 1), k2 = min(kt + 2, nk - 1);
-  const EdgeCopy<W> cb{cp, A, B, k1, ragged && k1 == nk - 1, t};
-  const EdgeCopy<W> ca{cp, A, B, k2, ragged && k2 == nk - 1, t};
-  kstage<D, W, S>(acc, f0, f1, fb, cb, ca, ragged && kt + 1 == nk - 1, A, kt, t);
+  const int k2 = min(kt + 2, nk - 1);
+  const EdgeCopy<W> c{cp, A, B, k2, ragged && k2 == nk - 1, t};
+  kstage<D, W, S>(acc, f0, f1, fb, c, ragged && kt + 1 == nk - 1, A, kt, t);
 }
 
 // acc[i][j] (this wave's WI x WJ blocks) = A_panel . B_panel^T over all of K.
@@ -424,10 +431,10 @@ __device__ __forceinline__ void gemm_nt_tile(f32x16_t (&acc)[Gemm<W>::WI][Gemm<W
   CopyPlan<W> cp;
   copy_plan<W>(cp, A, B, t);
   lds_barrier();  // every wave is done with the buffers of any previous use
-  // stage 0 whole, stage 1's operand-A half (clamped as in kstage_edge)
+  // stages 0 and 1 (clamped as in kstage_edge)
   copy_range<W, 0, 0, 2 * H>(cp, A, B, 0, nk, ragged, t);
-  copy_range<W, 1, 0, H>(cp, A, B, min(1, nk - 1), nk, ragged, t);
-  wait_vmcnt<H>();
+  copy_range<W, 1, 0, 2 * H>(cp, A, B, min(1, nk - 1), nk, ragged, t);
+  wait_vmcnt<2 * H>();
   if (ragged && nk == 1) zero_tail<W, 0>(A, 0, t);
   lds_barrier();
   FragBase fb;
@@ -458,6 +465,35 @@ __device__ __forceinline__ int xcd_logical_id(int bid, int nblocks) {
   const int q = nblocks / 8, rem = nblocks % 8;
   const int xcd = bid % 8, k = bid / 8;
   return xcd < rem ? xcd * (q + 1) + k : rem * (q + 1) + (xcd - rem) * q + k;
+}
+
+// Tile order for a grid over na x nb output tiles (a: the dimension whose
+// panels are shared along b, and the reverse).  Workgroups are dealt to the
+// 8 XCDs round robin and run one per CU, so 32 of them share an XCD's L2 at a
+// time.  Numbered as below, those 32 cover a GA x GB = 4 x 8 block of tiles:
+// 12 distinct operand panels per K-stage in L2, where a row-major order
+// (e.g. 16 x 2) would need 18.  The grid is padded to whole blocks; a padding
+// workgroup gets valid = false and must exit at once.
+constexpr int GROUP_A = 4, GROUP_B = 8;
+
+__host__ __device__ inline int grouped_grid(int na, int nb) {
+  return ((na + GROUP_A - 1) / GROUP_A) * ((nb + GROUP_B - 1) / GROUP_B) * GROUP_A * GROUP_B;
+}
+
+struct TileAB {
+  int a, b;
+  bool valid;
+};
+
+__device__ __forceinline__ TileAB grouped_tile(int bid, int nblocks, int na, int nb) {
+  const int L = xcd_logical_id(bid, nblocks);
+  const int nga = (na + GROUP_A - 1) / GROUP_A;
+  const int g = L / (GROUP_A * GROUP_B), w = L % (GROUP_A * GROUP_B);
+  TileAB r;
+  r.a = (g % nga) * GROUP_A + w % GROUP_A;
+  r.b = (g / nga) * GROUP_B + w / GROUP_A;
+  r.valid = r.a < na && r.b < nb;
+  return r;
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -107,8 +107,9 @@ __global__ __launch_bounds__(W * 64) void fwd_tiles_kernel(FwdArgs a) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = Gemm<W>::wm(wave), wn = Gemm<W>::wn(wave), r32 = lane & 31, half = lane >> 5;
 
-  const int L = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int tt = L % a.n_tok_tiles, split = L / a.n_tok_tiles;
+  const TileAB ti = grouped_tile(blockIdx.x, gridDim.x, a.n_tok_tiles, a.n_splits);
+  if (!ti.valid) return;
+  const int tt = ti.a, split = ti.b;
   const int64_t n0 = (int64_t)tt * TILE;
   const int vt_begin = split * a.tiles_per_split;
   const int vt_end = min(vt_begin + a.tiles_per_split, a.n_voc_tiles);
@@ -430,8 +431,9 @@ __global__ __launch_bounds__(W * 64) void bwd_g_kernel(GArgs a) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = Gemm<W>::wm(wave), wn = Gemm<W>::wn(wave), r32 = lane & 31, half = lane >> 5;
 
-  const int L = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int tt = L % a.n_tok_tiles, vt = L / a.n_tok_tiles;
+  const TileAB ti = grouped_tile(blockIdx.x, gridDim.x, a.n_tok_tiles, a.n_voc_tiles);
+  if (!ti.valid) return;
+  const int tt = ti.a, vt = ti.b;
   const int64_t n0 = (int64_t)tt * TILE;
   const int vl0 = vt * TILE;              // chunk-local first id of the tile
   const int64_t v0 = a.c0 + vl0;          // global first id
@@ -566,8 +568,9 @@ __global__ __launch_bounds__(W * 64) void bwd_dh_kernel(DhArgs a) {
   constexpr int EB = Elem<D>::bytes, WI = Gemm<W>::WI, WJ = Gemm<W>::WJ;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = Gemm<W>::wm(wave), wn = Gemm<W>::wn(wave), r32 = lane & 31, half = lane >> 5;
-  const int L = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int tt = L % a.n_tok_tiles, ht = L / a.n_tok_tiles;
+  const TileAB ti = grouped_tile(blockIdx.x, gridDim.x, a.n_tok_tiles, a.n_h_tiles);
+  if (!ti.valid) return;
+  const int tt = ti.a, ht = ti.b;
   const int64_t n0 = (int64_t)tt * TILE, h0 = (int64_t)ht * TILE;
   const int64_t kb = (int64_t)a.cvpad * EB;
   Panel A{a.G + n0 * kb, kb, (int)min<int64_t>(TILE, a.N - n0), kb};
@@ -602,8 +605,9 @@ __global__ __launch_bounds__(W * 64) void bwd_dw_kernel(DwArgs a) {
   constexpr int EB = Elem<D>::bytes, WI = Gemm<W>::WI, WJ = Gemm<W>::WJ;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = Gemm<W>::wm(wave), wn = Gemm<W>::wn(wave), r32 = lane & 31, half = lane >> 5;
-  const int L = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int ht = L % a.n_h_tiles, vt = L / a.n_h_tiles;
+  const TileAB ti = grouped_tile(blockIdx.x, gridDim.x, a.n_h_tiles, a.n_voc_tiles);
+  if (!ti.valid) return;
+  const int ht = ti.a, vt = ti.b;
   const int64_t v0 = (int64_t)vt * TILE, h0 = (int64_t)ht * TILE;
   const int64_t kb = (int64_t)a.npad * EB;
   Panel A{a.GT + v0 * kb, kb, (int)min<int64_t>(TILE, a.cv - v0), kb};
@@ -642,7 +646,7 @@ static inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + p
 
 template <int D>
 static hipError_t fwd_tiles_dispatch(bool metrics, bool bias, bool cap, const FwdArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)(a.n_tok_tiles * a.n_splits)), block(kFwdWaves * 64);
+  const dim3 grid((unsigned)grouped_grid(a.n_tok_tiles, a.n_splits)), block(kFwdWaves * 64);
 #define FLCE_FWD(M, B, C)                                                                \
   if (metrics == M && bias == B && cap == C) {                                           \
     hipLaunchKernelGGL((fwd_tiles_kernel<D, M, B, C, kFwdWaves>), grid, block, 0, st, a); \
@@ -693,7 +697,7 @@ hipError_t launch_transpose(int dtype, const TransposeArgs& a, hipStream_t st) {
 template <int D>
 static hipError_t g_dispatch(bool bias, bool cap, const GArgs& a, hipStream_t st) {
   constexpr int W = kRecomputeWaves;
-  const dim3 grid((unsigned)(a.n_tok_tiles * a.n_voc_tiles)), block(W * 64);
+  const dim3 grid((unsigned)grouped_grid(a.n_tok_tiles, a.n_voc_tiles)), block(W * 64);
   if (!bias && !cap) hipLaunchKernelGGL((bwd_g_kernel<D, false, false, W>), grid, block, 0, st, a);
   else if (!bias && cap) hipLaunchKernelGGL((bwd_g_kernel<D, false, true, W>), grid, block, 0, st, a);
   else if (bias && !cap) hipLaunchKernelGGL((bwd_g_kernel<D, true, false, W>), grid, block, 0, st, a);
@@ -711,7 +715,7 @@ hipError_t launch_backward_g(int dtype, bool bias, bool cap, const GArgs& a, hip
 }
 
 hipError_t launch_backward_dh(int dtype, const DhArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)(a.n_tok_tiles * a.n_h_tiles)), block(kContractWaves * 64);
+  const dim3 grid((unsigned)grouped_grid(a.n_tok_tiles, a.n_h_tiles)), block(kContractWaves * 64);
   switch (dtype) {
     case DT_F32: hipLaunchKernelGGL((bwd_dh_kernel<DT_F32, kContractWaves>), grid, block, 0, st, a); break;
     case DT_F16: hipLaunchKernelGGL((bwd_dh_kernel<DT_F16, kContractWaves>), grid, block, 0, st, a); break;
@@ -722,7 +726,7 @@ hipError_t launch_backward_dh(int dtype, const DhArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_backward_dw(int dtype, const DwArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)(a.n_voc_tiles * a.n_h_tiles)), block(kContractWaves * 64);
+  const dim3 grid((unsigned)grouped_grid(a.n_h_tiles, a.n_voc_tiles)), block(kContractWaves * 64);
   switch (dtype) {
     case DT_F32: hipLaunchKernelGGL((bwd_dw_kernel<DT_F32, kContractWaves>), grid, block, 0, st, a); break;
     case DT_F16: hipLaunchKernelGGL((bwd_dw_kernel<DT_F16, kContractWaves>), grid, block, 0, st, a); break;
