@@ -395,23 +395,40 @@ __global__ __launch_bounds__(1024) void bwd_prep_kernel(PrepArgs a) {
   }
 }
 
-// dst[c][r] = src[r][c] for r < rows, 0 for rows <= r < rpad.  64x64 tiles.
+// dst[c][r] = src[r][c] for r < rows, 0 for rows <= r < rpad.  A workgroup
+// moves a 64-row x 256-byte tile: 16-byte loads along src rows, through LDS,
+// 16-byte stores along dst rows.  Needs cols*EB and src_ld*EB multiples of 16
+// (hidden*bytes % 16 == 0 is checked at the boundary) and rpad % 64 == 0.
 template <int EB>
 __global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
   typedef typename std::conditional<EB == 4, uint32_t, uint16_t>::type U;
-  __shared__ U tile[64][65];
-  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+  constexpr int E = 16 / EB;           // elements per 16 bytes
+  constexpr int TR = 64, TC = 16 * E;  // tile: TR src rows x TC src cols
+  constexpr int PITCH = TC + E;        // LDS row pitch: 16-byte aligned, not a multiple of 128 bytes
+  constexpr int SEGS = TR / E;         // 16-byte pieces per dst row of the tile
+  __shared__ __attribute__((aligned(16))) U tile[TR * PITCH];
+  const int64_t r0 = (int64_t)blockIdx.x * TR, c0 = (int64_t)blockIdx.y * TC;
   const U* src = reinterpret_cast<const U*>(a.src);
   U* dst = reinterpret_cast<U*>(a.dst);
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int k = ty; k < 64; k += 4) {
-    const int64_t r = r0 + k, c = c0 + tx;
-    tile[k][tx] = (r < a.rows && c < a.cols) ? src[r * a.src_ld + c] : (U)0;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = t + 256 * i, row = q >> 4, seg = q & 15;
+    const int64_t r = r0 + row, c = c0 + seg * E;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r < a.rows && c < a.cols) v = *reinterpret_cast<const uint4*>(src + r * a.src_ld + c);
+    *reinterpret_cast<uint4*>(tile + row * PITCH + seg * E) = v;
   }
   __syncthreads();
-  for (int k = ty; k < 64; k += 4) {
-    const int64_t c = c0 + k, r = r0 + tx;
-    if (c < a.cols && r < a.rpad) dst[c * a.rpad + r] = tile[tx][k];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = t + 256 * i, cc = q / SEGS, sg = q % SEGS;
+    const int64_t c = c0 + cc, r = r0 + sg * E;
+    if (c >= a.cols || r >= a.rpad) continue;
+    alignas(16) U e[E];
+#pragma unroll
+    for (int k = 0; k < E; ++k) e[k] = tile[(sg * E + k) * PITCH + cc];
+    *reinterpret_cast<uint4*>(dst + c * a.rpad + r) = *reinterpret_cast<const uint4*>(e);
   }
 }
 
@@ -688,7 +705,8 @@ hipError_t launch_backward_prep(const PrepArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_transpose(int dtype, const TransposeArgs& a, hipStream_t st) {
-  const dim3 grid(blocks_for(a.rpad, 64), blocks_for(a.cols, 64)), block(256);
+  const int tc = dtype == DT_F32 ? 64 : 128;
+  const dim3 grid(blocks_for(a.rpad, 64), blocks_for(a.cols, tc)), block(256);
   if (dtype == DT_F32) hipLaunchKernelGGL(transpose_kernel<4>, grid, block, 0, st, a);
   else hipLaunchKernelGGL(transpose_kernel<2>, grid, block, 0, st, a);
   return hipGetLastError();
