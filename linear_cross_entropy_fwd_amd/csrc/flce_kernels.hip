@@ -281,31 +281,50 @@ __global__ __launch_bounds__(W * 64) void fwd_tiles_kernel(FwdArgs a) {
 
 // ------------------------------------------------------------------ forward combine / reduce
 
+// One workgroup per 32 rows; the 8 groups of 32 threads each fold the
+// splits k = p, p+8, p+16, ... of their row into a partial state, then the
+// first group merges the 8 partials in the order p = 0..7 (a fixed order, so
+// a row's result does not depend on the launch or on N).
 template <bool METRICS>
 __global__ __launch_bounds__(256) void fwd_combine_kernel(CombineArgs a) {
-  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (n >= a.N) return;
+  constexpr int ROWS = 32, PARTS = 8;
+  __shared__ float sh[5][PARTS][ROWS];
+  const int t = threadIdx.x, rl = t % ROWS, p = t / ROWS;
+  const int64_t n = (int64_t)blockIdx.x * ROWS + rl;
+  const bool in = n < a.N;
+  const int64_t stride = (int64_t)a.n_splits * a.N;
+  const float* pm = a.part + (in ? n : 0);
+  float M = -INFINITY, S = 0.f, U = 0.f, av = -INFINITY;
+  int ai = 0x7fffffff;
+  if (in) {
+    for (int k = p; k < a.n_splits; k += PARTS) M = fmaxf(M, pm[(int64_t)k * a.N]);
+    for (int k = p; k < a.n_splits; k += PARTS) {
+      const float mk = pm[(int64_t)k * a.N];
+      if (mk != -INFINITY) {
+        const float d = mk - M;
+        const float al = fast_exp2(d * LOG2E);
+        const float sk = pm[stride + (int64_t)k * a.N];
+        S = S + sk * al;
+        if (METRICS) U = U + al * fmaf(d, sk, pm[2 * stride + (int64_t)k * a.N]);
+      }
+      if (METRICS)
+        argmax_merge(av, ai, pm[4 * stride + (int64_t)k * a.N], __float_as_int(pm[5 * stride + (int64_t)k * a.N]));
+    }
+  }
+  sh[0][p][rl] = M;
+  sh[1][p][rl] = S;
+  sh[2][p][rl] = U;
+  sh[3][p][rl] = av;
+  sh[4][p][rl] = __int_as_float(ai);
+  __syncthreads();
+  if (p != 0 || !in) return;
+  for (int q = 1; q < PARTS; ++q) {
+    lse_merge<METRICS>(M, S, U, sh[0][q][rl], sh[1][q][rl], sh[2][q][rl]);
+    if (METRICS) argmax_merge(av, ai, sh[3][q][rl], __float_as_int(sh[4][q][rl]));
+  }
   const int64_t tv = a.targets[n];
   const bool valid = tv != a.ignore_index;
   const bool bad = valid && (tv < 0 || tv >= a.V);
-  const int64_t stride = (int64_t)a.n_splits * a.N;
-  const float* pm = a.part + n;
-  float M = -INFINITY;
-  for (int k = 0; k < a.n_splits; ++k) M = fmaxf(M, pm[(int64_t)k * a.N]);
-  float S = 0.f, U = 0.f;
-  float av = -INFINITY;
-  int ai = 0x7fffffff;
-  for (int k = 0; k < a.n_splits; ++k) {
-    const float mk = pm[(int64_t)k * a.N];
-    if (mk != -INFINITY) {
-      const float d = mk - M;
-      const float al = fast_exp2(d * LOG2E);
-      S = S + pm[stride + (int64_t)k * a.N] * al;
-      if (METRICS) U = U + al * fmaf(d, pm[stride + (int64_t)k * a.N], pm[2 * stride + (int64_t)k * a.N]);
-    }
-    if (METRICS)
-      argmax_merge(av, ai, pm[4 * stride + (int64_t)k * a.N], __float_as_int(pm[5 * stride + (int64_t)k * a.N]));
-  }
   const float logS = logf(S);
   const float lse = M + logS;
   float row = 0.f;
@@ -579,52 +598,84 @@ __global__ __launch_bounds__(W * 64) void bwd_g_kernel(GArgs a) {
 
 // ------------------------------------------------------------------ backward contractions
 
+// grad_hidden puts H on the MFMA row axis, so that a lane's four consecutive
+// accumulator rows are four consecutive hidden indices of one output row: one
+// 16-byte access of the fp32 accumulator (8-byte store of 16-bit output) per
+// group.
+template <int D>
+__device__ __forceinline__ void store4(typename Elem<D>::T* p, float x0, float x1, float x2, float x3) {
+  if constexpr (Elem<D>::bytes == 2) {
+    typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+    u16x4 v;
+    v[0] = __builtin_bit_cast(uint16_t, from_f32<D>(x0));
+    v[1] = __builtin_bit_cast(uint16_t, from_f32<D>(x1));
+    v[2] = __builtin_bit_cast(uint16_t, from_f32<D>(x2));
+    v[3] = __builtin_bit_cast(uint16_t, from_f32<D>(x3));
+    *reinterpret_cast<u16x4*>(p) = v;
+  } else {
+    *reinterpret_cast<float4*>(p) = make_float4(x0, x1, x2, x3);
+  }
+}
+
+// grad_hidden[n][h] (+)= scale * sum_v G[n][v] W[v][h] over one vocabulary
+// chunk: A = W_c^T (h rows), B = G (n rows), K = the chunk.
 template <int D, int W>
 __global__ __launch_bounds__(W * 64) void bwd_dh_kernel(DhArgs a) {
   typedef typename Elem<D>::T T;
   constexpr int EB = Elem<D>::bytes, WI = Gemm<W>::WI, WJ = Gemm<W>::WJ;
+  const TileAB ti = grouped_tile(blockIdx.x, gridDim.x, a.n_h_tiles, a.n_tok_tiles);
+  if (!ti.valid) return;
+  const int ht = ti.a, tt = ti.b;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = Gemm<W>::wm(wave), wn = Gemm<W>::wn(wave), r32 = lane & 31, half = lane >> 5;
-  const TileAB ti = grouped_tile(blockIdx.x, gridDim.x, a.n_tok_tiles, a.n_h_tiles);
-  if (!ti.valid) return;
-  const int tt = ti.a, ht = ti.b;
   const int64_t n0 = (int64_t)tt * TILE, h0 = (int64_t)ht * TILE;
   const int64_t kb = (int64_t)a.cvpad * EB;
-  Panel A{a.G + n0 * kb, kb, (int)min<int64_t>(TILE, a.N - n0), kb};
-  Panel B{a.WcT + h0 * kb, kb, (int)min<int64_t>(TILE, a.H - h0), kb};
+  Panel A{a.WcT + h0 * kb, kb, (int)min<int64_t>(TILE, a.H - h0), kb};
+  Panel B{a.G + n0 * kb, kb, (int)min<int64_t>(TILE, a.N - n0), kb};
   f32x16_t acc[WI][WJ];
   gemm_nt_tile<D, W>(acc, A, B);
   const float scale = a.scale[0];
   T* out = reinterpret_cast<T*>(a.out);
 #pragma unroll
-  for (int i = 0; i < WI; ++i)
+  for (int j = 0; j < WJ; ++j) {
+    const int64_t n = n0 + wn * 32 * WJ + 32 * j + r32;
+    if (n >= a.N) continue;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t n = n0 + wm * 32 * WI + 32 * i + acc_row(r, half);
-      if (n >= a.N) continue;
+    for (int i = 0; i < WI; ++i)
 #pragma unroll
-      for (int j = 0; j < WJ; ++j) {
-        const int64_t h = h0 + wn * 32 * WJ + 32 * j + r32;
+      for (int g = 0; g < 4; ++g) {
+        const int64_t h = h0 + wm * 32 * WI + 32 * i + 8 * g + 4 * half;  // H % 4 == 0: all four in range
         if (h >= a.H) continue;
         const int64_t idx = n * a.H + h;
-        const float val = acc[i][j][r] * scale;
-        if (a.first && a.last) out[idx] = from_f32<D>(val);
-        else if (a.first) a.acc[idx] = val;
-        else if (a.last) out[idx] = from_f32<D>(a.acc[idx] + val);
-        else a.acc[idx] = a.acc[idx] + val;
+        float v0 = acc[i][j][4 * g] * scale, v1 = acc[i][j][4 * g + 1] * scale;
+        float v2 = acc[i][j][4 * g + 2] * scale, v3 = acc[i][j][4 * g + 3] * scale;
+        if (!a.first) {
+          const float4 o = *reinterpret_cast<const float4*>(a.acc + idx);
+          v0 = o.x + v0;
+          v1 = o.y + v1;
+          v2 = o.z + v2;
+          v3 = o.w + v3;
+        }
+        if (a.last) store4<D>(out + idx, v0, v1, v2, v3);
+        else *reinterpret_cast<float4*>(a.acc + idx) = make_float4(v0, v1, v2, v3);
       }
-    }
+  }
 }
 
+// grad_weight[v][h] = scale * sum_n G[n][v] H[n][h] for one vocabulary chunk:
+// A = G^T (v rows), B = H^T (h rows), K = tokens.  Here the hidden index runs
+// along the lanes: a store instruction writes two 64-byte row pieces, which
+// the memory system takes better than the 32 scattered 16-byte pieces of the
+// transposed arrangement.
 template <int D, int W>
 __global__ __launch_bounds__(W * 64) void bwd_dw_kernel(DwArgs a) {
   typedef typename Elem<D>::T T;
   constexpr int EB = Elem<D>::bytes, WI = Gemm<W>::WI, WJ = Gemm<W>::WJ;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = Gemm<W>::wm(wave), wn = Gemm<W>::wn(wave), r32 = lane & 31, half = lane >> 5;
   const TileAB ti = grouped_tile(blockIdx.x, gridDim.x, a.n_h_tiles, a.n_voc_tiles);
   if (!ti.valid) return;
   const int ht = ti.a, vt = ti.b;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = Gemm<W>::wm(wave), wn = Gemm<W>::wn(wave), r32 = lane & 31, half = lane >> 5;
   const int64_t v0 = (int64_t)vt * TILE, h0 = (int64_t)ht * TILE;
   const int64_t kb = (int64_t)a.npad * EB;
   Panel A{a.GT + v0 * kb, kb, (int)min<int64_t>(TILE, a.cv - v0), kb};
@@ -687,7 +738,7 @@ hipError_t launch_forward_tiles(int dtype, bool metrics, bool bias, bool cap, co
 }
 
 hipError_t launch_forward_combine(bool metrics, const CombineArgs& a, hipStream_t st) {
-  const dim3 grid(blocks_for(a.N, 256)), block(256);
+  const dim3 grid(blocks_for(a.N, 32)), block(256);
   if (metrics) hipLaunchKernelGGL(fwd_combine_kernel<true>, grid, block, 0, st, a);
   else hipLaunchKernelGGL(fwd_combine_kernel<false>, grid, block, 0, st, a);
   return hipGetLastError();
@@ -733,7 +784,7 @@ hipError_t launch_backward_g(int dtype, bool bias, bool cap, const GArgs& a, hip
 }
 
 hipError_t launch_backward_dh(int dtype, const DhArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)grouped_grid(a.n_tok_tiles, a.n_h_tiles)), block(kContractWaves * 64);
+  const dim3 grid((unsigned)grouped_grid(a.n_h_tiles, a.n_tok_tiles)), block(kContractWaves * 64);
   switch (dtype) {
     case DT_F32: hipLaunchKernelGGL((bwd_dh_kernel<DT_F32, kContractWaves>), grid, block, 0, st, a); break;
     case DT_F16: hipLaunchKernelGGL((bwd_dh_kernel<DT_F16, kContractWaves>), grid, block, 0, st, a); break;
