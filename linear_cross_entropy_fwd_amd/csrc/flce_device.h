@@ -4,9 +4,9 @@
 // the two gradient contractions share.
 //
 // Tile geometry: a workgroup owns a 256 x 256 fp32 output tile, split over
-// its 4 or 8 wave64s as blocks of the 32x32 MFMA (Gemm<W> below); operands
-// stream through a four-stage LDS ring fed by direct global-to-LDS copies
-// (see gemm_nt_tile below).
+// its 8 wave64s as blocks of the 16x16 MFMA (Gemm<W> below); operands stream
+// through two LDS stage buffers fed by direct global-to-LDS copies (see
+// gemm_nt_tile below).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -18,7 +18,7 @@ enum Dt : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 template <int D> struct Elem;
 template <> struct Elem<DT_F32> { typedef float T; static constexpr int bytes = 4; };
@@ -35,30 +35,32 @@ constexpr int TILE = 256;          // output tile edge (rows and columns)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
-// One 16-byte fragment pair -> MFMA update of one 32x32 block.
-//  16-bit types: lane l holds row (l&31), k = 8*(l>>5) .. +7 of the 16-deep slab.
-//  fp32: the same 16 bytes are 4 consecutive k of the 8-deep slab; four
-//  32x32x2 MFMAs contract (k, k+4) pairs so every k is used exactly once.
-template <int D> __device__ __forceinline__ void mfma_frag(f32x16_t& acc, uint4 a, uint4 b);
+// One 16-byte fragment pair -> MFMA update of one 16x16 block.
+//  16-bit types: lane l holds row (l&15), k = 8*(l>>4) .. +7 of the 32-deep
+//  slab (v_mfma_f32_16x16x32).
+//  fp32: the same 16 bytes are k = 4*(l>>4) .. +3 of the 16-deep slab; four
+//  16x16x4 MFMAs each take element c of every lane (k = 4*(l>>4) + c), so
+//  together they use every k of the slab exactly once.
+template <int D> __device__ __forceinline__ void mfma_frag(f32x4_t& acc, uint4 a, uint4 b);
 
-template <> __device__ __forceinline__ void mfma_frag<DT_BF16>(f32x16_t& acc, uint4 a, uint4 b) {
-  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+template <> __device__ __forceinline__ void mfma_frag<DT_BF16>(f32x4_t& acc, uint4 a, uint4 b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                 __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
 }
-template <> __device__ __forceinline__ void mfma_frag<DT_F16>(f32x16_t& acc, uint4 a, uint4 b) {
-  acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+template <> __device__ __forceinline__ void mfma_frag<DT_F16>(f32x4_t& acc, uint4 a, uint4 b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
                                                __builtin_bit_cast(f16x8_t, b), acc, 0, 0, 0);
 }
-template <> __device__ __forceinline__ void mfma_frag<DT_F32>(f32x16_t& acc, uint4 a, uint4 b) {
-  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+template <> __device__ __forceinline__ void mfma_frag<DT_F32>(f32x4_t& acc, uint4 a, uint4 b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
 }
 
-// Output element (row, col) of accumulator register r of a 32x32 block, for lane l:
-//   col = l & 31,  row = 8*(r>>2) + 4*(l>>5) + (r&3).
-__device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
+// Output element (row, col) of accumulator register e (0..3) of a 16x16
+// block, for lane l:  col = l & 15,  row = 4*(l>>4) + e.
+__device__ __forceinline__ int acc_row(int e, int lane) { return 4 * (lane >> 4) + e; }
 
 // An operand panel: 256 rows starting at `base` (rows past `rows` re-read the
 // last valid row; their results are never stored), `ld` bytes apart,
@@ -77,16 +79,15 @@ struct Panel {
 // 256 rows of A and of B (64 KB); one copy instruction moves 8 whole rows
 // (1 KB).  Rows are stored 128 bytes apart with the eight 16-byte chunks of
 // row r at positions c ^ ((r>>1)&7), so that the 16 lanes that read one
-// chunk of 16 consecutive rows hit all 64 LDS banks once.  A stage has four
-// 32-byte slabs; the fragments of the next slab are read while the MFMAs of
-// the current one run, and the one barrier per stage sits before the last
-// slab's MFMAs.
+// chunk of 16 consecutive rows hit all 64 LDS banks once.  A stage has two
+// 64-byte slabs; the fragments of the next slab are read while the MFMAs of
+// the current one run, and the one barrier per stage sits between them.
 
 constexpr int ROWB = 128;                // K bytes per row per stage
 constexpr int OPB = TILE * ROWB;         // one operand, one stage: 32 KB
 constexpr int STB = 2 * OPB;             // A + B: 64 KB
 constexpr int NSTAGES = 2;               // 128 KB of LDS
-constexpr int NSLABS = ROWB / 32;        // 32-byte MFMA slabs per stage
+constexpr int NSLABS = ROWB / 64;        // 64-byte MFMA slabs per stage
 
 __shared__ __attribute__((aligned(1024))) char g_stage0[STB];
 __shared__ __attribute__((aligned(1024))) char g_stage1[STB];
@@ -145,27 +146,29 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // Wave layout of a workgroup of W waves over the 256 x 256 tile: a GM x GN
-// grid of wave tiles of WI x WJ 32x32 blocks.
-//   W = 4: one wave per SIMD, 128 x 128 per wave (256 accumulator registers).
-//   W = 8: two waves per SIMD, 128 x 64 per wave (128 accumulator registers);
-//          while one wave of a SIMD waits (a copy being issued, a barrier),
-//          the other keeps the MFMA unit busy.
+// grid of wave tiles of WI x WJ 16x16 blocks.  W = 8: two waves per SIMD,
+// 128 x 64 per wave (128 accumulator registers); while one wave of a SIMD
+// waits (a copy being issued, a barrier), the other keeps the MFMA unit busy.
+// (One wave per SIMD with 128 x 128 each ran at half the rate.)
 template <int W> struct Geo;
-template <> struct Geo<4> { static constexpr int WI = 4, WJ = 4; };
-template <> struct Geo<8> { static constexpr int WI = 4, WJ = 2; };
+template <> struct Geo<8> { static constexpr int WI = 8, WJ = 4; };
 template <int W> struct Gemm {
   static constexpr int WI = Geo<W>::WI, WJ = Geo<W>::WJ;
-  static constexpr int GN = TILE / (32 * WJ);       // wave columns
+  static constexpr int GN = TILE / (16 * WJ);       // wave columns
   static constexpr int NBLK = 2 * TILE / 8;         // 8-row copy blocks per stage (64)
   static constexpr int NCOP = NBLK / W;             // copies per thread per stage
-  static constexpr int NREAD = WI + WJ;             // fragment reads per slab
   static constexpr int NSTEP = WI * WJ;             // MFMAs per slab
   __device__ static int wm(int wave) { return wave / GN; }
   __device__ static int wn(int wave) { return wave % GN; }
 };
 
+// Fragment registers.  The MFMAs of a slab run row block by row block (A
+// fragment i with every B fragment, then i+1), so A fragment i is dead after
+// its last MFMA and is refilled in place with the next slab's; the B
+// fragments are used until the end of the slab and alternate between two
+// sets (slab 0 of a stage uses b[0], slab 1 b[1]).
 template <int W> struct Frags {
-  uint4 a[Gemm<W>::WI], b[Gemm<W>::WJ];
+  uint4 a[Gemm<W>::WI], b[2][Gemm<W>::WJ];
 };
 
 // Per-thread global byte offsets of its copies.  Block b = 0..63 of a stage
@@ -240,57 +243,54 @@ __device__ __forceinline__ void zero_tail(const Panel& A, int kt, int t) {
 
 // Byte offsets, inside a stage buffer, of this lane's fragment chunk of each
 // slab for its first A and first B row block.  The lane reads rows
-// r0 + 32*i + (l&31): they differ by multiples of 32, so the swizzle term
-// ((row>>1)&7) = ((l&31)>>1)&7 is the same for all its blocks, which then sit
-// 32*ROWB bytes apart (an immediate offset).
+// r0 + 16*i + (l&15): they differ by multiples of 16, so the swizzle term
+// ((row>>1)&7) = ((l&15)>>1)&7 is the same for all its blocks, which then sit
+// 16*ROWB bytes apart (an immediate offset).
 struct FragBase {
   uint32_t a[NSLABS], b[NSLABS];
 };
 
 template <int W>
 __device__ __forceinline__ void frag_base(FragBase& fb, int wave, int lane) {
-  const int r32 = lane & 31, half = lane >> 5, x = (r32 >> 1) & 7;
-  const int ra = Gemm<W>::wm(wave) * 32 * Gemm<W>::WI, rb = Gemm<W>::wn(wave) * 32 * Gemm<W>::WJ;
+  const int r16 = lane & 15, q = lane >> 4, x = (r16 >> 1) & 7;
+  const int ra = Gemm<W>::wm(wave) * 16 * Gemm<W>::WI, rb = Gemm<W>::wn(wave) * 16 * Gemm<W>::WJ;
 #pragma unroll
   for (int s = 0; s < NSLABS; ++s) {
-    const uint32_t coff = (uint32_t)(((2 * s + half) ^ x) << 4);
-    fb.a[s] = (uint32_t)((ra + r32) * ROWB) + coff;
-    fb.b[s] = (uint32_t)(OPB + (rb + r32) * ROWB) + coff;
+    const uint32_t coff = (uint32_t)(((4 * s + q) ^ x) << 4);
+    fb.a[s] = (uint32_t)((ra + r16) * ROWB) + coff;
+    fb.b[s] = (uint32_t)(OPB + (rb + r16) * ROWB) + coff;
   }
 }
 
-// Fragment P (0..WI-1: A row block P; WI..: B row block P-WI) of slab SL of
-// buffer S: lane (l&31, l>>5) reads chunk 2*SL + (l>>5) of its row.
-template <int W, int S, int SL, int P>
-__device__ __forceinline__ void frag_read_one(Frags<W>& f, const FragBase& fb) {
-  constexpr int WI = Gemm<W>::WI;
-  const char* base = stage_buf<S>();
-  if constexpr (P < WI)
-    f.a[P] = *reinterpret_cast<const uint4*>(base + fb.a[SL] + P * 32 * ROWB);
-  else
-    f.b[P - WI] = *reinterpret_cast<const uint4*>(base + fb.b[SL] + (P - WI) * 32 * ROWB);
+// A fragment I / B fragment J of slab SL of buffer S: lane (l&15, l>>4)
+// reads chunk 4*SL + (l>>4) of its row.  B fragments of slab SL go to set SL.
+template <int W, int S, int SL, int I>
+__device__ __forceinline__ void read_a(Frags<W>& f, const FragBase& fb) {
+  f.a[I] = *reinterpret_cast<const uint4*>(stage_buf<S>() + fb.a[SL] + I * 16 * ROWB);
+}
+template <int W, int S, int SL, int J>
+__device__ __forceinline__ void read_b(Frags<W>& f, const FragBase& fb) {
+  f.b[SL][J] = *reinterpret_cast<const uint4*>(stage_buf<S>() + fb.b[SL] + J * 16 * ROWB);
 }
 
-// The order in which a slab's fragments are read: A0, B0 .. B(WJ-1), A1 ..
-// A(WI-1) -- the MFMAs run row block by row block (A0 with every B, then
-// A1, ...), so each fragment is read in the order it is first needed.
-template <int W> __device__ __forceinline__ constexpr int read_order(int k) {
-  constexpr int WI = Gemm<W>::WI, WJ = Gemm<W>::WJ;
-  return k == 0 ? 0 : (k <= WJ ? WI + k - 1 : k - WJ);
+// Item k of M spread evenly over N steps goes after step floor(k*N/M).
+__device__ __forceinline__ constexpr int spread(int s, int M, int N) {
+  const int k = (s * M + N - 1) / N;
+  return (k < M && (k * N) / M == s) ? k : -1;
 }
 
-// Which read (0..NREAD-1) and which copy (0..NCOP-1) follow MFMA step s of
-// a slab; -1 for none.  With copies (COPIES, every copy of a stage in one
-// slab): W = 4: 16 steps, a copy after each, a read after every even one;
-// W = 8: 8 steps, a copy after each, reads after steps 0..5.  Without:
-// W = 4 reads after even steps; W = 8 after 0 1 3 4 6 7.
-template <int W, bool COPIES> __device__ __forceinline__ constexpr int step_read(int s) {
-  if constexpr (W == 4) return (s & 1) == 0 ? s / 2 : -1;
-  else if constexpr (COPIES) return s < 6 ? s : -1;
-  else return s == 2 || s == 5 ? -1 : (s < 2 ? s : (s < 5 ? s - 1 : s - 2));
+// What follows MFMA step s = (i, j) of a slab (i = s / WJ, j = s % WJ):
+//  - after the last MFMA of row block i (j = WJ-1): the next slab's A fragment i;
+//  - the next slab's B fragment k after step floor(k * NSTEP / WJ) + 1, so
+//    that each lands at least NSTEP - NSTEP/WJ steps before its first use;
+//  - with COPIES (every copy of a stage in one slab): copy k after step
+//    floor(k * NSTEP / NCOP) + 2.
+template <int W> __device__ __forceinline__ constexpr int step_read_b(int s) {
+  return s >= 1 ? spread(s - 1, Gemm<W>::WJ, Gemm<W>::NSTEP) : -1;
 }
 template <int W, bool COPIES> __device__ __forceinline__ constexpr int step_copy(int s) {
-  return COPIES ? s : -1;
+  if constexpr (!COPIES) return -1;
+  else return s >= 2 ? spread(s - 2, Gemm<W>::NCOP, Gemm<W>::NSTEP) : -1;
 }
 
 // Copy issuers for slab_phase.  PlainCopy: a stage that lies wholly inside K
@@ -322,61 +322,59 @@ struct NoCopy {
   template <int S, int I> __device__ __forceinline__ void issue() const {}
 };
 
-// One slab's WI x WJ MFMAs on `fm`, with the NREAD fragment reads of slab RSL
-// of buffer RS (into `fr`) and, if COPIES, the phase's NCOP/2 copies (C0 ..
-// into buffer CS) placed between them as step_read / step_copy say: a wave
-// issues in order and would otherwise stall its MFMAs behind a burst of
-// copies or reads.
-template <int D, int W, int RS, int RSL, int CS, int C0, bool COPIES, int STEP = 0, class Copy>
-__device__ __forceinline__ void slab_phase(f32x16_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], const Frags<W>& fm,
-                                           Frags<W>& fr, const FragBase& fb, const Copy& cp) {
+// One slab's WI x WJ MFMAs on A fragments f.a and B fragments f.b[SC], with
+// the fragment reads of the next slab (slab RSL of buffer RS) and, if COPIES,
+// the stage's NCOP copies (into buffer CS) placed between them as the step
+// functions above say: a wave issues in order and would otherwise stall its
+// MFMAs behind a burst of copies or reads.
+template <int D, int W, int SC, int RS, int RSL, int CS, bool COPIES, int STEP = 0, class Copy>
+__device__ __forceinline__ void slab_phase(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], Frags<W>& f,
+                                           const FragBase& fb, const Copy& cp) {
   constexpr int WJ = Gemm<W>::WJ;
   if constexpr (STEP < Gemm<W>::NSTEP) {
     constexpr int I = STEP / WJ, J = STEP % WJ;
-    mfma_frag<D>(acc[I][J], fm.a[I], fm.b[J]);
-    constexpr int rd = step_read<W, COPIES>(STEP), cpy = step_copy<W, COPIES>(STEP);
-    if constexpr (rd >= 0) frag_read_one<W, RS, RSL, read_order<W>(rd)>(fr, fb);
-    if constexpr (cpy >= 0) cp.template issue<CS, C0 + cpy>();
+    mfma_frag<D>(acc[I][J], f.a[I], f.b[SC][J]);
+    if constexpr (J == WJ - 1) read_a<W, RS, RSL, I>(f, fb);
+    constexpr int rb = step_read_b<W>(STEP), cpy = step_copy<W, COPIES>(STEP);
+    if constexpr (rb >= 0) read_b<W, RS, RSL, rb>(f, fb);
+    if constexpr (cpy >= 0) cp.template issue<CS, cpy>();
     sched_fence();
-    slab_phase<D, W, RS, RSL, CS, C0, COPIES, STEP + 1>(acc, fm, fr, fb, cp);
+    slab_phase<D, W, SC, RS, RSL, CS, COPIES, STEP + 1>(acc, f, fb, cp);
   }
 }
 
-// All NREAD fragments of slab SL of buffer S, in read_order (so that every
-// path into a stage has the same reads pending).
+// Every fragment of slab SL of buffer S.
 template <int W, int S, int SL, int K = 0>
 __device__ __forceinline__ void frag_read(Frags<W>& f, const FragBase& fb) {
-  if constexpr (K < Gemm<W>::NREAD) {
-    frag_read_one<W, S, SL, read_order<W>(K)>(f, fb);
+  if constexpr (K < Gemm<W>::WI) {
+    read_a<W, S, SL, K>(f, fb);
+    frag_read<W, S, SL, K + 1>(f, fb);
+  } else if constexpr (K < Gemm<W>::WI + Gemm<W>::WJ) {
+    read_b<W, S, SL, K - Gemm<W>::WI>(f, fb);
     frag_read<W, S, SL, K + 1>(f, fb);
   }
 }
 
-// Stage kt from buffer S (f0 holds its slab 0; stage kt+1's copies are in
+// Stage kt from buffer S (f holds its slab 0; stage kt+1's copies are in
 // flight into S^1):
 //   slab 0: MFMAs | reads of slab 1
-//   slab 1: MFMAs | reads of slab 2
-//   slab 2: MFMAs | reads of slab 3
 //   wait for every copy (stage kt+1), zero its ragged tail, barrier: every
 //   wave is done reading buffer S and stage kt+1 is visible
-//   slab 3: MFMAs | reads of slab 0 of stage kt+1 (S^1) | every copy of
-//   stage kt+2 (into S), as early as the buffer allows, so that each copy
-//   has at least three slabs of MFMAs to land
+//   slab 1: MFMAs | reads of slab 0 of stage kt+1 (S^1) | every copy of
+//   stage kt+2 (into S), as early as the buffer allows
 template <int D, int W, int S, class C>
-__device__ __forceinline__ void kstage(f32x16_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], Frags<W>& f0, Frags<W>& f1,
+__device__ __forceinline__ void kstage(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], Frags<W>& f,
                                        const FragBase& fb, const C& c, bool zero_next, const Panel& A, int kt,
                                        int t) {
-  static_assert(NSLABS == 4, "the schedule below assumes four slabs");
+  static_assert(NSLABS == 2, "the schedule below assumes two slabs");
   constexpr int SN = S ^ 1;
   const NoCopy nc;
   sched_fence();
-  slab_phase<D, W, S, 1, SN, 0, false>(acc, f0, f1, fb, nc);
-  slab_phase<D, W, S, 2, SN, 0, false>(acc, f1, f0, fb, nc);
-  slab_phase<D, W, S, 3, SN, 0, false>(acc, f0, f1, fb, nc);
+  slab_phase<D, W, 0, S, 1, SN, false>(acc, f, fb, nc);
   wait_vmcnt<0>();
   if (zero_next) zero_tail<W, SN>(A, kt + 1, t);
   lds_barrier();
-  slab_phase<D, W, SN, 0, S, 0, true>(acc, f1, f0, fb, c);
+  slab_phase<D, W, 1, SN, 0, S, true>(acc, f, fb, c);
 }
 
 // Both operands' copies of one stage: copy I < NCOP/2 is of A, the rest of B.
@@ -389,32 +387,32 @@ template <int W> struct PlainCopy2 {
 };
 
 template <int D, int W, int S>
-__device__ __forceinline__ void kstage_plain(f32x16_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], Frags<W>& f0,
-                                             Frags<W>& f1, const CopyPlan<W>& cp, const FragBase& fb,
+__device__ __forceinline__ void kstage_plain(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], Frags<W>& f,
+                                             const CopyPlan<W>& cp, const FragBase& fb,
                                              const Panel& A, const Panel& B, int kt, uint32_t wave_lds,
                                              int t) {
   const int64_t k0 = (int64_t)(kt + 2) * ROWB;
   const PlainCopy2<W> c{{cp, uniform_ptr(A.base + k0), wave_lds}, {cp, uniform_ptr(B.base + k0), wave_lds}};
-  kstage<D, W, S>(acc, f0, f1, fb, c, false, A, kt, t);
+  kstage<D, W, S>(acc, f, fb, c, false, A, kt, t);
 }
 
 // Past the end of K a copy re-reads the last stage (never used), so the
 // schedule still has no branches.
 template <int D, int W, int S>
-__device__ __forceinline__ void kstage_edge(f32x16_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], Frags<W>& f0,
-                                            Frags<W>& f1, const CopyPlan<W>& cp, const FragBase& fb,
+__device__ __forceinline__ void kstage_edge(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], Frags<W>& f,
+                                            const CopyPlan<W>& cp, const FragBase& fb,
                                             const Panel& A, const Panel& B, int kt, int nk, bool ragged,
                                             int t) {
   const int k2 = min(kt + 2, nk - 1);
   const EdgeCopy<W> c{cp, A, B, k2, ragged && k2 == nk - 1, t};
-  kstage<D, W, S>(acc, f0, f1, fb, c, ragged && kt + 1 == nk - 1, A, kt, t);
+  kstage<D, W, S>(acc, f, fb, c, ragged && kt + 1 == nk - 1, A, kt, t);
 }
 
 // acc[i][j] (this wave's WI x WJ blocks) = A_panel . B_panel^T over all of K.
 // Uses the stage buffers; returns after a barrier with no copy in flight, so
 // the caller may reuse them (e.g. g_stage0) right away.
 template <int D, int W>
-__device__ __forceinline__ void gemm_nt_tile(f32x16_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], const Panel& A,
+__device__ __forceinline__ void gemm_nt_tile(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], const Panel& A,
                                              const Panel& B) {
   static_assert(NSTAGES == 2, "the loops below alternate two buffers");
   constexpr int H = Gemm<W>::NCOP / 2;
@@ -424,7 +422,7 @@ __device__ __forceinline__ void gemm_nt_tile(f32x16_t (&acc)[Gemm<W>::WI][Gemm<W
 #pragma unroll
     for (int j = 0; j < Gemm<W>::WJ; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
   const int nk = (int)((A.kbytes + ROWB - 1) / ROWB);
   const bool ragged = (A.kbytes % ROWB) != 0;
   const uint32_t wave_lds = (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024u;
@@ -439,8 +437,8 @@ __device__ __forceinline__ void gemm_nt_tile(f32x16_t (&acc)[Gemm<W>::WI][Gemm<W
   lds_barrier();
   FragBase fb;
   frag_base<W>(fb, wave, lane);
-  Frags<W> f0, f1;
-  frag_read<W, 0, 0>(f0, fb);
+  Frags<W> f;
+  frag_read<W, 0, 0>(f, fb);
   // Pairs of plain stages (every copy they issue lies inside K and is not
   // ragged: kt+1+2 <= last_plain), then pairs of edge stages.  A loop header
   // with only two predecessors keeps the waitcnt pass from falling back to a
@@ -448,12 +446,12 @@ __device__ __forceinline__ void gemm_nt_tile(f32x16_t (&acc)[Gemm<W>::WI][Gemm<W
   const int last_plain = ragged ? nk - 2 : nk - 1;
   int kt = 0;
   for (; kt + 3 <= last_plain; kt += 2) {
-    kstage_plain<D, W, 0>(acc, f0, f1, cp, fb, A, B, kt, wave_lds, t);
-    kstage_plain<D, W, 1>(acc, f0, f1, cp, fb, A, B, kt + 1, wave_lds, t);
+    kstage_plain<D, W, 0>(acc, f, cp, fb, A, B, kt, wave_lds, t);
+    kstage_plain<D, W, 1>(acc, f, cp, fb, A, B, kt + 1, wave_lds, t);
   }
   for (; kt < nk; kt += 2) {
-    kstage_edge<D, W, 0>(acc, f0, f1, cp, fb, A, B, kt, nk, ragged, t);
-    if (kt + 1 < nk) kstage_edge<D, W, 1>(acc, f0, f1, cp, fb, A, B, kt + 1, nk, ragged, t);
+    kstage_edge<D, W, 0>(acc, f, cp, fb, A, B, kt, nk, ragged, t);
+    if (kt + 1 < nk) kstage_edge<D, W, 1>(acc, f, cp, fb, A, B, kt + 1, nk, ragged, t);
   }
   wait_vmcnt<0>();
   lds_barrier();

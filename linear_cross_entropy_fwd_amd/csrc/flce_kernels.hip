@@ -76,36 +76,56 @@ __device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2)
   }
 }
 
+// Bias of the rows this lane holds: row vq + 16*i + e of accumulator
+// element [i][.][e] (vq = the wave's first row + 4*(lane>>4)).
 template <int D, bool BIAS, int WI>
-__device__ __forceinline__ void load_bias_rows(float (&bv)[WI][16], const char* bias, int vbase,
-                                               int64_t V, int half) {
+__device__ __forceinline__ void load_bias_rows(float (&bv)[WI][4], const char* bias, int vq, int64_t V) {
   typedef typename Elem<D>::T T;
   const T* b = reinterpret_cast<const T*>(bias);
 #pragma unroll
   for (int i = 0; i < WI; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int e = 0; e < 4; ++e) {
       if (BIAS) {
-        int64_t v = (int64_t)vbase + 32 * i + acc_row(r, half);
+        int64_t v = (int64_t)vq + 16 * i + e;
         v = v < V ? v : V - 1;
-        bv[i][r] = to_f32<D>(b[v]);
+        bv[i][e] = to_f32<D>(b[v]);
       } else {
-        bv[i][r] = 0.f;
+        bv[i][e] = 0.f;
       }
     }
 }
 
+// The four lanes l, l^16, l^32, l^48 hold the same accumulator column over
+// disjoint rows.  Butterfly reductions over them: every lane ends with the
+// same bits (each step adds or compares a pair in either order).
+__device__ __forceinline__ float col_max4(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float col_sum4(float x) {
+  x = x + __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
+__device__ __forceinline__ int col_min4(int x) {
+  x = min(x, __shfl_xor(x, 16));
+  return min(x, __shfl_xor(x, 32));
+}
+
 // ------------------------------------------------------------------ forward tiles
 
-// 28 KB next to the 128 KB stage ring: 7 values x WJ token columns per thread.
-__shared__ float g_fwd_state[7 * 4 * 256];
+// Per-column online state between vocabulary tiles, in LDS so that it does
+// not occupy registers across the GEMM: 7 values x WJ column blocks x 16
+// columns per wave (14 KB next to the 128 KB stage buffers).
+__shared__ float g_fwd_state[7 * 4 * 8 * 16];
 
 template <int D, bool METRICS, bool BIAS, bool CAP, int W>
 __global__ __launch_bounds__(W * 64) void fwd_tiles_kernel(FwdArgs a) {
-  constexpr int EB = Elem<D>::bytes, WI = Gemm<W>::WI, WJ = Gemm<W>::WJ, NT = W * 64;
-  static_assert(7 * WJ * NT <= 7 * 4 * 256, "online state does not fit g_fwd_state");
+  constexpr int EB = Elem<D>::bytes, WI = Gemm<W>::WI, WJ = Gemm<W>::WJ;
+  static_assert(7 * WJ * W * 16 <= 7 * 4 * 8 * 16, "online state does not fit g_fwd_state");
+  static_assert(Gemm<W>::GN * 16 * WJ == TILE && 2 * 16 * WI == TILE, "two wave rows share each column");
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = Gemm<W>::wm(wave), wn = Gemm<W>::wn(wave), r32 = lane & 31, half = lane >> 5;
+  const int wm = Gemm<W>::wm(wave), wn = Gemm<W>::wn(wave), c16 = lane & 15, q = lane >> 4;
 
   const TileAB ti = grouped_tile(blockIdx.x, gridDim.x, a.n_tok_tiles, a.n_splits);
   if (!ti.valid) return;
@@ -117,54 +137,59 @@ __global__ __launch_bounds__(W * 64) void fwd_tiles_kernel(FwdArgs a) {
 
   Panel B{a.hidden + n0 * rowb, rowb, (int)min<int64_t>(TILE, a.N - n0), rowb};
 
-  // Per-row online state, kept in this thread's own LDS slots between vocab
-  // tiles so that it does not occupy registers across the GEMM.  Slot k of
-  // token column j: 0 m, 1 S, 2 U, 3 z_target, 4 argmax value, 5 argmax id,
-  // 6 target id (-1 when the row is ignored or its target is out of range).
-  float* st = g_fwd_state + t;
-#define FST(k, j) st[((k) * WJ + (j)) * NT]
+  // Slot k of column block j of this lane's column: 0 m, 1 S, 2 U,
+  // 3 z_target, 4 argmax value, 5 argmax id, 6 target id (-1 when the row is
+  // ignored or its target is out of range).  The four lanes of a column hold
+  // the same m, S, U and argmax (they are merged every tile); z_target is
+  // written only by the lane that holds the target's row.
+  float* st = g_fwd_state + wave * 16 + c16;
+#define FST(k, j) st[((k) * WJ + (j)) * (W * 16)]
+  if (q == 0) {
 #pragma unroll
-  for (int j = 0; j < WJ; ++j) {
-    const int64_t n = n0 + wn * 32 * WJ + 32 * j + r32;
-    const int64_t tv = n < a.N ? a.targets[n] : a.ignore_index;
-    FST(0, j) = -INFINITY;
-    FST(1, j) = 0.f;
-    FST(2, j) = 0.f;
-    FST(3, j) = 0.f;
-    FST(4, j) = -INFINITY;
-    FST(5, j) = __int_as_float(0x7fffffff);
-    FST(6, j) = __int_as_float((tv != a.ignore_index && tv >= 0 && tv < a.V) ? (int)tv : -1);
+    for (int j = 0; j < WJ; ++j) {
+      const int64_t n = n0 + wn * 16 * WJ + 16 * j + c16;
+      const int64_t tv = n < a.N ? a.targets[n] : a.ignore_index;
+      FST(0, j) = -INFINITY;
+      FST(1, j) = 0.f;
+      FST(2, j) = 0.f;
+      FST(3, j) = 0.f;
+      FST(4, j) = -INFINITY;
+      FST(5, j) = __int_as_float(0x7fffffff);
+      FST(6, j) = __int_as_float((tv != a.ignore_index && tv >= 0 && tv < a.V) ? (int)tv : -1);
+    }
   }
 
-  f32x16_t acc[WI][WJ];
+  f32x4_t acc[WI][WJ];
   for (int vt = vt_begin; vt < vt_end; ++vt) {
     const int64_t v0 = (int64_t)vt * TILE;
     Panel A{a.weight + v0 * rowb, rowb, (int)min<int64_t>(TILE, a.V - v0), rowb};
     gemm_nt_tile<D, W>(acc, A, B);
 
     const int to = opaque_int(t);
-    const int half = (to >> 5) & 1;
-    const int vbase = (int)v0 + Gemm<W>::wm(to >> 6) * 32 * WI;
+    const int qo = (to >> 4) & 3;
+    const int vbase = (int)v0 + Gemm<W>::wm(to >> 6) * 16 * WI;  // this wave's first row
+    const int vq = vbase + 4 * qo;                                // row of acc[i][.][e]: vq + 16 i + e
     const bool ragged = v0 + TILE > a.V;
-    float bv[WI][16];
-    load_bias_rows<D, BIAS, WI>(bv, a.bias, vbase, a.V, half);
+    float bv[WI][4];
+    load_bias_rows<D, BIAS, WI>(bv, a.bias, vq, a.V);
 
 #pragma unroll
     for (int j = 0; j < WJ; ++j) {
-      float z[WI][16];
-      float zmax = -INFINITY;
+      float z[WI][4];
+      float zl = -INFINITY;
 #pragma unroll
       for (int i = 0; i < WI; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float y = acc[i][j][r];
-          if (BIAS) y = y + bv[i][r];
+        for (int e = 0; e < 4; ++e) {
+          float y = acc[i][j][e];
+          if (BIAS) y = y + bv[i][e];
           y = a.s * y;
           if (CAP) y = soft_cap(y, a.cap, a.inv_cap);
-          if (ragged && vbase + 32 * i + acc_row(r, half) >= a.V) y = -INFINITY;
-          z[i][r] = y;
-          zmax = fmaxf(zmax, y);
+          if (ragged && vq + 16 * i + e >= a.V) y = -INFINITY;
+          z[i][e] = y;
+          zl = fmaxf(zl, y);
         }
+      const float zmax = col_max4(zl);
       const float mold = FST(0, j);
       const float mnew = fmaxf(mold, zmax);
       if (mnew != -INFINITY) {
@@ -172,45 +197,52 @@ __global__ __launch_bounds__(W * 64) void fwd_tiles_kernel(FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < WI; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float d = z[i][r] - mnew;
-            const float e = fast_exp2(d * LOG2E);
-            sum = sum + e;
-            if (METRICS) usum = fmaf(e, fmaxf(d, -1e30f), usum);
+          for (int e = 0; e < 4; ++e) {
+            const float d = z[i][e] - mnew;
+            const float ex = fast_exp2(d * LOG2E);
+            sum = sum + ex;
+            if (METRICS) usum = fmaf(ex, fmaxf(d, -1e30f), usum);
           }
-        if (mold == -INFINITY) {
-          FST(1, j) = sum;
-          if (METRICS) FST(2, j) = usum;
-        } else {
-          const float dm = mold - mnew;
-          const float al = fast_exp2(dm * LOG2E);
-          const float Sold = FST(1, j);
-          if (METRICS) FST(2, j) = fmaf(al, fmaf(dm, Sold, FST(2, j)), usum);
-          FST(1, j) = fmaf(Sold, al, sum);
+        sum = col_sum4(sum);
+        if (METRICS) usum = col_sum4(usum);
+        if (q == 0) {
+          if (mold == -INFINITY) {
+            FST(1, j) = sum;
+            if (METRICS) FST(2, j) = usum;
+          } else {
+            const float dm = mold - mnew;
+            const float al = fast_exp2(dm * LOG2E);
+            const float Sold = FST(1, j);
+            if (METRICS) FST(2, j) = fmaf(al, fmaf(dm, Sold, FST(2, j)), usum);
+            FST(1, j) = fmaf(Sold, al, sum);
+          }
+          FST(0, j) = mnew;
         }
-        FST(0, j) = mnew;
       }
       if (METRICS && zmax > FST(4, j)) {
         int idx = 0x7fffffff;
 #pragma unroll
         for (int i = 0; i < WI; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int v = vbase + 32 * i + acc_row(r, half);
-            if (z[i][r] == zmax && v < idx) idx = v;
+          for (int e = 0; e < 4; ++e) {
+            const int v = vq + 16 * i + e;
+            if (z[i][e] == zmax && v < idx) idx = v;
           }
-        FST(4, j) = zmax;
-        FST(5, j) = __int_as_float(idx);
+        idx = col_min4(idx);
+        if (q == 0) {
+          FST(4, j) = zmax;
+          FST(5, j) = __int_as_float(idx);
+        }
       }
       const int local = __float_as_int(FST(6, j)) - vbase;
-      if (local >= 0 && local < 32 * WI && ((local >> 2) & 1) == half) {
-        const int ti = local >> 5, tr = ((local & 31) >> 3) * 4 + (local & 3);
+      if (local >= 0 && local < 16 * WI && ((local & 15) >> 2) == qo) {
+        const int ti = local >> 4, te = local & 3;
         float zv = 0.f;
 #pragma unroll
         for (int i = 0; i < WI; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (i == ti && r == tr) zv = z[i][r];
+          for (int e = 0; e < 4; ++e)
+            if (i == ti && e == te) zv = z[i][e];
         FST(3, j) = zv;
       }
     }
@@ -229,25 +261,12 @@ __global__ __launch_bounds__(W * 64) void fwd_tiles_kernel(FwdArgs a) {
   }
 #undef FST
 
-  // Lanes l and l^32 hold the same token columns over disjoint vocab rows.
-#pragma unroll
-  for (int j = 0; j < WJ; ++j) {
-    const float m2 = __shfl_xor(m[j], 32), S2 = __shfl_xor(S[j], 32);
-    const float U2 = __shfl_xor(U[j], 32), z2 = __shfl_xor(zt[j], 32);
-    const float av2 = __shfl_xor(av[j], 32);
-    const int ai2 = __shfl_xor(ai[j], 32);
-    lse_merge<METRICS>(m[j], S[j], U[j], m2, S2, U2);
-    zt[j] = zt[j] + z2;  // the non-owner holds +0
-    if (METRICS) argmax_merge(av[j], ai[j], av2, ai2);
-  }
-
-  // Waves wm=0 and wm=1 hold the same tokens over disjoint vocab rows.
+  // Waves wm=0 and wm=1 hold the same columns over disjoint vocab rows.
   float* xs = reinterpret_cast<float*>(g_stage0);  // free after gemm_nt_tile returns
-  static_assert(TILE / (32 * WI) == 2, "two wave rows share each token column");
-  if (wm == 1 && half == 0) {
+  if (wm == 1 && q == 0) {
 #pragma unroll
     for (int j = 0; j < WJ; ++j) {
-      const int tok = wn * 32 * WJ + 32 * j + r32;
+      const int tok = wn * 16 * WJ + 16 * j + c16;
       xs[0 * TILE + tok] = m[j];
       xs[1 * TILE + tok] = S[j];
       xs[2 * TILE + tok] = U[j];
@@ -257,12 +276,12 @@ __global__ __launch_bounds__(W * 64) void fwd_tiles_kernel(FwdArgs a) {
     }
   }
   __syncthreads();
-  if (wm == 0 && half == 0) {
+  if (wm == 0 && q == 0) {
 #pragma unroll
     for (int j = 0; j < WJ; ++j) {
-      const int tok = wn * 32 * WJ + 32 * j + r32;
+      const int tok = wn * 16 * WJ + 16 * j + c16;
       lse_merge<METRICS>(m[j], S[j], U[j], xs[0 * TILE + tok], xs[1 * TILE + tok], xs[2 * TILE + tok]);
-      zt[j] = zt[j] + xs[3 * TILE + tok];
+      zt[j] = zt[j] + xs[3 * TILE + tok];  // the non-owner holds +0
       if (METRICS) argmax_merge(av[j], ai[j], xs[4 * TILE + tok], __float_as_int(xs[5 * TILE + tok]));
       const int64_t n = n0 + tok;
       if (n < a.N) {
@@ -459,13 +478,54 @@ __global__ void fill_zero_kernel(uint8_t* p, int64_t bytes) {
 
 // ------------------------------------------------------------------ backward G (recompute)
 
+// A 256 x 256 tile of 16-bit values, row r's 16-byte chunk c stored at chunk
+// position c ^ (r & 31) (rows 512 bytes apart), rows 0..127 in g_stage0 and
+// 128..255 in g_stage1 (both free once gemm_nt_tile has returned).  Lanes
+// writing 8 bytes of 16 different rows then spread over the LDS banks, and a
+// row can be read back as 16-byte pieces and stored fully coalesced.
+__device__ __forceinline__ char* tile16_addr(int row, int col) {
+  char* buf = row < 128 ? g_stage0 : g_stage1;
+  const int r = row & 127;
+  return buf + r * 512 + ((((col >> 3) ^ (r & 31))) << 4) + (col & 7) * 2;
+}
+
+// Four consecutive columns col..col+3 (col % 4 == 0) of row `row`.
+template <int D>
+__device__ __forceinline__ void tile16_put4(int row, int col, float x0, float x1, float x2, float x3) {
+  typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+  u16x4 v;
+  v[0] = __builtin_bit_cast(uint16_t, from_f32<D>(x0));
+  v[1] = __builtin_bit_cast(uint16_t, from_f32<D>(x1));
+  v[2] = __builtin_bit_cast(uint16_t, from_f32<D>(x2));
+  v[3] = __builtin_bit_cast(uint16_t, from_f32<D>(x3));
+  *reinterpret_cast<u16x4*>(tile16_addr(row, col)) = v;
+}
+
+// Stores the staged tile: row r, columns c0.. go to dst + r * ld (elements),
+// for r < rows and chunk columns below cols (a multiple of 8).  Callers put a
+// barrier between the last tile16_put4 and this.
+template <int NT>
+__device__ __forceinline__ void tile16_store(uint16_t* dst, int64_t ld, int rows, int cols, int t) {
+#pragma unroll 4
+  for (int k = t; k < TILE * 32; k += NT) {
+    const int r = k >> 5, c = k & 31;
+    if (r < rows && 8 * c < cols) {
+      const uint4 v = *reinterpret_cast<const uint4*>(tile16_addr(r, 8 * c));
+      *reinterpret_cast<uint4*>(dst + (int64_t)r * ld + 8 * c) = v;
+    }
+  }
+}
+
+// Recompute one (token tile, vocabulary tile) of the chunk and write
+// G = coef * (softmax - onehot) * dz/draw (and G^T, grad_bias partials).
+// A = weight rows (vocabulary on the MFMA row axis), B = hidden rows.
 template <int D, bool BIAS, bool CAP, int W>
 __global__ __launch_bounds__(W * 64) void bwd_g_kernel(GArgs a) {
   typedef typename Elem<D>::T T;
   constexpr int EB = Elem<D>::bytes, WI = Gemm<W>::WI, WJ = Gemm<W>::WJ;
   static_assert(Gemm<W>::GN == kBiasParts || W != kRecomputeWaves, "grad_bias partials per token tile");
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = Gemm<W>::wm(wave), wn = Gemm<W>::wn(wave), r32 = lane & 31, half = lane >> 5;
+  const int wm = Gemm<W>::wm(wave), wn = Gemm<W>::wn(wave), c16 = lane & 15, q = lane >> 4;
 
   const TileAB ti = grouped_tile(blockIdx.x, gridDim.x, a.n_tok_tiles, a.n_voc_tiles);
   if (!ti.valid) return;
@@ -477,7 +537,7 @@ __global__ __launch_bounds__(W * 64) void bwd_g_kernel(GArgs a) {
 
   Panel A{a.weight + v0 * rowb, rowb, (int)min<int64_t>(TILE, a.V - v0), rowb};
   Panel B{a.hidden + n0 * rowb, rowb, (int)min<int64_t>(TILE, a.N - n0), rowb};
-  f32x16_t acc[WI][WJ];
+  f32x4_t acc[WI][WJ];
   gemm_nt_tile<D, W>(acc, A, B);
 
   float lse[WJ], coef[WJ];
@@ -485,7 +545,7 @@ __global__ __launch_bounds__(W * 64) void bwd_g_kernel(GArgs a) {
   bool live[WJ];
 #pragma unroll
   for (int j = 0; j < WJ; ++j) {
-    const int64_t n = n0 + wn * 32 * WJ + 32 * j + r32;
+    const int64_t n = n0 + wn * 16 * WJ + 16 * j + c16;
     live[j] = false;
     tgt[j] = -1;
     lse[j] = 0.f;
@@ -505,103 +565,100 @@ __global__ __launch_bounds__(W * 64) void bwd_g_kernel(GArgs a) {
     }
   }
 
-  const int vbase = (int)v0 + wm * 32 * WI;
-  float bv[WI][16];
-  load_bias_rows<D, BIAS, WI>(bv, a.bias, vbase, a.V, half);
+  const int vq = (int)v0 + wm * 16 * WI + 4 * q;  // row of acc[i][.][e]: vq + 16 i + e
+  float bv[WI][4];
+  load_bias_rows<D, BIAS, WI>(bv, a.bias, vq, a.V);
 #pragma unroll
   for (int i = 0; i < WI; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int v = vbase + 32 * i + acc_row(r, half);
+    for (int e = 0; e < 4; ++e) {
+      const int v = vq + 16 * i + e;
       const int vl = v - (int)a.c0;
       const bool vin = v < a.V && vl < a.cv;
 #pragma unroll
       for (int j = 0; j < WJ; ++j) {
-        float y = acc[i][j][r];
-        if (BIAS) y = y + bv[i][r];
+        float y = acc[i][j][e];
+        if (BIAS) y = y + bv[i][e];
         y = a.s * y;
         if (CAP) y = soft_cap(y, a.cap, a.inv_cap);
         const float p = fast_exp2((y - lse[j]) * LOG2E);
         float g = v == tgt[j] ? p - 1.f : p;
         if (CAP) {
-          const float q = y * a.inv_cap;
-          g = g * fmaf(-q, q, 1.f);
+          const float qc = y * a.inv_cap;
+          g = g * fmaf(-qc, qc, 1.f);
         }
         g = g * coef[j];
-        acc[i][j][r] = (vin && live[j]) ? g : 0.f;
+        acc[i][j][e] = (vin && live[j]) ? g : 0.f;
       }
     }
 
-  // G[n][vl] (row pitch cvpad): 4 consecutive ids per lane -> one vector store.
+  const int vlq = vl0 + wm * 16 * WI + 4 * q;  // chunk-local row of acc[i][.][e]: vlq + 16 i + e
+  // G[n][vl] (row pitch cvpad): 16-bit types through the LDS tile, fp32 directly.
   if (a.G) {
-    T* G = reinterpret_cast<T*>(a.G);
+    if constexpr (EB == 2) {
 #pragma unroll
-    for (int j = 0; j < WJ; ++j) {
-      const int64_t n = n0 + wn * 32 * WJ + 32 * j + r32;
-      if (n >= a.npad) continue;
+      for (int j = 0; j < WJ; ++j)
 #pragma unroll
-      for (int i = 0; i < WI; ++i)
+        for (int i = 0; i < WI; ++i)
+          tile16_put4<D>(wn * 16 * WJ + 16 * j + c16, wm * 16 * WI + 16 * i + 4 * q, acc[i][j][0], acc[i][j][1],
+                         acc[i][j][2], acc[i][j][3]);
+      __syncthreads();
+      tile16_store<W * 64>(reinterpret_cast<uint16_t*>(a.G) + n0 * a.cvpad + vl0, a.cvpad,
+                           (int)min<int64_t>(TILE, a.npad - n0), min(TILE, a.cvpad - vl0), t);
+    } else {
+      float* G = reinterpret_cast<float*>(a.G);
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int vl = vl0 + wm * 32 * WI + 32 * i + 8 * g4 + 4 * half;
-          if (vl >= a.cvpad) continue;
-          T* dst = G + n * a.cvpad + vl;
-          if constexpr (EB == 2) {
-            typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
-            u16x4 pk;
+      for (int j = 0; j < WJ; ++j) {
+        const int64_t n = n0 + wn * 16 * WJ + 16 * j + c16;
+        if (n >= a.npad) continue;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pk[e] = __builtin_bit_cast(uint16_t, from_f32<D>(acc[i][j][4 * g4 + e]));
-            *reinterpret_cast<u16x4*>(dst) = pk;
-          } else {
-            *reinterpret_cast<float4*>(dst) =
-                make_float4(acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2], acc[i][j][4 * g4 + 3]);
-          }
+        for (int i = 0; i < WI; ++i) {
+          const int vl = vlq + 16 * i;
+          if (vl < a.cvpad)
+            *reinterpret_cast<float4*>(G + n * a.cvpad + vl) =
+                make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
         }
+      }
     }
   }
-  // G^T[vl][n] (row pitch npad): lanes of a half-wave cover 32 consecutive tokens.
+  // G^T[vl][n] (row pitch npad): the 16 lanes of a row group cover 16 consecutive tokens.
   if (a.GT) {
     T* GT = reinterpret_cast<T*>(a.GT);
 #pragma unroll
     for (int i = 0; i < WI; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int vl = vl0 + wm * 32 * WI + 32 * i + acc_row(r, half);
+      for (int e = 0; e < 4; ++e) {
+        const int vl = vlq + 16 * i + e;
         if (vl >= a.cvpad) continue;
 #pragma unroll
         for (int j = 0; j < WJ; ++j) {
-          const int64_t n = n0 + wn * 32 * WJ + 32 * j + r32;
-          if (n < a.npad) GT[(int64_t)vl * a.npad + n] = from_f32<D>(acc[i][j][r]);
+          const int64_t n = n0 + wn * 16 * WJ + 16 * j + c16;
+          if (n < a.npad) GT[(int64_t)vl * a.npad + n] = from_f32<D>(acc[i][j][e]);
         }
       }
   }
-  // grad_bias partials: sum over this wave's 32*WJ tokens, per vocabulary id.
+  // grad_bias partials: sum over this wave's 16*WJ tokens, per vocabulary id.
   if (a.dbpart) {
 #pragma unroll
     for (int i = 0; i < WI; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float s = acc[i][0][r];
+      for (int e = 0; e < 4; ++e) {
+        float sb = acc[i][0][e];
 #pragma unroll
-        for (int j = 1; j < WJ; ++j) s = s + acc[i][j][r];
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 4);
-        s += __shfl_xor(s, 8);
-        s += __shfl_xor(s, 16);
-        const int v = vbase + 32 * i + acc_row(r, half);
+        for (int j = 1; j < WJ; ++j) sb = sb + acc[i][j][e];
+        sb += __shfl_xor(sb, 1);
+        sb += __shfl_xor(sb, 2);
+        sb += __shfl_xor(sb, 4);
+        sb += __shfl_xor(sb, 8);
+        const int v = vq + 16 * i + e;
         const int vl = v - (int)a.c0;
-        if (r32 == 0 && v < a.V && vl < a.cv) a.dbpart[(int64_t)(Gemm<W>::GN * tt + wn) * a.V + v] = s;
+        if (c16 == 0 && v < a.V && vl < a.cv) a.dbpart[(int64_t)(Gemm<W>::GN * tt + wn) * a.V + v] = sb;
       }
   }
 }
 
 // ------------------------------------------------------------------ backward contractions
 
-// grad_hidden puts H on the MFMA row axis, so that a lane's four consecutive
-// accumulator rows are four consecutive hidden indices of one output row: one
-// 16-byte access of the fp32 accumulator (8-byte store of 16-bit output) per
-// group.
 template <int D>
 __device__ __forceinline__ void store4(typename Elem<D>::T* p, float x0, float x1, float x2, float x3) {
   if constexpr (Elem<D>::bytes == 2) {
@@ -617,8 +674,12 @@ __device__ __forceinline__ void store4(typename Elem<D>::T* p, float x0, float x
   }
 }
 
+// Both contractions put H on the MFMA row axis, so that a lane's four
+// accumulator rows are four consecutive hidden indices of one output row.
+//
 // grad_hidden[n][h] (+)= scale * sum_v G[n][v] W[v][h] over one vocabulary
-// chunk: A = W_c^T (h rows), B = G (n rows), K = the chunk.
+// chunk: A = W_c^T (h rows), B = G (n rows), K = the chunk.  The fp32
+// accumulator is read and written 16 bytes per lane.
 template <int D, int W>
 __global__ __launch_bounds__(W * 64) void bwd_dh_kernel(DhArgs a) {
   typedef typename Elem<D>::T T;
@@ -627,46 +688,42 @@ __global__ __launch_bounds__(W * 64) void bwd_dh_kernel(DhArgs a) {
   if (!ti.valid) return;
   const int ht = ti.a, tt = ti.b;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = Gemm<W>::wm(wave), wn = Gemm<W>::wn(wave), r32 = lane & 31, half = lane >> 5;
+  const int wm = Gemm<W>::wm(wave), wn = Gemm<W>::wn(wave), c16 = lane & 15, q = lane >> 4;
   const int64_t n0 = (int64_t)tt * TILE, h0 = (int64_t)ht * TILE;
   const int64_t kb = (int64_t)a.cvpad * EB;
   Panel A{a.WcT + h0 * kb, kb, (int)min<int64_t>(TILE, a.H - h0), kb};
   Panel B{a.G + n0 * kb, kb, (int)min<int64_t>(TILE, a.N - n0), kb};
-  f32x16_t acc[WI][WJ];
+  f32x4_t acc[WI][WJ];
   gemm_nt_tile<D, W>(acc, A, B);
   const float scale = a.scale[0];
   T* out = reinterpret_cast<T*>(a.out);
 #pragma unroll
   for (int j = 0; j < WJ; ++j) {
-    const int64_t n = n0 + wn * 32 * WJ + 32 * j + r32;
+    const int64_t n = n0 + wn * 16 * WJ + 16 * j + c16;
     if (n >= a.N) continue;
 #pragma unroll
-    for (int i = 0; i < WI; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int64_t h = h0 + wm * 32 * WI + 32 * i + 8 * g + 4 * half;  // H % 4 == 0: all four in range
-        if (h >= a.H) continue;
-        const int64_t idx = n * a.H + h;
-        float v0 = acc[i][j][4 * g] * scale, v1 = acc[i][j][4 * g + 1] * scale;
-        float v2 = acc[i][j][4 * g + 2] * scale, v3 = acc[i][j][4 * g + 3] * scale;
-        if (!a.first) {
-          const float4 o = *reinterpret_cast<const float4*>(a.acc + idx);
-          v0 = o.x + v0;
-          v1 = o.y + v1;
-          v2 = o.z + v2;
-          v3 = o.w + v3;
-        }
-        if (a.last) store4<D>(out + idx, v0, v1, v2, v3);
-        else *reinterpret_cast<float4*>(a.acc + idx) = make_float4(v0, v1, v2, v3);
+    for (int i = 0; i < WI; ++i) {
+      const int64_t h = h0 + wm * 16 * WI + 16 * i + 4 * q;  // H % 4 == 0: all four in range
+      if (h >= a.H) continue;
+      const int64_t idx = n * a.H + h;
+      float v0 = acc[i][j][0] * scale, v1 = acc[i][j][1] * scale;
+      float v2 = acc[i][j][2] * scale, v3 = acc[i][j][3] * scale;
+      if (!a.first) {
+        const float4 o = *reinterpret_cast<const float4*>(a.acc + idx);
+        v0 = o.x + v0;
+        v1 = o.y + v1;
+        v2 = o.z + v2;
+        v3 = o.w + v3;
       }
+      if (a.last) store4<D>(out + idx, v0, v1, v2, v3);
+      else *reinterpret_cast<float4*>(a.acc + idx) = make_float4(v0, v1, v2, v3);
+    }
   }
 }
 
 // grad_weight[v][h] = scale * sum_n G[n][v] H[n][h] for one vocabulary chunk:
-// A = G^T (v rows), B = H^T (h rows), K = tokens.  Here the hidden index runs
-// along the lanes: a store instruction writes two 64-byte row pieces, which
-// the memory system takes better than the 32 scattered 16-byte pieces of the
-// transposed arrangement.
+// A = H^T (h rows), B = G^T (v rows), K = tokens.  16-bit results go through
+// the LDS tile and leave as whole 512-byte row pieces; fp32 directly.
 template <int D, int W>
 __global__ __launch_bounds__(W * 64) void bwd_dw_kernel(DwArgs a) {
   typedef typename Elem<D>::T T;
@@ -675,27 +732,39 @@ __global__ __launch_bounds__(W * 64) void bwd_dw_kernel(DwArgs a) {
   if (!ti.valid) return;
   const int ht = ti.a, vt = ti.b;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = Gemm<W>::wm(wave), wn = Gemm<W>::wn(wave), r32 = lane & 31, half = lane >> 5;
+  const int wm = Gemm<W>::wm(wave), wn = Gemm<W>::wn(wave), c16 = lane & 15, q = lane >> 4;
   const int64_t v0 = (int64_t)vt * TILE, h0 = (int64_t)ht * TILE;
   const int64_t kb = (int64_t)a.npad * EB;
-  Panel A{a.GT + v0 * kb, kb, (int)min<int64_t>(TILE, a.cv - v0), kb};
-  Panel B{a.HT + h0 * kb, kb, (int)min<int64_t>(TILE, a.H - h0), kb};
-  f32x16_t acc[WI][WJ];
+  Panel A{a.HT + h0 * kb, kb, (int)min<int64_t>(TILE, a.H - h0), kb};
+  Panel B{a.GT + v0 * kb, kb, (int)min<int64_t>(TILE, a.cv - v0), kb};
+  f32x4_t acc[WI][WJ];
   gemm_nt_tile<D, W>(acc, A, B);
   const float scale = a.scale[0];
-  T* out = reinterpret_cast<T*>(a.out);
+  if constexpr (EB == 2) {
 #pragma unroll
-  for (int i = 0; i < WI; ++i)
+    for (int j = 0; j < WJ; ++j)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t v = v0 + wm * 32 * WI + 32 * i + acc_row(r, half);
+      for (int i = 0; i < WI; ++i)
+        tile16_put4<D>(wn * 16 * WJ + 16 * j + c16, wm * 16 * WI + 16 * i + 4 * q, acc[i][j][0] * scale,
+                       acc[i][j][1] * scale, acc[i][j][2] * scale, acc[i][j][3] * scale);
+    __syncthreads();
+    tile16_store<W * 64>(reinterpret_cast<uint16_t*>(a.out) + v0 * a.H + h0, a.H,
+                         (int)min<int64_t>(TILE, a.cv - v0), (int)min<int64_t>(TILE, a.H - h0), t);
+  } else {
+    T* out = reinterpret_cast<T*>(a.out);
+#pragma unroll
+    for (int j = 0; j < WJ; ++j) {
+      const int64_t v = v0 + wn * 16 * WJ + 16 * j + c16;
       if (v >= a.cv) continue;
 #pragma unroll
-      for (int j = 0; j < WJ; ++j) {
-        const int64_t h = h0 + wn * 32 * WJ + 32 * j + r32;
-        if (h < a.H) out[v * a.H + h] = from_f32<D>(acc[i][j][r] * scale);
+      for (int i = 0; i < WI; ++i) {
+        const int64_t h = h0 + wm * 16 * WI + 16 * i + 4 * q;
+        if (h < a.H)
+          store4<D>(out + v * a.H + h, acc[i][j][0] * scale, acc[i][j][1] * scale, acc[i][j][2] * scale,
+                    acc[i][j][3] * scale);
       }
     }
+  }
 }
 
 template <int D>
