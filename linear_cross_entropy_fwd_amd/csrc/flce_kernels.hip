@@ -516,6 +516,40 @@ __device__ __forceinline__ void tile16_store(uint16_t* dst, int64_t ld, int rows
   }
 }
 
+// Stores the staged tile transposed: dst[c][r] (row pitch ld elements) for
+// tile row r < rows, column c < cols, from transposed LDS reads.  In a group
+// of 16 lanes, lane i reads row r0 + i/4, columns c0 + 4*(i%4) .. +3 (8
+// bytes); ds_read_b64_tr_b16 hands lane j the four values of column c0 + j
+// in rows r0 .. r0+3.  Two such reads give a lane 8 consecutive rows of one
+// column: a 16-byte piece of a dst row.  The four groups of a wave take
+// consecutive 8-row pieces of the same 16 columns, so a wave stores 16 dst
+// row pieces of 64 bytes.  Callers put a barrier between the last
+// tile16_put4 and this.
+__device__ __forceinline__ void tile16_store_t(uint16_t* dst, int64_t ld, int rows, int cols, int t) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const int w = t >> 6, gw = (t >> 4) & 3, i = t & 15;
+#pragma unroll 2
+  for (int it = 0; it < 16; ++it) {
+    const int cb = w + 8 * (it & 1);        // 16-column block (tile column = dst row)
+    const int rb = 4 * (it >> 1) + gw;      // 8-row block (tile row = dst column)
+    const int r0 = 8 * rb, c0 = 16 * cb;
+    const int rr = r0 + (i >> 2), cc = c0 + 4 * (i & 3);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<__attribute__((address_space(3))) s16x4*>(lds_addr(tile16_addr(rr, cc))));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<__attribute__((address_space(3))) s16x4*>(lds_addr(tile16_addr(rr + 4, cc))));
+    const int c = c0 + i;
+    if (c < cols && r0 < rows) {
+      uint4 v;
+      v.x = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+      v.y = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+      v.z = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+      v.w = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+      *reinterpret_cast<uint4*>(dst + (int64_t)c * ld + r0) = v;
+    }
+  }
+}
+
 // Recompute one (token tile, vocabulary tile) of the chunk and write
 // G = coef * (softmax - onehot) * dz/draw (and G^T, grad_bias partials).
 // A = weight rows (vocabulary on the MFMA row axis), B = hidden rows.
@@ -593,9 +627,10 @@ __global__ __launch_bounds__(W * 64) void bwd_g_kernel(GArgs a) {
     }
 
   const int vlq = vl0 + wm * 16 * WI + 4 * q;  // chunk-local row of acc[i][.][e]: vlq + 16 i + e
-  // G[n][vl] (row pitch cvpad): 16-bit types through the LDS tile, fp32 directly.
-  if (a.G) {
-    if constexpr (EB == 2) {
+  // 16-bit types: the tile goes to LDS as [n][v] and leaves as G rows and,
+  // read transposed, as G^T rows.
+  if constexpr (EB == 2) {
+    if (a.G || a.GT) {
 #pragma unroll
       for (int j = 0; j < WJ; ++j)
 #pragma unroll
@@ -603,9 +638,14 @@ __global__ __launch_bounds__(W * 64) void bwd_g_kernel(GArgs a) {
           tile16_put4<D>(wn * 16 * WJ + 16 * j + c16, wm * 16 * WI + 16 * i + 4 * q, acc[i][j][0], acc[i][j][1],
                          acc[i][j][2], acc[i][j][3]);
       __syncthreads();
-      tile16_store<W * 64>(reinterpret_cast<uint16_t*>(a.G) + n0 * a.cvpad + vl0, a.cvpad,
-                           (int)min<int64_t>(TILE, a.npad - n0), min(TILE, a.cvpad - vl0), t);
-    } else {
+      const int rows = (int)min<int64_t>(TILE, a.npad - n0), cols = min(TILE, a.cvpad - vl0);
+      if (a.G) tile16_store<W * 64>(reinterpret_cast<uint16_t*>(a.G) + n0 * a.cvpad + vl0, a.cvpad, rows, cols, t);
+      if (a.GT) tile16_store_t(reinterpret_cast<uint16_t*>(a.GT) + (int64_t)vl0 * a.npad + n0, a.npad, rows, cols, t);
+    }
+  }
+  // fp32: G[n][vl] (row pitch cvpad) and G^T[vl][n] (row pitch npad) directly.
+  if constexpr (EB == 4) {
+    if (a.G) {
       float* G = reinterpret_cast<float*>(a.G);
 #pragma unroll
       for (int j = 0; j < WJ; ++j) {
@@ -621,8 +661,7 @@ __global__ __launch_bounds__(W * 64) void bwd_g_kernel(GArgs a) {
       }
     }
   }
-  // G^T[vl][n] (row pitch npad): the 16 lanes of a row group cover 16 consecutive tokens.
-  if (a.GT) {
+  if (EB == 4 && a.GT) {
     T* GT = reinterpret_cast<T*>(a.GT);
 #pragma unroll
     for (int i = 0; i < WI; ++i)
