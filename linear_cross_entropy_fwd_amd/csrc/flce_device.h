@@ -281,16 +281,16 @@ __device__ __forceinline__ constexpr int spread(int s, int M, int N) {
 
 // What follows MFMA step s = (i, j) of a slab (i = s / WJ, j = s % WJ):
 //  - after the last MFMA of row block i (j = WJ-1): the next slab's A fragment i;
-//  - the next slab's B fragment k after step floor(k * NSTEP / WJ) + 1, so
-//    that each lands at least NSTEP - NSTEP/WJ steps before its first use;
+//  - the next slab's B fragment k after step 2k (early: the next slab needs
+//    all of them in its first WJ steps);
 //  - with COPIES (every copy of a stage in one slab): copy k after step
-//    floor(k * NSTEP / NCOP) + 2.
+//    floor(k * NSTEP / NCOP), the first right after the barrier.
 template <int W> __device__ __forceinline__ constexpr int step_read_b(int s) {
-  return s >= 1 ? spread(s - 1, Gemm<W>::WJ, Gemm<W>::NSTEP) : -1;
+  return (s & 1) == 0 && s < 2 * Gemm<W>::WJ ? s / 2 : -1;
 }
 template <int W, bool COPIES> __device__ __forceinline__ constexpr int step_copy(int s) {
   if constexpr (!COPIES) return -1;
-  else return s >= 2 ? spread(s - 2, Gemm<W>::NCOP, Gemm<W>::NSTEP) : -1;
+  else return spread(s, Gemm<W>::NCOP, Gemm<W>::NSTEP);
 }
 
 // Copy issuers for slab_phase.  PlainCopy: a stage that lies wholly inside K
