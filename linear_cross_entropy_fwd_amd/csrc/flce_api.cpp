@@ -34,7 +34,11 @@ flce_status_t hip_fail(hipError_t e, const char* what) {
 
 constexpr int64_t kTile = 256;
 constexpr int64_t kAlign = 256;
-constexpr int64_t kDefaultChunk = 8192;
+// 48 vocabulary tiles: with 16 token tiles (4096 tokens) the recompute and
+// grad_weight grids are three full rounds of 256 workgroups, and the fp32
+// grad_hidden accumulator is re-read 11 times at V = 128256 instead of 16
+// (measured 0.45 ms faster than 8192 there).
+constexpr int64_t kDefaultChunk = 12288;
 constexpr int kMaxSplits = 64;
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -113,7 +117,16 @@ BwdLayout bwd_layout(const flce_problem_t& p) {
   BwdLayout L{};
   const int64_t N = p.n_tokens, H = p.hidden, V = p.vocab;
   const int eb = elem_bytes(p.dtype);
-  L.chunk = std::min<int64_t>(p.bwd_vocab_chunk > 0 ? p.bwd_vocab_chunk : kDefaultChunk, round_up(V, kTile));
+  if (p.bwd_vocab_chunk > 0) {
+    L.chunk = p.bwd_vocab_chunk;
+  } else {
+    // kDefaultChunk, or a quarter of V if that is smaller (at least a tile).
+    // It depends on V only, so that a row's gradient does not depend on how
+    // many rows share the call (the chunking fixes grad_hidden's summation
+    // order); with N >= H the chunk buffers then stay below an N x V buffer.
+    L.chunk = std::max<int64_t>(kTile, std::min<int64_t>(kDefaultChunk, V / 4 / kTile * kTile));
+  }
+  L.chunk = std::min<int64_t>(L.chunk, round_up(V, kTile));
   L.n_chunks = (int)cdiv(V, L.chunk);
   L.npad = round_up(std::max<int64_t>(N, 1), 64);
   L.cvpad_max = round_up(std::min(L.chunk, V), 64);

@@ -125,8 +125,9 @@ def test_workspace_sizes_scale_and_never_hold_n_by_v():
             assert 0 < fwd < nv_bytes or n * v < 1 << 20
             # the largest single backward buffer is a (N x chunk) gradient slab, far below N x V
             assert bwd < nv_bytes or n * v < 1 << 20
+    # default plan at the head shape: the chunk buffers stay well under an N x V buffer
     big = make_problem(4096, 4096, 128256, BF16)
-    assert _abi.flce_backward_workspace_size(big) < 400e6
+    assert _abi.flce_backward_workspace_size(big) < 0.4 * 4096 * 128256 * 2
 
 
 def test_plan_overrides_change_workspace():
