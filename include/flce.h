@@ -107,7 +107,9 @@ flce_status_t flce_forward(const flce_problem_t* p, const void* hidden, const vo
  *               MEAN/SUM, [N] for NONE; NULL means 1.
  *   grad_hidden (N,H), grad_weight (V,H), grad_bias (V): outputs, each may
  *               be NULL when not wanted (grad_bias requires has_bias).  They
- *               are overwritten, not accumulated into. */
+ *               are overwritten, not accumulated into.
+ * FLCE_ERR_UNSUPPORTED when n_tokens or the vocabulary chunk times
+ * sizeof(dtype) reaches 16 MiB (the operand tiles use 32-bit offsets). */
 flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const void* weight,
                             const int64_t* targets, const void* bias, const float* lse,
                             const float* grad_loss, void* grad_hidden, void* grad_weight,

@@ -107,6 +107,8 @@ FwdLayout fwd_layout(const flce_problem_t& p) {
 
 // ---------------------------------------------------------------- backward plan
 
+constexpr int64_t kMaxPanelPitch = int64_t(1) << 24;  // bytes
+
 struct BwdLayout {
   int64_t chunk, npad, cvpad_max;
   int n_chunks, n_tok_tiles, n_h_tiles;
@@ -274,6 +276,11 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
   if ((bias && !aligned(bias, (uintptr_t)eb)) || (grad_bias && !aligned(grad_bias, (uintptr_t)eb)))
     return fail(FLCE_ERR_INVALID_ARGUMENT, "bias / grad_bias misaligned");
   const BwdLayout L = bwd_layout(*p);
+  // The GEMM tiles read their operand panels through 32-bit buffer offsets:
+  // 256 row pitches (tokens or chunk ids times the element size) stay below 4 GiB.
+  if (L.npad * eb >= kMaxPanelPitch || L.cvpad_max * eb >= kMaxPanelPitch)
+    return fail(FLCE_ERR_UNSUPPORTED, "backward needs n_tokens and the vocabulary chunk times sizeof(dtype) "
+                "below 16 MiB (n_tokens=%lld, chunk=%lld)", (long long)N, (long long)L.chunk);
   s = check_workspace(workspace, workspace_bytes, L.total);
   if (s != FLCE_OK) return s;
 
@@ -306,7 +313,10 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
     const int64_t c0 = (int64_t)c * L.chunk;
     const int cv = (int)std::min<int64_t>(L.chunk, V - c0);
     const int cvpad = (int)round_up(cv, 64);
-    if (want_dh) {
+    // 16-bit types with at least 4 token tiles: the recompute kernel writes
+    // W_c^T as a side job; otherwise the transpose kernel does.
+    const bool fused_wct = want_dh && eb == 2 && L.n_tok_tiles >= 4;
+    if (want_dh && !fused_wct) {
       flce::TransposeArgs ta{reinterpret_cast<const char*>(weight) + c0 * H * eb, wct, cv, H, H, cvpad};
       if ((e = flce::launch_transpose(p->dtype, ta, st)) != hipSuccess) return hip_fail(e, "transpose kernel");
     }
@@ -319,6 +329,7 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
     ga.grad_rows = p->reduction == FLCE_NONE ? grad_loss : nullptr;
     ga.G = want_dh ? g : nullptr;
     ga.GT = want_dw ? gt : nullptr;
+    ga.WcT = fused_wct ? wct : nullptr;
     ga.dbpart = want_db ? db : nullptr;
     ga.N = N;
     ga.H = H;

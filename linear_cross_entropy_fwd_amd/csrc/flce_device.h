@@ -62,9 +62,11 @@ template <> __device__ __forceinline__ void mfma_frag<DT_F32>(f32x4_t& acc, uint
 // block, for lane l:  col = l & 15,  row = 4*(l>>4) + e.
 __device__ __forceinline__ int acc_row(int e, int lane) { return 4 * (lane >> 4) + e; }
 
-// An operand panel: 256 rows starting at `base` (rows past `rows` re-read the
-// last valid row; their results are never stored), `ld` bytes apart,
-// `kbytes` bytes of K (a multiple of 16; a ragged last stage reads zeros).
+// An operand panel: 256 rows starting at `base`, `ld` bytes apart, `kbytes`
+// bytes of K (a multiple of 16).  Only rows < `rows` and bytes < kbytes of
+// them are read from memory: reads past the panel's last valid byte return
+// zeros, K past kbytes is zeroed in LDS, and results of rows past `rows` are
+// never stored.
 struct Panel {
   const char* base;
   int64_t ld;
@@ -74,8 +76,8 @@ struct Panel {
 
 // ---------------------------------------------------------------------------
 // Two-stage operand pipeline.  Global memory is copied straight into LDS
-// (global_load_lds_dwordx4, 16 bytes per lane) one K-stage ahead of use into
-// two buffers.  A stage is 128 bytes of K (one cache line per row) for all
+// (buffer_load_dwordx4 ... lds, 16 bytes per lane) one K-stage ahead of use
+// into two buffers.  A stage is 128 bytes of K (one cache line per row) for all
 // 256 rows of A and of B (64 KB); one copy instruction moves 8 whole rows
 // (1 KB).  Rows are stored 128 bytes apart with the eight 16-byte chunks of
 // row r at positions c ^ ((r>>1)&7), so that the 16 lanes that read one
@@ -103,15 +105,19 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-// One wave-wide copy of 16 bytes per lane from global memory into LDS: lane l
-// writes LDS bytes [lds + 16*l, +16).  Issued through inline asm so that only
-// the pipeline's explicit vmcnt waits order it (the compiler would otherwise
-// wait for every outstanding copy before any LDS read of a stage buffer).
-// `gbase` and `lds` are wave-uniform; `voff` is the lane's byte offset.
-__device__ __forceinline__ void lds_copy16(const char* gbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+
+// One wave-wide copy of 16 bytes per lane from a buffer into LDS: lane l
+// writes LDS bytes [lds + 16*l, +16) with the 16 bytes at byte offset `voff`
+// of the buffer `rsrc`, or zeros where voff lies past its num_records (the
+// range check that makes clamping unnecessary).  Issued through inline asm
+// so that only the pipeline's explicit vmcnt waits order it (the compiler
+// would otherwise wait for every outstanding copy before any LDS read of a
+// stage buffer).  `rsrc` and `lds` are wave-uniform.
+__device__ __forceinline__ void lds_copy16(const i32x4_t& rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "v"(voff), "s"(gbase), "s"(lds)
+               : "v"(voff), "s"(rsrc), "s"(lds)
                : "memory");
 }
 
@@ -171,13 +177,30 @@ template <int W> struct Frags {
   uint4 a[Gemm<W>::WI], b[2][Gemm<W>::WJ];
 };
 
-// Per-thread global byte offsets of its copies.  Block b = 0..63 of a stage
-// is operand b>>5, rows (b&31)*8 .. +8.  Copy i of wave w is block w + W*i
-// (copies 0 .. NCOP/2-1 are of operand A, the rest of B).  Lane L covers row
-// (b&31)*8 + L/8 (clamped to the panel) and LDS chunk position L&7, which
-// holds global chunk (L&7) ^ ((row>>1)&7) of that row.
+// Raw buffer resource (stride 0) over a panel's valid bytes, rows 0 ..
+// rows-1 up to kbytes in the last one; everything in it is wave-uniform.
+// The host keeps 256 row pitches below 2^32 bytes.
+__device__ __forceinline__ i32x4_t panel_rsrc(const Panel& p) {
+  const uint64_t u = (uint64_t)(uintptr_t)p.base;
+  const int64_t extent = (int64_t)(p.rows - 1) * p.ld + p.kbytes;
+  i32x4_t r;
+  r[0] = (int32_t)__builtin_amdgcn_readfirstlane((uint32_t)u);
+  r[1] = (int32_t)(__builtin_amdgcn_readfirstlane((uint32_t)(u >> 32)) & 0xFFFFu);
+  r[2] = (int32_t)__builtin_amdgcn_readfirstlane((uint32_t)extent);
+  r[3] = 0x00020000;  // gfx9 data format word: 32-bit, no swizzle
+  return r;
+}
+
+// The copies of a stage.  Block b = 0..63 of a stage is operand b>>5, rows
+// (b&31)*8 .. +8.  Copy i of wave w is block w + W*i (copies 0 .. NCOP/2-1
+// are of operand A, the rest of B), so copy i of an operand covers rows
+// 64*i + 8*w + L/8 for lane L: its offset is the lane's first one plus
+// 64*i row pitches.  Lane L fills LDS chunk position L&7 of its row, which
+// holds global chunk (L&7) ^ ((row>>1)&7) -- the same for every i.
 template <int W> struct CopyPlan {
-  uint32_t off[Gemm<W>::NCOP];
+  i32x4_t ra, rb;   // buffer resources of A and B
+  uint32_t oa, ob;  // the lane's byte offset in copy 0 of A / of B
+  uint32_t sa, sb;  // 64 row pitches of A / of B (wave-uniform)
 };
 
 template <int W> __device__ __forceinline__ constexpr int copy_block(int i, int wave) { return wave + W * i; }
@@ -187,43 +210,37 @@ __device__ __forceinline__ int copy_chunk(int row, int L) { return (L & 7) ^ ((r
 template <int W>
 __device__ __forceinline__ void copy_plan(CopyPlan<W>& cp, const Panel& A, const Panel& B, int t) {
   const int wave = t >> 6, L = t & 63;
-#pragma unroll
-  for (int i = 0; i < Gemm<W>::NCOP; ++i) {
-    const int blk = copy_block<W>(i, wave);
-    const Panel& p = blk < 32 ? A : B;
-    int row = copy_row(blk, L);
-    const int c = copy_chunk(row, L);
-    row = row < p.rows ? row : p.rows - 1;
-    cp.off[i] = (uint32_t)(row * p.ld) + (uint32_t)(c * 16);
+  const int row = copy_row(copy_block<W>(0, wave), L);
+  const uint32_t c16 = (uint32_t)(copy_chunk(row, L) * 16);
+  cp.ra = panel_rsrc(A);
+  cp.rb = panel_rsrc(B);
+  cp.oa = (uint32_t)(row * A.ld) + c16;
+  cp.ob = (uint32_t)(row * B.ld) + c16;
+  cp.sa = __builtin_amdgcn_readfirstlane((uint32_t)(64 * A.ld));
+  cp.sb = __builtin_amdgcn_readfirstlane((uint32_t)(64 * B.ld));
+}
+
+// Copy I of the stage at K byte offset k0 into buffer S.  Stages past K (the
+// pipeline runs two ahead) and rows past the panel read zeros.
+template <int W> struct StageCopy {
+  const CopyPlan<W>& cp;
+  uint32_t k0;        // wave-uniform
+  uint32_t wave_lds;  // wave * 1024 (wave-uniform)
+  template <int S, int I> __device__ __forceinline__ void issue() const {
+    constexpr int H = Gemm<W>::NCOP / 2;
+    constexpr bool OPA = I < H;
+    constexpr uint32_t ii = OPA ? I : I - H;
+    const uint32_t soff = k0 + ii * (OPA ? cp.sa : cp.sb);
+    lds_copy16(OPA ? cp.ra : cp.rb, (OPA ? cp.oa : cp.ob) + soff,
+               lds_addr(stage_buf<S>() + W * I * 1024) + wave_lds);
   }
-}
+};
 
-// Copy I of stage kc into buffer S.  `masked` (ragged last stage only): a
-// chunk past K is read from the row's last valid 16 bytes instead (the offset
-// stays non-negative, so the address stays inside the row) and zeroed after
-// it lands.  The choice is a select, not a branch.
-template <int W, int S, int I>
-__device__ __forceinline__ void copy_one_any(const CopyPlan<W>& cp, const Panel& A, const Panel& B, int kc,
-                                            bool masked, int t) {
-  const int wave = t >> 6, L = t & 63;
-  const int64_t k0 = (int64_t)kc * ROWB;
-  constexpr bool OPA = I < Gemm<W>::NCOP / 2;
-  const Panel& p = OPA ? A : B;
-  const int blk = copy_block<W>(I, wave);
-  const int c = copy_chunk(copy_row(blk, L), L);
-  const uint32_t off = (masked && k0 + c * 16 >= p.kbytes)
-                           ? cp.off[I] - (uint32_t)(c * 16) + (uint32_t)(p.kbytes - 16 - k0)
-                           : cp.off[I];
-  const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(stage_buf<S>() + blk * 1024));
-  lds_copy16(uniform_ptr(p.base + k0), off, dst);
-}
-
-template <int W, int S, int I0, int I1>
-__device__ __forceinline__ void copy_range(const CopyPlan<W>& cp, const Panel& A, const Panel& B, int kt,
-                                           int nk, bool ragged, int t) {
-  if constexpr (I0 < I1) {
-    copy_one_any<W, S, I0>(cp, A, B, kt, ragged && kt == nk - 1, t);
-    copy_range<W, S, I0 + 1, I1>(cp, A, B, kt, nk, ragged, t);
+template <int W, int S, int I = 0>
+__device__ __forceinline__ void copy_stage(const StageCopy<W>& c) {
+  if constexpr (I < Gemm<W>::NCOP) {
+    c.template issue<S, I>();
+    copy_stage<W, S, I + 1>(c);
   }
 }
 
@@ -293,33 +310,16 @@ template <int W, bool COPIES> __device__ __forceinline__ constexpr int step_copy
   else return spread(s, Gemm<W>::NCOP, Gemm<W>::NSTEP);
 }
 
-// Copy issuers for slab_phase.  PlainCopy: a stage that lies wholly inside K
-// (no clamp, no mask); everything but the lane's fixed offset cp.off[I] is
-// scalar (the stage's global base and the LDS destination in m0).
-template <int W> struct PlainCopy {
-  const CopyPlan<W>& cp;
-  const char* base;   // operand base + the copied stage's K offset (wave-uniform)
-  uint32_t wave_lds;  // wave * 1024 (wave-uniform)
-  template <int S, int I> __device__ __forceinline__ void issue() const {
-    lds_copy16(base, cp.off[I], lds_addr(stage_buf<S>() + W * I * 1024) + wave_lds);
-  }
-};
-
-// EdgeCopy: a stage at the end of K -- clamped to the last stage and masked
-// when that one is ragged (copy_one_any).
-template <int W> struct EdgeCopy {
-  const CopyPlan<W>& cp;
-  const Panel& A;
-  const Panel& B;
-  int kc;
-  bool masked;
-  int t;
-  template <int S, int I> __device__ __forceinline__ void issue() const {
-    copy_one_any<W, S, I>(cp, A, B, kc, masked, t);
-  }
-};
 struct NoCopy {
   template <int S, int I> __device__ __forceinline__ void issue() const {}
+};
+
+// Extra work a kernel may run on stage kt's operands while they sit in
+// buffer S (called once per stage, in order, before the stage's first
+// MFMA; the buffer is not overwritten before the stage's barrier).  It
+// should add no branches to the K loop.  NoSide: none.
+struct NoSide {
+  template <int S> __device__ __forceinline__ void run(int) {}
 };
 
 // One slab's WI x WJ MFMAs on A fragments f.a and B fragments f.b[SC], with
@@ -362,13 +362,15 @@ __device__ __forceinline__ void frag_read(Frags<W>& f, const FragBase& fb) {
 //   wave is done reading buffer S and stage kt+1 is visible
 //   slab 1: MFMAs | reads of slab 0 of stage kt+1 (S^1) | every copy of
 //   stage kt+2 (into S), as early as the buffer allows
-template <int D, int W, int S, class C>
+template <int D, int W, int S, class C, class Side>
 __device__ __forceinline__ void kstage(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], Frags<W>& f,
                                        const FragBase& fb, const C& c, bool zero_next, const Panel& A, int kt,
-                                       int t) {
+                                       int t, Side& side) {
   static_assert(NSLABS == 2, "the schedule below assumes two slabs");
   constexpr int SN = S ^ 1;
   const NoCopy nc;
+  sched_fence();
+  side.template run<S>(kt);
   sched_fence();
   slab_phase<D, W, 0, S, 1, SN, false>(acc, f, fb, nc);
   wait_vmcnt<0>();
@@ -377,43 +379,22 @@ __device__ __forceinline__ void kstage(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ],
   slab_phase<D, W, 1, SN, 0, S, true>(acc, f, fb, c);
 }
 
-// Both operands' copies of one stage: copy I < NCOP/2 is of A, the rest of B.
-template <int W> struct PlainCopy2 {
-  PlainCopy<W> a, b;
-  template <int S, int I> __device__ __forceinline__ void issue() const {
-    if constexpr (I < Gemm<W>::NCOP / 2) a.template issue<S, I>();
-    else b.template issue<S, I>();
-  }
-};
-
-template <int D, int W, int S>
-__device__ __forceinline__ void kstage_plain(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], Frags<W>& f,
-                                             const CopyPlan<W>& cp, const FragBase& fb,
-                                             const Panel& A, const Panel& B, int kt, uint32_t wave_lds,
-                                             int t) {
-  const int64_t k0 = (int64_t)(kt + 2) * ROWB;
-  const PlainCopy2<W> c{{cp, uniform_ptr(A.base + k0), wave_lds}, {cp, uniform_ptr(B.base + k0), wave_lds}};
-  kstage<D, W, S>(acc, f, fb, c, false, A, kt, t);
-}
-
-// Past the end of K a copy re-reads the last stage (never used), so the
-// schedule still has no branches.
-template <int D, int W, int S>
-__device__ __forceinline__ void kstage_edge(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], Frags<W>& f,
-                                            const CopyPlan<W>& cp, const FragBase& fb,
-                                            const Panel& A, const Panel& B, int kt, int nk, bool ragged,
-                                            int t) {
-  const int k2 = min(kt + 2, nk - 1);
-  const EdgeCopy<W> c{cp, A, B, k2, ragged && k2 == nk - 1, t};
-  kstage<D, W, S>(acc, f, fb, c, ragged && kt + 1 == nk - 1, A, kt, t);
+// Stage kt; the copies it issues are of stage kt+2.  zero_next: stage kt+1
+// is the ragged last one.
+template <int D, int W, int S, bool EDGE, class Side>
+__device__ __forceinline__ void kstage_at(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], Frags<W>& f,
+                                          const CopyPlan<W>& cp, const FragBase& fb, const Panel& A, int kt,
+                                          int nk, bool ragged, uint32_t wave_lds, int t, Side& side) {
+  const StageCopy<W> c{cp, (uint32_t)(kt + 2) * ROWB, wave_lds};
+  kstage<D, W, S>(acc, f, fb, c, EDGE && ragged && kt + 1 == nk - 1, A, kt, t, side);
 }
 
 // acc[i][j] (this wave's WI x WJ blocks) = A_panel . B_panel^T over all of K.
 // Uses the stage buffers; returns after a barrier with no copy in flight, so
 // the caller may reuse them (e.g. g_stage0) right away.
-template <int D, int W>
+template <int D, int W, class Side>
 __device__ __forceinline__ void gemm_nt_tile(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], const Panel& A,
-                                             const Panel& B) {
+                                             const Panel& B, Side& side) {
   static_assert(NSTAGES == 2, "the loops below alternate two buffers");
   constexpr int H = Gemm<W>::NCOP / 2;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -429,9 +410,9 @@ __device__ __forceinline__ void gemm_nt_tile(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>
   CopyPlan<W> cp;
   copy_plan<W>(cp, A, B, t);
   lds_barrier();  // every wave is done with the buffers of any previous use
-  // stages 0 and 1 (clamped as in kstage_edge)
-  copy_range<W, 0, 0, 2 * H>(cp, A, B, 0, nk, ragged, t);
-  copy_range<W, 1, 0, 2 * H>(cp, A, B, min(1, nk - 1), nk, ragged, t);
+  // stages 0 and 1
+  copy_stage<W, 0>(StageCopy<W>{cp, 0u, wave_lds});
+  copy_stage<W, 1>(StageCopy<W>{cp, (uint32_t)ROWB, wave_lds});
   wait_vmcnt<2 * H>();
   if (ragged && nk == 1) zero_tail<W, 0>(A, 0, t);
   lds_barrier();
@@ -439,22 +420,28 @@ __device__ __forceinline__ void gemm_nt_tile(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>
   frag_base<W>(fb, wave, lane);
   Frags<W> f;
   frag_read<W, 0, 0>(f, fb);
-  // Pairs of plain stages (every copy they issue lies inside K and is not
-  // ragged: kt+1+2 <= last_plain), then pairs of edge stages.  A loop header
-  // with only two predecessors keeps the waitcnt pass from falling back to a
-  // full wait at the top of every round.
+  // Pairs of stages none of whose successors is the ragged last stage, then
+  // the rest.  A loop header with only two predecessors keeps the waitcnt
+  // pass from falling back to a full wait at the top of every round.
   const int last_plain = ragged ? nk - 2 : nk - 1;
   int kt = 0;
   for (; kt + 3 <= last_plain; kt += 2) {
-    kstage_plain<D, W, 0>(acc, f, cp, fb, A, B, kt, wave_lds, t);
-    kstage_plain<D, W, 1>(acc, f, cp, fb, A, B, kt + 1, wave_lds, t);
+    kstage_at<D, W, 0, false>(acc, f, cp, fb, A, kt, nk, ragged, wave_lds, t, side);
+    kstage_at<D, W, 1, false>(acc, f, cp, fb, A, kt + 1, nk, ragged, wave_lds, t, side);
   }
   for (; kt < nk; kt += 2) {
-    kstage_edge<D, W, 0>(acc, f, cp, fb, A, B, kt, nk, ragged, t);
-    if (kt + 1 < nk) kstage_edge<D, W, 1>(acc, f, cp, fb, A, B, kt + 1, nk, ragged, t);
+    kstage_at<D, W, 0, true>(acc, f, cp, fb, A, kt, nk, ragged, wave_lds, t, side);
+    if (kt + 1 < nk) kstage_at<D, W, 1, true>(acc, f, cp, fb, A, kt + 1, nk, ragged, wave_lds, t, side);
   }
   wait_vmcnt<0>();
   lds_barrier();
+}
+
+template <int D, int W>
+__device__ __forceinline__ void gemm_nt_tile(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], const Panel& A,
+                                             const Panel& B) {
+  NoSide none;
+  gemm_nt_tile<D, W>(acc, A, B, none);
 }
 
 // Bijective remap of a 1-D workgroup id so that consecutive logical ids land

@@ -550,6 +550,91 @@ __device__ __forceinline__ void tile16_store_t(uint16_t* dst, int64_t ld, int ro
   }
 }
 
+// Side job of the recompute kernel (16-bit types): while stage kt of the
+// weight tile (256 vocabulary rows x 64 hidden columns) sits in LDS, the
+// workgroups that share the vocabulary tile also write it transposed into
+// W_c^T[h][vl] (row pitch cvpad), so grad_hidden needs no separate
+// transpose of the chunk.  A stage is cut into 4 pieces of 64 vocabulary
+// rows; piece q = 4 kt + p goes to token tile q mod n_tok_tiles (the host
+// asks for this only with at least 4 token tiles, so that a workgroup has
+// at most one piece per stage), which spreads the work thinly over the K
+// loop.
+//
+// In a piece, wave w takes hidden columns 16 (w >> 1) + [0, 16) and rows
+// 32 (w & 1) + [0, 32); lane i of 16-lane group g reads row
+// 32 (w & 1) + 4 g + i / 4 and 16 + that row, 4 columns at 4 (i % 4), with
+// ds_read_b64_tr_b16, which hands lane i column i of rows 4 g + [0, 4)
+// (and 16 + those): two 8-byte stores into row h of W_c^T.  The row swizzle
+// (row >> 1) & 7 is the same for both rows, so the second read is the first
+// at +2048 bytes.  Lane math, reads, wait and stores sit in one asm block
+// that workgroups without a piece jump over (exec mask empty): the K loop
+// gets no branch and no register that lives across it.
+struct WcTSide {
+  uint16_t* wct;
+  int64_t H;
+  int cvpad, vl0, ntt;
+  uint32_t wave;  // wave-uniform
+  int qn;         // next piece of this workgroup (piece = 4 stage + part)
+  template <int S> __device__ __forceinline__ void run(int kt) {
+    const int p = qn - 4 * kt;  // wave-uniform
+    const bool in = (unsigned)p < 4u;
+    const bool sel = in & (vl0 + 64 * (p & 3) < cvpad);  // bitwise: no branch
+    qn += in ? ntt : 0;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(sel);  // exec or 0, without a branch
+    const int hrem = (int)min<int64_t>(64, H - (int64_t)kt * (ROWB / 2));
+    // wave-uniform parts: hidden block hb = wave >> 1, row half wave & 1
+    const uint32_t hb16 = 16u * (wave >> 1), w32 = 32u * (wave & 1u), ch16 = 32u * (wave >> 1);
+    const uint32_t lb = lds_addr(stage_buf<S>()) + 8192u * (uint32_t)(p & 3) + 128u * w32;
+    const char* sb =
+        uniform_ptr(reinterpret_cast<const char*>(wct + (int64_t)kt * (ROWB / 2) * cvpad + vl0 + 64 * (p & 3)));
+    // lane L = 16 g + i (recomputed here: no lane register lives across the
+    // K loop); read row 32 (w & 1) + L / 4, chunk (2 hb + (i >> 1) & 1) ^
+    // ((L >> 3) & 7), byte 8 (i & 1) in it; column hl = 16 hb + i.
+    uint64_t save, lo;
+    uint32_t t0, t1, t2;
+    asm volatile(
+        "s_mov_b64 %[sv], exec\n\t"
+        "s_mov_b64 exec, %[m]\n\t"
+        "s_cbranch_execz 1f\n\t"
+        "v_mbcnt_lo_u32_b32 %[t2], -1, 0\n\t"
+        "v_mbcnt_hi_u32_b32 %[t2], -1, %[t2]\n\t"   // L
+        "v_and_b32 %[t0], -4, %[t2]\n\t"
+        "v_lshlrev_b32 %[t0], 5, %[t0]\n\t"          // 128 (L / 4)
+        "v_lshlrev_b32 %[t1], 3, %[t2]\n\t"
+        "v_and_b32 %[t1], 24, %[t1]\n\t"             // 16 ((L >> 1) & 1) + 8 (L & 1)
+        "v_xor_b32 %[t0], %[t0], %[t1]\n\t"
+        "v_lshlrev_b32 %[t1], 1, %[t2]\n\t"
+        "v_and_b32 %[t1], 0x70, %[t1]\n\t"           // 16 ((L >> 3) & 7)
+        "v_xor_b32 %[t0], %[t0], %[t1]\n\t"
+        "v_xor_b32 %[t0], %[ch], %[t0]\n\t"          // ^ 32 hb
+        "v_add_u32 %[t0], %[lb], %[t0]\n\t"          // LDS byte address
+        "v_and_b32 %[t1], 15, %[t2]\n\t"
+        "v_add_u32 %[t1], %[hb], %[t1]\n\t"          // hl
+        "v_cmp_gt_i32 vcc, %[hr], %[t1]\n\t"         // hl < hrem
+        "s_mov_b64 exec, vcc\n\t"
+        "s_cbranch_execz 1f\n\t"
+        "ds_read_b64_tr_b16 %[lo], %[t0]\n\t"
+        // store byte offset 2 (hl cvpad + 4 g + 32 (w & 1))
+        "v_mul_lo_u32 %[t1], %[t1], %[cp]\n\t"
+        "v_lshrrev_b32 %[t2], 2, %[t2]\n\t"
+        "v_and_b32 %[t2], 12, %[t2]\n\t"
+        "v_add3_u32 %[t1], %[t1], %[t2], %[w32]\n\t"
+        "v_lshlrev_b32 %[t1], 1, %[t1]\n\t"
+        "s_waitcnt lgkmcnt(0)\n\t"
+        "global_store_dwordx2 %[t1], %[lo], %[sb]\n\t"
+        // rows 16 .. 19 further on (one data register pair, reused)
+        "ds_read_b64_tr_b16 %[lo], %[t0] offset:2048\n\t"
+        "s_waitcnt lgkmcnt(0)\n\t"
+        "global_store_dwordx2 %[t1], %[lo], %[sb] offset:32\n"
+        "1:\n\t"
+        "s_mov_b64 exec, %[sv]"
+        : [sv] "=&s"(save), [lo] "=&v"(lo), [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2)
+        : [m] "s"(m), [hr] "s"(hrem), [cp] "s"(cvpad), [lb] "s"(lb), [sb] "s"(sb), [hb] "s"(hb16),
+          [w32] "s"(w32), [ch] "s"(ch16)
+        : "memory", "vcc");
+  }
+};
+
 // Recompute one (token tile, vocabulary tile) of the chunk and write
 // G = coef * (softmax - onehot) * dz/draw (and G^T, grad_bias partials).
 // A = weight rows (vocabulary on the MFMA row axis), B = hidden rows.
@@ -572,7 +657,14 @@ __global__ __launch_bounds__(W * 64) void bwd_g_kernel(GArgs a) {
   Panel A{a.weight + v0 * rowb, rowb, (int)min<int64_t>(TILE, a.V - v0), rowb};
   Panel B{a.hidden + n0 * rowb, rowb, (int)min<int64_t>(TILE, a.N - n0), rowb};
   f32x4_t acc[WI][WJ];
-  gemm_nt_tile<D, W>(acc, A, B);
+  if constexpr (EB == 2) {
+    // no W_c^T wanted: a first piece past every stage selects none
+    WcTSide side{reinterpret_cast<uint16_t*>(a.WcT), a.H, a.cvpad, vl0, a.n_tok_tiles,
+                 (uint32_t)__builtin_amdgcn_readfirstlane(t >> 6), a.WcT != nullptr ? tt : (1 << 30)};
+    gemm_nt_tile<D, W>(acc, A, B, side);
+  } else {
+    gemm_nt_tile<D, W>(acc, A, B);
+  }
 
   float lse[WJ], coef[WJ];
   int tgt[WJ];

@@ -80,7 +80,8 @@ struct GArgs {
   const float* grad_rows;  // reduction "none": per-row upstream gradient (null = 1)
   char* G;                 // [npad][cvpad] or null
   char* GT;                // [cvpad][npad] or null
-  float* dbpart;           // [2*n_tok_tiles][V] or null
+  char* WcT;               // [H][cvpad]: W_c^T, 16-bit types only, or null
+  float* dbpart;           // [kBiasParts*n_tok_tiles][V] or null
   int64_t N, H, V, ignore_index, c0;
   int cv, cvpad, npad, n_tok_tiles, n_voc_tiles;
   int none_reduction;

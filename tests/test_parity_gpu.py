@@ -97,6 +97,16 @@ def test_hidden_not_multiple_of_stage(h, dtype):
     run_case(W["midvocab_bf16"].resized(n=100, h=h, v=600, dtype=dtype))
 
 
+# At least 4 token tiles: the recompute kernel itself writes the transposed
+# weight chunk for grad_hidden (16-bit types).  Ragged hidden stage, ragged
+# vocabulary tile in the last chunk, several chunks, exactly 4 and 5 tiles.
+@pytest.mark.parametrize("n,h,v,dtype,chunk", [(1030, 200, 2600, "bf16", 1024),
+                                               (1024, 328, 1800, "f16", 512),
+                                               (1100, 256, 700, "bf16", 0)])
+def test_many_token_tiles(n, h, v, dtype, chunk):
+    run_case(W["transforms_bf16"].resized(n=n, h=h, v=v, dtype=dtype), bwd_vocab_chunk=chunk)
+
+
 @pytest.mark.parametrize("tps,chunk", [(1, 256), (3, 768), (100, 0)])
 def test_plan_overrides(tps, chunk):
     run_case(W["transforms_bf16"].resized(n=300, h=256, v=2600), fwd_tiles_per_split=tps,
