@@ -315,11 +315,16 @@ struct NoCopy {
 };
 
 // Extra work a kernel may run on stage kt's operands while they sit in
-// buffer S (called once per stage, in order, before the stage's first
-// MFMA; the buffer is not overwritten before the stage's barrier).  It
-// should add no branches to the K loop.  NoSide: none.
+// buffer S, in two parts per stage, called in stage order:
+//   run<S>(kt):   after the stage's MFMAs have read all of buffer S and the
+//                 copies of stage kt+1 have landed, just before the barrier
+//                 after which buffer S is overwritten (its LDS writes are
+//                 complete and visible after that barrier);
+//   after<S>(kt): right after that barrier, before the stage's second slab.
+// Neither should add a branch to the K loop.  NoSide: none.
 struct NoSide {
   template <int S> __device__ __forceinline__ void run(int) {}
+  template <int S> __device__ __forceinline__ void after(int) {}
 };
 
 // One slab's WI x WJ MFMAs on A fragments f.a and B fragments f.b[SC], with
@@ -370,12 +375,15 @@ __device__ __forceinline__ void kstage(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ],
   constexpr int SN = S ^ 1;
   const NoCopy nc;
   sched_fence();
-  side.template run<S>(kt);
-  sched_fence();
   slab_phase<D, W, 0, S, 1, SN, false>(acc, f, fb, nc);
   wait_vmcnt<0>();
   if (zero_next) zero_tail<W, SN>(A, kt + 1, t);
+  sched_fence();
+  side.template run<S>(kt);
+  sched_fence();
   lds_barrier();
+  side.template after<S>(kt);
+  sched_fence();
   slab_phase<D, W, 1, SN, 0, S, true>(acc, f, fb, c);
 }
 

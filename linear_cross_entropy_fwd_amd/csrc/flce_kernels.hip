@@ -551,87 +551,148 @@ __device__ __forceinline__ void tile16_store_t(uint16_t* dst, int64_t ld, int ro
 }
 
 // Side job of the recompute kernel (16-bit types): while stage kt of the
-// weight tile (256 vocabulary rows x 64 hidden columns) sits in LDS, the
-// workgroups that share the vocabulary tile also write it transposed into
-// W_c^T[h][vl] (row pitch cvpad), so grad_hidden needs no separate
-// transpose of the chunk.  A stage is cut into 4 pieces of 64 vocabulary
-// rows; piece q = 4 kt + p goes to token tile q mod n_tok_tiles (the host
-// asks for this only with at least 4 token tiles, so that a workgroup has
-// at most one piece per stage), which spreads the work thinly over the K
-// loop.
+// weight tile (256 vocabulary rows x 64 hidden columns) sits in LDS, one of
+// the workgroups that share the vocabulary tile also writes it transposed
+// into W_c^T[h][vl] (row pitch cvpad), so grad_hidden needs no separate
+// transpose of the chunk.  Token tile tt takes the stages kt = tt mod
+// n_tok_tiles (the host asks for this only with at least 4 token tiles).
 //
-// In a piece, wave w takes hidden columns 16 (w >> 1) + [0, 16) and rows
-// 32 (w & 1) + [0, 32); lane i of 16-lane group g reads row
-// 32 (w & 1) + 4 g + i / 4 and 16 + that row, 4 columns at 4 (i % 4), with
+// Part 1, before the stage's barrier: the stage is transposed into a 32 KB
+// LDS tile T[h][vl] (64 rows of 512 bytes; 16-byte chunk c of row h sits at
+// c ^ (h & 31), conflict-free for both passes).  Wave w takes hidden
+// columns 16 (w >> 1) + [0, 16) and, in each of the four 64-row parts p of
+// the stage, rows 64 p + 32 (w & 1) + [0, 32).  Lane L = 16 g + i reads row
+// 64 p + 32 (w & 1) + L / 4 and 16 + that row, 4 columns at 4 (i % 4), with
 // ds_read_b64_tr_b16, which hands lane i column i of rows 4 g + [0, 4)
-// (and 16 + those): two 8-byte stores into row h of W_c^T.  The row swizzle
-// (row >> 1) & 7 is the same for both rows, so the second read is the first
-// at +2048 bytes.  Lane math, reads, wait and stores sit in one asm block
-// that workgroups without a piece jump over (exec mask empty): the K loop
-// gets no branch and no register that lives across it.
+// (and 16 + those): two 8-byte writes into row h = 16 (w >> 1) + i of T.
+// The stage's row swizzle (row >> 1) & 7 is the same for all eight rows a
+// lane reads, so they are one address at immediate offsets; in T, part p
+// and the second read are the first write address xor 128 p and xor 32.
+// Part 2, after the barrier: wave w stores rows 8 w + [0, 8) of T, two rows
+// of 512 bytes per instruction (whole cache lines; 8-byte stores straight
+// from the transposed reads ran several times slower).
+// Each part is one asm block that the other workgroups jump over (exec mask
+// empty): the K loop gets no branch and no register that lives across it.
+__shared__ __attribute__((aligned(1024))) char g_wct_tile[64 * 512];
+
 struct WcTSide {
   uint16_t* wct;
   int64_t H;
   int cvpad, vl0, ntt;
   uint32_t wave;  // wave-uniform
-  int qn;         // next piece of this workgroup (piece = 4 stage + part)
+  int ks;         // next stage of this workgroup
+  uint64_t m;     // this stage: exec if selected, else 0
   template <int S> __device__ __forceinline__ void run(int kt) {
-    const int p = qn - 4 * kt;  // wave-uniform
-    const bool in = (unsigned)p < 4u;
-    const bool sel = in & (vl0 + 64 * (p & 3) < cvpad);  // bitwise: no branch
-    qn += in ? ntt : 0;
-    const uint64_t m = __builtin_amdgcn_ballot_w64(sel);  // exec or 0, without a branch
+    const bool in = kt == ks;  // wave-uniform
+    ks += in ? ntt : 0;
+    m = __builtin_amdgcn_ballot_w64(in);  // exec or 0, without a branch
     const int hrem = (int)min<int64_t>(64, H - (int64_t)kt * (ROWB / 2));
-    // wave-uniform parts: hidden block hb = wave >> 1, row half wave & 1
+    const int vrem = cvpad - vl0;  // rows of the tile inside W_c^T (a multiple of 64)
     const uint32_t hb16 = 16u * (wave >> 1), w32 = 32u * (wave & 1u), ch16 = 32u * (wave >> 1);
-    const uint32_t lb = lds_addr(stage_buf<S>()) + 8192u * (uint32_t)(p & 3) + 128u * w32;
-    const char* sb =
-        uniform_ptr(reinterpret_cast<const char*>(wct + (int64_t)kt * (ROWB / 2) * cvpad + vl0 + 64 * (p & 3)));
-    // lane L = 16 g + i (recomputed here: no lane register lives across the
-    // K loop); read row 32 (w & 1) + L / 4, chunk (2 hb + (i >> 1) & 1) ^
-    // ((L >> 3) & 7), byte 8 (i & 1) in it; column hl = 16 hb + i.
-    uint64_t save, lo;
-    uint32_t t0, t1, t2;
+    const uint32_t lb = lds_addr(stage_buf<S>()) + 128u * w32;
+    const uint32_t tb = lds_addr(g_wct_tile);
+    uint64_t save, lo, hi;
+    uint32_t t0, t1, t2, t3;
+#define FLCE_WCT_PART(P, NEXT)                                            \
+  "s_cmp_gt_i32 %[vr], " #P "*64\n\t"                                     \
+  "s_cbranch_scc0 1f\n\t"                                                 \
+  "ds_read_b64_tr_b16 %[lo], %[t0] offset:" #P "*8192\n\t"                \
+  "ds_read_b64_tr_b16 %[hi], %[t0] offset:" #P "*8192+2048\n\t"           \
+  "s_waitcnt lgkmcnt(0)\n\t"                                              \
+  "ds_write_b64 %[t1], %[lo]\n\t"                                         \
+  "v_xor_b32 %[t3], 32, %[t1]\n\t"                                        \
+  "ds_write_b64 %[t3], %[hi]\n\t"                                         \
+  "v_xor_b32 %[t1], " #NEXT ", %[t1]\n\t"
     asm volatile(
         "s_mov_b64 %[sv], exec\n\t"
         "s_mov_b64 exec, %[m]\n\t"
         "s_cbranch_execz 1f\n\t"
         "v_mbcnt_lo_u32_b32 %[t2], -1, 0\n\t"
         "v_mbcnt_hi_u32_b32 %[t2], -1, %[t2]\n\t"   // L
+        // transposed-read address: 128 (L / 4) + 16 ((2 hb + (L >> 1) & 1) ^ ((L >> 3) & 7)) + 8 (L & 1)
         "v_and_b32 %[t0], -4, %[t2]\n\t"
-        "v_lshlrev_b32 %[t0], 5, %[t0]\n\t"          // 128 (L / 4)
+        "v_lshlrev_b32 %[t0], 5, %[t0]\n\t"
+        "v_xor_b32 %[t0], %[ch], %[t0]\n\t"
         "v_lshlrev_b32 %[t1], 3, %[t2]\n\t"
-        "v_and_b32 %[t1], 24, %[t1]\n\t"             // 16 ((L >> 1) & 1) + 8 (L & 1)
+        "v_and_b32 %[t1], 24, %[t1]\n\t"
         "v_xor_b32 %[t0], %[t0], %[t1]\n\t"
         "v_lshlrev_b32 %[t1], 1, %[t2]\n\t"
-        "v_and_b32 %[t1], 0x70, %[t1]\n\t"           // 16 ((L >> 3) & 7)
+        "v_and_b32 %[t1], 0x70, %[t1]\n\t"
         "v_xor_b32 %[t0], %[t0], %[t1]\n\t"
-        "v_xor_b32 %[t0], %[ch], %[t0]\n\t"          // ^ 32 hb
-        "v_add_u32 %[t0], %[lb], %[t0]\n\t"          // LDS byte address
+        "v_add_u32 %[t0], %[lb], %[t0]\n\t"
         "v_and_b32 %[t1], 15, %[t2]\n\t"
         "v_add_u32 %[t1], %[hb], %[t1]\n\t"          // hl
         "v_cmp_gt_i32 vcc, %[hr], %[t1]\n\t"         // hl < hrem
         "s_mov_b64 exec, vcc\n\t"
         "s_cbranch_execz 1f\n\t"
-        "ds_read_b64_tr_b16 %[lo], %[t0]\n\t"
-        // store byte offset 2 (hl cvpad + 4 g + 32 (w & 1))
-        "v_mul_lo_u32 %[t1], %[t1], %[cp]\n\t"
-        "v_lshrrev_b32 %[t2], 2, %[t2]\n\t"
-        "v_and_b32 %[t2], 12, %[t2]\n\t"
-        "v_add3_u32 %[t1], %[t1], %[t2], %[w32]\n\t"
-        "v_lshlrev_b32 %[t1], 1, %[t1]\n\t"
-        "s_waitcnt lgkmcnt(0)\n\t"
-        "global_store_dwordx2 %[t1], %[lo], %[sb]\n\t"
-        // rows 16 .. 19 further on (one data register pair, reused)
-        "ds_read_b64_tr_b16 %[lo], %[t0] offset:2048\n\t"
-        "s_waitcnt lgkmcnt(0)\n\t"
-        "global_store_dwordx2 %[t1], %[lo], %[sb] offset:32\n"
+        // T write address of part 0: tb + 512 hl + ((8 g + 64 (w & 1)) ^ 16 (hl & 31))
+        "v_and_b32 %[t3], 31, %[t1]\n\t"
+        "v_lshlrev_b32 %[t3], 4, %[t3]\n\t"
+        "v_lshrrev_b32 %[t2], 1, %[t2]\n\t"
+        "v_and_b32 %[t2], 24, %[t2]\n\t"
+        "v_or_b32 %[t2], %[w64], %[t2]\n\t"
+        "v_xor_b32 %[t2], %[t2], %[t3]\n\t"
+        "v_lshl_add_u32 %[t1], %[t1], 9, %[t2]\n\t"
+        "v_add_u32 %[t1], %[tb], %[t1]\n\t"
+        FLCE_WCT_PART(0, 128) FLCE_WCT_PART(1, 384) FLCE_WCT_PART(2, 128) FLCE_WCT_PART(3, 0)
         "1:\n\t"
         "s_mov_b64 exec, %[sv]"
-        : [sv] "=&s"(save), [lo] "=&v"(lo), [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2)
-        : [m] "s"(m), [hr] "s"(hrem), [cp] "s"(cvpad), [lb] "s"(lb), [sb] "s"(sb), [hb] "s"(hb16),
-          [w32] "s"(w32), [ch] "s"(ch16)
+        : [sv] "=&s"(save), [lo] "=&v"(lo), [hi] "=&v"(hi), [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2),
+          [t3] "=&v"(t3)
+        : [m] "s"(m), [hr] "s"(hrem), [vr] "s"(vrem), [lb] "s"(lb), [tb] "s"(tb), [hb] "s"(hb16),
+          [w64] "s"(2u * w32), [ch] "s"(ch16)
+        : "memory", "vcc", "scc");
+#undef FLCE_WCT_PART
+  }
+  template <int S> __device__ __forceinline__ void after(int kt) {
+    const int hrem = (int)min<int64_t>(64, H - (int64_t)kt * (ROWB / 2));
+    const int vrem = cvpad - vl0;
+    const uint32_t tb = lds_addr(g_wct_tile);
+    const char* sb = uniform_ptr(reinterpret_cast<const char*>(wct + (int64_t)kt * (ROWB / 2) * cvpad + vl0));
+    uint64_t save, rows;
+    uint4 d;
+    uint32_t t0, t1, t2, t3;
+    // row h = 8 w + 2 J + L / 32, chunk c = L & 31: T at tb + 512 h + 16 (c ^ (h & 31)),
+    // W_c^T at sb + 2 cvpad h + 16 c
+#define FLCE_WCT_ROW(J)                                                   \
+  "s_mov_b64 exec, %[rw]\n\t"                                             \
+  "v_add3_u32 %[t0], %[h8], " #J "*2, %[t2]\n\t"                          \
+  "v_cmp_gt_i32 vcc, %[hr], %[t0]\n\t"                                    \
+  "s_mov_b64 exec, vcc\n\t"                                               \
+  "s_cbranch_execz 2f\n\t"                                                \
+  "v_and_b32 %[t1], 31, %[t0]\n\t"                                        \
+  "v_xor_b32 %[t1], %[t1], %[t3]\n\t"                                     \
+  "v_lshlrev_b32 %[t1], 4, %[t1]\n\t"                                     \
+  "v_lshl_add_u32 %[t1], %[t0], 9, %[t1]\n\t"                             \
+  "v_add_u32 %[t1], %[tb], %[t1]\n\t"                                     \
+  "ds_read_b128 %[d], %[t1]\n\t"                                          \
+  "v_mul_lo_u32 %[t0], %[t0], %[cp2]\n\t"                                 \
+  "v_lshl_add_u32 %[t0], %[t3], 4, %[t0]\n\t"                             \
+  "s_waitcnt lgkmcnt(0)\n\t"                                              \
+  "global_store_dwordx4 %[t0], %[d], %[sb]\n"                             \
+  "2:\n\t"
+    asm volatile(
+        "s_mov_b64 %[sv], exec\n\t"
+        "s_mov_b64 exec, %[m]\n\t"
+        "s_cbranch_execz 1f\n\t"
+        "v_mbcnt_lo_u32_b32 %[t2], -1, 0\n\t"
+        "v_mbcnt_hi_u32_b32 %[t2], -1, %[t2]\n\t"   // L
+        "v_and_b32 %[t3], 31, %[t2]\n\t"             // c
+        "v_lshlrev_b32 %[t0], 3, %[t3]\n\t"
+        "v_cmp_gt_i32 vcc, %[vr], %[t0]\n\t"         // 8 c < vrem
+        "s_mov_b64 exec, vcc\n\t"
+        "s_cbranch_execz 1f\n\t"
+        "s_mov_b64 %[rw], exec\n\t"
+        "v_lshrrev_b32 %[t2], 5, %[t2]\n\t"          // L / 32
+        FLCE_WCT_ROW(0) FLCE_WCT_ROW(1) FLCE_WCT_ROW(2) FLCE_WCT_ROW(3)
+        "1:\n\t"
+        "s_mov_b64 exec, %[sv]"
+        : [sv] "=&s"(save), [rw] "=&s"(rows), [d] "=&v"(d), [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2),
+          [t3] "=&v"(t3)
+        : [m] "s"(m), [hr] "s"(hrem), [vr] "s"(vrem), [tb] "s"(tb), [sb] "s"(sb), [h8] "s"(8u * wave),
+          [cp2] "s"(2 * cvpad)
         : "memory", "vcc");
+#undef FLCE_WCT_ROW
   }
 };
 
@@ -658,9 +719,9 @@ __global__ __launch_bounds__(W * 64) void bwd_g_kernel(GArgs a) {
   Panel B{a.hidden + n0 * rowb, rowb, (int)min<int64_t>(TILE, a.N - n0), rowb};
   f32x4_t acc[WI][WJ];
   if constexpr (EB == 2) {
-    // no W_c^T wanted: a first piece past every stage selects none
+    // no W_c^T wanted: a first stage past every stage selects none
     WcTSide side{reinterpret_cast<uint16_t*>(a.WcT), a.H, a.cvpad, vl0, a.n_tok_tiles,
-                 (uint32_t)__builtin_amdgcn_readfirstlane(t >> 6), a.WcT != nullptr ? tt : (1 << 30)};
+                 (uint32_t)__builtin_amdgcn_readfirstlane(t >> 6), a.WcT != nullptr ? tt : (1 << 30), 0ull};
     gemm_nt_tile<D, W>(acc, A, B, side);
   } else {
     gemm_nt_tile<D, W>(acc, A, B);
