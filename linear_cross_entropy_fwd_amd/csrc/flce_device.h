@@ -194,13 +194,13 @@ __device__ __forceinline__ i32x4_t panel_rsrc(const Panel& p) {
 // The copies of a stage.  Block b = 0..63 of a stage is operand b>>5, rows
 // (b&31)*8 .. +8.  Copy i of wave w is block w + W*i (copies 0 .. NCOP/2-1
 // are of operand A, the rest of B), so copy i of an operand covers rows
-// 64*i + 8*w + L/8 for lane L: its offset is the lane's first one plus
-// 64*i row pitches.  Lane L fills LDS chunk position L&7 of its row, which
+// 8*W*i + 8*w + L/8 for lane L: its offset is the lane's first one plus
+// 8*W*i row pitches.  Lane L fills LDS chunk position L&7 of its row, which
 // holds global chunk (L&7) ^ ((row>>1)&7) -- the same for every i.
 template <int W> struct CopyPlan {
   i32x4_t ra, rb;   // buffer resources of A and B
   uint32_t oa, ob;  // the lane's byte offset in copy 0 of A / of B
-  uint32_t sa, sb;  // 64 row pitches of A / of B (wave-uniform)
+  uint32_t sa, sb;  // 8*W row pitches of A / of B (wave-uniform)
 };
 
 template <int W> __device__ __forceinline__ constexpr int copy_block(int i, int wave) { return wave + W * i; }
@@ -216,8 +216,8 @@ __device__ __forceinline__ void copy_plan(CopyPlan<W>& cp, const Panel& A, const
   cp.rb = panel_rsrc(B);
   cp.oa = (uint32_t)(row * A.ld) + c16;
   cp.ob = (uint32_t)(row * B.ld) + c16;
-  cp.sa = __builtin_amdgcn_readfirstlane((uint32_t)(64 * A.ld));
-  cp.sb = __builtin_amdgcn_readfirstlane((uint32_t)(64 * B.ld));
+  cp.sa = __builtin_amdgcn_readfirstlane((uint32_t)(8 * W * A.ld));
+  cp.sb = __builtin_amdgcn_readfirstlane((uint32_t)(8 * W * B.ld));
 }
 
 // Copy I of the stage at K byte offset k0 into buffer S.  Stages past K (the
@@ -461,16 +461,19 @@ __device__ __forceinline__ int xcd_logical_id(int bid, int nblocks) {
 }
 
 // Tile order for a grid over na x nb output tiles (a: the dimension whose
-// panels are shared along b, and the reverse).  Workgroups are dealt to the
-// 8 XCDs round robin and run one per CU, so 32 of them share an XCD's L2 at a
-// time.  Numbered as below, those 32 cover a GA x GB = 4 x 8 block of tiles:
-// 12 distinct operand panels per K-stage in L2, where a row-major order
-// (e.g. 16 x 2) would need 18.  The grid is padded to whole blocks; a padding
-// workgroup gets valid = false and must exit at once.
-constexpr int GROUP_A = 4, GROUP_B = 8;
-
+// panels are shared along b, and the reverse): blocks of GA x GB tiles.
+// Workgroups are dealt to the 8 XCDs round robin and run one per CU, so 32
+// of them share an XCD's L2 at a time.  With XCD, logical ids are remapped so
+// that consecutive ones share an XCD, and a 4 x 8 block is what those 32
+// cover: 12 distinct operand panels per K-stage in L2, where a row-major
+// order (e.g. 16 x 2) would need 18.  Without it, a block is spread over all
+// XCDs (the panels then meet in the last-level cache rather than in L2).
+// Which is faster depends on the launch and is measured, not derived.  The
+// grid is padded to whole blocks; a padding workgroup gets valid = false and
+// must exit at once.
+template <int GA, int GB>
 __host__ __device__ inline int grouped_grid(int na, int nb) {
-  return ((na + GROUP_A - 1) / GROUP_A) * ((nb + GROUP_B - 1) / GROUP_B) * GROUP_A * GROUP_B;
+  return ((na + GA - 1) / GA) * ((nb + GB - 1) / GB) * GA * GB;
 }
 
 struct TileAB {
@@ -478,13 +481,14 @@ struct TileAB {
   bool valid;
 };
 
+template <int GA, int GB, bool XCD>
 __device__ __forceinline__ TileAB grouped_tile(int bid, int nblocks, int na, int nb) {
-  const int L = xcd_logical_id(bid, nblocks);
-  const int nga = (na + GROUP_A - 1) / GROUP_A;
-  const int g = L / (GROUP_A * GROUP_B), w = L % (GROUP_A * GROUP_B);
+  const int L = XCD ? xcd_logical_id(bid, nblocks) : bid;
+  const int nga = (na + GA - 1) / GA;
+  const int g = L / (GA * GB), w = L % (GA * GB);
   TileAB r;
-  r.a = (g % nga) * GROUP_A + w % GROUP_A;
-  r.b = (g / nga) * GROUP_B + w / GROUP_A;
+  r.a = (g % nga) * GA + w % GA;
+  r.b = (g / nga) * GB + w / GA;
   r.valid = r.a < na && r.b < nb;
   return r;
 }

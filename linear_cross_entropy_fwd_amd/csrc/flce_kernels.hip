@@ -127,7 +127,7 @@ __global__ __launch_bounds__(W * 64) void fwd_tiles_kernel(FwdArgs a) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = Gemm<W>::wm(wave), wn = Gemm<W>::wn(wave), c16 = lane & 15, q = lane >> 4;
 
-  const TileAB ti = grouped_tile(blockIdx.x, gridDim.x, a.n_tok_tiles, a.n_splits);
+  const TileAB ti = grouped_tile<kFwdGA, kFwdGB, kFwdXcd>(blockIdx.x, gridDim.x, a.n_tok_tiles, a.n_splits);
   if (!ti.valid) return;
   const int tt = ti.a, split = ti.b;
   const int64_t n0 = (int64_t)tt * TILE;
@@ -707,7 +707,7 @@ __global__ __launch_bounds__(W * 64) void bwd_g_kernel(GArgs a) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = Gemm<W>::wm(wave), wn = Gemm<W>::wn(wave), c16 = lane & 15, q = lane >> 4;
 
-  const TileAB ti = grouped_tile(blockIdx.x, gridDim.x, a.n_tok_tiles, a.n_voc_tiles);
+  const TileAB ti = grouped_tile<kRecGA, kRecGB, kRecXcd>(blockIdx.x, gridDim.x, a.n_tok_tiles, a.n_voc_tiles);
   if (!ti.valid) return;
   const int tt = ti.a, vt = ti.b;
   const int64_t n0 = (int64_t)tt * TILE;
@@ -876,7 +876,7 @@ template <int D, int W>
 __global__ __launch_bounds__(W * 64) void bwd_dh_kernel(DhArgs a) {
   typedef typename Elem<D>::T T;
   constexpr int EB = Elem<D>::bytes, WI = Gemm<W>::WI, WJ = Gemm<W>::WJ;
-  const TileAB ti = grouped_tile(blockIdx.x, gridDim.x, a.n_h_tiles, a.n_tok_tiles);
+  const TileAB ti = grouped_tile<kDhGA, kDhGB, kDhXcd>(blockIdx.x, gridDim.x, a.n_h_tiles, a.n_tok_tiles);
   if (!ti.valid) return;
   const int ht = ti.a, tt = ti.b;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -920,7 +920,7 @@ template <int D, int W>
 __global__ __launch_bounds__(W * 64) void bwd_dw_kernel(DwArgs a) {
   typedef typename Elem<D>::T T;
   constexpr int EB = Elem<D>::bytes, WI = Gemm<W>::WI, WJ = Gemm<W>::WJ;
-  const TileAB ti = grouped_tile(blockIdx.x, gridDim.x, a.n_h_tiles, a.n_voc_tiles);
+  const TileAB ti = grouped_tile<kDwGA, kDwGB, kDwXcd>(blockIdx.x, gridDim.x, a.n_h_tiles, a.n_voc_tiles);
   if (!ti.valid) return;
   const int ht = ti.a, vt = ti.b;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -975,7 +975,7 @@ static inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + p
 
 template <int D>
 static hipError_t fwd_tiles_dispatch(bool metrics, bool bias, bool cap, const FwdArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)grouped_grid(a.n_tok_tiles, a.n_splits)), block(kFwdWaves * 64);
+  const dim3 grid((unsigned)grouped_grid<kFwdGA, kFwdGB>(a.n_tok_tiles, a.n_splits)), block(kFwdWaves * 64);
 #define FLCE_FWD(M, B, C)                                                                \
   if (metrics == M && bias == B && cap == C) {                                           \
     hipLaunchKernelGGL((fwd_tiles_kernel<D, M, B, C, kFwdWaves>), grid, block, 0, st, a); \
@@ -1027,7 +1027,7 @@ hipError_t launch_transpose(int dtype, const TransposeArgs& a, hipStream_t st) {
 template <int D>
 static hipError_t g_dispatch(bool bias, bool cap, const GArgs& a, hipStream_t st) {
   constexpr int W = kRecomputeWaves;
-  const dim3 grid((unsigned)grouped_grid(a.n_tok_tiles, a.n_voc_tiles)), block(W * 64);
+  const dim3 grid((unsigned)grouped_grid<kRecGA, kRecGB>(a.n_tok_tiles, a.n_voc_tiles)), block(W * 64);
   if (!bias && !cap) hipLaunchKernelGGL((bwd_g_kernel<D, false, false, W>), grid, block, 0, st, a);
   else if (!bias && cap) hipLaunchKernelGGL((bwd_g_kernel<D, false, true, W>), grid, block, 0, st, a);
   else if (bias && !cap) hipLaunchKernelGGL((bwd_g_kernel<D, true, false, W>), grid, block, 0, st, a);
@@ -1045,7 +1045,7 @@ hipError_t launch_backward_g(int dtype, bool bias, bool cap, const GArgs& a, hip
 }
 
 hipError_t launch_backward_dh(int dtype, const DhArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)grouped_grid(a.n_h_tiles, a.n_tok_tiles)), block(kContractWaves * 64);
+  const dim3 grid((unsigned)grouped_grid<kDhGA, kDhGB>(a.n_h_tiles, a.n_tok_tiles)), block(kContractWaves * 64);
   switch (dtype) {
     case DT_F32: hipLaunchKernelGGL((bwd_dh_kernel<DT_F32, kContractWaves>), grid, block, 0, st, a); break;
     case DT_F16: hipLaunchKernelGGL((bwd_dh_kernel<DT_F16, kContractWaves>), grid, block, 0, st, a); break;
@@ -1056,7 +1056,7 @@ hipError_t launch_backward_dh(int dtype, const DhArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_backward_dw(int dtype, const DwArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)grouped_grid(a.n_h_tiles, a.n_voc_tiles)), block(kContractWaves * 64);
+  const dim3 grid((unsigned)grouped_grid<kDwGA, kDwGB>(a.n_h_tiles, a.n_voc_tiles)), block(kContractWaves * 64);
   switch (dtype) {
     case DT_F32: hipLaunchKernelGGL((bwd_dw_kernel<DT_F32, kContractWaves>), grid, block, 0, st, a); break;
     case DT_F16: hipLaunchKernelGGL((bwd_dw_kernel<DT_F16, kContractWaves>), grid, block, 0, st, a); break;
