@@ -169,14 +169,15 @@ __global__ __launch_bounds__(W * 64) void fwd_tiles_kernel(FwdArgs a) {
     const int qo = (to >> 4) & 3;
     const int vbase = (int)v0 + Gemm<W>::wm(to >> 6) * 16 * WI;  // this wave's first row
     const int vq = vbase + 4 * qo;                                // row of acc[i][.][e]: vq + 16 i + e
-    const bool ragged = v0 + TILE > a.V;
+    // rows of this lane at or past V (only in the last, ragged tile): vq + 16 i + e >= V
+    const int vrem = (int)min<int64_t>(a.V - vq, 1 << 20);
+    const bool ragged = vrem < 16 * WI;  // wave-uniform
     float bv[WI][4];
     load_bias_rows<D, BIAS, WI>(bv, a.bias, vq, a.V);
 
 #pragma unroll
     for (int j = 0; j < WJ; ++j) {
       float z[WI][4];
-      float zl = -INFINITY;
 #pragma unroll
       for (int i = 0; i < WI; ++i)
 #pragma unroll
@@ -185,24 +186,38 @@ __global__ __launch_bounds__(W * 64) void fwd_tiles_kernel(FwdArgs a) {
           if (BIAS) y = y + bv[i][e];
           y = a.s * y;
           if (CAP) y = soft_cap(y, a.cap, a.inv_cap);
-          if (ragged && vq + 16 * i + e >= a.V) y = -INFINITY;
           z[i][e] = y;
-          zl = fmaxf(zl, y);
         }
+      if (ragged) {  // a branch only the last tile takes, not a select per element
+#pragma unroll
+        for (int i = 0; i < WI; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (16 * i + e >= vrem) z[i][e] = -INFINITY;
+      }
+      float zl = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < WI; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) zl = fmaxf(zl, z[i][e]);
       const float zmax = col_max4(zl);
       const float mold = FST(0, j);
       const float mnew = fmaxf(mold, zmax);
       if (mnew != -INFINITY) {
-        float sum = 0.f, usum = 0.f;
+        // four independent partial sums (one per accumulator register), so
+        // that the adds do not wait on each exp in turn
+        float sp[4] = {0.f, 0.f, 0.f, 0.f}, up[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < WI; ++i)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float d = z[i][e] - mnew;
             const float ex = fast_exp2(d * LOG2E);
-            sum = sum + ex;
-            if (METRICS) usum = fmaf(ex, fmaxf(d, -1e30f), usum);
+            sp[e] = sp[e] + ex;
+            if (METRICS) up[e] = fmaf(ex, fmaxf(d, -1e30f), up[e]);
           }
+        float sum = (sp[0] + sp[1]) + (sp[2] + sp[3]), usum = 0.f;
+        if (METRICS) usum = (up[0] + up[1]) + (up[2] + up[3]);
         sum = col_sum4(sum);
         if (METRICS) usum = col_sum4(usum);
         if (q == 0) {
@@ -727,20 +742,20 @@ __global__ __launch_bounds__(W * 64) void bwd_g_kernel(GArgs a) {
     gemm_nt_tile<D, W>(acc, A, B);
   }
 
+  // Per column: lse, the gradient factor and the target id.  A dead column
+  // (past N or ignored) gets lse = +inf and factor 0, so its p is 0 and its
+  // G column 0 without a select per element.
   float lse[WJ], coef[WJ];
   int tgt[WJ];
-  bool live[WJ];
 #pragma unroll
   for (int j = 0; j < WJ; ++j) {
     const int64_t n = n0 + wn * 16 * WJ + 16 * j + c16;
-    live[j] = false;
     tgt[j] = -1;
-    lse[j] = 0.f;
+    lse[j] = INFINITY;
     coef[j] = 0.f;
     if (n < a.N) {
       const int64_t tv = a.targets[n];
       if (tv != a.ignore_index) {
-        live[j] = true;
         lse[j] = a.lse[n];
         if (tv < 0 || tv >= a.V) {
           coef[j] = NAN;
@@ -755,29 +770,75 @@ __global__ __launch_bounds__(W * 64) void bwd_g_kernel(GArgs a) {
   const int vq = (int)v0 + wm * 16 * WI + 4 * q;  // row of acc[i][.][e]: vq + 16 i + e
   float bv[WI][4];
   load_bias_rows<D, BIAS, WI>(bv, a.bias, vq, a.V);
+  // The one-hot term: column j's target row, as 16 i + e relative to vq, when
+  // this lane holds it (rare), and its value dz/draw * factor there.
+  int tl[WJ];
+  bool any_t = false;
+#pragma unroll
+  for (int j = 0; j < WJ; ++j) {
+    tl[j] = tgt[j] - vq;
+    const bool here = tgt[j] >= 0 && tl[j] >= 0 && tl[j] < 16 * WI && (tl[j] & 15) < 4;
+    if (!here) tl[j] = -1;
+    any_t |= here;
+  }
+  float onehot[WJ];
+#pragma unroll
+  for (int j = 0; j < WJ; ++j) onehot[j] = 0.f;
+  if (any_t) {
+#pragma unroll
+    for (int j = 0; j < WJ; ++j) {
+      float yr = 0.f;
+#pragma unroll
+      for (int i = 0; i < WI; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (16 * i + e == tl[j]) yr = BIAS ? acc[i][j][e] + bv[i][e] : acc[i][j][e];
+      float cf = 1.f;
+      if (CAP) {
+        const float qc = soft_cap(a.s * yr, a.cap, a.inv_cap) * a.inv_cap;
+        cf = fmaf(-qc, qc, 1.f);
+      }
+      if (tl[j] >= 0) onehot[j] = cf * coef[j];
+    }
+  }
 #pragma unroll
   for (int i = 0; i < WI; ++i)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int v = vq + 16 * i + e;
-      const int vl = v - (int)a.c0;
-      const bool vin = v < a.V && vl < a.cv;
+    for (int e = 0; e < 4; ++e)
 #pragma unroll
       for (int j = 0; j < WJ; ++j) {
         float y = acc[i][j][e];
         if (BIAS) y = y + bv[i][e];
         y = a.s * y;
         if (CAP) y = soft_cap(y, a.cap, a.inv_cap);
-        const float p = fast_exp2((y - lse[j]) * LOG2E);
-        float g = v == tgt[j] ? p - 1.f : p;
+        float g = fast_exp2((y - lse[j]) * LOG2E);
         if (CAP) {
           const float qc = y * a.inv_cap;
           g = g * fmaf(-qc, qc, 1.f);
         }
-        g = g * coef[j];
-        acc[i][j][e] = (vin && live[j]) ? g : 0.f;
+        acc[i][j][e] = g * coef[j];
       }
-    }
+  if (any_t) {
+#pragma unroll
+    for (int j = 0; j < WJ; ++j)
+#pragma unroll
+      for (int i = 0; i < WI; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (16 * i + e == tl[j]) acc[i][j][e] = acc[i][j][e] - onehot[j];
+  }
+  // rows past V or past the chunk (only in a ragged last tile): G = 0
+  const int vrem = (int)min<int64_t>(min<int64_t>(a.V, a.c0 + a.cv) - vq, 1 << 20);
+  if (vrem < 16 * WI) {
+#pragma unroll
+    for (int i = 0; i < WI; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (16 * i + e >= vrem) {
+#pragma unroll
+          for (int j = 0; j < WJ; ++j) acc[i][j][e] = 0.f;
+        }
+  }
 
   const int vlq = vl0 + wm * 16 * WI + 4 * q;  // chunk-local row of acc[i][.][e]: vlq + 16 i + e
   // 16-bit types: the tile goes to LDS as [n][v] and leaves as G rows and,
