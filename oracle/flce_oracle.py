@@ -29,6 +29,19 @@ Readings of points the card leaves open (each is stated where it is used):
   * metrics average over non-ignored rows;
   * a non-ignored target outside [0, V) raises ValueError.
 
+Three loss variants that run on the same vocabulary sweep (not defined on
+the pages; textbook definitions, each a stated reading):
+  * label smoothing eps: the target distribution is (1 - eps) one-hot plus
+    eps / V uniform, so row_loss = lse - (1 - eps) z_t - (eps / V) sum_j z_j;
+  * z-loss coefficient zl: row_loss += zl * lse^2 (penalises the partition
+    function's log);
+  * class weights w (V,): row i's whole loss (including the z-loss term) is
+    multiplied by w[t_i], and the mean divides by the sum of w[t_i] over
+    non-ignored rows.  Alone, label smoothing and class weights each match
+    torch's cross_entropy; together, torch weights the smoothing term per
+    class instead, which this reading does not.
+  Metrics (accuracy, entropy) are unweighted and unaffected.
+
 Every function here is pinned by CPU tests against library routines
 (torch cross_entropy and autograd, scipy logsumexp / softmax / entropy),
 closed forms (zero weight, zero scale, two classes), invariants and central
@@ -85,20 +98,44 @@ def row_statistics(z):
     return lse, p, entropy, argmax, gap
 
 
+def _row_weights(t, valid, class_weight):
+    """w[t_i] on non-ignored rows (1 without class weights), 0 on ignored ones."""
+    if class_weight is None:
+        return valid.astype(np.float64)
+    cw = np.asarray(class_weight, dtype=np.float64)
+    return np.where(valid, cw[np.where(valid, t, 0)], 0.0)
+
+
+def _reduction_coef(reduction, grad_output, rw, n):
+    """Per-row factor of the gradient of the reduced loss w.r.t. each row's
+    unweighted loss: row weight times the upstream gradient, divided by the
+    weight total for mean."""
+    if reduction == "none":
+        g = np.ones(n) if grad_output is None else np.asarray(grad_output, np.float64).reshape(n)
+        return rw * g
+    g = 1.0 if grad_output is None else float(np.asarray(grad_output, np.float64).reshape(()))
+    wsum = rw.sum()
+    if reduction == "sum":
+        return rw * g
+    return rw * (g / wsum) if wsum > 0 else np.zeros(n)
+
+
 def flce_reference(hidden, weight, targets, bias=None, ignore_index=-100,
                    logit_scale=1.0, softcap=None, reduction="mean",
-                   grad_output=None, compute_grads=True, row_block=256):
+                   grad_output=None, compute_grads=True, row_block=256,
+                   label_smoothing=0.0, z_loss=0.0, class_weight=None):
     """Forward and backward of the loss, by its definition, in fp64.
 
     Arguments follow the card's "Full signature": hidden (N,H), weight (V,H),
     targets (N,) integer ids, bias (V,) or None, ignore_index, logit_scale,
     softcap (None or > 0), reduction "mean" | "sum" | "none".  ``grad_output``
     is the upstream gradient of the returned loss: a scalar for mean/sum, an
-    (N,) vector for none; None means 1.
+    (N,) vector for none; None means 1.  ``label_smoothing``, ``z_loss`` and
+    ``class_weight`` are the variants described in the module docstring.
 
     Returns a dict with
       loss            scalar (mean/sum) or (N,) (none)
-      row_loss        (N,)  lse_i - z_{i,t_i}, 0 on ignored rows
+      row_loss        (N,)  the row's (weighted) loss, 0 on ignored rows
       lse             (N,)  log-sum-exp of the final logits
       argmax, gap     (N,)  first-index argmax and top-1/top-2 gap of z
       hit             (N,)  valid and argmax == target
@@ -121,15 +158,13 @@ def flce_reference(hidden, weight, targets, bias=None, ignore_index=-100,
     if np.any(valid & ((t < 0) | (t >= v))):
         raise ValueError("target id outside [0, V) on a non-ignored row")
     n_valid = int(valid.sum())
+    eps = float(label_smoothing)
+    zl = float(z_loss)
+    rw = _row_weights(t, valid, class_weight)
 
-    # Per-row coefficient of the gradient of the reduced loss w.r.t. row_loss_i.
-    if reduction == "none":
-        g = np.ones(n) if grad_output is None else np.asarray(grad_output, np.float64).reshape(n)
-        coef = np.where(valid, g, 0.0)
-    else:
-        g = 1.0 if grad_output is None else float(np.asarray(grad_output, np.float64).reshape(()))
-        scale = g / n_valid if (reduction == "mean" and n_valid > 0) else (g if reduction == "sum" else 0.0)
-        coef = np.where(valid, scale, 0.0)
+    # Per-row coefficient of the gradient of the reduced loss w.r.t. the
+    # row's unweighted loss (row weight folded in).
+    coef = _reduction_coef(reduction, grad_output, rw, n)
 
     row_loss = np.zeros(n)
     lse = np.zeros(n)
@@ -151,15 +186,19 @@ def flce_reference(hidden, weight, targets, bias=None, ignore_index=-100,
         vr = valid[r0:r1]
         rows = np.arange(r1 - r0)
         zt = np.where(vr, z[rows, np.where(vr, tr, 0)], 0.0)
-        row_loss[r0:r1] = np.where(vr, lse_r - zt, 0.0)
+        # cross-entropy against the smoothed target, plus the z-loss term,
+        # times the row's class weight
+        ce = lse_r - (1.0 - eps) * zt - (eps / v) * z.sum(axis=1)
+        row_loss[r0:r1] = np.where(vr, rw[r0:r1] * (ce + zl * lse_r ** 2), 0.0)
         lse[r0:r1] = lse_r
         argmax[r0:r1] = am_r
         gap[r0:r1] = gap_r
         row_entropy[r0:r1] = ent_r
         if compute_grads:
-            # d loss_i / d z_ij = p_ij - [j == t_i]  (card: "Algorithm", p - onehot)
-            gz = p.copy()
-            gz[rows[vr], tr[vr]] -= 1.0
+            # d loss_i / d z_ij = p_ij - [j == t_i]  (card: "Algorithm", p - onehot);
+            # with the variants (1 + 2 zl lse_i) p_ij - (1 - eps) [j == t_i] - eps / V
+            gz = p * (1.0 + 2.0 * zl * lse_r)[:, None] - eps / v
+            gz[rows[vr], tr[vr]] -= 1.0 - eps
             gz[~vr] = 0.0
             graw = coef[r0:r1, None] * gz * transform_derivative(z, logit_scale, softcap)
             if b is not None:
@@ -169,12 +208,13 @@ def flce_reference(hidden, weight, targets, bias=None, ignore_index=-100,
             grad_w += graw.T @ hr                          # (p - onehot).T @ hidden
 
     hit = valid & (argmax == t)
+    wsum = float(rw.sum())
     if reduction == "none":
         loss = row_loss.copy()
     elif reduction == "sum":
         loss = float(row_loss[valid].sum())
     else:
-        loss = float(row_loss[valid].sum() / n_valid) if n_valid > 0 else math.nan
+        loss = float(row_loss[valid].sum() / wsum) if n_valid > 0 else math.nan
     accuracy = float(hit.sum() / n_valid) if n_valid > 0 else math.nan
     entropy = float(row_entropy[valid].sum() / n_valid) if n_valid > 0 else math.nan
 

@@ -358,3 +358,139 @@ def test_gradient_samples_match_autograd(reduction):
         np.testing.assert_allclose(smp["grad_hidden"], gh[rows], rtol=1e-10, atol=1e-13)
         np.testing.assert_allclose(smp["grad_weight"], gw[vids], rtol=1e-10, atol=1e-13)
         np.testing.assert_allclose(smp["grad_bias"], gb[vids], rtol=1e-10, atol=1e-13)
+
+
+# --------------------------------------------------------------------------- loss variants
+# Label smoothing and class weights each against torch's cross_entropy (value
+# and autograd gradients); the z-loss against torch's logsumexp under
+# autograd and a closed form; the three together by finite differences.
+
+def torch_variant_loss(h, w, b, t, ignore_index, s, cap, reduction, g, eps=0.0, cw=None, zl=0.0):
+    th = torch.tensor(h, requires_grad=True)
+    tw = torch.tensor(w, requires_grad=True)
+    tb = torch.tensor(b, requires_grad=True) if b is not None else None
+    logits = F.linear(th, tw, tb) * s
+    if cap is not None:
+        logits = cap * torch.tanh(logits / cap)
+    tt = torch.tensor(t)
+    loss = F.cross_entropy(logits, tt, ignore_index=ignore_index, reduction=reduction,
+                           label_smoothing=eps, weight=None if cw is None else torch.tensor(cw))
+    if zl:
+        # z-loss term per row, zero on ignored rows, reduced like the loss (no class weights here)
+        valid = (tt != ignore_index).double()
+        zrow = zl * torch.logsumexp(logits, dim=1) ** 2 * valid
+        if reduction == "none":
+            loss = loss + zrow
+        elif reduction == "sum":
+            loss = loss + zrow.sum()
+        else:
+            loss = loss + zrow.sum() / valid.sum()
+    if reduction == "none":
+        (loss * torch.tensor(g)).sum().backward()
+    else:
+        (loss * float(g)).backward()
+    return (loss.detach().numpy(), th.grad.numpy(), tw.grad.numpy(),
+            tb.grad.numpy() if tb is not None else None)
+
+
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+def test_label_smoothing_matches_torch(reduction):
+    h, w, b, t = problem(21, 31, 12, 47, bias=True, wstd=1.0)
+    g = np.random.default_rng(7).standard_normal(31) if reduction == "none" else 0.9
+    for eps, s, cap in [(0.1, 1.0, None), (0.3, 0.7, 2.5), (1.0, 1.0, None)]:
+        ref = flce_reference(h, w, t, b, logit_scale=s, softcap=cap, reduction=reduction, grad_output=g,
+                             label_smoothing=eps)
+        tl, gh, gw, gb = torch_variant_loss(h, w, b, t, -100, s, cap, reduction, g, eps=eps)
+        np.testing.assert_allclose(ref["loss"], tl, rtol=1e-12, atol=1e-13)
+        assert maxnorm_rel(ref["grad_hidden"], gh) < 1e-11
+        assert maxnorm_rel(ref["grad_weight"], gw) < 1e-11
+        assert maxnorm_rel(ref["grad_bias"], gb) < 1e-11
+
+
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+def test_class_weights_match_torch(reduction):
+    h, w, b, t = problem(22, 33, 10, 29, bias=False, wstd=1.0)
+    cw = np.random.default_rng(8).uniform(0.2, 3.0, 29)
+    cw[5] = 0.0
+    g = np.random.default_rng(9).standard_normal(33) if reduction == "none" else 1.4
+    ref = flce_reference(h, w, t, None, reduction=reduction, grad_output=g, class_weight=cw)
+    tl, gh, gw, _ = torch_variant_loss(h, w, None, t, -100, 1.0, None, reduction, g, cw=cw)
+    np.testing.assert_allclose(ref["loss"], tl, rtol=1e-12, atol=1e-13)
+    assert maxnorm_rel(ref["grad_hidden"], gh) < 1e-11
+    assert maxnorm_rel(ref["grad_weight"], gw) < 1e-11
+
+
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+def test_z_loss_matches_autograd(reduction):
+    h, w, b, t = problem(23, 27, 14, 41, bias=True, wstd=1.0)
+    g = np.random.default_rng(10).standard_normal(27) if reduction == "none" else 0.6
+    for zl, s, cap in [(1e-4, 1.0, None), (0.05, 0.8, 3.0)]:
+        ref = flce_reference(h, w, t, b, logit_scale=s, softcap=cap, reduction=reduction, grad_output=g,
+                             z_loss=zl)
+        tl, gh, gw, gb = torch_variant_loss(h, w, b, t, -100, s, cap, reduction, g, zl=zl)
+        np.testing.assert_allclose(ref["loss"], tl, rtol=1e-12, atol=1e-13)
+        assert maxnorm_rel(ref["grad_hidden"], gh) < 1e-11
+        assert maxnorm_rel(ref["grad_weight"], gw) < 1e-11
+        assert maxnorm_rel(ref["grad_bias"], gb) < 1e-11
+
+
+def test_z_loss_and_smoothing_zero_weight_closed_form():
+    # zero weight: every z is 0, lse = ln V, the smoothed cross-entropy is ln V
+    # for any eps, and the z-loss adds zl (ln V)^2; dL/dz_j = (1 + 2 zl ln V)/V
+    # - (1 - eps)[j = t] - eps/V, so grad_weight[j] = sum_i coef_i dL/dz_ij h_i.
+    v = 1000
+    lnv = golden_ln_v()[v]
+    rng = np.random.default_rng(24)
+    n, hd = 9, 5
+    h = rng.standard_normal((n, hd))
+    w = np.zeros((v, hd))
+    t = rng.integers(0, v, n)
+    zl, eps = 0.01, 0.2
+    ref = flce_reference(h, w, t, reduction="sum", label_smoothing=eps, z_loss=zl)
+    assert abs(ref["loss"] - n * (lnv + zl * lnv ** 2)) < 1e-9 * n * lnv
+    dz = np.full((n, v), (1.0 + 2.0 * zl * lnv) / v - eps / v)
+    dz[np.arange(n), t] -= 1.0 - eps
+    assert maxnorm_rel(ref["grad_weight"], dz.T @ h) < 1e-12
+    assert np.max(np.abs(ref["grad_hidden"])) == 0.0
+
+
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+def test_variants_together_finite_differences(reduction):
+    h, w, b, t = problem(25, 3, 4, 6, bias=True, ignore_frac=0.0, wstd=1.0)
+    t[1] = -100
+    cw = np.array([0.5, 2.0, 1.0, 0.0, 1.5, 3.0])
+    g = np.array([0.7, -1.1, 1.9]) if reduction == "none" else 1.0
+    kw = dict(logit_scale=0.8, softcap=1.2, reduction=reduction, label_smoothing=0.15, z_loss=0.03,
+              class_weight=cw)
+    ref = flce_reference(h, w, t, b, grad_output=g, **kw)
+
+    def f(hh, ww, bb):
+        out = flce_reference(hh, ww, t, bb, compute_grads=False, **kw)["loss"]
+        return float(np.sum(out * g)) if reduction == "none" else float(out)
+
+    eps = 1e-6
+    for name, arr, grad in [("h", h, ref["grad_hidden"]), ("w", w, ref["grad_weight"]),
+                            ("b", b, ref["grad_bias"])]:
+        fd = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            ap, am = arr.copy(), arr.copy()
+            ap[idx] += eps
+            am[idx] -= eps
+            args_p = {"h": (ap, w, b), "w": (h, ap, b), "b": (h, w, ap)}[name]
+            args_m = {"h": (am, w, b), "w": (h, am, b), "b": (h, w, am)}[name]
+            fd[idx] = (f(*args_p) - f(*args_m)) / (2 * eps)
+        assert maxnorm_rel(grad, fd) < 1e-6, name
+
+
+def test_class_weights_scale_whole_row_loss():
+    # the combination reading: with uniform weights c the mean is unchanged and
+    # the sum scales by c; every variant term is inside the weighted row loss
+    h, w, b, t = problem(26, 20, 6, 15, bias=False)
+    kw = dict(label_smoothing=0.1, z_loss=0.02)
+    base_m = flce_reference(h, w, t, compute_grads=False, reduction="mean", **kw)["loss"]
+    base_s = flce_reference(h, w, t, compute_grads=False, reduction="sum", **kw)["loss"]
+    cw = np.full(15, 2.5)
+    assert abs(flce_reference(h, w, t, compute_grads=False, reduction="mean", class_weight=cw, **kw)["loss"]
+               - base_m) < 1e-12 * abs(base_m)
+    assert abs(flce_reference(h, w, t, compute_grads=False, reduction="sum", class_weight=cw, **kw)["loss"]
+               - 2.5 * base_s) < 1e-12 * abs(base_s)
