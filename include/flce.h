@@ -81,6 +81,18 @@ typedef struct flce_problem {
    * not the result beyond fp32 summation order. */
   int32_t fwd_tiles_per_split; /* vocabulary tiles (256 ids) per forward split      */
   int32_t bwd_vocab_chunk;     /* vocabulary ids per backward chunk (multiple of 256) */
+  /* Cross-entropy variants on the same vocabulary sweep (textbook
+   * definitions, not the card's; 0 / NULL = plain cross-entropy, bit for bit):
+   *   label_smoothing eps in [0, 1]: target (1 - eps) one-hot + eps/V uniform,
+   *     row loss lse - (1 - eps) z_t - (eps/V) sum_j z_j;
+   *   z_loss zl (finite): row loss += zl * lse^2;
+   *   class_weight: device fp32 [V] or NULL: row i's whole loss times
+   *     w[t_i]; the mean divides by the sum of w[t_i] over non-ignored rows
+   *     (metrics stay unweighted).  Weights must be finite; not read for
+   *     ignored rows or out-of-range targets. */
+  float label_smoothing;
+  float z_loss;
+  const float* class_weight;
 } flce_problem_t;
 
 /* Bytes of workspace flce_forward / flce_backward need for problem *p

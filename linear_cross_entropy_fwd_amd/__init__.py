@@ -52,21 +52,33 @@ def _check_inputs(hidden, weight, targets, bias):
             raise ValueError("tensors must be contiguous")
 
 
+def _check_class_weight(class_weight, weight):
+    if class_weight is None:
+        return
+    if (class_weight.shape != (weight.shape[0],) or class_weight.dtype != torch.float32
+            or class_weight.device != weight.device or not class_weight.is_contiguous()):
+        raise ValueError("class_weight must be a contiguous float32 (V,) tensor on the device of weight")
+
+
 def problem_for(hidden, weight, bias, ignore_index=-100, logit_scale=1.0, softcap=None,
                 reduction="mean", return_metrics=False, fwd_tiles_per_split=0,
-                bwd_vocab_chunk=0) -> Problem:
+                bwd_vocab_chunk=0, label_smoothing=0.0, z_loss=0.0, class_weight=None) -> Problem:
+    _check_class_weight(class_weight, weight)
     return make_problem(hidden.shape[0], hidden.shape[1], weight.shape[0], _DTYPES[hidden.dtype],
                         reduction, ignore_index, logit_scale, softcap, return_metrics,
-                        bias is not None, fwd_tiles_per_split, bwd_vocab_chunk)
+                        bias is not None, fwd_tiles_per_split, bwd_vocab_chunk, label_smoothing,
+                        z_loss, _ptr(class_weight))
 
 
 def flce_forward(hidden, weight, targets, bias=None, *, ignore_index=-100, logit_scale=1.0,
                  softcap=None, reduction="mean", return_metrics=False, want_lse=True,
-                 workspace: Optional[torch.Tensor] = None, fwd_tiles_per_split=0):
+                 workspace: Optional[torch.Tensor] = None, fwd_tiles_per_split=0,
+                 label_smoothing=0.0, z_loss=0.0, class_weight=None):
     """Tensor-level ``flce_forward``: returns (loss, lse or None, metrics or None)."""
     _check_inputs(hidden, weight, targets, bias)
     p = problem_for(hidden, weight, bias, ignore_index, logit_scale, softcap, reduction,
-                    return_metrics, fwd_tiles_per_split=fwd_tiles_per_split)
+                    return_metrics, fwd_tiles_per_split=fwd_tiles_per_split,
+                    label_smoothing=label_smoothing, z_loss=z_loss, class_weight=class_weight)
     n = hidden.shape[0]
     dev = hidden.device
     loss = torch.empty(n if reduction == "none" else 1, dtype=torch.float32, device=dev)
@@ -88,11 +100,12 @@ def flce_forward(hidden, weight, targets, bias=None, *, ignore_index=-100, logit
 def flce_backward(hidden, weight, targets, bias, lse, grad_loss=None, *, ignore_index=-100,
                   logit_scale=1.0, softcap=None, reduction="mean", need_hidden=True,
                   need_weight=True, need_bias=True, workspace: Optional[torch.Tensor] = None,
-                  bwd_vocab_chunk=0):
+                  bwd_vocab_chunk=0, label_smoothing=0.0, z_loss=0.0, class_weight=None):
     """Tensor-level ``flce_backward``: returns (grad_hidden, grad_weight, grad_bias)."""
     _check_inputs(hidden, weight, targets, bias)
     p = problem_for(hidden, weight, bias, ignore_index, logit_scale, softcap, reduction,
-                    False, bwd_vocab_chunk=bwd_vocab_chunk)
+                    False, bwd_vocab_chunk=bwd_vocab_chunk, label_smoothing=label_smoothing,
+                    z_loss=z_loss, class_weight=class_weight)
     dev = hidden.device
     if grad_loss is not None:
         grad_loss = grad_loss.to(device=dev, dtype=torch.float32).contiguous()
@@ -116,12 +129,14 @@ def flce_backward(hidden, weight, targets, bias, lse, grad_loss=None, *, ignore_
 class _FusedLinearCrossEntropy(torch.autograd.Function):
     @staticmethod
     def forward(ctx, hidden, weight, targets, bias, ignore_index, logit_scale, softcap,
-                reduction, return_metrics):
+                reduction, return_metrics, label_smoothing, z_loss, class_weight):
         loss, lse, metrics = flce_forward(hidden, weight, targets, bias, ignore_index=ignore_index,
                                           logit_scale=logit_scale, softcap=softcap,
-                                          reduction=reduction, return_metrics=return_metrics)
-        ctx.save_for_backward(hidden, weight, targets, bias, lse)
-        ctx.opts = (ignore_index, logit_scale, softcap, reduction)
+                                          reduction=reduction, return_metrics=return_metrics,
+                                          label_smoothing=label_smoothing, z_loss=z_loss,
+                                          class_weight=class_weight)
+        ctx.save_for_backward(hidden, weight, targets, bias, lse, class_weight)
+        ctx.opts = (ignore_index, logit_scale, softcap, reduction, label_smoothing, z_loss)
         if metrics is None:
             metrics = torch.empty(0, device=hidden.device)
         ctx.mark_non_differentiable(metrics)
@@ -129,30 +144,36 @@ class _FusedLinearCrossEntropy(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, grad_loss, _grad_metrics):
-        hidden, weight, targets, bias, lse = ctx.saved_tensors
-        ignore_index, logit_scale, softcap, reduction = ctx.opts
+        hidden, weight, targets, bias, lse, class_weight = ctx.saved_tensors
+        ignore_index, logit_scale, softcap, reduction, label_smoothing, z_loss = ctx.opts
         nh, nw, _, nb = ctx.needs_input_grad[:4]
         gh, gw, gb = flce_backward(hidden, weight, targets, bias, lse, grad_loss,
                                    ignore_index=ignore_index, logit_scale=logit_scale,
                                    softcap=softcap, reduction=reduction, need_hidden=nh,
-                                   need_weight=nw, need_bias=nb and bias is not None)
-        return gh, gw, None, gb, None, None, None, None, None
+                                   need_weight=nw, need_bias=nb and bias is not None,
+                                   label_smoothing=label_smoothing, z_loss=z_loss,
+                                   class_weight=class_weight)
+        return gh, gw, None, gb, None, None, None, None, None, None, None, None
 
 
 def fused_linear_cross_entropy(hidden, weight, targets, bias=None, ignore_index=-100,
                                logit_scale=1.0, softcap=None, reduction="mean",
-                               return_metrics=False):
+                               return_metrics=False, label_smoothing=0.0, z_loss=0.0,
+                               class_weight=None):
     """Cross-entropy of ``hidden @ weight.T (+ bias)`` without materialising logits.
 
     Returns ``loss`` (fp32; scalar for mean/sum, (N,) for none), or
     ``(loss, {"mean_token_accuracy": ..., "entropy": ...})`` with
     ``return_metrics=True``.  hidden, weight and bias receive gradients.
+    ``label_smoothing``, ``z_loss`` and ``class_weight`` (fp32 (V,), not
+    differentiated) select the variants described in include/flce.h.
     """
     if reduction not in ("mean", "sum", "none"):
         raise ValueError(f"unknown reduction {reduction!r}")
     loss, metrics = _FusedLinearCrossEntropy.apply(hidden, weight, targets, bias, ignore_index,
                                                    logit_scale, softcap, reduction,
-                                                   return_metrics)
+                                                   return_metrics, label_smoothing, z_loss,
+                                                   class_weight)
     if not return_metrics:
         return loss
     return loss, {"mean_token_accuracy": metrics[0], "entropy": metrics[1]}

@@ -70,6 +70,11 @@ flce_status_t check_problem(const flce_problem_t* p) {
   if (p->fwd_tiles_per_split < 0) return fail(FLCE_ERR_INVALID_ARGUMENT, "fwd_tiles_per_split < 0");
   if (p->bwd_vocab_chunk < 0 || p->bwd_vocab_chunk % kTile != 0)
     return fail(FLCE_ERR_INVALID_ARGUMENT, "bwd_vocab_chunk must be 0 or a positive multiple of 256");
+  if (!(p->label_smoothing >= 0.f && p->label_smoothing <= 1.f))
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "label_smoothing must be in [0, 1]");
+  if (!isfinite(p->z_loss)) return fail(FLCE_ERR_INVALID_ARGUMENT, "z_loss is not finite");
+  if (p->class_weight && !aligned(p->class_weight, 4))
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "class_weight is misaligned");
   return FLCE_OK;
 }
 
@@ -77,7 +82,7 @@ flce_status_t check_problem(const flce_problem_t* p) {
 
 struct FwdLayout {
   int n_tok_tiles, n_voc_tiles, tiles_per_split, n_splits;
-  size_t off_status, off_part, off_rowloss, off_rowent, off_rowflag, total;
+  size_t off_status, off_part, off_rowloss, off_rowent, off_rowflag, off_roww, total;
 };
 
 FwdLayout fwd_layout(const flce_problem_t& p) {
@@ -97,10 +102,11 @@ FwdLayout fwd_layout(const flce_problem_t& p) {
     return o;
   };
   L.off_status = take(16);
-  L.off_part = take((size_t)6 * L.n_splits * N * 4);
+  L.off_part = take((size_t)7 * L.n_splits * N * 4);
   L.off_rowloss = take((size_t)N * 4);
   L.off_rowent = take((size_t)N * 4);
   L.off_rowflag = take((size_t)N * 4);
+  L.off_roww = take((size_t)N * 4);
   L.total = off;
   return L;
 }
@@ -219,6 +225,7 @@ flce_status_t flce_forward(const flce_problem_t* p, const void* hidden, const vo
     fa.s = p->logit_scale;
     fa.cap = cap_of(*p);
     fa.inv_cap = 1.f / fa.cap;
+    fa.zsum = p->label_smoothing > 0.f;
     e = flce::launch_forward_tiles(p->dtype, metrics_on, p->has_bias != 0, p->softcap > 0.f, fa, st);
     if (e != hipSuccess) return hip_fail(e, "forward tile kernel");
 
@@ -235,6 +242,11 @@ flce_status_t flce_forward(const flce_problem_t* p, const void* hidden, const vo
     ca.ignore_index = p->ignore_index;
     ca.tiles_per_split = L.tiles_per_split;
     ca.n_splits = L.n_splits;
+    ca.zsum = fa.zsum;
+    ca.eps = p->label_smoothing;
+    ca.z_loss = p->z_loss;
+    ca.class_weight = p->class_weight;
+    ca.row_w = p->class_weight ? reinterpret_cast<float*>(ws + L.off_roww) : nullptr;
     e = flce::launch_forward_combine(metrics_on, ca, st);
     if (e != hipSuccess) return hip_fail(e, "forward combine kernel");
   }
@@ -242,6 +254,7 @@ flce_status_t flce_forward(const flce_problem_t* p, const void* hidden, const vo
   ra.row_loss = reinterpret_cast<const float*>(ws + L.off_rowloss);
   ra.row_ent = reinterpret_cast<const float*>(ws + L.off_rowent);
   ra.row_flag = reinterpret_cast<const int*>(ws + L.off_rowflag);
+  ra.row_w = p->class_weight ? reinterpret_cast<const float*>(ws + L.off_roww) : nullptr;
   ra.loss = loss;
   ra.metrics = metrics;
   ra.status = reinterpret_cast<uint32_t*>(ws + L.off_status);
@@ -296,7 +309,8 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
   }
 
   float* scale = reinterpret_cast<float*>(ws + L.off_scale);
-  flce::PrepArgs pa{targets, grad_loss, scale, N, p->ignore_index, p->reduction, p->logit_scale};
+  flce::PrepArgs pa{targets, grad_loss, p->class_weight, scale, N, V, p->ignore_index, p->reduction,
+                    p->logit_scale};
   if ((e = flce::launch_backward_prep(pa, st)) != hipSuccess) return hip_fail(e, "backward prep kernel");
 
   char* ht = ws + L.off_ht;
@@ -345,6 +359,10 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
     ga.s = p->logit_scale;
     ga.cap = cap_of(*p);
     ga.inv_cap = 1.f / ga.cap;
+    ga.class_weight = p->class_weight;
+    ga.eps_v = p->label_smoothing / (float)V;
+    ga.keep = 1.f - p->label_smoothing;
+    ga.zl2 = 2.f * p->z_loss;
     if ((e = flce::launch_backward_g(p->dtype, p->has_bias != 0, p->softcap > 0.f, ga, st)) != hipSuccess)
       return hip_fail(e, "backward G kernel");
     if (want_dh) {

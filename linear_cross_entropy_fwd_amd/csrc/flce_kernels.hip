@@ -117,12 +117,12 @@ __device__ __forceinline__ int col_min4(int x) {
 // Per-column online state between vocabulary tiles, in LDS so that it does
 // not occupy registers across the GEMM: 7 values x WJ column blocks x 16
 // columns per wave (14 KB next to the 128 KB stage buffers).
-__shared__ float g_fwd_state[7 * 4 * 8 * 16];
+__shared__ float g_fwd_state[8 * 4 * 8 * 16];
 
 template <int D, bool METRICS, bool BIAS, bool CAP, int W>
 __global__ __launch_bounds__(W * 64) void fwd_tiles_kernel(FwdArgs a) {
   constexpr int EB = Elem<D>::bytes, WI = Gemm<W>::WI, WJ = Gemm<W>::WJ;
-  static_assert(7 * WJ * W * 16 <= 7 * 4 * 8 * 16, "online state does not fit g_fwd_state");
+  static_assert(8 * WJ * W * 16 <= 8 * 4 * 8 * 16, "online state does not fit g_fwd_state");
   static_assert(Gemm<W>::GN * 16 * WJ == TILE && 2 * 16 * WI == TILE, "two wave rows share each column");
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = Gemm<W>::wm(wave), wn = Gemm<W>::wn(wave), c16 = lane & 15, q = lane >> 4;
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(W * 64) void fwd_tiles_kernel(FwdArgs a) {
 
   // Slot k of column block j of this lane's column: 0 m, 1 S, 2 U,
   // 3 z_target, 4 argmax value, 5 argmax id, 6 target id (-1 when the row is
-  // ignored or its target is out of range).  The four lanes of a column hold
+  // ignored or its target is out of range), 7 sum of z (label smoothing).  The four lanes of a column hold
   // the same m, S, U and argmax (they are merged every tile); z_target is
   // written only by the lane that holds the target's row.
   float* st = g_fwd_state + wave * 16 + c16;
@@ -156,6 +156,7 @@ __global__ __launch_bounds__(W * 64) void fwd_tiles_kernel(FwdArgs a) {
       FST(4, j) = -INFINITY;
       FST(5, j) = __int_as_float(0x7fffffff);
       FST(6, j) = __int_as_float((tv != a.ignore_index && tv >= 0 && tv < a.V) ? (int)tv : -1);
+      FST(7, j) = 0.f;
     }
   }
 
@@ -200,6 +201,16 @@ __global__ __launch_bounds__(W * 64) void fwd_tiles_kernel(FwdArgs a) {
       for (int i = 0; i < WI; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) zl = fmaxf(zl, z[i][e]);
+      if (a.zsum) {  // label smoothing: the sum of z over the vocabulary
+        float zs = 0.f;
+#pragma unroll
+        for (int i = 0; i < WI; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (!ragged || 16 * i + e < vrem) zs = zs + z[i][e];
+        zs = col_sum4(zs);
+        if (q == 0) FST(7, j) = FST(7, j) + zs;
+      }
       const float zmax = col_max4(zl);
       const float mold = FST(0, j);
       const float mnew = fmaxf(mold, zmax);
@@ -263,7 +274,7 @@ __global__ __launch_bounds__(W * 64) void fwd_tiles_kernel(FwdArgs a) {
     }
   }
 
-  float m[WJ], S[WJ], U[WJ], zt[WJ], av[WJ];
+  float m[WJ], S[WJ], U[WJ], zt[WJ], av[WJ], zs[WJ];
   int ai[WJ];
 #pragma unroll
   for (int j = 0; j < WJ; ++j) {
@@ -273,6 +284,7 @@ __global__ __launch_bounds__(W * 64) void fwd_tiles_kernel(FwdArgs a) {
     zt[j] = FST(3, j);
     av[j] = FST(4, j);
     ai[j] = __float_as_int(FST(5, j));
+    zs[j] = FST(7, j);
   }
 #undef FST
 
@@ -288,6 +300,7 @@ __global__ __launch_bounds__(W * 64) void fwd_tiles_kernel(FwdArgs a) {
       xs[3 * TILE + tok] = zt[j];
       xs[4 * TILE + tok] = av[j];
       xs[5 * TILE + tok] = __int_as_float(ai[j]);
+      xs[6 * TILE + tok] = zs[j];
     }
   }
   __syncthreads();
@@ -297,6 +310,7 @@ __global__ __launch_bounds__(W * 64) void fwd_tiles_kernel(FwdArgs a) {
       const int tok = wn * 16 * WJ + 16 * j + c16;
       lse_merge<METRICS>(m[j], S[j], U[j], xs[0 * TILE + tok], xs[1 * TILE + tok], xs[2 * TILE + tok]);
       zt[j] = zt[j] + xs[3 * TILE + tok];  // the non-owner holds +0
+      zs[j] = zs[j] + xs[6 * TILE + tok];
       if (METRICS) argmax_merge(av[j], ai[j], xs[4 * TILE + tok], __float_as_int(xs[5 * TILE + tok]));
       const int64_t n = n0 + tok;
       if (n < a.N) {
@@ -308,6 +322,7 @@ __global__ __launch_bounds__(W * 64) void fwd_tiles_kernel(FwdArgs a) {
         p[3 * stride] = zt[j];
         p[4 * stride] = av[j];
         p[5 * stride] = __int_as_float(ai[j]);
+        if (a.zsum) p[6 * stride] = zs[j];
       }
     }
   }
@@ -322,16 +337,18 @@ __global__ __launch_bounds__(W * 64) void fwd_tiles_kernel(FwdArgs a) {
 template <bool METRICS>
 __global__ __launch_bounds__(256) void fwd_combine_kernel(CombineArgs a) {
   constexpr int ROWS = 32, PARTS = 8;
-  __shared__ float sh[5][PARTS][ROWS];
+  __shared__ float sh[6][PARTS][ROWS];
   const int t = threadIdx.x, rl = t % ROWS, p = t / ROWS;
   const int64_t n = (int64_t)blockIdx.x * ROWS + rl;
   const bool in = n < a.N;
   const int64_t stride = (int64_t)a.n_splits * a.N;
   const float* pm = a.part + (in ? n : 0);
-  float M = -INFINITY, S = 0.f, U = 0.f, av = -INFINITY;
+  float M = -INFINITY, S = 0.f, U = 0.f, av = -INFINITY, Z = 0.f;
   int ai = 0x7fffffff;
   if (in) {
     for (int k = p; k < a.n_splits; k += PARTS) M = fmaxf(M, pm[(int64_t)k * a.N]);
+    if (a.zsum)
+      for (int k = p; k < a.n_splits; k += PARTS) Z = Z + pm[6 * stride + (int64_t)k * a.N];
     for (int k = p; k < a.n_splits; k += PARTS) {
       const float mk = pm[(int64_t)k * a.N];
       if (mk != -INFINITY) {
@@ -350,26 +367,33 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(CombineArgs a) {
   sh[2][p][rl] = U;
   sh[3][p][rl] = av;
   sh[4][p][rl] = __int_as_float(ai);
+  sh[5][p][rl] = Z;
   __syncthreads();
   if (p != 0 || !in) return;
   for (int q = 1; q < PARTS; ++q) {
     lse_merge<METRICS>(M, S, U, sh[0][q][rl], sh[1][q][rl], sh[2][q][rl]);
     if (METRICS) argmax_merge(av, ai, sh[3][q][rl], __float_as_int(sh[4][q][rl]));
+    Z = Z + sh[5][q][rl];
   }
   const int64_t tv = a.targets[n];
   const bool valid = tv != a.ignore_index;
   const bool bad = valid && (tv < 0 || tv >= a.V);
   const float logS = logf(S);
   const float lse = M + logS;
-  float row = 0.f;
+  float row = 0.f, rw = 0.f;
   if (valid) {
     if (bad) {
       row = NAN;
     } else {
       const int owner = (int)((tv / TILE) / a.tiles_per_split);
-      row = lse - pm[3 * stride + (int64_t)owner * a.N];
+      const float zt = pm[3 * stride + (int64_t)owner * a.N];
+      // smoothed cross-entropy + z-loss, times the row's class weight (all
+      // of it exact for the plain loss: eps = 0, z_loss = 0, weight 1)
+      rw = a.class_weight ? a.class_weight[tv] : 1.f;
+      row = rw * ((lse - (1.f - a.eps) * zt) - (a.eps / (float)a.V) * Z + a.z_loss * (lse * lse));
     }
   }
+  if (a.row_w) a.row_w[n] = rw;
   if (a.lse_out) a.lse_out[n] = lse;
   if (a.loss_rows) a.loss_rows[n] = row;
   a.row_loss[n] = row;
@@ -383,14 +407,15 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(CombineArgs a) {
 
 template <bool METRICS>
 __global__ __launch_bounds__(1024) void fwd_reduce_kernel(ReduceArgs a) {
-  __shared__ double sh_l[1024], sh_e[1024];
+  __shared__ double sh_l[1024], sh_e[1024], sh_w[1024];
   __shared__ int sh_v[1024], sh_h[1024], sh_b[1024];
   const int t = threadIdx.x;
-  double sl = 0.0, se = 0.0;
+  double sl = 0.0, se = 0.0, sw = 0.0;
   int nv = 0, nh = 0, nb = 0;
   for (int64_t n = t; n < a.N; n += 1024) {
     const int f = a.row_flag[n];
     sl += (double)a.row_loss[n];
+    if (a.row_w) sw += (double)a.row_w[n];
     nv += f & 1;
     nh += (f >> 1) & 1;
     nb |= (f >> 2) & 1;
@@ -398,6 +423,7 @@ __global__ __launch_bounds__(1024) void fwd_reduce_kernel(ReduceArgs a) {
   }
   sh_l[t] = sl;
   sh_e[t] = se;
+  sh_w[t] = sw;
   sh_v[t] = nv;
   sh_h[t] = nh;
   sh_b[t] = nb;
@@ -406,6 +432,7 @@ __global__ __launch_bounds__(1024) void fwd_reduce_kernel(ReduceArgs a) {
     if (t < w) {
       sh_l[t] += sh_l[t + w];
       sh_e[t] += sh_e[t + w];
+      sh_w[t] += sh_w[t + w];
       sh_v[t] += sh_v[t + w];
       sh_h[t] += sh_h[t + w];
       sh_b[t] |= sh_b[t + w];
@@ -414,7 +441,9 @@ __global__ __launch_bounds__(1024) void fwd_reduce_kernel(ReduceArgs a) {
   }
   if (t == 0) {
     const int64_t nvalid = sh_v[0];
-    if (a.reduction == 0) a.loss[0] = nvalid > 0 ? (float)(sh_l[0] / (double)nvalid) : NAN;
+    // mean: over the count of valid rows, or over their class-weight total
+    const double den = a.row_w ? sh_w[0] : (double)nvalid;
+    if (a.reduction == 0) a.loss[0] = nvalid > 0 ? (float)(sh_l[0] / den) : NAN;
     if (a.reduction == 1) a.loss[0] = (float)sh_l[0];
     if (METRICS && a.metrics) {
       a.metrics[0] = nvalid > 0 ? (float)((double)sh_h[0] / (double)nvalid) : NAN;
@@ -427,10 +456,18 @@ __global__ __launch_bounds__(1024) void fwd_reduce_kernel(ReduceArgs a) {
 // ------------------------------------------------------------------ backward helpers
 
 __global__ __launch_bounds__(1024) void bwd_prep_kernel(PrepArgs a) {
-  __shared__ int sh[1024];
+  // the mean's denominator: the count of non-ignored rows, or with class
+  // weights their weight total (in-range targets only; a bad target makes
+  // the gradient NaN anyway), summed in fp64 in a fixed order
+  __shared__ double sh[1024];
   const int t = threadIdx.x;
-  int nv = 0;
-  for (int64_t n = t; n < a.N; n += 1024) nv += a.targets[n] != a.ignore_index ? 1 : 0;
+  double nv = 0.0;
+  for (int64_t n = t; n < a.N; n += 1024) {
+    const int64_t tv = a.targets[n];
+    if (tv == a.ignore_index) continue;
+    if (!a.class_weight) nv += 1.0;
+    else if (tv >= 0 && tv < a.V) nv += (double)a.class_weight[tv];
+  }
   sh[t] = nv;
   __syncthreads();
   for (int w = 512; w > 0; w >>= 1) {
@@ -441,7 +478,7 @@ __global__ __launch_bounds__(1024) void bwd_prep_kernel(PrepArgs a) {
     float scale = 1.f;
     if (a.reduction != 2) {
       const float g = a.grad_loss ? a.grad_loss[0] : 1.f;
-      if (a.reduction == 0) scale = sh[0] > 0 ? g / (float)sh[0] : 0.f;
+      if (a.reduction == 0) scale = sh[0] > 0.0 ? (float)((double)g / sh[0]) : 0.f;
       else scale = g;
     }
     a.scale[0] = scale * a.s;
@@ -742,10 +779,12 @@ __global__ __launch_bounds__(W * 64) void bwd_g_kernel(GArgs a) {
     gemm_nt_tile<D, W>(acc, A, B);
   }
 
-  // Per column: lse, the gradient factor and the target id.  A dead column
-  // (past N or ignored) gets lse = +inf and factor 0, so its p is 0 and its
-  // G column 0 without a select per element.
-  float lse[WJ], coef[WJ];
+  // Per column: lse, the gradient factor (row weight times the per-row
+  // upstream gradient), the softmax factor 1 + 2 z_loss lse and the target
+  // id.  A dead column (past N or ignored) gets lse = +inf and factor 0, so
+  // its p is 0 and its G column 0 without a select per element.
+  //   dL/dz_j = w (pscale p_j - keep [j = t] - eps/V),  keep = 1 - eps
+  float lse[WJ], coef[WJ], pscale[WJ];
   int tgt[WJ];
 #pragma unroll
   for (int j = 0; j < WJ; ++j) {
@@ -753,15 +792,18 @@ __global__ __launch_bounds__(W * 64) void bwd_g_kernel(GArgs a) {
     tgt[j] = -1;
     lse[j] = INFINITY;
     coef[j] = 0.f;
+    pscale[j] = 1.f;
     if (n < a.N) {
       const int64_t tv = a.targets[n];
       if (tv != a.ignore_index) {
         lse[j] = a.lse[n];
+        pscale[j] = fmaf(a.zl2, lse[j], 1.f);
         if (tv < 0 || tv >= a.V) {
           coef[j] = NAN;
         } else {
           tgt[j] = (int)tv;
           coef[j] = (a.none_reduction && a.grad_rows) ? a.grad_rows[n] : 1.f;
+          if (a.class_weight) coef[j] = coef[j] * a.class_weight[tv];
         }
       }
     }
@@ -798,7 +840,7 @@ __global__ __launch_bounds__(W * 64) void bwd_g_kernel(GArgs a) {
         const float qc = soft_cap(a.s * yr, a.cap, a.inv_cap) * a.inv_cap;
         cf = fmaf(-qc, qc, 1.f);
       }
-      if (tl[j] >= 0) onehot[j] = cf * coef[j];
+      if (tl[j] >= 0) onehot[j] = cf * (coef[j] * a.keep);
     }
   }
 #pragma unroll
@@ -811,7 +853,7 @@ __global__ __launch_bounds__(W * 64) void bwd_g_kernel(GArgs a) {
         if (BIAS) y = y + bv[i][e];
         y = a.s * y;
         if (CAP) y = soft_cap(y, a.cap, a.inv_cap);
-        float g = fast_exp2((y - lse[j]) * LOG2E);
+        float g = fmaf(fast_exp2((y - lse[j]) * LOG2E), pscale[j], -a.eps_v);
         if (CAP) {
           const float qc = y * a.inv_cap;
           g = g * fmaf(-qc, qc, 1.f);

@@ -39,9 +39,10 @@ struct FwdArgs {
   const char* weight;
   const char* bias;
   const int64_t* targets;
-  float* part;  // [6][n_splits][N]: m, S, U, z_target, argmax value, argmax id
+  float* part;  // [7][n_splits][N]: m, S, U, z_target, argmax value, argmax id, sum of z
   int64_t N, H, V, ignore_index;
   int n_tok_tiles, n_voc_tiles, tiles_per_split, n_splits;
+  int zsum;  // 1: also the sum of z over the vocabulary (label smoothing)
   float s, cap, inv_cap;
 };
 
@@ -53,14 +54,19 @@ struct CombineArgs {
   float* row_loss;  // workspace [N]
   float* row_ent;   // workspace [N]
   int* row_flag;    // workspace [N]: bit0 valid, bit1 hit, bit2 bad target
+  const float* class_weight;  // [V] or null
+  float* row_w;     // workspace [N]: the row's weight (0 if ignored or bad), or null
   int64_t N, V, ignore_index;
   int tiles_per_split, n_splits;
+  int zsum;         // partial 6 holds the sum of z
+  float eps, z_loss;  // label smoothing, z-loss coefficient
 };
 
 struct ReduceArgs {
   const float* row_loss;
   const float* row_ent;
   const int* row_flag;
+  const float* row_w;  // null: mean over the count of valid rows; else over the sum of row_w
   float* loss;      // [1] (mean/sum), unused for none
   float* metrics;   // [2] or null
   uint32_t* status;
@@ -71,8 +77,9 @@ struct ReduceArgs {
 struct PrepArgs {
   const int64_t* targets;
   const float* grad_loss;  // null = 1
+  const float* class_weight;  // [V] or null: mean over the weight total
   float* scale;            // out [1]: uniform gradient factor (reduction * upstream * s)
-  int64_t N, ignore_index;
+  int64_t N, V, ignore_index;
   int reduction;
   float s;
 };
@@ -98,6 +105,8 @@ struct GArgs {
   int cv, cvpad, npad, n_tok_tiles, n_voc_tiles;
   int none_reduction;
   float s, cap, inv_cap;
+  const float* class_weight;  // [V] or null
+  float eps_v, keep, zl2;     // eps / V, 1 - eps, 2 * z_loss
 };
 
 struct DhArgs {

@@ -59,6 +59,11 @@ def base(**kw):
     (dict(softcap=float("inf")), INVALID),
     (dict(fwd_tiles_per_split=-2), INVALID),
     (dict(bwd_vocab_chunk=1000), INVALID),
+    (dict(label_smoothing=-0.1), INVALID),
+    (dict(label_smoothing=1.5), INVALID),
+    (dict(label_smoothing=float("nan")), INVALID),
+    (dict(z_loss=float("inf")), INVALID),
+    (dict(class_weight=(1 << 40) + 2), INVALID),    # misaligned fp32 array
 ])
 def test_invalid_problems(kw, status):
     p = base(**kw)

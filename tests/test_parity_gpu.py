@@ -16,29 +16,33 @@ pytestmark = pytest.mark.gpu
 
 
 def run_case(w: fi.Workload, *, backward=True, bwd_vocab_chunk=0, fwd_tiles_per_split=0,
-             grad_output=None, d=None):
+             grad_output=None, d=None, label_smoothing=0.0, z_loss=0.0, class_weight=None):
     import linear_cross_entropy_fwd_amd as flce
     log_case(f"{w.name} n={w.n} h={w.h} v={w.v} dtype={w.dtype} red={w.reduction} "
-             f"chunk={bwd_vocab_chunk} tps={fwd_tiles_per_split}")
+             f"chunk={bwd_vocab_chunk} tps={fwd_tiles_per_split} eps={label_smoothing} zl={z_loss} "
+             f"cw={class_weight is not None}")
     if d is None:
         d = fill_argmax_targets(w, fi.generate(w))
     g = gpu_inputs(d)
+    cw = None if class_weight is None else torch.as_tensor(class_weight, dtype=torch.float32).cuda()
+    var = dict(label_smoothing=label_smoothing, z_loss=z_loss, class_weight=cw)
     loss, lse, metrics = flce.flce_forward(
         g["hidden"], g["weight"], g["targets"], g["bias"], ignore_index=w.ignore_index,
         logit_scale=w.logit_scale, softcap=w.softcap, reduction=w.reduction,
-        return_metrics=w.return_metrics, fwd_tiles_per_split=fwd_tiles_per_split)
+        return_metrics=w.return_metrics, fwd_tiles_per_split=fwd_tiles_per_split, **var)
     grads = None
     if backward:
         go = None if grad_output is None else torch.as_tensor(grad_output, dtype=torch.float32)
         grads = flce.flce_backward(
             g["hidden"], g["weight"], g["targets"], g["bias"], lse, go, ignore_index=w.ignore_index,
             logit_scale=w.logit_scale, softcap=w.softcap, reduction=w.reduction,
-            bwd_vocab_chunk=bwd_vocab_chunk)
+            bwd_vocab_chunk=bwd_vocab_chunk, **var)
     torch.cuda.synchronize()
     h, wt, t, b = oracle_inputs(d)
     ref = flce_reference(h, wt, t, b, ignore_index=w.ignore_index, logit_scale=w.logit_scale,
                          softcap=w.softcap, reduction=w.reduction, grad_output=grad_output,
-                         compute_grads=backward)
+                         compute_grads=backward, label_smoothing=label_smoothing, z_loss=z_loss,
+                         class_weight=None if class_weight is None else np.asarray(class_weight, np.float64))
     out = check_against_oracle(w, d, ref, loss=loss, lse=lse, metrics=metrics, grads=grads,
                                what=w.name)
     print("  errors:", out, flush=True)
@@ -140,3 +144,49 @@ def test_empty_batch():
     assert loss.item() == 0.0
     gh, gw, gb = flce.flce_backward(h, w, t, b, lse)
     assert gh.numel() == 0 and torch.all(gw == 0) and torch.all(gb == 0)
+
+
+# --------------------------------------------------------------------------- loss variants
+
+def class_weights(v, seed):
+    cw = np.random.default_rng(seed).uniform(0.2, 3.0, v).astype(np.float32)
+    cw[::7] = 0.0
+    return cw
+
+
+@pytest.mark.parametrize("red", ["mean", "sum", "none"])
+def test_variants_f32_tight(red):
+    w = W["tiny_f32"].resized(n=200, h=64, v=700, reduction=red)
+    run_case(w, label_smoothing=0.2, z_loss=1e-3, class_weight=class_weights(700, 1))
+    run_case(w, label_smoothing=0.1)
+    run_case(w, z_loss=0.01)
+    run_case(w, class_weight=class_weights(700, 2))
+
+
+def test_variants_bias_scale_cap_metrics():
+    w = W["transforms_bf16"].resized(n=300, h=256, v=2600)
+    run_case(w, label_smoothing=0.1, z_loss=1e-4, class_weight=class_weights(2600, 3), bwd_vocab_chunk=1024)
+    run_case(w.resized(reduction="none"), label_smoothing=1.0, backward=False)
+
+
+def test_variants_multichunk_and_fused_transpose():
+    # several chunks, at least 4 token tiles (the recompute kernel writes W_c^T), f16
+    w = W["headvocab_bf16"].resized(n=1030, h=200, v=2600, dtype="f16")
+    run_case(w, label_smoothing=0.05, z_loss=2e-4, class_weight=class_weights(2600, 4), bwd_vocab_chunk=1024)
+
+
+def test_variants_leave_plain_loss_bit_identical():
+    import linear_cross_entropy_fwd_amd as flce
+    w = W["midvocab_bf16"].resized(n=300, h=256, v=3000)
+    d = fi.generate(w)
+    g = gpu_inputs(d)
+    args = (g["hidden"], g["weight"], g["targets"], g["bias"])
+    a = flce.flce_forward(*args, reduction="sum")
+    b = flce.flce_forward(*args, reduction="sum", label_smoothing=0.0, z_loss=0.0,
+                          class_weight=torch.ones(3000, dtype=torch.float32, device="cuda"))
+    ga = flce.flce_backward(*args, a[1], reduction="sum")
+    gb = flce.flce_backward(*args, a[1], reduction="sum",
+                            class_weight=torch.ones(3000, dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    assert torch.equal(ga[0], gb[0]) and torch.equal(ga[1], gb[1])
