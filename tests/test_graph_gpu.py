@@ -1,0 +1,73 @@
+"""The forward and backward calls under HIP graph capture: the library
+allocates nothing and synchronises nothing, so both calls record into one
+graph.  Every replay (with the program's own eager work and synchronisations
+between replays, and new input values written into the captured buffers)
+must equal the eager result bit for bit (the path is deterministic)."""
+import pytest
+import torch
+
+import flce_inputs as fi
+from flce_testutil import gpu_inputs, log_case
+
+pytestmark = pytest.mark.gpu
+
+W = fi.WORKLOADS
+
+
+def _run(flce, g, w, ws_f, ws_b):
+    loss, lse, m = flce.flce_forward(g["hidden"], g["weight"], g["targets"], g["bias"],
+                                     ignore_index=w.ignore_index, logit_scale=w.logit_scale,
+                                     softcap=w.softcap, reduction=w.reduction,
+                                     return_metrics=w.return_metrics, workspace=ws_f)
+    gh, gw, gb = flce.flce_backward(g["hidden"], g["weight"], g["targets"], g["bias"], lse,
+                                    ignore_index=w.ignore_index, logit_scale=w.logit_scale,
+                                    softcap=w.softcap, reduction=w.reduction, workspace=ws_b,
+                                    bwd_vocab_chunk=1024)
+    return [x for x in (loss, lse, m, gh, gw, gb) if x is not None]
+
+
+def test_graph_replays_match_eager():
+    import linear_cross_entropy_fwd_amd as flce
+    w = W["transforms_bf16"].resized(n=1030, h=256, v=2600)   # bias, scale, cap, metrics; fused W_c^T
+    log_case(f"graph capture {w.name} n={w.n} h={w.h} v={w.v}")
+    d1 = fi.generate(w)
+    d2 = fi.generate(w.resized(seed=w.seed + 100))
+    g = gpu_inputs(d1)
+    g2 = gpu_inputs(d2)
+    p = flce.problem_for(g["hidden"], g["weight"], g["bias"], w.ignore_index, w.logit_scale, w.softcap,
+                         w.reduction, w.return_metrics, bwd_vocab_chunk=1024)
+    ws_f = torch.empty(flce._abi.flce_forward_workspace_size(p), dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(flce._abi.flce_backward_workspace_size(p), dtype=torch.uint8, device="cuda")
+
+    eager1 = [x.clone() for x in _run(flce, g, w, ws_f, ws_b)]
+    g_alt = {k: (v.clone() if v is not None else None) for k, v in g.items()}
+    for k in ("hidden", "weight", "bias"):
+        if g_alt[k] is not None:
+            g_alt[k].copy_(g2[k])
+    eager2 = [x.clone() for x in _run(flce, g_alt, w, ws_f, ws_b)]
+    torch.cuda.synchronize()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        _run(flce, g, w, ws_f, ws_b)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = _run(flce, g, w, ws_f, ws_b)
+
+    for rep in range(4):
+        # eager work and a synchronisation between replays
+        x = torch.randn(512, 512, device="cuda")
+        (x @ x).sum().item()
+        src = g2 if rep % 2 else None
+        for k in ("hidden", "weight", "bias"):
+            if g[k] is not None:
+                g[k].copy_(src[k] if src is not None else gpu_inputs(d1)[k])
+        graph.replay()
+        torch.cuda.synchronize()
+        want = eager2 if rep % 2 else eager1
+        for got, ref in zip(outs, want):
+            assert torch.equal(got, ref), f"replay {rep}"
