@@ -93,7 +93,13 @@ def main():
     ap.add_argument("--phase", choices=["both", "fwd"], default="both",
                     help="'fwd' runs forward passes only (for per-kernel counter runs); "
                          "the headline line is 'both'")
+    ap.add_argument("--label-smoothing", type=float, default=0.0,
+                    help="loss variant (not the headline): label smoothing eps")
+    ap.add_argument("--z-loss", type=float, default=0.0, help="loss variant (not the headline): z-loss coefficient")
+    ap.add_argument("--class-weights", action="store_true",
+                    help="loss variant (not the headline): seeded class weights, uniform in [0.5, 1.5)")
     args = ap.parse_args()
+    variants = bool(args.label_smoothing or args.z_loss or args.class_weights)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
               f"multi-GPU path.", file=sys.stderr)
@@ -117,8 +123,13 @@ def main():
     base_mem = torch.cuda.memory_allocated()
     torch.cuda.reset_peak_memory_stats()
 
+    cw = None
+    if args.class_weights:
+        gen = torch.Generator().manual_seed(7)
+        cw = (torch.rand(w.v, generator=gen, dtype=torch.float32) + 0.5).to(dev)
     p = flce.problem_for(hidden, weight, bias, w.ignore_index, w.logit_scale, w.softcap,
-                         w.reduction, w.return_metrics)
+                         w.reduction, w.return_metrics, label_smoothing=args.label_smoothing,
+                         z_loss=args.z_loss, class_weight=cw)
     fws = torch.empty(_abi.flce_forward_workspace_size(p), dtype=torch.uint8, device=dev)
     bws = torch.empty(_abi.flce_backward_workspace_size(p), dtype=torch.uint8, device=dev)
     loss = torch.empty(w.n if w.reduction == "none" else 1, dtype=torch.float32, device=dev)
@@ -185,7 +196,8 @@ def main():
     fwd_tflops = 2.0 * w.n * w.h * w.v / (fwd_ms * 1e-3) / 1e12
     traffic = stored_traffic()
     out = {
-        "metric": METRIC if run_bwd else "forward only TFLOP/s (2*N*H*V), not the headline",
+        "metric": (METRIC if not variants else METRIC + ", with loss variants (not the headline)")
+                  if run_bwd else "forward only TFLOP/s (2*N*H*V), not the headline",
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -199,7 +211,9 @@ def main():
         "data": "synthetic (seeded counter-hash inputs generated on the GPU)",
         "config": {"workload": w.name, "n_tokens": w.n, "hidden": w.h, "vocab": w.v,
                    "reduction": w.reduction, "targets": f"{w.targets}, {w.ignore_frac:.0%} ignored",
-                   "global_batch": w.n, "parallelism": "none (1 GPU)"},
+                   "global_batch": w.n, "parallelism": "none (1 GPU)",
+                   **({"label_smoothing": args.label_smoothing, "z_loss": args.z_loss,
+                       "class_weights": bool(args.class_weights)} if variants else {})},
         "mfma_util": round(tflops / PEAK_BF16_TFLOPS, 4),
         "fwd_ms": round(fwd_ms, 4),
         "bwd_ms": round(bwd_ms, 4),
