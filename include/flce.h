@@ -93,6 +93,10 @@ typedef struct flce_problem {
   float label_smoothing;
   float z_loss;
   const float* class_weight;
+  /* Optional forward output: device int64 [N], each row's predicted token
+   * (the first-index argmax of z, the one the accuracy metric uses; written
+   * for ignored rows too), or NULL.  Requires return_metrics = 1. */
+  int64_t* predictions;
 } flce_problem_t;
 
 /* Bytes of workspace flce_forward / flce_backward need for problem *p

@@ -62,23 +62,30 @@ def _check_class_weight(class_weight, weight):
 
 def problem_for(hidden, weight, bias, ignore_index=-100, logit_scale=1.0, softcap=None,
                 reduction="mean", return_metrics=False, fwd_tiles_per_split=0,
-                bwd_vocab_chunk=0, label_smoothing=0.0, z_loss=0.0, class_weight=None) -> Problem:
+                bwd_vocab_chunk=0, label_smoothing=0.0, z_loss=0.0, class_weight=None,
+                predictions=None) -> Problem:
     _check_class_weight(class_weight, weight)
     return make_problem(hidden.shape[0], hidden.shape[1], weight.shape[0], _DTYPES[hidden.dtype],
                         reduction, ignore_index, logit_scale, softcap, return_metrics,
                         bias is not None, fwd_tiles_per_split, bwd_vocab_chunk, label_smoothing,
-                        z_loss, _ptr(class_weight))
+                        z_loss, _ptr(class_weight), _ptr(predictions))
 
 
 def flce_forward(hidden, weight, targets, bias=None, *, ignore_index=-100, logit_scale=1.0,
                  softcap=None, reduction="mean", return_metrics=False, want_lse=True,
                  workspace: Optional[torch.Tensor] = None, fwd_tiles_per_split=0,
-                 label_smoothing=0.0, z_loss=0.0, class_weight=None):
-    """Tensor-level ``flce_forward``: returns (loss, lse or None, metrics or None)."""
+                 label_smoothing=0.0, z_loss=0.0, class_weight=None,
+                 predictions: Optional[torch.Tensor] = None):
+    """Tensor-level ``flce_forward``: returns (loss, lse or None, metrics or None).
+    ``predictions`` (int64 (N,), needs return_metrics) receives each row's argmax id."""
     _check_inputs(hidden, weight, targets, bias)
+    if predictions is not None and (predictions.shape != (hidden.shape[0],) or predictions.dtype != torch.int64
+                                    or predictions.device != hidden.device):
+        raise ValueError("predictions must be an int64 (N,) tensor on the device of hidden")
     p = problem_for(hidden, weight, bias, ignore_index, logit_scale, softcap, reduction,
                     return_metrics, fwd_tiles_per_split=fwd_tiles_per_split,
-                    label_smoothing=label_smoothing, z_loss=z_loss, class_weight=class_weight)
+                    label_smoothing=label_smoothing, z_loss=z_loss, class_weight=class_weight,
+                    predictions=predictions)
     n = hidden.shape[0]
     dev = hidden.device
     loss = torch.empty(n if reduction == "none" else 1, dtype=torch.float32, device=dev)

@@ -40,6 +40,7 @@ class Problem(ctypes.Structure):
         ("label_smoothing", ctypes.c_float),
         ("z_loss", ctypes.c_float),
         ("class_weight", ctypes.c_void_p),
+        ("predictions", ctypes.c_void_p),
     ]
 
 
@@ -97,14 +98,16 @@ def check(status: int) -> None:
 
 def make_problem(n, h, v, dtype, reduction="mean", ignore_index=-100, logit_scale=1.0,
                  softcap=None, return_metrics=False, has_bias=False, fwd_tiles_per_split=0,
-                 bwd_vocab_chunk=0, label_smoothing=0.0, z_loss=0.0, class_weight=0) -> Problem:
-    """class_weight: integer device address of an fp32 [V] array, or 0."""
+                 bwd_vocab_chunk=0, label_smoothing=0.0, z_loss=0.0, class_weight=0,
+                 predictions=0) -> Problem:
+    """class_weight / predictions: integer device addresses (fp32 [V] in,
+    int64 [N] out), or 0."""
     return Problem(int(n), int(h), int(v), int(ignore_index), int(dtype),
                    REDUCTIONS[reduction] if isinstance(reduction, str) else int(reduction),
                    float(logit_scale), 0.0 if softcap is None else float(softcap),
                    int(bool(return_metrics)), int(bool(has_bias)), int(fwd_tiles_per_split),
                    int(bwd_vocab_chunk), float(label_smoothing), float(z_loss),
-                   int(class_weight) or None)
+                   int(class_weight) or None, int(predictions) or None)
 
 
 def flce_forward_workspace_size(p: Problem) -> int:

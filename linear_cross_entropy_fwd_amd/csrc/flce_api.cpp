@@ -75,6 +75,10 @@ flce_status_t check_problem(const flce_problem_t* p) {
   if (!isfinite(p->z_loss)) return fail(FLCE_ERR_INVALID_ARGUMENT, "z_loss is not finite");
   if (p->class_weight && !aligned(p->class_weight, 4))
     return fail(FLCE_ERR_INVALID_ARGUMENT, "class_weight is misaligned");
+  if (p->predictions && !aligned(p->predictions, 8))
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "predictions is misaligned");
+  if (p->predictions && !p->return_metrics)
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "predictions need return_metrics=1");
   return FLCE_OK;
 }
 
@@ -247,6 +251,7 @@ flce_status_t flce_forward(const flce_problem_t* p, const void* hidden, const vo
     ca.z_loss = p->z_loss;
     ca.class_weight = p->class_weight;
     ca.row_w = p->class_weight ? reinterpret_cast<float*>(ws + L.off_roww) : nullptr;
+    ca.predictions = p->predictions;
     e = flce::launch_forward_combine(metrics_on, ca, st);
     if (e != hipSuccess) return hip_fail(e, "forward combine kernel");
   }

@@ -399,6 +399,7 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(CombineArgs a) {
   a.row_loss[n] = row;
   int flag = (valid ? 1 : 0) | (bad ? 4 : 0);
   if (METRICS) {
+    if (a.predictions) a.predictions[n] = (int64_t)ai;
     if (valid && !bad && ai == tv) flag |= 2;
     a.row_ent[n] = valid ? logS - U / S : 0.f;
   }

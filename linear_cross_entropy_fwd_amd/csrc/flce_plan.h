@@ -56,6 +56,7 @@ struct CombineArgs {
   int* row_flag;    // workspace [N]: bit0 valid, bit1 hit, bit2 bad target
   const float* class_weight;  // [V] or null
   float* row_w;     // workspace [N]: the row's weight (0 if ignored or bad), or null
+  int64_t* predictions;  // [N] argmax ids (needs METRICS), or null
   int64_t N, V, ignore_index;
   int tiles_per_split, n_splits;
   int zsum;         // partial 6 holds the sum of z

@@ -64,6 +64,8 @@ def base(**kw):
     (dict(label_smoothing=float("nan")), INVALID),
     (dict(z_loss=float("inf")), INVALID),
     (dict(class_weight=(1 << 40) + 2), INVALID),    # misaligned fp32 array
+    (dict(predictions=(1 << 40) + 4, return_metrics=True), INVALID),  # misaligned int64 array
+    (dict(predictions=1 << 40), INVALID),            # predictions without return_metrics
 ])
 def test_invalid_problems(kw, status):
     p = base(**kw)

@@ -26,10 +26,12 @@ def run_case(w: fi.Workload, *, backward=True, bwd_vocab_chunk=0, fwd_tiles_per_
     g = gpu_inputs(d)
     cw = None if class_weight is None else torch.as_tensor(class_weight, dtype=torch.float32).cuda()
     var = dict(label_smoothing=label_smoothing, z_loss=z_loss, class_weight=cw)
+    pred = torch.empty(w.n, dtype=torch.int64, device="cuda") if w.return_metrics else None
     loss, lse, metrics = flce.flce_forward(
         g["hidden"], g["weight"], g["targets"], g["bias"], ignore_index=w.ignore_index,
         logit_scale=w.logit_scale, softcap=w.softcap, reduction=w.reduction,
-        return_metrics=w.return_metrics, fwd_tiles_per_split=fwd_tiles_per_split, **var)
+        return_metrics=w.return_metrics, fwd_tiles_per_split=fwd_tiles_per_split,
+        predictions=pred, **var)
     grads = None
     if backward:
         go = None if grad_output is None else torch.as_tensor(grad_output, dtype=torch.float32)
@@ -45,6 +47,12 @@ def run_case(w: fi.Workload, *, backward=True, bwd_vocab_chunk=0, fwd_tiles_per_
                          class_weight=None if class_weight is None else np.asarray(class_weight, np.float64))
     out = check_against_oracle(w, d, ref, loss=loss, lse=lse, metrics=metrics, grads=grads,
                                what=w.name)
+    if pred is not None and w.n > 0:
+        # predicted tokens: the oracle's first-index argmax, except on near-ties
+        from flce_testutil import TIE
+        ties = ref["gap"] <= TIE[w.dtype] * np.maximum(1.0, np.abs(ref["lse"]))
+        got = to_np(pred)
+        assert np.all((got == ref["argmax"]) | ties), np.nonzero((got != ref["argmax"]) & ~ties)
     print("  errors:", out, flush=True)
     return loss, lse, metrics, grads, ref, d
 
