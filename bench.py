@@ -98,8 +98,10 @@ def main():
     ap.add_argument("--z-loss", type=float, default=0.0, help="loss variant (not the headline): z-loss coefficient")
     ap.add_argument("--class-weights", action="store_true",
                     help="loss variant (not the headline): seeded class weights, uniform in [0.5, 1.5)")
+    ap.add_argument("--grad-weight-fp32", action="store_true",
+                    help="write grad_weight / grad_bias in fp32 (not the headline)")
     args = ap.parse_args()
-    variants = bool(args.label_smoothing or args.z_loss or args.class_weights)
+    variants = bool(args.label_smoothing or args.z_loss or args.class_weights or args.grad_weight_fp32)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
               f"multi-GPU path.", file=sys.stderr)
@@ -129,15 +131,16 @@ def main():
         cw = (torch.rand(w.v, generator=gen, dtype=torch.float32) + 0.5).to(dev)
     p = flce.problem_for(hidden, weight, bias, w.ignore_index, w.logit_scale, w.softcap,
                          w.reduction, w.return_metrics, label_smoothing=args.label_smoothing,
-                         z_loss=args.z_loss, class_weight=cw)
+                         z_loss=args.z_loss, class_weight=cw, grad_weight_fp32=args.grad_weight_fp32)
     fws = torch.empty(_abi.flce_forward_workspace_size(p), dtype=torch.uint8, device=dev)
     bws = torch.empty(_abi.flce_backward_workspace_size(p), dtype=torch.uint8, device=dev)
     loss = torch.empty(w.n if w.reduction == "none" else 1, dtype=torch.float32, device=dev)
     lse = torch.empty(w.n, dtype=torch.float32, device=dev)
     metrics = torch.empty(2, dtype=torch.float32, device=dev) if w.return_metrics else None
     gh = torch.empty_like(hidden)
-    gw = torch.empty_like(weight)
-    gb = torch.empty_like(bias) if bias is not None else None
+    gdt = torch.float32 if args.grad_weight_fp32 else weight.dtype
+    gw = torch.empty(weight.shape, dtype=gdt, device=dev)
+    gb = torch.empty(bias.shape, dtype=gdt, device=dev) if bias is not None else None
     ptr = lambda t: 0 if t is None else t.data_ptr()
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
@@ -196,7 +199,7 @@ def main():
     fwd_tflops = 2.0 * w.n * w.h * w.v / (fwd_ms * 1e-3) / 1e12
     traffic = stored_traffic()
     out = {
-        "metric": (METRIC if not variants else METRIC + ", with loss variants (not the headline)")
+        "metric": (METRIC if not variants else METRIC + ", with loss or output variants (not the headline)")
                   if run_bwd else "forward only TFLOP/s (2*N*H*V), not the headline",
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
@@ -213,7 +216,8 @@ def main():
                    "reduction": w.reduction, "targets": f"{w.targets}, {w.ignore_frac:.0%} ignored",
                    "global_batch": w.n, "parallelism": "none (1 GPU)",
                    **({"label_smoothing": args.label_smoothing, "z_loss": args.z_loss,
-                       "class_weights": bool(args.class_weights)} if variants else {})},
+                       "class_weights": bool(args.class_weights),
+                       "grad_weight_fp32": bool(args.grad_weight_fp32)} if variants else {})},
         "mfma_util": round(tflops / PEAK_BF16_TFLOPS, 4),
         "fwd_ms": round(fwd_ms, 4),
         "bwd_ms": round(bwd_ms, 4),

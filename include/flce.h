@@ -97,6 +97,9 @@ typedef struct flce_problem {
    * (the first-index argmax of z, the one the accuracy metric uses; written
    * for ignored rows too), or NULL.  Requires return_metrics = 1. */
   int64_t* predictions;
+  /* 1: grad_weight and grad_bias are written as fp32 arrays whatever the
+   * input dtype (master-weight trainers); 0: in the input dtype. */
+  int32_t grad_weight_fp32;
 } flce_problem_t;
 
 /* Bytes of workspace flce_forward / flce_backward need for problem *p
@@ -123,7 +126,8 @@ flce_status_t flce_forward(const flce_problem_t* p, const void* hidden, const vo
  *               MEAN/SUM, [N] for NONE; NULL means 1.
  *   grad_hidden (N,H), grad_weight (V,H), grad_bias (V): outputs, each may
  *               be NULL when not wanted (grad_bias requires has_bias).  They
- *               are overwritten, not accumulated into.
+ *               are overwritten, not accumulated into.  grad_weight and
+ *               grad_bias are fp32 when grad_weight_fp32 = 1.
  * FLCE_ERR_UNSUPPORTED when n_tokens or the vocabulary chunk times
  * sizeof(dtype) reaches 16 MiB (the operand tiles use 32-bit offsets). */
 flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const void* weight,

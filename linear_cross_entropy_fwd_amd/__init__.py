@@ -63,12 +63,12 @@ def _check_class_weight(class_weight, weight):
 def problem_for(hidden, weight, bias, ignore_index=-100, logit_scale=1.0, softcap=None,
                 reduction="mean", return_metrics=False, fwd_tiles_per_split=0,
                 bwd_vocab_chunk=0, label_smoothing=0.0, z_loss=0.0, class_weight=None,
-                predictions=None) -> Problem:
+                predictions=None, grad_weight_fp32=False) -> Problem:
     _check_class_weight(class_weight, weight)
     return make_problem(hidden.shape[0], hidden.shape[1], weight.shape[0], _DTYPES[hidden.dtype],
                         reduction, ignore_index, logit_scale, softcap, return_metrics,
                         bias is not None, fwd_tiles_per_split, bwd_vocab_chunk, label_smoothing,
-                        z_loss, _ptr(class_weight), _ptr(predictions))
+                        z_loss, _ptr(class_weight), _ptr(predictions), grad_weight_fp32)
 
 
 def flce_forward(hidden, weight, targets, bias=None, *, ignore_index=-100, logit_scale=1.0,
@@ -107,12 +107,14 @@ def flce_forward(hidden, weight, targets, bias=None, *, ignore_index=-100, logit
 def flce_backward(hidden, weight, targets, bias, lse, grad_loss=None, *, ignore_index=-100,
                   logit_scale=1.0, softcap=None, reduction="mean", need_hidden=True,
                   need_weight=True, need_bias=True, workspace: Optional[torch.Tensor] = None,
-                  bwd_vocab_chunk=0, label_smoothing=0.0, z_loss=0.0, class_weight=None):
-    """Tensor-level ``flce_backward``: returns (grad_hidden, grad_weight, grad_bias)."""
+                  bwd_vocab_chunk=0, label_smoothing=0.0, z_loss=0.0, class_weight=None,
+                  grad_weight_fp32=False):
+    """Tensor-level ``flce_backward``: returns (grad_hidden, grad_weight, grad_bias);
+    grad_weight and grad_bias are fp32 with ``grad_weight_fp32``."""
     _check_inputs(hidden, weight, targets, bias)
     p = problem_for(hidden, weight, bias, ignore_index, logit_scale, softcap, reduction,
                     False, bwd_vocab_chunk=bwd_vocab_chunk, label_smoothing=label_smoothing,
-                    z_loss=z_loss, class_weight=class_weight)
+                    z_loss=z_loss, class_weight=class_weight, grad_weight_fp32=grad_weight_fp32)
     dev = hidden.device
     if grad_loss is not None:
         grad_loss = grad_loss.to(device=dev, dtype=torch.float32).contiguous()
@@ -120,8 +122,9 @@ def flce_backward(hidden, weight, targets, bias, lse, grad_loss=None, *, ignore_
         if grad_loss.numel() != expect:
             raise ValueError(f"grad_loss must have {expect} elements")
     gh = torch.empty_like(hidden) if need_hidden else None
-    gw = torch.empty_like(weight) if need_weight else None
-    gb = torch.empty_like(bias) if (need_bias and bias is not None) else None
+    gdt = torch.float32 if grad_weight_fp32 else weight.dtype
+    gw = torch.empty(weight.shape, dtype=gdt, device=dev) if need_weight else None
+    gb = torch.empty(bias.shape, dtype=gdt, device=dev) if (need_bias and bias is not None) else None
     need = _abi.flce_backward_workspace_size(p)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)

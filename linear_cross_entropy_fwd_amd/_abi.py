@@ -41,6 +41,7 @@ class Problem(ctypes.Structure):
         ("z_loss", ctypes.c_float),
         ("class_weight", ctypes.c_void_p),
         ("predictions", ctypes.c_void_p),
+        ("grad_weight_fp32", ctypes.c_int32),
     ]
 
 
@@ -99,15 +100,15 @@ def check(status: int) -> None:
 def make_problem(n, h, v, dtype, reduction="mean", ignore_index=-100, logit_scale=1.0,
                  softcap=None, return_metrics=False, has_bias=False, fwd_tiles_per_split=0,
                  bwd_vocab_chunk=0, label_smoothing=0.0, z_loss=0.0, class_weight=0,
-                 predictions=0) -> Problem:
+                 predictions=0, grad_weight_fp32=False) -> Problem:
     """class_weight / predictions: integer device addresses (fp32 [V] in,
-    int64 [N] out), or 0."""
+    int64 [N] out), or 0.  grad_weight_fp32: 1 for fp32 grad_weight / grad_bias."""
     return Problem(int(n), int(h), int(v), int(ignore_index), int(dtype),
                    REDUCTIONS[reduction] if isinstance(reduction, str) else int(reduction),
                    float(logit_scale), 0.0 if softcap is None else float(softcap),
                    int(bool(return_metrics)), int(bool(has_bias)), int(fwd_tiles_per_split),
                    int(bwd_vocab_chunk), float(label_smoothing), float(z_loss),
-                   int(class_weight) or None, int(predictions) or None)
+                   int(class_weight) or None, int(predictions) or None, int(grad_weight_fp32))
 
 
 def flce_forward_workspace_size(p: Problem) -> int:

@@ -77,6 +77,8 @@ flce_status_t check_problem(const flce_problem_t* p) {
     return fail(FLCE_ERR_INVALID_ARGUMENT, "class_weight is misaligned");
   if (p->predictions && !aligned(p->predictions, 8))
     return fail(FLCE_ERR_INVALID_ARGUMENT, "predictions is misaligned");
+  if (p->grad_weight_fp32 != 0 && p->grad_weight_fp32 != 1)
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "grad_weight_fp32 must be 0 or 1");
   if (p->predictions && !p->return_metrics)
     return fail(FLCE_ERR_INVALID_ARGUMENT, "predictions need return_metrics=1");
   return FLCE_OK;
@@ -284,6 +286,7 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
   const bool want_dh = grad_hidden != nullptr && N > 0;
   const bool want_dw = grad_weight != nullptr;
   const bool want_db = grad_bias != nullptr;
+  const int geb = p->grad_weight_fp32 ? 4 : eb;  // bytes per grad_weight / grad_bias element
   if (!want_dh && !want_dw && !want_db) return FLCE_OK;
   if (N > 0 && (!hidden || !weight || !targets || !lse))
     return fail(FLCE_ERR_INVALID_ARGUMENT, "hidden, weight, targets and lse must be non-NULL");
@@ -291,7 +294,7 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
     return fail(FLCE_ERR_INVALID_ARGUMENT, "hidden, weight, grad_hidden and grad_weight must be 16-byte aligned");
   if (!aligned(targets, 8) || !aligned(lse, 4) || !aligned(grad_loss, 4))
     return fail(FLCE_ERR_INVALID_ARGUMENT, "targets / lse / grad_loss misaligned");
-  if ((bias && !aligned(bias, (uintptr_t)eb)) || (grad_bias && !aligned(grad_bias, (uintptr_t)eb)))
+  if ((bias && !aligned(bias, (uintptr_t)eb)) || (grad_bias && !aligned(grad_bias, (uintptr_t)geb)))
     return fail(FLCE_ERR_INVALID_ARGUMENT, "bias / grad_bias misaligned");
   const BwdLayout L = bwd_layout(*p);
   // The GEMM tiles read their operand panels through 32-bit buffer offsets:
@@ -306,9 +309,9 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
   char* ws = reinterpret_cast<char*>(workspace);
   hipError_t e;
   if (N == 0) {  // every gradient is zero
-    if (want_dw && (e = flce::launch_fill_zero(grad_weight, (size_t)V * H * eb, st)) != hipSuccess)
+    if (want_dw && (e = flce::launch_fill_zero(grad_weight, (size_t)V * H * geb, st)) != hipSuccess)
       return hip_fail(e, "zero fill");
-    if (want_db && (e = flce::launch_fill_zero(grad_bias, (size_t)V * eb, st)) != hipSuccess)
+    if (want_db && (e = flce::launch_fill_zero(grad_bias, (size_t)V * geb, st)) != hipSuccess)
       return hip_fail(e, "zero fill");
     return FLCE_OK;
   }
@@ -390,7 +393,8 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
       flce::DwArgs wa{};
       wa.GT = gt;
       wa.HT = ht;
-      wa.out = reinterpret_cast<char*>(grad_weight) + c0 * H * eb;
+      wa.out = reinterpret_cast<char*>(grad_weight) + c0 * H * geb;
+      wa.out_f32 = p->grad_weight_fp32;
       wa.scale = scale;
       wa.H = H;
       wa.cv = cv;
@@ -401,7 +405,8 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
     }
   }
   if (want_db) {
-    flce::DbArgs ba{db, reinterpret_cast<char*>(grad_bias), scale, V, flce::kBiasParts * L.n_tok_tiles};
+    flce::DbArgs ba{db, reinterpret_cast<char*>(grad_bias), scale, V, flce::kBiasParts * L.n_tok_tiles,
+                    p->grad_weight_fp32};
     if ((e = flce::launch_backward_db(p->dtype, ba, st)) != hipSuccess) return hip_fail(e, "grad_bias kernel");
   }
   return FLCE_OK;

@@ -1019,10 +1019,11 @@ __global__ __launch_bounds__(W * 64) void bwd_dh_kernel(DhArgs a) {
 
 // grad_weight[v][h] = scale * sum_n G[n][v] H[n][h] for one vocabulary chunk:
 // A = H^T (h rows), B = G^T (v rows), K = tokens.  16-bit results go through
-// the LDS tile and leave as whole 512-byte row pieces; fp32 directly.
+// the LDS tile and leave as whole 512-byte row pieces; fp32 results (fp32
+// inputs, or out_f32) are stored straight from the accumulators, each
+// quarter-wave writing 64 contiguous bytes of one row.
 template <int D, int W>
 __global__ __launch_bounds__(W * 64) void bwd_dw_kernel(DwArgs a) {
-  typedef typename Elem<D>::T T;
   constexpr int EB = Elem<D>::bytes, WI = Gemm<W>::WI, WJ = Gemm<W>::WJ;
   const TileAB ti = grouped_tile<kDwGA, kDwGB, kDwXcd>(blockIdx.x, gridDim.x, a.n_h_tiles, a.n_voc_tiles);
   if (!ti.valid) return;
@@ -1037,28 +1038,30 @@ __global__ __launch_bounds__(W * 64) void bwd_dw_kernel(DwArgs a) {
   gemm_nt_tile<D, W>(acc, A, B);
   const float scale = a.scale[0];
   if constexpr (EB == 2) {
+    if (!a.out_f32) {
 #pragma unroll
-    for (int j = 0; j < WJ; ++j)
+      for (int j = 0; j < WJ; ++j)
 #pragma unroll
-      for (int i = 0; i < WI; ++i)
-        tile16_put4<D>(wn * 16 * WJ + 16 * j + c16, wm * 16 * WI + 16 * i + 4 * q, acc[i][j][0] * scale,
-                       acc[i][j][1] * scale, acc[i][j][2] * scale, acc[i][j][3] * scale);
-    __syncthreads();
-    tile16_store<W * 64>(reinterpret_cast<uint16_t*>(a.out) + v0 * a.H + h0, a.H,
-                         (int)min<int64_t>(TILE, a.cv - v0), (int)min<int64_t>(TILE, a.H - h0), t);
-  } else {
-    T* out = reinterpret_cast<T*>(a.out);
+        for (int i = 0; i < WI; ++i)
+          tile16_put4<D>(wn * 16 * WJ + 16 * j + c16, wm * 16 * WI + 16 * i + 4 * q, acc[i][j][0] * scale,
+                         acc[i][j][1] * scale, acc[i][j][2] * scale, acc[i][j][3] * scale);
+      __syncthreads();
+      tile16_store<W * 64>(reinterpret_cast<uint16_t*>(a.out) + v0 * a.H + h0, a.H,
+                           (int)min<int64_t>(TILE, a.cv - v0), (int)min<int64_t>(TILE, a.H - h0), t);
+      return;
+    }
+  }
+  float* out = reinterpret_cast<float*>(a.out);
 #pragma unroll
-    for (int j = 0; j < WJ; ++j) {
-      const int64_t v = v0 + wn * 16 * WJ + 16 * j + c16;
-      if (v >= a.cv) continue;
+  for (int j = 0; j < WJ; ++j) {
+    const int64_t v = v0 + wn * 16 * WJ + 16 * j + c16;
+    if (v >= a.cv) continue;
 #pragma unroll
-      for (int i = 0; i < WI; ++i) {
-        const int64_t h = h0 + wm * 16 * WI + 16 * i + 4 * q;
-        if (h < a.H)
-          store4<D>(out + v * a.H + h, acc[i][j][0] * scale, acc[i][j][1] * scale, acc[i][j][2] * scale,
-                    acc[i][j][3] * scale);
-      }
+    for (int i = 0; i < WI; ++i) {
+      const int64_t h = h0 + wm * 16 * WI + 16 * i + 4 * q;
+      if (h < a.H)
+        *reinterpret_cast<float4*>(out + v * a.H + h) = make_float4(
+            acc[i][j][0] * scale, acc[i][j][1] * scale, acc[i][j][2] * scale, acc[i][j][3] * scale);
     }
   }
 }
@@ -1070,7 +1073,8 @@ __global__ __launch_bounds__(256) void bwd_db_kernel(DbArgs a) {
   if (v >= a.V) return;
   float s = 0.f;
   for (int p = 0; p < a.n_parts; ++p) s = s + a.dbpart[(int64_t)p * a.V + v];
-  reinterpret_cast<T*>(a.out)[v] = from_f32<D>(s * a.scale[0]);
+  if (a.out_f32) reinterpret_cast<float*>(a.out)[v] = s * a.scale[0];
+  else reinterpret_cast<T*>(a.out)[v] = from_f32<D>(s * a.scale[0]);
 }
 
 // ------------------------------------------------------------------ launchers

@@ -127,6 +127,7 @@ struct DwArgs {
   const float* scale;
   int64_t H;
   int cv, npad, n_voc_tiles, n_h_tiles;
+  int out_f32;       // 1: out is fp32 whatever the input dtype
 };
 
 struct DbArgs {
@@ -135,6 +136,7 @@ struct DbArgs {
   const float* scale;
   int64_t V;
   int n_parts;
+  int out_f32;       // 1: out is fp32 whatever the input dtype
 };
 
 // Launchers (flce_kernels.hip).  All asynchronous on `st`.

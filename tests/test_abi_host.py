@@ -66,6 +66,7 @@ def base(**kw):
     (dict(class_weight=(1 << 40) + 2), INVALID),    # misaligned fp32 array
     (dict(predictions=(1 << 40) + 4, return_metrics=True), INVALID),  # misaligned int64 array
     (dict(predictions=1 << 40), INVALID),            # predictions without return_metrics
+    (dict(grad_weight_fp32=2), INVALID),
 ])
 def test_invalid_problems(kw, status):
     p = base(**kw)

@@ -198,3 +198,56 @@ def test_variants_leave_plain_loss_bit_identical():
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
     assert torch.equal(ga[0], gb[0]) and torch.equal(ga[1], gb[1])
+
+
+# --------------------------------------------------------------------------- fp32 gradient output
+
+@pytest.mark.parametrize("dtype,chunk", [("bf16", 1024), ("f16", 0)])
+def test_fp32_grad_weight_output(dtype, chunk):
+    """grad_weight_fp32 stores the same fp32 accumulators the 16-bit outputs
+    are rounded from: rounding them to the input dtype (nearest even) gives
+    the 16-bit gradients bit for bit, grad_hidden is untouched, and the fp32
+    gradients meet the oracle at the 16-bit tolerance."""
+    import linear_cross_entropy_fwd_amd as flce
+    w = W["transforms_bf16"].resized(n=1030, h=200, v=2600, dtype=dtype)
+    d = fill_argmax_targets(w, fi.generate(w))
+    g = gpu_inputs(d)
+    log_case(f"fp32 grads {w.name} n={w.n} h={w.h} v={w.v} dtype={dtype} chunk={chunk}")
+    args = (g["hidden"], g["weight"], g["targets"], g["bias"])
+    kw = dict(ignore_index=w.ignore_index, logit_scale=w.logit_scale, softcap=w.softcap,
+              reduction=w.reduction)
+    loss, lse, _ = flce.flce_forward(*args, **kw)
+    g16 = flce.flce_backward(*args, lse, None, bwd_vocab_chunk=chunk, **kw)
+    g32 = flce.flce_backward(*args, lse, None, bwd_vocab_chunk=chunk, grad_weight_fp32=True, **kw)
+    torch.cuda.synchronize()
+    assert g32[1].dtype == torch.float32 and g32[2].dtype == torch.float32
+    assert torch.equal(g16[0], g32[0])
+    assert torch.equal(g16[1], g32[1].to(g16[1].dtype))
+    assert torch.equal(g16[2], g32[2].to(g16[2].dtype))
+    h, wt, t, b = oracle_inputs(d)
+    ref = flce_reference(h, wt, t, b, **kw)
+    check_against_oracle(w, d, ref, loss=loss, lse=lse, grads=g32, what="fp32 grads")
+
+
+def test_fp32_grad_weight_output_f32_inputs_and_empty():
+    import linear_cross_entropy_fwd_amd as flce
+    w = W["tiny_f32"].resized(n=300, h=64, v=700)
+    d = fi.generate(w)
+    g = gpu_inputs(d)
+    args = (g["hidden"], g["weight"], g["targets"], g["bias"])
+    _, lse, _ = flce.flce_forward(*args)
+    a = flce.flce_backward(*args, lse)
+    b = flce.flce_backward(*args, lse, grad_weight_fp32=True)
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(a, b) if x is not None)
+    # no tokens: the fp32 gradients are zero-filled over their full size
+    h = torch.empty(0, 64, dtype=torch.bfloat16, device="cuda")
+    wt = torch.randn(700, 64, device="cuda").bfloat16()
+    t = torch.empty(0, dtype=torch.int64, device="cuda")
+    b = torch.randn(700, device="cuda").bfloat16()
+    lse0 = torch.empty(0, dtype=torch.float32, device="cuda")
+    gh, gw, gb = flce.flce_backward(h, wt, t, b, lse0, grad_weight_fp32=True)
+    torch.cuda.synchronize()
+    assert gh.numel() == 0
+    assert gw.dtype == torch.float32 and gw.shape == (700, 64) and bool((gw == 0).all())
+    assert gb.dtype == torch.float32 and gb.shape == (700,) and bool((gb == 0).all())
