@@ -100,6 +100,25 @@ typedef struct flce_problem {
   /* 1: grad_weight and grad_bias are written as fp32 arrays whatever the
    * input dtype (master-weight trainers); 0: in the input dtype. */
   int32_t grad_weight_fp32;
+  /* Token layout; all zero means hidden (N,H) and targets (N,) contiguous.
+   * Token n = s * seq_len + t (0 <= t < seq_len; N a multiple of seq_len)
+   * has its hidden row at element s * hidden_seq_stride + t *
+   * hidden_row_stride of hidden and its target at element s *
+   * targets_seq_stride + t * targets_stride of targets, so that views such
+   * as hidden[:, :-1, :] and labels[:, 1:] of an (S, T+1) batch are taken as
+   * they are.  Zero selects the default: seq_len N, hidden_row_stride H,
+   * hidden_seq_stride seq_len * hidden_row_stride, targets_stride 1,
+   * targets_seq_stride seq_len * targets_stride.  Strides are >= 0; the two
+   * hidden strides times sizeof(dtype) are multiples of 16 bytes.  Outputs
+   * indexed by token (lse, loss rows, predictions, grad_hidden) stay
+   * contiguous in n.  Hidden rows that are not contiguous are gathered
+   * into the workspace first (2 N H sizeof(dtype) bytes moved), and so are
+   * targets that are not (16 N bytes). */
+  int64_t seq_len;
+  int64_t hidden_row_stride;
+  int64_t hidden_seq_stride;
+  int64_t targets_stride;
+  int64_t targets_seq_stride;
 } flce_problem_t;
 
 /* Bytes of workspace flce_forward / flce_backward need for problem *p
@@ -145,6 +164,9 @@ flce_status_t flce_forward_status(const flce_problem_t* p, const void* workspace
 const char* flce_status_str(flce_status_t s);
 const char* flce_last_error(void);
 const char* flce_version(void);
+/* sizeof(flce_problem_t) as this library was built, for bindings that lay
+ * the struct out themselves. */
+size_t flce_problem_size(void);
 
 #ifdef __cplusplus
 }

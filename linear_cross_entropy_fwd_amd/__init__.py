@@ -22,7 +22,7 @@ from . import _abi
 from ._abi import FlceError, Problem, library, make_problem  # noqa: F401
 
 __all__ = ["fused_linear_cross_entropy", "flce_forward", "flce_backward", "FlceError",
-           "Problem", "make_problem", "library"]
+           "Problem", "make_problem", "library", "token_layout"]
 
 _DTYPES = {torch.float32: _abi.F32, torch.float16: _abi.F16, torch.bfloat16: _abi.BF16}
 
@@ -32,11 +32,21 @@ def _ptr(t: Optional[torch.Tensor]) -> int:
 
 
 def _check_inputs(hidden, weight, targets, bias):
+    """Validates shapes, dtypes and devices; returns the token layout keywords
+    of ``make_problem`` for the strides of hidden and targets.
+
+    hidden is (N, H) or (S, T, H) with unit stride along H; targets is (N,)
+    or (S, T) (or (S*T,)).  Other strides are passed to the library as they
+    are (e.g. ``hidden[:, :-1]`` and ``labels[:, 1:]``), so no copy is made."""
     if not hidden.is_cuda:
         raise ValueError("hidden must be a GPU tensor (there is no CPU path)")
-    if hidden.dim() != 2 or weight.dim() != 2 or targets.dim() != 1:
-        raise ValueError("expected hidden (N,H), weight (V,H), targets (N,)")
-    if weight.shape[1] != hidden.shape[1] or targets.shape[0] != hidden.shape[0]:
+    if hidden.dim() not in (2, 3) or weight.dim() != 2 or targets.dim() not in (1, 2):
+        raise ValueError("expected hidden (N,H) or (S,T,H), weight (V,H), targets (N,) or (S,T)")
+    lead = tuple(hidden.shape[:-1])
+    n = 1
+    for d in lead:
+        n *= d
+    if weight.shape[1] != hidden.shape[-1] or (tuple(targets.shape) != lead and tuple(targets.shape) != (n,)):
         raise ValueError(f"shape mismatch: hidden {tuple(hidden.shape)}, weight {tuple(weight.shape)}, "
                          f"targets {tuple(targets.shape)}")
     if hidden.dtype not in _DTYPES or weight.dtype != hidden.dtype:
@@ -48,8 +58,42 @@ def _check_inputs(hidden, weight, targets, bias):
     for t in (hidden, weight, targets) + ((bias,) if bias is not None else ()):
         if t.device != hidden.device:
             raise ValueError("all tensors must be on one device")
+    for t in (weight,) + ((bias,) if bias is not None else ()):
         if not t.is_contiguous():
-            raise ValueError("tensors must be contiguous")
+            raise ValueError("weight and bias must be contiguous")
+    return token_layout(hidden, targets)
+
+
+def token_layout(hidden, targets) -> dict:
+    """The token layout keywords of ``make_problem`` (seq_len and strides in
+    elements, 0 = default) for hidden (N, H) / (S, T, H) and targets (N,) /
+    (S, T) / (S*T,) as they sit in memory."""
+    lead = tuple(hidden.shape[:-1])
+    n = 1
+    for d in lead:
+        n *= d
+    if hidden.shape[-1] > 1 and hidden.stride(-1) != 1:
+        raise ValueError("hidden must have unit stride along its last dimension")
+    seq = lead[-1] if len(lead) == 2 else n
+    n_seq = lead[0] if len(lead) == 2 else 1
+    # strides of size-1 dimensions do not matter: pass the default (0)
+    hr = hidden.stride(-2) if seq > 1 else 0
+    hs = hidden.stride(0) if (len(lead) == 2 and n_seq > 1) else 0
+    if targets.dim() == 2:
+        ts = targets.stride(1) if seq > 1 else 0
+        tss = targets.stride(0) if n_seq > 1 else 0
+        t_broadcast = (seq > 1 and ts == 0) or (n_seq > 1 and tss == 0)
+    else:
+        ts = targets.stride(0) if n > 1 else 0
+        tss = seq * ts if (len(lead) == 2 and n_seq > 1) else 0
+        t_broadcast = n > 1 and ts == 0
+    if (seq > 1 and hr == 0) or (n_seq > 1 and hs == 0) or t_broadcast:
+        raise ValueError("broadcast (zero-stride) hidden rows or targets are not supported")
+    eb = hidden.element_size()
+    if (hr * eb) % 16 or (hs * eb) % 16:
+        raise ValueError("hidden row and sequence strides must be multiples of 16 bytes")
+    return dict(seq_len=seq if len(lead) == 2 else 0, hidden_row_stride=hr, hidden_seq_stride=hs,
+                targets_stride=ts, targets_seq_stride=tss)
 
 
 def _check_class_weight(class_weight, weight):
@@ -63,12 +107,15 @@ def _check_class_weight(class_weight, weight):
 def problem_for(hidden, weight, bias, ignore_index=-100, logit_scale=1.0, softcap=None,
                 reduction="mean", return_metrics=False, fwd_tiles_per_split=0,
                 bwd_vocab_chunk=0, label_smoothing=0.0, z_loss=0.0, class_weight=None,
-                predictions=None, grad_weight_fp32=False) -> Problem:
+                predictions=None, grad_weight_fp32=False, layout=None) -> Problem:
+    """``layout``: the token layout keywords ``_check_inputs`` returns (None = contiguous)."""
     _check_class_weight(class_weight, weight)
-    return make_problem(hidden.shape[0], hidden.shape[1], weight.shape[0], _DTYPES[hidden.dtype],
+    n = hidden.numel() // hidden.shape[-1] if hidden.shape[-1] else 0
+    return make_problem(n, hidden.shape[-1], weight.shape[0], _DTYPES[hidden.dtype],
                         reduction, ignore_index, logit_scale, softcap, return_metrics,
                         bias is not None, fwd_tiles_per_split, bwd_vocab_chunk, label_smoothing,
-                        z_loss, _ptr(class_weight), _ptr(predictions), grad_weight_fp32)
+                        z_loss, _ptr(class_weight), _ptr(predictions), grad_weight_fp32,
+                        **(layout or {}))
 
 
 def flce_forward(hidden, weight, targets, bias=None, *, ignore_index=-100, logit_scale=1.0,
@@ -77,16 +124,18 @@ def flce_forward(hidden, weight, targets, bias=None, *, ignore_index=-100, logit
                  label_smoothing=0.0, z_loss=0.0, class_weight=None,
                  predictions: Optional[torch.Tensor] = None):
     """Tensor-level ``flce_forward``: returns (loss, lse or None, metrics or None).
-    ``predictions`` (int64 (N,), needs return_metrics) receives each row's argmax id."""
-    _check_inputs(hidden, weight, targets, bias)
-    if predictions is not None and (predictions.shape != (hidden.shape[0],) or predictions.dtype != torch.int64
-                                    or predictions.device != hidden.device):
+    ``predictions`` (int64 (N,), needs return_metrics) receives each row's argmax id.
+    hidden may be (S, T, H) and targets (S, T), strided (see ``_check_inputs``);
+    per-token outputs are flat (N,) = (S*T,)."""
+    layout = _check_inputs(hidden, weight, targets, bias)
+    n = targets.numel()
+    if predictions is not None and (predictions.shape != (n,) or predictions.dtype != torch.int64
+                                    or predictions.device != hidden.device or not predictions.is_contiguous()):
         raise ValueError("predictions must be an int64 (N,) tensor on the device of hidden")
     p = problem_for(hidden, weight, bias, ignore_index, logit_scale, softcap, reduction,
                     return_metrics, fwd_tiles_per_split=fwd_tiles_per_split,
                     label_smoothing=label_smoothing, z_loss=z_loss, class_weight=class_weight,
-                    predictions=predictions)
-    n = hidden.shape[0]
+                    predictions=predictions, layout=layout)
     dev = hidden.device
     loss = torch.empty(n if reduction == "none" else 1, dtype=torch.float32, device=dev)
     lse = torch.empty(n, dtype=torch.float32, device=dev) if want_lse else None
@@ -110,18 +159,20 @@ def flce_backward(hidden, weight, targets, bias, lse, grad_loss=None, *, ignore_
                   bwd_vocab_chunk=0, label_smoothing=0.0, z_loss=0.0, class_weight=None,
                   grad_weight_fp32=False):
     """Tensor-level ``flce_backward``: returns (grad_hidden, grad_weight, grad_bias);
-    grad_weight and grad_bias are fp32 with ``grad_weight_fp32``."""
-    _check_inputs(hidden, weight, targets, bias)
+    grad_weight and grad_bias are fp32 with ``grad_weight_fp32``; grad_hidden is
+    contiguous, in the shape of hidden."""
+    layout = _check_inputs(hidden, weight, targets, bias)
     p = problem_for(hidden, weight, bias, ignore_index, logit_scale, softcap, reduction,
                     False, bwd_vocab_chunk=bwd_vocab_chunk, label_smoothing=label_smoothing,
-                    z_loss=z_loss, class_weight=class_weight, grad_weight_fp32=grad_weight_fp32)
+                    z_loss=z_loss, class_weight=class_weight, grad_weight_fp32=grad_weight_fp32,
+                    layout=layout)
     dev = hidden.device
     if grad_loss is not None:
         grad_loss = grad_loss.to(device=dev, dtype=torch.float32).contiguous()
-        expect = hidden.shape[0] if reduction == "none" else 1
+        expect = targets.numel() if reduction == "none" else 1
         if grad_loss.numel() != expect:
             raise ValueError(f"grad_loss must have {expect} elements")
-    gh = torch.empty_like(hidden) if need_hidden else None
+    gh = torch.empty(hidden.shape, dtype=hidden.dtype, device=dev) if need_hidden else None
     gdt = torch.float32 if grad_weight_fp32 else weight.dtype
     gw = torch.empty(weight.shape, dtype=gdt, device=dev) if need_weight else None
     gb = torch.empty(bias.shape, dtype=gdt, device=dev) if (need_bias and bias is not None) else None

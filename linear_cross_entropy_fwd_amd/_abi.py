@@ -42,6 +42,11 @@ class Problem(ctypes.Structure):
         ("class_weight", ctypes.c_void_p),
         ("predictions", ctypes.c_void_p),
         ("grad_weight_fp32", ctypes.c_int32),
+        ("seq_len", ctypes.c_int64),
+        ("hidden_row_stride", ctypes.c_int64),
+        ("hidden_seq_stride", ctypes.c_int64),
+        ("targets_stride", ctypes.c_int64),
+        ("targets_seq_stride", ctypes.c_int64),
     ]
 
 
@@ -67,6 +72,7 @@ _SIGNATURES = {
     "flce_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "flce_last_error": (ctypes.c_char_p, []),
     "flce_version": (ctypes.c_char_p, []),
+    "flce_problem_size": (ctypes.c_size_t, []),
 }
 
 
@@ -100,15 +106,19 @@ def check(status: int) -> None:
 def make_problem(n, h, v, dtype, reduction="mean", ignore_index=-100, logit_scale=1.0,
                  softcap=None, return_metrics=False, has_bias=False, fwd_tiles_per_split=0,
                  bwd_vocab_chunk=0, label_smoothing=0.0, z_loss=0.0, class_weight=0,
-                 predictions=0, grad_weight_fp32=False) -> Problem:
+                 predictions=0, grad_weight_fp32=False, seq_len=0, hidden_row_stride=0,
+                 hidden_seq_stride=0, targets_stride=0, targets_seq_stride=0) -> Problem:
     """class_weight / predictions: integer device addresses (fp32 [V] in,
-    int64 [N] out), or 0.  grad_weight_fp32: 1 for fp32 grad_weight / grad_bias."""
+    int64 [N] out), or 0.  grad_weight_fp32: 1 for fp32 grad_weight / grad_bias.
+    seq_len and the strides (elements) describe a strided token layout; 0 = default."""
     return Problem(int(n), int(h), int(v), int(ignore_index), int(dtype),
                    REDUCTIONS[reduction] if isinstance(reduction, str) else int(reduction),
                    float(logit_scale), 0.0 if softcap is None else float(softcap),
                    int(bool(return_metrics)), int(bool(has_bias)), int(fwd_tiles_per_split),
                    int(bwd_vocab_chunk), float(label_smoothing), float(z_loss),
-                   int(class_weight) or None, int(predictions) or None, int(grad_weight_fp32))
+                   int(class_weight) or None, int(predictions) or None, int(grad_weight_fp32),
+                   int(seq_len), int(hidden_row_stride), int(hidden_seq_stride), int(targets_stride),
+                   int(targets_seq_stride))
 
 
 def flce_forward_workspace_size(p: Problem) -> int:

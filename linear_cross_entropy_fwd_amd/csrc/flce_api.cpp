@@ -81,14 +81,76 @@ flce_status_t check_problem(const flce_problem_t* p) {
     return fail(FLCE_ERR_INVALID_ARGUMENT, "grad_weight_fp32 must be 0 or 1");
   if (p->predictions && !p->return_metrics)
     return fail(FLCE_ERR_INVALID_ARGUMENT, "predictions need return_metrics=1");
+  if (p->seq_len < 0 || p->hidden_row_stride < 0 || p->hidden_seq_stride < 0 || p->targets_stride < 0 ||
+      p->targets_seq_stride < 0)
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "seq_len and strides must be >= 0");
+  if (p->seq_len > 0 && p->n_tokens % p->seq_len != 0)
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "n_tokens (%lld) must be a multiple of seq_len (%lld)",
+                (long long)p->n_tokens, (long long)p->seq_len);
+  if ((p->hidden_row_stride * elem_bytes(p->dtype)) % 16 != 0 ||
+      (p->hidden_seq_stride * elem_bytes(p->dtype)) % 16 != 0)
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "hidden strides times sizeof(dtype) must be multiples of 16 bytes");
   return FLCE_OK;
+}
+
+// ---------------------------------------------------------------- token layout
+
+// Token n = s * T + t.  Hidden rows and targets that are not contiguous are
+// gathered into contiguous workspace rows first: the GEMM tiles keep one
+// compile-time-shaped panel per tile (a runtime row pitch there costs
+// registers in the K loop).
+struct TokLayout {
+  int64_t T, hr, hs, ts, tss;  // hidden strides in elements, target strides in elements
+  bool h_gather, t_gather;
+};
+
+TokLayout tok_layout(const flce_problem_t& p) {
+  TokLayout L{};
+  const int64_t N = p.n_tokens;
+  L.T = p.seq_len > 0 ? p.seq_len : std::max<int64_t>(N, 1);
+  const bool one_seq = N <= L.T;
+  L.hr = p.hidden_row_stride > 0 ? p.hidden_row_stride : p.hidden;
+  L.hs = p.hidden_seq_stride > 0 ? p.hidden_seq_stride : L.T * L.hr;
+  L.ts = p.targets_stride > 0 ? p.targets_stride : 1;
+  L.tss = p.targets_seq_stride > 0 ? p.targets_seq_stride : L.T * L.ts;
+  L.h_gather = N > 0 && !(L.hr == p.hidden && (one_seq || L.hs == L.T * L.hr));
+  L.t_gather = N > 0 && !(L.ts == 1 && (one_seq || L.tss == L.T));
+  return L;
+}
+
+// The hidden rows and targets the kernels read: in place, or gathered into
+// the workspace at off_h / off_t.
+struct TokInputs {
+  const char* hidden;  // N contiguous rows of H elements
+  const int64_t* targets;
+};
+
+hipError_t tok_inputs(const flce_problem_t& p, const TokLayout& L, const void* hidden, const int64_t* targets,
+                      char* ws, size_t off_h, size_t off_t, hipStream_t st, TokInputs& out) {
+  const int eb = elem_bytes(p.dtype);
+  out.hidden = reinterpret_cast<const char*>(hidden);
+  out.targets = targets;
+  hipError_t e;
+  if (L.h_gather) {
+    flce::GatherRowsArgs a{out.hidden, ws + off_h, p.n_tokens, L.T, p.hidden * eb, L.hr * eb, L.hs * eb};
+    if ((e = flce::launch_gather_rows(a, st)) != hipSuccess) return e;
+    out.hidden = ws + off_h;
+  }
+  if (L.t_gather) {
+    int64_t* dst = reinterpret_cast<int64_t*>(ws + off_t);
+    flce::GatherTargetsArgs a{targets, dst, p.n_tokens, L.T, L.ts, L.tss};
+    if ((e = flce::launch_gather_targets(a, st)) != hipSuccess) return e;
+    out.targets = dst;
+  }
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------- forward plan
 
 struct FwdLayout {
   int n_tok_tiles, n_voc_tiles, tiles_per_split, n_splits;
-  size_t off_status, off_part, off_rowloss, off_rowent, off_rowflag, off_roww, total;
+  TokLayout tok;
+  size_t off_status, off_part, off_rowloss, off_rowent, off_rowflag, off_roww, off_hrows, off_tgt, total;
 };
 
 FwdLayout fwd_layout(const flce_problem_t& p) {
@@ -113,6 +175,9 @@ FwdLayout fwd_layout(const flce_problem_t& p) {
   L.off_rowent = take((size_t)N * 4);
   L.off_rowflag = take((size_t)N * 4);
   L.off_roww = take((size_t)N * 4);
+  L.tok = tok_layout(p);
+  L.off_hrows = take(L.tok.h_gather ? (size_t)N * p.hidden * elem_bytes(p.dtype) : 0);
+  L.off_tgt = take(L.tok.t_gather ? (size_t)N * 8 : 0);
   L.total = off;
   return L;
 }
@@ -124,7 +189,8 @@ constexpr int64_t kMaxPanelPitch = int64_t(1) << 24;  // bytes
 struct BwdLayout {
   int64_t chunk, npad, cvpad_max;
   int n_chunks, n_tok_tiles, n_h_tiles;
-  size_t off_scale, off_ht, off_wct, off_g, off_gt, off_dh, off_db, total;
+  TokLayout tok;
+  size_t off_scale, off_ht, off_wct, off_g, off_gt, off_dh, off_db, off_hrows, off_tgt, total;
 };
 
 BwdLayout bwd_layout(const flce_problem_t& p) {
@@ -159,6 +225,9 @@ BwdLayout bwd_layout(const flce_problem_t& p) {
   L.off_gt = take((size_t)L.cvpad_max * L.npad * eb);
   L.off_dh = take(L.n_chunks > 1 ? (size_t)N * H * 4 : 0);
   L.off_db = take(p.has_bias ? (size_t)flce::kBiasParts * L.n_tok_tiles * V * 4 : 0);
+  L.tok = tok_layout(p);
+  L.off_hrows = take(L.tok.h_gather ? (size_t)N * H * eb : 0);
+  L.off_tgt = take(L.tok.t_gather ? (size_t)N * 8 : 0);
   L.total = off;
   return L;
 }
@@ -214,8 +283,12 @@ flce_status_t flce_forward(const flce_problem_t* p, const void* hidden, const vo
   const bool metrics_on = p->return_metrics != 0;
   hipError_t e;
   if (N > 0) {
+    TokInputs in{};
+    if ((e = tok_inputs(*p, L.tok, hidden, targets, ws, L.off_hrows, L.off_tgt, st, in)) != hipSuccess)
+      return hip_fail(e, "gather kernel");
+    targets = in.targets;
     flce::FwdArgs fa{};
-    fa.hidden = reinterpret_cast<const char*>(hidden);
+    fa.hidden = in.hidden;
     fa.weight = reinterpret_cast<const char*>(weight);
     fa.bias = reinterpret_cast<const char*>(bias);
     fa.targets = targets;
@@ -316,6 +389,10 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
     return FLCE_OK;
   }
 
+  TokInputs in{};
+  if ((e = tok_inputs(*p, L.tok, hidden, targets, ws, L.off_hrows, L.off_tgt, st, in)) != hipSuccess)
+    return hip_fail(e, "gather kernel");
+  targets = in.targets;
   float* scale = reinterpret_cast<float*>(ws + L.off_scale);
   flce::PrepArgs pa{targets, grad_loss, p->class_weight, scale, N, V, p->ignore_index, p->reduction,
                     p->logit_scale};
@@ -328,7 +405,7 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
   float* dh = reinterpret_cast<float*>(ws + L.off_dh);
   float* db = reinterpret_cast<float*>(ws + L.off_db);
   if (want_dw) {
-    flce::TransposeArgs ta{reinterpret_cast<const char*>(hidden), ht, N, H, H, L.npad};
+    flce::TransposeArgs ta{in.hidden, ht, N, H, H, L.npad};
     if ((e = flce::launch_transpose(p->dtype, ta, st)) != hipSuccess) return hip_fail(e, "transpose kernel");
   }
   for (int c = 0; c < L.n_chunks; ++c) {
@@ -343,7 +420,7 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
       if ((e = flce::launch_transpose(p->dtype, ta, st)) != hipSuccess) return hip_fail(e, "transpose kernel");
     }
     flce::GArgs ga{};
-    ga.hidden = reinterpret_cast<const char*>(hidden);
+    ga.hidden = in.hidden;
     ga.weight = reinterpret_cast<const char*>(weight);
     ga.bias = reinterpret_cast<const char*>(bias);
     ga.targets = targets;
@@ -440,5 +517,6 @@ const char* flce_status_str(flce_status_t s) {
 const char* flce_last_error(void) { return g_last_error.c_str(); }
 
 const char* flce_version(void) { return "flce-gfx950 0.1.0"; }
+size_t flce_problem_size(void) { return sizeof(flce_problem_t); }
 
 }  // extern "C"

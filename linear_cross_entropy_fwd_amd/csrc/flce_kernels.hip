@@ -1077,6 +1077,25 @@ __global__ __launch_bounds__(256) void bwd_db_kernel(DbArgs a) {
   else reinterpret_cast<T*>(a.out)[v] = from_f32<D>(s * a.scale[0]);
 }
 
+// ------------------------------------------------------------------ strided token layouts
+
+// One workgroup per token row: 16-byte pieces of the row (row_bytes is a
+// multiple of 16, and so are both source strides).
+__global__ __launch_bounds__(256) void gather_rows_kernel(GatherRowsArgs a) {
+  const int64_t n = blockIdx.x, s = n / a.T, t = n - s * a.T;
+  const char* src = a.src + s * a.seq_bytes + t * a.row_pitch;
+  char* dst = a.dst + n * a.row_bytes;
+  for (int64_t c = (int64_t)threadIdx.x * 16; c < a.row_bytes; c += 256 * 16)
+    *reinterpret_cast<uint4*>(dst + c) = *reinterpret_cast<const uint4*>(src + c);
+}
+
+__global__ __launch_bounds__(256) void gather_targets_kernel(GatherTargetsArgs a) {
+  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (n >= a.N) return;
+  const int64_t s = n / a.T, t = n - s * a.T;
+  a.dst[n] = a.src[s * a.seq_stride + t * a.stride];
+}
+
 // ------------------------------------------------------------------ launchers
 
 static inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
@@ -1190,6 +1209,18 @@ hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t st) {
   const unsigned grid = (unsigned)std::min<int64_t>(4096, ((int64_t)bytes + 255) / 256);
   hipLaunchKernelGGL(fill_zero_kernel, dim3(grid), dim3(256), 0, st, reinterpret_cast<uint8_t*>(dst),
                      (int64_t)bytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const GatherRowsArgs& a, hipStream_t st) {
+  if (a.N <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)a.N), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_targets(const GatherTargetsArgs& a, hipStream_t st) {
+  if (a.N <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_targets_kernel, dim3(blocks_for(a.N, 256)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -91,6 +91,20 @@ struct TransposeArgs {
   int64_t rows, cols, src_ld, rpad;
 };
 
+// Token n = s * T + t of a strided layout into contiguous rows: hidden row
+// bytes at src + s * seq_bytes + t * row_pitch, targets at element
+// s * seq_stride + t * stride.
+struct GatherRowsArgs {
+  const char* src;
+  char* dst;           // [N][row_bytes]
+  int64_t N, T, row_bytes, row_pitch, seq_bytes;
+};
+struct GatherTargetsArgs {
+  const int64_t* src;
+  int64_t* dst;        // [N]
+  int64_t N, T, stride, seq_stride;
+};
+
 struct GArgs {
   const char* hidden;
   const char* weight;   // full (V,H)
@@ -151,5 +165,7 @@ hipError_t launch_backward_dh(int dtype, const DhArgs& a, hipStream_t st);
 hipError_t launch_backward_dw(int dtype, const DwArgs& a, hipStream_t st);
 hipError_t launch_backward_db(int dtype, const DbArgs& a, hipStream_t st);
 hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t st);
+hipError_t launch_gather_rows(const GatherRowsArgs& a, hipStream_t st);
+hipError_t launch_gather_targets(const GatherTargetsArgs& a, hipStream_t st);
 
 }  // namespace flce

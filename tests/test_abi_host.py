@@ -31,6 +31,11 @@ def test_library_exports_every_declared_function():
     assert _abi.flce_version().startswith("flce-gfx950")
 
 
+def test_problem_struct_matches_the_library():
+    import ctypes
+    assert _abi.library().flce_problem_size() == ctypes.sizeof(_abi.Problem)
+
+
 def test_status_strings():
     lib = _abi.library()
     for code, name in _abi.STATUS.items():
@@ -67,6 +72,12 @@ def base(**kw):
     (dict(predictions=(1 << 40) + 4, return_metrics=True), INVALID),  # misaligned int64 array
     (dict(predictions=1 << 40), INVALID),            # predictions without return_metrics
     (dict(grad_weight_fp32=2), INVALID),
+    (dict(seq_len=-1), INVALID),
+    (dict(seq_len=48), INVALID),                     # 64 tokens are not whole sequences of 48
+    (dict(hidden_row_stride=129), INVALID),          # 516-byte rows: not 16-byte multiples
+    (dict(hidden_seq_stride=-4), INVALID),
+    (dict(targets_stride=-1), INVALID),
+    (dict(seq_len=16, hidden_seq_stride=2049), INVALID),
 ])
 def test_invalid_problems(kw, status):
     p = base(**kw)
@@ -147,6 +158,28 @@ def test_plan_overrides_change_workspace():
     assert c < d
 
 
+def test_token_layout_workspace():
+    """Contiguous rows are read in place; any other layout adds one gathered
+    copy of hidden (N*H elements) and / or of the targets (N int64)."""
+    n, h, v = 512, 256, 50000
+    for size in (_abi.flce_forward_workspace_size, _abi.flce_backward_workspace_size):
+        plain = size(make_problem(n, h, v, BF16))
+        # explicit defaults, and sequences back to back: contiguous, no gather
+        assert size(make_problem(n, h, v, BF16, hidden_row_stride=h, targets_stride=1)) == plain
+        assert size(make_problem(n, h, v, BF16, seq_len=128, hidden_seq_stride=128 * h,
+                                 targets_seq_stride=128)) == plain
+        # a wider row pitch: hidden gathered
+        wide = size(make_problem(n, h, v, BF16, hidden_row_stride=h + 64))
+        assert n * h * 2 <= wide - plain < n * h * 2 + 256
+        # hidden[:, :-1] of (4, 129, h) and labels[:, 1:] of (4, 129): both gathered
+        shifted = size(make_problem(n, h, v, BF16, seq_len=128, hidden_seq_stride=129 * h,
+                                    targets_seq_stride=129))
+        assert n * h * 2 + n * 8 <= shifted - plain < n * h * 2 + n * 8 + 2 * 256
+        # strided targets alone
+        t_only = size(make_problem(n, h, v, BF16, targets_stride=2))
+        assert n * 8 <= t_only - plain < n * 8 + 256
+
+
 def test_valid_call_without_gpu_reports_hip_error():
     import torch
     if torch.cuda.is_available():
@@ -155,3 +188,36 @@ def test_valid_call_without_gpu_reports_hip_error():
     st = _abi.flce_forward(p, 0, 0, 0, 0, FAKE, 0, 0, FAKE, 1 << 20, 0)
     assert st == HIP
     assert "device" in _abi.last_error().lower() or _abi.last_error()
+
+
+def test_token_layout_from_tensor_views():
+    import torch
+    from linear_cross_entropy_fwd_amd import token_layout
+    h = torch.zeros(4, 129, 64, dtype=torch.bfloat16)
+    lab = torch.zeros(4, 129, dtype=torch.int64)
+    # contiguous (N, H) / (N,): the defaults, read in place
+    lay = token_layout(h.view(-1, 64), lab.view(-1))
+    assert lay == dict(seq_len=0, hidden_row_stride=64, hidden_seq_stride=0, targets_stride=1,
+                       targets_seq_stride=0)
+    # the shifted views of a causal LM batch
+    lay = token_layout(h[:, :-1], lab[:, 1:])
+    assert lay == dict(seq_len=128, hidden_row_stride=64, hidden_seq_stride=129 * 64, targets_stride=1,
+                       targets_seq_stride=129)
+    p = make_problem(4 * 128, 64, 1000, BF16, **lay)
+    plain = _abi.flce_forward_workspace_size(make_problem(4 * 128, 64, 1000, BF16))
+    assert _abi.flce_forward_workspace_size(p) >= plain + 4 * 128 * (64 * 2 + 8)
+    # (S, T, H) with contiguous (S*T,) targets
+    lay = token_layout(h, lab.view(-1))
+    assert lay["seq_len"] == 129 and lay["targets_stride"] == 1 and lay["targets_seq_stride"] == 129
+    # a size-1 sequence dimension: its stride is irrelevant
+    lay = token_layout(h[:1, :-1], lab[:1, 1:])
+    assert lay["hidden_seq_stride"] == 0 and lay["targets_seq_stride"] == 0
+    # one token per sequence: no row stride
+    lay = token_layout(h[:, :1], lab[:, :1])
+    assert lay["hidden_row_stride"] == 0 and lay["targets_stride"] == 0 and lay["seq_len"] == 1
+    with pytest.raises(ValueError):
+        token_layout(h[:, :, ::2], lab)                      # no unit stride along H
+    with pytest.raises(ValueError):
+        token_layout(h[:1].expand(4, 129, 64), lab)          # broadcast rows
+    with pytest.raises(ValueError):
+        token_layout(torch.zeros(4, 129, 68, dtype=torch.bfloat16)[:, :, :64], lab)  # 136-byte pitch
