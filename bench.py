@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 
 METRIC = "fwd+bwd TFLOP/s (8*N*H*V) and MFMA util at N=4096,H=4096,V=128256 bf16"
 PEAK_BF16_TFLOPS = 2516.6          # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+PEAK_TFLOPS = {"bf16": PEAK_BF16_TFLOPS, "f16": PEAK_BF16_TFLOPS, "f32": 157.3}  # dense MFMA per dtype
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_tiles_headvocab_traffic.json")
 KERNEL_SOURCES = ["linear_cross_entropy_fwd_amd/csrc/flce_kernels.hip",
@@ -98,6 +99,8 @@ def main():
     ap.add_argument("--z-loss", type=float, default=0.0, help="loss variant (not the headline): z-loss coefficient")
     ap.add_argument("--class-weights", action="store_true",
                     help="loss variant (not the headline): seeded class weights, uniform in [0.5, 1.5)")
+    ap.add_argument("--dtype", choices=["bf16", "f16", "f32"], default=None,
+                    help="run the workload in another dtype (not the headline)")
     ap.add_argument("--grad-weight-fp32", action="store_true",
                     help="write grad_weight / grad_bias in fp32 (not the headline)")
     args = ap.parse_args()
@@ -119,6 +122,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = fi.WORKLOADS[args.workload]
+    if args.dtype and args.dtype != w.dtype:
+        w = w.resized(dtype=args.dtype, name=w.name.replace(w.dtype, args.dtype))
+        variants = True
     d = fi.generate(w, device=dev)
     hidden, weight, targets, bias = d["hidden"], d["weight"], d["targets"], d["bias"]
     torch.cuda.synchronize()
@@ -218,15 +224,15 @@ def main():
                    **({"label_smoothing": args.label_smoothing, "z_loss": args.z_loss,
                        "class_weights": bool(args.class_weights),
                        "grad_weight_fp32": bool(args.grad_weight_fp32)} if variants else {})},
-        "mfma_util": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "mfma_util": round(tflops / PEAK_TFLOPS[w.dtype], 4),
         "fwd_ms": round(fwd_ms, 4),
         "bwd_ms": round(bwd_ms, 4),
         "peak_mem_incr_mb": round(peak_incr / 2**20, 1),
         "n_by_v_bytes_mb": round(w.n * w.v * 2 / 2**20, 1),
         "wall_s_timed": round(t_wall, 3),
         "roofline": {"kernel": "fwd_tiles_kernel (forward logit tiles + online LSE)",
-                     "bound": "mfma", "achieved": round(fwd_tflops, 3), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
+                     "bound": "mfma", "achieved": round(fwd_tflops, 3), "peak": PEAK_TFLOPS[w.dtype],
+                     "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_TFLOPS[w.dtype], 4),
                      "traffic": traffic,
                      "flops_per_launch": 2 * w.n * w.h * w.v,
                      "window": "HIP events around flce_forward (tile kernel + combine + reduce)"},

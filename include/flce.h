@@ -155,6 +155,22 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
                             void* grad_bias, void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/* Forward and backward in one call, for callers that know the upstream
+ * gradient when they compute the loss (the gradient-in-forward use of the
+ * Liger FLCE pull requests, Summary: loss and gradients from one fused
+ * call).  Same arguments as the two calls above; lse may be NULL (it is
+ * then kept in the workspace), grad_loss as in flce_backward (NULL = 1; a
+ * per-row [N] gradient with reduction NONE).  One workspace of
+ * flce_forward_backward_workspace_size bytes serves both passes; the
+ * forward's region comes first, so flce_forward_status reads it afterwards.
+ * Results are bit-identical to flce_forward followed by flce_backward. */
+size_t flce_forward_backward_workspace_size(const flce_problem_t* p);
+flce_status_t flce_forward_backward(const flce_problem_t* p, const void* hidden, const void* weight,
+                                    const int64_t* targets, const void* bias, float* loss, float* lse,
+                                    float* metrics, const float* grad_loss, void* grad_hidden,
+                                    void* grad_weight, void* grad_bias, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
 /* Synchronously reads the device status word the last flce_forward call
  * left in `workspace` (bit 0: a non-ignored target outside [0,V)).
  * Waits for `stream`.  Debug helper, not for hot loops. */

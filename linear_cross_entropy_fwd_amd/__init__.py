@@ -21,7 +21,7 @@ import torch
 from . import _abi
 from ._abi import FlceError, Problem, library, make_problem  # noqa: F401
 
-__all__ = ["fused_linear_cross_entropy", "flce_forward", "flce_backward", "FlceError",
+__all__ = ["fused_linear_cross_entropy", "flce_forward", "flce_backward", "flce_forward_backward", "FlceError",
            "Problem", "make_problem", "library", "token_layout"]
 
 _DTYPES = {torch.float32: _abi.F32, torch.float16: _abi.F16, torch.bfloat16: _abi.BF16}
@@ -185,6 +185,52 @@ def flce_backward(hidden, weight, targets, bias, lse, grad_loss=None, *, ignore_
                                   _ptr(lse), _ptr(grad_loss), _ptr(gh), _ptr(gw), _ptr(gb),
                                   _ptr(workspace), workspace.numel(), stream))
     return gh, gw, gb
+
+
+def flce_forward_backward(hidden, weight, targets, bias=None, grad_loss=None, *, ignore_index=-100,
+                          logit_scale=1.0, softcap=None, reduction="mean", return_metrics=False,
+                          want_lse=False, need_hidden=True, need_weight=True, need_bias=True,
+                          workspace: Optional[torch.Tensor] = None, fwd_tiles_per_split=0,
+                          bwd_vocab_chunk=0, label_smoothing=0.0, z_loss=0.0, class_weight=None,
+                          predictions: Optional[torch.Tensor] = None, grad_weight_fp32=False):
+    """Loss and gradients in one library call (``flce_forward_backward``):
+    returns (loss, lse or None, metrics or None, (grad_hidden, grad_weight,
+    grad_bias)).  ``grad_loss`` is the upstream gradient as in
+    ``flce_backward`` (None = 1)."""
+    layout = _check_inputs(hidden, weight, targets, bias)
+    n = targets.numel()
+    if predictions is not None and (predictions.shape != (n,) or predictions.dtype != torch.int64
+                                    or predictions.device != hidden.device or not predictions.is_contiguous()):
+        raise ValueError("predictions must be an int64 (N,) tensor on the device of hidden")
+    p = problem_for(hidden, weight, bias, ignore_index, logit_scale, softcap, reduction,
+                    return_metrics, fwd_tiles_per_split=fwd_tiles_per_split,
+                    bwd_vocab_chunk=bwd_vocab_chunk, label_smoothing=label_smoothing, z_loss=z_loss,
+                    class_weight=class_weight, predictions=predictions,
+                    grad_weight_fp32=grad_weight_fp32, layout=layout)
+    dev = hidden.device
+    if grad_loss is not None:
+        grad_loss = grad_loss.to(device=dev, dtype=torch.float32).contiguous()
+        if grad_loss.numel() != (n if reduction == "none" else 1):
+            raise ValueError("grad_loss must have N elements for reduction 'none', else 1")
+    loss = torch.empty(n if reduction == "none" else 1, dtype=torch.float32, device=dev)
+    lse = torch.empty(n, dtype=torch.float32, device=dev) if want_lse else None
+    metrics = torch.empty(2, dtype=torch.float32, device=dev) if return_metrics else None
+    gh = torch.empty(hidden.shape, dtype=hidden.dtype, device=dev) if need_hidden else None
+    gdt = torch.float32 if grad_weight_fp32 else weight.dtype
+    gw = torch.empty(weight.shape, dtype=gdt, device=dev) if need_weight else None
+    gb = torch.empty(bias.shape, dtype=gdt, device=dev) if (need_bias and bias is not None) else None
+    need = _abi.flce_forward_backward_workspace_size(p)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream().cuda_stream
+    _abi.check(_abi.flce_forward_backward(p, _ptr(hidden), _ptr(weight), _ptr(targets), _ptr(bias),
+                                          _ptr(loss), _ptr(lse), _ptr(metrics), _ptr(grad_loss),
+                                          _ptr(gh), _ptr(gw), _ptr(gb), _ptr(workspace),
+                                          workspace.numel(), stream))
+    if reduction != "none":
+        loss = loss.view(())
+    return loss, lse, metrics, (gh, gw, gb)
 
 
 class _FusedLinearCrossEntropy(torch.autograd.Function):

@@ -68,6 +68,9 @@ _SIGNATURES = {
     "flce_forward": (ctypes.c_int, [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
     "flce_backward": (ctypes.c_int, [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                      ctypes.c_size_t, _VP]),
+    "flce_forward_backward_workspace_size": (ctypes.c_size_t, [_PP]),
+    "flce_forward_backward": (ctypes.c_int, [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                             _VP, ctypes.c_size_t, _VP]),
     "flce_forward_status": (ctypes.c_int, [_PP, _VP, ctypes.POINTER(ctypes.c_uint32), _VP]),
     "flce_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "flce_last_error": (ctypes.c_char_p, []),
@@ -134,6 +137,17 @@ def flce_forward(p: Problem, hidden, weight, targets, bias, loss, lse, metrics, 
     """Raw call with integer device addresses (0 = NULL); returns the status."""
     return library().flce_forward(ctypes.byref(p), hidden, weight, targets, bias, loss, lse,
                                   metrics, workspace, workspace_bytes, stream)
+
+
+def flce_forward_backward_workspace_size(p: Problem) -> int:
+    return int(library().flce_forward_backward_workspace_size(ctypes.byref(p)))
+
+
+def flce_forward_backward(p: Problem, hidden, weight, targets, bias, loss, lse, metrics, grad_loss,
+                          grad_hidden, grad_weight, grad_bias, workspace, workspace_bytes, stream) -> int:
+    return library().flce_forward_backward(ctypes.byref(p), hidden, weight, targets, bias, loss, lse,
+                                           metrics, grad_loss, grad_hidden, grad_weight, grad_bias,
+                                           workspace, workspace_bytes, stream)
 
 
 def flce_backward(p: Problem, hidden, weight, targets, bias, lse, grad_loss, grad_hidden,

@@ -232,6 +232,20 @@ BwdLayout bwd_layout(const flce_problem_t& p) {
   return L;
 }
 
+// One workspace for flce_forward_backward: [forward][lse][backward].
+struct FwdBwdLayout {
+  size_t fwd_bytes, off_lse, off_bwd, total;
+};
+
+FwdBwdLayout fwdbwd_layout(const flce_problem_t& p) {
+  FwdBwdLayout L{};
+  L.fwd_bytes = (size_t)round_up((int64_t)fwd_layout(p).total, kAlign);
+  L.off_lse = L.fwd_bytes;
+  L.off_bwd = (size_t)round_up((int64_t)(L.off_lse + (size_t)p.n_tokens * 4), kAlign);
+  L.total = L.off_bwd + bwd_layout(p).total;
+  return L;
+}
+
 flce_status_t check_workspace(const void* ws, size_t bytes, size_t need) {
   if (need == 0) return FLCE_OK;
   if (!ws) return fail(FLCE_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
@@ -345,22 +359,19 @@ flce_status_t flce_forward(const flce_problem_t* p, const void* hidden, const vo
   return FLCE_OK;
 }
 
-flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const void* weight,
-                            const int64_t* targets, const void* bias, const float* lse,
-                            const float* grad_loss, void* grad_hidden, void* grad_weight,
-                            void* grad_bias, void* workspace, size_t workspace_bytes, void* stream) {
-  flce_status_t s = check_problem(p);
-  if (s != FLCE_OK) return s;
-  const int64_t N = p->n_tokens, H = p->hidden, V = p->vocab;
+// The backward's argument checks (no launch): flce_backward and
+// flce_forward_backward run them before anything is enqueued.
+static flce_status_t check_backward_args(const flce_problem_t* p, const void* hidden, const void* weight,
+                                         const int64_t* targets, const void* bias, const float* lse,
+                                         const float* grad_loss, void* grad_hidden, void* grad_weight,
+                                         void* grad_bias) {
+  const int64_t N = p->n_tokens;
   const int eb = elem_bytes(p->dtype);
   if (grad_bias && !p->has_bias) return fail(FLCE_ERR_INVALID_ARGUMENT, "grad_bias given but has_bias=0");
   if (p->has_bias && !bias) return fail(FLCE_ERR_INVALID_ARGUMENT, "has_bias=1 but bias is NULL");
   if (!p->has_bias && bias) return fail(FLCE_ERR_INVALID_ARGUMENT, "bias given but has_bias=0");
-  const bool want_dh = grad_hidden != nullptr && N > 0;
-  const bool want_dw = grad_weight != nullptr;
-  const bool want_db = grad_bias != nullptr;
   const int geb = p->grad_weight_fp32 ? 4 : eb;  // bytes per grad_weight / grad_bias element
-  if (!want_dh && !want_dw && !want_db) return FLCE_OK;
+  if (!(grad_hidden && N > 0) && !grad_weight && !grad_bias) return FLCE_OK;
   if (N > 0 && (!hidden || !weight || !targets || !lse))
     return fail(FLCE_ERR_INVALID_ARGUMENT, "hidden, weight, targets and lse must be non-NULL");
   if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(grad_hidden, 16) || !aligned(grad_weight, 16))
@@ -375,6 +386,25 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
   if (L.npad * eb >= kMaxPanelPitch || L.cvpad_max * eb >= kMaxPanelPitch)
     return fail(FLCE_ERR_UNSUPPORTED, "backward needs n_tokens and the vocabulary chunk times sizeof(dtype) "
                 "below 16 MiB (n_tokens=%lld, chunk=%lld)", (long long)N, (long long)L.chunk);
+  return FLCE_OK;
+}
+
+flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const void* weight,
+                            const int64_t* targets, const void* bias, const float* lse,
+                            const float* grad_loss, void* grad_hidden, void* grad_weight,
+                            void* grad_bias, void* workspace, size_t workspace_bytes, void* stream) {
+  flce_status_t s = check_problem(p);
+  if (s != FLCE_OK) return s;
+  s = check_backward_args(p, hidden, weight, targets, bias, lse, grad_loss, grad_hidden, grad_weight, grad_bias);
+  if (s != FLCE_OK) return s;
+  const int64_t N = p->n_tokens, H = p->hidden, V = p->vocab;
+  const int eb = elem_bytes(p->dtype);
+  const bool want_dh = grad_hidden != nullptr && N > 0;
+  const bool want_dw = grad_weight != nullptr;
+  const bool want_db = grad_bias != nullptr;
+  const int geb = p->grad_weight_fp32 ? 4 : eb;  // bytes per grad_weight / grad_bias element
+  if (!want_dh && !want_dw && !want_db) return FLCE_OK;
+  const BwdLayout L = bwd_layout(*p);
   s = check_workspace(workspace, workspace_bytes, L.total);
   if (s != FLCE_OK) return s;
 
@@ -487,6 +517,34 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
     if ((e = flce::launch_backward_db(p->dtype, ba, st)) != hipSuccess) return hip_fail(e, "grad_bias kernel");
   }
   return FLCE_OK;
+}
+
+size_t flce_forward_backward_workspace_size(const flce_problem_t* p) {
+  if (check_problem(p) != FLCE_OK) return 0;
+  const FwdBwdLayout L = fwdbwd_layout(*p);
+  return L.total;
+}
+
+flce_status_t flce_forward_backward(const flce_problem_t* p, const void* hidden, const void* weight,
+                                    const int64_t* targets, const void* bias, float* loss, float* lse,
+                                    float* metrics, const float* grad_loss, void* grad_hidden,
+                                    void* grad_weight, void* grad_bias, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  flce_status_t s = check_problem(p);
+  if (s != FLCE_OK) return s;
+  const FwdBwdLayout L = fwdbwd_layout(*p);
+  s = check_workspace(workspace, workspace_bytes, L.total);
+  if (s != FLCE_OK) return s;
+  char* ws = reinterpret_cast<char*>(workspace);
+  float* lse_use = lse ? lse : reinterpret_cast<float*>(ws + L.off_lse);
+  // the backward's checks first, so that a call it would refuse enqueues nothing
+  s = check_backward_args(p, hidden, weight, targets, bias, lse_use, grad_loss, grad_hidden, grad_weight,
+                          grad_bias);
+  if (s != FLCE_OK) return s;
+  s = flce_forward(p, hidden, weight, targets, bias, loss, lse_use, metrics, ws, L.fwd_bytes, stream);
+  if (s != FLCE_OK) return s;
+  return flce_backward(p, hidden, weight, targets, bias, lse_use, grad_loss, grad_hidden, grad_weight,
+                       grad_bias, ws + L.off_bwd, L.total - L.off_bwd, stream);
 }
 
 flce_status_t flce_forward_status(const flce_problem_t* p, const void* workspace, uint32_t* status_out,

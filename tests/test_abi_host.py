@@ -221,3 +221,27 @@ def test_token_layout_from_tensor_views():
         token_layout(h[:1].expand(4, 129, 64), lab)          # broadcast rows
     with pytest.raises(ValueError):
         token_layout(torch.zeros(4, 129, 68, dtype=torch.bfloat16)[:, :, :64], lab)  # 136-byte pitch
+
+
+def test_forward_backward_workspace_holds_both_passes():
+    for n, h, v in [(0, 128, 1000), (64, 128, 1000), (4096, 4096, 128256)]:
+        p = make_problem(n, h, v, BF16)
+        f, b = _abi.flce_forward_workspace_size(p), _abi.flce_backward_workspace_size(p)
+        both = _abi.flce_forward_backward_workspace_size(p)
+        assert f + b + 4 * n <= both < f + b + 4 * n + 3 * 256
+    assert _abi.flce_forward_backward_workspace_size(base(n=-1)) == 0
+
+
+def test_forward_backward_validates_like_the_two_calls():
+    p = base()
+    need = _abi.flce_forward_backward_workspace_size(p)
+    # NULL inputs, a short workspace, an invalid problem: rejected before any launch
+    assert _abi.flce_forward_backward(p, 0, FAKE, FAKE, 0, FAKE, 0, 0, 0, FAKE, FAKE, 0, FAKE, need, 0) == INVALID
+    assert _abi.flce_forward_backward(p, FAKE, FAKE, FAKE, 0, FAKE, 0, 0, 0, FAKE, FAKE, 0, FAKE, need - 1,
+                                      0) == WORKSPACE
+    assert _abi.flce_forward_backward(base(reduction=9), FAKE, FAKE, FAKE, 0, FAKE, 0, 0, 0, FAKE, FAKE, 0,
+                                      FAKE, need, 0) == INVALID
+    # a gradient the backward would refuse (grad_bias without a bias) is caught before the forward runs
+    assert _abi.flce_forward_backward(p, FAKE, FAKE, FAKE, 0, FAKE, 0, 0, 0, FAKE, FAKE, FAKE, FAKE, need,
+                                      0) == INVALID
+    assert "grad_bias" in _abi.last_error()

@@ -251,3 +251,33 @@ def test_fp32_grad_weight_output_f32_inputs_and_empty():
     assert gh.numel() == 0
     assert gw.dtype == torch.float32 and gw.shape == (700, 64) and bool((gw == 0).all())
     assert gb.dtype == torch.float32 and gb.shape == (700,) and bool((gb == 0).all())
+
+
+# --------------------------------------------------------------------------- one call
+
+@pytest.mark.parametrize("wname,red,lse_out", [("transforms_bf16", "sum", False), ("midvocab_bf16", "none", True),
+                                               ("tiny_f32", "mean", False)])
+def test_forward_backward_in_one_call(wname, red, lse_out):
+    """flce_forward_backward gives the two calls' results bit for bit, and
+    the oracle's within tolerance."""
+    import linear_cross_entropy_fwd_amd as flce
+    w = W[wname].resized(n=700, h=200 if wname != "tiny_f32" else 64, v=2600, reduction=red)
+    log_case(f"one call {w.name} red={red} lse_out={lse_out}")
+    d = fill_argmax_targets(w, fi.generate(w))
+    g = gpu_inputs(d)
+    args = (g["hidden"], g["weight"], g["targets"], g["bias"])
+    kw = dict(ignore_index=w.ignore_index, logit_scale=w.logit_scale, softcap=w.softcap, reduction=red)
+    go = torch.linspace(0.25, 2.0, w.n, device="cuda") if red == "none" else torch.tensor([0.75], device="cuda")
+    var = dict(label_smoothing=0.1, z_loss=1e-4) if red != "none" else {}
+    loss, lse, metrics, grads = flce.flce_forward_backward(*args, go, return_metrics=True, want_lse=lse_out,
+                                                           bwd_vocab_chunk=1024, **var, **kw)
+    loss2, lse2, metrics2 = flce.flce_forward(*args, return_metrics=True, **var, **kw)
+    grads2 = flce.flce_backward(*args, lse2, go, bwd_vocab_chunk=1024, **var, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(loss, loss2) and torch.equal(metrics, metrics2)
+    assert (lse is None) != lse_out and (lse is None or torch.equal(lse, lse2))
+    for a, b in zip(grads, grads2):
+        assert (a is None and b is None) or torch.equal(a, b)
+    h, wt, t, b = oracle_inputs(d)
+    ref = flce_reference(h, wt, t, b, grad_output=to_np(go) if red == "none" else 0.75, **var, **kw)
+    check_against_oracle(w, d, ref, loss=loss, lse=lse2, metrics=metrics, grads=grads, what="one call")
