@@ -844,23 +844,44 @@ __global__ __launch_bounds__(W * 64) void bwd_g_kernel(GArgs a) {
       if (tl[j] >= 0) onehot[j] = cf * (coef[j] * a.keep);
     }
   }
+  if constexpr (CAP) {
 #pragma unroll
-  for (int i = 0; i < WI; ++i)
+    for (int i = 0; i < WI; ++i)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+      for (int e = 0; e < 4; ++e)
 #pragma unroll
-      for (int j = 0; j < WJ; ++j) {
-        float y = acc[i][j][e];
-        if (BIAS) y = y + bv[i][e];
-        y = a.s * y;
-        if (CAP) y = soft_cap(y, a.cap, a.inv_cap);
-        float g = fmaf(fast_exp2((y - lse[j]) * LOG2E), pscale[j], -a.eps_v);
-        if (CAP) {
+        for (int j = 0; j < WJ; ++j) {
+          float y = acc[i][j][e];
+          if (BIAS) y = y + bv[i][e];
+          y = soft_cap(a.s * y, a.cap, a.inv_cap);
+          float g = fmaf(fast_exp2((y - lse[j]) * LOG2E), pscale[j], -a.eps_v);
           const float qc = y * a.inv_cap;
           g = g * fmaf(-qc, qc, 1.f);
+          acc[i][j][e] = g * coef[j];
         }
-        acc[i][j][e] = g * coef[j];
-      }
+  } else {
+    // G = coef (pscale exp2(y s log2e - lse log2e) - eps/V): two FMAs around
+    // the exp, the per-column factors folded ahead (a dead column has
+    // lse = +inf and coef = 0: exp2(-inf) = 0 and both factors 0).
+    const float sl = a.s * LOG2E;
+    float ll[WJ], pc[WJ], ec[WJ];
+#pragma unroll
+    for (int j = 0; j < WJ; ++j) {
+      ll[j] = lse[j] * LOG2E;
+      pc[j] = pscale[j] * coef[j];
+      ec[j] = a.eps_v * coef[j];
+    }
+#pragma unroll
+    for (int i = 0; i < WI; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int j = 0; j < WJ; ++j) {
+          float y = acc[i][j][e];
+          if (BIAS) y = y + bv[i][e];
+          acc[i][j][e] = fmaf(fast_exp2(fmaf(y, sl, -ll[j])), pc[j], -ec[j]);
+        }
+  }
   if (any_t) {
 #pragma unroll
     for (int j = 0; j < WJ; ++j)
