@@ -397,12 +397,28 @@ __device__ __forceinline__ void kstage_at(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>::W
   kstage<D, W, S>(acc, f, fb, c, EDGE && ragged && kt + 1 == nk - 1, A, kt, t, side);
 }
 
-// acc[i][j] (this wave's WI x WJ blocks) = A_panel . B_panel^T over all of K.
-// Uses the stage buffers; returns after a barrier with no copy in flight, so
-// the caller may reuse them (e.g. g_stage0) right away.
+// The first two stages of a tile: the copy plan and the copies of stages 0
+// and 1.  Waits (at a barrier) until every wave is done with the stage
+// buffers of any previous use; the caller may then run code that touches
+// neither the stage buffers nor vector memory counters it waits on exactly
+// (e.g. the previous tile's epilogue) before gemm_run.
+template <int W>
+__device__ __forceinline__ void gemm_prefetch(CopyPlan<W>& cp, const Panel& A, const Panel& B) {
+  const int t = threadIdx.x;
+  const uint32_t wave_lds = (uint32_t)__builtin_amdgcn_readfirstlane(t >> 6) * 1024u;
+  copy_plan<W>(cp, A, B, t);
+  lds_barrier();  // every wave is done with the buffers of any previous use
+  copy_stage<W, 0>(StageCopy<W>{cp, 0u, wave_lds});
+  copy_stage<W, 1>(StageCopy<W>{cp, (uint32_t)ROWB, wave_lds});
+}
+
+// acc[i][j] (this wave's WI x WJ blocks) = A_panel . B_panel^T over all of K,
+// from a gemm_prefetch of the same panels.  Uses the stage buffers; returns
+// after a barrier with no copy in flight, so the caller may reuse them (e.g.
+// g_stage0) right away.
 template <int D, int W, class Side>
-__device__ __forceinline__ void gemm_nt_tile(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], const Panel& A,
-                                             const Panel& B, Side& side) {
+__device__ __forceinline__ void gemm_run(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], const CopyPlan<W>& cp,
+                                         const Panel& A, Side& side) {
   static_assert(NSTAGES == 2, "the loops below alternate two buffers");
   constexpr int H = Gemm<W>::NCOP / 2;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -415,12 +431,8 @@ __device__ __forceinline__ void gemm_nt_tile(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>
   const int nk = (int)((A.kbytes + ROWB - 1) / ROWB);
   const bool ragged = (A.kbytes % ROWB) != 0;
   const uint32_t wave_lds = (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024u;
-  CopyPlan<W> cp;
-  copy_plan<W>(cp, A, B, t);
-  lds_barrier();  // every wave is done with the buffers of any previous use
-  // stages 0 and 1
-  copy_stage<W, 0>(StageCopy<W>{cp, 0u, wave_lds});
-  copy_stage<W, 1>(StageCopy<W>{cp, (uint32_t)ROWB, wave_lds});
+  // stage 0 has landed once at most the 2H younger copies (stage 1, and any
+  // later vector memory op) are outstanding: they complete in order
   wait_vmcnt<2 * H>();
   if (ragged && nk == 1) zero_tail<W, 0>(A, 0, t);
   lds_barrier();
@@ -443,6 +455,14 @@ __device__ __forceinline__ void gemm_nt_tile(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>
   }
   wait_vmcnt<0>();
   lds_barrier();
+}
+
+template <int D, int W, class Side>
+__device__ __forceinline__ void gemm_nt_tile(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], const Panel& A,
+                                             const Panel& B, Side& side) {
+  CopyPlan<W> cp;
+  gemm_prefetch<W>(cp, A, B);
+  gemm_run<D, W>(acc, cp, A, side);
 }
 
 template <int D, int W>

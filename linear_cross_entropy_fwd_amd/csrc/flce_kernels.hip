@@ -161,10 +161,21 @@ __global__ __launch_bounds__(W * 64) void fwd_tiles_kernel(FwdArgs a) {
   }
 
   f32x4_t acc[WI][WJ];
+  // The first two stages of each next vocabulary tile are copied before this
+  // tile's epilogue (which touches only registers and g_fwd_state), so the
+  // copies' latency hides behind it.
+  CopyPlan<W> cp;
+  {
+    const int64_t v0 = (int64_t)vt_begin * TILE;
+    gemm_prefetch<W>(cp, Panel{a.weight + v0 * rowb, rowb, (int)min<int64_t>(TILE, a.V - v0), rowb}, B);
+  }
   for (int vt = vt_begin; vt < vt_end; ++vt) {
     const int64_t v0 = (int64_t)vt * TILE;
     Panel A{a.weight + v0 * rowb, rowb, (int)min<int64_t>(TILE, a.V - v0), rowb};
-    gemm_nt_tile<D, W>(acc, A, B);
+    NoSide none;
+    gemm_run<D, W>(acc, cp, A, none);
+    if (vt + 1 < vt_end)
+      gemm_prefetch<W>(cp, Panel{A.base + TILE * rowb, rowb, (int)min<int64_t>(TILE, a.V - v0 - TILE), rowb}, B);
 
     const int to = opaque_int(t);
     const int qo = (to >> 4) & 3;
