@@ -228,15 +228,16 @@ __global__ __launch_bounds__(W * 64) void fwd_tiles_kernel(FwdArgs a) {
       if (mnew != -INFINITY) {
         // four independent partial sums (one per accumulator register), so
         // that the adds do not wait on each exp in turn
+        // exp(z - m) as exp2(z log2e - m log2e): one FMA for the argument
         float sp[4] = {0.f, 0.f, 0.f, 0.f}, up[4] = {0.f, 0.f, 0.f, 0.f};
+        const float ml = mnew * LOG2E;
 #pragma unroll
         for (int i = 0; i < WI; ++i)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float d = z[i][e] - mnew;
-            const float ex = fast_exp2(d * LOG2E);
+            const float ex = fast_exp2(fmaf(z[i][e], LOG2E, -ml));
             sp[e] = sp[e] + ex;
-            if (METRICS) up[e] = fmaf(ex, fmaxf(d, -1e30f), up[e]);
+            if (METRICS) up[e] = fmaf(ex, fmaxf(z[i][e] - mnew, -1e30f), up[e]);
           }
         float sum = (sp[0] + sp[1]) + (sp[2] + sp[3]), usum = 0.f;
         if (METRICS) usum = (up[0] + up[1]) + (up[2] + up[3]);
