@@ -122,6 +122,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = fi.WORKLOADS[args.workload]
+    if args.workload != "headvocab_bf16":
+        variants = True
     if args.dtype and args.dtype != w.dtype:
         w = w.resized(dtype=args.dtype, name=w.name.replace(w.dtype, args.dtype))
         variants = True
@@ -205,7 +207,7 @@ def main():
     fwd_tflops = 2.0 * w.n * w.h * w.v / (fwd_ms * 1e-3) / 1e12
     traffic = stored_traffic()
     out = {
-        "metric": (METRIC if not variants else METRIC + ", with loss or output variants (not the headline)")
+        "metric": (METRIC if not variants else f"fwd+bwd TFLOP/s (8*N*H*V) on {w.name}" + ", other workload or options (not the headline)")
                   if run_bwd else "forward only TFLOP/s (2*N*H*V), not the headline",
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
@@ -237,8 +239,22 @@ def main():
                      "flops_per_launch": 2 * w.n * w.h * w.v,
                      "window": "HIP events around flce_forward (tile kernel + combine + reduce)"},
     }
+    if w.dtype == "f32":
+        # fp32 at small H is memory- and launch-bound, not MFMA-bound: the
+        # roofline entry is HBM bandwidth over the whole step, counting the
+        # algorithmic bytes (forward reads W and H; the backward reads them
+        # for the recompute and again for the contractions, and writes
+        # grad_weight and grad_hidden)
+        wh = (w.v * w.h + w.n * w.h) * 4
+        step_bytes = (wh if not run_bwd else 4 * wh) + w.n * 8
+        gbs = step_bytes / (ms_step * 1e-3) / 1e9
+        out["roofline"] = {"kernel": "whole step (every launch of the forward and backward)",
+                           "bound": "hbm", "achieved": round(gbs, 3), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": round(gbs / PEAK_HBM_GBS, 6), "traffic": None,
+                           "bytes_per_step": step_bytes,
+                           "window": "HIP events around each step"}
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(d, w, args.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline(d, w, min(args.cpu_rows, w.n))
     print(json.dumps(out), flush=True)
 
 
