@@ -34,15 +34,49 @@ flce_status_t hip_fail(hipError_t e, const char* what) {
 
 constexpr int64_t kTile = 256;
 constexpr int64_t kAlign = 256;
-// 48 vocabulary tiles: with 16 token tiles (4096 tokens) the recompute and
-// grad_weight grids are three full rounds of 256 workgroups, and the fp32
-// grad_hidden accumulator is re-read 11 times at V = 128256 instead of 16
-// (measured 0.45 ms faster than 8192 there).
-constexpr int64_t kDefaultChunk = 12288;
+// At most 48 vocabulary tiles per backward chunk: at the head shape (16
+// token tiles, 16 hidden tiles) the recompute and grad_weight grids are then
+// three full rounds of 256 workgroups, and the fp32 grad_hidden accumulator
+// is re-read 11 times at V = 128256 instead of 16 (measured 0.45 ms faster
+// than 8192 there); larger chunks measured slower (their G buffers outgrow
+// the last-level cache).
+constexpr int64_t kMaxChunkTiles = 48;
+constexpr int64_t kCUs = 256;  // MI355X compute units: one workgroup of a GEMM grid each at a time
+
 constexpr int kMaxSplits = 64;
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 int64_t cdiv(int64_t x, int64_t m) { return (x + m - 1) / m; }
+
+// The default backward chunk, in vocabulary tiles.  It depends on V and H
+// only, never on N, so that a row's gradient does not depend on how many
+// rows share the call (the chunking fixes grad_hidden's summation order).
+// At most cap = min(a quarter of V, kMaxChunkTiles) tiles, so the chunk
+// buffers stay far below N x V.  The candidates are cap and the multiples of
+// 16 tiles below it (with those the recompute grid, token tiles x chunk
+// tiles, is whole rounds over the CUs whenever N is a multiple of 4096).
+// Each is scored by how full the last round of its grad_weight grid is
+// (hidden tiles x chunk tiles workgroups, each a full-K GEMM tile); the
+// largest candidate within 5 % of the best score wins (fewer chunks re-read
+// the grad_hidden accumulator fewer times).  Measured with N = 16384,
+// H = 2048: 32 tiles (one round of 256) against 48 (1.5 rounds), 4.8 % off
+// the backward; a 36-tile chunk at H = 3584 (a full last grad_weight round
+// but 4.5 recompute rounds) was 8 % slower than 48.
+int64_t default_chunk_tiles(int64_t H, int64_t V) {
+  const int64_t cap = std::max<int64_t>(1, std::min<int64_t>(kMaxChunkTiles, V / 4 / kTile));
+  const int64_t h_tiles = cdiv(H, kTile);
+  auto eff = [&](int64_t k) {
+    const int64_t wg = h_tiles * k;
+    return (double)wg / (double)(cdiv(wg, kCUs) * kCUs);
+  };
+  double best_eff = eff(cap);
+  for (int64_t k = 16; k < cap; k += 16) best_eff = std::max(best_eff, eff(k));
+  if (eff(cap) >= best_eff - 0.05) return cap;
+  int64_t best = 16;
+  for (int64_t k = 16; k < cap; k += 16)
+    if (eff(k) >= best_eff - 0.05) best = k;
+  return best;
+}
 int elem_bytes(int dtype) { return dtype == FLCE_F32 ? 4 : 2; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -200,11 +234,7 @@ BwdLayout bwd_layout(const flce_problem_t& p) {
   if (p.bwd_vocab_chunk > 0) {
     L.chunk = p.bwd_vocab_chunk;
   } else {
-    // kDefaultChunk, or a quarter of V if that is smaller (at least a tile).
-    // It depends on V only, so that a row's gradient does not depend on how
-    // many rows share the call (the chunking fixes grad_hidden's summation
-    // order); with N >= H the chunk buffers then stay below an N x V buffer.
-    L.chunk = std::max<int64_t>(kTile, std::min<int64_t>(kDefaultChunk, V / 4 / kTile * kTile));
+    L.chunk = default_chunk_tiles(H, V) * kTile;
   }
   L.chunk = std::min<int64_t>(L.chunk, round_up(V, kTile));
   L.n_chunks = (int)cdiv(V, L.chunk);
