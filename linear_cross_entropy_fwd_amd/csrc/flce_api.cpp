@@ -222,7 +222,7 @@ constexpr int64_t kMaxPanelPitch = int64_t(1) << 24;  // bytes
 
 struct BwdLayout {
   int64_t chunk, npad, cvpad_max;
-  int n_chunks, n_tok_tiles, n_h_tiles;
+  int n_chunks, n_tok_tiles, n_h_tiles, dh_split;
   TokLayout tok;
   size_t off_scale, off_ht, off_wct, off_g, off_gt, off_dh, off_db, off_hrows, off_tgt, total;
 };
@@ -253,7 +253,14 @@ BwdLayout bwd_layout(const flce_problem_t& p) {
   L.off_wct = take((size_t)H * L.cvpad_max * eb);
   L.off_g = take((size_t)L.npad * L.cvpad_max * eb);
   L.off_gt = take((size_t)L.cvpad_max * L.npad * eb);
-  L.off_dh = take(L.n_chunks > 1 ? (size_t)N * H * 4 : 0);
+  // grad_hidden's grid is token tiles x hidden tiles; when that is a small
+  // part of the CUs, the chunk's K is split over 2 or 4 workgroups per tile,
+  // each into an accumulator of its own, summed in a fixed order at the end.
+  // (Rows of grad_hidden then depend on N only through this split: calls
+  // whose grids fall in the same class give bit-identical rows.)
+  const int64_t dh_tiles = (int64_t)L.n_tok_tiles * L.n_h_tiles;
+  L.dh_split = dh_tiles <= kCUs / 4 ? 4 : dh_tiles <= kCUs / 2 ? 2 : 1;
+  L.off_dh = take(L.n_chunks > 1 || L.dh_split > 1 ? (size_t)L.dh_split * N * H * 4 : 0);
   L.off_db = take(p.has_bias ? (size_t)flce::kBiasParts * L.n_tok_tiles * V * 4 : 0);
   L.tok = tok_layout(p);
   L.off_hrows = take(L.tok.h_gather ? (size_t)N * H * eb : 0);
@@ -524,7 +531,15 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
       da.n_h_tiles = L.n_h_tiles;
       da.first = c == 0;
       da.last = c == L.n_chunks - 1;
+      da.ksplit = L.dh_split;
+      da.kpart = (int)round_up(cdiv(cvpad, L.dh_split), 64);
+      da.acc_stride = N * H;
       if ((e = flce::launch_backward_dh(p->dtype, da, st)) != hipSuccess) return hip_fail(e, "grad_hidden kernel");
+      if (da.last && L.dh_split > 1) {
+        flce::DhFinalArgs fa{dh, reinterpret_cast<char*>(grad_hidden), N * H, N * H, L.dh_split};
+        if ((e = flce::launch_backward_dh_final(p->dtype, fa, st)) != hipSuccess)
+          return hip_fail(e, "grad_hidden sum kernel");
+      }
     }
     if (want_dw) {
       flce::DwArgs wa{};

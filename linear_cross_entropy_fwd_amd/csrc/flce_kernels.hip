@@ -1020,11 +1020,22 @@ __global__ __launch_bounds__(W * 64) void bwd_dh_kernel(DhArgs a) {
   const int wm = Gemm<W>::wm(wave), wn = Gemm<W>::wn(wave), c16 = lane & 15, q = lane >> 4;
   const int64_t n0 = (int64_t)tt * TILE, h0 = (int64_t)ht * TILE;
   const int64_t kb = (int64_t)a.cvpad * EB;
-  Panel A{a.WcT + h0 * kb, kb, (int)min<int64_t>(TILE, a.H - h0), kb};
-  Panel B{a.G + n0 * kb, kb, (int)min<int64_t>(TILE, a.N - n0), kb};
+  // split blockIdx.y takes ids [k0, k0 + kn) of the chunk into its own accumulator
+  const int k0 = (int)blockIdx.y * a.kpart, kn = min(a.kpart, a.cvpad - k0);
   f32x4_t acc[WI][WJ];
-  gemm_nt_tile<D, W>(acc, A, B);
+  if (kn > 0) {
+    Panel A{a.WcT + h0 * kb + (int64_t)k0 * EB, kb, (int)min<int64_t>(TILE, a.H - h0), (int64_t)kn * EB};
+    Panel B{a.G + n0 * kb + (int64_t)k0 * EB, kb, (int)min<int64_t>(TILE, a.N - n0), (int64_t)kn * EB};
+    gemm_nt_tile<D, W>(acc, A, B);
+  } else {  // a split past a short last chunk adds nothing
+#pragma unroll
+    for (int i = 0; i < WI; ++i)
+#pragma unroll
+      for (int j = 0; j < WJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
   const float scale = a.scale[0];
+  float* accbuf = a.acc + (int64_t)blockIdx.y * a.acc_stride;
+  const bool finish = a.last && a.ksplit == 1;  // else a separate pass sums the splits
   T* out = reinterpret_cast<T*>(a.out);
 #pragma unroll
   for (int j = 0; j < WJ; ++j) {
@@ -1038,16 +1049,33 @@ __global__ __launch_bounds__(W * 64) void bwd_dh_kernel(DhArgs a) {
       float v0 = acc[i][j][0] * scale, v1 = acc[i][j][1] * scale;
       float v2 = acc[i][j][2] * scale, v3 = acc[i][j][3] * scale;
       if (!a.first) {
-        const float4 o = *reinterpret_cast<const float4*>(a.acc + idx);
+        const float4 o = *reinterpret_cast<const float4*>(accbuf + idx);
         v0 = o.x + v0;
         v1 = o.y + v1;
         v2 = o.z + v2;
         v3 = o.w + v3;
       }
-      if (a.last) store4<D>(out + idx, v0, v1, v2, v3);
-      else *reinterpret_cast<float4*>(a.acc + idx) = make_float4(v0, v1, v2, v3);
+      if (finish) store4<D>(out + idx, v0, v1, v2, v3);
+      else *reinterpret_cast<float4*>(accbuf + idx) = make_float4(v0, v1, v2, v3);
     }
   }
+}
+
+// grad_hidden = sum over s = 0, 1, ... of the split accumulators, in that
+// order, four elements per thread.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dh_final_kernel(DhFinalArgs a) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= a.count) return;
+  float4 v = *reinterpret_cast<const float4*>(a.acc + i);
+  for (int s = 1; s < a.ksplit; ++s) {
+    const float4 o = *reinterpret_cast<const float4*>(a.acc + (int64_t)s * a.acc_stride + i);
+    v.x = v.x + o.x;
+    v.y = v.y + o.y;
+    v.z = v.z + o.z;
+    v.w = v.w + o.w;
+  }
+  store4<D>(reinterpret_cast<typename Elem<D>::T*>(a.out) + i, v.x, v.y, v.z, v.w);
 }
 
 // grad_weight[v][h] = scale * sum_n G[n][v] H[n][h] for one vocabulary chunk:
@@ -1205,11 +1233,24 @@ hipError_t launch_backward_g(int dtype, bool bias, bool cap, const GArgs& a, hip
 }
 
 hipError_t launch_backward_dh(int dtype, const DhArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)grouped_grid<kDhGA, kDhGB>(a.n_h_tiles, a.n_tok_tiles)), block(kContractWaves * 64);
+  const dim3 grid((unsigned)grouped_grid<kDhGA, kDhGB>(a.n_h_tiles, a.n_tok_tiles), (unsigned)a.ksplit),
+      block(kContractWaves * 64);
   switch (dtype) {
     case DT_F32: hipLaunchKernelGGL((bwd_dh_kernel<DT_F32, kContractWaves>), grid, block, 0, st, a); break;
     case DT_F16: hipLaunchKernelGGL((bwd_dh_kernel<DT_F16, kContractWaves>), grid, block, 0, st, a); break;
     case DT_BF16: hipLaunchKernelGGL((bwd_dh_kernel<DT_BF16, kContractWaves>), grid, block, 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_backward_dh_final(int dtype, const DhFinalArgs& a, hipStream_t st) {
+  if (a.count <= 0) return hipSuccess;
+  const dim3 grid(blocks_for(a.count / 4, 256)), block(256);
+  switch (dtype) {
+    case DT_F32: hipLaunchKernelGGL(bwd_dh_final_kernel<DT_F32>, grid, block, 0, st, a); break;
+    case DT_F16: hipLaunchKernelGGL(bwd_dh_final_kernel<DT_F16>, grid, block, 0, st, a); break;
+    case DT_BF16: hipLaunchKernelGGL(bwd_dh_final_kernel<DT_BF16>, grid, block, 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

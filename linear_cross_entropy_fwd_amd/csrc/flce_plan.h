@@ -127,11 +127,20 @@ struct GArgs {
 struct DhArgs {
   const char* G;     // [npad][cvpad]
   const char* WcT;   // [H][cvpad]
-  float* acc;        // [N][H] fp32 accumulator across chunks
+  float* acc;        // ksplit x [N][H] fp32 accumulators across chunks (split s at acc + s * acc_stride)
   char* out;         // grad_hidden (N,H)
   const float* scale;
-  int64_t N, H;
+  int64_t N, H, acc_stride;
   int cvpad, n_tok_tiles, n_h_tiles, first, last;
+  int ksplit, kpart;  // the chunk's K in ksplit parts of kpart ids (grid.y = ksplit)
+};
+
+// grad_hidden = the fixed-order sum of the ksplit accumulators, in the dtype.
+struct DhFinalArgs {
+  const float* acc;
+  char* out;
+  int64_t count, acc_stride;  // count = N * H (a multiple of 4)
+  int ksplit;
 };
 
 struct DwArgs {
@@ -162,6 +171,7 @@ hipError_t launch_backward_prep(const PrepArgs& a, hipStream_t st);
 hipError_t launch_transpose(int dtype, const TransposeArgs& a, hipStream_t st);
 hipError_t launch_backward_g(int dtype, bool bias, bool cap, const GArgs& a, hipStream_t st);
 hipError_t launch_backward_dh(int dtype, const DhArgs& a, hipStream_t st);
+hipError_t launch_backward_dh_final(int dtype, const DhFinalArgs& a, hipStream_t st);
 hipError_t launch_backward_dw(int dtype, const DwArgs& a, hipStream_t st);
 hipError_t launch_backward_db(int dtype, const DbArgs& a, hipStream_t st);
 hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t st);
