@@ -39,8 +39,17 @@ __device__ __forceinline__ int opaque_int(int x) {
   return x;
 }
 
+// tanh from its definition, tanh x = sign(x) (1 - 2 / (e^{2|x|} + 1)), with
+// the hardware exp2 and reciprocal: an absolute error of a few 1e-7 (so
+// cap * tanh is off by a few 1e-7 cap at most); e^{2|x|} = inf past
+// |x| ~ 44 gives exactly +-1, and NaN stays NaN.
+__device__ __forceinline__ float tanh_exp(float x) {
+  const float t = __builtin_amdgcn_exp2f(fabsf(x) * (2.f * LOG2E));
+  return copysignf(fmaf(-2.f, __builtin_amdgcn_rcpf(t + 1.f), 1.f), x);
+}
+
 __device__ __forceinline__ float soft_cap(float y, float cap, float inv_cap) {
-  return cap * tanhf(y * inv_cap);
+  return cap * tanh_exp(y * inv_cap);
 }
 
 // Merge online-softmax state (m2,S2,U2) into (m,S,U).  Symmetric in its two

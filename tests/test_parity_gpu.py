@@ -154,6 +154,15 @@ def test_empty_batch():
     assert gh.numel() == 0 and torch.all(gw == 0) and torch.all(gb == 0)
 
 
+@pytest.mark.parametrize("cap,scale", [(5.0, 3.0), (30.0, 1.0), (0.5, 4.0)])
+def test_softcap_f32_tight(cap, scale):
+    """fp32 at the tight tolerance through the softcap (deep into tanh's
+    saturation for the small caps), with metrics and both passes."""
+    w = W["tiny_f32"].resized(n=300, h=64, v=700, softcap=cap, logit_scale=scale)
+    run_case(w)
+    run_case(w.resized(reduction="sum"), bwd_vocab_chunk=256)
+
+
 # --------------------------------------------------------------------------- loss variants
 
 def class_weights(v, seed):
