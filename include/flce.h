@@ -108,8 +108,9 @@ typedef struct flce_problem {
    * as hidden[:, :-1, :] and labels[:, 1:] of an (S, T+1) batch are taken as
    * they are.  Zero selects the default: seq_len N, hidden_row_stride H,
    * hidden_seq_stride seq_len * hidden_row_stride, targets_stride 1,
-   * targets_seq_stride seq_len * targets_stride.  Strides are >= 0; the two
-   * hidden strides times sizeof(dtype) are multiples of 16 bytes.  Outputs
+   * targets_seq_stride seq_len * targets_stride.  Strides are >= 0 and
+   * below 2^40 elements; the two hidden strides times sizeof(dtype) are
+   * multiples of 16 bytes.  Outputs
    * indexed by token (lse, loss rows, predictions, grad_hidden) stay
    * contiguous in n.  Hidden rows that are not contiguous are gathered
    * into the workspace first (2 N H sizeof(dtype) bytes moved), and so are

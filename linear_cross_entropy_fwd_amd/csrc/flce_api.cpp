@@ -118,6 +118,10 @@ flce_status_t check_problem(const flce_problem_t* p) {
   if (p->seq_len < 0 || p->hidden_row_stride < 0 || p->hidden_seq_stride < 0 || p->targets_stride < 0 ||
       p->targets_seq_stride < 0)
     return fail(FLCE_ERR_INVALID_ARGUMENT, "seq_len and strides must be >= 0");
+  constexpr int64_t kMaxStride = int64_t(1) << 40;  // elements; keeps every offset product in range
+  if (p->hidden_row_stride >= kMaxStride || p->hidden_seq_stride >= kMaxStride ||
+      p->targets_stride >= kMaxStride || p->targets_seq_stride >= kMaxStride)
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "strides must be below 2^40 elements");
   if (p->seq_len > 0 && p->n_tokens % p->seq_len != 0)
     return fail(FLCE_ERR_INVALID_ARGUMENT, "n_tokens (%lld) must be a multiple of seq_len (%lld)",
                 (long long)p->n_tokens, (long long)p->seq_len);

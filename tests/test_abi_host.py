@@ -78,6 +78,7 @@ def base(**kw):
     (dict(hidden_seq_stride=-4), INVALID),
     (dict(targets_stride=-1), INVALID),
     (dict(seq_len=16, hidden_seq_stride=2049), INVALID),
+    (dict(targets_seq_stride=1 << 40), INVALID),
 ])
 def test_invalid_problems(kw, status):
     p = base(**kw)
