@@ -48,10 +48,6 @@ __device__ __forceinline__ float tanh_exp(float x) {
   return copysignf(fmaf(-2.f, __builtin_amdgcn_rcpf(t + 1.f), 1.f), x);
 }
 
-__device__ __forceinline__ float soft_cap(float y, float cap, float inv_cap) {
-  return cap * tanh_exp(y * inv_cap);
-}
-
 // Merge online-softmax state (m2,S2,U2) into (m,S,U).  Symmetric in its two
 // operands (fp add / mul commute), so the merge order of a pair never
 // changes the bits.  U = sum e^{z-m}(z-m) rescales as e^{m-M}(U + (m-M) S).
@@ -205,9 +201,8 @@ __global__ __launch_bounds__(W * 64) void fwd_tiles_kernel(FwdArgs a) {
         for (int e = 0; e < 4; ++e) {
           float y = acc[i][j][e];
           if (BIAS) y = y + bv[i][e];
-          y = a.s * y;
-          if (CAP) y = soft_cap(y, a.cap, a.inv_cap);
-          z[i][e] = y;
+          // softcap: z = cap tanh(s y / cap), the two scales as one product
+          z[i][e] = CAP ? a.cap * tanh_exp(y * (a.s * a.inv_cap)) : a.s * y;
         }
       if (ragged) {  // a branch only the last tile takes, not a select per element
 #pragma unroll
@@ -859,13 +854,25 @@ __global__ __launch_bounds__(W * 64) void bwd_g_kernel(GArgs a) {
           if (16 * i + e == tl[j]) yr = BIAS ? acc[i][j][e] + bv[i][e] : acc[i][j][e];
       float cf = 1.f;
       if (CAP) {
-        const float qc = soft_cap(a.s * yr, a.cap, a.inv_cap) * a.inv_cap;
+        const float qc = tanh_exp(yr * (a.s * a.inv_cap));  // z / cap
         cf = fmaf(-qc, qc, 1.f);
       }
       if (tl[j] >= 0) onehot[j] = cf * (coef[j] * a.keep);
     }
   }
+  // G = coef (pscale exp2(z log2e - lse log2e) - eps/V) [* (1 - (z/cap)^2)]:
+  // FMAs around the exp, the per-column factors folded ahead (a dead column
+  // has lse = +inf and coef = 0: exp2(-inf) = 0 and both factors 0).
+  float ll[WJ], pc[WJ], ec[WJ];
+#pragma unroll
+  for (int j = 0; j < WJ; ++j) {
+    ll[j] = lse[j] * LOG2E;
+    pc[j] = pscale[j] * coef[j];
+    ec[j] = a.eps_v * coef[j];
+  }
   if constexpr (CAP) {
+    // z = cap th with th = tanh(s y / cap); dz/dy = s (1 - th^2)
+    const float sic = a.s * a.inv_cap, cl = a.cap * LOG2E;
 #pragma unroll
     for (int i = 0; i < WI; ++i)
 #pragma unroll
@@ -874,24 +881,11 @@ __global__ __launch_bounds__(W * 64) void bwd_g_kernel(GArgs a) {
         for (int j = 0; j < WJ; ++j) {
           float y = acc[i][j][e];
           if (BIAS) y = y + bv[i][e];
-          y = soft_cap(a.s * y, a.cap, a.inv_cap);
-          float g = fmaf(fast_exp2((y - lse[j]) * LOG2E), pscale[j], -a.eps_v);
-          const float qc = y * a.inv_cap;
-          g = g * fmaf(-qc, qc, 1.f);
-          acc[i][j][e] = g * coef[j];
+          const float th = tanh_exp(y * sic);
+          acc[i][j][e] = fmaf(fast_exp2(fmaf(th, cl, -ll[j])), pc[j], -ec[j]) * fmaf(-th, th, 1.f);
         }
   } else {
-    // G = coef (pscale exp2(y s log2e - lse log2e) - eps/V): two FMAs around
-    // the exp, the per-column factors folded ahead (a dead column has
-    // lse = +inf and coef = 0: exp2(-inf) = 0 and both factors 0).
     const float sl = a.s * LOG2E;
-    float ll[WJ], pc[WJ], ec[WJ];
-#pragma unroll
-    for (int j = 0; j < WJ; ++j) {
-      ll[j] = lse[j] * LOG2E;
-      pc[j] = pscale[j] * coef[j];
-      ec[j] = a.eps_v * coef[j];
-    }
 #pragma unroll
     for (int i = 0; i < WI; ++i)
 #pragma unroll
