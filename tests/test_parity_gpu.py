@@ -72,6 +72,16 @@ def test_headvocab_shape_multichunk_bf16():
     run_case(W["headvocab_bf16"].resized(n=512, h=512, v=8200), bwd_vocab_chunk=2048)
 
 
+@pytest.mark.parametrize("n,h,split", [(2304, 2048, 2), (4352, 2048, 1), (1030, 512, 4)])
+def test_grad_hidden_k_split_classes(n, h, split):
+    """grad_hidden's grid (token tiles x hidden tiles) picks how many
+    workgroups share each tile's K: 72 tiles -> 2, 136 -> 1, 15 -> 4; each
+    class against the oracle over several chunks."""
+    tiles = -(-n // 256) * -(-h // 256)
+    assert split == (4 if tiles <= 64 else 2 if tiles <= 128 else 1)
+    run_case(W["midvocab_bf16"].resized(n=n, h=h, v=1300), bwd_vocab_chunk=512)
+
+
 def test_transforms_shape_bias_scale_cap_sum_metrics():
     run_case(W["transforms_bf16"].resized(n=384, h=384, v=5000), bwd_vocab_chunk=1024)
 
