@@ -71,3 +71,50 @@ def test_graph_replays_match_eager():
         want = eager2 if rep % 2 else eager1
         for got, ref in zip(outs, want):
             assert torch.equal(got, ref), f"replay {rep}"
+
+
+def test_graph_one_call_with_shifted_views():
+    """flce_forward_backward on hidden[:, :-1] / labels[:, 1:] views (the
+    gather kernels and the split grad_hidden sum in the graph too)."""
+    import linear_cross_entropy_fwd_amd as flce
+    w = W["midvocab_bf16"].resized(n=3 * 301, h=256, v=2600)
+    log_case(f"graph capture, one call on shifted views {w.name}")
+    d1, d2 = fi.generate(w), fi.generate(w.resized(seed=w.seed + 100))
+    hid = d1["hidden"].cuda().view(3, 301, 256)
+    lab = d1["targets"].cuda().view(3, 301)
+    wt = d1["weight"].cuda()
+    hv, tv = hid[:, :-1], lab[:, 1:]
+    p = flce.problem_for(hv, wt, None, layout=flce.token_layout(hv, tv))
+    ws = torch.empty(flce._abi.flce_forward_backward_workspace_size(p), dtype=torch.uint8, device="cuda")
+
+    def run():
+        loss, lse, _, (gh, gw, _) = flce.flce_forward_backward(hv, wt, tv, None, want_lse=True, workspace=ws,
+                                                               bwd_vocab_chunk=1024)
+        return [loss, lse, gh, gw]
+
+    def load(d):
+        hid.copy_(d["hidden"].cuda().view(3, 301, 256))
+        wt.copy_(d["weight"].cuda())
+
+    eager1 = [x.clone() for x in run()]
+    load(d2)
+    eager2 = [x.clone() for x in run()]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = run()
+    for rep in range(4):
+        x = torch.randn(256, 256, device="cuda")
+        (x @ x).sum().item()
+        load(d2 if rep % 2 else d1)
+        graph.replay()
+        torch.cuda.synchronize()
+        want = eager2 if rep % 2 else eager1
+        for got, ref in zip(outs, want):
+            assert torch.equal(got, ref), f"replay {rep}"
