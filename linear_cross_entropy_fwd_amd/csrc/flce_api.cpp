@@ -225,7 +225,7 @@ FwdLayout fwd_layout(const flce_problem_t& p) {
 constexpr int64_t kMaxPanelPitch = int64_t(1) << 24;  // bytes
 
 struct BwdLayout {
-  int64_t chunk, npad, cvpad_max;
+  int64_t chunk, last_chunk, npad, cvpad_max;  // chunks of `chunk` ids, the last of last_chunk
   int n_chunks, n_tok_tiles, n_h_tiles, dh_split;
   TokLayout tok;
   size_t off_scale, off_ht, off_wct, off_g, off_gt, off_dh, off_db, off_hrows, off_tgt, total;
@@ -242,8 +242,13 @@ BwdLayout bwd_layout(const flce_problem_t& p) {
   }
   L.chunk = std::min<int64_t>(L.chunk, round_up(V, kTile));
   L.n_chunks = (int)cdiv(V, L.chunk);
+  // A default plan's last chunk of under a quarter of a chunk joins the one
+  // before it (three launches and a grad_hidden read-modify-write saved).
+  if (p.bwd_vocab_chunk <= 0 && L.n_chunks > 1 && 4 * (V - (int64_t)(L.n_chunks - 1) * L.chunk) < L.chunk)
+    --L.n_chunks;
+  L.last_chunk = V - (int64_t)(L.n_chunks - 1) * L.chunk;
   L.npad = round_up(std::max<int64_t>(N, 1), 64);
-  L.cvpad_max = round_up(std::min(L.chunk, V), 64);
+  L.cvpad_max = round_up(std::max(std::min(L.chunk, V), L.last_chunk), 64);
   L.n_tok_tiles = (int)cdiv(N, kTile);
   L.n_h_tiles = (int)cdiv(H, kTile);
   size_t off = 0;
@@ -481,7 +486,7 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
   }
   for (int c = 0; c < L.n_chunks; ++c) {
     const int64_t c0 = (int64_t)c * L.chunk;
-    const int cv = (int)std::min<int64_t>(L.chunk, V - c0);
+    const int cv = (int)(c == L.n_chunks - 1 ? L.last_chunk : L.chunk);
     const int cvpad = (int)round_up(cv, 64);
     // 16-bit types with at least 4 token tiles: the recompute kernel writes
     // W_c^T as a side job; otherwise the transpose kernel does.
