@@ -24,7 +24,8 @@
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers, row-major and dense:
  *     hidden (N,H), weight (V,H), bias (V), targets (N) int64, grad_hidden
- *     (N,H), grad_weight (V,H), grad_bias (V).  hidden, weight, grad_hidden,
+ *     (N,H), grad_weight (V,H), grad_bias (V); hidden and targets may
+ *     instead follow the strided token layout of flce_problem_t.  hidden, weight, grad_hidden,
  *     grad_weight must be 16-byte aligned.  hidden/weight/bias and the
  *     gradient outputs share the problem's dtype; loss, lse, metrics and
  *     grad_loss are fp32.
@@ -110,9 +111,8 @@ typedef struct flce_problem {
    * hidden_seq_stride seq_len * hidden_row_stride, targets_stride 1,
    * targets_seq_stride seq_len * targets_stride.  Strides are >= 0 and
    * below 2^40 elements; the two hidden strides times sizeof(dtype) are
-   * multiples of 16 bytes.  Outputs
-   * indexed by token (lse, loss rows, predictions, grad_hidden) stay
-   * contiguous in n.  Hidden rows that are not contiguous are gathered
+   * multiples of 16 bytes.  Outputs indexed by token (lse, loss rows,
+   * predictions, grad_hidden) stay contiguous in n.  Hidden rows that are not contiguous are gathered
    * into the workspace first (2 N H sizeof(dtype) bytes moved), and so are
    * targets that are not (16 N bytes). */
   int64_t seq_len;
