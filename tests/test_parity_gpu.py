@@ -274,9 +274,11 @@ def test_fp32_grad_weight_output_f32_inputs_and_empty():
 
 # --------------------------------------------------------------------------- one call
 
-@pytest.mark.parametrize("wname,red,lse_out", [("transforms_bf16", "sum", False), ("midvocab_bf16", "none", True),
-                                               ("tiny_f32", "mean", False)])
-def test_forward_backward_in_one_call(wname, red, lse_out):
+@pytest.mark.parametrize("wname,red,lse_out,g32", [("transforms_bf16", "sum", False, False),
+                                                   ("transforms_bf16", "mean", False, True),
+                                                   ("midvocab_bf16", "none", True, False),
+                                                   ("tiny_f32", "mean", False, False)])
+def test_forward_backward_in_one_call(wname, red, lse_out, g32):
     """flce_forward_backward gives the two calls' results bit for bit, and
     the oracle's within tolerance."""
     import linear_cross_entropy_fwd_amd as flce
@@ -289,9 +291,12 @@ def test_forward_backward_in_one_call(wname, red, lse_out):
     go = torch.linspace(0.25, 2.0, w.n, device="cuda") if red == "none" else torch.tensor([0.75], device="cuda")
     var = dict(label_smoothing=0.1, z_loss=1e-4) if red != "none" else {}
     loss, lse, metrics, grads = flce.flce_forward_backward(*args, go, return_metrics=True, want_lse=lse_out,
-                                                           bwd_vocab_chunk=1024, **var, **kw)
+                                                           bwd_vocab_chunk=1024, grad_weight_fp32=g32,
+                                                           **var, **kw)
     loss2, lse2, metrics2 = flce.flce_forward(*args, return_metrics=True, **var, **kw)
-    grads2 = flce.flce_backward(*args, lse2, go, bwd_vocab_chunk=1024, **var, **kw)
+    grads2 = flce.flce_backward(*args, lse2, go, bwd_vocab_chunk=1024, grad_weight_fp32=g32, **var, **kw)
+    if g32:
+        assert grads[1].dtype == torch.float32 and grads[2].dtype == torch.float32
     torch.cuda.synchronize()
     assert torch.equal(loss, loss2) and torch.equal(metrics, metrics2)
     assert (lse is None) != lse_out and (lse is None or torch.equal(lse, lse2))
