@@ -545,7 +545,7 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
       da.acc_stride = N * H;
       if ((e = flce::launch_backward_dh(p->dtype, da, st)) != hipSuccess) return hip_fail(e, "grad_hidden kernel");
       if (da.last && L.dh_split > 1) {
-        flce::DhFinalArgs fa{dh, reinterpret_cast<char*>(grad_hidden), N * H, N * H, L.dh_split};
+        flce::DhFinalArgs fa{dh, scale, reinterpret_cast<char*>(grad_hidden), N * H, N * H, L.dh_split};
         if ((e = flce::launch_backward_dh_final(p->dtype, fa, st)) != hipSuccess)
           return hip_fail(e, "grad_hidden sum kernel");
       }

@@ -416,18 +416,23 @@ __device__ __forceinline__ void gemm_prefetch(CopyPlan<W>& cp, const Panel& A, c
 // from a gemm_prefetch of the same panels.  Uses the stage buffers; returns
 // after a barrier with no copy in flight, so the caller may reuse them (e.g.
 // g_stage0) right away.
-template <int D, int W, class Side>
+// ZERO = false: acc arrives holding values to add to (loaded by the caller
+// before gemm_prefetch, so that those loads complete in order ahead of the
+// stage copies and the first wait below covers them).
+template <int D, int W, class Side, bool ZERO = true>
 __device__ __forceinline__ void gemm_run(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], const CopyPlan<W>& cp,
                                          const Panel& A, Side& side) {
   static_assert(NSTAGES == 2, "the loops below alternate two buffers");
   constexpr int H = Gemm<W>::NCOP / 2;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  if constexpr (ZERO) {
 #pragma unroll
-  for (int i = 0; i < Gemm<W>::WI; ++i)
+    for (int i = 0; i < Gemm<W>::WI; ++i)
 #pragma unroll
-    for (int j = 0; j < Gemm<W>::WJ; ++j)
+      for (int j = 0; j < Gemm<W>::WJ; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
+        for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
+  }
   const int nk = (int)((A.kbytes + ROWB - 1) / ROWB);
   const bool ragged = (A.kbytes % ROWB) != 0;
   const uint32_t wave_lds = (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024u;

@@ -1025,20 +1025,35 @@ __global__ __launch_bounds__(W * 64) void bwd_dh_kernel(DhArgs a) {
   const int64_t kb = (int64_t)a.cvpad * EB;
   // split blockIdx.y takes ids [k0, k0 + kn) of the chunk into its own accumulator
   const int k0 = (int)blockIdx.y * a.kpart, kn = min(a.kpart, a.cvpad - k0);
+  // The chunks' contributions accumulate unscaled; the running sum is read
+  // into the accumulators before the K loop (its loads overlap the first
+  // stages' copies instead of following the last MFMA), and the scale is
+  // applied once, when grad_hidden is written.
+  float* accbuf = a.acc + (int64_t)blockIdx.y * a.acc_stride;
   f32x4_t acc[WI][WJ];
-  if (kn > 0) {
+#pragma unroll
+  for (int j = 0; j < WJ; ++j) {
+    const int64_t n = n0 + wn * 16 * WJ + 16 * j + c16;
+#pragma unroll
+    for (int i = 0; i < WI; ++i) {
+      const int64_t h = h0 + wm * 16 * WI + 16 * i + 4 * q;  // H % 4 == 0: all four in range
+      acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (!a.first && n < a.N && h < a.H) {
+        const float4 o = *reinterpret_cast<const float4*>(accbuf + n * a.H + h);
+        acc[i][j] = f32x4_t{o.x, o.y, o.z, o.w};
+      }
+    }
+  }
+  if (kn > 0) {  // a split past a short last chunk adds nothing
     Panel A{a.WcT + h0 * kb + (int64_t)k0 * EB, kb, (int)min<int64_t>(TILE, a.H - h0), (int64_t)kn * EB};
     Panel B{a.G + n0 * kb + (int64_t)k0 * EB, kb, (int)min<int64_t>(TILE, a.N - n0), (int64_t)kn * EB};
-    gemm_nt_tile<D, W>(acc, A, B);
-  } else {  // a split past a short last chunk adds nothing
-#pragma unroll
-    for (int i = 0; i < WI; ++i)
-#pragma unroll
-      for (int j = 0; j < WJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    CopyPlan<W> cp;
+    gemm_prefetch<W>(cp, A, B);
+    NoSide none;
+    gemm_run<D, W, NoSide, false>(acc, cp, A, none);
   }
-  const float scale = a.scale[0];
-  float* accbuf = a.acc + (int64_t)blockIdx.y * a.acc_stride;
   const bool finish = a.last && a.ksplit == 1;  // else a separate pass sums the splits
+  const float scale = a.scale[0];
   T* out = reinterpret_cast<T*>(a.out);
 #pragma unroll
   for (int j = 0; j < WJ; ++j) {
@@ -1046,26 +1061,20 @@ __global__ __launch_bounds__(W * 64) void bwd_dh_kernel(DhArgs a) {
     if (n >= a.N) continue;
 #pragma unroll
     for (int i = 0; i < WI; ++i) {
-      const int64_t h = h0 + wm * 16 * WI + 16 * i + 4 * q;  // H % 4 == 0: all four in range
+      const int64_t h = h0 + wm * 16 * WI + 16 * i + 4 * q;
       if (h >= a.H) continue;
       const int64_t idx = n * a.H + h;
-      float v0 = acc[i][j][0] * scale, v1 = acc[i][j][1] * scale;
-      float v2 = acc[i][j][2] * scale, v3 = acc[i][j][3] * scale;
-      if (!a.first) {
-        const float4 o = *reinterpret_cast<const float4*>(accbuf + idx);
-        v0 = o.x + v0;
-        v1 = o.y + v1;
-        v2 = o.z + v2;
-        v3 = o.w + v3;
-      }
-      if (finish) store4<D>(out + idx, v0, v1, v2, v3);
-      else *reinterpret_cast<float4*>(accbuf + idx) = make_float4(v0, v1, v2, v3);
+      if (finish)
+        store4<D>(out + idx, acc[i][j][0] * scale, acc[i][j][1] * scale, acc[i][j][2] * scale,
+                  acc[i][j][3] * scale);
+      else
+        *reinterpret_cast<float4*>(accbuf + idx) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
     }
   }
 }
 
-// grad_hidden = sum over s = 0, 1, ... of the split accumulators, in that
-// order, four elements per thread.
+// grad_hidden = scale * (sum over s = 0, 1, ... of the split accumulators,
+// in that order), four elements per thread.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dh_final_kernel(DhFinalArgs a) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
@@ -1078,7 +1087,8 @@ __global__ __launch_bounds__(256) void bwd_dh_final_kernel(DhFinalArgs a) {
     v.z = v.z + o.z;
     v.w = v.w + o.w;
   }
-  store4<D>(reinterpret_cast<typename Elem<D>::T*>(a.out) + i, v.x, v.y, v.z, v.w);
+  const float sc = a.scale[0];
+  store4<D>(reinterpret_cast<typename Elem<D>::T*>(a.out) + i, v.x * sc, v.y * sc, v.z * sc, v.w * sc);
 }
 
 // grad_weight[v][h] = scale * sum_n G[n][v] H[n][h] for one vocabulary chunk:

@@ -127,7 +127,7 @@ struct GArgs {
 struct DhArgs {
   const char* G;     // [npad][cvpad]
   const char* WcT;   // [H][cvpad]
-  float* acc;        // ksplit x [N][H] fp32 accumulators across chunks (split s at acc + s * acc_stride)
+  float* acc;        // ksplit x [N][H] fp32 unscaled running sums across chunks (split s at acc + s * acc_stride)
   char* out;         // grad_hidden (N,H)
   const float* scale;
   int64_t N, H, acc_stride;
@@ -138,6 +138,7 @@ struct DhArgs {
 // grad_hidden = the fixed-order sum of the ksplit accumulators, in the dtype.
 struct DhFinalArgs {
   const float* acc;
+  const float* scale;
   char* out;
   int64_t count, acc_stride;  // count = N * H (a multiple of 4)
   int ksplit;
