@@ -226,7 +226,8 @@ constexpr int64_t kMaxPanelPitch = int64_t(1) << 24;  // bytes
 
 struct BwdLayout {
   int64_t chunk, last_chunk, npad, cvpad_max;  // chunks of `chunk` ids, the last of last_chunk
-  int n_chunks, n_tok_tiles, n_h_tiles, dh_split;
+  int64_t cvpad_reg, gld;  // a full chunk's padded width; row pitch of the G and W_c^T buffers
+  int n_chunks, n_tok_tiles, n_h_tiles, dh_split, dh_pair;
   TokLayout tok;
   size_t off_scale, off_ht, off_wct, off_g, off_gt, off_dh, off_db, off_hrows, off_tgt, total;
 };
@@ -251,6 +252,16 @@ BwdLayout bwd_layout(const flce_problem_t& p) {
   L.cvpad_max = round_up(std::max(std::min(L.chunk, V), L.last_chunk), 64);
   L.n_tok_tiles = (int)cdiv(N, kTile);
   L.n_h_tiles = (int)cdiv(H, kTile);
+  // With many chunks grad_hidden runs once per pair of them: the pair's G
+  // and W_c^T sit side by side in K (a full chunk, then the next), so the
+  // fp32 running sum is read and written half as often, for one more chunk
+  // of G and W_c^T in the workspace.  Measured: 0.9-2.2 % off the backward
+  // with 32 chunks (N = 16384, H = 2048, V = 262144), within noise with the
+  // head shape's 11, so it is kept to 16 chunks or more.  (It depends on V
+  // and H only, like the chunks.)
+  L.dh_pair = L.n_chunks >= 16 ? 2 : 1;
+  L.cvpad_reg = round_up(std::min(L.chunk, V), 64);
+  L.gld = L.dh_pair == 2 ? L.cvpad_reg + L.cvpad_max : L.cvpad_max;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -259,8 +270,8 @@ BwdLayout bwd_layout(const flce_problem_t& p) {
   };
   L.off_scale = take(16);
   L.off_ht = take((size_t)H * L.npad * eb);
-  L.off_wct = take((size_t)H * L.cvpad_max * eb);
-  L.off_g = take((size_t)L.npad * L.cvpad_max * eb);
+  L.off_wct = take((size_t)H * L.gld * eb);
+  L.off_g = take((size_t)L.npad * L.gld * eb);
   L.off_gt = take((size_t)L.cvpad_max * L.npad * eb);
   // grad_hidden's grid is token tiles x hidden tiles; when that is a small
   // part of the CUs, the chunk's K is split over 2 or 4 workgroups per tile,
@@ -269,7 +280,7 @@ BwdLayout bwd_layout(const flce_problem_t& p) {
   // whose grids fall in the same class give bit-identical rows.)
   const int64_t dh_tiles = (int64_t)L.n_tok_tiles * L.n_h_tiles;
   L.dh_split = dh_tiles <= kCUs / 4 ? 4 : dh_tiles <= kCUs / 2 ? 2 : 1;
-  L.off_dh = take(L.n_chunks > 1 || L.dh_split > 1 ? (size_t)L.dh_split * N * H * 4 : 0);
+  L.off_dh = take(L.n_chunks > L.dh_pair || L.dh_split > 1 ? (size_t)L.dh_split * N * H * 4 : 0);
   L.off_db = take(p.has_bias ? (size_t)flce::kBiasParts * L.n_tok_tiles * V * 4 : 0);
   L.tok = tok_layout(p);
   L.off_hrows = take(L.tok.h_gather ? (size_t)N * H * eb : 0);
@@ -429,7 +440,7 @@ static flce_status_t check_backward_args(const flce_problem_t* p, const void* hi
   const BwdLayout L = bwd_layout(*p);
   // The GEMM tiles read their operand panels through 32-bit buffer offsets:
   // 256 row pitches (tokens or chunk ids times the element size) stay below 4 GiB.
-  if (L.npad * eb >= kMaxPanelPitch || L.cvpad_max * eb >= kMaxPanelPitch)
+  if (L.npad * eb >= kMaxPanelPitch || L.gld * eb >= kMaxPanelPitch)
     return fail(FLCE_ERR_UNSUPPORTED, "backward needs n_tokens and the vocabulary chunk times sizeof(dtype) "
                 "below 16 MiB (n_tokens=%lld, chunk=%lld)", (long long)N, (long long)L.chunk);
   return FLCE_OK;
@@ -481,18 +492,23 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
   float* dh = reinterpret_cast<float*>(ws + L.off_dh);
   float* db = reinterpret_cast<float*>(ws + L.off_db);
   if (want_dw) {
-    flce::TransposeArgs ta{in.hidden, ht, N, H, H, L.npad};
+    flce::TransposeArgs ta{in.hidden, ht, N, H, H, L.npad, L.npad};
     if ((e = flce::launch_transpose(p->dtype, ta, st)) != hipSuccess) return hip_fail(e, "transpose kernel");
   }
   for (int c = 0; c < L.n_chunks; ++c) {
     const int64_t c0 = (int64_t)c * L.chunk;
     const int cv = (int)(c == L.n_chunks - 1 ? L.last_chunk : L.chunk);
     const int cvpad = (int)round_up(cv, 64);
+    // slot 0 of a pair is a full chunk at column 0 of G and W_c^T; slot 1 follows it
+    const int slot = c % L.dh_pair;
+    const int64_t col = slot == 0 ? 0 : L.cvpad_reg;
+    char* g_c = g + col * eb;
+    char* wct_c = wct + col * eb;
     // 16-bit types with at least 4 token tiles: the recompute kernel writes
     // W_c^T as a side job; otherwise the transpose kernel does.
     const bool fused_wct = want_dh && eb == 2 && L.n_tok_tiles >= 4;
     if (want_dh && !fused_wct) {
-      flce::TransposeArgs ta{reinterpret_cast<const char*>(weight) + c0 * H * eb, wct, cv, H, H, cvpad};
+      flce::TransposeArgs ta{reinterpret_cast<const char*>(weight) + c0 * H * eb, wct_c, cv, H, H, cvpad, L.gld};
       if ((e = flce::launch_transpose(p->dtype, ta, st)) != hipSuccess) return hip_fail(e, "transpose kernel");
     }
     flce::GArgs ga{};
@@ -502,9 +518,11 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
     ga.targets = targets;
     ga.lse = lse;
     ga.grad_rows = p->reduction == FLCE_NONE ? grad_loss : nullptr;
-    ga.G = want_dh ? g : nullptr;
+    ga.G = want_dh ? g_c : nullptr;
     ga.GT = want_dw ? gt : nullptr;
-    ga.WcT = fused_wct ? wct : nullptr;
+    ga.WcT = fused_wct ? wct_c : nullptr;
+    ga.g_ld = (int)L.gld;
+    ga.wct_ld = (int)L.gld;
     ga.dbpart = want_db ? db : nullptr;
     ga.N = N;
     ga.H = H;
@@ -526,30 +544,6 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
     ga.zl2 = 2.f * p->z_loss;
     if ((e = flce::launch_backward_g(p->dtype, p->has_bias != 0, p->softcap > 0.f, ga, st)) != hipSuccess)
       return hip_fail(e, "backward G kernel");
-    if (want_dh) {
-      flce::DhArgs da{};
-      da.G = g;
-      da.WcT = wct;
-      da.acc = dh;
-      da.out = reinterpret_cast<char*>(grad_hidden);
-      da.scale = scale;
-      da.N = N;
-      da.H = H;
-      da.cvpad = cvpad;
-      da.n_tok_tiles = L.n_tok_tiles;
-      da.n_h_tiles = L.n_h_tiles;
-      da.first = c == 0;
-      da.last = c == L.n_chunks - 1;
-      da.ksplit = L.dh_split;
-      da.kpart = (int)round_up(cdiv(cvpad, L.dh_split), 64);
-      da.acc_stride = N * H;
-      if ((e = flce::launch_backward_dh(p->dtype, da, st)) != hipSuccess) return hip_fail(e, "grad_hidden kernel");
-      if (da.last && L.dh_split > 1) {
-        flce::DhFinalArgs fa{dh, scale, reinterpret_cast<char*>(grad_hidden), N * H, N * H, L.dh_split};
-        if ((e = flce::launch_backward_dh_final(p->dtype, fa, st)) != hipSuccess)
-          return hip_fail(e, "grad_hidden sum kernel");
-      }
-    }
     if (want_dw) {
       flce::DwArgs wa{};
       wa.GT = gt;
@@ -563,6 +557,35 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
       wa.n_voc_tiles = (int)cdiv(cv, kTile);
       wa.n_h_tiles = L.n_h_tiles;
       if ((e = flce::launch_backward_dw(p->dtype, wa, st)) != hipSuccess) return hip_fail(e, "grad_weight kernel");
+    }
+    // grad_hidden once the pair is complete (or at the last chunk); after
+    // grad_weight, which needs this chunk's G^T before the next chunk's
+    // recompute overwrites it
+    if (want_dh && (slot == L.dh_pair - 1 || c == L.n_chunks - 1)) {
+      const int pair = c / L.dh_pair;
+      flce::DhArgs da{};
+      da.G = g;
+      da.WcT = wct;
+      da.acc = dh;
+      da.out = reinterpret_cast<char*>(grad_hidden);
+      da.scale = scale;
+      da.N = N;
+      da.H = H;
+      da.ld = (int)L.gld;
+      da.kdim = (int)(col + cvpad);
+      da.n_tok_tiles = L.n_tok_tiles;
+      da.n_h_tiles = L.n_h_tiles;
+      da.first = pair == 0;
+      da.last = c == L.n_chunks - 1;
+      da.ksplit = L.dh_split;
+      da.kpart = (int)round_up(cdiv(da.kdim, L.dh_split), 64);
+      da.acc_stride = N * H;
+      if ((e = flce::launch_backward_dh(p->dtype, da, st)) != hipSuccess) return hip_fail(e, "grad_hidden kernel");
+      if (da.last && L.dh_split > 1) {
+        flce::DhFinalArgs fa{dh, scale, reinterpret_cast<char*>(grad_hidden), N * H, N * H, L.dh_split};
+        if ((e = flce::launch_backward_dh_final(p->dtype, fa, st)) != hipSuccess)
+          return hip_fail(e, "grad_hidden sum kernel");
+      }
     }
   }
   if (want_db) {

@@ -502,7 +502,7 @@ __global__ __launch_bounds__(1024) void bwd_prep_kernel(PrepArgs a) {
   }
 }
 
-// dst[c][r] = src[r][c] for r < rows, 0 for rows <= r < rpad.  A workgroup
+// dst[c][r] (row pitch dst_ld) = src[r][c] for r < rows, 0 for rows <= r < rpad.  A workgroup
 // moves a 64-row x 256-byte tile: 16-byte loads along src rows, through LDS,
 // 16-byte stores along dst rows.  Needs cols*EB and src_ld*EB multiples of 16
 // (hidden*bytes % 16 == 0 is checked at the boundary) and rpad % 64 == 0.
@@ -535,7 +535,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
     alignas(16) U e[E];
 #pragma unroll
     for (int k = 0; k < E; ++k) e[k] = tile[(sg * E + k) * PITCH + cc];
-    *reinterpret_cast<uint4*>(dst + c * a.rpad + r) = *reinterpret_cast<const uint4*>(e);
+    *reinterpret_cast<uint4*>(dst + c * a.dst_ld + r) = *reinterpret_cast<const uint4*>(e);
   }
 }
 
@@ -622,7 +622,7 @@ __device__ __forceinline__ void tile16_store_t(uint16_t* dst, int64_t ld, int ro
 // Side job of the recompute kernel (16-bit types): while stage kt of the
 // weight tile (256 vocabulary rows x 64 hidden columns) sits in LDS, one of
 // the workgroups that share the vocabulary tile also writes it transposed
-// into W_c^T[h][vl] (row pitch cvpad), so grad_hidden needs no separate
+// into W_c^T[h][vl] (row pitch ld), so grad_hidden needs no separate
 // transpose of the chunk.  Token tile tt takes the stages kt = tt mod
 // n_tok_tiles (the host asks for this only with at least 4 token tiles).
 //
@@ -647,7 +647,7 @@ __shared__ __attribute__((aligned(1024))) char g_wct_tile[64 * 512];
 struct WcTSide {
   uint16_t* wct;
   int64_t H;
-  int cvpad, vl0, ntt;
+  int cvpad, ld, vl0, ntt;  // columns of this chunk, row pitch of W_c^T
   uint32_t wave;  // wave-uniform
   int ks;         // next stage of this workgroup
   uint64_t m;     // this stage: exec if selected, else 0
@@ -717,12 +717,12 @@ struct WcTSide {
     const int hrem = (int)min<int64_t>(64, H - (int64_t)kt * (ROWB / 2));
     const int vrem = cvpad - vl0;
     const uint32_t tb = lds_addr(g_wct_tile);
-    const char* sb = uniform_ptr(reinterpret_cast<const char*>(wct + (int64_t)kt * (ROWB / 2) * cvpad + vl0));
+    const char* sb = uniform_ptr(reinterpret_cast<const char*>(wct + (int64_t)kt * (ROWB / 2) * ld + vl0));
     uint64_t save, rows;
     uint4 d;
     uint32_t t0, t1, t2, t3;
     // row h = 8 w + 2 J + L / 32, chunk c = L & 31: T at tb + 512 h + 16 (c ^ (h & 31)),
-    // W_c^T at sb + 2 cvpad h + 16 c
+    // W_c^T at sb + 2 ld h + 16 c
 #define FLCE_WCT_ROW(J)                                                   \
   "s_mov_b64 exec, %[rw]\n\t"                                             \
   "v_add3_u32 %[t0], %[h8], " #J "*2, %[t2]\n\t"                          \
@@ -759,7 +759,7 @@ struct WcTSide {
         : [sv] "=&s"(save), [rw] "=&s"(rows), [d] "=&v"(d), [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2),
           [t3] "=&v"(t3)
         : [m] "s"(m), [hr] "s"(hrem), [vr] "s"(vrem), [tb] "s"(tb), [sb] "s"(sb), [h8] "s"(8u * wave),
-          [cp2] "s"(2 * cvpad)
+          [cp2] "s"(2 * ld)
         : "memory", "vcc");
 #undef FLCE_WCT_ROW
   }
@@ -789,7 +789,7 @@ __global__ __launch_bounds__(W * 64) void bwd_g_kernel(GArgs a) {
   f32x4_t acc[WI][WJ];
   if constexpr (EB == 2) {
     // no W_c^T wanted: a first stage past every stage selects none
-    WcTSide side{reinterpret_cast<uint16_t*>(a.WcT), a.H, a.cvpad, vl0, a.n_tok_tiles,
+    WcTSide side{reinterpret_cast<uint16_t*>(a.WcT), a.H, a.cvpad, a.wct_ld, vl0, a.n_tok_tiles,
                  (uint32_t)__builtin_amdgcn_readfirstlane(t >> 6), a.WcT != nullptr ? tt : (1 << 30), 0ull};
     gemm_nt_tile<D, W>(acc, A, B, side);
   } else {
@@ -932,11 +932,11 @@ __global__ __launch_bounds__(W * 64) void bwd_g_kernel(GArgs a) {
                          acc[i][j][2], acc[i][j][3]);
       __syncthreads();
       const int rows = (int)min<int64_t>(TILE, a.npad - n0), cols = min(TILE, a.cvpad - vl0);
-      if (a.G) tile16_store<W * 64>(reinterpret_cast<uint16_t*>(a.G) + n0 * a.cvpad + vl0, a.cvpad, rows, cols, t);
+      if (a.G) tile16_store<W * 64>(reinterpret_cast<uint16_t*>(a.G) + n0 * a.g_ld + vl0, a.g_ld, rows, cols, t);
       if (a.GT) tile16_store_t(reinterpret_cast<uint16_t*>(a.GT) + (int64_t)vl0 * a.npad + n0, a.npad, rows, cols, t);
     }
   }
-  // fp32: G[n][vl] (row pitch cvpad) and G^T[vl][n] (row pitch npad) directly.
+  // fp32: G[n][vl] (row pitch g_ld) and G^T[vl][n] (row pitch npad) directly.
   if constexpr (EB == 4) {
     if (a.G) {
       float* G = reinterpret_cast<float*>(a.G);
@@ -948,7 +948,7 @@ __global__ __launch_bounds__(W * 64) void bwd_g_kernel(GArgs a) {
         for (int i = 0; i < WI; ++i) {
           const int vl = vlq + 16 * i;
           if (vl < a.cvpad)
-            *reinterpret_cast<float4*>(G + n * a.cvpad + vl) =
+            *reinterpret_cast<float4*>(G + n * a.g_ld + vl) =
                 make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
         }
       }
@@ -1022,9 +1022,9 @@ __global__ __launch_bounds__(W * 64) void bwd_dh_kernel(DhArgs a) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = Gemm<W>::wm(wave), wn = Gemm<W>::wn(wave), c16 = lane & 15, q = lane >> 4;
   const int64_t n0 = (int64_t)tt * TILE, h0 = (int64_t)ht * TILE;
-  const int64_t kb = (int64_t)a.cvpad * EB;
+  const int64_t kb = (int64_t)a.ld * EB;
   // split blockIdx.y takes ids [k0, k0 + kn) of the chunk into its own accumulator
-  const int k0 = (int)blockIdx.y * a.kpart, kn = min(a.kpart, a.cvpad - k0);
+  const int k0 = (int)blockIdx.y * a.kpart, kn = min(a.kpart, a.kdim - k0);
   // The chunks' contributions accumulate unscaled; the running sum is read
   // into the accumulators before the K loop (its loads overlap the first
   // stages' copies instead of following the last MFMA), and the scale is

@@ -87,8 +87,8 @@ struct PrepArgs {
 
 struct TransposeArgs {
   const char* src;   // rows x cols, leading dim src_ld elements
-  char* dst;         // cols x rpad, leading dim rpad elements; zeros for rows >= rows
-  int64_t rows, cols, src_ld, rpad;
+  char* dst;         // cols x rpad, leading dim dst_ld elements; zeros for rows <= r < rpad
+  int64_t rows, cols, src_ld, rpad, dst_ld;
 };
 
 // Token n = s * T + t of a strided layout into contiguous rows: hidden row
@@ -112,12 +112,13 @@ struct GArgs {
   const int64_t* targets;
   const float* lse;
   const float* grad_rows;  // reduction "none": per-row upstream gradient (null = 1)
-  char* G;                 // [npad][cvpad] or null
+  char* G;                 // [npad][g_ld] (this chunk's cvpad columns) or null
   char* GT;                // [cvpad][npad] or null
-  char* WcT;               // [H][cvpad]: W_c^T, 16-bit types only, or null
+  char* WcT;               // [H][wct_ld] (this chunk's cvpad columns): W_c^T, 16-bit types only, or null
   float* dbpart;           // [kBiasParts*n_tok_tiles][V] or null
   int64_t N, H, V, ignore_index, c0;
   int cv, cvpad, npad, n_tok_tiles, n_voc_tiles;
+  int g_ld, wct_ld;        // row pitches (elements) of G and W_c^T
   int none_reduction;
   float s, cap, inv_cap;
   const float* class_weight;  // [V] or null
@@ -125,14 +126,14 @@ struct GArgs {
 };
 
 struct DhArgs {
-  const char* G;     // [npad][cvpad]
-  const char* WcT;   // [H][cvpad]
+  const char* G;     // [npad][ld]: K = kdim columns (one or two chunks side by side)
+  const char* WcT;   // [H][ld]
   float* acc;        // ksplit x [N][H] fp32 unscaled running sums across chunks (split s at acc + s * acc_stride)
   char* out;         // grad_hidden (N,H)
   const float* scale;
   int64_t N, H, acc_stride;
-  int cvpad, n_tok_tiles, n_h_tiles, first, last;
-  int ksplit, kpart;  // the chunk's K in ksplit parts of kpart ids (grid.y = ksplit)
+  int ld, kdim, n_tok_tiles, n_h_tiles, first, last;
+  int ksplit, kpart;  // K in ksplit parts of kpart ids (grid.y = ksplit)
 };
 
 // grad_hidden = the fixed-order sum of the ksplit accumulators, in the dtype.

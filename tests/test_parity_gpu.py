@@ -82,6 +82,13 @@ def test_grad_hidden_k_split_classes(n, h, split):
     run_case(W["midvocab_bf16"].resized(n=n, h=h, v=1300), bwd_vocab_chunk=512)
 
 
+@pytest.mark.parametrize("v,dtype", [(5000, "bf16"), (4700, "f16"), (4700, "f32")])
+def test_grad_hidden_over_pairs_of_chunks(v, dtype):
+    """16 chunks or more: grad_hidden runs once per pair of chunks (20
+    chunks: ten pairs; 19: nine pairs and a last chunk alone)."""
+    run_case(W["transforms_bf16"].resized(n=1030, h=256, v=v, dtype=dtype), bwd_vocab_chunk=256)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_default_plan_with_an_absorbed_last_chunk(dtype):
     """V = 2600 in default chunks of 512 ids leaves 40 ids, which join the
