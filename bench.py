@@ -94,6 +94,8 @@ def main():
     ap.add_argument("--phase", choices=["both", "fwd"], default="both",
                     help="'fwd' runs forward passes only (for per-kernel counter runs); "
                          "the headline line is 'both'")
+    ap.add_argument("--reduction", choices=["mean", "sum", "none"], default=None,
+                    help="override the workload's reduction (not the headline)")
     ap.add_argument("--label-smoothing", type=float, default=0.0,
                     help="loss variant (not the headline): label smoothing eps")
     ap.add_argument("--z-loss", type=float, default=0.0, help="loss variant (not the headline): z-loss coefficient")
@@ -126,6 +128,9 @@ def main():
         variants = True
     if args.dtype and args.dtype != w.dtype:
         w = w.resized(dtype=args.dtype, name=w.name.replace(w.dtype, args.dtype))
+        variants = True
+    if args.reduction and args.reduction != w.reduction:
+        w = w.resized(reduction=args.reduction)
         variants = True
     d = fi.generate(w, device=dev)
     hidden, weight, targets, bias = d["hidden"], d["weight"], d["targets"], d["bias"]
