@@ -108,7 +108,7 @@ def main():
     args = ap.parse_args()
     variants = bool(args.label_smoothing or args.z_loss or args.class_weights or args.grad_weight_fp32)
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no "
               f"multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 

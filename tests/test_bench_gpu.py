@@ -1,0 +1,34 @@
+"""bench.py's output contract on a small workload: one JSON line with the
+fields the benchmark promises (throughput, roofline entry, configuration)."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_bench_prints_one_json_line_with_the_contract_fields():
+    cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "midvocab_bf16", "--steps", "2",
+           "--warmup", "1", "--no-cpu-baseline"]
+    print("\n[case] bench.py on the mid-vocab workload", flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert res.returncode == 0, res.stderr[-2000:]
+    lines = [line for line in res.stdout.splitlines() if line.strip()]
+    assert len(lines) == 1, res.stdout
+    out = json.loads(lines[0])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                "scaling", "vs_baseline", "dtype", "data", "config", "roofline"):
+        assert key in out, key
+    assert out["n_gpus"] == 1 and out["steps"] == 2 and out["warmup"] == 1
+    assert out["value"] > 0 and out["ms_per_step"] > 0 and out["unit"] == "TFLOP/s"
+    assert out["config"]["workload"].startswith("midvocab_bf16")
+    assert "not the headline" in out["metric"]
+    roof = out["roofline"]
+    for key in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
+        assert key in roof, key
+    assert roof["bound"] == "mfma" and 0 < roof["frac"] < 1
