@@ -201,13 +201,27 @@ template <int W> struct CopyPlan {
   i32x4_t ra, rb;   // buffer resources of A and B
   uint32_t oa, ob;  // the lane's byte offset in copy 0 of A / of B
   uint32_t sa, sb;  // 8*W row pitches of A / of B (wave-uniform)
+  uint32_t kb;      // B bytes per stage: ROWB, or 64 row pitches when B is K-major
 };
+
+// K-major B (16-bit types): the B panel is stored [k][col], 256 columns
+// (512 bytes) per K row, and a stage holds 64 K rows of it (the same 32 KB).
+// Copy block bb = 0..31 of B is K rows 2 bb, 2 bb + 1; lane L fills chunk
+// position L & 31 of row 2 bb + L / 32.  Chunk c of K row r sits at position
+// c ^ kswz(r): the 16 rows that one transposed fragment read touches
+// (8 g + [0, 4) and 8 g + 4 + [0, 4) for g = 0..3) then spread their 32-byte
+// pieces over all eight 32-byte bank groups, two rows each.  kswz depends on
+// bits 0, 1 and 3 of r only, so it is the same for rows 16 apart (the copies
+// of one lane), 4 apart (a fragment's two reads) and 32 apart (the slabs).
+__device__ __forceinline__ constexpr int kswz(int r) { return 2 * ((r & 3) | (((r >> 3) & 1) << 2)); }
 
 template <int W> __device__ __forceinline__ constexpr int copy_block(int i, int wave) { return wave + W * i; }
 __device__ __forceinline__ int copy_row(int blk, int L) { return (blk & 31) * 8 + (L >> 3); }
 __device__ __forceinline__ int copy_chunk(int row, int L) { return (L & 7) ^ ((row >> 1) & 7); }
 
-template <int W>
+// BK: B is K-major (B.rows = K rows, B.kbytes = 512 column bytes; the host
+// keeps every K-row offset of the panel below 2^32 bytes).
+template <int W, bool BK = false>
 __device__ __forceinline__ void copy_plan(CopyPlan<W>& cp, const Panel& A, const Panel& B, int t) {
   const int wave = t >> 6, L = t & 63;
   const int row = copy_row(copy_block<W>(0, wave), L);
@@ -215,9 +229,18 @@ __device__ __forceinline__ void copy_plan(CopyPlan<W>& cp, const Panel& A, const
   cp.ra = panel_rsrc(A);
   cp.rb = panel_rsrc(B);
   cp.oa = (uint32_t)(row * A.ld) + c16;
-  cp.ob = (uint32_t)(row * B.ld) + c16;
   cp.sa = __builtin_amdgcn_readfirstlane((uint32_t)(8 * W * A.ld));
-  cp.sb = __builtin_amdgcn_readfirstlane((uint32_t)(8 * W * B.ld));
+  if constexpr (BK) {
+    static_assert(W == 8, "four B copies of 2 K rows per wave and stage");
+    const int kr = 2 * wave + (L >> 5);  // K row of copy 0; copy i adds 16 i
+    cp.ob = (uint32_t)(kr * B.ld) + (uint32_t)((((L & 31) ^ kswz(kr))) * 16);
+    cp.sb = __builtin_amdgcn_readfirstlane((uint32_t)(16 * B.ld));
+    cp.kb = __builtin_amdgcn_readfirstlane((uint32_t)(64 * B.ld));
+  } else {
+    cp.ob = (uint32_t)(row * B.ld) + c16;
+    cp.sb = __builtin_amdgcn_readfirstlane((uint32_t)(8 * W * B.ld));
+    cp.kb = (uint32_t)ROWB;
+  }
 }
 
 // Copy I of the stage at K byte offset k0 into buffer S.  Stages past K (the
@@ -226,11 +249,12 @@ template <int W> struct StageCopy {
   const CopyPlan<W>& cp;
   uint32_t k0;        // wave-uniform
   uint32_t wave_lds;  // wave * 1024 (wave-uniform)
+  uint32_t kb0;       // B's offset of the stage (k0 unless B is K-major)
   template <int S, int I> __device__ __forceinline__ void issue() const {
     constexpr int H = Gemm<W>::NCOP / 2;
     constexpr bool OPA = I < H;
     constexpr uint32_t ii = OPA ? I : I - H;
-    const uint32_t soff = k0 + ii * (OPA ? cp.sa : cp.sb);
+    const uint32_t soff = (OPA ? k0 : kb0) + ii * (OPA ? cp.sa : cp.sb);
     lds_copy16(OPA ? cp.ra : cp.rb, (OPA ? cp.oa : cp.ob) + soff,
                lds_addr(stage_buf<S>() + W * I * 1024) + wave_lds);
   }
@@ -267,7 +291,7 @@ struct FragBase {
   uint32_t a[NSLABS], b[NSLABS];
 };
 
-template <int W>
+template <int W, bool BK = false>
 __device__ __forceinline__ void frag_base(FragBase& fb, int wave, int lane) {
   const int r16 = lane & 15, q = lane >> 4, x = (r16 >> 1) & 7;
   const int ra = Gemm<W>::wm(wave) * 16 * Gemm<W>::WI, rb = Gemm<W>::wn(wave) * 16 * Gemm<W>::WJ;
@@ -277,6 +301,16 @@ __device__ __forceinline__ void frag_base(FragBase& fb, int wave, int lane) {
     fb.a[s] = (uint32_t)((ra + r16) * ROWB) + coff;
     fb.b[s] = (uint32_t)(OPB + (rb + r16) * ROWB) + coff;
   }
+  if constexpr (BK) {
+    // K-major B, first read of fragment 0 of slab 0: lane 16 g + i addresses
+    // K row 8 g + i / 4, columns rb + 4 (i & 3) .. +3 (chunk rb / 8 + (i & 3) / 2,
+    // byte 8 (i & 1) in it).  Fragment J flips chunk bits 1-2 (offset ^ 32 J),
+    // the second read is 4 rows on (+2048), slab 1 is 32 rows on (+16384).
+    const int kr = 8 * q + (r16 >> 2);
+    const int chunk = rb / 8 + ((r16 & 3) >> 1);
+    fb.b[0] = (uint32_t)(OPB + kr * 512 + ((chunk ^ kswz(kr)) << 4) + 8 * (r16 & 1));
+    fb.b[1] = fb.b[0] + 16384u;
+  }
 }
 
 // A fragment I / B fragment J of slab SL of buffer S: lane (l&15, l>>4)
@@ -285,9 +319,22 @@ template <int W, int S, int SL, int I>
 __device__ __forceinline__ void read_a(Frags<W>& f, const FragBase& fb) {
   f.a[I] = *reinterpret_cast<const uint4*>(stage_buf<S>() + fb.a[SL] + I * 16 * ROWB);
 }
-template <int W, int S, int SL, int J>
+template <int W, int S, int SL, int J, bool BK = false>
 __device__ __forceinline__ void read_b(Frags<W>& f, const FragBase& fb) {
-  f.b[SL][J] = *reinterpret_cast<const uint4*>(stage_buf<S>() + fb.b[SL] + J * 16 * ROWB);
+  if constexpr (BK) {
+    // two transposed reads: lane 16 g + i gets column i of K rows 8 g + [0, 4)
+    // and 8 g + 4 + [0, 4) of the fragment, i.e. its k = 8 g .. 8 g + 7
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4* lp;
+    const uint32_t off = fb.b[SL] ^ (uint32_t)(32 * J);
+    const uint32_t base = lds_addr(stage_buf<S>());
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lp>(base + off));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lp>(base + off + 2048u));
+    const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+    f.b[SL][J] = make_uint4(l2.x, l2.y, h2.x, h2.y);
+  } else {
+    f.b[SL][J] = *reinterpret_cast<const uint4*>(stage_buf<S>() + fb.b[SL] + J * 16 * ROWB);
+  }
 }
 
 // Item k of M spread evenly over N steps goes after step floor(k*N/M).
@@ -332,7 +379,7 @@ struct NoSide {
 // the stage's NCOP copies (into buffer CS) placed between them as the step
 // functions above say: a wave issues in order and would otherwise stall its
 // MFMAs behind a burst of copies or reads.
-template <int D, int W, int SC, int RS, int RSL, int CS, bool COPIES, int STEP = 0, class Copy>
+template <int D, int W, int SC, int RS, int RSL, int CS, bool COPIES, bool BK, int STEP = 0, class Copy>
 __device__ __forceinline__ void slab_phase(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], Frags<W>& f,
                                            const FragBase& fb, const Copy& cp) {
   constexpr int WJ = Gemm<W>::WJ;
@@ -341,22 +388,22 @@ __device__ __forceinline__ void slab_phase(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>::
     mfma_frag<D>(acc[I][J], f.a[I], f.b[SC][J]);
     if constexpr (J == WJ - 1) read_a<W, RS, RSL, I>(f, fb);
     constexpr int rb = step_read_b<W>(STEP), cpy = step_copy<W, COPIES>(STEP);
-    if constexpr (rb >= 0) read_b<W, RS, RSL, rb>(f, fb);
+    if constexpr (rb >= 0) read_b<W, RS, RSL, rb, BK>(f, fb);
     if constexpr (cpy >= 0) cp.template issue<CS, cpy>();
     sched_fence();
-    slab_phase<D, W, SC, RS, RSL, CS, COPIES, STEP + 1>(acc, f, fb, cp);
+    slab_phase<D, W, SC, RS, RSL, CS, COPIES, BK, STEP + 1>(acc, f, fb, cp);
   }
 }
 
 // Every fragment of slab SL of buffer S.
-template <int W, int S, int SL, int K = 0>
+template <int W, int S, int SL, bool BK, int K = 0>
 __device__ __forceinline__ void frag_read(Frags<W>& f, const FragBase& fb) {
   if constexpr (K < Gemm<W>::WI) {
     read_a<W, S, SL, K>(f, fb);
-    frag_read<W, S, SL, K + 1>(f, fb);
+    frag_read<W, S, SL, BK, K + 1>(f, fb);
   } else if constexpr (K < Gemm<W>::WI + Gemm<W>::WJ) {
-    read_b<W, S, SL, K - Gemm<W>::WI>(f, fb);
-    frag_read<W, S, SL, K + 1>(f, fb);
+    read_b<W, S, SL, K - Gemm<W>::WI, BK>(f, fb);
+    frag_read<W, S, SL, BK, K + 1>(f, fb);
   }
 }
 
@@ -367,7 +414,7 @@ __device__ __forceinline__ void frag_read(Frags<W>& f, const FragBase& fb) {
 //   wave is done reading buffer S and stage kt+1 is visible
 //   slab 1: MFMAs | reads of slab 0 of stage kt+1 (S^1) | every copy of
 //   stage kt+2 (into S), as early as the buffer allows
-template <int D, int W, int S, class C, class Side>
+template <int D, int W, int S, bool BK, class C, class Side>
 __device__ __forceinline__ void kstage(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], Frags<W>& f,
                                        const FragBase& fb, const C& c, bool zero_next, const Panel& A, int kt,
                                        int t, Side& side) {
@@ -375,7 +422,7 @@ __device__ __forceinline__ void kstage(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ],
   constexpr int SN = S ^ 1;
   const NoCopy nc;
   sched_fence();
-  slab_phase<D, W, 0, S, 1, SN, false>(acc, f, fb, nc);
+  slab_phase<D, W, 0, S, 1, SN, false, BK>(acc, f, fb, nc);
   wait_vmcnt<0>();
   if (zero_next) zero_tail<W, SN>(A, kt + 1, t);
   sched_fence();
@@ -384,17 +431,20 @@ __device__ __forceinline__ void kstage(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ],
   lds_barrier();
   side.template after<S>(kt);
   sched_fence();
-  slab_phase<D, W, 1, SN, 0, S, true>(acc, f, fb, c);
+  slab_phase<D, W, 1, SN, 0, S, true, BK>(acc, f, fb, c);
 }
 
 // Stage kt; the copies it issues are of stage kt+2.  zero_next: stage kt+1
 // is the ragged last one.
-template <int D, int W, int S, bool EDGE, class Side>
+template <int D, int W, int S, bool EDGE, bool BK, class Side>
 __device__ __forceinline__ void kstage_at(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], Frags<W>& f,
                                           const CopyPlan<W>& cp, const FragBase& fb, const Panel& A, int kt,
                                           int nk, bool ragged, uint32_t wave_lds, int t, Side& side) {
-  const StageCopy<W> c{cp, (uint32_t)(kt + 2) * ROWB, wave_lds};
-  kstage<D, W, S>(acc, f, fb, c, EDGE && ragged && kt + 1 == nk - 1, A, kt, t, side);
+  const uint32_t k0 = (uint32_t)(kt + 2) * ROWB;
+  uint32_t kb0 = k0;
+  if constexpr (BK) kb0 = (uint32_t)(kt + 2) * cp.kb;
+  const StageCopy<W> c{cp, k0, wave_lds, kb0};
+  kstage<D, W, S, BK>(acc, f, fb, c, EDGE && ragged && kt + 1 == nk - 1, A, kt, t, side);
 }
 
 // The first two stages of a tile: the copy plan and the copies of stages 0
@@ -402,14 +452,14 @@ __device__ __forceinline__ void kstage_at(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>::W
 // buffers of any previous use; the caller may then run code that touches
 // neither the stage buffers nor vector memory counters it waits on exactly
 // (e.g. the previous tile's epilogue) before gemm_run.
-template <int W>
+template <int W, bool BK = false>
 __device__ __forceinline__ void gemm_prefetch(CopyPlan<W>& cp, const Panel& A, const Panel& B) {
   const int t = threadIdx.x;
   const uint32_t wave_lds = (uint32_t)__builtin_amdgcn_readfirstlane(t >> 6) * 1024u;
-  copy_plan<W>(cp, A, B, t);
+  copy_plan<W, BK>(cp, A, B, t);
   lds_barrier();  // every wave is done with the buffers of any previous use
-  copy_stage<W, 0>(StageCopy<W>{cp, 0u, wave_lds});
-  copy_stage<W, 1>(StageCopy<W>{cp, (uint32_t)ROWB, wave_lds});
+  copy_stage<W, 0>(StageCopy<W>{cp, 0u, wave_lds, 0u});
+  copy_stage<W, 1>(StageCopy<W>{cp, (uint32_t)ROWB, wave_lds, BK ? cp.kb : (uint32_t)ROWB});
 }
 
 // acc[i][j] (this wave's WI x WJ blocks) = A_panel . B_panel^T over all of K,
@@ -419,7 +469,7 @@ __device__ __forceinline__ void gemm_prefetch(CopyPlan<W>& cp, const Panel& A, c
 // ZERO = false: acc arrives holding values to add to (loaded by the caller
 // before gemm_prefetch, so that those loads complete in order ahead of the
 // stage copies and the first wait below covers them).
-template <int D, int W, class Side, bool ZERO = true>
+template <int D, int W, class Side, bool ZERO = true, bool BK = false>
 __device__ __forceinline__ void gemm_run(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], const CopyPlan<W>& cp,
                                          const Panel& A, Side& side) {
   static_assert(NSTAGES == 2, "the loops below alternate two buffers");
@@ -442,21 +492,21 @@ __device__ __forceinline__ void gemm_run(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ
   if (ragged && nk == 1) zero_tail<W, 0>(A, 0, t);
   lds_barrier();
   FragBase fb;
-  frag_base<W>(fb, wave, lane);
+  frag_base<W, BK>(fb, wave, lane);
   Frags<W> f;
-  frag_read<W, 0, 0>(f, fb);
+  frag_read<W, 0, 0, BK>(f, fb);
   // Pairs of stages none of whose successors is the ragged last stage, then
   // the rest.  A loop header with only two predecessors keeps the waitcnt
   // pass from falling back to a full wait at the top of every round.
   const int last_plain = ragged ? nk - 2 : nk - 1;
   int kt = 0;
   for (; kt + 3 <= last_plain; kt += 2) {
-    kstage_at<D, W, 0, false>(acc, f, cp, fb, A, kt, nk, ragged, wave_lds, t, side);
-    kstage_at<D, W, 1, false>(acc, f, cp, fb, A, kt + 1, nk, ragged, wave_lds, t, side);
+    kstage_at<D, W, 0, false, BK>(acc, f, cp, fb, A, kt, nk, ragged, wave_lds, t, side);
+    kstage_at<D, W, 1, false, BK>(acc, f, cp, fb, A, kt + 1, nk, ragged, wave_lds, t, side);
   }
   for (; kt < nk; kt += 2) {
-    kstage_at<D, W, 0, true>(acc, f, cp, fb, A, kt, nk, ragged, wave_lds, t, side);
-    if (kt + 1 < nk) kstage_at<D, W, 1, true>(acc, f, cp, fb, A, kt + 1, nk, ragged, wave_lds, t, side);
+    kstage_at<D, W, 0, true, BK>(acc, f, cp, fb, A, kt, nk, ragged, wave_lds, t, side);
+    if (kt + 1 < nk) kstage_at<D, W, 1, true, BK>(acc, f, cp, fb, A, kt + 1, nk, ragged, wave_lds, t, side);
   }
   wait_vmcnt<0>();
   lds_barrier();
@@ -468,6 +518,19 @@ __device__ __forceinline__ void gemm_nt_tile(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>
   CopyPlan<W> cp;
   gemm_prefetch<W>(cp, A, B);
   gemm_run<D, W>(acc, cp, A, side);
+}
+
+// acc = A_panel . B^T with B K-major (16-bit types): B.base is column 0 of
+// K row 0, B.ld the K-row pitch, B.rows the K rows (at least A's K), and
+// B.kbytes = 512.  A's K must be whole stages (a multiple of ROWB bytes).
+template <int D, int W>
+__device__ __forceinline__ void gemm_tile_kmajor_b(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], const Panel& A,
+                                                   const Panel& B) {
+  static_assert(Elem<D>::bytes == 2, "transposed fragment reads are of 16-bit elements");
+  NoSide none;
+  CopyPlan<W> cp;
+  gemm_prefetch<W, true>(cp, A, B);
+  gemm_run<D, W, NoSide, true, true>(acc, cp, A, none);
 }
 
 template <int D, int W>

@@ -1092,11 +1092,13 @@ __global__ __launch_bounds__(256) void bwd_dh_final_kernel(DhFinalArgs a) {
 }
 
 // grad_weight[v][h] = scale * sum_n G[n][v] H[n][h] for one vocabulary chunk:
-// A = H^T (h rows), B = G^T (v rows), K = tokens.  16-bit results go through
+// A = H^T (h rows), B = G^T (v rows), K = tokens; with BK (16-bit types) B
+// is G itself, read K-major (token rows of the chunk's columns, transposed in
+// the fragment reads), so the recompute kernel writes no G^T.  16-bit results go through
 // the LDS tile and leave as whole 512-byte row pieces; fp32 results (fp32
 // inputs, or out_f32) are stored straight from the accumulators, each
 // quarter-wave writing 64 contiguous bytes of one row.
-template <int D, int W>
+template <int D, int W, bool BK>
 __global__ __launch_bounds__(W * 64) void bwd_dw_kernel(DwArgs a) {
   constexpr int EB = Elem<D>::bytes, WI = Gemm<W>::WI, WJ = Gemm<W>::WJ;
   const TileAB ti = grouped_tile<kDwGA, kDwGB, kDwXcd>(blockIdx.x, gridDim.x, a.n_h_tiles, a.n_voc_tiles);
@@ -1107,9 +1109,14 @@ __global__ __launch_bounds__(W * 64) void bwd_dw_kernel(DwArgs a) {
   const int64_t v0 = (int64_t)vt * TILE, h0 = (int64_t)ht * TILE;
   const int64_t kb = (int64_t)a.npad * EB;
   Panel A{a.HT + h0 * kb, kb, (int)min<int64_t>(TILE, a.H - h0), kb};
-  Panel B{a.GT + v0 * kb, kb, (int)min<int64_t>(TILE, a.cv - v0), kb};
   f32x4_t acc[WI][WJ];
-  gemm_nt_tile<D, W>(acc, A, B);
+  if constexpr (BK) {
+    // columns v0 .. v0 + 255 of G's npad token rows (pitch gld elements); columns
+    // past the chunk read whatever follows and only feed outputs never stored
+    gemm_tile_kmajor_b<D, W>(acc, A, Panel{a.GT + v0 * EB, (int64_t)a.gld * EB, a.npad, 2 * TILE});
+  } else {
+    gemm_nt_tile<D, W>(acc, A, Panel{a.GT + v0 * kb, kb, (int)min<int64_t>(TILE, a.cv - v0), kb});
+  }
   const float scale = a.scale[0];
   if constexpr (EB == 2) {
     if (!a.out_f32) {
@@ -1272,9 +1279,15 @@ hipError_t launch_backward_dh_final(int dtype, const DhFinalArgs& a, hipStream_t
 hipError_t launch_backward_dw(int dtype, const DwArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)grouped_grid<kDwGA, kDwGB>(a.n_h_tiles, a.n_voc_tiles)), block(kContractWaves * 64);
   switch (dtype) {
-    case DT_F32: hipLaunchKernelGGL((bwd_dw_kernel<DT_F32, kContractWaves>), grid, block, 0, st, a); break;
-    case DT_F16: hipLaunchKernelGGL((bwd_dw_kernel<DT_F16, kContractWaves>), grid, block, 0, st, a); break;
-    case DT_BF16: hipLaunchKernelGGL((bwd_dw_kernel<DT_BF16, kContractWaves>), grid, block, 0, st, a); break;
+    case DT_F32: hipLaunchKernelGGL((bwd_dw_kernel<DT_F32, kContractWaves, false>), grid, block, 0, st, a); break;
+    case DT_F16:
+      if (a.gk) hipLaunchKernelGGL((bwd_dw_kernel<DT_F16, kContractWaves, true>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((bwd_dw_kernel<DT_F16, kContractWaves, false>), grid, block, 0, st, a);
+      break;
+    case DT_BF16:
+      if (a.gk) hipLaunchKernelGGL((bwd_dw_kernel<DT_BF16, kContractWaves, true>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((bwd_dw_kernel<DT_BF16, kContractWaves, false>), grid, block, 0, st, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

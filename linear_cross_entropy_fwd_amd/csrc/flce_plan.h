@@ -146,13 +146,15 @@ struct DhFinalArgs {
 };
 
 struct DwArgs {
-  const char* GT;    // [cvpad][npad]
+  const char* GT;    // [cvpad][npad]; with gk, G itself: [npad][gld] from the chunk's first column
   const char* HT;    // [H][npad]
   char* out;         // grad_weight rows [c0, c0+cv)
   const float* scale;
   int64_t H;
   int cv, npad, n_voc_tiles, n_h_tiles;
   int out_f32;       // 1: out is fp32 whatever the input dtype
+  int gk;            // 1 (16-bit types): GT is G, read K-major
+  int gld;           // row pitch of G in elements (gk only)
 };
 
 struct DbArgs {
