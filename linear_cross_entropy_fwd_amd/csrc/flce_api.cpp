@@ -229,6 +229,7 @@ struct BwdLayout {
   int64_t cvpad_reg, gld;  // a full chunk's padded width; row pitch of the G and W_c^T buffers
   int n_chunks, n_tok_tiles, n_h_tiles, dh_split, dh_pair;
   bool gk;  // grad_weight reads G K-major (no G^T buffer)
+  bool dk;  // grad_hidden reads the weight rows K-major (no W_c^T buffer)
   TokLayout tok;
   size_t off_scale, off_ht, off_wct, off_g, off_gt, off_dh, off_db, off_hrows, off_tgt, total;
 };
@@ -271,7 +272,12 @@ BwdLayout bwd_layout(const flce_problem_t& p) {
   };
   L.off_scale = take(16);
   L.off_ht = take((size_t)H * L.npad * eb);
-  L.off_wct = take((size_t)H * L.gld * eb);
+  // 16-bit types: grad_hidden reads the chunk's weight rows as a K-major
+  // operand, so W_c^T is neither written (the recompute kernel's side job,
+  // 22 us of its time a chunk at the head shape) nor read.  Its copy offsets
+  // span a pair's K ids plus two stages of weight rows.
+  L.dk = eb == 2 && (L.gld + 128) * H * eb + 512 < (int64_t(1) << 32);
+  L.off_wct = take(L.dk ? 0 : (size_t)H * L.gld * eb);
   L.off_g = take((size_t)L.npad * L.gld * eb);
   // 16-bit types: grad_weight reads G itself as a K-major operand, so the
   // recompute kernel writes no G^T (measured 29 us of its 348 us a chunk at
@@ -510,10 +516,11 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
     const int64_t col = slot == 0 ? 0 : L.cvpad_reg;
     char* g_c = g + col * eb;
     char* wct_c = wct + col * eb;
-    // 16-bit types with at least 4 token tiles: the recompute kernel writes
-    // W_c^T as a side job; otherwise the transpose kernel does.
-    const bool fused_wct = want_dh && eb == 2 && L.n_tok_tiles >= 4;
-    if (want_dh && !fused_wct) {
+    // W_c^T, when grad_hidden does not read the weight rows K-major: with
+    // 16-bit types and at least 4 token tiles the recompute kernel writes it
+    // as a side job, otherwise the transpose kernel does.
+    const bool fused_wct = want_dh && eb == 2 && L.n_tok_tiles >= 4 && !L.dk;
+    if (want_dh && !fused_wct && !L.dk) {
       flce::TransposeArgs ta{reinterpret_cast<const char*>(weight) + c0 * H * eb, wct_c, cv, H, H, cvpad, L.gld};
       if ((e = flce::launch_transpose(p->dtype, ta, st)) != hipSuccess) return hip_fail(e, "transpose kernel");
     }
@@ -588,6 +595,9 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
       da.ksplit = L.dh_split;
       da.kpart = (int)round_up(cdiv(da.kdim, L.dh_split), 64);
       da.acc_stride = N * H;
+      da.bk = L.dk ? 1 : 0;
+      da.Wk = reinterpret_cast<const char*>(weight) + (int64_t)(c - slot) * L.chunk * H * eb;
+      da.wrows = V - (int64_t)(c - slot) * L.chunk;
       if ((e = flce::launch_backward_dh(p->dtype, da, st)) != hipSuccess) return hip_fail(e, "grad_hidden kernel");
       if (da.last && L.dh_split > 1) {
         flce::DhFinalArgs fa{dh, scale, reinterpret_cast<char*>(grad_hidden), N * H, N * H, L.dh_split};

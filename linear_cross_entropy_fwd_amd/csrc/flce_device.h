@@ -219,7 +219,7 @@ template <int W> __device__ __forceinline__ constexpr int copy_block(int i, int 
 __device__ __forceinline__ int copy_row(int blk, int L) { return (blk & 31) * 8 + (L >> 3); }
 __device__ __forceinline__ int copy_chunk(int row, int L) { return (L & 7) ^ ((row >> 1) & 7); }
 
-// BK: B is K-major (B.rows = K rows, B.kbytes = 512 column bytes; the host
+// BK: B is K-major (B.rows = K rows, B.kbytes = the last row's valid column bytes; the host
 // keeps every K-row offset of the panel below 2^32 bytes).
 template <int W, bool BK = false>
 __device__ __forceinline__ void copy_plan(CopyPlan<W>& cp, const Panel& A, const Panel& B, int t) {
@@ -521,16 +521,19 @@ __device__ __forceinline__ void gemm_nt_tile(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>
 }
 
 // acc = A_panel . B^T with B K-major (16-bit types): B.base is column 0 of
-// K row 0, B.ld the K-row pitch, B.rows the K rows (at least A's K), and
-// B.kbytes = 512.  A's K must be whole stages (a multiple of ROWB bytes).
-template <int D, int W>
+// K row 0, B.ld the K-row pitch, B.rows the valid K rows and B.kbytes the
+// valid column bytes of the last of them (at most 512): the copies read 512
+// bytes of every K row, zeros past that range.  A's K must be whole stages
+// (a multiple of ROWB bytes).  ZERO = false: acc arrives holding values to
+// add to, as in gemm_run.
+template <int D, int W, bool ZERO = true>
 __device__ __forceinline__ void gemm_tile_kmajor_b(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>::WJ], const Panel& A,
                                                    const Panel& B) {
   static_assert(Elem<D>::bytes == 2, "transposed fragment reads are of 16-bit elements");
   NoSide none;
   CopyPlan<W> cp;
   gemm_prefetch<W, true>(cp, A, B);
-  gemm_run<D, W, NoSide, true, true>(acc, cp, A, none);
+  gemm_run<D, W, NoSide, ZERO, true>(acc, cp, A, none);
 }
 
 template <int D, int W>

@@ -1012,7 +1012,7 @@ __device__ __forceinline__ void store4(typename Elem<D>::T* p, float x0, float x
 // grad_hidden[n][h] (+)= scale * sum_v G[n][v] W[v][h] over one vocabulary
 // chunk: A = W_c^T (h rows), B = G (n rows), K = the chunk.  The fp32
 // accumulator is read and written 16 bytes per lane.
-template <int D, int W>
+template <int D, int W, bool BK>
 __global__ __launch_bounds__(W * 64) void bwd_dh_kernel(DhArgs a) {
   typedef typename Elem<D>::T T;
   constexpr int EB = Elem<D>::bytes, WI = Gemm<W>::WI, WJ = Gemm<W>::WJ;
@@ -1031,6 +1031,71 @@ __global__ __launch_bounds__(W * 64) void bwd_dh_kernel(DhArgs a) {
   // applied once, when grad_hidden is written.
   float* accbuf = a.acc + (int64_t)blockIdx.y * a.acc_stride;
   f32x4_t acc[WI][WJ];
+  if constexpr (BK) {
+    // Tokens on the MFMA row axis (A = G), hidden on the column axis (B = the
+    // chunk's weight rows, K-major): acc[i][j][e] is token nr + 16 i + e,
+    // hidden hc + 16 j.  The running sum moves one float per lane, 64
+    // contiguous bytes per quarter-wave.
+    // One row pointer walks the lane's 32 token rows (a second per-row
+    // address would keep 32 pointers live across the loads); whole tiles
+    // take no bounds checks.
+    const int64_t nr = n0 + wm * 16 * WI + 4 * q, hc = h0 + wn * 16 * WJ + c16;
+    const bool whole = n0 + TILE <= a.N && h0 + TILE <= a.H;  // wave-uniform
+    float* rp = accbuf + nr * a.H + hc;
+#pragma unroll
+    for (int i = 0; i < WI; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float* r = rp + (int64_t)(16 * i + e) * a.H;
+#pragma unroll
+        for (int j = 0; j < WJ; ++j) {
+          if (a.first) {
+            acc[i][j][e] = 0.f;
+          } else if (whole) {
+            acc[i][j][e] = r[16 * j];
+          } else {
+            const bool in = nr + 16 * i + e < a.N && hc + 16 * j < a.H;
+            acc[i][j][e] = in ? r[16 * j] : 0.f;
+          }
+        }
+      }
+    // K ids past the weight's last row (padding of the last chunk, whose G
+    // columns are zero) add nothing: a split that holds only those is skipped
+    const int64_t wr = min<int64_t>(kn, a.wrows - k0);
+    if (kn > 0 && wr > 0) {
+      const int64_t hb = a.H * EB;
+      Panel A{a.G + n0 * kb + (int64_t)k0 * EB, kb, (int)min<int64_t>(TILE, a.N - n0), (int64_t)kn * EB};
+      Panel B{a.Wk + (int64_t)k0 * hb + h0 * EB, hb, (int)wr, min<int64_t>(TILE, a.H - h0) * EB};
+      gemm_tile_kmajor_b<D, W, false>(acc, A, B);
+    }
+    if (a.last && a.ksplit == 1) {
+      // grad_hidden in the dtype through the LDS tile ([h][n] in, read
+      // transposed into whole 16-byte pieces of grad_hidden rows)
+      const float scale = a.scale[0];
+      if constexpr (EB == 2) {
+#pragma unroll
+        for (int i = 0; i < WI; ++i)
+#pragma unroll
+          for (int j = 0; j < WJ; ++j)
+            tile16_put4<D>(wn * 16 * WJ + 16 * j + c16, wm * 16 * WI + 16 * i + 4 * q, acc[i][j][0] * scale,
+                           acc[i][j][1] * scale, acc[i][j][2] * scale, acc[i][j][3] * scale);
+        __syncthreads();
+        tile16_store_t(reinterpret_cast<uint16_t*>(a.out) + n0 * a.H + h0, a.H, (int)min<int64_t>(TILE, a.H - h0),
+                       (int)min<int64_t>(TILE, a.N - n0), t);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < WI; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float* r = rp + (int64_t)(16 * i + e) * a.H;
+#pragma unroll
+          for (int j = 0; j < WJ; ++j)
+            if (whole || (nr + 16 * i + e < a.N && hc + 16 * j < a.H)) r[16 * j] = acc[i][j][e];
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < WJ; ++j) {
     const int64_t n = n0 + wn * 16 * WJ + 16 * j + c16;
@@ -1111,9 +1176,12 @@ __global__ __launch_bounds__(W * 64) void bwd_dw_kernel(DwArgs a) {
   Panel A{a.HT + h0 * kb, kb, (int)min<int64_t>(TILE, a.H - h0), kb};
   f32x4_t acc[WI][WJ];
   if constexpr (BK) {
-    // columns v0 .. v0 + 255 of G's npad token rows (pitch gld elements); columns
-    // past the chunk read whatever follows and only feed outputs never stored
-    gemm_tile_kmajor_b<D, W>(acc, A, Panel{a.GT + v0 * EB, (int64_t)a.gld * EB, a.npad, 2 * TILE});
+    // columns v0 .. v0 + 255 of G's npad token rows (pitch gld elements).  The
+    // panel's range ends at column cv of the last row, inside G; columns past
+    // the chunk in earlier rows read the next ones' data and feed only
+    // outputs that are never stored.
+    const int64_t cb = (int64_t)min(TILE, a.cv - (int)v0) * EB;
+    gemm_tile_kmajor_b<D, W>(acc, A, Panel{a.GT + v0 * EB, (int64_t)a.gld * EB, a.npad, cb});
   } else {
     gemm_nt_tile<D, W>(acc, A, Panel{a.GT + v0 * kb, kb, (int)min<int64_t>(TILE, a.cv - v0), kb});
   }
@@ -1256,9 +1324,15 @@ hipError_t launch_backward_dh(int dtype, const DhArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)grouped_grid<kDhGA, kDhGB>(a.n_h_tiles, a.n_tok_tiles), (unsigned)a.ksplit),
       block(kContractWaves * 64);
   switch (dtype) {
-    case DT_F32: hipLaunchKernelGGL((bwd_dh_kernel<DT_F32, kContractWaves>), grid, block, 0, st, a); break;
-    case DT_F16: hipLaunchKernelGGL((bwd_dh_kernel<DT_F16, kContractWaves>), grid, block, 0, st, a); break;
-    case DT_BF16: hipLaunchKernelGGL((bwd_dh_kernel<DT_BF16, kContractWaves>), grid, block, 0, st, a); break;
+    case DT_F32: hipLaunchKernelGGL((bwd_dh_kernel<DT_F32, kContractWaves, false>), grid, block, 0, st, a); break;
+    case DT_F16:
+      if (a.bk) hipLaunchKernelGGL((bwd_dh_kernel<DT_F16, kContractWaves, true>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((bwd_dh_kernel<DT_F16, kContractWaves, false>), grid, block, 0, st, a);
+      break;
+    case DT_BF16:
+      if (a.bk) hipLaunchKernelGGL((bwd_dh_kernel<DT_BF16, kContractWaves, true>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((bwd_dh_kernel<DT_BF16, kContractWaves, false>), grid, block, 0, st, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

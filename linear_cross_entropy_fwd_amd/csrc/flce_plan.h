@@ -134,6 +134,11 @@ struct DhArgs {
   int64_t N, H, acc_stride;
   int ld, kdim, n_tok_tiles, n_h_tiles, first, last;
   int ksplit, kpart;  // K in ksplit parts of kpart ids (grid.y = ksplit)
+  // bk (16-bit types): no W_c^T; B is the weight rows themselves, read K-major:
+  // K id k is weight row k of Wk, valid for k < wrows
+  int bk;
+  const char* Wk;
+  int64_t wrows;
 };
 
 // grad_hidden = the fixed-order sum of the ksplit accumulators, in the dtype.
