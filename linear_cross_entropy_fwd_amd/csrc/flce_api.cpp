@@ -292,7 +292,9 @@ BwdLayout bwd_layout(const flce_problem_t& p) {
   // whose grids fall in the same class give bit-identical rows.)
   const int64_t dh_tiles = (int64_t)L.n_tok_tiles * L.n_h_tiles;
   L.dh_split = dh_tiles <= kCUs / 4 ? 4 : dh_tiles <= kCUs / 2 ? 2 : 1;
-  L.off_dh = take(L.n_chunks > L.dh_pair || L.dh_split > 1 ? (size_t)L.dh_split * N * H * 4 : 0);
+  // (the K-major grad_hidden kernel keeps whole 256 x 256 tiles)
+  const int64_t acc_elems = L.dk ? (int64_t)L.n_tok_tiles * L.n_h_tiles * kTile * kTile : N * H;
+  L.off_dh = take(L.n_chunks > L.dh_pair || L.dh_split > 1 ? (size_t)L.dh_split * acc_elems * 4 : 0);
   L.off_db = take(p.has_bias ? (size_t)flce::kBiasParts * L.n_tok_tiles * V * 4 : 0);
   L.tok = tok_layout(p);
   L.off_hrows = take(L.tok.h_gather ? (size_t)N * H * eb : 0);
@@ -594,13 +596,14 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
       da.last = c == L.n_chunks - 1;
       da.ksplit = L.dh_split;
       da.kpart = (int)round_up(cdiv(da.kdim, L.dh_split), 64);
-      da.acc_stride = N * H;
+      da.acc_stride = L.dk ? (int64_t)L.n_tok_tiles * L.n_h_tiles * kTile * kTile : N * H;
       da.bk = L.dk ? 1 : 0;
       da.Wk = reinterpret_cast<const char*>(weight) + (int64_t)(c - slot) * L.chunk * H * eb;
       da.wrows = V - (int64_t)(c - slot) * L.chunk;
       if ((e = flce::launch_backward_dh(p->dtype, da, st)) != hipSuccess) return hip_fail(e, "grad_hidden kernel");
       if (da.last && L.dh_split > 1) {
-        flce::DhFinalArgs fa{dh, scale, reinterpret_cast<char*>(grad_hidden), N * H, N * H, L.dh_split};
+        flce::DhFinalArgs fa{dh, scale, reinterpret_cast<char*>(grad_hidden), da.acc_stride, da.acc_stride,
+                             L.dh_split, L.dk ? 1 : 0, N, H, L.n_h_tiles};
         if ((e = flce::launch_backward_dh_final(p->dtype, fa, st)) != hipSuccess)
           return hip_fail(e, "grad_hidden sum kernel");
       }

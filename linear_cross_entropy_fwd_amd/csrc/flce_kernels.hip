@@ -1036,27 +1036,21 @@ __global__ __launch_bounds__(W * 64) void bwd_dh_kernel(DhArgs a) {
     // chunk's weight rows, K-major): acc[i][j][e] is token nr + 16 i + e,
     // hidden hc + 16 j.  The running sum moves one float per lane, 64
     // contiguous bytes per quarter-wave.
-    // One row pointer walks the lane's 32 token rows (a second per-row
-    // address would keep 32 pointers live across the loads); whole tiles
-    // take no bounds checks.
-    const int64_t nr = n0 + wm * 16 * WI + 4 * q, hc = h0 + wn * 16 * WJ + c16;
-    const bool whole = n0 + TILE <= a.N && h0 + TILE <= a.H;  // wave-uniform
-    float* rp = accbuf + nr * a.H + hc;
+    // The running sum is private to these kernels and kept in their own tile
+    // layout: block (i, j) of thread t of tile (tt, ht) is the float4 at
+    // ((tt * n_h_tiles + ht) * WI * WJ + i * WJ + j) * 512 + t, so each wave
+    // moves 1 KB per instruction.  Tiles past N or H hold entries that are
+    // never written out.
+    float4* tp = reinterpret_cast<float4*>(accbuf) + ((int64_t)(tt * a.n_h_tiles + ht) * (WI * WJ)) * (W * 64) + t;
 #pragma unroll
     for (int i = 0; i < WI; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float* r = rp + (int64_t)(16 * i + e) * a.H;
-#pragma unroll
-        for (int j = 0; j < WJ; ++j) {
-          if (a.first) {
-            acc[i][j][e] = 0.f;
-          } else if (whole) {
-            acc[i][j][e] = r[16 * j];
-          } else {
-            const bool in = nr + 16 * i + e < a.N && hc + 16 * j < a.H;
-            acc[i][j][e] = in ? r[16 * j] : 0.f;
-          }
+      for (int j = 0; j < WJ; ++j) {
+        if (a.first) {
+          acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        } else {
+          const float4 o = tp[(i * WJ + j) * (W * 64)];
+          acc[i][j] = f32x4_t{o.x, o.y, o.z, o.w};
         }
       }
     // K ids past the weight's last row (padding of the last chunk, whose G
@@ -1087,12 +1081,8 @@ __global__ __launch_bounds__(W * 64) void bwd_dh_kernel(DhArgs a) {
 #pragma unroll
       for (int i = 0; i < WI; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float* r = rp + (int64_t)(16 * i + e) * a.H;
-#pragma unroll
-          for (int j = 0; j < WJ; ++j)
-            if (whole || (nr + 16 * i + e < a.N && hc + 16 * j < a.H)) r[16 * j] = acc[i][j][e];
-        }
+        for (int j = 0; j < WJ; ++j)
+          tp[(i * WJ + j) * (W * 64)] = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
     }
     return;
   }
@@ -1144,6 +1134,33 @@ template <int D>
 __global__ __launch_bounds__(256) void bwd_dh_final_kernel(DhFinalArgs a) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= a.count) return;
+  if (a.bk) {
+    // tile layout of the K-major grad_hidden kernel (8 waves, 8 x 4 blocks a
+    // wave): float4 f = ((tile * 32 + blk) * 512 + t) holds tokens
+    // n0 + wm 128 + 16 (blk / 4) + 4 q + [0, 4) of hidden h0 + wn 64 + 16 (blk % 4) + (t & 15)
+    const int64_t f = i / 4;
+    const int t = (int)(f % 512), blk = (int)((f / 512) % 32);
+    const int64_t tile = f / (512 * 32);
+    const int wave = t >> 6, lane = t & 63;
+    const int64_t n = (tile / a.n_h_tiles) * TILE + (wave / 4) * 128 + 16 * (blk / 4) + 4 * (lane >> 4);
+    const int64_t h = (tile % a.n_h_tiles) * TILE + (wave % 4) * 64 + 16 * (blk % 4) + (lane & 15);
+    if (h >= a.H) return;
+    float4 v = *reinterpret_cast<const float4*>(a.acc + i);
+    for (int s = 1; s < a.ksplit; ++s) {
+      const float4 o = *reinterpret_cast<const float4*>(a.acc + (int64_t)s * a.acc_stride + i);
+      v.x = v.x + o.x;
+      v.y = v.y + o.y;
+      v.z = v.z + o.z;
+      v.w = v.w + o.w;
+    }
+    const float sc = a.scale[0];
+    typename Elem<D>::T* out = reinterpret_cast<typename Elem<D>::T*>(a.out);
+    const float x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (n + e < a.N) out[(n + e) * a.H + h] = from_f32<D>(x[e] * sc);
+    return;
+  }
   float4 v = *reinterpret_cast<const float4*>(a.acc + i);
   for (int s = 1; s < a.ksplit; ++s) {
     const float4 o = *reinterpret_cast<const float4*>(a.acc + (int64_t)s * a.acc_stride + i);

@@ -146,8 +146,11 @@ struct DhFinalArgs {
   const float* acc;
   const float* scale;
   char* out;
-  int64_t count, acc_stride;  // count = N * H (a multiple of 4)
+  int64_t count, acc_stride;  // count = N * H (a multiple of 4); with bk, float4 blocks of the tiles
   int ksplit;
+  int bk;                      // accumulators in the tile layout of the K-major grad_hidden kernel
+  int64_t N, H;
+  int n_h_tiles;
 };
 
 struct DwArgs {
