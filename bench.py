@@ -235,6 +235,9 @@ def main():
         "fwd_ms": round(fwd_ms, 4),
         "bwd_ms": round(bwd_ms, 4),
         "peak_mem_incr_mb": round(peak_incr / 2**20, 1),
+        "workspace_mb": round((fws.numel() + bws.numel()) / 2**20, 1),
+        "outputs_mb": round(sum(t.numel() * t.element_size()
+                                for t in (loss, lse, metrics, gh, gw, gb) if t is not None) / 2**20, 1),
         "n_by_v_bytes_mb": round(w.n * w.v * 2 / 2**20, 1),
         "wall_s_timed": round(t_wall, 3),
         "roofline": {"kernel": "fwd_tiles_kernel (forward logit tiles + online LSE)",

@@ -32,3 +32,7 @@ def test_bench_prints_one_json_line_with_the_contract_fields():
     for key in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
         assert key in roof, key
     assert roof["bound"] == "mfma" and 0 < roof["frac"] < 1
+    # The library's own memory is the workspace, which never holds an N x V
+    # array; everything else the step allocates is an output the caller wanted.
+    assert out["workspace_mb"] < out["n_by_v_bytes_mb"]
+    assert out["peak_mem_incr_mb"] <= out["workspace_mb"] + out["outputs_mb"] + 1.0
