@@ -103,6 +103,9 @@ def main():
                     help="loss variant (not the headline): seeded class weights, uniform in [0.5, 1.5)")
     ap.add_argument("--dtype", choices=["bf16", "f16", "f32"], default=None,
                     help="run the workload in another dtype (not the headline)")
+    ap.add_argument("--cold", action="store_true",
+                    help="write a 512 MiB scrub buffer before every step, outside the step's timed window, "
+                         "so that no operand is left in L2 or the last-level cache (not the headline)")
     ap.add_argument("--grad-weight-fp32", action="store_true",
                     help="write grad_weight / grad_bias in fp32 (not the headline)")
     args = ap.parse_args()
@@ -128,6 +131,8 @@ def main():
         variants = True
     if args.dtype and args.dtype != w.dtype:
         w = w.resized(dtype=args.dtype, name=w.name.replace(w.dtype, args.dtype))
+        variants = True
+    if args.cold:
         variants = True
     if args.reduction and args.reduction != w.reduction:
         w = w.resized(reduction=args.reduction)
@@ -183,12 +188,16 @@ def main():
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # 512 MiB is twice the MI355X last-level cache (256 MB) and far above the L2s.
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
     start.record(stream)
-    for e0, e1, e2 in ev:
+    for i, (e0, e1, e2) in enumerate(ev):
+        if scrub is not None:
+            scrub.fill_(i & 0xFF)
         e0.record(stream)
         forward()
         e1.record(stream)
@@ -198,11 +207,12 @@ def main():
     stop.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    total_ms = start.elapsed_time(stop)
+    step_times = sorted(e0.elapsed_time(e2) for e0, _, e2 in ev)
+    total_ms = start.elapsed_time(stop) if scrub is None else sum(step_times)
     ms_step = total_ms / args.steps
     fwd_ms = sum(e0.elapsed_time(e1) for e0, e1, _ in ev) / args.steps
     bwd_ms = sum(e1.elapsed_time(e2) for _, e1, e2 in ev) / args.steps
-    peak_incr = torch.cuda.max_memory_allocated() - base_mem
+    peak_incr = torch.cuda.max_memory_allocated() - base_mem - (scrub.numel() if scrub is not None else 0)
     if not torch.isfinite(loss).all() or (run_bwd and not torch.isfinite(gw.float().abs().max())):
         print("non-finite result", file=sys.stderr)
         sys.exit(3)
@@ -230,8 +240,12 @@ def main():
                    "global_batch": w.n, "parallelism": "none (1 GPU)",
                    **({"label_smoothing": args.label_smoothing, "z_loss": args.z_loss,
                        "class_weights": bool(args.class_weights),
-                       "grad_weight_fp32": bool(args.grad_weight_fp32)} if variants else {})},
+                       "grad_weight_fp32": bool(args.grad_weight_fp32),
+                       "cold_cache": bool(args.cold)} if variants else {})},
         "mfma_util": round(tflops / PEAK_TFLOPS[w.dtype], 4),
+        "step_ms": {"p50": round(step_times[len(step_times) // 2], 4), "min": round(step_times[0], 4),
+                    "max": round(step_times[-1], 4),
+                    "cache": "cold (512 MiB scrub before each step)" if scrub is not None else "warm"},
         "fwd_ms": round(fwd_ms, 4),
         "bwd_ms": round(bwd_ms, 4),
         "peak_mem_incr_mb": round(peak_incr / 2**20, 1),
