@@ -32,7 +32,6 @@ METRIC = "fwd+bwd TFLOP/s (8*N*H*V) and MFMA util at N=4096,H=4096,V=128256 bf16
 PEAK_BF16_TFLOPS = 2516.6          # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
 PEAK_TFLOPS = {"bf16": PEAK_BF16_TFLOPS, "f16": PEAK_BF16_TFLOPS, "f32": 157.3}  # dense MFMA per dtype
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_tiles_headvocab_traffic.json")
 KERNEL_SOURCES = ["linear_cross_entropy_fwd_amd/csrc/flce_kernels.hip",
                   "linear_cross_entropy_fwd_amd/csrc/flce_device.h"]
 
@@ -45,21 +44,80 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic():
-    """HBM bytes per forward-tile launch from the committed counter runs, or
-    None when the kernel sources changed since they were taken."""
+def traffic_file(workload_key: str) -> str:
+    return os.path.join(ROOT, "profiles", f"fwd_tiles_{workload_key}_traffic.json")
+
+
+def kernel_template(dtype: str, metrics: bool, bias: bool, cap: bool) -> str:
+    """The forward tile kernel's template instance a run launches."""
+    return f"{dtype}, metrics={int(metrics)}, bias={int(bias)}, softcap={int(cap)}"
+
+
+def stored_traffic(workload_key: str, template: str, variants: bool):
+    """HBM bytes per forward-tile launch from the committed counter runs of
+    this workload and kernel template, or None: when no such record exists,
+    when the run has options the record was not taken with, or when the
+    kernel sources changed since the counters were read."""
+    if variants:
+        return None
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(workload_key)) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if (rec.get("workload_key") != workload_key or rec.get("template") != template
+            or rec.get("kernel_source_hash") != kernel_source_hash()):
         return None
     return rec.get("hbm_bytes_per_launch")
 
 
+def cpu_info():
+    """CPU model name, physical cores and logical CPUs this process may use."""
+    model, cores = None, set()
+    try:
+        phys = None
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                k, _, v = line.partition(":")
+                k, v = k.strip(), v.strip()
+                if k == "model name" and model is None:
+                    model = v
+                elif k == "physical id":
+                    phys = v
+                elif k == "core id":
+                    cores.add((phys, v))
+    except OSError:
+        pass
+    return model, (len(cores) or None), len(os.sched_getaffinity(0))
+
+
+def argmax_targets_gpu(w, d):
+    """Rows chosen for argmax targets get their row's first-index argmax of
+    the final logits, computed on the GPU with torch in fp32 blocks (inputs
+    of the timed run only; the parity tests take the oracle's ids)."""
+    import torch
+    rows = d["argmax_rows"]
+    if not bool(rows.any()):
+        return d["targets"]
+    wt = d["weight"].float()
+    b = None if d["bias"] is None else d["bias"].float()
+    ids = torch.empty(w.n, dtype=torch.int64, device=d["targets"].device)
+    for r0 in range(0, w.n, 1024):
+        z = d["hidden"][r0:r0 + 1024].float() @ wt.T
+        if b is not None:
+            z += b
+        z *= w.logit_scale
+        if w.softcap is not None:
+            z = w.softcap * torch.tanh(z / w.softcap)
+        ids[r0:r0 + 1024] = torch.argmax(z, dim=1)
+        del z
+    del wt
+    return torch.where(rows, ids, d["targets"])
+
+
 def cpu_baseline(d, w, rows: int):
-    """fp64 oracle (as it stands) on the first `rows` rows of the same inputs."""
+    """fp64 oracle (as it stands) on the first `rows` rows of the same inputs
+    (all of them when rows >= N); "cores" is the BLAS threads it ran with."""
     import numpy as np
     import threadpoolctl
     from oracle import flce_reference
@@ -74,10 +132,12 @@ def cpu_baseline(d, w, rows: int):
                    softcap=w.softcap, reduction=w.reduction)
     dt = time.perf_counter() - t0
     flops = 8.0 * rows * w.h * w.v
+    model, phys, logical = cpu_info()
+    what = (f"the whole workload ({rows} rows)" if rows >= w.n else f"first {rows} of {w.n} rows") + \
+        f", H={w.h}, V={w.v}, fwd+bwd in fp64 with numpy BLAS, {dt:.2f} s wall, 8*rows*H*V flops"
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"first {rows} of {w.n} rows (full H={w.h}, V={w.v}), fwd+bwd in fp64, "
-                      f"{dt:.2f} s wall, 8*rows*H*V flops"}
+            "kind": "oracle", "sample": what, "cpu_model": model, "physical_cores": phys,
+            "logical_cpus_available": logical, "wall_s": round(dt, 3)}
 
 
 def main():
@@ -86,8 +146,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=2048,
-                    help="rows of the workload the CPU oracle baseline runs (about 10-20 s)")
+    ap.add_argument("--cpu-rows", type=int, default=4096,
+                    help="rows of the workload the CPU oracle baseline runs (the whole head-shape "
+                         "workload by default, about 20 s on 16 threads)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="run one device-to-device copy of this size first (HBM counter calibration)")
     ap.add_argument("--workload", default="headvocab_bf16")
@@ -127,8 +188,6 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = fi.WORKLOADS[args.workload]
-    if args.workload != "headvocab_bf16":
-        variants = True
     if args.dtype and args.dtype != w.dtype:
         w = w.resized(dtype=args.dtype, name=w.name.replace(w.dtype, args.dtype))
         variants = True
@@ -137,7 +196,12 @@ def main():
     if args.reduction and args.reduction != w.reduction:
         w = w.resized(reduction=args.reduction)
         variants = True
+    # options beyond the workload's own (the stored counter records hold none)
+    options_changed = variants
+    if args.workload != "headvocab_bf16":
+        variants = True
     d = fi.generate(w, device=dev)
+    d["targets"] = argmax_targets_gpu(w, d)
     hidden, weight, targets, bias = d["hidden"], d["weight"], d["targets"], d["bias"]
     torch.cuda.synchronize()
     base_mem = torch.cuda.memory_allocated()
@@ -220,7 +284,8 @@ def main():
     flops = (8.0 if run_bwd else 2.0) * w.n * w.h * w.v
     tflops = flops / (ms_step * 1e-3) / 1e12
     fwd_tflops = 2.0 * w.n * w.h * w.v / (fwd_ms * 1e-3) / 1e12
-    traffic = stored_traffic()
+    template = kernel_template(w.dtype, w.return_metrics, bias is not None, w.softcap is not None)
+    traffic = stored_traffic(args.workload, template, options_changed or not run_bwd)
     out = {
         "metric": (METRIC if not variants else f"fwd+bwd TFLOP/s (8*N*H*V) on {w.name}" + ", other workload or options (not the headline)")
                   if run_bwd else "forward only TFLOP/s (2*N*H*V), not the headline",
@@ -257,7 +322,7 @@ def main():
         "roofline": {"kernel": "fwd_tiles_kernel (forward logit tiles + online LSE)",
                      "bound": "mfma", "achieved": round(fwd_tflops, 3), "peak": PEAK_TFLOPS[w.dtype],
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_TFLOPS[w.dtype], 4),
-                     "traffic": traffic,
+                     "traffic": traffic, "template": template,
                      "flops_per_launch": 2 * w.n * w.h * w.v,
                      "window": "HIP events around flce_forward (tile kernel + combine + reduce)"},
     }

@@ -40,8 +40,16 @@
  *     flce_last_error() then gives a thread-local message.  FLCE_ERR_HIP
  *     reports a HIP runtime failure (including "no device").
  *   - Out-of-range targets (not ignore_index, outside [0,V)) cannot be seen
- *     without a sync: such a row's loss and gradient rows are NaN and bit 0
- *     of the device status word is set (read it with flce_forward_status).
+ *     without a sync.  The forward gives such a row a NaN loss, so a mean or
+ *     sum loss is NaN, and sets bit 0 of the device status word (read it with
+ *     flce_forward_status); its lse and every other row's loss are unaffected.
+ *     The backward gives the row's softmax-minus-one-hot row a NaN factor,
+ *     so its grad_hidden row is NaN and, since grad_weight and grad_bias
+ *     contract over every row, every entry of grad_weight and grad_bias is
+ *     NaN too; the other rows of grad_hidden are unaffected.  (The Liger
+ *     FLCE pull request's contract refuses bad input loudly rather than
+ *     silently mis-scaling; a NaN that reaches every parameter gradient is
+ *     this library's loud form of that, since it cannot raise without a sync.)
  */
 #ifndef FLCE_H
 #define FLCE_H
@@ -123,9 +131,22 @@ typedef struct flce_problem {
 } flce_problem_t;
 
 /* Bytes of workspace flce_forward / flce_backward need for problem *p
- * (0 if *p is invalid; never fails otherwise).  Pure host function. */
+ * (0 if *p is invalid; never fails otherwise).  Pure host function.
+ * The caller allocates it: every entry point only writes to memory the
+ * caller preallocated, the contract the tdt-loss pull request
+ * (huggingface/kernels-community #882, its torch.compile comment) states for
+ * the fake implementations of its ops. */
 size_t flce_forward_workspace_size(const flce_problem_t* p);
 size_t flce_backward_workspace_size(const flce_problem_t* p);
+
+/* The backward's vocabulary chunking for problem *p (card: "Algorithm",
+ * backward: each logit tile is recomputed; here the vocabulary is swept in
+ * chunks of *chunk ids, the last one *last_chunk ids, *n_chunks in all, each
+ * chunk's grad_weight rows complete after it).  The default plan depends on
+ * H and V only (bwd_vocab_chunk overrides it).  Pure host function; any
+ * output pointer may be NULL.  FLCE_ERR_INVALID_ARGUMENT for an invalid *p. */
+flce_status_t flce_backward_plan(const flce_problem_t* p, int64_t* chunk, int64_t* n_chunks,
+                                 int64_t* last_chunk);
 
 /* Forward pass (card: "Algorithm", forward; "Metrics for free").
  *   hidden, weight, targets, bias (NULL iff !has_bias): inputs as above.
@@ -178,6 +199,14 @@ flce_status_t flce_forward_backward(const flce_problem_t* p, const void* hidden,
 flce_status_t flce_forward_status(const flce_problem_t* p, const void* workspace,
                                   uint32_t* status_out, void* stream);
 
+/* Host-side validation and refusal (the Liger FLCE pull request #1287,
+ * Summary: host-side validation and by-design-refusal contracts, refusing
+ * loudly): every entry point checks its arguments on the host before
+ * anything is enqueued and returns a status instead of raising.
+ * flce_status_str names a status ("FLCE_OK", ...; "FLCE_ERR_UNKNOWN" for
+ * other values); flce_last_error returns this thread's message for the last
+ * non-OK status (valid until this thread's next failing call; "" if none).
+ * Both strings are owned by the library. */
 const char* flce_status_str(flce_status_t s);
 const char* flce_last_error(void);
 const char* flce_version(void);

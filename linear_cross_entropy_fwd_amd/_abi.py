@@ -72,6 +72,8 @@ _SIGNATURES = {
     "flce_forward_backward": (ctypes.c_int, [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                              _VP, ctypes.c_size_t, _VP]),
     "flce_forward_status": (ctypes.c_int, [_PP, _VP, ctypes.POINTER(ctypes.c_uint32), _VP]),
+    "flce_backward_plan": (ctypes.c_int, [_PP, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
+                                          ctypes.POINTER(ctypes.c_int64)]),
     "flce_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "flce_last_error": (ctypes.c_char_p, []),
     "flce_version": (ctypes.c_char_p, []),
@@ -161,6 +163,13 @@ def flce_forward_status(p: Problem, workspace, stream) -> int:
     out = ctypes.c_uint32(0)
     check(library().flce_forward_status(ctypes.byref(p), workspace, ctypes.byref(out), stream))
     return int(out.value)
+
+
+def flce_backward_plan(p: Problem):
+    """(chunk, n_chunks, last_chunk): the backward's vocabulary chunking."""
+    c, n, last = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int64(0)
+    check(library().flce_backward_plan(ctypes.byref(p), ctypes.byref(c), ctypes.byref(n), ctypes.byref(last)))
+    return int(c.value), int(n.value), int(last.value)
 
 
 def flce_version() -> str:

@@ -331,6 +331,17 @@ float cap_of(const flce_problem_t& p) { return p.softcap > 0.f ? p.softcap : 1.f
 
 extern "C" {
 
+flce_status_t flce_backward_plan(const flce_problem_t* p, int64_t* chunk, int64_t* n_chunks,
+                                 int64_t* last_chunk) {
+  const flce_status_t s = check_problem(p);
+  if (s != FLCE_OK) return s;
+  const BwdLayout L = bwd_layout(*p);
+  if (chunk) *chunk = L.chunk;
+  if (n_chunks) *n_chunks = L.n_chunks;
+  if (last_chunk) *last_chunk = L.last_chunk;
+  return FLCE_OK;
+}
+
 size_t flce_forward_workspace_size(const flce_problem_t* p) {
   if (check_problem(p) != FLCE_OK) return 0;
   return fwd_layout(*p).total;

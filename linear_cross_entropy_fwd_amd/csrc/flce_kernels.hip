@@ -12,14 +12,18 @@
 // is written: only 6 words per (row, split).
 //
 // Backward (card: "Algorithm", backward): per vocabulary chunk of Cv ids,
-// recompute the logit tiles, form G = (p - onehot) * coef * dz/draw in the
-// input dtype (both G and G^T), then contract
+// recompute the logit tiles and form G = (p - onehot) * coef * dz/draw in the
+// input dtype, then contract
 //   grad_hidden += G . W_c        (fp32 accumulator across chunks)
 //   grad_weight[c] = G^T . hidden (complete per chunk, written once)
-// with the same NT GEMM tile (W_c and hidden are transposed into the
-// workspace first so that both operands of every contraction are
-// K-contiguous).  grad_bias sums G over rows per tile, then over tiles in a
-// fixed order.  No atomics: results are deterministic.
+// with the same GEMM tile.  For 16-bit types both contractions read their B
+// operand K-major through transposed LDS fragment reads (G itself for
+// grad_weight, the chunk's weight rows for grad_hidden), so only hidden is
+// transposed, once per call.  The fp32 path, which has no transposed
+// 32-bit fragment read, has the recompute kernel write G^T as well and
+// transposes the chunk's weight rows into W_c^T.  grad_bias sums G over rows
+// per tile, then over tiles in a fixed order.  No atomics: results are
+// deterministic.
 #include <math.h>
 
 #include <type_traits>
@@ -766,7 +770,7 @@ struct WcTSide {
 };
 
 // Recompute one (token tile, vocabulary tile) of the chunk and write
-// G = coef * (softmax - onehot) * dz/draw (and G^T, grad_bias partials).
+// G = coef * (softmax - onehot) * dz/draw (G^T too when asked, grad_bias partials).
 // A = weight rows (vocabulary on the MFMA row axis), B = hidden rows.
 template <int D, bool BIAS, bool CAP, int W>
 __global__ __launch_bounds__(W * 64) void bwd_g_kernel(GArgs a) {

@@ -12,7 +12,7 @@ namespace flce {
 // tile; 4 = one wave per SIMD with 128 x 128 per wave, 8 = two per SIMD with
 // 128 x 64 per wave).
 constexpr int kFwdWaves = 8;        // forward logit tiles
-constexpr int kRecomputeWaves = 8;  // backward recompute (G, G^T, grad_bias partials)
+constexpr int kRecomputeWaves = 8;  // backward recompute (G; G^T on the fp32 path; grad_bias partials)
 constexpr int kContractWaves = 8;   // grad_hidden and grad_weight contractions
 
 // Tile orders (grouped_tile): GA x GB blocks, remapped per XCD or not
@@ -32,8 +32,9 @@ constexpr int kBiasParts = kRecomputeWaves == 8 ? 4 : 2;
 
 // Forward: one workgroup per (token tile, vocabulary split); a split is a run
 // of consecutive 256-id vocabulary tiles whose per-row online state the
-// workgroup carries in registers.  The split size depends on V only, so a
-// row's result does not depend on how many rows share the call.
+// workgroup carries in LDS between tiles (so that the state takes no
+// registers from the K loop).  The split size depends on V only, so a row's
+// result does not depend on how many rows share the call.
 struct FwdArgs {
   const char* hidden;
   const char* weight;

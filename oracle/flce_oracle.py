@@ -226,8 +226,10 @@ def flce_reference(hidden, weight, targets, bias=None, ignore_index=-100,
 
 
 def row_argmax_ids(hidden, weight, bias=None, logit_scale=1.0, softcap=None, row_block=256):
-    """First-index argmax of each row's final logits (used to build targets
-    that equal the row argmax)."""
+    """First-index argmax of each row's final logits z (after bias, scale and
+    soft cap, as in ``transform_logits``); used to build targets that equal
+    the row argmax.  Ties resolve to the smallest id (numpy's argmax), the
+    same reading as the accuracy metric (card: "Metrics for free")."""
     h = _f64(hidden)
     w = _f64(weight)
     b = _f64(bias)
@@ -290,3 +292,118 @@ def gradient_samples(hidden, weight, targets, lse, rows, vocab_ids, bias=None, i
     grad_w = grawc.T @ h
     grad_b = grawc.sum(axis=0)
     return dict(grad_hidden=grad_h, grad_weight=grad_w, grad_bias=grad_b)
+
+
+def _lse_merge(m, s, z):
+    """Folds a block of logits z (R, B) into each row's running maximum m and
+    rescaled sum s = sum_j exp(z_j - m): the online log-sum-exp of the card's
+    "Algorithm" (the old sum is rescaled by exp(m_old - m_new))."""
+    m_new = np.maximum(m, z.max(axis=1))
+    s_new = s * np.exp(m - m_new) + np.exp(z - m_new[:, None]).sum(axis=1)
+    return m_new, s_new
+
+
+def streaming_reference(hidden, weight_rows, vocab, targets, rows=(), vocab_ids=(), bias=None,
+                        ignore_index=-100, logit_scale=1.0, softcap=None, reduction="mean",
+                        grad_output=None, weight_block=65536, row_block=2048):
+    """The loss and selected gradient entries by the definition, in fp64, for
+    shapes whose weight is too large to hold in fp64 at once.
+
+    ``weight_rows(r0, r1)`` returns weight rows r0..r1-1 (values exactly
+    representable in fp64); ``vocab`` is V.  The weight is visited in blocks
+    of ``weight_block`` rows and the tokens in blocks of ``row_block`` rows;
+    every logit is formed from its definition (``transform_logits``) and
+    nothing of size N x V is held.  Same readings as ``flce_reference``
+    (plain cross-entropy; no loss variants).
+
+    Passes:
+      1. lse of every row over the whole vocabulary, merged block by block
+         (``_lse_merge``), and each row's target logit;
+      2. grad_hidden of the selected ``rows``: sum over weight blocks of
+         (p - onehot) * coef * dz/draw times the block's rows (card:
+         "Algorithm", backward);
+      3. grad_weight and grad_bias of the selected ``vocab_ids``: that logit
+         column for every token, (p - onehot) * coef * dz/draw, contracted
+         with hidden.
+
+    Returns a dict: lse (N,), row_loss (N,), loss, n_valid, grad_hidden
+    (len(rows), H), grad_weight (len(vocab_ids), H), grad_bias
+    (len(vocab_ids),) or None without a bias.
+    """
+    if reduction not in ("mean", "sum", "none"):
+        raise ValueError(f"unknown reduction {reduction!r}")
+    h = _f64(hidden)
+    b = _f64(bias)
+    t = np.asarray(targets, dtype=np.int64)
+    n = h.shape[0]
+    v = int(vocab)
+    valid = t != ignore_index
+    if np.any(valid & ((t < 0) | (t >= v))):
+        raise ValueError("target id outside [0, V) on a non-ignored row")
+    n_valid = int(valid.sum())
+    coef = _reduction_coef(reduction, grad_output, valid.astype(np.float64), n)
+
+    def wblock(r0, r1):
+        return np.asarray(weight_rows(r0, r1), dtype=np.float64)
+
+    # pass 1: lse and the target logit of every row
+    m = np.full(n, -np.inf)
+    s = np.zeros(n)
+    zt = np.zeros(n)
+    for v0 in range(0, v, weight_block):
+        v1 = min(v, v0 + weight_block)
+        wb = wblock(v0, v1)
+        bb = None if b is None else b[v0:v1]
+        for r0 in range(0, n, row_block):
+            r1 = min(n, r0 + row_block)
+            z = transform_logits(h[r0:r1] @ wb.T, bb, logit_scale, softcap)
+            m[r0:r1], s[r0:r1] = _lse_merge(m[r0:r1], s[r0:r1], z)
+            tr = t[r0:r1]
+            here = valid[r0:r1] & (tr >= v0) & (tr < v1)
+            idx = np.nonzero(here)[0]
+            zt[r0 + idx] = z[idx, tr[idx] - v0]
+    lse = m + np.log(s)
+    row_loss = np.where(valid, lse - zt, 0.0)
+    if reduction == "none":
+        loss = row_loss.copy()
+    elif reduction == "sum":
+        loss = float(row_loss[valid].sum())
+    else:
+        loss = float(row_loss[valid].sum() / n_valid) if n_valid > 0 else math.nan
+
+    # pass 2: grad_hidden of the selected rows
+    rows = np.asarray(rows, dtype=np.int64)
+    grad_h = np.zeros((len(rows), h.shape[1]))
+    if len(rows):
+        hs = h[rows]
+        for v0 in range(0, v, weight_block):
+            v1 = min(v, v0 + weight_block)
+            wb = wblock(v0, v1)
+            z = transform_logits(hs @ wb.T, None if b is None else b[v0:v1], logit_scale, softcap)
+            gz = np.exp(z - lse[rows, None])
+            for k, i in enumerate(rows):
+                if not valid[i]:
+                    gz[k] = 0.0
+                elif v0 <= t[i] < v1:
+                    gz[k, t[i] - v0] -= 1.0
+            grad_h += (coef[rows, None] * gz * transform_derivative(z, logit_scale, softcap)) @ wb
+
+    # pass 3: grad_weight / grad_bias of the selected vocabulary ids
+    vids = np.asarray(vocab_ids, dtype=np.int64)
+    grad_w = np.zeros((len(vids), h.shape[1]))
+    grad_b = np.zeros(len(vids)) if b is not None else None
+    if len(vids):
+        wv = np.concatenate([wblock(int(j), int(j) + 1) for j in vids], axis=0)
+        bv = None if b is None else b[vids]
+        for r0 in range(0, n, row_block):
+            r1 = min(n, r0 + row_block)
+            zc = transform_logits(h[r0:r1] @ wv.T, bv, logit_scale, softcap)
+            gzc = np.exp(zc - lse[r0:r1, None])
+            gzc -= (t[r0:r1, None] == vids[None, :]) & valid[r0:r1, None]
+            gzc[~valid[r0:r1]] = 0.0
+            graw = coef[r0:r1, None] * gzc * transform_derivative(zc, logit_scale, softcap)
+            grad_w += graw.T @ h[r0:r1]
+            if grad_b is not None:
+                grad_b += graw.sum(axis=0)
+    return dict(lse=lse, row_loss=row_loss, loss=loss, n_valid=n_valid, grad_hidden=grad_h,
+                grad_weight=grad_w, grad_bias=grad_b)

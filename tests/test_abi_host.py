@@ -248,3 +248,40 @@ def test_forward_backward_validates_like_the_two_calls():
     assert _abi.flce_forward_backward(p, FAKE, FAKE, FAKE, 0, FAKE, 0, 0, 0, FAKE, FAKE, FAKE, FAKE, need,
                                       0) == INVALID
     assert "grad_bias" in _abi.last_error()
+
+
+# The default backward plan at the four bf16 workloads (chunk ids, chunks, last chunk).  The
+# chunk is at most a quarter of V and 48 tiles, scored by how full grad_weight's last round of
+# 256 workgroups is; a last chunk under a quarter of a chunk joins the one before it.
+@pytest.mark.parametrize("n,h,v,plan", [
+    (2048, 2048, 32000, (7936, 4, 8192)),       # 31-tile chunks; the 256-id remainder joins the last
+    (4096, 4096, 128256, (12288, 11, 5376)),
+    (8192, 3584, 152064, (12288, 13, 4608)),
+    (16384, 2048, 262144, (8192, 32, 8192)),    # 32 tiles: one full round of 8 x 32 grad_weight tiles
+])
+def test_backward_plan_at_the_workloads(n, h, v, plan):
+    assert _abi.flce_backward_plan(make_problem(n, h, v, BF16)) == plan
+
+
+def test_backward_plan_override_and_invalid():
+    assert _abi.flce_backward_plan(make_problem(4096, 4096, 128256, BF16, bwd_vocab_chunk=4096)) == (4096, 32, 1280)
+    with pytest.raises(_abi.FlceError):
+        _abi.flce_backward_plan(make_problem(64, 100, 1000, BF16))   # 200-byte rows: refused
+
+
+# No buffer of N x V elements: the whole workspace of a forward + backward stays below the bytes
+# of one N x V matrix in the input dtype at every 16-bit workload (the memory claim of the fused
+# method), with and without the all-transforms options.
+@pytest.mark.parametrize("n,h,v,kw", [
+    (2048, 2048, 32000, {}),
+    (4096, 4096, 128256, {}),
+    (8192, 3584, 152064, dict(has_bias=True, logit_scale=0.5, softcap=30.0, reduction="sum",
+                              return_metrics=True)),
+    (16384, 2048, 262144, {}),
+    (16384, 2048, 262144, dict(reduction="none")),
+])
+def test_workspace_below_one_n_by_v_matrix(n, h, v, kw):
+    p = make_problem(n, h, v, BF16, **kw)
+    total = _abi.flce_forward_workspace_size(p) + _abi.flce_backward_workspace_size(p)
+    assert 0 < total < n * v * 2, (total, n * v * 2)
+    assert _abi.flce_forward_backward_workspace_size(p) < n * v * 2

@@ -169,7 +169,23 @@ def test_out_of_range_target_sets_status_and_nan_row():
     lossc = loss.cpu()
     assert math.isnan(lossc[5]) and math.isnan(lossc[9])
     assert torch.isfinite(torch.cat([lossc[:5], lossc[10:]])).all()
-    gh, _, _ = flce.flce_backward(g["hidden"], g["weight"], g["targets"], g["bias"], lse,
-                                  reduction="none")
+    # the documented spread: the bad rows' grad_hidden rows are NaN, the other rows are finite,
+    # and every grad_weight entry is NaN (grad_weight contracts over every row)
+    gh, gw, _ = flce.flce_backward(g["hidden"], g["weight"], g["targets"], g["bias"], lse,
+                                   reduction="none")
     ghc = gh.cpu()
-    assert torch.isnan(ghc[5]).all() and torch.isfinite(ghc[10:]).all()
+    assert torch.isnan(ghc[5]).all() and torch.isnan(ghc[9]).all()
+    assert torch.isfinite(torch.cat([ghc[:5], ghc[6:9], ghc[10:]])).all()
+    assert torch.isnan(gw.cpu()).all()
+    # a mean loss is NaN; with a bias, every grad_bias entry is NaN too
+    wb = W["transforms_bf16"].resized(n=64, h=64, v=600, softcap=None, reduction="mean", return_metrics=False)
+    gb_in = gpu_inputs(fi.generate(wb))
+    gb_in["targets"][3] = 600
+    lossm, lsem, _ = flce.flce_forward(gb_in["hidden"], gb_in["weight"], gb_in["targets"], gb_in["bias"],
+                                       reduction="mean", logit_scale=wb.logit_scale)
+    assert math.isnan(lossm.item())
+    ghm, gwm, gbm = flce.flce_backward(gb_in["hidden"], gb_in["weight"], gb_in["targets"], gb_in["bias"], lsem,
+                                       reduction="mean", logit_scale=wb.logit_scale)
+    ghm = ghm.float().cpu()
+    assert torch.isnan(ghm[3]).all() and torch.isfinite(torch.cat([ghm[:3], ghm[4:]])).all()
+    assert torch.isnan(gwm.float().cpu()).all() and torch.isnan(gbm.float().cpu()).all()

@@ -494,3 +494,81 @@ def test_class_weights_scale_whole_row_loss():
                - base_m) < 1e-12 * abs(base_m)
     assert abs(flce_reference(h, w, t, compute_grads=False, reduction="sum", class_weight=cw, **kw)["loss"]
                - 2.5 * base_s) < 1e-12 * abs(base_s)
+
+
+# --------------------------------------------------------------------------- row argmax targets
+# row_argmax_ids builds the peaked workload's "target = row argmax" rows; it is
+# pinned to torch's argmax (first maximal index) of logits that torch computes
+# itself, with a bias, a scale and a soft cap, and exact ties planted by
+# duplicated weight rows.
+
+def _torch_argmax(h, w, b, s, cap):
+    logits = F.linear(torch.tensor(h), torch.tensor(w), None if b is None else torch.tensor(b)) * s
+    if cap is not None:
+        logits = cap * torch.tanh(logits / cap)
+    return torch.argmax(logits, dim=1).numpy()
+
+
+def test_row_argmax_ids_match_torch():
+    h, w, b, _ = problem(31, 37, 10, 53, bias=True, wstd=0.8)
+    b = b * 10.0                     # a bias large enough to move most rows' argmax
+    w[41] = w[12]                    # exact ties between ids 12 and 41 (same row, same bias)
+    b[41] = b[12]
+    h[5] = w[12] * 3.0               # row 5 peaks on the tied pair
+    for s, cap, bb in [(1.0, None, None), (1.0, None, b), (0.5, 2.0, b), (2.5, 30.0, b)]:
+        got = orc.row_argmax_ids(h, w, bb, s, cap, row_block=8)
+        np.testing.assert_array_equal(got, _torch_argmax(h, w, bb, s, cap))
+    # the tie resolves to the smaller id
+    assert orc.row_argmax_ids(h, w, b, 1.0, None)[5] == 12
+    # zero weight: every row is an all-way tie, so every argmax is id 0
+    assert np.all(orc.row_argmax_ids(h, np.zeros_like(w)) == 0)
+
+
+def test_mutation_argmax_of_raw_logits_is_caught(monkeypatch):
+    monkeypatch.setattr(orc, "transform_logits", lambda raw, bias, s, cap: raw)
+    _pins_fail(test_row_argmax_ids_match_torch)
+
+
+def test_mutation_argmax_without_bias_is_caught(monkeypatch):
+    real = orc.transform_logits
+    monkeypatch.setattr(orc, "transform_logits", lambda raw, bias, s, cap: real(raw, None, s, cap))
+    _pins_fail(test_row_argmax_ids_match_torch)
+
+
+# --------------------------------------------------------------------------- streaming reference
+# streaming_reference serves shapes whose weight cannot be held in fp64 at
+# once.  It is pinned to torch (logsumexp, cross_entropy, autograd) directly,
+# with weight and token blocks that do not divide the sizes.
+
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+def test_streaming_reference_matches_torch(reduction):
+    h, w, b, t = problem(41, 29, 12, 61, bias=True, ignore_frac=0.2, wstd=1.2)
+    g = np.random.default_rng(3).standard_normal(29) if reduction == "none" else 0.8
+    rows = [0, 4, 17, 28] + list(np.nonzero(t == -100)[0][:1])
+    vids = [0, 7, int(t[t >= 0][0]), 60]
+    for s, cap, bb in [(1.0, None, None), (0.6, 3.0, b), (1.0, None, b)]:
+        out = orc.streaming_reference(h, lambda r0, r1: w[r0:r1], 61, t, rows, vids, bb,
+                                      logit_scale=s, softcap=cap, reduction=reduction, grad_output=g,
+                                      weight_block=7, row_block=5)
+        th = torch.tensor(h)
+        logits = F.linear(th, torch.tensor(w), None if bb is None else torch.tensor(bb)) * s
+        if cap is not None:
+            logits = cap * torch.tanh(logits / cap)
+        np.testing.assert_allclose(out["lse"], torch.logsumexp(logits, dim=1).numpy(), rtol=1e-12)
+        ref_loss, gh, gw, gb = torch_loss(h, w, bb, t, -100, s, cap, reduction, g)
+        np.testing.assert_allclose(out["loss"], ref_loss, rtol=1e-11, atol=1e-14)
+        np.testing.assert_allclose(out["grad_hidden"], gh[rows], rtol=1e-10, atol=1e-13)
+        np.testing.assert_allclose(out["grad_weight"], gw[vids], rtol=1e-10, atol=1e-13)
+        if bb is not None:
+            np.testing.assert_allclose(out["grad_bias"], gb[vids], rtol=1e-10, atol=1e-13)
+        else:
+            assert out["grad_bias"] is None
+
+
+def test_mutation_streaming_merge_without_rescale_is_caught(monkeypatch):
+    def wrong(m, s, z):
+        m_new = np.maximum(m, z.max(axis=1))
+        return m_new, s + np.exp(z - m_new[:, None]).sum(axis=1)   # old sum not rescaled
+    monkeypatch.setattr(orc, "_lse_merge", wrong)
+    _pins_fail(lambda: test_streaming_reference_matches_torch("mean"))
+
