@@ -160,6 +160,24 @@ flce_status_t flce_forward(const flce_problem_t* p, const void* hidden, const vo
                            float* metrics, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* The forward pass without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments and results as
+ * flce_forward (bit for bit), but the workspace is a fixed array of 32 MiB
+ * per device inside the library, held until the process ends; the call
+ * allocates nothing.  Problems whose forward workspace
+ * (flce_forward_workspace_size) exceeds 32 MiB return FLCE_ERR_WORKSPACE
+ * before anything is launched (e.g. a strided hidden layout that must be
+ * gathered at N*H*sizeof(dtype) > ~30 MiB).  `stream` must belong to the
+ * current device.  Every call on a device shares that device's array: calls
+ * that overlap on one device (other streams, other threads) race and must
+ * be ordered by the caller.  The device status word it writes lives in that
+ * array, so flce_forward_status cannot read it; an out-of-range target still
+ * shows as a NaN row loss. */
+flce_status_t flce_forward_noalloc(const flce_problem_t* p, const void* hidden, const void* weight,
+                                   const int64_t* targets, const void* bias, float* loss, float* lse,
+                                   float* metrics, void* stream);
+
 /* Backward pass (card: "Algorithm", backward: recompute each logit tile,
  * form p - onehot, accumulate the three gradients).
  *   lse:        in, [N] from flce_forward with the same problem and inputs.

@@ -68,6 +68,7 @@ _SIGNATURES = {
     "flce_forward": (ctypes.c_int, [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
     "flce_backward": (ctypes.c_int, [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                      ctypes.c_size_t, _VP]),
+    "flce_forward_noalloc": (ctypes.c_int, [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "flce_forward_backward_workspace_size": (ctypes.c_size_t, [_PP]),
     "flce_forward_backward": (ctypes.c_int, [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                              _VP, ctypes.c_size_t, _VP]),
@@ -139,6 +140,12 @@ def flce_forward(p: Problem, hidden, weight, targets, bias, loss, lse, metrics, 
     """Raw call with integer device addresses (0 = NULL); returns the status."""
     return library().flce_forward(ctypes.byref(p), hidden, weight, targets, bias, loss, lse,
                                   metrics, workspace, workspace_bytes, stream)
+
+
+def flce_forward_noalloc(p: Problem, hidden, weight, targets, bias, loss, lse, metrics, stream) -> int:
+    """Raw call of the allocation-free forward (workspace inside the library)."""
+    return library().flce_forward_noalloc(ctypes.byref(p), hidden, weight, targets, bias, loss, lse,
+                                          metrics, stream)
 
 
 def flce_forward_backward_workspace_size(p: Problem) -> int:

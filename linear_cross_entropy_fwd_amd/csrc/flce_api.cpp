@@ -441,6 +441,22 @@ flce_status_t flce_forward(const flce_problem_t* p, const void* hidden, const vo
   return FLCE_OK;
 }
 
+flce_status_t flce_forward_noalloc(const flce_problem_t* p, const void* hidden, const void* weight,
+                                   const int64_t* targets, const void* bias, float* loss, float* lse,
+                                   float* metrics, void* stream) {
+  const flce_status_t s = check_problem(p);
+  if (s != FLCE_OK) return s;
+  const size_t need = fwd_layout(*p).total;
+  if (need > flce::kScratchBytes)
+    return fail(FLCE_ERR_WORKSPACE,
+                "flce_forward_noalloc: this problem needs %zu bytes of workspace; the fixed scratch holds %zu "
+                "(use flce_forward with a workspace)", need, flce::kScratchBytes);
+  void* ws = nullptr;
+  const hipError_t e = flce::scratch_address(&ws);
+  if (e != hipSuccess) return hip_fail(e, "scratch address");
+  return flce_forward(p, hidden, weight, targets, bias, loss, lse, metrics, ws, flce::kScratchBytes, stream);
+}
+
 // The backward's argument checks (no launch): flce_backward and
 // flce_forward_backward run them before anything is enqueued.
 static flce_status_t check_backward_args(const flce_problem_t* p, const void* hidden, const void* weight,

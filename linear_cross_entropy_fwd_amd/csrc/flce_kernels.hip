@@ -26,6 +26,7 @@
 // deterministic.
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "flce_device.h"
@@ -1417,6 +1418,35 @@ hipError_t launch_gather_targets(const GatherTargetsArgs& a, hipStream_t st) {
   if (a.N <= 0) return hipSuccess;
   hipLaunchKernelGGL(gather_targets_kernel, dim3(blocks_for(a.N, 256)), dim3(256), 0, st, a);
   return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ fixed scratch
+
+// The workspace of the allocation-free forward entry point: one array per
+// device, of kScratchBytes, alive until the process ends.  Host code never
+// passes this name to a kernel (on the host it is only a stand-in for the
+// symbol): it takes the device address hipGetSymbolAddress gives, once per
+// device, with that device current.  Every call on a device shares the
+// array, so calls that overlap on one device race.
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+hipError_t scratch_address(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace flce

@@ -191,4 +191,10 @@ hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t st);
 hipError_t launch_gather_rows(const GatherRowsArgs& a, hipStream_t st);
 hipError_t launch_gather_targets(const GatherTargetsArgs& a, hipStream_t st);
 
+// The allocation-free forward's fixed workspace (a device array of this many
+// bytes in flce_kernels.hip): its device address on the current device,
+// looked up once per device.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+hipError_t scratch_address(void** out);
+
 }  // namespace flce

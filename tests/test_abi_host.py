@@ -285,3 +285,13 @@ def test_workspace_below_one_n_by_v_matrix(n, h, v, kw):
     total = _abi.flce_forward_workspace_size(p) + _abi.flce_backward_workspace_size(p)
     assert 0 < total < n * v * 2, (total, n * v * 2)
     assert _abi.flce_forward_backward_workspace_size(p) < n * v * 2
+
+
+def test_noalloc_forward_refuses_past_its_scratch_before_any_launch():
+    # 64 splits x 7 partials x 20000 rows x 4 B: more than the fixed 32 MiB scratch
+    p = make_problem(20000, 128, 262144, BF16)
+    assert _abi.flce_forward_workspace_size(p) > 32 << 20
+    st = _abi.flce_forward_noalloc(p, FAKE, FAKE, FAKE, 0, FAKE, FAKE, 0, 0)
+    assert st == WORKSPACE and "fixed scratch" in _abi.last_error()
+    # invalid problems get the forward's own status first
+    assert _abi.flce_forward_noalloc(base(h=30), FAKE, FAKE, FAKE, 0, FAKE, FAKE, 0, 0) == UNSUPPORTED
