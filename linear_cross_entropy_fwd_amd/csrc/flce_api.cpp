@@ -230,6 +230,10 @@ struct BwdLayout {
   int n_chunks, n_tok_tiles, n_h_tiles, dh_split, dh_pair;
   bool gk;  // grad_weight reads G K-major (no G^T buffer)
   bool dk;  // grad_hidden reads the weight rows K-major (no W_c^T buffer)
+  // gk and dk: one launch per chunk runs the recompute of the next chunk with
+  // both contractions of the last one (bwd_step_kernel), so G is kept twice
+  // (the chunk, or pair of chunks, being contracted and the one being written)
+  bool fused;
   TokLayout tok;
   size_t off_scale, off_ht, off_wct, off_g, off_gt, off_dh, off_db, off_hrows, off_tgt, total;
 };
@@ -270,28 +274,35 @@ BwdLayout bwd_layout(const flce_problem_t& p) {
     off = (size_t)round_up((int64_t)(off + bytes), kAlign);
     return o;
   };
-  L.off_scale = take(16);
-  L.off_ht = take((size_t)H * L.npad * eb);
   // 16-bit types: grad_hidden reads the chunk's weight rows as a K-major
   // operand, so W_c^T is neither written (the recompute kernel's side job,
   // 22 us of its time a chunk at the head shape) nor read.  Its copy offsets
   // span a pair's K ids plus two stages of weight rows.
   L.dk = eb == 2 && (L.gld + 128) * H * eb + 512 < (int64_t(1) << 32);
-  L.off_wct = take(L.dk ? 0 : (size_t)H * L.gld * eb);
-  L.off_g = take((size_t)L.npad * L.gld * eb);
   // 16-bit types: grad_weight reads G itself as a K-major operand, so the
   // recompute kernel writes no G^T (measured 29 us of its 348 us a chunk at
   // the head shape).  The tile's 32-bit copy offsets must reach two stages
   // past the last token row.
   L.gk = eb == 2 && (L.npad + 128) * L.gld * eb + 512 < (int64_t(1) << 32);
+  L.fused = L.dk && L.gk;
+  L.off_scale = take(16);
+  L.off_ht = take((size_t)H * L.npad * eb);
+  L.off_wct = take(L.dk ? 0 : (size_t)H * L.gld * eb);
+  L.off_g = take((size_t)(L.fused ? 2 : 1) * L.npad * L.gld * eb);
   L.off_gt = take(L.gk ? 0 : (size_t)L.cvpad_max * L.npad * eb);
   // grad_hidden's grid is token tiles x hidden tiles; when that is a small
   // part of the CUs, the chunk's K is split over 2 or 4 workgroups per tile,
   // each into an accumulator of its own, summed in a fixed order at the end.
+  // In the one-launch steps grad_hidden shares the CUs with the other two
+  // parts, so it only needs its workgroups no longer than a few of theirs:
+  // 2 splits up to a quarter of the CUs' worth of tiles, else none.
   // (Rows of grad_hidden then depend on N only through this split: calls
   // whose grids fall in the same class give bit-identical rows.)
   const int64_t dh_tiles = (int64_t)L.n_tok_tiles * L.n_h_tiles;
-  L.dh_split = dh_tiles <= kCUs / 4 ? 4 : dh_tiles <= kCUs / 2 ? 2 : 1;
+  if (L.fused)
+    L.dh_split = dh_tiles <= kCUs / 4 ? 2 : 1;
+  else
+    L.dh_split = dh_tiles <= kCUs / 4 ? 4 : dh_tiles <= kCUs / 2 ? 2 : 1;
   // (the K-major grad_hidden kernel keeps whole 256 x 256 tiles)
   const int64_t acc_elems = L.dk ? (int64_t)L.n_tok_tiles * L.n_h_tiles * kTile * kTile : N * H;
   L.off_dh = take(L.n_chunks > L.dh_pair || L.dh_split > 1 ? (size_t)L.dh_split * acc_elems * 4 : 0);
@@ -487,6 +498,91 @@ static flce_status_t check_backward_args(const flce_problem_t* p, const void* hi
   return FLCE_OK;
 }
 
+// The backward of the 16-bit K-major path as n_chunks + 1 launches of
+// bwd_step_kernel: launch k recomputes chunk k (if k < n_chunks) into G
+// buffer (k / dh_pair) % 2 and contracts chunk k - 1 (grad_weight, and
+// grad_hidden once its pair is complete), which an earlier launch wrote into
+// the other buffer or into the other column slot of the same pair.
+static hipError_t backward_fused(const flce_problem_t& p, const BwdLayout& L, const flce::GArgs& gbase,
+                                 const char* weight, const char* ht, char* g, float* dh, const float* scale,
+                                 void* grad_hidden, void* grad_weight, bool want_dh, bool want_dw, hipStream_t st) {
+  const int64_t H = p.hidden, V = p.vocab;
+  const int eb = elem_bytes(p.dtype);
+  const int geb = p.grad_weight_fp32 ? 4 : eb;
+  const size_t gbuf = (size_t)L.npad * L.gld * eb;
+  auto chunk_cv = [&](int c) { return (int)(c == L.n_chunks - 1 ? L.last_chunk : L.chunk); };
+  auto g_of = [&](int c) {  // this chunk's G columns: its pair's buffer, its slot in the pair
+    const int pair = c / L.dh_pair, slot = c % L.dh_pair;
+    return g + (size_t)(pair % 2) * gbuf + (size_t)(slot == 0 ? 0 : L.cvpad_reg) * eb;
+  };
+  hipError_t e;
+  for (int k = 0; k <= L.n_chunks; ++k) {
+    flce::StepArgs sa{};
+    if (k < L.n_chunks) {
+      const int cv = chunk_cv(k);
+      sa.g = gbase;
+      sa.g.G = (want_dh || want_dw) ? g_of(k) : nullptr;
+      sa.g.c0 = (int64_t)k * L.chunk;
+      sa.g.cv = cv;
+      sa.g.cvpad = (int)round_up(cv, 64);
+      sa.g.n_voc_tiles = (int)cdiv(cv, kTile);
+      sa.nb_g = flce::backward_g_grid(L.n_tok_tiles, sa.g.n_voc_tiles);
+    }
+    const int c = k - 1;  // the chunk contracted in this launch
+    if (c >= 0 && want_dw) {
+      const int cv = chunk_cv(c);
+      flce::DwArgs& wa = sa.dw;
+      wa.GT = g_of(c);
+      wa.gk = 1;
+      wa.gld = (int)L.gld;
+      wa.HT = ht;
+      wa.out = reinterpret_cast<char*>(grad_weight) + (int64_t)c * L.chunk * H * geb;
+      wa.out_f32 = p.grad_weight_fp32;
+      wa.scale = scale;
+      wa.H = H;
+      wa.cv = cv;
+      wa.npad = (int)L.npad;
+      wa.n_voc_tiles = (int)cdiv(cv, kTile);
+      wa.n_h_tiles = L.n_h_tiles;
+      sa.nb_dw = flce::backward_dw_grid(L.n_h_tiles, wa.n_voc_tiles);
+    }
+    const int slot = c >= 0 ? c % L.dh_pair : 0;
+    if (c >= 0 && want_dh && (slot == L.dh_pair - 1 || c == L.n_chunks - 1)) {
+      const int pair = c / L.dh_pair;
+      const int64_t col = slot == 0 ? 0 : L.cvpad_reg;
+      flce::DhArgs& da = sa.dh;
+      da.G = g + (size_t)(pair % 2) * gbuf;
+      da.WcT = nullptr;
+      da.acc = dh;
+      da.out = reinterpret_cast<char*>(grad_hidden);
+      da.scale = scale;
+      da.N = p.n_tokens;
+      da.H = H;
+      da.ld = (int)L.gld;
+      da.kdim = (int)(col + round_up(chunk_cv(c), 64));
+      da.n_tok_tiles = L.n_tok_tiles;
+      da.n_h_tiles = L.n_h_tiles;
+      da.first = pair == 0;
+      da.last = c == L.n_chunks - 1;
+      da.ksplit = L.dh_split;
+      da.kpart = (int)round_up(cdiv(da.kdim, L.dh_split), 64);
+      da.acc_stride = (int64_t)L.n_tok_tiles * L.n_h_tiles * kTile * kTile;
+      da.bk = 1;
+      da.Wk = weight + (int64_t)(c - slot) * L.chunk * H * eb;
+      da.wrows = V - (int64_t)(c - slot) * L.chunk;
+      sa.dh_grid = flce::backward_dh_grid(L.n_h_tiles, L.n_tok_tiles);
+      sa.nb_dh = sa.dh_grid * L.dh_split;
+    }
+    if ((e = flce::launch_backward_step(p.dtype, p.has_bias != 0, p.softcap > 0.f, sa, st)) != hipSuccess) return e;
+    if (sa.nb_dh > 0 && sa.dh.last && L.dh_split > 1) {
+      flce::DhFinalArgs fa{dh, scale, reinterpret_cast<char*>(grad_hidden), sa.dh.acc_stride, sa.dh.acc_stride,
+                           L.dh_split, 1, p.n_tokens, H, L.n_h_tiles};
+      if ((e = flce::launch_backward_dh_final(p.dtype, fa, st)) != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
 flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const void* weight,
                             const int64_t* targets, const void* bias, const float* lse,
                             const float* grad_loss, void* grad_hidden, void* grad_weight,
@@ -536,7 +632,38 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
     flce::TransposeArgs ta{in.hidden, ht, N, H, H, L.npad, L.npad};
     if ((e = flce::launch_transpose(p->dtype, ta, st)) != hipSuccess) return hip_fail(e, "transpose kernel");
   }
-  for (int c = 0; c < L.n_chunks; ++c) {
+  if (L.fused) {
+    flce::GArgs gb{};
+    gb.hidden = in.hidden;
+    gb.weight = reinterpret_cast<const char*>(weight);
+    gb.bias = reinterpret_cast<const char*>(bias);
+    gb.targets = targets;
+    gb.lse = lse;
+    gb.grad_rows = p->reduction == FLCE_NONE ? grad_loss : nullptr;
+    gb.GT = nullptr;
+    gb.WcT = nullptr;
+    gb.g_ld = (int)L.gld;
+    gb.wct_ld = (int)L.gld;
+    gb.dbpart = want_db ? db : nullptr;
+    gb.N = N;
+    gb.H = H;
+    gb.V = V;
+    gb.ignore_index = p->ignore_index;
+    gb.npad = (int)L.npad;
+    gb.n_tok_tiles = L.n_tok_tiles;
+    gb.none_reduction = p->reduction == FLCE_NONE;
+    gb.s = p->logit_scale;
+    gb.cap = cap_of(*p);
+    gb.inv_cap = 1.f / gb.cap;
+    gb.class_weight = p->class_weight;
+    gb.eps_v = p->label_smoothing / (float)V;
+    gb.keep = 1.f - p->label_smoothing;
+    gb.zl2 = 2.f * p->z_loss;
+    if ((e = backward_fused(*p, L, gb, reinterpret_cast<const char*>(weight), ht, g, dh, scale, grad_hidden,
+                            grad_weight, want_dh, want_dw, st)) != hipSuccess)
+      return hip_fail(e, "backward step kernel");
+  }
+  for (int c = 0; c < (L.fused ? 0 : L.n_chunks); ++c) {
     const int64_t c0 = (int64_t)c * L.chunk;
     const int cv = (int)(c == L.n_chunks - 1 ? L.last_chunk : L.chunk);
     const int cvpad = (int)round_up(cv, 64);

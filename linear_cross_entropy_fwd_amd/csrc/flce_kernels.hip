@@ -773,15 +773,17 @@ struct WcTSide {
 // Recompute one (token tile, vocabulary tile) of the chunk and write
 // G = coef * (softmax - onehot) * dz/draw (G^T too when asked, grad_bias partials).
 // A = weight rows (vocabulary on the MFMA row axis), B = hidden rows.
-template <int D, bool BIAS, bool CAP, int W>
-__global__ __launch_bounds__(W * 64) void bwd_g_kernel(GArgs a) {
+// Workgroup `bid` of a grid of `nblocks` (the tile order of grouped_tile).
+// WCT: the W_c^T side job may be asked for (16-bit types).
+template <int D, bool BIAS, bool CAP, int W, bool WCT>
+__device__ __forceinline__ void g_tile(const GArgs& a, int bid, int nblocks) {
   typedef typename Elem<D>::T T;
   constexpr int EB = Elem<D>::bytes, WI = Gemm<W>::WI, WJ = Gemm<W>::WJ;
   static_assert(Gemm<W>::GN == kBiasParts || W != kRecomputeWaves, "grad_bias partials per token tile");
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = Gemm<W>::wm(wave), wn = Gemm<W>::wn(wave), c16 = lane & 15, q = lane >> 4;
 
-  const TileAB ti = grouped_tile<kRecGA, kRecGB, kRecXcd>(blockIdx.x, gridDim.x, a.n_tok_tiles, a.n_voc_tiles);
+  const TileAB ti = grouped_tile<kRecGA, kRecGB, kRecXcd>(bid, nblocks, a.n_tok_tiles, a.n_voc_tiles);
   if (!ti.valid) return;
   const int tt = ti.a, vt = ti.b;
   const int64_t n0 = (int64_t)tt * TILE;
@@ -792,7 +794,7 @@ __global__ __launch_bounds__(W * 64) void bwd_g_kernel(GArgs a) {
   Panel A{a.weight + v0 * rowb, rowb, (int)min<int64_t>(TILE, a.V - v0), rowb};
   Panel B{a.hidden + n0 * rowb, rowb, (int)min<int64_t>(TILE, a.N - n0), rowb};
   f32x4_t acc[WI][WJ];
-  if constexpr (EB == 2) {
+  if constexpr (EB == 2 && WCT) {
     // no W_c^T wanted: a first stage past every stage selects none
     WcTSide side{reinterpret_cast<uint16_t*>(a.WcT), a.H, a.cvpad, a.wct_ld, vl0, a.n_tok_tiles,
                  (uint32_t)__builtin_amdgcn_readfirstlane(t >> 6), a.WcT != nullptr ? tt : (1 << 30), 0ull};
@@ -994,6 +996,11 @@ __global__ __launch_bounds__(W * 64) void bwd_g_kernel(GArgs a) {
   }
 }
 
+template <int D, bool BIAS, bool CAP, int W>
+__global__ __launch_bounds__(W * 64) void bwd_g_kernel(GArgs a) {
+  g_tile<D, BIAS, CAP, W, true>(a, blockIdx.x, gridDim.x);
+}
+
 // ------------------------------------------------------------------ backward contractions
 
 template <int D>
@@ -1017,24 +1024,26 @@ __device__ __forceinline__ void store4(typename Elem<D>::T* p, float x0, float x
 // grad_hidden[n][h] (+)= scale * sum_v G[n][v] W[v][h] over one vocabulary
 // chunk: A = W_c^T (h rows), B = G (n rows), K = the chunk.  The fp32
 // accumulator is read and written 16 bytes per lane.
+// Workgroup `bid` of a grid of `nblocks` (the tile order of grouped_tile), K
+// split `ks`.
 template <int D, int W, bool BK>
-__global__ __launch_bounds__(W * 64) void bwd_dh_kernel(DhArgs a) {
+__device__ __forceinline__ void dh_tile(const DhArgs& a, int bid, int nblocks, int ks) {
   typedef typename Elem<D>::T T;
   constexpr int EB = Elem<D>::bytes, WI = Gemm<W>::WI, WJ = Gemm<W>::WJ;
-  const TileAB ti = grouped_tile<kDhGA, kDhGB, kDhXcd>(blockIdx.x, gridDim.x, a.n_h_tiles, a.n_tok_tiles);
+  const TileAB ti = grouped_tile<kDhGA, kDhGB, kDhXcd>(bid, nblocks, a.n_h_tiles, a.n_tok_tiles);
   if (!ti.valid) return;
   const int ht = ti.a, tt = ti.b;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = Gemm<W>::wm(wave), wn = Gemm<W>::wn(wave), c16 = lane & 15, q = lane >> 4;
   const int64_t n0 = (int64_t)tt * TILE, h0 = (int64_t)ht * TILE;
   const int64_t kb = (int64_t)a.ld * EB;
-  // split blockIdx.y takes ids [k0, k0 + kn) of the chunk into its own accumulator
-  const int k0 = (int)blockIdx.y * a.kpart, kn = min(a.kpart, a.kdim - k0);
+  // split ks takes ids [k0, k0 + kn) of the chunk into its own accumulator
+  const int k0 = ks * a.kpart, kn = min(a.kpart, a.kdim - k0);
   // The chunks' contributions accumulate unscaled; the running sum is read
   // into the accumulators before the K loop (its loads overlap the first
   // stages' copies instead of following the last MFMA), and the scale is
   // applied once, when grad_hidden is written.
-  float* accbuf = a.acc + (int64_t)blockIdx.y * a.acc_stride;
+  float* accbuf = a.acc + (int64_t)ks * a.acc_stride;
   f32x4_t acc[WI][WJ];
   if constexpr (BK) {
     // Tokens on the MFMA row axis (A = G), hidden on the column axis (B = the
@@ -1133,6 +1142,11 @@ __global__ __launch_bounds__(W * 64) void bwd_dh_kernel(DhArgs a) {
   }
 }
 
+template <int D, int W, bool BK>
+__global__ __launch_bounds__(W * 64) void bwd_dh_kernel(DhArgs a) {
+  dh_tile<D, W, BK>(a, blockIdx.x, gridDim.x, blockIdx.y);
+}
+
 // grad_hidden = scale * (sum over s = 0, 1, ... of the split accumulators,
 // in that order), four elements per thread.
 template <int D>
@@ -1186,9 +1200,9 @@ __global__ __launch_bounds__(256) void bwd_dh_final_kernel(DhFinalArgs a) {
 // inputs, or out_f32) are stored straight from the accumulators, each
 // quarter-wave writing 64 contiguous bytes of one row.
 template <int D, int W, bool BK>
-__global__ __launch_bounds__(W * 64) void bwd_dw_kernel(DwArgs a) {
+__device__ __forceinline__ void dw_tile(const DwArgs& a, int bid, int nblocks) {
   constexpr int EB = Elem<D>::bytes, WI = Gemm<W>::WI, WJ = Gemm<W>::WJ;
-  const TileAB ti = grouped_tile<kDwGA, kDwGB, kDwXcd>(blockIdx.x, gridDim.x, a.n_h_tiles, a.n_voc_tiles);
+  const TileAB ti = grouped_tile<kDwGA, kDwGB, kDwXcd>(bid, nblocks, a.n_h_tiles, a.n_voc_tiles);
   if (!ti.valid) return;
   const int ht = ti.a, vt = ti.b;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -1235,6 +1249,35 @@ __global__ __launch_bounds__(W * 64) void bwd_dw_kernel(DwArgs a) {
             acc[i][j][0] * scale, acc[i][j][1] * scale, acc[i][j][2] * scale, acc[i][j][3] * scale);
     }
   }
+}
+
+template <int D, int W, bool BK>
+__global__ __launch_bounds__(W * 64) void bwd_dw_kernel(DwArgs a) {
+  dw_tile<D, W, BK>(a, blockIdx.x, gridDim.x);
+}
+
+// One backward step of the 16-bit K-major path in one launch: grad_hidden of
+// a finished chunk (or pair of chunks), grad_weight of the last finished
+// chunk and the recompute of the next chunk into the other G buffer.  The
+// three grids are laid end to end (grad_hidden's, the longest workgroups,
+// first); each part's size is a multiple of 32, so a workgroup's XCD
+// (block id mod 8) is the same as in a launch of its own.  The parts touch
+// disjoint outputs and read only G written by an earlier launch.
+template <int D, bool BIAS, bool CAP>
+__global__ __launch_bounds__(kContractWaves * 64) void bwd_step_kernel(StepArgs a) {
+  static_assert(kContractWaves == kRecomputeWaves, "one workgroup shape for every part");
+  int b = blockIdx.x;
+  if (b < a.nb_dh) {
+    dh_tile<D, kContractWaves, true>(a.dh, b % a.dh_grid, a.dh_grid, b / a.dh_grid);
+    return;
+  }
+  b -= a.nb_dh;
+  if (b < a.nb_dw) {
+    dw_tile<D, kContractWaves, true>(a.dw, b, a.nb_dw);
+    return;
+  }
+  b -= a.nb_dw;
+  g_tile<D, BIAS, CAP, kRecomputeWaves, false>(a.g, b, a.nb_g);
 }
 
 template <int D>
@@ -1387,6 +1430,29 @@ hipError_t launch_backward_dw(int dtype, const DwArgs& a, hipStream_t st) {
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int D>
+static hipError_t step_dispatch(bool bias, bool cap, const StepArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)(a.nb_dh + a.nb_dw + a.nb_g)), block(kContractWaves * 64);
+  if (!bias && !cap) hipLaunchKernelGGL((bwd_step_kernel<D, false, false>), grid, block, 0, st, a);
+  else if (!bias && cap) hipLaunchKernelGGL((bwd_step_kernel<D, false, true>), grid, block, 0, st, a);
+  else if (bias && !cap) hipLaunchKernelGGL((bwd_step_kernel<D, true, false>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((bwd_step_kernel<D, true, true>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+int backward_g_grid(int n_tok_tiles, int n_voc_tiles) { return grouped_grid<kRecGA, kRecGB>(n_tok_tiles, n_voc_tiles); }
+int backward_dh_grid(int n_h_tiles, int n_tok_tiles) { return grouped_grid<kDhGA, kDhGB>(n_h_tiles, n_tok_tiles); }
+int backward_dw_grid(int n_h_tiles, int n_voc_tiles) { return grouped_grid<kDwGA, kDwGB>(n_h_tiles, n_voc_tiles); }
+
+hipError_t launch_backward_step(int dtype, bool bias, bool cap, const StepArgs& a, hipStream_t st) {
+  if (a.nb_dh + a.nb_dw + a.nb_g == 0) return hipSuccess;
+  switch (dtype) {
+    case DT_F16: return step_dispatch<DT_F16>(bias, cap, a, st);
+    case DT_BF16: return step_dispatch<DT_BF16>(bias, cap, a, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_backward_db(int dtype, const DbArgs& a, hipStream_t st) {

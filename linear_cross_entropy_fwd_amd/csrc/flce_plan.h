@@ -175,6 +175,16 @@ struct DbArgs {
   int out_f32;       // 1: out is fp32 whatever the input dtype
 };
 
+// One launch of the 16-bit K-major backward: nb_dh grad_hidden workgroups
+// (dh_grid per K split), then nb_dw grad_weight workgroups, then nb_g
+// recompute workgroups; a part with 0 workgroups is skipped.
+struct StepArgs {
+  GArgs g;
+  DwArgs dw;
+  DhArgs dh;
+  int nb_dh, dh_grid, nb_dw, nb_g;
+};
+
 // Launchers (flce_kernels.hip).  All asynchronous on `st`.
 hipError_t launch_forward_tiles(int dtype, bool metrics, bool bias, bool cap, const FwdArgs& a,
                                 hipStream_t st);
@@ -187,6 +197,11 @@ hipError_t launch_backward_dh(int dtype, const DhArgs& a, hipStream_t st);
 hipError_t launch_backward_dh_final(int dtype, const DhFinalArgs& a, hipStream_t st);
 hipError_t launch_backward_dw(int dtype, const DwArgs& a, hipStream_t st);
 hipError_t launch_backward_db(int dtype, const DbArgs& a, hipStream_t st);
+hipError_t launch_backward_step(int dtype, bool bias, bool cap, const StepArgs& a, hipStream_t st);
+// Grid sizes (workgroups, padded to whole tile groups) of the three parts.
+int backward_g_grid(int n_tok_tiles, int n_voc_tiles);
+int backward_dh_grid(int n_h_tiles, int n_tok_tiles);
+int backward_dw_grid(int n_h_tiles, int n_voc_tiles);
 hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t st);
 hipError_t launch_gather_rows(const GatherRowsArgs& a, hipStream_t st);
 hipError_t launch_gather_targets(const GatherTargetsArgs& a, hipStream_t st);

@@ -72,14 +72,20 @@ def test_headvocab_shape_multichunk_bf16():
     run_case(W["headvocab_bf16"].resized(n=512, h=512, v=8200), bwd_vocab_chunk=2048)
 
 
-@pytest.mark.parametrize("n,h,split", [(2304, 2048, 2), (4352, 2048, 1), (1030, 512, 4)])
-def test_grad_hidden_k_split_classes(n, h, split):
+@pytest.mark.parametrize("n,h,dtype,split", [(2304, 2048, "bf16", 1), (1030, 512, "bf16", 2),
+                                             (1030, 512, "f32", 4), (4352, 1024, "f32", 2), (4352, 2048, "f32", 1)])
+def test_grad_hidden_k_split_classes(n, h, dtype, split):
     """grad_hidden's grid (token tiles x hidden tiles) picks how many
-    workgroups share each tile's K: 72 tiles -> 2, 136 -> 1, 15 -> 4; each
-    class against the oracle over several chunks."""
+    workgroups share each tile's K.  16-bit types, where grad_hidden shares
+    its launches with the recompute and grad_weight: up to 64 tiles -> 2,
+    more -> 1.  fp32, launched alone: up to 64 -> 4, up to 128 -> 2, more
+    -> 1.  Each class against the oracle over several chunks."""
     tiles = -(-n // 256) * -(-h // 256)
-    assert split == (4 if tiles <= 64 else 2 if tiles <= 128 else 1)
-    run_case(W["midvocab_bf16"].resized(n=n, h=h, v=1300), bwd_vocab_chunk=512)
+    if dtype == "f32":
+        assert split == (4 if tiles <= 64 else 2 if tiles <= 128 else 1)
+    else:
+        assert split == (2 if tiles <= 64 else 1)
+    run_case(W["midvocab_bf16"].resized(n=n, h=h, v=1300, dtype=dtype), bwd_vocab_chunk=512)
 
 
 @pytest.mark.parametrize("v,dtype", [(5000, "bf16"), (4700, "f16"), (4700, "f32")])
