@@ -33,6 +33,7 @@ PEAK_BF16_TFLOPS = 2516.6          # MI355X dense bf16 MFMA (256 CU x 4096 flop/
 PEAK_TFLOPS = {"bf16": PEAK_BF16_TFLOPS, "f16": PEAK_BF16_TFLOPS, "f32": 157.3}  # dense MFMA per dtype
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["linear_cross_entropy_fwd_amd/csrc/flce_kernels.hip",
+                  "linear_cross_entropy_fwd_amd/csrc/flce_small.hip",
                   "linear_cross_entropy_fwd_amd/csrc/flce_device.h"]
 
 
@@ -44,8 +45,8 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_file(workload_key: str) -> str:
-    return os.path.join(ROOT, "profiles", f"fwd_tiles_{workload_key}_traffic.json")
+def traffic_file(kernel: str, workload_key: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{kernel}_{workload_key}_traffic.json")
 
 
 def kernel_template(dtype: str, metrics: bool, bias: bool, cap: bool) -> str:
@@ -53,15 +54,16 @@ def kernel_template(dtype: str, metrics: bool, bias: bool, cap: bool) -> str:
     return f"{dtype}, metrics={int(metrics)}, bias={int(bias)}, softcap={int(cap)}"
 
 
-def stored_traffic(workload_key: str, template: str, variants: bool):
-    """HBM bytes per forward-tile launch from the committed counter runs of
-    this workload and kernel template, or None: when no such record exists,
-    when the run has options the record was not taken with, or when the
-    kernel sources changed since the counters were read."""
+def stored_traffic(kernel: str, workload_key: str, template: str, variants: bool):
+    """HBM bytes per launch of `kernel` (fwd_tiles, bwd_step) from the
+    committed counter runs of this workload and kernel template, or None:
+    when no such record exists, when the run has options the record was not
+    taken with, or when the kernel sources changed since the counters were
+    read."""
     if variants:
         return None
     try:
-        with open(traffic_file(workload_key)) as f:
+        with open(traffic_file(kernel, workload_key)) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
@@ -285,7 +287,8 @@ def main():
     tflops = flops / (ms_step * 1e-3) / 1e12
     fwd_tflops = 2.0 * w.n * w.h * w.v / (fwd_ms * 1e-3) / 1e12
     template = kernel_template(w.dtype, w.return_metrics, bias is not None, w.softcap is not None)
-    traffic = stored_traffic(args.workload, template, options_changed or not run_bwd)
+    traffic = stored_traffic("fwd_tiles", args.workload, template, options_changed or not run_bwd)
+    chunk, n_chunks, _, one_launch = _abi.flce_backward_plan(p, with_launches=True)
     out = {
         "metric": (METRIC if not variants else f"fwd+bwd TFLOP/s (8*N*H*V) on {w.name}" + ", other workload or options (not the headline)")
                   if run_bwd else "forward only TFLOP/s (2*N*H*V), not the headline",
@@ -319,13 +322,34 @@ def main():
                                 for t in (loss, lse, metrics, gh, gw, gb) if t is not None) / 2**20, 1),
         "n_by_v_bytes_mb": round(w.n * w.v * 2 / 2**20, 1),
         "wall_s_timed": round(t_wall, 3),
-        "roofline": {"kernel": "fwd_tiles_kernel (forward logit tiles + online LSE)",
-                     "bound": "mfma", "achieved": round(fwd_tflops, 3), "peak": PEAK_TFLOPS[w.dtype],
-                     "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_TFLOPS[w.dtype], 4),
-                     "traffic": traffic, "template": template,
-                     "flops_per_launch": 2 * w.n * w.h * w.v,
-                     "window": "HIP events around flce_forward (tile kernel + combine + reduce)"},
+        "roofline_forward": {"kernel": "fwd_tiles_kernel (forward logit tiles + online LSE)",
+                             "bound": "mfma", "achieved": round(fwd_tflops, 3), "peak": PEAK_TFLOPS[w.dtype],
+                             "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_TFLOPS[w.dtype], 4),
+                             "traffic": traffic, "template": template,
+                             "flops_per_launch": 2 * w.n * w.h * w.v,
+                             "window": "HIP events around flce_forward (tile kernel + combine + reduce)"},
     }
+    out["roofline"] = out["roofline_forward"]
+    if run_bwd and one_launch:
+        # The dominant kernel: the backward's n_chunks + 1 launches of bwd_step_kernel (each the
+        # recompute of one vocabulary chunk with both contractions of the previous one) hold
+        # 6*N*H*V flops per backward pass, so per launch on average 6*N*H*V / (n_chunks + 1).
+        # Achieved = that over the average launch duration, i.e. 6*N*H*V over the backward's
+        # HIP-event window (which also holds the 5 us prep kernel and the hidden transpose).
+        launches = n_chunks + 1
+        bwd_tflops = 6.0 * w.n * w.h * w.v / (bwd_ms * 1e-3) / 1e12
+        step_traffic = stored_traffic("bwd_step", args.workload, "bwd_step " + template, options_changed)
+        out["roofline"] = {"kernel": "bwd_step_kernel (per vocabulary chunk: recompute + grad_weight + "
+                                     "grad_hidden in one launch)",
+                           "bound": "mfma", "achieved": round(bwd_tflops, 3), "peak": PEAK_TFLOPS[w.dtype],
+                           "unit": "TFLOP/s", "frac": round(bwd_tflops / PEAK_TFLOPS[w.dtype], 4),
+                           "traffic": step_traffic,
+                           "template": "bwd_step " + template,
+                           "launches_per_backward": launches, "vocab_chunk": chunk,
+                           "flops_per_launch": round(6 * w.n * w.h * w.v / launches),
+                           "avg_launch_ms": round(bwd_ms / launches, 4),
+                           "window": "HIP events around flce_backward (the bwd_step_kernel launches, "
+                                     "prep and hidden transpose), divided by the launch count"}
     if w.dtype == "f32":
         # fp32 at small H is memory- and launch-bound, not MFMA-bound: the
         # roofline entry is HBM bandwidth over the whole step, counting the

@@ -142,11 +142,18 @@ size_t flce_backward_workspace_size(const flce_problem_t* p);
 /* The backward's vocabulary chunking for problem *p (card: "Algorithm",
  * backward: each logit tile is recomputed; here the vocabulary is swept in
  * chunks of *chunk ids, the last one *last_chunk ids, *n_chunks in all, each
- * chunk's grad_weight rows complete after it).  The default plan depends on
- * H and V only (bwd_vocab_chunk overrides it).  Pure host function; any
- * output pointer may be NULL.  FLCE_ERR_INVALID_ARGUMENT for an invalid *p. */
+ * chunk's grad_weight rows complete after it).  *one_launch_per_chunk is 1
+ * when each chunk's recompute and the previous chunk's two contractions run
+ * in one launch (n_chunks + 1 launches of the GEMM kernel; 16-bit inputs
+ * whose operand offsets fit 32 bits), else 0 (three kernels per chunk).
+ * The default plan depends on H and V only (bwd_vocab_chunk overrides it).
+ * fp32 problems of at most 256 tokens, 8192 ids and a hidden size of 1024
+ * with the default plan run a small path without chunks (one workgroup per
+ * token or per 8 vocabulary rows, plain fp32 FMAs): *chunk = V, *n_chunks = 1.
+ * Pure host function; any output pointer may be NULL.
+ * FLCE_ERR_INVALID_ARGUMENT or FLCE_ERR_UNSUPPORTED for an invalid *p. */
 flce_status_t flce_backward_plan(const flce_problem_t* p, int64_t* chunk, int64_t* n_chunks,
-                                 int64_t* last_chunk);
+                                 int64_t* last_chunk, int32_t* one_launch_per_chunk);
 
 /* Forward pass (card: "Algorithm", forward; "Metrics for free").
  *   hidden, weight, targets, bias (NULL iff !has_bias): inputs as above.

@@ -74,7 +74,7 @@ _SIGNATURES = {
                                              _VP, ctypes.c_size_t, _VP]),
     "flce_forward_status": (ctypes.c_int, [_PP, _VP, ctypes.POINTER(ctypes.c_uint32), _VP]),
     "flce_backward_plan": (ctypes.c_int, [_PP, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
-                                          ctypes.POINTER(ctypes.c_int64)]),
+                                          ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32)]),
     "flce_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "flce_last_error": (ctypes.c_char_p, []),
     "flce_version": (ctypes.c_char_p, []),
@@ -172,11 +172,14 @@ def flce_forward_status(p: Problem, workspace, stream) -> int:
     return int(out.value)
 
 
-def flce_backward_plan(p: Problem):
-    """(chunk, n_chunks, last_chunk): the backward's vocabulary chunking."""
-    c, n, last = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int64(0)
-    check(library().flce_backward_plan(ctypes.byref(p), ctypes.byref(c), ctypes.byref(n), ctypes.byref(last)))
-    return int(c.value), int(n.value), int(last.value)
+def flce_backward_plan(p: Problem, with_launches: bool = False):
+    """(chunk, n_chunks, last_chunk): the backward's vocabulary chunking; with
+    ``with_launches`` also whether each chunk is one launch (1) or three (0)."""
+    c, n, last, one = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int32(0)
+    check(library().flce_backward_plan(ctypes.byref(p), ctypes.byref(c), ctypes.byref(n), ctypes.byref(last),
+                                       ctypes.byref(one)))
+    out = (int(c.value), int(n.value), int(last.value))
+    return out + (int(one.value),) if with_launches else out
 
 
 def flce_version() -> str:

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libflce.so")
 
-SOURCES = ["flce_kernels.hip", "flce_api.cpp"]
+SOURCES = ["flce_kernels.hip", "flce_small.hip", "flce_api.cpp"]
 HEADERS = ["flce_device.h", "flce_plan.h"]
 
 FLAGS = [

@@ -338,18 +338,53 @@ flce_status_t check_workspace(const void* ws, size_t bytes, size_t need) {
 
 float cap_of(const flce_problem_t& p) { return p.softcap > 0.f ? p.softcap : 1.f; }
 
+// fp32 problems small enough that the 256 x 256 tiles would leave most CUs
+// idle run the small path (flce_small.hip) when the plan is the default one
+// (the plan overrides address the tiled path).
+bool small_path(const flce_problem_t& p) {
+  return p.dtype == FLCE_F32 && p.n_tokens <= flce::kSmallMaxN && p.vocab <= flce::kSmallMaxV &&
+         p.hidden <= flce::kSmallMaxH && p.fwd_tiles_per_split == 0 && p.bwd_vocab_chunk == 0;
+}
+
+flce::SmallArgs small_args(const flce_problem_t& p, const char* hidden, const void* weight, const void* bias,
+                           const int64_t* targets) {
+  flce::SmallArgs a{};
+  a.hidden = hidden;
+  a.weight = reinterpret_cast<const char*>(weight);
+  a.bias = reinterpret_cast<const char*>(bias);
+  a.targets = targets;
+  a.N = p.n_tokens;
+  a.H = p.hidden;
+  a.V = p.vocab;
+  a.ignore_index = p.ignore_index;
+  a.s = p.logit_scale;
+  a.cap = cap_of(p);
+  a.inv_cap = 1.f / a.cap;
+  a.has_cap = p.softcap > 0.f;
+  a.class_weight = p.class_weight;
+  a.eps = p.label_smoothing;
+  a.z_loss = p.z_loss;
+  a.reduction = p.reduction;
+  a.eps_v = p.label_smoothing / (float)p.vocab;
+  a.keep = 1.f - p.label_smoothing;
+  a.zl2 = 2.f * p.z_loss;
+  return a;
+}
+
 }  // namespace
 
 extern "C" {
 
 flce_status_t flce_backward_plan(const flce_problem_t* p, int64_t* chunk, int64_t* n_chunks,
-                                 int64_t* last_chunk) {
+                                 int64_t* last_chunk, int32_t* one_launch_per_chunk) {
   const flce_status_t s = check_problem(p);
   if (s != FLCE_OK) return s;
   const BwdLayout L = bwd_layout(*p);
-  if (chunk) *chunk = L.chunk;
-  if (n_chunks) *n_chunks = L.n_chunks;
-  if (last_chunk) *last_chunk = L.last_chunk;
+  const bool small = small_path(*p);  // no chunks: the whole vocabulary at once
+  if (chunk) *chunk = small ? p->vocab : L.chunk;
+  if (n_chunks) *n_chunks = small ? 1 : L.n_chunks;
+  if (last_chunk) *last_chunk = small ? p->vocab : L.last_chunk;
+  if (one_launch_per_chunk) *one_launch_per_chunk = L.fused && !small ? 1 : 0;
   return FLCE_OK;
 }
 
@@ -394,48 +429,61 @@ flce_status_t flce_forward(const flce_problem_t* p, const void* hidden, const vo
     if ((e = tok_inputs(*p, L.tok, hidden, targets, ws, L.off_hrows, L.off_tgt, st, in)) != hipSuccess)
       return hip_fail(e, "gather kernel");
     targets = in.targets;
-    flce::FwdArgs fa{};
-    fa.hidden = in.hidden;
-    fa.weight = reinterpret_cast<const char*>(weight);
-    fa.bias = reinterpret_cast<const char*>(bias);
-    fa.targets = targets;
-    fa.part = reinterpret_cast<float*>(ws + L.off_part);
-    fa.N = N;
-    fa.H = p->hidden;
-    fa.V = p->vocab;
-    fa.ignore_index = p->ignore_index;
-    fa.n_tok_tiles = L.n_tok_tiles;
-    fa.n_voc_tiles = L.n_voc_tiles;
-    fa.tiles_per_split = L.tiles_per_split;
-    fa.n_splits = L.n_splits;
-    fa.s = p->logit_scale;
-    fa.cap = cap_of(*p);
-    fa.inv_cap = 1.f / fa.cap;
-    fa.zsum = p->label_smoothing > 0.f;
-    e = flce::launch_forward_tiles(p->dtype, metrics_on, p->has_bias != 0, p->softcap > 0.f, fa, st);
-    if (e != hipSuccess) return hip_fail(e, "forward tile kernel");
+    if (small_path(*p)) {
+      flce::SmallArgs sa = small_args(*p, in.hidden, weight, bias, targets);
+      sa.lse_out = lse;
+      sa.loss_rows = p->reduction == FLCE_NONE ? loss : nullptr;
+      sa.row_loss = reinterpret_cast<float*>(ws + L.off_rowloss);
+      sa.row_ent = reinterpret_cast<float*>(ws + L.off_rowent);
+      sa.row_flag = reinterpret_cast<int*>(ws + L.off_rowflag);
+      sa.row_w = p->class_weight ? reinterpret_cast<float*>(ws + L.off_roww) : nullptr;
+      sa.predictions = p->predictions;
+      e = flce::launch_small_forward(metrics_on, sa, st);
+      if (e != hipSuccess) return hip_fail(e, "small forward kernel");
+    } else {
+      flce::FwdArgs fa{};
+      fa.hidden = in.hidden;
+      fa.weight = reinterpret_cast<const char*>(weight);
+      fa.bias = reinterpret_cast<const char*>(bias);
+      fa.targets = targets;
+      fa.part = reinterpret_cast<float*>(ws + L.off_part);
+      fa.N = N;
+      fa.H = p->hidden;
+      fa.V = p->vocab;
+      fa.ignore_index = p->ignore_index;
+      fa.n_tok_tiles = L.n_tok_tiles;
+      fa.n_voc_tiles = L.n_voc_tiles;
+      fa.tiles_per_split = L.tiles_per_split;
+      fa.n_splits = L.n_splits;
+      fa.s = p->logit_scale;
+      fa.cap = cap_of(*p);
+      fa.inv_cap = 1.f / fa.cap;
+      fa.zsum = p->label_smoothing > 0.f;
+      e = flce::launch_forward_tiles(p->dtype, metrics_on, p->has_bias != 0, p->softcap > 0.f, fa, st);
+      if (e != hipSuccess) return hip_fail(e, "forward tile kernel");
 
-    flce::CombineArgs ca{};
-    ca.targets = targets;
-    ca.part = fa.part;
-    ca.lse_out = lse;
-    ca.loss_rows = p->reduction == FLCE_NONE ? loss : nullptr;
-    ca.row_loss = reinterpret_cast<float*>(ws + L.off_rowloss);
-    ca.row_ent = reinterpret_cast<float*>(ws + L.off_rowent);
-    ca.row_flag = reinterpret_cast<int*>(ws + L.off_rowflag);
-    ca.N = N;
-    ca.V = p->vocab;
-    ca.ignore_index = p->ignore_index;
-    ca.tiles_per_split = L.tiles_per_split;
-    ca.n_splits = L.n_splits;
-    ca.zsum = fa.zsum;
-    ca.eps = p->label_smoothing;
-    ca.z_loss = p->z_loss;
-    ca.class_weight = p->class_weight;
-    ca.row_w = p->class_weight ? reinterpret_cast<float*>(ws + L.off_roww) : nullptr;
-    ca.predictions = p->predictions;
-    e = flce::launch_forward_combine(metrics_on, ca, st);
-    if (e != hipSuccess) return hip_fail(e, "forward combine kernel");
+      flce::CombineArgs ca{};
+      ca.targets = targets;
+      ca.part = fa.part;
+      ca.lse_out = lse;
+      ca.loss_rows = p->reduction == FLCE_NONE ? loss : nullptr;
+      ca.row_loss = reinterpret_cast<float*>(ws + L.off_rowloss);
+      ca.row_ent = reinterpret_cast<float*>(ws + L.off_rowent);
+      ca.row_flag = reinterpret_cast<int*>(ws + L.off_rowflag);
+      ca.N = N;
+      ca.V = p->vocab;
+      ca.ignore_index = p->ignore_index;
+      ca.tiles_per_split = L.tiles_per_split;
+      ca.n_splits = L.n_splits;
+      ca.zsum = fa.zsum;
+      ca.eps = p->label_smoothing;
+      ca.z_loss = p->z_loss;
+      ca.class_weight = p->class_weight;
+      ca.row_w = p->class_weight ? reinterpret_cast<float*>(ws + L.off_roww) : nullptr;
+      ca.predictions = p->predictions;
+      e = flce::launch_forward_combine(metrics_on, ca, st);
+      if (e != hipSuccess) return hip_fail(e, "forward combine kernel");
+    }
   }
   flce::ReduceArgs ra{};
   ra.row_loss = reinterpret_cast<const float*>(ws + L.off_rowloss);
@@ -617,6 +665,16 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
   if ((e = tok_inputs(*p, L.tok, hidden, targets, ws, L.off_hrows, L.off_tgt, st, in)) != hipSuccess)
     return hip_fail(e, "gather kernel");
   targets = in.targets;
+  if (small_path(*p)) {
+    flce::SmallArgs sa = small_args(*p, in.hidden, weight, bias, targets);
+    sa.lse = lse;
+    sa.grad_loss = grad_loss;
+    sa.grad_hidden = want_dh ? reinterpret_cast<char*>(grad_hidden) : nullptr;
+    sa.grad_weight = want_dw ? reinterpret_cast<char*>(grad_weight) : nullptr;
+    sa.grad_bias = want_db ? reinterpret_cast<char*>(grad_bias) : nullptr;
+    if ((e = flce::launch_small_backward(sa, st)) != hipSuccess) return hip_fail(e, "small backward kernel");
+    return FLCE_OK;
+  }
   float* scale = reinterpret_cast<float*>(ws + L.off_scale);
   flce::PrepArgs pa{targets, grad_loss, p->class_weight, scale, N, V, p->ignore_index, p->reduction,
                     p->logit_scale};

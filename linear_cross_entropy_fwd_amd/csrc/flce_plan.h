@@ -185,7 +185,40 @@ struct StepArgs {
   int nb_dh, dh_grid, nb_dw, nb_g;
 };
 
-// Launchers (flce_kernels.hip).  All asynchronous on `st`.
+// The small fp32 path (flce_small.hip): at most kSmallMaxN tokens,
+// kSmallMaxV ids and a hidden size of kSmallMaxH.
+constexpr int64_t kSmallMaxN = 256, kSmallMaxV = 8192, kSmallMaxH = 1024;
+constexpr int kSmallDwRows = 8;  // vocabulary rows per grad_weight workgroup
+
+struct SmallArgs {
+  const char* hidden;      // [N][H] fp32, contiguous rows
+  const char* weight;      // [V][H] fp32
+  const char* bias;        // [V] fp32 or null
+  const int64_t* targets;  // [N], contiguous
+  int64_t N, H, V, ignore_index;
+  float s, cap, inv_cap;   // cap = inv_cap = 1 without a soft cap
+  int has_cap;
+  const float* class_weight;  // [V] or null
+  float eps, z_loss;       // label smoothing, z-loss coefficient
+  // forward outputs (as the split combine of the tiled path writes them)
+  float* lse_out;          // [N] or null
+  float* loss_rows;        // [N] for reduction "none", else null
+  float* row_loss;         // [N] workspace
+  float* row_ent;          // [N] workspace (metrics)
+  int* row_flag;           // [N] workspace
+  float* row_w;            // [N] workspace or null
+  int64_t* predictions;    // [N] or null
+  // backward
+  const float* lse;        // [N]
+  const float* grad_loss;  // [1] (mean / sum) or [N] (none), null = 1
+  int reduction;
+  float eps_v, keep, zl2;  // eps / V, 1 - eps, 2 z_loss
+  char* grad_hidden;       // [N][H] or null
+  char* grad_weight;       // [V][H] or null
+  char* grad_bias;         // [V] or null
+};
+
+// Launchers (flce_kernels.hip, flce_small.hip).  All asynchronous on `st`.
 hipError_t launch_forward_tiles(int dtype, bool metrics, bool bias, bool cap, const FwdArgs& a,
                                 hipStream_t st);
 hipError_t launch_forward_combine(bool metrics, const CombineArgs& a, hipStream_t st);
@@ -198,6 +231,8 @@ hipError_t launch_backward_dh_final(int dtype, const DhFinalArgs& a, hipStream_t
 hipError_t launch_backward_dw(int dtype, const DwArgs& a, hipStream_t st);
 hipError_t launch_backward_db(int dtype, const DbArgs& a, hipStream_t st);
 hipError_t launch_backward_step(int dtype, bool bias, bool cap, const StepArgs& a, hipStream_t st);
+hipError_t launch_small_forward(bool metrics, const SmallArgs& a, hipStream_t st);
+hipError_t launch_small_backward(const SmallArgs& a, hipStream_t st);
 // Grid sizes (workgroups, padded to whole tile groups) of the three parts.
 int backward_g_grid(int n_tok_tiles, int n_voc_tiles);
 int backward_dh_grid(int n_h_tiles, int n_tok_tiles);

@@ -265,6 +265,11 @@ def test_backward_plan_at_the_workloads(n, h, v, plan):
 
 def test_backward_plan_override_and_invalid():
     assert _abi.flce_backward_plan(make_problem(4096, 4096, 128256, BF16, bwd_vocab_chunk=4096)) == (4096, 32, 1280)
+    # one launch per chunk for 16-bit inputs; fp32 and operands past 32-bit offsets keep three kernels
+    assert _abi.flce_backward_plan(make_problem(4096, 4096, 128256, BF16), with_launches=True)[3] == 1
+    assert _abi.flce_backward_plan(make_problem(64, 128, 1000, F32), with_launches=True)[3] == 0
+    assert _abi.flce_backward_plan(make_problem(65536, 128, 32768, BF16, bwd_vocab_chunk=32768),
+                                   with_launches=True)[3] == 0
     with pytest.raises(_abi.FlceError):
         _abi.flce_backward_plan(make_problem(64, 100, 1000, BF16))   # 200-byte rows: refused
 

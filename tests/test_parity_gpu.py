@@ -240,6 +240,24 @@ def test_variants_leave_plain_loss_bit_identical():
     assert torch.equal(ga[0], gb[0]) and torch.equal(ga[1], gb[1])
 
 
+# --------------------------------------------------------------------------- small fp32 path
+
+@pytest.mark.parametrize("red", ["mean", "sum", "none"])
+def test_small_fp32_path_and_tiled_path(red):
+    """fp32 problems of at most 256 tokens (8192 ids, H <= 1024) run the small
+    path with the default plan (the plan query reports one chunk); a plan
+    override sends the same problem down the tiled path.  Both against the
+    oracle with bias, scale, cap, metrics, predictions and, for none, per-row
+    upstream gradients; then a single token with H = 4 and an odd V."""
+    from linear_cross_entropy_fwd_amd import _abi
+    w = W["transforms_bf16"].resized(n=256, h=128, v=3000, dtype="f32", reduction=red)
+    assert _abi.flce_backward_plan(_abi.make_problem(w.n, w.h, w.v, _abi.F32, has_bias=True)) == (3000, 1, 3000)
+    go = np.random.default_rng(5).standard_normal(w.n) if red == "none" else 0.7
+    run_case(w, grad_output=go)
+    run_case(w, grad_output=go, fwd_tiles_per_split=2, bwd_vocab_chunk=1024)
+    run_case(W["tiny_f32"].resized(n=1, h=4, v=37, reduction=red))
+
+
 # --------------------------------------------------------------------------- fp32 gradient output
 
 @pytest.mark.parametrize("dtype,chunk", [("bf16", 1024), ("f16", 0)])
