@@ -1,0 +1,195 @@
+// Host-only driver of the C ABI (test infrastructure): calls every entry
+// point over a sweep of problems with fake device addresses, against the
+// launcher stand-ins of flce_host_stubs.cpp, so that AddressSanitizer and
+// UndefinedBehaviorSanitizer check the host layer and the stubs check every
+// workspace range it hands a kernel.  Prints "ok <calls> <launches>" and
+// exits 0 when nothing was flagged.
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "flce.h"
+
+namespace hoststub {
+extern int violations, launches;
+extern const void* hidden_ptr;
+void begin(const void* ws, size_t bytes);
+int end();
+}  // namespace hoststub
+
+static char* A(uint64_t x) { return reinterpret_cast<char*>(uintptr_t(x)); }
+// Fake device address ranges (never dereferenced), 1 TiB apart.
+static char* const HID = A(0x100000000000ull);
+static char* const WGT = A(0x110000000000ull);
+static char* const TGT = A(0x120000000000ull);
+static char* const BIA = A(0x130000000000ull);
+static char* const OUT = A(0x140000000000ull);
+static char* const WSP = A(0x200000000000ull);
+static char* const NOALLOC = A(0x7f0000000000ull);  // the stubs' scratch address
+
+static int calls = 0, failures = 0;
+
+static void expect(flce_status_t got, flce_status_t want, const char* what, const flce_problem_t& p) {
+  ++calls;
+  if (got != want) {
+    ++failures;
+    fprintf(stderr, "FAIL %s: status %d (want %d) N=%lld H=%lld V=%lld dtype=%d: %s\n", what, got, want,
+            (long long)p.n_tokens, (long long)p.hidden, (long long)p.vocab, p.dtype, flce_last_error());
+  }
+}
+
+static flce_problem_t base(int64_t n, int64_t h, int64_t v, int dtype) {
+  flce_problem_t p;
+  memset(&p, 0, sizeof p);
+  p.n_tokens = n;
+  p.hidden = h;
+  p.vocab = v;
+  p.ignore_index = -100;
+  p.dtype = dtype;
+  p.reduction = FLCE_MEAN;
+  p.logit_scale = 1.0f;
+  return p;
+}
+
+static void run(flce_problem_t p, bool strided = false) {
+  const bool none = p.reduction == FLCE_NONE;
+  float* loss = reinterpret_cast<float*>(OUT);
+  float* lse = reinterpret_cast<float*>(OUT + (1ull << 36));
+  float* metrics = p.return_metrics ? reinterpret_cast<float*>(OUT + (2ull << 36)) : nullptr;
+  float* gl = reinterpret_cast<float*>(OUT + (3ull << 36));
+  void* gh = OUT + (4ull << 36);
+  void* gw = OUT + (5ull << 36);
+  void* gb = p.has_bias ? OUT + (6ull << 36) : nullptr;
+  const void* bias = p.has_bias ? BIA : nullptr;
+  if (strided) {
+    p.seq_len = p.n_tokens / 4;
+    p.hidden_row_stride = p.hidden + 8 * (p.dtype == FLCE_F32 ? 4 : 8);
+    p.hidden_seq_stride = (p.seq_len + 1) * p.hidden_row_stride;
+    p.targets_stride = 2;
+    p.targets_seq_stride = 2 * (p.seq_len + 1);
+  }
+  hoststub::hidden_ptr = HID;
+  const size_t fs = flce_forward_workspace_size(&p), bs = flce_backward_workspace_size(&p);
+  const size_t fbs = flce_forward_backward_workspace_size(&p);
+  hoststub::begin(WSP, fs);
+  expect(flce_forward(&p, HID, WGT, reinterpret_cast<const int64_t*>(TGT), bias, loss, lse, metrics, WSP, fs, nullptr),
+         FLCE_OK, "forward", p);
+  hoststub::end();
+  hoststub::begin(WSP, bs);
+  expect(flce_backward(&p, HID, WGT, reinterpret_cast<const int64_t*>(TGT), bias, lse, none ? gl : nullptr, gh, gw,
+                       gb, WSP, bs, nullptr),
+         FLCE_OK, "backward", p);
+  hoststub::end();
+  // only some gradients wanted
+  hoststub::begin(WSP, bs);
+  expect(flce_backward(&p, HID, WGT, reinterpret_cast<const int64_t*>(TGT), bias, lse, nullptr, gh, nullptr,
+                       nullptr, WSP, bs, nullptr),
+         FLCE_OK, "backward grad_hidden only", p);
+  hoststub::end();
+  hoststub::begin(WSP, bs);
+  expect(flce_backward(&p, HID, WGT, reinterpret_cast<const int64_t*>(TGT), bias, lse, nullptr, nullptr, gw, gb,
+                       WSP, bs, nullptr),
+         FLCE_OK, "backward grad_weight only", p);
+  hoststub::end();
+  hoststub::begin(WSP, fbs);
+  expect(flce_forward_backward(&p, HID, WGT, reinterpret_cast<const int64_t*>(TGT), bias, loss, nullptr, metrics,
+                               none ? gl : nullptr, gh, gw, gb, WSP, fbs, nullptr),
+         FLCE_OK, "forward_backward", p);
+  hoststub::end();
+  if (fs <= (size_t(32) << 20)) {
+    hoststub::begin(NOALLOC, size_t(32) << 20);
+    expect(flce_forward_noalloc(&p, HID, WGT, reinterpret_cast<const int64_t*>(TGT), bias, loss, lse, metrics, nullptr),
+           FLCE_OK, "forward_noalloc", p);
+    hoststub::end();
+  }
+  // a workspace one byte short is refused before any launch
+  if (fs > 0) {
+    const int before = hoststub::launches;
+    expect(flce_forward(&p, HID, WGT, reinterpret_cast<const int64_t*>(TGT), bias, loss, lse, metrics, WSP, fs - 1,
+                        nullptr),
+           FLCE_ERR_WORKSPACE, "forward short workspace", p);
+    if (hoststub::launches != before) {
+      ++failures;
+      fprintf(stderr, "FAIL: a refused forward launched something\n");
+    }
+  }
+}
+
+int main() {
+  const int dts[3] = {FLCE_F32, FLCE_F16, FLCE_BF16};
+  // the five workloads
+  {
+    flce_problem_t p = base(64, 128, 1000, FLCE_F32);
+    p.return_metrics = 1;
+    run(p);
+    run(base(2048, 2048, 32000, FLCE_BF16));
+    run(base(4096, 4096, 128256, FLCE_BF16));
+    p = base(8192, 3584, 152064, FLCE_BF16);
+    p.has_bias = 1;
+    p.logit_scale = 0.5f;
+    p.softcap = 30.f;
+    p.reduction = FLCE_SUM;
+    p.return_metrics = 1;
+    run(p);
+    run(base(16384, 2048, 262144, FLCE_BF16));
+    p = base(16384, 2048, 262144, FLCE_BF16);
+    p.reduction = FLCE_NONE;
+    run(p);
+  }
+  // a sweep of shapes, dtypes, options and plans
+  const int64_t ns[] = {0, 1, 63, 256, 300, 1030};
+  const int64_t hs[] = {8, 64, 200, 256, 1024, 1032};
+  const int64_t vs[] = {1, 37, 1000, 2600, 8192, 8193, 33000};
+  for (int d = 0; d < 3; ++d)
+    for (int64_t n : ns)
+      for (int64_t h : hs)
+        for (int64_t v : vs) {
+          if ((h * (dts[d] == FLCE_F32 ? 4 : 2)) % 16) continue;
+          flce_problem_t p = base(n, h, v, dts[d]);
+          const int k = (int)(n + h + v) % 5;
+          p.reduction = k % 3;
+          p.has_bias = k & 1;
+          p.return_metrics = (k >> 1) & 1;
+          p.softcap = k == 4 ? 5.f : 0.f;
+          p.label_smoothing = k == 3 ? 0.1f : 0.f;
+          p.z_loss = k == 2 ? 1e-3f : 0.f;
+          p.grad_weight_fp32 = k == 1;
+          run(p);
+          p.bwd_vocab_chunk = 256;
+          p.fwd_tiles_per_split = 3;
+          run(p);
+          if (n >= 4 && n % 4 == 0) run(p, true);
+        }
+  // invalid arguments: a status, nothing launched
+  {
+    flce_problem_t p = base(64, 128, 1000, FLCE_BF16);
+    const int before = hoststub::launches;
+    float loss;
+    expect(flce_forward(&p, nullptr, WGT, reinterpret_cast<const int64_t*>(TGT), nullptr, &loss, nullptr, nullptr, WSP,
+                        1 << 20, nullptr),
+           FLCE_ERR_INVALID_ARGUMENT, "null hidden", p);
+    expect(flce_forward(&p, HID + 8, WGT, reinterpret_cast<const int64_t*>(TGT), nullptr, &loss, nullptr, nullptr, WSP,
+                        1 << 20, nullptr),
+           FLCE_ERR_INVALID_ARGUMENT, "misaligned hidden", p);
+    p.softcap = -1.f;
+    expect(flce_forward(&p, HID, WGT, reinterpret_cast<const int64_t*>(TGT), nullptr, &loss, nullptr, nullptr, WSP,
+                        1 << 20, nullptr),
+           FLCE_ERR_INVALID_ARGUMENT, "negative softcap", p);
+    p = base(64, 100, 1000, FLCE_BF16);
+    expect(flce_forward(&p, HID, WGT, reinterpret_cast<const int64_t*>(TGT), nullptr, &loss, nullptr, nullptr, WSP,
+                        1 << 20, nullptr),
+           FLCE_ERR_UNSUPPORTED, "row bytes not a multiple of 16", p);
+    expect(flce_forward_status(nullptr, WSP, nullptr, nullptr), FLCE_ERR_INVALID_ARGUMENT, "status of null problem", p);
+    if (hoststub::launches != before) {
+      ++failures;
+      fprintf(stderr, "FAIL: an invalid call launched something\n");
+    }
+    if (strcmp(flce_status_str((flce_status_t)77), "FLCE_ERR_UNKNOWN") != 0) ++failures;
+  }
+  if (failures || hoststub::violations) {
+    fprintf(stderr, "%d failures, %d violations\n", failures, hoststub::violations);
+    return 1;
+  }
+  printf("ok %d %d\n", calls, hoststub::launches);
+  return 0;
+}
