@@ -543,47 +543,6 @@ __device__ __forceinline__ void gemm_nt_tile(f32x4_t (&acc)[Gemm<W>::WI][Gemm<W>
   gemm_nt_tile<D, W>(acc, A, B, none);
 }
 
-// Bijective remap of a 1-D workgroup id so that consecutive logical ids land
-// on the same XCD (workgroups are dispatched round-robin over 8 XCDs).
-__device__ __forceinline__ int xcd_logical_id(int bid, int nblocks) {
-  const int q = nblocks / 8, rem = nblocks % 8;
-  const int xcd = bid % 8, k = bid / 8;
-  return xcd < rem ? xcd * (q + 1) + k : rem * (q + 1) + (xcd - rem) * q + k;
-}
-
-// Tile order for a grid over na x nb output tiles (a: the dimension whose
-// panels are shared along b, and the reverse): blocks of GA x GB tiles.
-// Workgroups are dealt to the 8 XCDs round robin and run one per CU, so 32
-// of them share an XCD's L2 at a time.  With XCD, logical ids are remapped so
-// that consecutive ones share an XCD, and a 4 x 8 block is what those 32
-// cover: 12 distinct operand panels per K-stage in L2, where a row-major
-// order (e.g. 16 x 2) would need 18.  Without it, a block is spread over all
-// XCDs (the panels then meet in the last-level cache rather than in L2).
-// Which is faster depends on the launch and is measured, not derived.  The
-// grid is padded to whole blocks; a padding workgroup gets valid = false and
-// must exit at once.
-template <int GA, int GB>
-__host__ __device__ inline int grouped_grid(int na, int nb) {
-  return ((na + GA - 1) / GA) * ((nb + GB - 1) / GB) * GA * GB;
-}
-
-struct TileAB {
-  int a, b;
-  bool valid;
-};
-
-template <int GA, int GB, bool XCD>
-__device__ __forceinline__ TileAB grouped_tile(int bid, int nblocks, int na, int nb) {
-  const int L = XCD ? xcd_logical_id(bid, nblocks) : bid;
-  const int nga = (na + GA - 1) / GA;
-  const int g = L / (GA * GB), w = L % (GA * GB);
-  TileAB r;
-  r.a = (g % nga) * GA + w % GA;
-  r.b = (g / nga) * GB + w / GA;
-  r.valid = r.a < na && r.b < nb;
-  return r;
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 }  // namespace flce

@@ -1260,7 +1260,7 @@ __global__ __launch_bounds__(W * 64) void bwd_dw_kernel(DwArgs a) {
 // a finished chunk (or pair of chunks), grad_weight of the last finished
 // chunk and the recompute of the next chunk into the other G buffer.  The
 // three grids are laid end to end (grad_hidden's, the longest workgroups,
-// first); each part's size is a multiple of 32, so a workgroup's XCD
+// first); each part's size is a multiple of 8, so a workgroup's XCD
 // (block id mod 8) is the same as in a launch of its own.  The parts touch
 // disjoint outputs and read only G written by an earlier launch.
 template <int D, bool BIAS, bool CAP>
@@ -1316,7 +1316,7 @@ static inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + p
 
 template <int D>
 static hipError_t fwd_tiles_dispatch(bool metrics, bool bias, bool cap, const FwdArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)grouped_grid<kFwdGA, kFwdGB>(a.n_tok_tiles, a.n_splits)), block(kFwdWaves * 64);
+  const dim3 grid((unsigned)grouped_grid<kFwdXcd>(a.n_tok_tiles, a.n_splits)), block(kFwdWaves * 64);
 #define FLCE_FWD(M, B, C)                                                                \
   if (metrics == M && bias == B && cap == C) {                                           \
     hipLaunchKernelGGL((fwd_tiles_kernel<D, M, B, C, kFwdWaves>), grid, block, 0, st, a); \
@@ -1368,7 +1368,7 @@ hipError_t launch_transpose(int dtype, const TransposeArgs& a, hipStream_t st) {
 template <int D>
 static hipError_t g_dispatch(bool bias, bool cap, const GArgs& a, hipStream_t st) {
   constexpr int W = kRecomputeWaves;
-  const dim3 grid((unsigned)grouped_grid<kRecGA, kRecGB>(a.n_tok_tiles, a.n_voc_tiles)), block(W * 64);
+  const dim3 grid((unsigned)grouped_grid<kRecXcd>(a.n_tok_tiles, a.n_voc_tiles)), block(W * 64);
   if (!bias && !cap) hipLaunchKernelGGL((bwd_g_kernel<D, false, false, W>), grid, block, 0, st, a);
   else if (!bias && cap) hipLaunchKernelGGL((bwd_g_kernel<D, false, true, W>), grid, block, 0, st, a);
   else if (bias && !cap) hipLaunchKernelGGL((bwd_g_kernel<D, true, false, W>), grid, block, 0, st, a);
@@ -1386,7 +1386,7 @@ hipError_t launch_backward_g(int dtype, bool bias, bool cap, const GArgs& a, hip
 }
 
 hipError_t launch_backward_dh(int dtype, const DhArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)grouped_grid<kDhGA, kDhGB>(a.n_h_tiles, a.n_tok_tiles), (unsigned)a.ksplit),
+  const dim3 grid((unsigned)grouped_grid<kDhXcd>(a.n_h_tiles, a.n_tok_tiles), (unsigned)a.ksplit),
       block(kContractWaves * 64);
   switch (dtype) {
     case DT_F32: hipLaunchKernelGGL((bwd_dh_kernel<DT_F32, kContractWaves, false>), grid, block, 0, st, a); break;
@@ -1416,7 +1416,7 @@ hipError_t launch_backward_dh_final(int dtype, const DhFinalArgs& a, hipStream_t
 }
 
 hipError_t launch_backward_dw(int dtype, const DwArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)grouped_grid<kDwGA, kDwGB>(a.n_h_tiles, a.n_voc_tiles)), block(kContractWaves * 64);
+  const dim3 grid((unsigned)grouped_grid<kDwXcd>(a.n_h_tiles, a.n_voc_tiles)), block(kContractWaves * 64);
   switch (dtype) {
     case DT_F32: hipLaunchKernelGGL((bwd_dw_kernel<DT_F32, kContractWaves, false>), grid, block, 0, st, a); break;
     case DT_F16:
@@ -1442,9 +1442,9 @@ static hipError_t step_dispatch(bool bias, bool cap, const StepArgs& a, hipStrea
   return hipGetLastError();
 }
 
-int backward_g_grid(int n_tok_tiles, int n_voc_tiles) { return grouped_grid<kRecGA, kRecGB>(n_tok_tiles, n_voc_tiles); }
-int backward_dh_grid(int n_h_tiles, int n_tok_tiles) { return grouped_grid<kDhGA, kDhGB>(n_h_tiles, n_tok_tiles); }
-int backward_dw_grid(int n_h_tiles, int n_voc_tiles) { return grouped_grid<kDwGA, kDwGB>(n_h_tiles, n_voc_tiles); }
+int backward_g_grid(int n_tok_tiles, int n_voc_tiles) { return grouped_grid<kRecXcd>(n_tok_tiles, n_voc_tiles); }
+int backward_dh_grid(int n_h_tiles, int n_tok_tiles) { return grouped_grid<kDhXcd>(n_h_tiles, n_tok_tiles); }
+int backward_dw_grid(int n_h_tiles, int n_voc_tiles) { return grouped_grid<kDwXcd>(n_h_tiles, n_voc_tiles); }
 
 hipError_t launch_backward_step(int dtype, bool bias, bool cap, const StepArgs& a, hipStream_t st) {
   if (a.nb_dh + a.nb_dw + a.nb_g == 0) return hipSuccess;

@@ -26,6 +26,58 @@ constexpr int kDhGA = 4, kDhGB = 8;
 constexpr bool kDhXcd = true;
 constexpr int kDwGA = 4, kDwGB = 8;
 constexpr bool kDwXcd = true;
+
+// Tile order of a GEMM-shaped grid over na x nb output tiles (a: the
+// dimension whose operand panels are shared along b, and the reverse).  The
+// tiles are numbered in blocks of up to GA x GB: rows of blocks GB tiles deep
+// in b, GA-wide blocks along a within a row, a fastest inside a block; a
+// block at the far edge of a or b is as wide as what is left, so the numbers
+// 0 .. na nb - 1 are exactly the tiles.
+//
+// Workgroups run one per CU and are dealt round robin to the 8 XCDs
+// (workgroup id mod 8), in order: when the next workgroup's XCD has no free
+// CU, the ones queued behind it wait too, even for other XCDs.  Without XCD,
+// workgroup bid takes tile number bid (grid na nb), and a block of 32 spreads
+// over all XCDs, its panels meeting in the last-level cache.  With XCD, the
+// grid is na nb rounded up to a multiple of 8 and each XCD is given one
+// contiguous range of tile numbers, all of equal length (the last XCDs one
+// shorter when na nb is not a multiple of 8: their last workgroup gets
+// valid = false and must exit at once), so that a block's panels meet in one
+// XCD's L2 and every XCD holds the same share of the work: an XCD with more
+// of a launch's long workgroups than the others would hold back the
+// dispatch of everything queued after them.
+struct TileAB {
+  int a, b;
+  bool valid;
+};
+
+template <bool XCD>
+__host__ __device__ inline int grouped_grid(int na, int nb) {
+  return XCD ? (na * nb + 7) / 8 * 8 : na * nb;
+}
+
+template <int GA, int GB, bool XCD>
+__host__ __device__ inline TileAB grouped_tile(int bid, int nblocks, int na, int nb) {
+  TileAB r{0, 0, false};
+  const int T = na * nb;
+  int L = bid;
+  if (XCD) {
+    // nblocks = grouped_grid<true>: XCDs [full, 8) get q - 1 tiles, the rest q
+    const int q = nblocks / 8, full = 8 - (nblocks - T);
+    const int x = bid % 8, k = bid / 8;
+    if (k >= (x < full ? q : q - 1)) return r;
+    L = x * q - (x > full ? x - full : 0) + k;
+  }
+  if (L >= T) return r;
+  const int gb = L / (na * GB), r0 = L - gb * (na * GB);
+  const int wb = nb - gb * GB < GB ? nb - gb * GB : GB;
+  const int ga = r0 / (GA * wb), r1 = r0 - ga * (GA * wb);
+  const int wa = na - ga * GA < GA ? na - ga * GA : GA;
+  r.a = ga * GA + r1 % wa;
+  r.b = gb * GB + r1 / wa;
+  r.valid = true;
+  return r;
+}
 // grad_bias partial sums per 256-token tile: one per wave column (64 tokens
 // each with 8 waves, 128 with 4).
 constexpr int kBiasParts = kRecomputeWaves == 8 ? 4 : 2;
@@ -233,7 +285,8 @@ hipError_t launch_backward_db(int dtype, const DbArgs& a, hipStream_t st);
 hipError_t launch_backward_step(int dtype, bool bias, bool cap, const StepArgs& a, hipStream_t st);
 hipError_t launch_small_forward(bool metrics, const SmallArgs& a, hipStream_t st);
 hipError_t launch_small_backward(const SmallArgs& a, hipStream_t st);
-// Grid sizes (workgroups, padded to whole tile groups) of the three parts.
+// Grid sizes (workgroups: grouped_grid of each part's tile grid, a multiple
+// of 8) of the three parts.
 int backward_g_grid(int n_tok_tiles, int n_voc_tiles);
 int backward_dh_grid(int n_h_tiles, int n_tok_tiles);
 int backward_dw_grid(int n_h_tiles, int n_voc_tiles);

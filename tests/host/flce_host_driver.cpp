@@ -8,7 +8,10 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <vector>
+
 #include "flce.h"
+#include "flce_plan.h"
 
 namespace hoststub {
 extern int violations, launches;
@@ -115,7 +118,65 @@ static void run(flce_problem_t p, bool strided = false) {
   }
 }
 
+// Tile orders: every tile of the grid exactly once; with the XCD remap, a
+// grid of a multiple of 8 and per-XCD tile counts at most one apart; and for
+// grids of whole 4 x 8 blocks the plain block order (blocks along a, then b;
+// a fastest inside a block; XCD x taking the x-th eighth of it).
+template <bool XCD>
+static void check_order(int na, int nb) {
+  const int nblocks = flce::grouped_grid<XCD>(na, nb);
+  std::vector<int> seen((size_t)na * nb, 0);
+  int per_xcd[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  bool whole = na % 4 == 0 && nb % 8 == 0;
+  if (XCD && nblocks % 8 != 0) ++failures;
+  for (int bid = 0; bid < nblocks; ++bid) {
+    const flce::TileAB t = flce::grouped_tile<4, 8, XCD>(bid, nblocks, na, nb);
+    if (!t.valid) continue;
+    if (t.a < 0 || t.a >= na || t.b < 0 || t.b >= nb) {
+      ++failures;
+      fprintf(stderr, "FAIL tile order %d x %d (xcd %d): block %d -> (%d, %d)\n", na, nb, XCD, bid, t.a, t.b);
+      continue;
+    }
+    ++seen[(size_t)t.b * na + t.a];
+    ++per_xcd[bid % 8];
+    if (whole) {
+      const int L = XCD ? (bid % 8) * (nblocks / 8) + bid / 8 : bid;
+      const int g = L / 32, w = L % 32, nga = na / 4;
+      if (t.a != (g % nga) * 4 + w % 4 || t.b != (g / nga) * 8 + w / 4) whole = false;
+    }
+  }
+  for (size_t i = 0; i < seen.size(); ++i)
+    if (seen[i] != 1) {
+      ++failures;
+      fprintf(stderr, "FAIL tile order %d x %d (xcd %d): tile %zu taken %d times\n", na, nb, XCD, i, seen[i]);
+      break;
+    }
+  if (XCD) {
+    int lo = per_xcd[0], hi = per_xcd[0];
+    for (int x = 1; x < 8; ++x) lo = per_xcd[x] < lo ? per_xcd[x] : lo, hi = per_xcd[x] > hi ? per_xcd[x] : hi;
+    if (hi - lo > 1) {
+      ++failures;
+      fprintf(stderr, "FAIL tile order %d x %d: XCD counts %d .. %d\n", na, nb, lo, hi);
+    }
+  }
+  if (na % 4 == 0 && nb % 8 == 0 && !whole) {
+    ++failures;
+    fprintf(stderr, "FAIL tile order %d x %d (xcd %d): not the plain block order\n", na, nb, XCD);
+  }
+  ++calls;
+}
+
 int main() {
+  for (int na = 1; na <= 40; ++na)
+    for (int nb = 1; nb <= 72; ++nb) {
+      check_order<false>(na, nb);
+      check_order<true>(na, nb);
+    }
+  const int big[][2] = {{16, 501}, {32, 594}, {64, 1024}, {14, 48}, {14, 32}, {8, 31}, {32, 48}, {16, 48}, {125, 8}};
+  for (const auto& g : big) {
+    check_order<false>(g[0], g[1]);
+    check_order<true>(g[0], g[1]);
+  }
   const int dts[3] = {FLCE_F32, FLCE_F16, FLCE_BF16};
   // the five workloads
   {

@@ -88,10 +88,9 @@ hipError_t hipStreamSynchronize(hipStream_t) { return hipSuccess; }
 namespace flce {
 
 static int eb_of(int dtype) { return dtype == 0 ? 4 : 2; }  // fp32 is dtype 0
-static int grid(int na, int nb) { return ((na + 3) / 4) * ((nb + 7) / 8) * 32; }  // 4 x 8 tile groups
-int backward_g_grid(int a, int b) { return grid(a, b); }
-int backward_dh_grid(int a, int b) { return grid(a, b); }
-int backward_dw_grid(int a, int b) { return grid(a, b); }
+int backward_g_grid(int a, int b) { return grouped_grid<kRecXcd>(a, b); }
+int backward_dh_grid(int a, int b) { return grouped_grid<kDhXcd>(a, b); }
+int backward_dw_grid(int a, int b) { return grouped_grid<kDwXcd>(a, b); }
 
 static char fake_scratch_tag;
 hipError_t scratch_address(void** out) {
