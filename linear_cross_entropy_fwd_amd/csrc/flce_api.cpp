@@ -43,7 +43,15 @@ constexpr int64_t kAlign = 256;
 constexpr int64_t kMaxChunkTiles = 48;
 constexpr int64_t kCUs = 256;  // MI355X compute units: one workgroup of a GEMM grid each at a time
 
-constexpr int kMaxSplits = 64;
+// Forward vocabulary splits: at least kMinSplitTiles tiles and at most
+// kMaxSplits splits (both by V only); a workgroup walks the splits of a run of
+// consecutive ones, at most kMaxWgTiles tiles in all (longer runs of one
+// workgroup through the vocabulary lose the operand sharing in L2 and the
+// last-level cache: 256 tiles a workgroup halved the forward's speed at
+// N = 16384, V = 262144).
+constexpr int kMinSplitTiles = 4;
+constexpr int kMaxSplits = 128;
+constexpr int kMaxWgTiles = 16;
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 int64_t cdiv(int64_t x, int64_t m) { return (x + m - 1) / m; }
@@ -186,10 +194,29 @@ hipError_t tok_inputs(const flce_problem_t& p, const TokLayout& L, const void* h
 // ---------------------------------------------------------------- forward plan
 
 struct FwdLayout {
-  int n_tok_tiles, n_voc_tiles, tiles_per_split, n_splits;
+  int n_tok_tiles, n_voc_tiles, tiles_per_split, n_splits, splits_per_wg, n_groups;
   TokLayout tok;
-  size_t off_status, off_part, off_rowloss, off_rowent, off_rowflag, off_roww, off_hrows, off_tgt, total;
+  size_t off_status, off_part, off_zt, off_rowloss, off_rowent, off_rowflag, off_roww, off_hrows, off_tgt, total;
 };
+
+// Splits a forward workgroup walks, one after the other (each still ends in
+// its own partial record, so the grouping changes no result and may depend
+// on N): the fewest rounds of kCUs workgroups times the tiles each walks, at
+// most kMaxWgTiles tiles; a tie goes to the longer run (fewer workgroups, so
+// fewer pipeline fills, and the next tile's copies overlap each epilogue).
+int fwd_splits_per_wg(int n_tok_tiles, int n_splits, int tiles_per_split) {
+  int best_g = 1;
+  int64_t best = INT64_MAX;
+  for (int g = 1; g <= n_splits && (g == 1 || g * tiles_per_split <= kMaxWgTiles); ++g) {
+    const int64_t wgs = (int64_t)n_tok_tiles * cdiv(n_splits, g);
+    const int64_t cost = cdiv(wgs, kCUs) * g * tiles_per_split;
+    if (cost <= best) {
+      best = cost;
+      best_g = g;
+    }
+  }
+  return best_g;
+}
 
 FwdLayout fwd_layout(const flce_problem_t& p) {
   FwdLayout L{};
@@ -199,8 +226,11 @@ FwdLayout fwd_layout(const flce_problem_t& p) {
   // Depends on V only (not N): a row's result must not depend on the batch.
   L.tiles_per_split = p.fwd_tiles_per_split > 0
                           ? std::min(p.fwd_tiles_per_split, L.n_voc_tiles)
-                          : (int)std::max<int64_t>(1, cdiv(L.n_voc_tiles, kMaxSplits));
+                          : (int)std::min<int64_t>(L.n_voc_tiles, std::max<int64_t>(kMinSplitTiles,
+                                                                                   cdiv(L.n_voc_tiles, kMaxSplits)));
   L.n_splits = (int)cdiv(L.n_voc_tiles, L.tiles_per_split);
+  L.splits_per_wg = fwd_splits_per_wg(L.n_tok_tiles, L.n_splits, L.tiles_per_split);
+  L.n_groups = (int)cdiv(L.n_splits, L.splits_per_wg);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -208,7 +238,11 @@ FwdLayout fwd_layout(const flce_problem_t& p) {
     return o;
   };
   L.off_status = take(16);
-  L.off_part = take((size_t)7 * L.n_splits * N * 4);
+  // records and target logits at a row pitch of whole tiles (the tile
+  // kernel stores whole tiles' columns without a predicate)
+  const int64_t npad = (int64_t)L.n_tok_tiles * kTile;
+  L.off_part = take((size_t)flce::part_fields(p.return_metrics != 0, p.label_smoothing > 0.f) * L.n_splits * npad * 4);
+  L.off_zt = take((size_t)2 * npad * 4);
   L.off_rowloss = take((size_t)N * 4);
   L.off_rowent = take((size_t)N * 4);
   L.off_rowflag = take((size_t)N * 4);
@@ -447,7 +481,9 @@ flce_status_t flce_forward(const flce_problem_t* p, const void* hidden, const vo
       fa.bias = reinterpret_cast<const char*>(bias);
       fa.targets = targets;
       fa.part = reinterpret_cast<float*>(ws + L.off_part);
+      fa.zt_rows = reinterpret_cast<float*>(ws + L.off_zt);
       fa.N = N;
+      fa.npad = (int64_t)L.n_tok_tiles * kTile;
       fa.H = p->hidden;
       fa.V = p->vocab;
       fa.ignore_index = p->ignore_index;
@@ -455,6 +491,8 @@ flce_status_t flce_forward(const flce_problem_t* p, const void* hidden, const vo
       fa.n_voc_tiles = L.n_voc_tiles;
       fa.tiles_per_split = L.tiles_per_split;
       fa.n_splits = L.n_splits;
+      fa.splits_per_wg = L.splits_per_wg;
+      fa.n_groups = L.n_groups;
       fa.s = p->logit_scale;
       fa.cap = cap_of(*p);
       fa.inv_cap = 1.f / fa.cap;
@@ -465,12 +503,14 @@ flce_status_t flce_forward(const flce_problem_t* p, const void* hidden, const vo
       flce::CombineArgs ca{};
       ca.targets = targets;
       ca.part = fa.part;
+      ca.zt_rows = fa.zt_rows;
       ca.lse_out = lse;
       ca.loss_rows = p->reduction == FLCE_NONE ? loss : nullptr;
       ca.row_loss = reinterpret_cast<float*>(ws + L.off_rowloss);
       ca.row_ent = reinterpret_cast<float*>(ws + L.off_rowent);
       ca.row_flag = reinterpret_cast<int*>(ws + L.off_rowflag);
       ca.N = N;
+      ca.npad = fa.npad;
       ca.V = p->vocab;
       ca.ignore_index = p->ignore_index;
       ca.tiles_per_split = L.tiles_per_split;

@@ -131,18 +131,19 @@ __shared__ float g_fwd_state[8 * 4 * 8 * 16];
 
 template <int D, bool METRICS, bool BIAS, bool CAP, int W>
 __global__ __launch_bounds__(W * 64) void fwd_tiles_kernel(FwdArgs a) {
-  constexpr int EB = Elem<D>::bytes, WI = Gemm<W>::WI, WJ = Gemm<W>::WJ;
+  constexpr int EB = Elem<D>::bytes, WI = Gemm<W>::WI, WJ = Gemm<W>::WJ, GN = Gemm<W>::GN;
   static_assert(8 * WJ * W * 16 <= 8 * 4 * 8 * 16, "online state does not fit g_fwd_state");
-  static_assert(Gemm<W>::GN * 16 * WJ == TILE && 2 * 16 * WI == TILE, "two wave rows share each column");
+  static_assert(GN * 16 * WJ == TILE && 2 * 16 * WI == TILE, "two wave rows share each column");
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = Gemm<W>::wm(wave), wn = Gemm<W>::wn(wave), c16 = lane & 15, q = lane >> 4;
 
-  const TileAB ti = grouped_tile<kFwdGA, kFwdGB, kFwdXcd>(blockIdx.x, gridDim.x, a.n_tok_tiles, a.n_splits);
+  const TileAB ti = grouped_tile<kFwdGA, kFwdGB, kFwdXcd>(blockIdx.x, gridDim.x, a.n_tok_tiles, a.n_groups);
   if (!ti.valid) return;
-  const int tt = ti.a, split = ti.b;
+  const int tt = ti.a;
+  const int split_first = ti.b * a.splits_per_wg;
+  const int split_last = min(split_first + a.splits_per_wg, a.n_splits);  // one past
   const int64_t n0 = (int64_t)tt * TILE;
-  const int vt_begin = split * a.tiles_per_split;
-  const int vt_end = min(vt_begin + a.tiles_per_split, a.n_voc_tiles);
+  const int wg_vt_end = min(split_last * a.tiles_per_split, a.n_voc_tiles);
   const int64_t rowb = a.H * EB;
 
   Panel B{a.hidden + n0 * rowb, rowb, (int)min<int64_t>(TILE, a.N - n0), rowb};
@@ -151,202 +152,199 @@ __global__ __launch_bounds__(W * 64) void fwd_tiles_kernel(FwdArgs a) {
   // 3 z_target, 4 argmax value, 5 argmax id, 6 target id (-1 when the row is
   // ignored or its target is out of range), 7 sum of z (label smoothing).  The four lanes of a column hold
   // the same m, S, U and argmax (they are merged every tile); z_target is
-  // written only by the lane that holds the target's row.
-  float* st = g_fwd_state + wave * 16 + c16;
-#define FST(k, j) st[((k) * WJ + (j)) * (W * 16)]
+  // written only by the lane that holds the target's row.  Slot 6 holds for
+  // the whole workgroup, the others start again with each split.
+  const int so = wave * 16 + c16;  // this lane's column slots
+#define FST(k, j) g_fwd_state[so + ((k) * WJ + (j)) * (W * 16)]
   if (q == 0) {
 #pragma unroll
     for (int j = 0; j < WJ; ++j) {
       const int64_t n = n0 + wn * 16 * WJ + 16 * j + c16;
       const int64_t tv = n < a.N ? a.targets[n] : a.ignore_index;
-      FST(0, j) = -INFINITY;
-      FST(1, j) = 0.f;
-      FST(2, j) = 0.f;
-      FST(3, j) = 0.f;
-      FST(4, j) = -INFINITY;
-      FST(5, j) = __int_as_float(0x7fffffff);
       FST(6, j) = __int_as_float((tv != a.ignore_index && tv >= 0 && tv < a.V) ? (int)tv : -1);
-      FST(7, j) = 0.f;
     }
   }
 
   f32x4_t acc[WI][WJ];
-  // The first two stages of each next vocabulary tile are copied before this
-  // tile's epilogue (which touches only registers and g_fwd_state), so the
-  // copies' latency hides behind it.
+  // The first two stages of each next vocabulary tile, also the next
+  // split's first, are copied before this tile's epilogue (which touches
+  // only registers and g_fwd_state), so the copies' latency hides behind it.
   CopyPlan<W> cp;
   {
-    const int64_t v0 = (int64_t)vt_begin * TILE;
+    const int64_t v0 = (int64_t)split_first * a.tiles_per_split * TILE;
     gemm_prefetch<W>(cp, Panel{a.weight + v0 * rowb, rowb, (int)min<int64_t>(TILE, a.V - v0), rowb}, B);
   }
-  for (int vt = vt_begin; vt < vt_end; ++vt) {
-    const int64_t v0 = (int64_t)vt * TILE;
-    Panel A{a.weight + v0 * rowb, rowb, (int)min<int64_t>(TILE, a.V - v0), rowb};
-    NoSide none;
-    gemm_run<D, W>(acc, cp, A, none);
-    if (vt + 1 < vt_end)
-      gemm_prefetch<W>(cp, Panel{A.base + TILE * rowb, rowb, (int)min<int64_t>(TILE, a.V - v0 - TILE), rowb}, B);
-
-    const int to = opaque_int(t);
-    const int qo = (to >> 4) & 3;
-    const int vbase = (int)v0 + Gemm<W>::wm(to >> 6) * 16 * WI;  // this wave's first row
-    const int vq = vbase + 4 * qo;                                // row of acc[i][.][e]: vq + 16 i + e
-    // rows of this lane at or past V (only in the last, ragged tile): vq + 16 i + e >= V
-    const int vrem = (int)min<int64_t>(a.V - vq, 1 << 20);
-    const bool ragged = vrem < 16 * WI;  // wave-uniform
-    float bv[WI][4];
-    load_bias_rows<D, BIAS, WI>(bv, a.bias, vq, a.V);
-
+  for (int split = split_first; split < split_last; ++split) {
+    if (q == 0) {
 #pragma unroll
-    for (int j = 0; j < WJ; ++j) {
-      float z[WI][4];
-#pragma unroll
-      for (int i = 0; i < WI; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float y = acc[i][j][e];
-          if (BIAS) y = y + bv[i][e];
-          // softcap: z = cap tanh(s y / cap), the two scales as one product
-          z[i][e] = CAP ? a.cap * tanh_exp(y * (a.s * a.inv_cap)) : a.s * y;
-        }
-      if (ragged) {  // a branch only the last tile takes, not a select per element
-#pragma unroll
-        for (int i = 0; i < WI; ++i)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (16 * i + e >= vrem) z[i][e] = -INFINITY;
-      }
-      float zl = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < WI; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) zl = fmaxf(zl, z[i][e]);
-      if (a.zsum) {  // label smoothing: the sum of z over the vocabulary
-        float zs = 0.f;
-#pragma unroll
-        for (int i = 0; i < WI; ++i)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (!ragged || 16 * i + e < vrem) zs = zs + z[i][e];
-        zs = col_sum4(zs);
-        if (q == 0) FST(7, j) = FST(7, j) + zs;
-      }
-      const float zmax = col_max4(zl);
-      const float mold = FST(0, j);
-      const float mnew = fmaxf(mold, zmax);
-      if (mnew != -INFINITY) {
-        // four independent partial sums (one per accumulator register), so
-        // that the adds do not wait on each exp in turn
-        // exp(z - m) as exp2(z log2e - m log2e): one FMA for the argument
-        float sp[4] = {0.f, 0.f, 0.f, 0.f}, up[4] = {0.f, 0.f, 0.f, 0.f};
-        const float ml = mnew * LOG2E;
-#pragma unroll
-        for (int i = 0; i < WI; ++i)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float ex = fast_exp2(fmaf(z[i][e], LOG2E, -ml));
-            sp[e] = sp[e] + ex;
-            if (METRICS) up[e] = fmaf(ex, fmaxf(z[i][e] - mnew, -1e30f), up[e]);
-          }
-        float sum = (sp[0] + sp[1]) + (sp[2] + sp[3]), usum = 0.f;
-        if (METRICS) usum = (up[0] + up[1]) + (up[2] + up[3]);
-        sum = col_sum4(sum);
-        if (METRICS) usum = col_sum4(usum);
-        if (q == 0) {
-          if (mold == -INFINITY) {
-            FST(1, j) = sum;
-            if (METRICS) FST(2, j) = usum;
-          } else {
-            const float dm = mold - mnew;
-            const float al = fast_exp2(dm * LOG2E);
-            const float Sold = FST(1, j);
-            if (METRICS) FST(2, j) = fmaf(al, fmaf(dm, Sold, FST(2, j)), usum);
-            FST(1, j) = fmaf(Sold, al, sum);
-          }
-          FST(0, j) = mnew;
-        }
-      }
-      if (METRICS && zmax > FST(4, j)) {
-        int idx = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < WI; ++i)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int v = vq + 16 * i + e;
-            if (z[i][e] == zmax && v < idx) idx = v;
-          }
-        idx = col_min4(idx);
-        if (q == 0) {
-          FST(4, j) = zmax;
-          FST(5, j) = __int_as_float(idx);
-        }
-      }
-      const int local = __float_as_int(FST(6, j)) - vbase;
-      if (local >= 0 && local < 16 * WI && ((local & 15) >> 2) == qo) {
-        const int ti = local >> 4, te = local & 3;
-        float zv = 0.f;
-#pragma unroll
-        for (int i = 0; i < WI; ++i)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (i == ti && e == te) zv = z[i][e];
-        FST(3, j) = zv;
+      for (int j = 0; j < WJ; ++j) {
+        FST(0, j) = -INFINITY;
+        FST(1, j) = 0.f;
+        FST(2, j) = 0.f;
+        FST(3, j) = 0.f;
+        FST(4, j) = -INFINITY;
+        FST(5, j) = __int_as_float(0x7fffffff);
+        FST(7, j) = 0.f;
       }
     }
-  }
+    const int vt_end = min((split + 1) * a.tiles_per_split, a.n_voc_tiles);
+    for (int vt = split * a.tiles_per_split; vt < vt_end; ++vt) {
+      const int64_t v0 = (int64_t)vt * TILE;
+      Panel A{a.weight + v0 * rowb, rowb, (int)min<int64_t>(TILE, a.V - v0), rowb};
+      NoSide none;
+      gemm_run<D, W>(acc, cp, A, none);
+      if (vt + 1 < wg_vt_end)
+        gemm_prefetch<W>(cp, Panel{A.base + TILE * rowb, rowb, (int)min<int64_t>(TILE, a.V - v0 - TILE), rowb}, B);
 
-  float m[WJ], S[WJ], U[WJ], zt[WJ], av[WJ], zs[WJ];
-  int ai[WJ];
+      const int to = opaque_int(t);
+      const int qo = (to >> 4) & 3;
+      const int vbase = (int)v0 + Gemm<W>::wm(to >> 6) * 16 * WI;  // this wave's first row
+      const int vq = vbase + 4 * qo;                                // row of acc[i][.][e]: vq + 16 i + e
+      // rows of this lane at or past V (only in the last, ragged tile): vq + 16 i + e >= V
+      const int vrem = (int)min<int64_t>(a.V - vq, 1 << 20);
+      const bool ragged = vrem < 16 * WI;  // wave-uniform
+      float bv[WI][4];
+      load_bias_rows<D, BIAS, WI>(bv, a.bias, vq, a.V);
+
 #pragma unroll
-  for (int j = 0; j < WJ; ++j) {
-    m[j] = FST(0, j);
-    S[j] = FST(1, j);
-    U[j] = FST(2, j);
-    zt[j] = FST(3, j);
-    av[j] = FST(4, j);
-    ai[j] = __float_as_int(FST(5, j));
-    zs[j] = FST(7, j);
+      for (int j = 0; j < WJ; ++j) {
+        float z[WI][4];
+#pragma unroll
+        for (int i = 0; i < WI; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float y = acc[i][j][e];
+            if (BIAS) y = y + bv[i][e];
+            // softcap: z = cap tanh(s y / cap), the two scales as one product
+            z[i][e] = CAP ? a.cap * tanh_exp(y * (a.s * a.inv_cap)) : a.s * y;
+          }
+        if (ragged) {  // a branch only the last tile takes, not a select per element
+#pragma unroll
+          for (int i = 0; i < WI; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (16 * i + e >= vrem) z[i][e] = -INFINITY;
+        }
+        float zl = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < WI; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) zl = fmaxf(zl, z[i][e]);
+        if (a.zsum) {  // label smoothing: the sum of z over the vocabulary
+          float zs = 0.f;
+#pragma unroll
+          for (int i = 0; i < WI; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (!ragged || 16 * i + e < vrem) zs = zs + z[i][e];
+          zs = col_sum4(zs);
+          if (q == 0) FST(7, j) = FST(7, j) + zs;
+        }
+        const float zmax = col_max4(zl);
+        const float mold = FST(0, j);
+        const float mnew = fmaxf(mold, zmax);
+        if (mnew != -INFINITY) {
+          // four independent partial sums (one per accumulator register), so
+          // that the adds do not wait on each exp in turn
+          // exp(z - m) as exp2(z log2e - m log2e): one FMA for the argument
+          float sp[4] = {0.f, 0.f, 0.f, 0.f}, up[4] = {0.f, 0.f, 0.f, 0.f};
+          const float ml = mnew * LOG2E;
+#pragma unroll
+          for (int i = 0; i < WI; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float ex = fast_exp2(fmaf(z[i][e], LOG2E, -ml));
+              sp[e] = sp[e] + ex;
+              if (METRICS) up[e] = fmaf(ex, fmaxf(z[i][e] - mnew, -1e30f), up[e]);
+            }
+          float sum = (sp[0] + sp[1]) + (sp[2] + sp[3]), usum = 0.f;
+          if (METRICS) usum = (up[0] + up[1]) + (up[2] + up[3]);
+          sum = col_sum4(sum);
+          if (METRICS) usum = col_sum4(usum);
+          if (q == 0) {
+            if (mold == -INFINITY) {
+              FST(1, j) = sum;
+              if (METRICS) FST(2, j) = usum;
+            } else {
+              const float dm = mold - mnew;
+              const float al = fast_exp2(dm * LOG2E);
+              const float Sold = FST(1, j);
+              if (METRICS) FST(2, j) = fmaf(al, fmaf(dm, Sold, FST(2, j)), usum);
+              FST(1, j) = fmaf(Sold, al, sum);
+            }
+            FST(0, j) = mnew;
+          }
+        }
+        if (METRICS && zmax > FST(4, j)) {
+          int idx = 0x7fffffff;
+#pragma unroll
+          for (int i = 0; i < WI; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int v = vq + 16 * i + e;
+              if (z[i][e] == zmax && v < idx) idx = v;
+            }
+          idx = col_min4(idx);
+          if (q == 0) {
+            FST(4, j) = zmax;
+            FST(5, j) = __int_as_float(idx);
+          }
+        }
+        const int local = __float_as_int(FST(6, j)) - vbase;
+        if (local >= 0 && local < 16 * WI && ((local & 15) >> 2) == qo) {
+          const int ti = local >> 4, te = local & 3;
+          float zv = 0.f;
+#pragma unroll
+          for (int i = 0; i < WI; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (i == ti && e == te) zv = z[i][e];
+          FST(3, j) = zv;
+        }
+      }
+    }
+
+    // The split is complete.  Waves wm = 0 and wm = 1 hold the same token
+    // columns over disjoint vocabulary rows: the first merges the second's
+    // state (read from its LDS slots) into its own and writes the split's
+    // record.  The stage buffers may hold the next split's first copies.
+    lds_barrier();
+    if (wm == 0) {
+      // rows of part and zt_rows are padded to whole tiles (pitch npad), so no
+      // lane needs a predicate: the four lanes of a column store the same
+      // values, columns past N land in the padding, and a split that does
+      // not hold a row's target writes the row's slot in zt_rows' second half
+      // (indices from an opaque copy of the thread id: derived from it
+      // outside, they would be kept live, and spilled, across the K loops)
+      const int tm = opaque_int(t), wv = tm >> 6, cm = tm & 15;
+      const int64_t stride = (int64_t)a.n_splits * a.npad;
+      const int po = (wv + GN) * 16 + cm;  // the partner's slots
+#define PST(k, j) g_fwd_state[po + ((k) * WJ + (j)) * (W * 16)]
+#pragma unroll
+      for (int j = 0; j < WJ; ++j) {
+        float m = FST(0, j), S = FST(1, j), U = FST(2, j), av = FST(4, j);
+        int ai = __float_as_int(FST(5, j));
+        lse_merge<METRICS>(m, S, U, PST(0, j), PST(1, j), PST(2, j));
+        if (METRICS) argmax_merge(av, ai, PST(4, j), __float_as_int(PST(5, j)));
+        const int col = Gemm<W>::wn(wv) * 16 * WJ + 16 * j + cm;
+        float* p = a.part + (int64_t)split * a.npad + n0 + col;
+        p[0] = m;
+        p[stride] = S;
+        if (METRICS) {
+          p[2 * stride] = U;
+          p[3 * stride] = av;
+          p[4 * stride] = __int_as_float(ai);
+        }
+        if (a.zsum) p[part_zs_field(METRICS) * stride] = FST(7, j) + PST(7, j);
+        const int tv = __float_as_int(FST(6, j));
+        const bool own = tv >= 0 && tv / TILE / a.tiles_per_split == split;
+        a.zt_rows[(own ? 0 : a.npad) + n0 + col] = FST(3, j) + PST(3, j);  // the non-owner holds +0
+      }
+#undef PST
+    }
+    lds_barrier();  // before the next split resets the state
   }
 #undef FST
-
-  // Waves wm=0 and wm=1 hold the same columns over disjoint vocab rows.
-  float* xs = reinterpret_cast<float*>(g_stage0);  // free after gemm_nt_tile returns
-  if (wm == 1 && q == 0) {
-#pragma unroll
-    for (int j = 0; j < WJ; ++j) {
-      const int tok = wn * 16 * WJ + 16 * j + c16;
-      xs[0 * TILE + tok] = m[j];
-      xs[1 * TILE + tok] = S[j];
-      xs[2 * TILE + tok] = U[j];
-      xs[3 * TILE + tok] = zt[j];
-      xs[4 * TILE + tok] = av[j];
-      xs[5 * TILE + tok] = __int_as_float(ai[j]);
-      xs[6 * TILE + tok] = zs[j];
-    }
-  }
-  __syncthreads();
-  if (wm == 0 && q == 0) {
-#pragma unroll
-    for (int j = 0; j < WJ; ++j) {
-      const int tok = wn * 16 * WJ + 16 * j + c16;
-      lse_merge<METRICS>(m[j], S[j], U[j], xs[0 * TILE + tok], xs[1 * TILE + tok], xs[2 * TILE + tok]);
-      zt[j] = zt[j] + xs[3 * TILE + tok];  // the non-owner holds +0
-      zs[j] = zs[j] + xs[6 * TILE + tok];
-      if (METRICS) argmax_merge(av[j], ai[j], xs[4 * TILE + tok], __float_as_int(xs[5 * TILE + tok]));
-      const int64_t n = n0 + tok;
-      if (n < a.N) {
-        const int64_t stride = (int64_t)a.n_splits * a.N;
-        float* p = a.part + (int64_t)split * a.N + n;
-        p[0 * stride] = m[j];
-        p[1 * stride] = S[j];
-        p[2 * stride] = U[j];
-        p[3 * stride] = zt[j];
-        p[4 * stride] = av[j];
-        p[5 * stride] = __int_as_float(ai[j]);
-        if (a.zsum) p[6 * stride] = zs[j];
-      }
-    }
-  }
 }
 
 // ------------------------------------------------------------------ forward combine / reduce
@@ -362,25 +360,27 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(CombineArgs a) {
   const int t = threadIdx.x, rl = t % ROWS, p = t / ROWS;
   const int64_t n = (int64_t)blockIdx.x * ROWS + rl;
   const bool in = n < a.N;
-  const int64_t stride = (int64_t)a.n_splits * a.N;
+  const int64_t stride = (int64_t)a.n_splits * a.npad;
   const float* pm = a.part + (in ? n : 0);
+  const int64_t zsf = part_zs_field(METRICS);
   float M = -INFINITY, S = 0.f, U = 0.f, av = -INFINITY, Z = 0.f;
   int ai = 0x7fffffff;
   if (in) {
-    for (int k = p; k < a.n_splits; k += PARTS) M = fmaxf(M, pm[(int64_t)k * a.N]);
+    for (int k = p; k < a.n_splits; k += PARTS) M = fmaxf(M, pm[(int64_t)k * a.npad]);
     if (a.zsum)
-      for (int k = p; k < a.n_splits; k += PARTS) Z = Z + pm[6 * stride + (int64_t)k * a.N];
+      for (int k = p; k < a.n_splits; k += PARTS) Z = Z + pm[zsf * stride + (int64_t)k * a.npad];
     for (int k = p; k < a.n_splits; k += PARTS) {
-      const float mk = pm[(int64_t)k * a.N];
+      const float mk = pm[(int64_t)k * a.npad];
       if (mk != -INFINITY) {
         const float d = mk - M;
         const float al = fast_exp2(d * LOG2E);
-        const float sk = pm[stride + (int64_t)k * a.N];
+        const float sk = pm[stride + (int64_t)k * a.npad];
         S = S + sk * al;
-        if (METRICS) U = U + al * fmaf(d, sk, pm[2 * stride + (int64_t)k * a.N]);
+        if (METRICS) U = U + al * fmaf(d, sk, pm[2 * stride + (int64_t)k * a.npad]);
       }
       if (METRICS)
-        argmax_merge(av, ai, pm[4 * stride + (int64_t)k * a.N], __float_as_int(pm[5 * stride + (int64_t)k * a.N]));
+        argmax_merge(av, ai, pm[3 * stride + (int64_t)k * a.npad],
+                     __float_as_int(pm[4 * stride + (int64_t)k * a.npad]));
     }
   }
   sh[0][p][rl] = M;
@@ -406,8 +406,7 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(CombineArgs a) {
     if (bad) {
       row = NAN;
     } else {
-      const int owner = (int)((tv / TILE) / a.tiles_per_split);
-      const float zt = pm[3 * stride + (int64_t)owner * a.N];
+      const float zt = a.zt_rows[n];
       // smoothed cross-entropy + z-loss, times the row's class weight (all
       // of it exact for the plain loss: eps = 0, z_loss = 0, weight 1)
       rw = a.class_weight ? a.class_weight[tv] : 1.f;
@@ -1316,7 +1315,7 @@ static inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + p
 
 template <int D>
 static hipError_t fwd_tiles_dispatch(bool metrics, bool bias, bool cap, const FwdArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)grouped_grid<kFwdXcd>(a.n_tok_tiles, a.n_splits)), block(kFwdWaves * 64);
+  const dim3 grid((unsigned)grouped_grid<kFwdXcd>(a.n_tok_tiles, a.n_groups)), block(kFwdWaves * 64);
 #define FLCE_FWD(M, B, C)                                                                \
   if (metrics == M && bias == B && cap == C) {                                           \
     hipLaunchKernelGGL((fwd_tiles_kernel<D, M, B, C, kFwdWaves>), grid, block, 0, st, a); \

@@ -82,26 +82,40 @@ __host__ __device__ inline TileAB grouped_tile(int bid, int nblocks, int na, int
 // each with 8 waves, 128 with 4).
 constexpr int kBiasParts = kRecomputeWaves == 8 ? 4 : 2;
 
-// Forward: one workgroup per (token tile, vocabulary split); a split is a run
-// of consecutive 256-id vocabulary tiles whose per-row online state the
-// workgroup carries in LDS between tiles (so that the state takes no
-// registers from the K loop).  The split size depends on V only, so a row's
-// result does not depend on how many rows share the call.
+// Fields of a forward partial record, part[field][split][row] (floats): m
+// and S; then U, the argmax value and the argmax id with metrics; then the
+// sum of z with label smoothing.
+__host__ __device__ inline int part_fields(bool metrics, bool zsum) {
+  return 2 + (metrics ? 3 : 0) + (zsum ? 1 : 0);
+}
+__host__ __device__ inline int part_zs_field(bool metrics) { return metrics ? 5 : 2; }
+
+// Forward: a split is a run of consecutive 256-id vocabulary tiles whose
+// per-row online state is carried in LDS between tiles (so that the state
+// takes no registers from the K loop) and ends in one partial record per
+// row.  The split size depends on V only, so a row's result does not depend
+// on how many rows share the call.  One workgroup per (token tile, group of
+// splits_per_wg consecutive splits), walking the group's tiles in order; the
+// group size depends on N and changes no result.
 struct FwdArgs {
   const char* hidden;
   const char* weight;
   const char* bias;
   const int64_t* targets;
-  float* part;  // [7][n_splits][N]: m, S, U, z_target, argmax value, argmax id, sum of z
+  float* part;     // [part_fields][n_splits][npad]
+  float* zt_rows;  // [2 npad]: the target's logit (from the split that holds the target), then scratch
   int64_t N, H, V, ignore_index;
+  int64_t npad;    // N rounded up to whole tiles
   int n_tok_tiles, n_voc_tiles, tiles_per_split, n_splits;
+  int splits_per_wg, n_groups;  // n_groups = ceil(n_splits / splits_per_wg)
   int zsum;  // 1: also the sum of z over the vocabulary (label smoothing)
   float s, cap, inv_cap;
 };
 
 struct CombineArgs {
   const int64_t* targets;
-  const float* part;
+  const float* part;     // [part_fields][n_splits][npad]
+  const float* zt_rows;  // [2 npad]
   float* lse_out;   // may be null
   float* loss_rows; // [N] output for reduction "none", else null
   float* row_loss;  // workspace [N]
@@ -111,8 +125,9 @@ struct CombineArgs {
   float* row_w;     // workspace [N]: the row's weight (0 if ignored or bad), or null
   int64_t* predictions;  // [N] argmax ids (needs METRICS), or null
   int64_t N, V, ignore_index;
+  int64_t npad;          // row pitch of part
   int tiles_per_split, n_splits;
-  int zsum;         // partial 6 holds the sum of z
+  int zsum;         // the partial records hold the sum of z
   float eps, z_loss;  // label smoothing, z-loss coefficient
 };
 

@@ -100,17 +100,32 @@ hipError_t scratch_address(void** out) {
   return hipSuccess;
 }
 
-hipError_t launch_forward_tiles(int dtype, bool, bool, bool, const FwdArgs& a, hipStream_t) {
+hipError_t launch_forward_tiles(int dtype, bool metrics, bool, bool, const FwdArgs& a, hipStream_t) {
   ++launches;
   maybe_ws("fwd_tiles", "hrows", a.hidden, (size_t)a.N * a.H * eb_of(dtype));
   maybe_ws("fwd_tiles", "tgt", a.targets, (size_t)a.N * 8);
-  ws("fwd_tiles", "part", a.part, (size_t)7 * a.n_splits * a.N * 4);
+  ws("fwd_tiles", "part", a.part, (size_t)part_fields(metrics, a.zsum != 0) * a.n_splits * a.npad * 4);
+  ws("fwd_tiles", "zt", a.zt_rows, (size_t)2 * a.npad * 4);
+  if (a.npad < (a.N + 255) / 256 * 256) {
+    ++violations;
+    fprintf(stderr, "VIOLATION forward row pitch %lld for %lld rows\n", (long long)a.npad, (long long)a.N);
+  }
+  // the launch covers every split: groups of splits_per_wg
+  if (a.splits_per_wg < 1 || (int64_t)a.n_groups * a.splits_per_wg < a.n_splits ||
+      (int64_t)(a.n_groups - 1) * a.splits_per_wg >= a.n_splits ||
+      (int64_t)a.n_splits * a.tiles_per_split < a.n_voc_tiles ||
+      (int64_t)(a.n_splits - 1) * a.tiles_per_split >= a.n_voc_tiles) {
+    ++violations;
+    fprintf(stderr, "VIOLATION forward plan: %d splits of %d tiles in %d groups of %d, %d tiles\n", a.n_splits,
+            a.tiles_per_split, a.n_groups, a.splits_per_wg, a.n_voc_tiles);
+  }
   return hipSuccess;
 }
-hipError_t launch_forward_combine(bool, const CombineArgs& a, hipStream_t) {
+hipError_t launch_forward_combine(bool metrics, const CombineArgs& a, hipStream_t) {
   ++launches;
   maybe_ws("combine", "tgt", a.targets, (size_t)a.N * 8);
-  ws("combine", "part", a.part, (size_t)7 * a.n_splits * a.N * 4);
+  ws("combine", "part", a.part, (size_t)part_fields(metrics, a.zsum != 0) * a.n_splits * a.npad * 4);
+  ws("combine", "zt", a.zt_rows, (size_t)2 * a.npad * 4);
   ws("combine", "rowloss", a.row_loss, (size_t)a.N * 4);
   ws("combine", "rowent", a.row_ent, (size_t)a.N * 4);
   ws("combine", "rowflag", a.row_flag, (size_t)a.N * 4);

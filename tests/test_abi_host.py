@@ -286,6 +286,8 @@ def test_backward_plan_override_and_invalid():
     (16384, 2048, 262144, dict(reduction="none")),
 ])
 def test_workspace_below_one_n_by_v_matrix(n, h, v, kw):
+    # and the forward alone fits the allocation-free forward's fixed 32 MiB
+    assert _abi.flce_forward_workspace_size(make_problem(n, h, v, BF16, **kw)) <= 32 << 20
     p = make_problem(n, h, v, BF16, **kw)
     total = _abi.flce_forward_workspace_size(p) + _abi.flce_backward_workspace_size(p)
     assert 0 < total < n * v * 2, (total, n * v * 2)
@@ -293,8 +295,8 @@ def test_workspace_below_one_n_by_v_matrix(n, h, v, kw):
 
 
 def test_noalloc_forward_refuses_past_its_scratch_before_any_launch():
-    # 64 splits x 7 partials x 20000 rows x 4 B: more than the fixed 32 MiB scratch
-    p = make_problem(20000, 128, 262144, BF16)
+    # 128 splits x 5 fields (metrics) x 20000 rows x 4 B: more than the fixed 32 MiB scratch
+    p = make_problem(20000, 128, 262144, BF16, return_metrics=True)
     assert _abi.flce_forward_workspace_size(p) > 32 << 20
     st = _abi.flce_forward_noalloc(p, FAKE, FAKE, FAKE, 0, FAKE, FAKE, 0, 0)
     assert st == WORKSPACE and "fixed scratch" in _abi.last_error()

@@ -65,8 +65,8 @@ def test_noalloc_forward_matches_flce_forward_twice(first, second):
 
 def test_noalloc_forward_refuses_a_problem_past_its_scratch():
     from linear_cross_entropy_fwd_amd import _abi
-    # 64 splits x 7 partials x 20000 rows x 4 B = 35.8 MB > 32 MiB
-    p = _abi.make_problem(20000, 128, 262144, _abi.BF16)
+    # 128 splits x 5 fields (metrics) x 20000 rows x 4 B = 51.2 MB > 32 MiB
+    p = _abi.make_problem(20000, 128, 262144, _abi.BF16, return_metrics=True)
     assert _abi.flce_forward_workspace_size(p) > 32 << 20
     fake = 0x100000
     st = _abi.flce_forward_noalloc(p, fake, fake, fake, 0, fake, fake, 0, 0)
