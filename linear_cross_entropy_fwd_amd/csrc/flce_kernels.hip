@@ -44,13 +44,13 @@ __device__ __forceinline__ int opaque_int(int x) {
   return x;
 }
 
-// tanh from its definition, tanh x = sign(x) (1 - 2 / (e^{2|x|} + 1)), with
-// the hardware exp2 and reciprocal: an absolute error of a few 1e-7 (so
-// cap * tanh is off by a few 1e-7 cap at most); e^{2|x|} = inf past
-// |x| ~ 44 gives exactly +-1, and NaN stays NaN.
-__device__ __forceinline__ float tanh_exp(float x) {
-  const float t = __builtin_amdgcn_exp2f(fabsf(x) * (2.f * LOG2E));
-  return copysignf(fmaf(-2.f, __builtin_amdgcn_rcpf(t + 1.f), 1.f), x);
+// tanh u from its definition, 1 - 2 / (e^{2u} + 1), given x = 2 u log2(e)
+// (so that e^{2u} = 2^x is one hardware exp2), with the hardware reciprocal:
+// an absolute error of a few 1e-7 (so cap * tanh is off by a few 1e-7 cap at
+// most).  No sign handling is needed: 2^x = inf (u past ~44) gives exactly 1,
+// 2^x = 0 gives exactly -1, and NaN stays NaN.
+__device__ __forceinline__ float tanh_of_exp2_arg(float x) {
+  return fmaf(-2.f, __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(x) + 1.f), 1.f);
 }
 
 // Merge online-softmax state (m2,S2,U2) into (m,S,U).  Symmetric in its two
@@ -116,6 +116,19 @@ __device__ __forceinline__ float col_max4(float x) {
 __device__ __forceinline__ float col_sum4(float x) {
   x = x + __shfl_xor(x, 16);
   return x + __shfl_xor(x, 32);
+}
+// Sum over the 16 lanes of a row (lanes 16 r .. 16 r + 15, one token column
+// each) by rotations within the row (DPP row_ror: VALU operands, no LDS):
+// every lane ends with the row's sum, lane 16 r in the order it is used.
+template <int N> __device__ __forceinline__ float row_ror(float x) {
+  static_assert(N >= 1 && N <= 15, "row_ror range");
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x120 + N, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x = x + row_ror<8>(x);
+  x = x + row_ror<4>(x);
+  x = x + row_ror<2>(x);
+  return x + row_ror<1>(x);
 }
 __device__ __forceinline__ int col_min4(int x) {
   x = min(x, __shfl_xor(x, 16));
@@ -203,20 +216,29 @@ __global__ __launch_bounds__(W * 64) void fwd_tiles_kernel(FwdArgs a) {
       // rows of this lane at or past V (only in the last, ragged tile): vq + 16 i + e >= V
       const int vrem = (int)min<int64_t>(a.V - vq, 1 << 20);
       const bool ragged = vrem < 16 * WI;  // wave-uniform
+      // Each logit as a key that orders like it: with a soft cap the tanh t
+      // (z = cap t, cap > 0), else z itself.  The bias folds into one FMA:
+      // with a cap, x = 2 log2(e) s (y + b) / cap is the exp2 argument of t.
+      const float kscale = CAP ? a.s * a.inv_cap * (2.f * LOG2E) : a.s;
       float bv[WI][4];
       load_bias_rows<D, BIAS, WI>(bv, a.bias, vq, a.V);
+      if (BIAS) {
+#pragma unroll
+        for (int i = 0; i < WI; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) bv[i][e] = bv[i][e] * kscale;
+      }
+      const float kz = CAP ? a.cap : 1.f;  // z = kz * key
 
 #pragma unroll
       for (int j = 0; j < WJ; ++j) {
-        float z[WI][4];
+        float z[WI][4];  // the keys
 #pragma unroll
         for (int i = 0; i < WI; ++i)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            float y = acc[i][j][e];
-            if (BIAS) y = y + bv[i][e];
-            // softcap: z = cap tanh(s y / cap), the two scales as one product
-            z[i][e] = CAP ? a.cap * tanh_exp(y * (a.s * a.inv_cap)) : a.s * y;
+            const float x = BIAS ? fmaf(acc[i][j][e], kscale, bv[i][e]) : acc[i][j][e] * kscale;
+            z[i][e] = CAP ? tanh_of_exp2_arg(x) : x;
           }
         if (ragged) {  // a branch only the last tile takes, not a select per element
 #pragma unroll
@@ -238,29 +260,34 @@ __global__ __launch_bounds__(W * 64) void fwd_tiles_kernel(FwdArgs a) {
             for (int e = 0; e < 4; ++e)
               if (!ragged || 16 * i + e < vrem) zs = zs + z[i][e];
           zs = col_sum4(zs);
-          if (q == 0) FST(7, j) = FST(7, j) + zs;
+          if (q == 0) FST(7, j) = fmaf(kz, zs, FST(7, j));
         }
-        const float zmax = col_max4(zl);
+        const float kmax = col_max4(zl);
+        const float zmax = kz * kmax;
         const float mold = FST(0, j);
         const float mnew = fmaxf(mold, zmax);
         if (mnew != -INFINITY) {
           // four independent partial sums (one per accumulator register), so
-          // that the adds do not wait on each exp in turn
-          // exp(z - m) as exp2(z log2e - m log2e): one FMA for the argument
+          // that the adds do not wait on each exp in turn.  The exp argument
+          // (z - m) log2(e) is one FMA of the key, and the entropy term
+          // e^{z-m} (z - m) is taken in those units (times ln 2 per column).
           float sp[4] = {0.f, 0.f, 0.f, 0.f}, up[4] = {0.f, 0.f, 0.f, 0.f};
-          const float ml = mnew * LOG2E;
+          const float ml = mnew * LOG2E, kl = kz * LOG2E;
 #pragma unroll
           for (int i = 0; i < WI; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float ex = fast_exp2(fmaf(z[i][e], LOG2E, -ml));
+              const float arg = fmaf(z[i][e], kl, -ml);
+              const float ex = fast_exp2(arg);
               sp[e] = sp[e] + ex;
-              if (METRICS) up[e] = fmaf(ex, fmaxf(z[i][e] - mnew, -1e30f), up[e]);
+              // (the floor keeps a logit of -inf, a row past V or a bias of
+              // -inf, at 0 * -1e30 = 0 instead of 0 * -inf = NaN)
+              if (METRICS) up[e] = fmaf(ex, fmaxf(arg, -1e30f), up[e]);
             }
           float sum = (sp[0] + sp[1]) + (sp[2] + sp[3]), usum = 0.f;
           if (METRICS) usum = (up[0] + up[1]) + (up[2] + up[3]);
           sum = col_sum4(sum);
-          if (METRICS) usum = col_sum4(usum);
+          if (METRICS) usum = col_sum4(usum) * LN2;
           if (q == 0) {
             if (mold == -INFINITY) {
               FST(1, j) = sum;
@@ -276,15 +303,14 @@ __global__ __launch_bounds__(W * 64) void fwd_tiles_kernel(FwdArgs a) {
           }
         }
         if (METRICS && zmax > FST(4, j)) {
-          int idx = 0x7fffffff;
+          // the first row of the column's largest key: a select per element,
+          // from the last row to the first
+          int loc = -1;
 #pragma unroll
-          for (int i = 0; i < WI; ++i)
+          for (int i = WI - 1; i >= 0; --i)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int v = vq + 16 * i + e;
-              if (z[i][e] == zmax && v < idx) idx = v;
-            }
-          idx = col_min4(idx);
+            for (int e = 3; e >= 0; --e) loc = z[i][e] == kmax ? 16 * i + e : loc;
+          const int idx = col_min4(loc >= 0 ? vq + loc : 0x7fffffff);
           if (q == 0) {
             FST(4, j) = zmax;
             FST(5, j) = __int_as_float(idx);
@@ -299,7 +325,7 @@ __global__ __launch_bounds__(W * 64) void fwd_tiles_kernel(FwdArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               if (i == ti && e == te) zv = z[i][e];
-          FST(3, j) = zv;
+          FST(3, j) = kz * zv;
         }
       }
     }
@@ -833,8 +859,18 @@ __device__ __forceinline__ void g_tile(const GArgs& a, int bid, int nblocks) {
   }
 
   const int vq = (int)v0 + wm * 16 * WI + 4 * q;  // row of acc[i][.][e]: vq + 16 i + e
+  // The logit's key as in the forward: with a soft cap the exp2 argument
+  // x = 2 log2(e) s (y + b) / cap of th = tanh(s (y + b) / cap), else
+  // s (y + b); the bias folds into one FMA.
+  const float kscale = CAP ? a.s * a.inv_cap * (2.f * LOG2E) : a.s;
   float bv[WI][4];
   load_bias_rows<D, BIAS, WI>(bv, a.bias, vq, a.V);
+  if (BIAS) {
+#pragma unroll
+    for (int i = 0; i < WI; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bv[i][e] = bv[i][e] * kscale;
+  }
   // The one-hot term: column j's target row, as 16 i + e relative to vq, when
   // this lane holds it (rare), and its value dz/draw * factor there.
   int tl[WJ];
@@ -852,15 +888,15 @@ __device__ __forceinline__ void g_tile(const GArgs& a, int bid, int nblocks) {
   if (any_t) {
 #pragma unroll
     for (int j = 0; j < WJ; ++j) {
-      float yr = 0.f;
+      float xr = 0.f;
 #pragma unroll
       for (int i = 0; i < WI; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (16 * i + e == tl[j]) yr = BIAS ? acc[i][j][e] + bv[i][e] : acc[i][j][e];
+          if (16 * i + e == tl[j]) xr = BIAS ? fmaf(acc[i][j][e], kscale, bv[i][e]) : acc[i][j][e] * kscale;
       float cf = 1.f;
       if (CAP) {
-        const float qc = tanh_exp(yr * (a.s * a.inv_cap));  // z / cap
+        const float qc = tanh_of_exp2_arg(xr);  // z / cap
         cf = fmaf(-qc, qc, 1.f);
       }
       if (tl[j] >= 0) onehot[j] = cf * (coef[j] * a.keep);
@@ -877,18 +913,27 @@ __device__ __forceinline__ void g_tile(const GArgs& a, int bid, int nblocks) {
     ec[j] = a.eps_v * coef[j];
   }
   if constexpr (CAP) {
-    // z = cap th with th = tanh(s y / cap); dz/dy = s (1 - th^2)
-    const float sic = a.s * a.inv_cap, cl = a.cap * LOG2E;
+    // z = cap th; dz/dy = s (1 - th^2)
+    const float cl = a.cap * LOG2E;
 #pragma unroll
     for (int i = 0; i < WI; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
 #pragma unroll
         for (int j = 0; j < WJ; ++j) {
-          float y = acc[i][j][e];
-          if (BIAS) y = y + bv[i][e];
-          const float th = tanh_exp(y * sic);
+          const float x = BIAS ? fmaf(acc[i][j][e], kscale, bv[i][e]) : acc[i][j][e] * kscale;
+          const float th = tanh_of_exp2_arg(x);
           acc[i][j][e] = fmaf(fast_exp2(fmaf(th, cl, -ll[j])), pc[j], -ec[j]) * fmaf(-th, th, 1.f);
+        }
+  } else if constexpr (BIAS) {
+#pragma unroll
+    for (int i = 0; i < WI; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int j = 0; j < WJ; ++j) {
+          const float z = fmaf(acc[i][j][e], kscale, bv[i][e]);
+          acc[i][j][e] = fmaf(fast_exp2(fmaf(z, LOG2E, -ll[j])), pc[j], -ec[j]);
         }
   } else {
     const float sl = a.s * LOG2E;
@@ -897,11 +942,7 @@ __device__ __forceinline__ void g_tile(const GArgs& a, int bid, int nblocks) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int j = 0; j < WJ; ++j) {
-          float y = acc[i][j][e];
-          if (BIAS) y = y + bv[i][e];
-          acc[i][j][e] = fmaf(fast_exp2(fmaf(y, sl, -ll[j])), pc[j], -ec[j]);
-        }
+        for (int j = 0; j < WJ; ++j) acc[i][j][e] = fmaf(fast_exp2(fmaf(acc[i][j][e], sl, -ll[j])), pc[j], -ec[j]);
   }
   if (any_t) {
 #pragma unroll
@@ -984,10 +1025,7 @@ __device__ __forceinline__ void g_tile(const GArgs& a, int bid, int nblocks) {
         float sb = acc[i][0][e];
 #pragma unroll
         for (int j = 1; j < WJ; ++j) sb = sb + acc[i][j][e];
-        sb += __shfl_xor(sb, 1);
-        sb += __shfl_xor(sb, 2);
-        sb += __shfl_xor(sb, 4);
-        sb += __shfl_xor(sb, 8);
+        sb = row_sum16(sb);
         const int v = vq + 16 * i + e;
         const int vl = v - (int)a.c0;
         if (c16 == 0 && v < a.V && vl < a.cv) a.dbpart[(int64_t)(Gemm<W>::GN * tt + wn) * a.V + v] = sb;
