@@ -102,6 +102,31 @@ def test_per_row_loss_independent_of_batch_split():
         assert bitwise_equal(sub[3][0], full[3][0][lo:hi].contiguous())  # grad_hidden rows
 
 
+def test_forward_rows_independent_of_split_grouping():
+    # V = 128256: 501 vocabulary tiles in 126 splits of 4 (by V only).  A forward
+    # workgroup walks a run of consecutive splits chosen from N: 4 splits at
+    # N = 4096 (16 token tiles), 2 at N = 1024, 1 at N = 256.  Each split ends in
+    # its own record, so every row's lse, loss and argmax must keep its bits.
+    import linear_cross_entropy_fwd_amd as flce
+    w = W["transforms_bf16"].resized(n=4096, h=64, v=128256, reduction="none")
+    log_case("split grouping " + w.name)
+    g = gpu_inputs(fi.generate(w))
+
+    def rows(n):
+        pred = torch.empty(n, dtype=torch.int64, device="cuda")
+        loss, lse, m = flce.flce_forward(g["hidden"][:n].contiguous(), g["weight"], g["targets"][:n].contiguous(),
+                                         g["bias"], ignore_index=w.ignore_index, logit_scale=w.logit_scale,
+                                         softcap=w.softcap, reduction="none", return_metrics=True, predictions=pred)
+        torch.cuda.synchronize()
+        return loss, lse, pred
+
+    full = rows(4096)
+    for n in (1024, 256):
+        sub = rows(n)
+        for a, b in zip(sub, full):
+            assert bitwise_equal(a, b[:n].contiguous())
+
+
 def test_zero_scale_gives_ln_v_and_zero_grads():
     w = W["transforms_bf16"].resized(n=200, h=128, v=3000, logit_scale=0.0, reduction="mean")
     log_case("zero scale " + w.name)
