@@ -139,6 +139,21 @@ typedef struct flce_problem {
 size_t flce_forward_workspace_size(const flce_problem_t* p);
 size_t flce_backward_workspace_size(const flce_problem_t* p);
 
+/* The forward's vocabulary splits for problem *p (card: "Algorithm", the
+ * online log-sum-exp over tiles, and "Metrics for free"): each row's
+ * vocabulary is swept in *n_splits runs of *tiles_per_split 256-id tiles (the
+ * last run may be shorter), each ending in one partial state per row, merged
+ * in a fixed order by the combine.  The split size depends on V only (or on
+ * fwd_tiles_per_split), so a row's result does not depend on N.
+ * *splits_per_workgroup consecutive splits of one 256-token tile are walked
+ * by one workgroup; that grouping depends on N and changes no result.
+ * Small fp32 problems (see flce_backward_plan) take no splits:
+ * *tiles_per_split = *n_splits = *splits_per_workgroup = 0.
+ * Pure host function; any output pointer may be NULL.
+ * FLCE_ERR_INVALID_ARGUMENT or FLCE_ERR_UNSUPPORTED for an invalid *p. */
+flce_status_t flce_forward_plan(const flce_problem_t* p, int32_t* tiles_per_split, int32_t* n_splits,
+                                int32_t* splits_per_workgroup);
+
 /* The backward's vocabulary chunking for problem *p (card: "Algorithm",
  * backward: each logit tile is recomputed; here the vocabulary is swept in
  * chunks of *chunk ids, the last one *last_chunk ids, *n_chunks in all, each

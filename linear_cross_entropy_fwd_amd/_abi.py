@@ -73,6 +73,8 @@ _SIGNATURES = {
     "flce_forward_backward": (ctypes.c_int, [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                              _VP, ctypes.c_size_t, _VP]),
     "flce_forward_status": (ctypes.c_int, [_PP, _VP, ctypes.POINTER(ctypes.c_uint32), _VP]),
+    "flce_forward_plan": (ctypes.c_int, [_PP, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
+                                         ctypes.POINTER(ctypes.c_int32)]),
     "flce_backward_plan": (ctypes.c_int, [_PP, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
                                           ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32)]),
     "flce_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -170,6 +172,14 @@ def flce_forward_status(p: Problem, workspace, stream) -> int:
     out = ctypes.c_uint32(0)
     check(library().flce_forward_status(ctypes.byref(p), workspace, ctypes.byref(out), stream))
     return int(out.value)
+
+
+def flce_forward_plan(p: Problem):
+    """(tiles_per_split, n_splits, splits_per_workgroup): the forward's
+    vocabulary splits and how many consecutive ones a workgroup walks."""
+    t, n, g = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    check(library().flce_forward_plan(ctypes.byref(p), ctypes.byref(t), ctypes.byref(n), ctypes.byref(g)))
+    return int(t.value), int(n.value), int(g.value)
 
 
 def flce_backward_plan(p: Problem, with_launches: bool = False):

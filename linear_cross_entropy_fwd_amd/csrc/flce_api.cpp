@@ -409,6 +409,18 @@ flce::SmallArgs small_args(const flce_problem_t& p, const char* hidden, const vo
 
 extern "C" {
 
+flce_status_t flce_forward_plan(const flce_problem_t* p, int32_t* tiles_per_split, int32_t* n_splits,
+                                int32_t* splits_per_workgroup) {
+  const flce_status_t s = check_problem(p);
+  if (s != FLCE_OK) return s;
+  const FwdLayout L = fwd_layout(*p);
+  const bool small = small_path(*p);
+  if (tiles_per_split) *tiles_per_split = small ? 0 : L.tiles_per_split;
+  if (n_splits) *n_splits = small ? 0 : L.n_splits;
+  if (splits_per_workgroup) *splits_per_workgroup = small ? 0 : L.splits_per_wg;
+  return FLCE_OK;
+}
+
 flce_status_t flce_backward_plan(const flce_problem_t* p, int64_t* chunk, int64_t* n_chunks,
                                  int64_t* last_chunk, int32_t* one_launch_per_chunk) {
   const flce_status_t s = check_problem(p);

@@ -72,6 +72,9 @@ static void run(flce_problem_t p, bool strided = false) {
     p.targets_seq_stride = 2 * (p.seq_len + 1);
   }
   hoststub::hidden_ptr = HID;
+  int32_t tps = -1, nsp = -1, gsp = -1;
+  expect(flce_forward_plan(&p, &tps, &nsp, &gsp), FLCE_OK, "forward plan", p);
+  expect(flce_forward_plan(&p, nullptr, nullptr, nullptr), FLCE_OK, "forward plan, no outputs", p);
   const size_t fs = flce_forward_workspace_size(&p), bs = flce_backward_workspace_size(&p);
   const size_t fbs = flce_forward_backward_workspace_size(&p);
   hoststub::begin(WSP, fs);

@@ -250,6 +250,34 @@ def test_forward_backward_validates_like_the_two_calls():
     assert "grad_bias" in _abi.last_error()
 
 
+# The default forward plan at the five workloads (tiles a split, splits, splits a workgroup).  A
+# split is at least 4 tiles and there are at most 128 of them (by V only); a workgroup walks the
+# run of splits with the fewest rounds of 256 workgroups times tiles walked, at most 16 tiles,
+# ties to the longer run.
+@pytest.mark.parametrize("n,h,v,dtype,plan", [
+    (2048, 2048, 32000, BF16, (4, 32, 1)),       # 8 x 32 = 256 workgroups: one round
+    (4096, 4096, 128256, BF16, (4, 126, 4)),     # 16 x 32 groups of 16 tiles: two rounds
+    (8192, 3584, 152064, BF16, (5, 119, 3)),     # 32 x 40 groups of 15 tiles: five rounds
+    (16384, 2048, 262144, BF16, (8, 128, 2)),    # 64 x 64 groups of 16 tiles: sixteen rounds
+    (64, 128, 1000, F32, (0, 0, 0)),             # the small fp32 path: no splits
+])
+def test_forward_plan_at_the_workloads(n, h, v, dtype, plan):
+    assert _abi.flce_forward_plan(make_problem(n, h, v, dtype)) == plan
+
+
+def test_forward_plan_split_by_v_only_and_override():
+    for v in (1000, 32000, 128256, 262144, 1 << 20):
+        plans = [_abi.flce_forward_plan(make_problem(n, 1024, v, BF16)) for n in (257, 1024, 4096, 16384, 65536)]
+        assert len({(t, s) for t, s, _ in plans}) == 1, plans       # the split: V only
+        for t, s, g in plans:
+            tiles = -(-v // 256)
+            assert t >= min(4, tiles) and s <= 128 and (s - 1) * t < tiles <= s * t
+            assert 1 <= g <= s and (g == 1 or g * t <= 16)
+    assert _abi.flce_forward_plan(make_problem(4096, 4096, 128256, BF16, fwd_tiles_per_split=3)) == (3, 167, 1)
+    with pytest.raises(_abi.FlceError):
+        _abi.flce_forward_plan(make_problem(64, 100, 1000, BF16))
+
+
 # The default backward plan at the four bf16 workloads (chunk ids, chunks, last chunk).  The
 # chunk is at most a quarter of V and 48 tiles, scored by how full grad_weight's last round of
 # 256 workgroups is; a last chunk under a quarter of a chunk joins the one before it.

@@ -120,6 +120,10 @@ def test_forward_rows_independent_of_split_grouping():
         torch.cuda.synchronize()
         return loss, lse, pred
 
+    from linear_cross_entropy_fwd_amd import _abi
+    groups = [_abi.flce_forward_plan(flce.problem_for(g["hidden"][:n], g["weight"], g["bias"], softcap=w.softcap,
+                                                      return_metrics=True)) for n in (4096, 1024, 256)]
+    assert groups == [(4, 126, 4), (4, 126, 2), (4, 126, 1)], groups
     full = rows(4096)
     for n in (1024, 256):
         sub = rows(n)
