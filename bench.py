@@ -32,9 +32,14 @@ METRIC = "fwd+bwd TFLOP/s (8*N*H*V) and MFMA util at N=4096,H=4096,V=128256 bf16
 PEAK_BF16_TFLOPS = 2516.6          # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
 PEAK_TFLOPS = {"bf16": PEAK_BF16_TFLOPS, "f16": PEAK_BF16_TFLOPS, "f32": 157.3}  # dense MFMA per dtype
 PEAK_HBM_GBS = 8000.0
+# The sources that decide what a launch reads and writes: the kernels, their
+# device headers (tile order, record layouts) and the host planner (splits,
+# chunks, grids).
 KERNEL_SOURCES = ["linear_cross_entropy_fwd_amd/csrc/flce_kernels.hip",
                   "linear_cross_entropy_fwd_amd/csrc/flce_small.hip",
-                  "linear_cross_entropy_fwd_amd/csrc/flce_device.h"]
+                  "linear_cross_entropy_fwd_amd/csrc/flce_device.h",
+                  "linear_cross_entropy_fwd_amd/csrc/flce_plan.h",
+                  "linear_cross_entropy_fwd_amd/csrc/flce_api.cpp"]
 
 
 def kernel_source_hash() -> str:
