@@ -333,7 +333,9 @@ __global__ __launch_bounds__(W * 64) void fwd_tiles_kernel(FwdArgs a) {
     // The split is complete.  Waves wm = 0 and wm = 1 hold the same token
     // columns over disjoint vocabulary rows: the first merges the second's
     // state (read from its LDS slots) into its own and writes the split's
-    // record.  The stage buffers may hold the next split's first copies.
+    // record.  The stage buffers may hold the next split's first copies; the
+    // record's stores are issued after them, so the next GEMM's first wait
+    // covers the stores too (once per split, not per tile).
     lds_barrier();
     if (wm == 0) {
       // rows of part and zt_rows are padded to whole tiles (pitch npad), so no
