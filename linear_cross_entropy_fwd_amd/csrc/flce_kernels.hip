@@ -9,7 +9,9 @@
 // ids run along the MFMA row axis, so each lane owns 4 token columns and
 // reduces its 64 logits per column in registers; the two half-waves and the
 // two waves that share a token merge once per split.  Nothing of size N x V
-// is written: only 6 words per (row, split).
+// is written: per (row, split) a record of m and S (plus U and the argmax
+// value and id with metrics, plus the logit sum with label smoothing), and
+// per row the target logit from the split that holds the target.
 //
 // Backward (card: "Algorithm", backward): per vocabulary chunk of Cv ids,
 // recompute the logit tiles and form G = (p - onehot) * coef * dz/draw in the
@@ -138,8 +140,9 @@ __device__ __forceinline__ int col_min4(int x) {
 // ------------------------------------------------------------------ forward tiles
 
 // Per-column online state between vocabulary tiles, in LDS so that it does
-// not occupy registers across the GEMM: 7 values x WJ column blocks x 16
-// columns per wave (14 KB next to the 128 KB stage buffers).
+// not occupy registers across the GEMM: 8 values (m, S, U, target logit,
+// argmax value and id, target id, logit sum) x WJ column blocks x 16 columns
+// per wave (16 KB next to the 128 KB stage buffers).
 __shared__ float g_fwd_state[8 * 4 * 8 * 16];
 
 template <int D, bool METRICS, bool BIAS, bool CAP, int W>
