@@ -155,7 +155,9 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 // grid of wave tiles of WI x WJ 16x16 blocks.  W = 8: two waves per SIMD,
 // 128 x 64 per wave (128 accumulator registers); while one wave of a SIMD
 // waits (a copy being issued, a barrier), the other keeps the MFMA unit busy.
-// (One wave per SIMD with 128 x 128 each ran at half the rate.)
+// (One wave per SIMD with 128 x 128 each, the 256 accumulators in AGPRs,
+// measured no faster in the K loops of the real kernels and slower in
+// their epilogues, where no second wave fills the latencies.)
 template <int W> struct Geo;
 template <> struct Geo<8> { static constexpr int WI = 8, WJ = 4; };
 template <int W> struct Gemm {
