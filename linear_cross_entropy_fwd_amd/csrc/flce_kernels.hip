@@ -800,6 +800,11 @@ struct WcTSide {
   }
 };
 
+// Per-token inputs of the recompute tile (see g_tile).
+__shared__ int g_col_code[TILE];
+__shared__ float g_col_lse[TILE];
+__shared__ float g_col_gr[TILE];
+
 // Recompute one (token tile, vocabulary tile) of the chunk and write
 // G = coef * (softmax - onehot) * dz/draw (G^T too when asked, grad_bias partials).
 // A = weight rows (vocabulary on the MFMA row axis), B = hidden rows.
@@ -823,8 +828,33 @@ __device__ __forceinline__ void g_tile(const GArgs& a, int bid, int nblocks) {
 
   Panel A{a.weight + v0 * rowb, rowb, (int)min<int64_t>(TILE, a.V - v0), rowb};
   Panel B{a.hidden + n0 * rowb, rowb, (int)min<int64_t>(TILE, a.N - n0), rowb};
+  // Without the W_c^T side job (whose LDS tile leaves no room), the tile's
+  // per-token inputs are loaded ahead of the operand copies (their latency
+  // then passes with the first stages') and parked in LDS until the
+  // epilogue: thread c < 256 takes token n0 + c.  Target code: the id, -1
+  // for a dead token (past N or ignored), -2 for an id outside [0, V).
+  constexpr bool PARK = !WCT;
   f32x4_t acc[WI][WJ];
-  if constexpr (EB == 2 && WCT) {
+  if constexpr (PARK) {
+    const int64_t cn = n0 + t;
+    int64_t col_tv = a.ignore_index;
+    float col_lse = 0.f, col_gr = 1.f;
+    if (t < TILE && cn < a.N) {
+      col_tv = a.targets[cn];
+      col_lse = a.lse[cn];
+      if (a.none_reduction && a.grad_rows) col_gr = a.grad_rows[cn];
+    }
+    CopyPlan<W> cp;
+    gemm_prefetch<W>(cp, A, B);
+    sched_fence();  // the loads' first use stays behind the copies
+    if (t < TILE) {
+      g_col_code[t] = col_tv == a.ignore_index ? -1 : (col_tv < 0 || col_tv >= a.V) ? -2 : (int)col_tv;
+      g_col_lse[t] = col_lse;
+      g_col_gr[t] = col_gr;
+    }
+    NoSide none;
+    gemm_run<D, W>(acc, cp, A, none);
+  } else if constexpr (EB == 2) {
     // no W_c^T wanted: a first stage past every stage selects none
     WcTSide side{reinterpret_cast<uint16_t*>(a.WcT), a.H, a.cvpad, a.wct_ld, vl0, a.n_tok_tiles,
                  (uint32_t)__builtin_amdgcn_readfirstlane(t >> 6), a.WcT != nullptr ? tt : (1 << 30), 0ull};
@@ -838,27 +868,38 @@ __device__ __forceinline__ void g_tile(const GArgs& a, int bid, int nblocks) {
   // id.  A dead column (past N or ignored) gets lse = +inf and factor 0, so
   // its p is 0 and its G column 0 without a select per element.
   //   dL/dz_j = w (pscale p_j - keep [j = t] - eps/V),  keep = 1 - eps
+  // (parked: g_col_* were written before the K loop's barriers)
   float lse[WJ], coef[WJ], pscale[WJ];
   int tgt[WJ];
 #pragma unroll
   for (int j = 0; j < WJ; ++j) {
-    const int64_t n = n0 + wn * 16 * WJ + 16 * j + c16;
+    const int col = wn * 16 * WJ + 16 * j + c16;
+    const int64_t n = n0 + col;
+    int code = -1;
+    float cl = 0.f, gr = 1.f;
+    if constexpr (PARK) {
+      code = g_col_code[col];
+      cl = g_col_lse[col];
+      gr = g_col_gr[col];
+    } else if (n < a.N) {
+      const int64_t tv = a.targets[n];
+      code = tv == a.ignore_index ? -1 : (tv < 0 || tv >= a.V) ? -2 : (int)tv;
+      if (code != -1) cl = a.lse[n];
+      if (code >= 0 && a.none_reduction && a.grad_rows) gr = a.grad_rows[n];
+    }
     tgt[j] = -1;
     lse[j] = INFINITY;
     coef[j] = 0.f;
     pscale[j] = 1.f;
-    if (n < a.N) {
-      const int64_t tv = a.targets[n];
-      if (tv != a.ignore_index) {
-        lse[j] = a.lse[n];
-        pscale[j] = fmaf(a.zl2, lse[j], 1.f);
-        if (tv < 0 || tv >= a.V) {
-          coef[j] = NAN;
-        } else {
-          tgt[j] = (int)tv;
-          coef[j] = (a.none_reduction && a.grad_rows) ? a.grad_rows[n] : 1.f;
-          if (a.class_weight) coef[j] = coef[j] * a.class_weight[tv];
-        }
+    if (code != -1) {
+      lse[j] = cl;
+      pscale[j] = fmaf(a.zl2, lse[j], 1.f);
+      if (code == -2) {
+        coef[j] = NAN;
+      } else {
+        tgt[j] = code;
+        coef[j] = gr;
+        if (a.class_weight) coef[j] = coef[j] * a.class_weight[code];
       }
     }
   }
@@ -918,16 +959,25 @@ __device__ __forceinline__ void g_tile(const GArgs& a, int bid, int nblocks) {
     ec[j] = a.eps_v * coef[j];
   }
   if constexpr (CAP) {
-    // z = cap th; dz/dy = s (1 - th^2)
+    // z = cap th; dz/dy = s (1 - th^2).  Two passes over the tile, each
+    // element's th kept in its accumulator in between: the elements of a
+    // pass are independent, so their exp2 / reciprocal latencies overlap
+    // (done per element in one go, the chain ran one element at a time).
     const float cl = a.cap * LOG2E;
 #pragma unroll
     for (int i = 0; i < WI; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
 #pragma unroll
+        for (int j = 0; j < WJ; ++j)
+          acc[i][j][e] = tanh_of_exp2_arg(BIAS ? fmaf(acc[i][j][e], kscale, bv[i][e]) : acc[i][j][e] * kscale);
+#pragma unroll
+    for (int i = 0; i < WI; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
         for (int j = 0; j < WJ; ++j) {
-          const float x = BIAS ? fmaf(acc[i][j][e], kscale, bv[i][e]) : acc[i][j][e] * kscale;
-          const float th = tanh_of_exp2_arg(x);
+          const float th = acc[i][j][e];
           acc[i][j][e] = fmaf(fast_exp2(fmaf(th, cl, -ll[j])), pc[j], -ec[j]) * fmaf(-th, th, 1.f);
         }
   } else if constexpr (BIAS) {
