@@ -156,6 +156,41 @@ def test_plan_overrides(tps, chunk):
              bwd_vocab_chunk=chunk)
 
 
+def _random_configs(count, seed=20261202):
+    """Seeded draws over sizes, dtypes and loss options (ragged N, H and V,
+    plan overrides and every transform), for the sweep below."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for k in range(count):
+        dtype = ["bf16", "f16", "f32"][k % 3]
+        step = 4 if dtype == "f32" else 8  # a row must be whole 16-byte pieces
+        n = int(rng.integers(1, 700))
+        h = int(step * rng.integers(1, 66))
+        v = int(rng.integers(1, 3200))
+        cap = [None, 5.0, 30.0][int(rng.integers(0, 3))]
+        bias = None if rng.random() < 0.5 else 0.1
+        scale = [1.0, 0.5, 2.0][int(rng.integers(0, 3))]
+        red = ["mean", "sum", "none"][int(rng.integers(0, 3))]
+        metrics = bool(rng.random() < 0.5)
+        ign = [0.0, 0.1][int(rng.integers(0, 2))]
+        chunk = [0, 256, 512][int(rng.integers(0, 3))]
+        tps = [0, 1, 2][int(rng.integers(0, 3))]
+        go = rng.standard_normal(n).astype(np.float32) if red == "none" else None
+        w = W["transforms_bf16"].resized(n=n, h=h, v=v, dtype=dtype, softcap=cap, bias_std=bias,
+                                         logit_scale=scale, reduction=red, return_metrics=metrics,
+                                         ignore_frac=ign, seed=1000 + k)
+        out.append(pytest.param(w, chunk, tps, go, id=f"{k}-{dtype}-n{n}-h{h}-v{v}"))
+    return out
+
+
+@pytest.mark.parametrize("w,chunk,tps,go", _random_configs(12))
+def test_random_configurations(w, chunk, tps, go):
+    """A seeded sweep of random shapes and options against the oracle: the
+    fixed cases above pin each feature, this one checks their combinations
+    at sizes nobody picked by hand."""
+    run_case(w, bwd_vocab_chunk=chunk, fwd_tiles_per_split=tps, grad_output=go)
+
+
 def test_ignore_index_edge_cases():
     base = W["tiny_f32"].resized(n=130, h=64, v=500)
     d = fi.generate(base)
