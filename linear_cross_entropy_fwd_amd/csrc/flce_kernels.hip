@@ -7,8 +7,9 @@
 // (running max m and rescaled sum S), together with the target-logit gather,
 // the running argmax and the entropy sum U = sum e^{z-m} (z-m).  Vocabulary
 // ids run along the MFMA row axis, so each lane owns 4 token columns and
-// reduces its 64 logits per column in registers; the two half-waves and the
-// two waves that share a token merge once per split.  Nothing of size N x V
+// reduces its 32 logits per column in registers; the four lanes that share
+// a column merge by lane shuffles every tile, and the two waves that share a
+// token merge once per split.  Nothing of size N x V
 // is written: per (row, split) a record of m and S (plus U and the argmax
 // value and id with metrics, plus the logit sum with label smoothing), and
 // per row the target logit from the split that holds the target.
