@@ -608,15 +608,19 @@ __device__ __forceinline__ void tile16_put4(int row, int col, float x0, float x1
 
 // Stores the staged tile: row r, columns c0.. go to dst + r * ld (elements),
 // for r < rows and chunk columns below cols (a multiple of 8).  Callers put a
-// barrier between the last tile16_put4 and this.
-template <int NT>
+// barrier between the last tile16_put4 and this.  STREAM: non-temporal
+// stores, which do not keep the lines in the caches.
+template <int NT, bool STREAM = false>
 __device__ __forceinline__ void tile16_store(uint16_t* dst, int64_t ld, int rows, int cols, int t) {
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 #pragma unroll 4
   for (int k = t; k < TILE * 32; k += NT) {
     const int r = k >> 5, c = k & 31;
     if (r < rows && 8 * c < cols) {
-      const uint4 v = *reinterpret_cast<const uint4*>(tile16_addr(r, 8 * c));
-      *reinterpret_cast<uint4*>(dst + (int64_t)r * ld + 8 * c) = v;
+      const u32x4v v = *reinterpret_cast<const u32x4v*>(tile16_addr(r, 8 * c));
+      u32x4v* p = reinterpret_cast<u32x4v*>(dst + (int64_t)r * ld + 8 * c);
+      if constexpr (STREAM) __builtin_nontemporal_store(v, p);
+      else *p = v;
     }
   }
 }
@@ -1035,7 +1039,11 @@ __device__ __forceinline__ void g_tile(const GArgs& a, int bid, int nblocks) {
                          acc[i][j][2], acc[i][j][3]);
       __syncthreads();
       const int rows = (int)min<int64_t>(TILE, a.npad - n0), cols = min(TILE, a.cvpad - vl0);
-      if (a.G) tile16_store<W * 64>(reinterpret_cast<uint16_t*>(a.G) + n0 * a.g_ld + vl0, a.g_ld, rows, cols, t);
+      if (a.G) {
+        uint16_t* gdst = reinterpret_cast<uint16_t*>(a.G) + n0 * a.g_ld + vl0;
+        if (a.g_stream) tile16_store<W * 64, true>(gdst, a.g_ld, rows, cols, t);
+        else tile16_store<W * 64>(gdst, a.g_ld, rows, cols, t);
+      }
       if (a.GT) tile16_store_t(reinterpret_cast<uint16_t*>(a.GT) + (int64_t)vl0 * a.npad + n0, a.npad, rows, cols, t);
     }
   }

@@ -187,6 +187,7 @@ struct GArgs {
   int64_t N, H, V, ignore_index, c0;
   int cv, cvpad, npad, n_tok_tiles, n_voc_tiles;
   int g_ld, wct_ld;        // row pitches (elements) of G and W_c^T
+  int g_stream;            // store G with streaming (non-temporal) stores
   int none_reduction;
   float s, cap, inv_cap;
   const float* class_weight;  // [V] or null
