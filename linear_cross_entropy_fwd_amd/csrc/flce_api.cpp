@@ -269,6 +269,9 @@ struct BwdLayout {
   // both contractions of the last one (bwd_step_kernel), so G is kept twice
   // (the chunk, or pair of chunks, being contracted and the one being written)
   bool fused;
+  // caching hints: G stored with streaming stores; grad_hidden's running
+  // sums read and written with streaming accesses
+  bool g_stream, acc_stream;
   TokLayout tok;
   size_t off_scale, off_ht, off_wct, off_g, off_gt, off_dh, off_db, off_hrows, off_tgt, total;
 };
@@ -342,6 +345,24 @@ BwdLayout bwd_layout(const flce_problem_t& p) {
   const int64_t acc_elems = L.dk ? (int64_t)L.n_tok_tiles * L.n_h_tiles * kTile * kTile : N * H;
   L.off_dh = take(L.n_chunks > L.dh_pair || L.dh_split > 1 ? (size_t)L.dh_split * acc_elems * 4 : 0);
   L.off_db = take(p.has_bias ? (size_t)flce::kBiasParts * L.n_tok_tiles * V * 4 : 0);
+  // Caching hints (results are the same bits either way), from A/B runs of
+  // one box session each.  G buffers larger than the last-level cache: G
+  // leaves with streaming stores (1.5-1.7 % off the backward at N = 16384,
+  // H = 2048, V = 262144, 0.2-0.7 % at N = 8192, H = 3584, V = 152064; at
+  // the head shape, whose two buffers fit, plain stores are 0.4 % faster).
+  // A launch's data (G buffers, running sums, the chunk's weight rows,
+  // hidden and hidden^T) larger than that cache: the running sums, read
+  // once at the start of a launch and written once at its end, bypass it
+  // (1.7 % off the backward at the head shape, 0.8 % at the two above; at
+  // N = 2048, H = 2048, V = 32000, where everything fits, 1.5 % slower).
+  const int64_t g_bytes = (L.fused ? 2 : 1) * L.npad * L.gld * eb;
+  L.g_stream = g_bytes > kLastLevelCacheBytes;
+  {
+    const int64_t sums = (L.n_chunks > L.dh_pair || L.dh_split > 1) ? (int64_t)L.dh_split * acc_elems * 4 : 0;
+    const int64_t rows = std::min<int64_t>(L.chunk * L.dh_pair, V) * H * eb;
+    const int64_t set = g_bytes + sums + rows + 2 * L.npad * H * eb;
+    L.acc_stream = set > kLastLevelCacheBytes;
+  }
   L.tok = tok_layout(p);
   L.off_hrows = take(L.tok.h_gather ? (size_t)N * H * eb : 0);
   L.off_tgt = take(L.tok.t_gather ? (size_t)N * 8 : 0);
@@ -671,6 +692,7 @@ static hipError_t backward_fused(const flce_problem_t& p, const BwdLayout& L, co
       da.bk = 1;
       da.Wk = weight + (int64_t)(c - slot) * L.chunk * H * eb;
       da.wrows = V - (int64_t)(c - slot) * L.chunk;
+      da.acc_stream = L.acc_stream;
       sa.dh_grid = flce::backward_dh_grid(L.n_h_tiles, L.n_tok_tiles);
       sa.nb_dh = sa.dh_grid * L.dh_split;
     }
@@ -755,12 +777,7 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
     gb.WcT = nullptr;
     gb.g_ld = (int)L.gld;
     gb.wct_ld = (int)L.gld;
-    // G buffers larger than the last-level cache: G goes out with streaming
-    // stores (measured: 1.7 % off the backward at N = 16384, H = 2048,
-    // V = 262144 and 0.7 % at N = 8192, H = 3584, V = 152064; at the head
-    // shape, whose two buffers fit, plain stores are 0.4 % faster).  A
-    // caching hint only: results are the same bits either way.
-    gb.g_stream = 2 * L.npad * L.gld * eb > kLastLevelCacheBytes;
+    gb.g_stream = L.g_stream;
     gb.dbpart = want_db ? db : nullptr;
     gb.N = N;
     gb.H = H;
@@ -871,6 +888,7 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
       da.bk = L.dk ? 1 : 0;
       da.Wk = reinterpret_cast<const char*>(weight) + (int64_t)(c - slot) * L.chunk * H * eb;
       da.wrows = V - (int64_t)(c - slot) * L.chunk;
+      da.acc_stream = L.acc_stream;
       if ((e = flce::launch_backward_dh(p->dtype, da, st)) != hipSuccess) return hip_fail(e, "grad_hidden kernel");
       if (da.last && L.dh_split > 1) {
         flce::DhFinalArgs fa{dh, scale, reinterpret_cast<char*>(grad_hidden), da.acc_stride, da.acc_stride,

@@ -1163,6 +1163,8 @@ __device__ __forceinline__ void dh_tile(const DhArgs& a, int bid, int nblocks, i
       for (int j = 0; j < WJ; ++j) {
         if (a.first) {
           acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        } else if (a.acc_stream) {
+          acc[i][j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(tp + (i * WJ + j) * (W * 64)));
         } else {
           const float4 o = tp[(i * WJ + j) * (W * 64)];
           acc[i][j] = f32x4_t{o.x, o.y, o.z, o.w};
@@ -1192,6 +1194,12 @@ __device__ __forceinline__ void dh_tile(const DhArgs& a, int bid, int nblocks, i
         tile16_store_t(reinterpret_cast<uint16_t*>(a.out) + n0 * a.H + h0, a.H, (int)min<int64_t>(TILE, a.H - h0),
                        (int)min<int64_t>(TILE, a.N - n0), t);
       }
+    } else if (a.acc_stream) {
+#pragma unroll
+      for (int i = 0; i < WI; ++i)
+#pragma unroll
+        for (int j = 0; j < WJ; ++j)
+          __builtin_nontemporal_store(acc[i][j], reinterpret_cast<f32x4_t*>(tp + (i * WJ + j) * (W * 64)));
     } else {
 #pragma unroll
       for (int i = 0; i < WI; ++i)

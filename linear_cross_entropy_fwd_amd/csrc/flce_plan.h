@@ -208,6 +208,7 @@ struct DhArgs {
   int bk;
   const char* Wk;
   int64_t wrows;
+  int acc_stream;  // bk: read and write the running sums with streaming (non-temporal) accesses
 };
 
 // grad_hidden = the fixed-order sum of the ksplit accumulators, in the dtype.
