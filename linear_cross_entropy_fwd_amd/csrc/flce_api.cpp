@@ -349,12 +349,13 @@ BwdLayout bwd_layout(const flce_problem_t& p) {
   // one box session each.  G buffers larger than the last-level cache: G
   // leaves with streaming stores (1.5-1.7 % off the backward at N = 16384,
   // H = 2048, V = 262144, 0.2-0.7 % at N = 8192, H = 3584, V = 152064; at
-  // the head shape, whose two buffers fit, plain stores are 0.4 % faster).
-  // A launch's data (G buffers, running sums, the chunk's weight rows,
-  // hidden and hidden^T) larger than that cache: the running sums, read
-  // once at the start of a launch and written once at its end, bypass it
-  // (1.7 % off the backward at the head shape, 0.8 % at the two above; at
-  // N = 2048, H = 2048, V = 32000, where everything fits, 1.5 % slower).
+  // N = 4096, H = 4096, V = 128256, whose two buffers fit, plain stores are
+  // 0.4-1 % faster).  A launch's data (G buffers, running sums, the chunk's
+  // weight rows, hidden and hidden^T) larger than that cache: the running
+  // sums, read once at the start of a launch and written once at its end,
+  // bypass it (1.7-2.1 % off the backward at N = 4096, H = 4096,
+  // V = 128256, 0.8-1.3 % at the two above; at N = 2048, H = 2048,
+  // V = 32000, where everything fits, 1.5 % slower).
   const int64_t g_bytes = (L.fused ? 2 : 1) * L.npad * L.gld * eb;
   L.g_stream = g_bytes > kLastLevelCacheBytes;
   {
