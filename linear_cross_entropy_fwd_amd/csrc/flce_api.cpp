@@ -60,8 +60,11 @@ int64_t cdiv(int64_t x, int64_t m) { return (x + m - 1) / m; }
 // The default backward chunk, in vocabulary tiles.  It depends on V and H
 // only, never on N, so that a row's gradient does not depend on how many
 // rows share the call (the chunking fixes grad_hidden's summation order).
-// At most cap = min(a quarter of V, kMaxChunkTiles) tiles, so the chunk
-// buffers stay far below N x V.  The candidates are cap and the multiples of
+// At most cap = min(a quarter of V rounded up to whole tiles, kMaxChunkTiles)
+// tiles, so the chunk buffers stay far below N x V.  (Rounded down, V = 32000
+// got 31-tile chunks: with 32 the recompute and grad_weight grids at
+// N = 2048, H = 2048 are whole rounds, 2.5-7 % off that backward.)  The
+// candidates are cap and the multiples of
 // 16 tiles below it (with those the recompute grid, token tiles x chunk
 // tiles, is whole rounds over the CUs whenever N is a multiple of 4096).
 // Each is scored by how full the last round of its grad_weight grid is
@@ -72,7 +75,7 @@ int64_t cdiv(int64_t x, int64_t m) { return (x + m - 1) / m; }
 // the backward; a 36-tile chunk at H = 3584 (a full last grad_weight round
 // but 4.5 recompute rounds) was 8 % slower than 48.
 int64_t default_chunk_tiles(int64_t H, int64_t V) {
-  const int64_t cap = std::max<int64_t>(1, std::min<int64_t>(kMaxChunkTiles, V / 4 / kTile));
+  const int64_t cap = std::max<int64_t>(1, std::min<int64_t>(kMaxChunkTiles, cdiv(V, 4 * kTile)));
   const int64_t h_tiles = cdiv(H, kTile);
   auto eff = [&](int64_t k) {
     const int64_t wg = h_tiles * k;

@@ -279,10 +279,11 @@ def test_forward_plan_split_by_v_only_and_override():
 
 
 # The default backward plan at the four bf16 workloads (chunk ids, chunks, last chunk).  The
-# chunk is at most a quarter of V and 48 tiles, scored by how full grad_weight's last round of
-# 256 workgroups is; a last chunk under a quarter of a chunk joins the one before it.
+# chunk is at most a quarter of V, rounded up to whole tiles, and 48 tiles, scored by how full
+# grad_weight's last round of 256 workgroups is; a last chunk under a quarter of a chunk joins
+# the one before it.
 @pytest.mark.parametrize("n,h,v,plan", [
-    (2048, 2048, 32000, (7936, 4, 8192)),       # 31-tile chunks; the 256-id remainder joins the last
+    (2048, 2048, 32000, (8192, 4, 7424)),       # 32-tile chunks: whole rounds of 256 workgroups
     (4096, 4096, 128256, (12288, 11, 5376)),
     (8192, 3584, 152064, (12288, 13, 4608)),
     (16384, 2048, 262144, (8192, 32, 8192)),    # 32 tiles: one full round of 8 x 32 grad_weight tiles

@@ -97,10 +97,10 @@ def test_grad_hidden_over_pairs_of_chunks(v, dtype):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_default_plan_with_an_absorbed_last_chunk(dtype):
-    """V = 2600 in default chunks of 512 ids leaves 40 ids, which join the
-    previous chunk (552 ids); with 5 token tiles the 16-bit recompute kernel
+    """V = 3100 in default chunks of 1024 ids leaves 28 ids, which join the
+    previous chunk (1052 ids); with 5 token tiles the 16-bit recompute kernel
     also writes W_c^T for that longer chunk."""
-    run_case(W["transforms_bf16"].resized(n=1030, h=256, v=2600, dtype=dtype))
+    run_case(W["transforms_bf16"].resized(n=1030, h=256, v=3100, dtype=dtype))
 
 
 def test_transforms_shape_bias_scale_cap_sum_metrics():
