@@ -8,7 +8,9 @@ flce_backward (recompute, grad_hidden, grad_weight) on the head-vocabulary
 workload N=4096 tokens, H=4096, V=128256, bf16, mean reduction, Zipf(1.1)
 targets with 5% ignored rows.  Inputs are synthetic (seeded), generated on
 the GPU and resident in HBM before the timed region; outputs and workspaces
-are allocated once and reused.
+are allocated once and reused.  Without --warmup the untimed warmup runs at
+least 3 steps and at least 0.5 s (the JSON line gives the count), since a
+sub-millisecond step otherwise starts at an idle clock.
 
 Prints one JSON line: throughput as TFLOP/s counting 8*N*H*V flops per step,
 the fraction of the dense bf16 MFMA peak, peak device memory above the
@@ -177,7 +179,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warmup steps (default: at least 3 and at least 0.5 s of them, so that "
+                         "short steps are timed at the clock a running job holds)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="rows of the workload the CPU oracle baseline runs (the whole head-shape "
@@ -277,11 +281,25 @@ def main():
         del src, dst
 
     run_bwd = args.phase == "both"
-    for _ in range(args.warmup):
-        forward()
-        if run_bwd:
-            backward()
-    torch.cuda.synchronize()
+    if args.warmup is not None:
+        for _ in range(args.warmup):
+            forward()
+            if run_bwd:
+                backward()
+        torch.cuda.synchronize()
+        warmup = args.warmup
+    else:
+        # Sub-millisecond steps start at an idle clock that takes tens of
+        # milliseconds of load to rise: warm for a time, not a step count.
+        warmup, group, t_warm = 0, 1, time.perf_counter()
+        while warmup < 3 or time.perf_counter() - t_warm < 0.5:
+            for _ in range(group):
+                forward()
+                if run_bwd:
+                    backward()
+            torch.cuda.synchronize()
+            warmup += group
+            group = min(2 * group, 64)
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -327,7 +345,7 @@ def main():
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",

@@ -63,7 +63,7 @@ int64_t cdiv(int64_t x, int64_t m) { return (x + m - 1) / m; }
 // At most cap = min(a quarter of V rounded up to whole tiles, kMaxChunkTiles)
 // tiles, so the chunk buffers stay far below N x V.  (Rounded down, V = 32000
 // got 31-tile chunks: with 32 the recompute and grad_weight grids at
-// N = 2048, H = 2048 are whole rounds, 2.5-7 % off that backward.)  The
+// N = 2048, H = 2048 are whole rounds, 0.4-0.8 % off that backward.)  The
 // candidates are cap and the multiples of
 // 16 tiles below it (with those the recompute grid, token tiles x chunk
 // tiles, is whole rounds over the CUs whenever N is a multiple of 4096).

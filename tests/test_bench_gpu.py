@@ -36,3 +36,16 @@ def test_bench_prints_one_json_line_with_the_contract_fields():
     # array; everything else the step allocates is an output the caller wanted.
     assert out["workspace_mb"] < out["n_by_v_bytes_mb"]
     assert out["peak_mem_incr_mb"] <= out["workspace_mb"] + out["outputs_mb"] + 1.0
+
+
+def test_bench_default_warmup_runs_for_a_time():
+    """Without --warmup the bench warms for at least 0.5 s and 3 steps and
+    reports the count it ran."""
+    cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "tiny_f32", "--steps", "2",
+           "--no-cpu-baseline"]
+    print("\n[case] bench.py on the tiny workload, default warmup", flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert res.returncode == 0, res.stderr[-2000:]
+    out = json.loads([line for line in res.stdout.splitlines() if line.strip()][-1])
+    # 0.5 s of steps well under 10 ms each
+    assert out["warmup"] >= 50 and out["steps"] == 2
