@@ -143,7 +143,7 @@ def test_workspace_sizes_scale_and_never_hold_n_by_v():
             bwd = _abi.flce_backward_workspace_size(p)
             nv_bytes = n * v * (4 if dt == F32 else 2)
             assert 0 < fwd < nv_bytes or n * v < 1 << 20
-            # the largest single backward buffer is a (N x chunk) gradient slab, at most N x V / 4;
+            # the largest single backward buffer is a (N x chunk) gradient slab, about N x V / 4 at most;
             # all of them together (with the split grad_hidden accumulators of small N x H grids)
             # stay within 1.5 N x V bytes
             assert bwd < 1.5 * nv_bytes or n * v < 1 << 20
@@ -290,6 +290,29 @@ def test_forward_plan_split_by_v_only_and_override():
 ])
 def test_backward_plan_at_the_workloads(n, h, v, plan):
     assert _abi.flce_backward_plan(make_problem(n, h, v, BF16)) == plan
+
+
+def test_default_backward_plan_properties():
+    """Over many (H, V): the default chunk is whole tiles, at most a quarter of
+    V rounded up to a tile and at most 48 tiles (either that cap or a multiple
+    of 16 tiles), the chunks cover V exactly, a longer last chunk is one that
+    absorbed under a quarter of a chunk, and the plan is the same for every N
+    (grad_hidden's summation order must not depend on the batch)."""
+    import random
+    rng = random.Random(20261202)
+    vs = [1, 255, 256, 257, 1000, 1023, 1024, 1025, 4096, 32000, 32001, 50257, 128256, 152064, 256000,
+          262144, 1 << 20] + [rng.randrange(1, 400000) for _ in range(40)]
+    for h in (128, 1024, 2048, 3584, 4096, 8192):
+        for v in vs:
+            plans = {_abi.flce_backward_plan(make_problem(n, h, v, BF16)) for n in (300, 4096, 50000)}
+            assert len(plans) == 1, (h, v, plans)
+            chunk, n_chunks, last = plans.pop()
+            cap = min(48, max(1, -(-v // 1024)))
+            tiles = chunk // 256
+            assert chunk % 256 == 0 and 1 <= tiles <= cap, (h, v, chunk)
+            assert tiles == cap or tiles % 16 == 0, (h, v, chunk)
+            assert (n_chunks - 1) * chunk + last == v and last > 0, (h, v, chunk, n_chunks, last)
+            assert last <= chunk or 4 * (last - chunk) < chunk, (h, v, chunk, last)
 
 
 def test_backward_plan_override_and_invalid():
