@@ -183,12 +183,36 @@ def _random_configs(count, seed=20261202):
     return out
 
 
-@pytest.mark.parametrize("w,chunk,tps,go", _random_configs(12))
+@pytest.mark.parametrize("w,chunk,tps,go", _random_configs(24))
 def test_random_configurations(w, chunk, tps, go):
     """A seeded sweep of random shapes and options against the oracle: the
     fixed cases above pin each feature, this one checks their combinations
     at sizes nobody picked by hand."""
     run_case(w, bwd_vocab_chunk=chunk, fwd_tiles_per_split=tps, grad_output=go)
+
+
+def _random_default_plans(count, seed=20261203):
+    """Seeded draws with larger vocabularies (4000 to 40000 ids) and the
+    default plans: chunks of 4 to 40 tiles, rounded-up quarters of V, joined
+    last chunks and forward split groups, at small N and H."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for k in range(count):
+        dtype = ["bf16", "f16"][k % 2]
+        n = int(rng.integers(1, 400))
+        h = int(8 * rng.integers(1, 33))
+        v = int(rng.integers(4000, 40001))
+        w = W["midvocab_bf16"].resized(n=n, h=h, v=v, dtype=dtype, return_metrics=bool(k % 3 == 0),
+                                       bias_std=0.1 if k % 4 == 1 else None, seed=2000 + k)
+        out.append(pytest.param(w, id=f"{k}-{dtype}-n{n}-h{h}-v{v}"))
+    return out
+
+
+@pytest.mark.parametrize("w", _random_default_plans(6))
+def test_random_default_plans(w):
+    """The default backward chunking and forward splits at vocabularies the
+    fixed cases do not reach, against the oracle."""
+    run_case(w)
 
 
 def test_ignore_index_edge_cases():
