@@ -128,6 +128,25 @@ typedef struct flce_problem {
   int64_t hidden_seq_stride;
   int64_t targets_stride;
   int64_t targets_seq_stride;
+  /* Vocabulary shard: one device's share of a vocabulary split across
+   * devices, the vocabulary-parallel FLCE that the Liger FusedLinearKLDivLoss
+   * pull request (#1423, its rebase comment) names as #1428.  vocab_total =
+   * 0: no shard (vocab_offset must be 0).  Otherwise weight, bias,
+   * grad_weight and grad_bias hold ids [vocab_offset, vocab_offset + vocab)
+   * of a vocabulary of vocab_total ids, while targets stay ids of the whole
+   * vocabulary: a target inside the shard is its own, one inside
+   * [0, vocab_total) but outside the shard belongs to another shard (no
+   * target term here), one outside [0, vocab_total) is out of range (the
+   * NaN behaviour above).  Used by flce_forward_shard and flce_backward;
+   * flce_forward, flce_forward_noalloc and flce_forward_backward refuse it.
+   * Not combined with label_smoothing, z_loss, class_weight or
+   * return_metrics (FLCE_ERR_UNSUPPORTED). */
+  int64_t vocab_offset;
+  int64_t vocab_total;
+  /* 1: flce_backward writes grad_hidden as an fp32 array whatever the input
+   * dtype (for example one shard's part of grad_hidden, summed over the
+   * shards in fp32); 0: in the input dtype. */
+  int32_t grad_hidden_fp32;
 } flce_problem_t;
 
 /* Bytes of workspace flce_forward / flce_backward need for problem *p
@@ -208,7 +227,12 @@ flce_status_t flce_forward_noalloc(const flce_problem_t* p, const void* hidden, 
  *   grad_hidden (N,H), grad_weight (V,H), grad_bias (V): outputs, each may
  *               be NULL when not wanted (grad_bias requires has_bias).  They
  *               are overwritten, not accumulated into.  grad_weight and
- *               grad_bias are fp32 when grad_weight_fp32 = 1.
+ *               grad_bias are fp32 when grad_weight_fp32 = 1, grad_hidden
+ *               when grad_hidden_fp32 = 1.
+ * With a vocabulary shard (vocab_total > 0): lse is the whole vocabulary's
+ * (flce_combine_shards), the mean divides by the non-ignored rows of the
+ * whole batch, grad_weight and grad_bias are the shard's rows, and
+ * grad_hidden is the shard's part: the sum over the shards is the gradient.
  * FLCE_ERR_UNSUPPORTED when n_tokens or the vocabulary chunk times
  * sizeof(dtype) reaches 16 MiB (the operand tiles use 32-bit offsets). */
 flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const void* weight,
@@ -232,6 +256,39 @@ flce_status_t flce_forward_backward(const flce_problem_t* p, const void* hidden,
                                     float* metrics, const float* grad_loss, void* grad_hidden,
                                     void* grad_weight, void* grad_bias, void* workspace,
                                     size_t workspace_bytes, void* stream);
+
+/* One shard's part of the forward (vocabulary-parallel; p->vocab_total > 0,
+ * see flce_problem_t): the card's "Algorithm" forward over the shard's ids
+ * only.  For every row n:
+ *   shard_lse[n]    = log sum over the shard's ids j of e^{z_nj};
+ *   target_logit[n] = z_{n,t_n} if t_n is one of the shard's ids, else 0
+ *                     (ignored rows and targets of other shards; NaN for a
+ *                     target outside [0, vocab_total)).
+ * Both outputs are device fp32 [N].  p->reduction is not applied here:
+ * flce_combine_shards turns the shards' outputs into the loss.  The
+ * workspace is flce_forward_workspace_size(p) bytes; the status word is set
+ * as by flce_forward. */
+flce_status_t flce_forward_shard(const flce_problem_t* p, const void* hidden, const void* weight,
+                                 const int64_t* targets, const void* bias, float* shard_lse,
+                                 float* target_logit, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The loss of a vocabulary split into n_shards shards, from the shards'
+ * flce_forward_shard outputs brought together (what each device does after
+ * gathering the per-row partials; on one device, the shards' calls in a
+ * row).  p describes the whole problem: vocab is the whole vocabulary,
+ * vocab_offset and vocab_total 0, and its reduction, ignore_index and token
+ * layout apply; no metrics or variants.  shard_lse and target_logit are
+ * device fp32 [n_shards][N] (shard-major, contiguous).  Writes
+ *   lse[n]  = log sum_k e^{shard_lse[k][n]} (fp32, k in order, after the
+ *             largest is taken out): the input of flce_backward;
+ *   loss    = per p->reduction of the rows lse[n] - sum_k target_logit[k][n]
+ *             (0 for ignored rows), as flce_forward would ([1] or [N]).
+ * lse may be NULL.  The workspace is flce_combine_shards_workspace_size(p)
+ * bytes (its status word is readable with flce_forward_status). */
+size_t flce_combine_shards_workspace_size(const flce_problem_t* p);
+flce_status_t flce_combine_shards(const flce_problem_t* p, int32_t n_shards, const float* shard_lse,
+                                  const float* target_logit, const int64_t* targets, float* loss, float* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* Synchronously reads the device status word the last flce_forward call
  * left in `workspace` (bit 0: a non-ignored target outside [0,V)).

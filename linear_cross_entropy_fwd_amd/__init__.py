@@ -21,8 +21,9 @@ import torch
 from . import _abi
 from ._abi import FlceError, Problem, library, make_problem  # noqa: F401
 
-__all__ = ["fused_linear_cross_entropy", "flce_forward", "flce_backward", "flce_forward_backward", "FlceError",
-           "Problem", "make_problem", "library", "token_layout"]
+__all__ = ["fused_linear_cross_entropy", "flce_forward", "flce_backward", "flce_forward_backward",
+           "flce_forward_shard", "flce_combine_shards", "FlceError", "Problem", "make_problem", "library",
+           "token_layout"]
 
 _DTYPES = {torch.float32: _abi.F32, torch.float16: _abi.F16, torch.bfloat16: _abi.BF16}
 
@@ -107,15 +108,19 @@ def _check_class_weight(class_weight, weight):
 def problem_for(hidden, weight, bias, ignore_index=-100, logit_scale=1.0, softcap=None,
                 reduction="mean", return_metrics=False, fwd_tiles_per_split=0,
                 bwd_vocab_chunk=0, label_smoothing=0.0, z_loss=0.0, class_weight=None,
-                predictions=None, grad_weight_fp32=False, layout=None) -> Problem:
-    """``layout``: the token layout keywords ``_check_inputs`` returns (None = contiguous)."""
+                predictions=None, grad_weight_fp32=False, layout=None, vocab_offset=0, vocab_total=0,
+                grad_hidden_fp32=False) -> Problem:
+    """``layout``: the token layout keywords ``_check_inputs`` returns (None = contiguous).
+    ``vocab_offset`` / ``vocab_total``: weight holds ids [vocab_offset, vocab_offset + V)
+    of a vocabulary of vocab_total ids (0 / 0: the whole vocabulary)."""
     _check_class_weight(class_weight, weight)
     n = hidden.numel() // hidden.shape[-1] if hidden.shape[-1] else 0
     return make_problem(n, hidden.shape[-1], weight.shape[0], _DTYPES[hidden.dtype],
                         reduction, ignore_index, logit_scale, softcap, return_metrics,
                         bias is not None, fwd_tiles_per_split, bwd_vocab_chunk, label_smoothing,
                         z_loss, _ptr(class_weight), _ptr(predictions), grad_weight_fp32,
-                        **(layout or {}))
+                        **(layout or {}), vocab_offset=vocab_offset, vocab_total=vocab_total,
+                        grad_hidden_fp32=grad_hidden_fp32)
 
 
 def flce_forward(hidden, weight, targets, bias=None, *, ignore_index=-100, logit_scale=1.0,
@@ -157,22 +162,28 @@ def flce_backward(hidden, weight, targets, bias, lse, grad_loss=None, *, ignore_
                   logit_scale=1.0, softcap=None, reduction="mean", need_hidden=True,
                   need_weight=True, need_bias=True, workspace: Optional[torch.Tensor] = None,
                   bwd_vocab_chunk=0, label_smoothing=0.0, z_loss=0.0, class_weight=None,
-                  grad_weight_fp32=False):
+                  grad_weight_fp32=False, grad_hidden_fp32=False, vocab_offset=0, vocab_total=0):
     """Tensor-level ``flce_backward``: returns (grad_hidden, grad_weight, grad_bias);
-    grad_weight and grad_bias are fp32 with ``grad_weight_fp32``; grad_hidden is
-    contiguous, in the shape of hidden."""
+    grad_weight and grad_bias are fp32 with ``grad_weight_fp32``, grad_hidden
+    with ``grad_hidden_fp32``; grad_hidden is contiguous, in the shape of hidden.
+    With a vocabulary shard (``vocab_total`` > 0; weight and bias hold ids
+    [vocab_offset, vocab_offset + V)), ``lse`` is the whole vocabulary's
+    (``flce_combine_shards``), grad_weight and grad_bias are the shard's rows
+    and grad_hidden is the shard's part of the gradient."""
     layout = _check_inputs(hidden, weight, targets, bias)
     p = problem_for(hidden, weight, bias, ignore_index, logit_scale, softcap, reduction,
                     False, bwd_vocab_chunk=bwd_vocab_chunk, label_smoothing=label_smoothing,
                     z_loss=z_loss, class_weight=class_weight, grad_weight_fp32=grad_weight_fp32,
-                    layout=layout)
+                    layout=layout, vocab_offset=vocab_offset, vocab_total=vocab_total,
+                    grad_hidden_fp32=grad_hidden_fp32)
     dev = hidden.device
     if grad_loss is not None:
         grad_loss = grad_loss.to(device=dev, dtype=torch.float32).contiguous()
         expect = targets.numel() if reduction == "none" else 1
         if grad_loss.numel() != expect:
             raise ValueError(f"grad_loss must have {expect} elements")
-    gh = torch.empty(hidden.shape, dtype=hidden.dtype, device=dev) if need_hidden else None
+    hdt = torch.float32 if grad_hidden_fp32 else hidden.dtype
+    gh = torch.empty(hidden.shape, dtype=hdt, device=dev) if need_hidden else None
     gdt = torch.float32 if grad_weight_fp32 else weight.dtype
     gw = torch.empty(weight.shape, dtype=gdt, device=dev) if need_weight else None
     gb = torch.empty(bias.shape, dtype=gdt, device=dev) if (need_bias and bias is not None) else None
@@ -231,6 +242,71 @@ def flce_forward_backward(hidden, weight, targets, bias=None, grad_loss=None, *,
     if reduction != "none":
         loss = loss.view(())
     return loss, lse, metrics, (gh, gw, gb)
+
+
+def flce_forward_shard(hidden, weight, targets, bias=None, *, vocab_offset, vocab_total, ignore_index=-100,
+                       logit_scale=1.0, softcap=None, workspace: Optional[torch.Tensor] = None,
+                       fwd_tiles_per_split=0):
+    """One vocabulary shard's part of the forward (``flce_forward_shard``):
+    weight and bias hold ids [vocab_offset, vocab_offset + V) of a vocabulary
+    of ``vocab_total`` ids; targets are ids of the whole vocabulary.  Returns
+    (shard_lse, target_logit), fp32 (N,): the row's log-sum-exp over the
+    shard's ids, and its target logit when the target is one of them (else 0)."""
+    layout = _check_inputs(hidden, weight, targets, bias)
+    p = problem_for(hidden, weight, bias, ignore_index, logit_scale, softcap, "none", False,
+                    fwd_tiles_per_split=fwd_tiles_per_split, layout=layout, vocab_offset=vocab_offset,
+                    vocab_total=vocab_total)
+    dev = hidden.device
+    n = targets.numel()
+    shard_lse = torch.empty(n, dtype=torch.float32, device=dev)
+    target_logit = torch.empty(n, dtype=torch.float32, device=dev)
+    need = _abi.flce_forward_workspace_size(p)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream().cuda_stream
+    _abi.check(_abi.flce_forward_shard(p, _ptr(hidden), _ptr(weight), _ptr(targets), _ptr(bias),
+                                       _ptr(shard_lse), _ptr(target_logit), _ptr(workspace),
+                                       workspace.numel(), stream))
+    return shard_lse, target_logit
+
+
+def flce_combine_shards(shard_lse, target_logit, targets, vocab_total, *, ignore_index=-100,
+                        reduction="mean", workspace: Optional[torch.Tensor] = None):
+    """The loss of a vocabulary split into shards (``flce_combine_shards``),
+    from the shards' ``flce_forward_shard`` outputs stacked as (n_shards, N)
+    fp32 tensors (shard order is the summation order).  Returns (loss, lse):
+    loss per ``reduction`` ((), or (N,) for "none") and the whole vocabulary's
+    per-row lse, the input of ``flce_backward``."""
+    if shard_lse.dim() != 2 or target_logit.shape != shard_lse.shape:
+        raise ValueError("shard_lse and target_logit must be (n_shards, N) tensors of one shape")
+    for t in (shard_lse, target_logit):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or t.device != targets.device:
+            raise ValueError("shard_lse and target_logit must be contiguous float32 tensors on the targets' device")
+    if targets.dtype != torch.int64 or targets.numel() != shard_lse.shape[1] or targets.dim() not in (1, 2):
+        raise ValueError("targets must be int64 (N,) or (S, T) with N = shard_lse.shape[1]")
+    n = targets.numel()
+    if targets.dim() == 2:
+        seq = targets.shape[1]
+        lay = dict(seq_len=seq, targets_stride=targets.stride(1) if seq > 1 else 0,
+                   targets_seq_stride=targets.stride(0) if targets.shape[0] > 1 else 0)
+    else:
+        lay = dict(targets_stride=targets.stride(0) if n > 1 else 0)
+    # the combine reads no hidden rows: H = 8 bf16 elements stands for any width
+    p = make_problem(n, 8, vocab_total, _abi.BF16, reduction, ignore_index, **lay)
+    dev = targets.device
+    loss = torch.empty(n if reduction == "none" else 1, dtype=torch.float32, device=dev)
+    lse = torch.empty(n, dtype=torch.float32, device=dev)
+    need = _abi.flce_combine_shards_workspace_size(p)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream().cuda_stream
+    _abi.check(_abi.flce_combine_shards(p, shard_lse.shape[0], _ptr(shard_lse), _ptr(target_logit), _ptr(targets),
+                                        _ptr(loss), _ptr(lse), _ptr(workspace), workspace.numel(), stream))
+    if reduction != "none":
+        loss = loss.view(())
+    return loss, lse
 
 
 class _FusedLinearCrossEntropy(torch.autograd.Function):

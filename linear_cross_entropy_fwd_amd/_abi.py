@@ -47,6 +47,9 @@ class Problem(ctypes.Structure):
         ("hidden_seq_stride", ctypes.c_int64),
         ("targets_stride", ctypes.c_int64),
         ("targets_seq_stride", ctypes.c_int64),
+        ("vocab_offset", ctypes.c_int64),
+        ("vocab_total", ctypes.c_int64),
+        ("grad_hidden_fp32", ctypes.c_int32),
     ]
 
 
@@ -73,6 +76,10 @@ _SIGNATURES = {
     "flce_forward_backward": (ctypes.c_int, [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                              _VP, ctypes.c_size_t, _VP]),
     "flce_forward_status": (ctypes.c_int, [_PP, _VP, ctypes.POINTER(ctypes.c_uint32), _VP]),
+    "flce_forward_shard": (ctypes.c_int, [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
+    "flce_combine_shards_workspace_size": (ctypes.c_size_t, [_PP]),
+    "flce_combine_shards": (ctypes.c_int, [_PP, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t,
+                                           _VP]),
     "flce_forward_plan": (ctypes.c_int, [_PP, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
                                          ctypes.POINTER(ctypes.c_int32)]),
     "flce_backward_plan": (ctypes.c_int, [_PP, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
@@ -115,10 +122,14 @@ def make_problem(n, h, v, dtype, reduction="mean", ignore_index=-100, logit_scal
                  softcap=None, return_metrics=False, has_bias=False, fwd_tiles_per_split=0,
                  bwd_vocab_chunk=0, label_smoothing=0.0, z_loss=0.0, class_weight=0,
                  predictions=0, grad_weight_fp32=False, seq_len=0, hidden_row_stride=0,
-                 hidden_seq_stride=0, targets_stride=0, targets_seq_stride=0) -> Problem:
+                 hidden_seq_stride=0, targets_stride=0, targets_seq_stride=0, vocab_offset=0,
+                 vocab_total=0, grad_hidden_fp32=False) -> Problem:
     """class_weight / predictions: integer device addresses (fp32 [V] in,
     int64 [N] out), or 0.  grad_weight_fp32: 1 for fp32 grad_weight / grad_bias.
-    seq_len and the strides (elements) describe a strided token layout; 0 = default."""
+    seq_len and the strides (elements) describe a strided token layout; 0 = default.
+    vocab_offset / vocab_total: a vocabulary shard (ids [vocab_offset,
+    vocab_offset + v) of vocab_total); 0 / 0 = none.  grad_hidden_fp32: 1 for
+    an fp32 grad_hidden."""
     return Problem(int(n), int(h), int(v), int(ignore_index), int(dtype),
                    REDUCTIONS[reduction] if isinstance(reduction, str) else int(reduction),
                    float(logit_scale), 0.0 if softcap is None else float(softcap),
@@ -126,7 +137,7 @@ def make_problem(n, h, v, dtype, reduction="mean", ignore_index=-100, logit_scal
                    int(bwd_vocab_chunk), float(label_smoothing), float(z_loss),
                    int(class_weight) or None, int(predictions) or None, int(grad_weight_fp32),
                    int(seq_len), int(hidden_row_stride), int(hidden_seq_stride), int(targets_stride),
-                   int(targets_seq_stride))
+                   int(targets_seq_stride), int(vocab_offset), int(vocab_total), int(grad_hidden_fp32))
 
 
 def flce_forward_workspace_size(p: Problem) -> int:
@@ -166,6 +177,22 @@ def flce_backward(p: Problem, hidden, weight, targets, bias, lse, grad_loss, gra
     return library().flce_backward(ctypes.byref(p), hidden, weight, targets, bias, lse,
                                    grad_loss, grad_hidden, grad_weight, grad_bias, workspace,
                                    workspace_bytes, stream)
+
+
+def flce_forward_shard(p: Problem, hidden, weight, targets, bias, shard_lse, target_logit, workspace,
+                       workspace_bytes, stream) -> int:
+    return library().flce_forward_shard(ctypes.byref(p), hidden, weight, targets, bias, shard_lse, target_logit,
+                                        workspace, workspace_bytes, stream)
+
+
+def flce_combine_shards_workspace_size(p: Problem) -> int:
+    return int(library().flce_combine_shards_workspace_size(ctypes.byref(p)))
+
+
+def flce_combine_shards(p: Problem, n_shards, shard_lse, target_logit, targets, loss, lse, workspace,
+                        workspace_bytes, stream) -> int:
+    return library().flce_combine_shards(ctypes.byref(p), int(n_shards), shard_lse, target_logit, targets, loss,
+                                         lse, workspace, workspace_bytes, stream)
 
 
 def flce_forward_status(p: Problem, workspace, stream) -> int:

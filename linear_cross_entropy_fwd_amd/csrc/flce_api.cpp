@@ -140,6 +140,21 @@ flce_status_t check_problem(const flce_problem_t* p) {
   if ((p->hidden_row_stride * elem_bytes(p->dtype)) % 16 != 0 ||
       (p->hidden_seq_stride * elem_bytes(p->dtype)) % 16 != 0)
     return fail(FLCE_ERR_INVALID_ARGUMENT, "hidden strides times sizeof(dtype) must be multiples of 16 bytes");
+  if (p->vocab_offset < 0 || p->vocab_total < 0)
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "vocab_offset and vocab_total must be >= 0");
+  if (p->vocab_total == 0 && p->vocab_offset != 0)
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "vocab_offset needs vocab_total > 0 (a vocabulary shard)");
+  if (p->vocab_total > 0) {
+    if (p->vocab_total >= (int64_t(1) << 31)) return fail(FLCE_ERR_UNSUPPORTED, "vocab_total must be < 2^31");
+    if (p->vocab_offset + p->vocab > p->vocab_total)
+      return fail(FLCE_ERR_INVALID_ARGUMENT, "the shard [vocab_offset, vocab_offset + vocab) = [%lld, %lld) must lie "
+                  "inside [0, vocab_total = %lld)", (long long)p->vocab_offset,
+                  (long long)(p->vocab_offset + p->vocab), (long long)p->vocab_total);
+    if (p->label_smoothing != 0.f || p->z_loss != 0.f || p->class_weight || p->return_metrics)
+      return fail(FLCE_ERR_UNSUPPORTED, "a vocabulary shard takes no metrics, label smoothing, z-loss or class weights");
+  }
+  if (p->grad_hidden_fp32 != 0 && p->grad_hidden_fp32 != 1)
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "grad_hidden_fp32 must be 0 or 1");
   return FLCE_OK;
 }
 
@@ -164,7 +179,8 @@ TokLayout tok_layout(const flce_problem_t& p) {
   L.ts = p.targets_stride > 0 ? p.targets_stride : 1;
   L.tss = p.targets_seq_stride > 0 ? p.targets_seq_stride : L.T * L.ts;
   L.h_gather = N > 0 && !(L.hr == p.hidden && (one_seq || L.hs == L.T * L.hr));
-  L.t_gather = N > 0 && !(L.ts == 1 && (one_seq || L.tss == L.T));
+  // a vocabulary shard's kernels read target codes (the mapping rides on the gather)
+  L.t_gather = N > 0 && (p.vocab_total > 0 || !(L.ts == 1 && (one_seq || L.tss == L.T)));
   return L;
 }
 
@@ -189,6 +205,13 @@ hipError_t tok_inputs(const flce_problem_t& p, const TokLayout& L, const void* h
   if (L.t_gather) {
     int64_t* dst = reinterpret_cast<int64_t*>(ws + off_t);
     flce::GatherTargetsArgs a{targets, dst, p.n_tokens, L.T, L.ts, L.tss};
+    if (p.vocab_total > 0) {
+      a.shard = 1;
+      a.ignore_index = p.ignore_index;
+      a.voff = p.vocab_offset;
+      a.vshard = p.vocab;
+      a.vtotal = p.vocab_total;
+    }
     if ((e = flce::launch_gather_targets(a, st)) != hipSuccess) return e;
     out.targets = dst;
   }
@@ -403,7 +426,8 @@ float cap_of(const flce_problem_t& p) { return p.softcap > 0.f ? p.softcap : 1.f
 // (the plan overrides address the tiled path).
 bool small_path(const flce_problem_t& p) {
   return p.dtype == FLCE_F32 && p.n_tokens <= flce::kSmallMaxN && p.vocab <= flce::kSmallMaxV &&
-         p.hidden <= flce::kSmallMaxH && p.fwd_tiles_per_split == 0 && p.bwd_vocab_chunk == 0;
+         p.hidden <= flce::kSmallMaxH && p.fwd_tiles_per_split == 0 && p.bwd_vocab_chunk == 0 &&
+         p.vocab_total == 0;
 }
 
 flce::SmallArgs small_args(const flce_problem_t& p, const char* hidden, const void* weight, const void* bias,
@@ -470,17 +494,70 @@ size_t flce_backward_workspace_size(const flce_problem_t* p) {
   return bwd_layout(*p).total;
 }
 
-flce_status_t flce_forward(const flce_problem_t* p, const void* hidden, const void* weight,
-                           const int64_t* targets, const void* bias, float* loss, float* lse,
-                           float* metrics, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// flce_combine_shards' workspace: the status word first (where
+// flce_forward_status reads it), the per-row loss and flags the reduce
+// kernel sums, and gathered targets for a strided layout.
+struct CombineLayout {
+  TokLayout tok;
+  size_t off_status, off_rowloss, off_rowflag, off_tgt, total;
+};
+
+CombineLayout combine_layout(const flce_problem_t& p) {
+  CombineLayout L{};
+  const int64_t N = p.n_tokens;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = (size_t)round_up((int64_t)(off + bytes), kAlign);
+    return o;
+  };
+  L.off_status = take(16);
+  L.off_rowloss = take((size_t)N * 4);
+  L.off_rowflag = take((size_t)N * 4);
+  L.tok = tok_layout(p);
+  L.off_tgt = take(L.tok.t_gather ? (size_t)N * 8 : 0);
+  L.total = off;
+  return L;
+}
+
+flce_status_t check_combine_problem(const flce_problem_t* p) {
+  const flce_status_t s = check_problem(p);
+  if (s != FLCE_OK) return s;
+  if (p->vocab_total != 0)
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "flce_combine_shards takes the whole problem: vocab = the whole "
+                "vocabulary, vocab_offset and vocab_total 0");
+  if (p->label_smoothing != 0.f || p->z_loss != 0.f || p->class_weight || p->return_metrics)
+    return fail(FLCE_ERR_UNSUPPORTED, "flce_combine_shards takes no metrics, label smoothing, z-loss or class weights");
+  return FLCE_OK;
+}
+
+// The forward of flce_forward and, with `shard` (a vocabulary shard), of
+// flce_forward_shard: then `loss` receives the per-row target logits and
+// `lse` the shard's per-row log-sum-exp, and no reduction is applied.
+flce_status_t forward_impl(const flce_problem_t* p, bool shard, const void* hidden, const void* weight,
+                           const int64_t* targets, const void* bias, float* loss, float* lse, float* metrics,
+                           void* workspace, size_t workspace_bytes, void* stream) {
   flce_status_t s = check_problem(p);
   if (s != FLCE_OK) return s;
+  if (!shard && p->vocab_total > 0)
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "a vocabulary shard (vocab_total > 0) runs flce_forward_shard");
+  if (shard && p->vocab_total == 0)
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "flce_forward_shard needs a vocabulary shard (vocab_total > 0)");
   const int64_t N = p->n_tokens;
   if (N > 0 && (!hidden || !weight || !targets))
     return fail(FLCE_ERR_INVALID_ARGUMENT, "hidden, weight and targets must be non-NULL");
   if (p->has_bias && !bias) return fail(FLCE_ERR_INVALID_ARGUMENT, "has_bias=1 but bias is NULL");
   if (!p->has_bias && bias) return fail(FLCE_ERR_INVALID_ARGUMENT, "bias given but has_bias=0");
-  if (!loss && !(p->reduction == FLCE_NONE && N == 0)) return fail(FLCE_ERR_INVALID_ARGUMENT, "loss is NULL");
+  if (shard && N > 0 && (!loss || !lse))
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "shard_lse and target_logit must be non-NULL");
+  if (!shard && !loss && !(p->reduction == FLCE_NONE && N == 0))
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "loss is NULL");
+  if (shard && (!aligned(loss, 4) || !aligned(lse, 4)))
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "shard_lse / target_logit misaligned");
   if (p->return_metrics && !metrics) return fail(FLCE_ERR_INVALID_ARGUMENT, "return_metrics=1 but metrics is NULL");
   if (!p->return_metrics && metrics) return fail(FLCE_ERR_INVALID_ARGUMENT, "metrics given but return_metrics=0");
   if (!aligned(hidden, 16) || !aligned(weight, 16))
@@ -524,7 +601,7 @@ flce_status_t flce_forward(const flce_problem_t* p, const void* hidden, const vo
       fa.npad = (int64_t)L.n_tok_tiles * kTile;
       fa.H = p->hidden;
       fa.V = p->vocab;
-      fa.ignore_index = p->ignore_index;
+      fa.ignore_index = shard ? flce::kShardIgnored : p->ignore_index;
       fa.n_tok_tiles = L.n_tok_tiles;
       fa.n_voc_tiles = L.n_voc_tiles;
       fa.tiles_per_split = L.tiles_per_split;
@@ -543,14 +620,16 @@ flce_status_t flce_forward(const flce_problem_t* p, const void* hidden, const vo
       ca.part = fa.part;
       ca.zt_rows = fa.zt_rows;
       ca.lse_out = lse;
-      ca.loss_rows = p->reduction == FLCE_NONE ? loss : nullptr;
+      ca.loss_rows = shard || p->reduction == FLCE_NONE ? loss : nullptr;
       ca.row_loss = reinterpret_cast<float*>(ws + L.off_rowloss);
       ca.row_ent = reinterpret_cast<float*>(ws + L.off_rowent);
       ca.row_flag = reinterpret_cast<int*>(ws + L.off_rowflag);
       ca.N = N;
       ca.npad = fa.npad;
       ca.V = p->vocab;
-      ca.ignore_index = p->ignore_index;
+      ca.ignore_index = fa.ignore_index;
+      ca.shard = shard ? 1 : 0;
+      ca.foreign = flce::kShardForeign;
       ca.tiles_per_split = L.tiles_per_split;
       ca.n_splits = L.n_splits;
       ca.zsum = fa.zsum;
@@ -568,13 +647,82 @@ flce_status_t flce_forward(const flce_problem_t* p, const void* hidden, const vo
   ra.row_ent = reinterpret_cast<const float*>(ws + L.off_rowent);
   ra.row_flag = reinterpret_cast<const int*>(ws + L.off_rowflag);
   ra.row_w = p->class_weight ? reinterpret_cast<const float*>(ws + L.off_roww) : nullptr;
-  ra.loss = loss;
+  ra.loss = shard ? nullptr : loss;
   ra.metrics = metrics;
   ra.status = reinterpret_cast<uint32_t*>(ws + L.off_status);
   ra.N = N;
-  ra.reduction = p->reduction;
+  ra.reduction = shard ? FLCE_NONE : p->reduction;  // a shard: the status word only
   e = flce::launch_forward_reduce(metrics_on, ra, st);
   if (e != hipSuccess) return hip_fail(e, "forward reduce kernel");
+  return FLCE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+flce_status_t flce_forward(const flce_problem_t* p, const void* hidden, const void* weight,
+                           const int64_t* targets, const void* bias, float* loss, float* lse,
+                           float* metrics, void* workspace, size_t workspace_bytes, void* stream) {
+  return forward_impl(p, false, hidden, weight, targets, bias, loss, lse, metrics, workspace, workspace_bytes,
+                      stream);
+}
+
+flce_status_t flce_forward_shard(const flce_problem_t* p, const void* hidden, const void* weight,
+                                 const int64_t* targets, const void* bias, float* shard_lse,
+                                 float* target_logit, void* workspace, size_t workspace_bytes, void* stream) {
+  return forward_impl(p, true, hidden, weight, targets, bias, target_logit, shard_lse, nullptr, workspace,
+                      workspace_bytes, stream);
+}
+
+size_t flce_combine_shards_workspace_size(const flce_problem_t* p) {
+  if (check_combine_problem(p) != FLCE_OK) return 0;
+  return combine_layout(*p).total;
+}
+
+flce_status_t flce_combine_shards(const flce_problem_t* p, int32_t n_shards, const float* shard_lse,
+                                  const float* target_logit, const int64_t* targets, float* loss, float* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  flce_status_t s = check_combine_problem(p);
+  if (s != FLCE_OK) return s;
+  if (n_shards < 1) return fail(FLCE_ERR_INVALID_ARGUMENT, "n_shards must be >= 1");
+  const int64_t N = p->n_tokens;
+  if (N > 0 && (!shard_lse || !target_logit || !targets))
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "shard_lse, target_logit and targets must be non-NULL");
+  if (!loss && !(p->reduction == FLCE_NONE && N == 0)) return fail(FLCE_ERR_INVALID_ARGUMENT, "loss is NULL");
+  if (!aligned(shard_lse, 4) || !aligned(target_logit, 4) || !aligned(loss, 4) || !aligned(lse, 4) ||
+      !aligned(targets, 8))
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "shard_lse / target_logit / loss / lse / targets misaligned");
+  if ((int64_t)n_shards * N >= (int64_t(1) << 40))
+    return fail(FLCE_ERR_UNSUPPORTED, "n_shards * n_tokens must be below 2^40");
+  const CombineLayout L = combine_layout(*p);
+  s = check_workspace(workspace, workspace_bytes, L.total);
+  if (s != FLCE_OK) return s;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  hipError_t e;
+  float* row_loss = reinterpret_cast<float*>(ws + L.off_rowloss);
+  int* row_flag = reinterpret_cast<int*>(ws + L.off_rowflag);
+  if (N > 0) {
+    const int64_t* tg = targets;
+    if (L.tok.t_gather) {
+      int64_t* dst = reinterpret_cast<int64_t*>(ws + L.off_tgt);
+      flce::GatherTargetsArgs ga{targets, dst, N, L.tok.T, L.tok.ts, L.tok.tss};
+      if ((e = flce::launch_gather_targets(ga, st)) != hipSuccess) return hip_fail(e, "gather kernel");
+      tg = dst;
+    }
+    flce::ShardCombineArgs a{shard_lse, target_logit, tg, lse, p->reduction == FLCE_NONE ? loss : nullptr,
+                             row_loss, row_flag, N, p->vocab, p->ignore_index, n_shards};
+    if ((e = flce::launch_shard_combine(a, st)) != hipSuccess) return hip_fail(e, "shard combine kernel");
+  }
+  flce::ReduceArgs ra{};
+  ra.row_loss = row_loss;
+  ra.row_flag = row_flag;
+  ra.loss = loss;
+  ra.status = reinterpret_cast<uint32_t*>(ws + L.off_status);
+  ra.N = N;
+  ra.reduction = p->reduction;
+  if ((e = flce::launch_forward_reduce(false, ra, st)) != hipSuccess) return hip_fail(e, "forward reduce kernel");
   return FLCE_OK;
 }
 
@@ -697,13 +845,14 @@ static hipError_t backward_fused(const flce_problem_t& p, const BwdLayout& L, co
       da.Wk = weight + (int64_t)(c - slot) * L.chunk * H * eb;
       da.wrows = V - (int64_t)(c - slot) * L.chunk;
       da.acc_stream = L.acc_stream;
+      da.out_f32 = p.grad_hidden_fp32;
       sa.dh_grid = flce::backward_dh_grid(L.n_h_tiles, L.n_tok_tiles);
       sa.nb_dh = sa.dh_grid * L.dh_split;
     }
     if ((e = flce::launch_backward_step(p.dtype, p.has_bias != 0, p.softcap > 0.f, sa, st)) != hipSuccess) return e;
     if (sa.nb_dh > 0 && sa.dh.last && L.dh_split > 1) {
       flce::DhFinalArgs fa{dh, scale, reinterpret_cast<char*>(grad_hidden), sa.dh.acc_stride, sa.dh.acc_stride,
-                           L.dh_split, 1, p.n_tokens, H, L.n_h_tiles};
+                           L.dh_split, 1, p.n_tokens, H, L.n_h_tiles, p.grad_hidden_fp32};
       if ((e = flce::launch_backward_dh_final(p.dtype, fa, st)) != hipSuccess) return e;
     }
   }
@@ -755,8 +904,11 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
     return FLCE_OK;
   }
   float* scale = reinterpret_cast<float*>(ws + L.off_scale);
-  flce::PrepArgs pa{targets, grad_loss, p->class_weight, scale, N, V, p->ignore_index, p->reduction,
-                    p->logit_scale};
+  // a vocabulary shard's kernels read target codes (tok_inputs mapped them)
+  const bool shard = p->vocab_total > 0;
+  const int64_t ignore = shard ? flce::kShardIgnored : p->ignore_index;
+  const int64_t foreign = shard ? flce::kShardForeign : p->ignore_index;
+  flce::PrepArgs pa{targets, grad_loss, p->class_weight, scale, N, V, ignore, p->reduction, p->logit_scale};
   if ((e = flce::launch_backward_prep(pa, st)) != hipSuccess) return hip_fail(e, "backward prep kernel");
 
   char* ht = ws + L.off_ht;
@@ -786,7 +938,8 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
     gb.N = N;
     gb.H = H;
     gb.V = V;
-    gb.ignore_index = p->ignore_index;
+    gb.ignore_index = ignore;
+    gb.foreign = foreign;
     gb.npad = (int)L.npad;
     gb.n_tok_tiles = L.n_tok_tiles;
     gb.none_reduction = p->reduction == FLCE_NONE;
@@ -834,7 +987,8 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
     ga.N = N;
     ga.H = H;
     ga.V = V;
-    ga.ignore_index = p->ignore_index;
+    ga.ignore_index = ignore;
+    ga.foreign = foreign;
     ga.c0 = c0;
     ga.cv = cv;
     ga.cvpad = cvpad;
@@ -893,10 +1047,11 @@ flce_status_t flce_backward(const flce_problem_t* p, const void* hidden, const v
       da.Wk = reinterpret_cast<const char*>(weight) + (int64_t)(c - slot) * L.chunk * H * eb;
       da.wrows = V - (int64_t)(c - slot) * L.chunk;
       da.acc_stream = L.acc_stream;
+      da.out_f32 = p->grad_hidden_fp32;
       if ((e = flce::launch_backward_dh(p->dtype, da, st)) != hipSuccess) return hip_fail(e, "grad_hidden kernel");
       if (da.last && L.dh_split > 1) {
         flce::DhFinalArgs fa{dh, scale, reinterpret_cast<char*>(grad_hidden), da.acc_stride, da.acc_stride,
-                             L.dh_split, L.dk ? 1 : 0, N, H, L.n_h_tiles};
+                             L.dh_split, L.dk ? 1 : 0, N, H, L.n_h_tiles, p->grad_hidden_fp32};
         if ((e = flce::launch_backward_dh_final(p->dtype, fa, st)) != hipSuccess)
           return hip_fail(e, "grad_hidden sum kernel");
       }
@@ -923,6 +1078,9 @@ flce_status_t flce_forward_backward(const flce_problem_t* p, const void* hidden,
                                     size_t workspace_bytes, void* stream) {
   flce_status_t s = check_problem(p);
   if (s != FLCE_OK) return s;
+  if (p->vocab_total > 0)
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "a vocabulary shard needs the combined lse before its backward: "
+                "flce_forward_shard, flce_combine_shards, flce_backward");
   const FwdBwdLayout L = fwdbwd_layout(*p);
   s = check_workspace(workspace, workspace_bytes, L.total);
   if (s != FLCE_OK) return s;

@@ -430,13 +430,16 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(CombineArgs a) {
   }
   const int64_t tv = a.targets[n];
   const bool valid = tv != a.ignore_index;
-  const bool bad = valid && (tv < 0 || tv >= a.V);
+  const bool foreign = a.shard && tv == a.foreign;  // another shard's id: no target logit here
+  const bool bad = valid && !foreign && (tv < 0 || tv >= a.V);
   const float logS = logf(S);
   const float lse = M + logS;
   float row = 0.f, rw = 0.f;
-  if (valid) {
+  if (valid && !foreign) {
     if (bad) {
       row = NAN;
+    } else if (a.shard) {
+      row = a.zt_rows[n];  // the target logit (no variants with shards)
     } else {
       const float zt = a.zt_rows[n];
       // smoothed cross-entropy + z-loss, times the row's class weight (all
@@ -504,6 +507,33 @@ __global__ __launch_bounds__(1024) void fwd_reduce_kernel(ReduceArgs a) {
     }
     a.status[0] = (uint32_t)sh_b[0];
   }
+}
+
+// The loss of a vocabulary split into shards.  Each shard's forward gives a
+// row's log-sum-exp over the shard's ids and, at the shard that holds the
+// row's target, the target logit (0 at the others).  Here lse = M + log sum_k
+// e^{lse_k - M} (M the largest, k in shard order) and the row loss is lse
+// minus the sum of the target logits.  One thread per row.
+__global__ __launch_bounds__(256) void shard_combine_kernel(ShardCombineArgs a) {
+  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (n >= a.N) return;
+  float M = -INFINITY;
+  for (int k = 0; k < a.n_shards; ++k) M = fmaxf(M, a.shard_lse[(int64_t)k * a.N + n]);
+  float S = 0.f, zt = 0.f;
+  for (int k = 0; k < a.n_shards; ++k) {
+    const float lk = a.shard_lse[(int64_t)k * a.N + n];
+    if (lk != -INFINITY) S = S + fast_exp2((lk - M) * LOG2E);
+    zt = zt + a.target_logit[(int64_t)k * a.N + n];
+  }
+  const float lse = M + logf(S);
+  const int64_t tv = a.targets[n];
+  const bool valid = tv != a.ignore_index;
+  const bool bad = valid && (tv < 0 || tv >= a.V);
+  const float row = !valid ? 0.f : bad ? NAN : lse - zt;
+  if (a.lse_out) a.lse_out[n] = lse;
+  if (a.loss_rows) a.loss_rows[n] = row;
+  a.row_loss[n] = row;
+  a.row_flag[n] = (valid ? 1 : 0) | (bad ? 4 : 0);
 }
 
 // ------------------------------------------------------------------ backward helpers
@@ -837,7 +867,8 @@ __device__ __forceinline__ void g_tile(const GArgs& a, int bid, int nblocks) {
   // per-token inputs are loaded ahead of the operand copies (their latency
   // then passes with the first stages') and parked in LDS until the
   // epilogue: thread c < 256 takes token n0 + c.  Target code: the id, -1
-  // for a dead token (past N or ignored), -2 for an id outside [0, V).
+  // for a dead token (past N or ignored), -2 for an id outside [0, V), -3
+  // for another vocabulary shard's id.
   constexpr bool PARK = !WCT;
   f32x4_t acc[WI][WJ];
   if constexpr (PARK) {
@@ -853,7 +884,10 @@ __device__ __forceinline__ void g_tile(const GArgs& a, int bid, int nblocks) {
     gemm_prefetch<W>(cp, A, B);
     sched_fence();  // the loads' first use stays behind the copies
     if (t < TILE) {
-      g_col_code[t] = col_tv == a.ignore_index ? -1 : (col_tv < 0 || col_tv >= a.V) ? -2 : (int)col_tv;
+      g_col_code[t] = col_tv == a.ignore_index ? -1
+                      : col_tv == a.foreign          ? -3
+                      : (col_tv < 0 || col_tv >= a.V) ? -2
+                                                      : (int)col_tv;
       g_col_lse[t] = col_lse;
       g_col_gr[t] = col_gr;
     }
@@ -888,9 +922,9 @@ __device__ __forceinline__ void g_tile(const GArgs& a, int bid, int nblocks) {
       gr = g_col_gr[col];
     } else if (n < a.N) {
       const int64_t tv = a.targets[n];
-      code = tv == a.ignore_index ? -1 : (tv < 0 || tv >= a.V) ? -2 : (int)tv;
+      code = tv == a.ignore_index ? -1 : tv == a.foreign ? -3 : (tv < 0 || tv >= a.V) ? -2 : (int)tv;
       if (code != -1) cl = a.lse[n];
-      if (code >= 0 && a.none_reduction && a.grad_rows) gr = a.grad_rows[n];
+      if (code != -1 && a.none_reduction && a.grad_rows) gr = a.grad_rows[n];
     }
     tgt[j] = -1;
     lse[j] = INFINITY;
@@ -902,9 +936,9 @@ __device__ __forceinline__ void g_tile(const GArgs& a, int bid, int nblocks) {
       if (code == -2) {
         coef[j] = NAN;
       } else {
-        tgt[j] = code;
+        tgt[j] = code;  // -3 (another shard's id) matches no row: no one-hot term
         coef[j] = gr;
-        if (a.class_weight) coef[j] = coef[j] * a.class_weight[code];
+        if (a.class_weight && code >= 0) coef[j] = coef[j] * a.class_weight[code];
       }
     }
   }
@@ -1181,9 +1215,26 @@ __device__ __forceinline__ void dh_tile(const DhArgs& a, int bid, int nblocks, i
     }
     if (a.last && a.ksplit == 1) {
       // grad_hidden in the dtype through the LDS tile ([h][n] in, read
-      // transposed into whole 16-byte pieces of grad_hidden rows)
+      // transposed into whole 16-byte pieces of grad_hidden rows); as fp32
+      // straight from the accumulators, four tokens of one hidden column a
+      // lane (a quarter-wave covers 64 contiguous bytes of each row)
       const float scale = a.scale[0];
-      if constexpr (EB == 2) {
+      if (a.out_f32) {
+        float* out = reinterpret_cast<float*>(a.out);
+        const int nr = wm * 16 * WI + 4 * q, hc = wn * 16 * WJ + c16;
+#pragma unroll
+        for (int j = 0; j < WJ; ++j) {
+          const int64_t h = h0 + hc + 16 * j;
+          if (h >= a.H) continue;
+#pragma unroll
+          for (int i = 0; i < WI; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int64_t n = n0 + nr + 16 * i + e;
+              if (n < a.N) out[n * a.H + h] = acc[i][j][e] * scale;
+            }
+        }
+      } else if constexpr (EB == 2) {
 #pragma unroll
         for (int i = 0; i < WI; ++i)
 #pragma unroll
@@ -1242,7 +1293,10 @@ __device__ __forceinline__ void dh_tile(const DhArgs& a, int bid, int nblocks, i
       const int64_t h = h0 + wm * 16 * WI + 16 * i + 4 * q;
       if (h >= a.H) continue;
       const int64_t idx = n * a.H + h;
-      if (finish)
+      if (finish && a.out_f32)
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + idx) = make_float4(
+            acc[i][j][0] * scale, acc[i][j][1] * scale, acc[i][j][2] * scale, acc[i][j][3] * scale);
+      else if (finish)
         store4<D>(out + idx, acc[i][j][0] * scale, acc[i][j][1] * scale, acc[i][j][2] * scale,
                   acc[i][j][3] * scale);
       else
@@ -1283,10 +1337,14 @@ __global__ __launch_bounds__(256) void bwd_dh_final_kernel(DhFinalArgs a) {
     }
     const float sc = a.scale[0];
     typename Elem<D>::T* out = reinterpret_cast<typename Elem<D>::T*>(a.out);
+    float* out32 = reinterpret_cast<float*>(a.out);
     const float x[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if (n + e < a.N) out[(n + e) * a.H + h] = from_f32<D>(x[e] * sc);
+      if (n + e < a.N) {
+        if (a.out_f32) out32[(n + e) * a.H + h] = x[e] * sc;
+        else out[(n + e) * a.H + h] = from_f32<D>(x[e] * sc);
+      }
     return;
   }
   float4 v = *reinterpret_cast<const float4*>(a.acc + i);
@@ -1298,7 +1356,10 @@ __global__ __launch_bounds__(256) void bwd_dh_final_kernel(DhFinalArgs a) {
     v.w = v.w + o.w;
   }
   const float sc = a.scale[0];
-  store4<D>(reinterpret_cast<typename Elem<D>::T*>(a.out) + i, v.x * sc, v.y * sc, v.z * sc, v.w * sc);
+  if (a.out_f32)
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + i) = make_float4(v.x * sc, v.y * sc, v.z * sc, v.w * sc);
+  else
+    store4<D>(reinterpret_cast<typename Elem<D>::T*>(a.out) + i, v.x * sc, v.y * sc, v.z * sc, v.w * sc);
 }
 
 // grad_weight[v][h] = scale * sum_n G[n][v] H[n][h] for one vocabulary chunk:
@@ -1416,7 +1477,15 @@ __global__ __launch_bounds__(256) void gather_targets_kernel(GatherTargetsArgs a
   const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (n >= a.N) return;
   const int64_t s = n / a.T, t = n - s * a.T;
-  a.dst[n] = a.src[s * a.seq_stride + t * a.stride];
+  int64_t tv = a.src[s * a.seq_stride + t * a.stride];
+  if (a.shard) {
+    const int64_t local = tv - a.voff;
+    tv = tv == a.ignore_index              ? kShardIgnored
+         : (local >= 0 && local < a.vshard) ? local
+         : (tv >= 0 && tv < a.vtotal)       ? kShardForeign
+                                            : kShardBad;
+  }
+  a.dst[n] = tv;
 }
 
 // ------------------------------------------------------------------ launchers
@@ -1458,6 +1527,12 @@ hipError_t launch_forward_combine(bool metrics, const CombineArgs& a, hipStream_
 hipError_t launch_forward_reduce(bool metrics, const ReduceArgs& a, hipStream_t st) {
   if (metrics) hipLaunchKernelGGL(fwd_reduce_kernel<true>, dim3(1), dim3(1024), 0, st, a);
   else hipLaunchKernelGGL(fwd_reduce_kernel<false>, dim3(1), dim3(1024), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_shard_combine(const ShardCombineArgs& a, hipStream_t st) {
+  if (a.N <= 0) return hipSuccess;
+  hipLaunchKernelGGL(shard_combine_kernel, dim3(blocks_for(a.N, 256)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

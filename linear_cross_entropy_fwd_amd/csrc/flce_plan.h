@@ -129,6 +129,25 @@ struct CombineArgs {
   int tiles_per_split, n_splits;
   int zsum;         // the partial records hold the sum of z
   float eps, z_loss;  // label smoothing, z-loss coefficient
+  // Vocabulary shard: loss_rows receives each row's target logit when the
+  // target code is a local id, 0 for ignored rows and for code `foreign`
+  // (another shard's id), NaN for a bad id (flagged as for the whole vocabulary).
+  int shard;
+  int64_t foreign;
+};
+
+// The loss of a vocabulary split into shards, from each shard's per-row
+// log-sum-exp and target logit (the target's owner holds it, the others 0).
+struct ShardCombineArgs {
+  const float* shard_lse;     // [n_shards][N]
+  const float* target_logit;  // [n_shards][N]
+  const int64_t* targets;     // [N] ids of the whole vocabulary
+  float* lse_out;             // [N] or null
+  float* loss_rows;           // [N] for reduction "none", else null
+  float* row_loss;            // workspace [N]
+  int* row_flag;              // workspace [N]: bit0 valid, bit2 bad target
+  int64_t N, V, ignore_index; // V: the whole vocabulary
+  int n_shards;
 };
 
 struct ReduceArgs {
@@ -171,7 +190,16 @@ struct GatherTargetsArgs {
   const int64_t* src;
   int64_t* dst;        // [N]
   int64_t N, T, stride, seq_stride;
+  // Vocabulary shard (shard = 1): dst holds the codes the shard's kernels
+  // read instead of ids: t - voff for the shard's ids [voff, voff + vshard),
+  // kShardIgnored for ignore_index, kShardForeign for another shard's id
+  // (inside [0, vtotal)), kShardBad for an id outside [0, vtotal).
+  int shard;
+  int64_t ignore_index, voff, vshard, vtotal;
 };
+
+// Target codes of a vocabulary shard (all negative, so none is a local id).
+constexpr int64_t kShardIgnored = -1, kShardBad = -2, kShardForeign = -3;
 
 struct GArgs {
   const char* hidden;
@@ -189,6 +217,8 @@ struct GArgs {
   int g_ld, wct_ld;        // row pitches (elements) of G and W_c^T
   int g_stream;            // store G with streaming (non-temporal) stores
   int none_reduction;
+  int64_t foreign;         // target code of another shard's id: no one-hot term, a finite factor
+                           // (ignore_index outside a vocabulary shard, which makes it unused)
   float s, cap, inv_cap;
   const float* class_weight;  // [V] or null
   float eps_v, keep, zl2;     // eps / V, 1 - eps, 2 * z_loss
@@ -209,6 +239,7 @@ struct DhArgs {
   const char* Wk;
   int64_t wrows;
   int acc_stream;  // bk: read and write the running sums with streaming (non-temporal) accesses
+  int out_f32;     // 1: grad_hidden is written as fp32 whatever the input dtype
 };
 
 // grad_hidden = the fixed-order sum of the ksplit accumulators, in the dtype.
@@ -221,6 +252,7 @@ struct DhFinalArgs {
   int bk;                      // accumulators in the tile layout of the K-major grad_hidden kernel
   int64_t N, H;
   int n_h_tiles;
+  int out_f32;                 // 1: out is fp32 whatever the input dtype
 };
 
 struct DwArgs {
@@ -292,6 +324,7 @@ hipError_t launch_forward_tiles(int dtype, bool metrics, bool bias, bool cap, co
                                 hipStream_t st);
 hipError_t launch_forward_combine(bool metrics, const CombineArgs& a, hipStream_t st);
 hipError_t launch_forward_reduce(bool metrics, const ReduceArgs& a, hipStream_t st);
+hipError_t launch_shard_combine(const ShardCombineArgs& a, hipStream_t st);
 hipError_t launch_backward_prep(const PrepArgs& a, hipStream_t st);
 hipError_t launch_transpose(int dtype, const TransposeArgs& a, hipStream_t st);
 hipError_t launch_backward_g(int dtype, bool bias, bool cap, const GArgs& a, hipStream_t st);

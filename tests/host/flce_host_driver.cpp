@@ -121,6 +121,63 @@ static void run(flce_problem_t p, bool strided = false) {
   }
 }
 
+// A vocabulary split into shards of the whole problem p: each shard's
+// forward and backward (fp32 grad_hidden), then the combine of the whole.
+// The entry points that refuse a shard do so before any launch.
+static void run_shards(flce_problem_t whole, const int64_t* bounds, int n_shards, bool strided = false) {
+  const bool none = whole.reduction == FLCE_NONE;
+  float* gl = reinterpret_cast<float*>(OUT + (3ull << 36));
+  float* slse = reinterpret_cast<float*>(OUT + (7ull << 36));
+  float* stl = reinterpret_cast<float*>(OUT + (8ull << 36));
+  float* loss = reinterpret_cast<float*>(OUT);
+  float* lse = reinterpret_cast<float*>(OUT + (1ull << 36));
+  if (strided) {
+    whole.seq_len = whole.n_tokens / 4;
+    whole.hidden_row_stride = whole.hidden + 8 * (whole.dtype == FLCE_F32 ? 4 : 8);
+    whole.hidden_seq_stride = (whole.seq_len + 1) * whole.hidden_row_stride;
+    whole.targets_stride = 2;
+    whole.targets_seq_stride = 2 * (whole.seq_len + 1);
+  }
+  hoststub::hidden_ptr = HID;
+  for (int k = 0; k < n_shards; ++k) {
+    flce_problem_t p = whole;
+    p.vocab_offset = bounds[k];
+    p.vocab = bounds[k + 1] - bounds[k];
+    p.vocab_total = whole.vocab;
+    p.grad_hidden_fp32 = 1;
+    const void* bias = p.has_bias ? BIA : nullptr;
+    const size_t fs = flce_forward_workspace_size(&p), bs = flce_backward_workspace_size(&p);
+    hoststub::begin(WSP, fs);
+    expect(flce_forward_shard(&p, HID, WGT, reinterpret_cast<const int64_t*>(TGT), bias, slse + k * p.n_tokens,
+                              stl + k * p.n_tokens, WSP, fs, nullptr),
+           FLCE_OK, "forward shard", p);
+    hoststub::end();
+    hoststub::begin(WSP, bs);
+    expect(flce_backward(&p, HID, WGT, reinterpret_cast<const int64_t*>(TGT), bias, lse, none ? gl : nullptr,
+                         OUT + (4ull << 36), OUT + (5ull << 36), p.has_bias ? OUT + (6ull << 36) : nullptr, WSP, bs,
+                         nullptr),
+           FLCE_OK, "backward shard", p);
+    hoststub::end();
+    const int before = hoststub::launches;
+    float l;
+    expect(flce_forward(&p, HID, WGT, reinterpret_cast<const int64_t*>(TGT), bias, &l, lse, nullptr, WSP, fs, nullptr),
+           FLCE_ERR_INVALID_ARGUMENT, "flce_forward of a shard", p);
+    expect(flce_forward_backward(&p, HID, WGT, reinterpret_cast<const int64_t*>(TGT), bias, &l, lse, nullptr, nullptr,
+                                 OUT + (4ull << 36), nullptr, nullptr, WSP, size_t(1) << 40, nullptr),
+           FLCE_ERR_INVALID_ARGUMENT, "forward_backward of a shard", p);
+    if (hoststub::launches != before) {
+      ++failures;
+      fprintf(stderr, "FAIL: a refused shard call launched something\n");
+    }
+  }
+  const size_t cs = flce_combine_shards_workspace_size(&whole);
+  hoststub::begin(WSP, cs);
+  expect(flce_combine_shards(&whole, n_shards, slse, stl, reinterpret_cast<const int64_t*>(TGT), loss, lse, WSP, cs,
+                             nullptr),
+         FLCE_OK, "combine shards", whole);
+  hoststub::end();
+}
+
 // Tile orders: every tile of the grid exactly once; with the XCD remap, a
 // grid of a multiple of 8 and per-XCD tile counts at most one apart; and for
 // grids of whole 4 x 8 blocks the plain block order (blocks along a, then b;
@@ -224,6 +281,58 @@ int main() {
           run(p);
           if (n >= 4 && n % 4 == 0) run(p, true);
         }
+  // vocabulary shards
+  {
+    const int64_t b2[] = {0, 1000, 2600}, b3[] = {0, 300, 301, 2600}, b8[9] = {0, 16032, 32064, 48096, 64128,
+                                                                               80160, 96192, 112224, 128256};
+    for (int d = 1; d < 3; ++d)
+      for (int r = 0; r < 3; ++r) {
+        flce_problem_t p = base(300, 256, 2600, dts[d]);
+        p.reduction = r;
+        p.has_bias = r == 1;
+        p.softcap = r == 2 ? 30.f : 0.f;
+        run_shards(p, b2, 2);
+        run_shards(p, b3, 3);
+        run_shards(p, b3, 3, true);
+      }
+    run_shards(base(4096, 4096, 128256, FLCE_BF16), b8, 8);
+    flce_problem_t p = base(64, 128, 1000, FLCE_F32);  // not the small path with a shard
+    const int64_t bf[] = {0, 500, 1000};
+    run_shards(p, bf, 2);
+    // refused shard descriptions: a status, nothing launched
+    const int before = hoststub::launches;
+    p = base(300, 256, 1000, FLCE_BF16);
+    p.vocab_offset = 1700;
+    p.vocab_total = 2600;
+    float l;
+    expect(flce_forward_shard(&p, HID, WGT, reinterpret_cast<const int64_t*>(TGT), nullptr, &l, &l, WSP, 1 << 30,
+                              nullptr),
+           FLCE_ERR_INVALID_ARGUMENT, "shard past the vocabulary", p);
+    p.vocab_offset = 1600;
+    p.return_metrics = 1;
+    expect(flce_forward_shard(&p, HID, WGT, reinterpret_cast<const int64_t*>(TGT), nullptr, &l, &l, WSP, 1 << 30,
+                              nullptr),
+           FLCE_ERR_UNSUPPORTED, "shard with metrics", p);
+    p.return_metrics = 0;
+    p.vocab_total = 0;
+    expect(flce_forward_shard(&p, HID, WGT, reinterpret_cast<const int64_t*>(TGT), nullptr, &l, &l, WSP, 1 << 30,
+                              nullptr),
+           FLCE_ERR_INVALID_ARGUMENT, "offset without a vocabulary total", p);
+    p.vocab_offset = 0;
+    expect(flce_forward_shard(&p, HID, WGT, reinterpret_cast<const int64_t*>(TGT), nullptr, &l, &l, WSP, 1 << 30,
+                              nullptr),
+           FLCE_ERR_INVALID_ARGUMENT, "forward shard without a shard", p);
+    p.vocab_total = 2600;
+    expect(flce_combine_shards(&p, 2, &l, &l, reinterpret_cast<const int64_t*>(TGT), &l, &l, WSP, 1 << 30, nullptr),
+           FLCE_ERR_INVALID_ARGUMENT, "combine of a shard problem", p);
+    p.vocab_total = 0;
+    expect(flce_combine_shards(&p, 0, &l, &l, reinterpret_cast<const int64_t*>(TGT), &l, &l, WSP, 1 << 30, nullptr),
+           FLCE_ERR_INVALID_ARGUMENT, "combine of no shards", p);
+    if (hoststub::launches != before) {
+      ++failures;
+      fprintf(stderr, "FAIL: a refused shard description launched something\n");
+    }
+  }
   // invalid arguments: a status, nothing launched
   {
     flce_problem_t p = base(64, 128, 1000, FLCE_BF16);

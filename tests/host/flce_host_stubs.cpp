@@ -142,6 +142,13 @@ hipError_t launch_forward_reduce(bool, const ReduceArgs& a, hipStream_t) {
   ++pass;
   return hipSuccess;
 }
+hipError_t launch_shard_combine(const ShardCombineArgs& a, hipStream_t) {
+  ++launches;
+  maybe_ws("shard_combine", "tgt", a.targets, (size_t)a.N * 8);
+  ws("shard_combine", "rowloss", a.row_loss, (size_t)a.N * 4);
+  ws("shard_combine", "rowflag", a.row_flag, (size_t)a.N * 4);
+  return hipSuccess;
+}
 hipError_t launch_backward_prep(const PrepArgs& a, hipStream_t) {
   ++launches;
   maybe_ws("prep", "tgt", a.targets, (size_t)a.N * 8);
