@@ -206,8 +206,13 @@ def main():
                          "so that no operand is left in L2 or the last-level cache (not the headline)")
     ap.add_argument("--grad-weight-fp32", action="store_true",
                     help="write grad_weight / grad_bias in fp32 (not the headline)")
+    ap.add_argument("--vocab-shards", type=int, default=1,
+                    help="time one device's share of a vocabulary split into this many equal shards "
+                         "(flce_forward_shard + flce_combine_shards + the shard's flce_backward; not the headline)")
+    ap.add_argument("--shard", type=int, default=0, help="which shard --vocab-shards times")
     args = ap.parse_args()
-    variants = bool(args.label_smoothing or args.z_loss or args.class_weights or args.grad_weight_fp32)
+    variants = bool(args.label_smoothing or args.z_loss or args.class_weights or args.grad_weight_fp32
+                    or args.vocab_shards > 1)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no "
               f"multi-GPU path.", file=sys.stderr)
@@ -251,12 +256,40 @@ def main():
     p = flce.problem_for(hidden, weight, bias, w.ignore_index, w.logit_scale, w.softcap,
                          w.reduction, w.return_metrics, label_smoothing=args.label_smoothing,
                          z_loss=args.z_loss, class_weight=cw, grad_weight_fp32=args.grad_weight_fp32)
+    n_shards = args.vocab_shards
+    v_eff = w.v  # the vocabulary ids one step sweeps
+    shard = None
+    if n_shards > 1:
+        # One device's share of a vocabulary split into n_shards equal shards:
+        # its forward, the combine of all shards' per-row outputs (the other
+        # shards' rows of those arrays stand in for what the other devices
+        # would send), and its backward with the combined lse.
+        if args.class_weights or args.label_smoothing or args.z_loss or w.return_metrics:
+            print("--vocab-shards takes no metrics or loss variants", file=sys.stderr)
+            sys.exit(2)
+        size = -(-w.v // n_shards)
+        a0 = args.shard * size
+        a1 = min(w.v, a0 + size)
+        if not 0 <= a0 < a1:
+            print(f"--shard {args.shard} of {n_shards} is empty", file=sys.stderr)
+            sys.exit(2)
+        v_eff = a1 - a0
+        weight = weight[a0:a1]
+        bias = None if bias is None else bias[a0:a1]
+        p = flce.problem_for(hidden, weight, bias, w.ignore_index, w.logit_scale, w.softcap, w.reduction,
+                             False, grad_weight_fp32=args.grad_weight_fp32, vocab_offset=a0, vocab_total=w.v,
+                             grad_hidden_fp32=True)
+        pc = _abi.make_problem(w.n, 8, w.v, _abi.BF16, w.reduction, w.ignore_index)
+        shard = dict(a0=a0, a1=a1, pc=pc,
+                     lse_all=torch.empty(n_shards, w.n, dtype=torch.float32, device=dev),
+                     tl_all=torch.empty(n_shards, w.n, dtype=torch.float32, device=dev),
+                     cws=torch.empty(_abi.flce_combine_shards_workspace_size(pc), dtype=torch.uint8, device=dev))
     fws = torch.empty(_abi.flce_forward_workspace_size(p), dtype=torch.uint8, device=dev)
     bws = torch.empty(_abi.flce_backward_workspace_size(p), dtype=torch.uint8, device=dev)
     loss = torch.empty(w.n if w.reduction == "none" else 1, dtype=torch.float32, device=dev)
     lse = torch.empty(w.n, dtype=torch.float32, device=dev)
     metrics = torch.empty(2, dtype=torch.float32, device=dev) if w.return_metrics else None
-    gh = torch.empty_like(hidden)
+    gh = torch.empty(hidden.shape, dtype=torch.float32 if shard else hidden.dtype, device=dev)
     gdt = torch.float32 if args.grad_weight_fp32 else weight.dtype
     gw = torch.empty(weight.shape, dtype=gdt, device=dev)
     gb = torch.empty(bias.shape, dtype=gdt, device=dev) if bias is not None else None
@@ -265,8 +298,29 @@ def main():
     sh = stream.cuda_stream
 
     def forward():
+        if shard is not None:
+            k = args.shard
+            _abi.check(_abi.flce_forward_shard(p, ptr(hidden), ptr(weight), ptr(targets), ptr(bias),
+                                               ptr(shard["lse_all"][k]), ptr(shard["tl_all"][k]), ptr(fws),
+                                               fws.numel(), sh))
+            _abi.check(_abi.flce_combine_shards(shard["pc"], n_shards, ptr(shard["lse_all"]),
+                                                ptr(shard["tl_all"]), ptr(targets), ptr(loss), ptr(lse),
+                                                ptr(shard["cws"]), shard["cws"].numel(), sh))
+            return
         _abi.check(_abi.flce_forward(p, ptr(hidden), ptr(weight), ptr(targets), ptr(bias), ptr(loss),
                                      ptr(lse), ptr(metrics), ptr(fws), fws.numel(), sh))
+
+    if shard is not None:
+        # the other shards' per-row outputs: this shard's, as stand-ins
+        # (target logits zeroed there, as a row's target lies in one shard)
+        _abi.check(_abi.flce_forward_shard(p, ptr(hidden), ptr(weight), ptr(targets), ptr(bias),
+                                           ptr(shard["lse_all"][args.shard]), ptr(shard["tl_all"][args.shard]),
+                                           ptr(fws), fws.numel(), sh))
+        for k in range(n_shards):
+            if k != args.shard:
+                shard["lse_all"][k].copy_(shard["lse_all"][args.shard])
+                shard["tl_all"][k].zero_()
+        torch.cuda.synchronize()
 
     def backward():
         _abi.check(_abi.flce_backward(p, ptr(hidden), ptr(weight), ptr(targets), ptr(bias), ptr(lse), 0,
@@ -332,15 +386,17 @@ def main():
         print("non-finite result", file=sys.stderr)
         sys.exit(3)
 
-    flops = (8.0 if run_bwd else 2.0) * w.n * w.h * w.v
+    flops = (8.0 if run_bwd else 2.0) * w.n * w.h * v_eff
     tflops = flops / (ms_step * 1e-3) / 1e12
-    fwd_tflops = 2.0 * w.n * w.h * w.v / (fwd_ms * 1e-3) / 1e12
+    fwd_tflops = 2.0 * w.n * w.h * v_eff / (fwd_ms * 1e-3) / 1e12
     template = kernel_template(w.dtype, w.return_metrics, bias is not None, w.softcap is not None)
     traffic = stored_traffic("fwd_tiles", args.workload, template, options_changed or not run_bwd)
     chunk, n_chunks, _, one_launch = _abi.flce_backward_plan(p, with_launches=True)
     out = {
         "metric": (METRIC if not variants else f"fwd+bwd TFLOP/s (8*N*H*V) on {w.name}" + ", other workload or options (not the headline)")
                   if run_bwd else "forward only TFLOP/s (2*N*H*V), not the headline",
+        **({"metric": f"one vocabulary shard's fwd+bwd TFLOP/s (8*N*H*V_shard) on {w.name}, shard "
+                      f"{args.shard} of {n_shards} (not the headline)"} if shard is not None and run_bwd else {}),
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -355,6 +411,10 @@ def main():
         "config": {"workload": w.name, "n_tokens": w.n, "hidden": w.h, "vocab": w.v,
                    "reduction": w.reduction, "targets": f"{w.targets}, {w.ignore_frac:.0%} ignored",
                    "global_batch": w.n, "parallelism": "none (1 GPU)",
+                   **({"parallelism": f"one of {n_shards} vocabulary shards on 1 GPU (the other shards' "
+                                      f"per-row outputs are stand-ins; no collective)",
+                       "vocab_shard": {"offset": shard["a0"], "ids": v_eff, "of": w.v,
+                                       "shards": n_shards}} if shard is not None else {}),
                    **({"label_smoothing": args.label_smoothing, "z_loss": args.z_loss,
                        "class_weights": bool(args.class_weights),
                        "grad_weight_fp32": bool(args.grad_weight_fp32),
@@ -369,13 +429,13 @@ def main():
         "workspace_mb": round((fws.numel() + bws.numel()) / 2**20, 1),
         "outputs_mb": round(sum(t.numel() * t.element_size()
                                 for t in (loss, lse, metrics, gh, gw, gb) if t is not None) / 2**20, 1),
-        "n_by_v_bytes_mb": round(w.n * w.v * 2 / 2**20, 1),
+        "n_by_v_bytes_mb": round(w.n * v_eff * 2 / 2**20, 1),
         "wall_s_timed": round(t_wall, 3),
         "roofline_forward": {"kernel": "fwd_tiles_kernel (forward logit tiles + online LSE)",
                              "bound": "mfma", "achieved": round(fwd_tflops, 3), "peak": PEAK_TFLOPS[w.dtype],
                              "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_TFLOPS[w.dtype], 4),
                              "traffic": traffic, "template": template,
-                             "flops_per_launch": 2 * w.n * w.h * w.v,
+                             "flops_per_launch": 2 * w.n * w.h * v_eff,
                              "window": "HIP events around flce_forward (tile kernel + combine + reduce)"},
     }
     out["roofline"] = out["roofline_forward"]
@@ -386,7 +446,7 @@ def main():
         # Achieved = that over the average launch duration, i.e. 6*N*H*V over the backward's
         # HIP-event window (which also holds the 5 us prep kernel and the hidden transpose).
         launches = n_chunks + 1
-        bwd_tflops = 6.0 * w.n * w.h * w.v / (bwd_ms * 1e-3) / 1e12
+        bwd_tflops = 6.0 * w.n * w.h * v_eff / (bwd_ms * 1e-3) / 1e12
         step_traffic = stored_traffic("bwd_step", args.workload, "bwd_step " + template, options_changed)
         out["roofline"] = {"kernel": "bwd_step_kernel (per vocabulary chunk: recompute + grad_weight + "
                                      "grad_hidden in one launch)",
@@ -395,7 +455,7 @@ def main():
                            "traffic": step_traffic,
                            "template": "bwd_step " + template,
                            "launches_per_backward": launches, "vocab_chunk": chunk,
-                           "flops_per_launch": round(6 * w.n * w.h * w.v / launches),
+                           "flops_per_launch": round(6 * w.n * w.h * v_eff / launches),
                            "avg_launch_ms": round(bwd_ms / launches, 4),
                            "window": "HIP events around flce_backward (the bwd_step_kernel launches, "
                                      "prep and hidden transpose), divided by the launch count"}
@@ -405,7 +465,7 @@ def main():
         # algorithmic bytes (forward reads W and H; the backward reads them
         # for the recompute and again for the contractions, and writes
         # grad_weight and grad_hidden)
-        wh = (w.v * w.h + w.n * w.h) * 4
+        wh = (v_eff * w.h + w.n * w.h) * 4
         step_bytes = (wh if not run_bwd else 4 * wh) + w.n * 8
         gbs = step_bytes / (ms_step * 1e-3) / 1e9
         out["roofline"] = {"kernel": "whole step (every launch of the forward and backward)",
@@ -413,7 +473,7 @@ def main():
                            "frac": round(gbs / PEAK_HBM_GBS, 6), "traffic": None,
                            "bytes_per_step": step_bytes,
                            "window": "HIP events around each step"}
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and shard is None:
         out["cpu_baseline"] = cpu_baseline(d, w, min(args.cpu_rows, w.n))
     print(json.dumps(out), flush=True)
 

@@ -49,3 +49,17 @@ def test_bench_default_warmup_runs_for_a_time():
     out = json.loads([line for line in res.stdout.splitlines() if line.strip()][-1])
     # 0.5 s of steps well under 10 ms each
     assert out["warmup"] >= 50 and out["steps"] == 2
+
+
+def test_bench_one_vocabulary_shard():
+    """--vocab-shards: one device's share of a split vocabulary, timed with
+    the combine and the shard's backward, reported as its own metric."""
+    cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "midvocab_bf16", "--steps", "2",
+           "--warmup", "1", "--no-cpu-baseline", "--vocab-shards", "4", "--shard", "1"]
+    print("\n[case] bench.py, shard 1 of 4 of the mid-vocab workload", flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert res.returncode == 0, res.stderr[-2000:]
+    out = json.loads([line for line in res.stdout.splitlines() if line.strip()][-1])
+    assert "one vocabulary shard" in out["metric"] and "not the headline" in out["metric"]
+    assert out["config"]["vocab_shard"] == {"offset": 8000, "ids": 8000, "of": 32000, "shards": 4}
+    assert out["value"] > 0 and out["roofline"]["traffic"] is None
