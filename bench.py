@@ -301,10 +301,10 @@ def main():
         if shard is not None:
             k = args.shard
             _abi.check(_abi.flce_forward_shard(p, ptr(hidden), ptr(weight), ptr(targets), ptr(bias),
-                                               ptr(shard["lse_all"][k]), ptr(shard["tl_all"][k]), ptr(fws),
-                                               fws.numel(), sh))
+                                               ptr(shard["lse_all"][k]), ptr(shard["tl_all"][k]), 0, 0, 0,
+                                               ptr(fws), fws.numel(), sh))
             _abi.check(_abi.flce_combine_shards(shard["pc"], n_shards, ptr(shard["lse_all"]),
-                                                ptr(shard["tl_all"]), ptr(targets), ptr(loss), ptr(lse),
+                                                ptr(shard["tl_all"]), 0, 0, 0, ptr(targets), ptr(loss), ptr(lse), 0,
                                                 ptr(shard["cws"]), shard["cws"].numel(), sh))
             return
         _abi.check(_abi.flce_forward(p, ptr(hidden), ptr(weight), ptr(targets), ptr(bias), ptr(loss),
@@ -315,7 +315,7 @@ def main():
         # (target logits zeroed there, as a row's target lies in one shard)
         _abi.check(_abi.flce_forward_shard(p, ptr(hidden), ptr(weight), ptr(targets), ptr(bias),
                                            ptr(shard["lse_all"][args.shard]), ptr(shard["tl_all"][args.shard]),
-                                           ptr(fws), fws.numel(), sh))
+                                           0, 0, 0, ptr(fws), fws.numel(), sh))
         for k in range(n_shards):
             if k != args.shard:
                 shard["lse_all"][k].copy_(shard["lse_all"][args.shard])

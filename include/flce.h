@@ -139,8 +139,8 @@ typedef struct flce_problem {
    * target term here), one outside [0, vocab_total) is out of range (the
    * NaN behaviour above).  Used by flce_forward_shard and flce_backward;
    * flce_forward, flce_forward_noalloc and flce_forward_backward refuse it.
-   * Not combined with label_smoothing, z_loss, class_weight or
-   * return_metrics (FLCE_ERR_UNSUPPORTED). */
+   * Not combined with label_smoothing, z_loss, class_weight or predictions
+   * (FLCE_ERR_UNSUPPORTED); metrics come from flce_combine_shards. */
   int64_t vocab_offset;
   int64_t vocab_total;
   /* 1: flce_backward writes grad_hidden as an fp32 array whatever the input
@@ -264,30 +264,44 @@ flce_status_t flce_forward_backward(const flce_problem_t* p, const void* hidden,
  *   target_logit[n] = z_{n,t_n} if t_n is one of the shard's ids, else 0
  *                     (ignored rows and targets of other shards; NaN for a
  *                     target outside [0, vocab_total)).
- * Both outputs are device fp32 [N].  p->reduction is not applied here:
- * flce_combine_shards turns the shards' outputs into the loss.  The
- * workspace is flce_forward_workspace_size(p) bytes; the status word is set
- * as by flce_forward. */
+ * Both outputs are device fp32 [N].  With return_metrics (card: "Metrics
+ * for free"), also per row: shard_max[n] the largest logit over the shard's
+ * ids, shard_argmax[n] its first id (an id of the whole vocabulary, int64),
+ * shard_entropy[n] the entropy of the softmax over the shard's ids (nats);
+ * these three are NULL iff !return_metrics.  p->reduction is not applied
+ * here: flce_combine_shards turns the shards' outputs into the loss and the
+ * metrics.  The workspace is flce_forward_workspace_size(p) bytes; the
+ * status word is set as by flce_forward. */
 flce_status_t flce_forward_shard(const flce_problem_t* p, const void* hidden, const void* weight,
                                  const int64_t* targets, const void* bias, float* shard_lse,
-                                 float* target_logit, void* workspace, size_t workspace_bytes, void* stream);
+                                 float* target_logit, float* shard_max, int64_t* shard_argmax,
+                                 float* shard_entropy, void* workspace, size_t workspace_bytes, void* stream);
 
 /* The loss of a vocabulary split into n_shards shards, from the shards'
  * flce_forward_shard outputs brought together (what each device does after
  * gathering the per-row partials; on one device, the shards' calls in a
  * row).  p describes the whole problem: vocab is the whole vocabulary,
  * vocab_offset and vocab_total 0, and its reduction, ignore_index and token
- * layout apply; no metrics or variants.  shard_lse and target_logit are
- * device fp32 [n_shards][N] (shard-major, contiguous).  Writes
+ * layout, return_metrics and predictions apply; no loss variants.  The
+ * shard arrays are device [n_shards][N] (shard-major, contiguous), the
+ * shards in the order of their ids.  Writes
  *   lse[n]  = log sum_k e^{shard_lse[k][n]} (fp32, k in order, after the
  *             largest is taken out): the input of flce_backward;
  *   loss    = per p->reduction of the rows lse[n] - sum_k target_logit[k][n]
- *             (0 for ignored rows), as flce_forward would ([1] or [N]).
- * lse may be NULL.  The workspace is flce_combine_shards_workspace_size(p)
- * bytes (its status word is readable with flce_forward_status). */
+ *             (0 for ignored rows), as flce_forward would ([1] or [N]);
+ *   metrics = {mean token accuracy, mean entropy} over non-ignored rows, from
+ *             the argmax of the first shard holding the largest shard_max
+ *             (the first id on ties) and H = lse - sum_k e^{lse_k - lse}
+ *             (lse_k - shard_entropy_k); p->predictions gets that argmax.
+ * lse may be NULL; shard_max, shard_argmax, shard_entropy and metrics are
+ * NULL iff !return_metrics.  The workspace is
+ * flce_combine_shards_workspace_size(p) bytes (its status word is readable
+ * with flce_forward_status). */
 size_t flce_combine_shards_workspace_size(const flce_problem_t* p);
 flce_status_t flce_combine_shards(const flce_problem_t* p, int32_t n_shards, const float* shard_lse,
-                                  const float* target_logit, const int64_t* targets, float* loss, float* lse,
+                                  const float* target_logit, const float* shard_max,
+                                  const int64_t* shard_argmax, const float* shard_entropy,
+                                  const int64_t* targets, float* loss, float* lse, float* metrics,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* Synchronously reads the device status word the last flce_forward call

@@ -245,44 +245,60 @@ def flce_forward_backward(hidden, weight, targets, bias=None, grad_loss=None, *,
 
 
 def flce_forward_shard(hidden, weight, targets, bias=None, *, vocab_offset, vocab_total, ignore_index=-100,
-                       logit_scale=1.0, softcap=None, workspace: Optional[torch.Tensor] = None,
-                       fwd_tiles_per_split=0):
+                       logit_scale=1.0, softcap=None, return_metrics=False,
+                       workspace: Optional[torch.Tensor] = None, fwd_tiles_per_split=0):
     """One vocabulary shard's part of the forward (``flce_forward_shard``):
     weight and bias hold ids [vocab_offset, vocab_offset + V) of a vocabulary
     of ``vocab_total`` ids; targets are ids of the whole vocabulary.  Returns
     (shard_lse, target_logit), fp32 (N,): the row's log-sum-exp over the
-    shard's ids, and its target logit when the target is one of them (else 0)."""
+    shard's ids, and its target logit when the target is one of them (else 0);
+    with ``return_metrics`` also (shard_max, shard_argmax, shard_entropy): the
+    row's largest logit, its first id (of the whole vocabulary, int64) and the
+    entropy of the softmax over the shard's ids."""
     layout = _check_inputs(hidden, weight, targets, bias)
-    p = problem_for(hidden, weight, bias, ignore_index, logit_scale, softcap, "none", False,
+    p = problem_for(hidden, weight, bias, ignore_index, logit_scale, softcap, "none", return_metrics,
                     fwd_tiles_per_split=fwd_tiles_per_split, layout=layout, vocab_offset=vocab_offset,
                     vocab_total=vocab_total)
     dev = hidden.device
     n = targets.numel()
     shard_lse = torch.empty(n, dtype=torch.float32, device=dev)
     target_logit = torch.empty(n, dtype=torch.float32, device=dev)
+    sm = ((torch.empty(n, dtype=torch.float32, device=dev), torch.empty(n, dtype=torch.int64, device=dev),
+           torch.empty(n, dtype=torch.float32, device=dev)) if return_metrics else (None, None, None))
     need = _abi.flce_forward_workspace_size(p)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream().cuda_stream
     _abi.check(_abi.flce_forward_shard(p, _ptr(hidden), _ptr(weight), _ptr(targets), _ptr(bias),
-                                       _ptr(shard_lse), _ptr(target_logit), _ptr(workspace),
-                                       workspace.numel(), stream))
-    return shard_lse, target_logit
+                                       _ptr(shard_lse), _ptr(target_logit), _ptr(sm[0]), _ptr(sm[1]), _ptr(sm[2]),
+                                       _ptr(workspace), workspace.numel(), stream))
+    return (shard_lse, target_logit) + (sm if return_metrics else ())
 
 
 def flce_combine_shards(shard_lse, target_logit, targets, vocab_total, *, ignore_index=-100,
-                        reduction="mean", workspace: Optional[torch.Tensor] = None):
+                        reduction="mean", shard_metrics=None, predictions: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None):
     """The loss of a vocabulary split into shards (``flce_combine_shards``),
     from the shards' ``flce_forward_shard`` outputs stacked as (n_shards, N)
-    fp32 tensors (shard order is the summation order).  Returns (loss, lse):
-    loss per ``reduction`` ((), or (N,) for "none") and the whole vocabulary's
-    per-row lse, the input of ``flce_backward``."""
+    tensors (shards in the order of their ids; that order is also the
+    summation order).  Returns (loss, lse, metrics or None): loss per
+    ``reduction`` ((), or (N,) for "none"), the whole vocabulary's per-row lse
+    (the input of ``flce_backward``), and with ``shard_metrics`` = the stacked
+    (shard_max, shard_argmax, shard_entropy) the two metrics; ``predictions``
+    (int64 (N,), needs shard_metrics) receives each row's argmax id."""
     if shard_lse.dim() != 2 or target_logit.shape != shard_lse.shape:
         raise ValueError("shard_lse and target_logit must be (n_shards, N) tensors of one shape")
-    for t in (shard_lse, target_logit):
-        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or t.device != targets.device:
-            raise ValueError("shard_lse and target_logit must be contiguous float32 tensors on the targets' device")
+    arrays = (shard_lse, target_logit) + (tuple(shard_metrics) if shard_metrics is not None else ())
+    for k, t in enumerate(arrays):
+        want = torch.int64 if k == 3 else torch.float32
+        if (t.dtype != want or not t.is_cuda or not t.is_contiguous() or t.device != targets.device
+                or t.shape != shard_lse.shape):
+            raise ValueError("shard arrays must be contiguous (n_shards, N) tensors on the targets' device "
+                             "(int64 argmax, float32 otherwise)")
+    if predictions is not None and (shard_metrics is None or predictions.dtype != torch.int64
+                                    or predictions.shape != (targets.numel(),) or not predictions.is_contiguous()):
+        raise ValueError("predictions must be an int64 (N,) tensor and needs shard_metrics")
     if targets.dtype != torch.int64 or targets.numel() != shard_lse.shape[1] or targets.dim() not in (1, 2):
         raise ValueError("targets must be int64 (N,) or (S, T) with N = shard_lse.shape[1]")
     n = targets.numel()
@@ -293,20 +309,25 @@ def flce_combine_shards(shard_lse, target_logit, targets, vocab_total, *, ignore
     else:
         lay = dict(targets_stride=targets.stride(0) if n > 1 else 0)
     # the combine reads no hidden rows: H = 8 bf16 elements stands for any width
-    p = make_problem(n, 8, vocab_total, _abi.BF16, reduction, ignore_index, **lay)
+    mon = shard_metrics is not None
+    p = make_problem(n, 8, vocab_total, _abi.BF16, reduction, ignore_index, return_metrics=mon,
+                     predictions=_ptr(predictions), **lay)
     dev = targets.device
     loss = torch.empty(n if reduction == "none" else 1, dtype=torch.float32, device=dev)
     lse = torch.empty(n, dtype=torch.float32, device=dev)
+    metrics = torch.empty(2, dtype=torch.float32, device=dev) if mon else None
+    sm = tuple(shard_metrics) if mon else (None, None, None)
     need = _abi.flce_combine_shards_workspace_size(p)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream().cuda_stream
-    _abi.check(_abi.flce_combine_shards(p, shard_lse.shape[0], _ptr(shard_lse), _ptr(target_logit), _ptr(targets),
-                                        _ptr(loss), _ptr(lse), _ptr(workspace), workspace.numel(), stream))
+    _abi.check(_abi.flce_combine_shards(p, shard_lse.shape[0], _ptr(shard_lse), _ptr(target_logit), _ptr(sm[0]),
+                                        _ptr(sm[1]), _ptr(sm[2]), _ptr(targets), _ptr(loss), _ptr(lse),
+                                        _ptr(metrics), _ptr(workspace), workspace.numel(), stream))
     if reduction != "none":
         loss = loss.view(())
-    return loss, lse
+    return loss, lse, metrics
 
 
 class _FusedLinearCrossEntropy(torch.autograd.Function):

@@ -76,10 +76,11 @@ _SIGNATURES = {
     "flce_forward_backward": (ctypes.c_int, [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                              _VP, ctypes.c_size_t, _VP]),
     "flce_forward_status": (ctypes.c_int, [_PP, _VP, ctypes.POINTER(ctypes.c_uint32), _VP]),
-    "flce_forward_shard": (ctypes.c_int, [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
+    "flce_forward_shard": (ctypes.c_int, [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                          ctypes.c_size_t, _VP]),
     "flce_combine_shards_workspace_size": (ctypes.c_size_t, [_PP]),
-    "flce_combine_shards": (ctypes.c_int, [_PP, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t,
-                                           _VP]),
+    "flce_combine_shards": (ctypes.c_int, [_PP, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                           _VP, ctypes.c_size_t, _VP]),
     "flce_forward_plan": (ctypes.c_int, [_PP, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
                                          ctypes.POINTER(ctypes.c_int32)]),
     "flce_backward_plan": (ctypes.c_int, [_PP, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
@@ -179,20 +180,21 @@ def flce_backward(p: Problem, hidden, weight, targets, bias, lse, grad_loss, gra
                                    workspace_bytes, stream)
 
 
-def flce_forward_shard(p: Problem, hidden, weight, targets, bias, shard_lse, target_logit, workspace,
-                       workspace_bytes, stream) -> int:
+def flce_forward_shard(p: Problem, hidden, weight, targets, bias, shard_lse, target_logit, shard_max,
+                       shard_argmax, shard_entropy, workspace, workspace_bytes, stream) -> int:
     return library().flce_forward_shard(ctypes.byref(p), hidden, weight, targets, bias, shard_lse, target_logit,
-                                        workspace, workspace_bytes, stream)
+                                        shard_max, shard_argmax, shard_entropy, workspace, workspace_bytes, stream)
 
 
 def flce_combine_shards_workspace_size(p: Problem) -> int:
     return int(library().flce_combine_shards_workspace_size(ctypes.byref(p)))
 
 
-def flce_combine_shards(p: Problem, n_shards, shard_lse, target_logit, targets, loss, lse, workspace,
-                        workspace_bytes, stream) -> int:
-    return library().flce_combine_shards(ctypes.byref(p), int(n_shards), shard_lse, target_logit, targets, loss,
-                                         lse, workspace, workspace_bytes, stream)
+def flce_combine_shards(p: Problem, n_shards, shard_lse, target_logit, shard_max, shard_argmax, shard_entropy,
+                        targets, loss, lse, metrics, workspace, workspace_bytes, stream) -> int:
+    return library().flce_combine_shards(ctypes.byref(p), int(n_shards), shard_lse, target_logit, shard_max,
+                                         shard_argmax, shard_entropy, targets, loss, lse, metrics, workspace,
+                                         workspace_bytes, stream)
 
 
 def flce_forward_status(p: Problem, workspace, stream) -> int:

@@ -150,8 +150,9 @@ flce_status_t check_problem(const flce_problem_t* p) {
       return fail(FLCE_ERR_INVALID_ARGUMENT, "the shard [vocab_offset, vocab_offset + vocab) = [%lld, %lld) must lie "
                   "inside [0, vocab_total = %lld)", (long long)p->vocab_offset,
                   (long long)(p->vocab_offset + p->vocab), (long long)p->vocab_total);
-    if (p->label_smoothing != 0.f || p->z_loss != 0.f || p->class_weight || p->return_metrics)
-      return fail(FLCE_ERR_UNSUPPORTED, "a vocabulary shard takes no metrics, label smoothing, z-loss or class weights");
+    if (p->label_smoothing != 0.f || p->z_loss != 0.f || p->class_weight || p->predictions)
+      return fail(FLCE_ERR_UNSUPPORTED, "a vocabulary shard takes no label smoothing, z-loss, class weights or "
+                  "predictions (the combine writes predictions)");
   }
   if (p->grad_hidden_fp32 != 0 && p->grad_hidden_fp32 != 1)
     return fail(FLCE_ERR_INVALID_ARGUMENT, "grad_hidden_fp32 must be 0 or 1");
@@ -503,7 +504,7 @@ namespace {
 // kernel sums, and gathered targets for a strided layout.
 struct CombineLayout {
   TokLayout tok;
-  size_t off_status, off_rowloss, off_rowflag, off_tgt, total;
+  size_t off_status, off_rowloss, off_rowflag, off_rowent, off_tgt, total;
 };
 
 CombineLayout combine_layout(const flce_problem_t& p) {
@@ -518,6 +519,7 @@ CombineLayout combine_layout(const flce_problem_t& p) {
   L.off_status = take(16);
   L.off_rowloss = take((size_t)N * 4);
   L.off_rowflag = take((size_t)N * 4);
+  L.off_rowent = take(p.return_metrics ? (size_t)N * 4 : 0);
   L.tok = tok_layout(p);
   L.off_tgt = take(L.tok.t_gather ? (size_t)N * 8 : 0);
   L.total = off;
@@ -530,17 +532,23 @@ flce_status_t check_combine_problem(const flce_problem_t* p) {
   if (p->vocab_total != 0)
     return fail(FLCE_ERR_INVALID_ARGUMENT, "flce_combine_shards takes the whole problem: vocab = the whole "
                 "vocabulary, vocab_offset and vocab_total 0");
-  if (p->label_smoothing != 0.f || p->z_loss != 0.f || p->class_weight || p->return_metrics)
-    return fail(FLCE_ERR_UNSUPPORTED, "flce_combine_shards takes no metrics, label smoothing, z-loss or class weights");
+  if (p->label_smoothing != 0.f || p->z_loss != 0.f || p->class_weight)
+    return fail(FLCE_ERR_UNSUPPORTED, "flce_combine_shards takes no label smoothing, z-loss or class weights");
   return FLCE_OK;
 }
 
 // The forward of flce_forward and, with `shard` (a vocabulary shard), of
 // flce_forward_shard: then `loss` receives the per-row target logits and
 // `lse` the shard's per-row log-sum-exp, and no reduction is applied.
+struct ShardMetrics {
+  float* max;
+  int64_t* argmax;
+  float* ent;
+};
+
 flce_status_t forward_impl(const flce_problem_t* p, bool shard, const void* hidden, const void* weight,
                            const int64_t* targets, const void* bias, float* loss, float* lse, float* metrics,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+                           void* workspace, size_t workspace_bytes, void* stream, ShardMetrics sm = {}) {
   flce_status_t s = check_problem(p);
   if (s != FLCE_OK) return s;
   if (!shard && p->vocab_total > 0)
@@ -558,8 +566,18 @@ flce_status_t forward_impl(const flce_problem_t* p, bool shard, const void* hidd
     return fail(FLCE_ERR_INVALID_ARGUMENT, "loss is NULL");
   if (shard && (!aligned(loss, 4) || !aligned(lse, 4)))
     return fail(FLCE_ERR_INVALID_ARGUMENT, "shard_lse / target_logit misaligned");
-  if (p->return_metrics && !metrics) return fail(FLCE_ERR_INVALID_ARGUMENT, "return_metrics=1 but metrics is NULL");
-  if (!p->return_metrics && metrics) return fail(FLCE_ERR_INVALID_ARGUMENT, "metrics given but return_metrics=0");
+  if (shard) {
+    const bool any = sm.max || sm.argmax || sm.ent, all = sm.max && sm.argmax && sm.ent;
+    if (p->return_metrics && N > 0 && !all)
+      return fail(FLCE_ERR_INVALID_ARGUMENT, "return_metrics=1 needs shard_max, shard_argmax and shard_entropy");
+    if (!p->return_metrics && any)
+      return fail(FLCE_ERR_INVALID_ARGUMENT, "shard metrics given but return_metrics=0");
+    if (!aligned(sm.max, 4) || !aligned(sm.argmax, 8) || !aligned(sm.ent, 4))
+      return fail(FLCE_ERR_INVALID_ARGUMENT, "shard metric outputs misaligned");
+  } else {
+    if (p->return_metrics && !metrics) return fail(FLCE_ERR_INVALID_ARGUMENT, "return_metrics=1 but metrics is NULL");
+    if (!p->return_metrics && metrics) return fail(FLCE_ERR_INVALID_ARGUMENT, "metrics given but return_metrics=0");
+  }
   if (!aligned(hidden, 16) || !aligned(weight, 16))
     return fail(FLCE_ERR_INVALID_ARGUMENT, "hidden and weight must be 16-byte aligned");
   if (!aligned(targets, 8)) return fail(FLCE_ERR_INVALID_ARGUMENT, "targets must be 8-byte aligned");
@@ -630,6 +648,10 @@ flce_status_t forward_impl(const flce_problem_t* p, bool shard, const void* hidd
       ca.ignore_index = fa.ignore_index;
       ca.shard = shard ? 1 : 0;
       ca.foreign = flce::kShardForeign;
+      ca.voff = p->vocab_offset;
+      ca.shard_max = sm.max;
+      ca.shard_argmax = sm.argmax;
+      ca.shard_ent = sm.ent;
       ca.tiles_per_split = L.tiles_per_split;
       ca.n_splits = L.n_splits;
       ca.zsum = fa.zsum;
@@ -670,9 +692,10 @@ flce_status_t flce_forward(const flce_problem_t* p, const void* hidden, const vo
 
 flce_status_t flce_forward_shard(const flce_problem_t* p, const void* hidden, const void* weight,
                                  const int64_t* targets, const void* bias, float* shard_lse,
-                                 float* target_logit, void* workspace, size_t workspace_bytes, void* stream) {
+                                 float* target_logit, float* shard_max, int64_t* shard_argmax,
+                                 float* shard_entropy, void* workspace, size_t workspace_bytes, void* stream) {
   return forward_impl(p, true, hidden, weight, targets, bias, target_logit, shard_lse, nullptr, workspace,
-                      workspace_bytes, stream);
+                      workspace_bytes, stream, ShardMetrics{shard_max, shard_argmax, shard_entropy});
 }
 
 size_t flce_combine_shards_workspace_size(const flce_problem_t* p) {
@@ -681,7 +704,9 @@ size_t flce_combine_shards_workspace_size(const flce_problem_t* p) {
 }
 
 flce_status_t flce_combine_shards(const flce_problem_t* p, int32_t n_shards, const float* shard_lse,
-                                  const float* target_logit, const int64_t* targets, float* loss, float* lse,
+                                  const float* target_logit, const float* shard_max,
+                                  const int64_t* shard_argmax, const float* shard_entropy,
+                                  const int64_t* targets, float* loss, float* lse, float* metrics,
                                   void* workspace, size_t workspace_bytes, void* stream) {
   flce_status_t s = check_combine_problem(p);
   if (s != FLCE_OK) return s;
@@ -691,8 +716,14 @@ flce_status_t flce_combine_shards(const flce_problem_t* p, int32_t n_shards, con
     return fail(FLCE_ERR_INVALID_ARGUMENT, "shard_lse, target_logit and targets must be non-NULL");
   if (!loss && !(p->reduction == FLCE_NONE && N == 0)) return fail(FLCE_ERR_INVALID_ARGUMENT, "loss is NULL");
   if (!aligned(shard_lse, 4) || !aligned(target_logit, 4) || !aligned(loss, 4) || !aligned(lse, 4) ||
-      !aligned(targets, 8))
-    return fail(FLCE_ERR_INVALID_ARGUMENT, "shard_lse / target_logit / loss / lse / targets misaligned");
+      !aligned(targets, 8) || !aligned(shard_max, 4) || !aligned(shard_argmax, 8) || !aligned(shard_entropy, 4) ||
+      !aligned(metrics, 4))
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "shard arrays / loss / lse / targets / metrics misaligned");
+  const bool mon = p->return_metrics != 0;
+  if (mon && (!metrics || (N > 0 && (!shard_max || !shard_argmax || !shard_entropy))))
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "return_metrics=1 needs metrics, shard_max, shard_argmax and shard_entropy");
+  if (!mon && (metrics || shard_max || shard_argmax || shard_entropy))
+    return fail(FLCE_ERR_INVALID_ARGUMENT, "metrics or shard metric arrays given but return_metrics=0");
   if ((int64_t)n_shards * N >= (int64_t(1) << 40))
     return fail(FLCE_ERR_UNSUPPORTED, "n_shards * n_tokens must be below 2^40");
   const CombineLayout L = combine_layout(*p);
@@ -713,16 +744,25 @@ flce_status_t flce_combine_shards(const flce_problem_t* p, int32_t n_shards, con
     }
     flce::ShardCombineArgs a{shard_lse, target_logit, tg, lse, p->reduction == FLCE_NONE ? loss : nullptr,
                              row_loss, row_flag, N, p->vocab, p->ignore_index, n_shards};
+    if (mon) {
+      a.shard_max = shard_max;
+      a.shard_argmax = shard_argmax;
+      a.shard_ent = shard_entropy;
+      a.row_ent = reinterpret_cast<float*>(ws + L.off_rowent);
+      a.predictions = p->predictions;
+    }
     if ((e = flce::launch_shard_combine(a, st)) != hipSuccess) return hip_fail(e, "shard combine kernel");
   }
   flce::ReduceArgs ra{};
   ra.row_loss = row_loss;
   ra.row_flag = row_flag;
+  ra.row_ent = mon ? reinterpret_cast<const float*>(ws + L.off_rowent) : nullptr;
   ra.loss = loss;
+  ra.metrics = metrics;
   ra.status = reinterpret_cast<uint32_t*>(ws + L.off_status);
   ra.N = N;
   ra.reduction = p->reduction;
-  if ((e = flce::launch_forward_reduce(false, ra, st)) != hipSuccess) return hip_fail(e, "forward reduce kernel");
+  if ((e = flce::launch_forward_reduce(mon, ra, st)) != hipSuccess) return hip_fail(e, "forward reduce kernel");
   return FLCE_OK;
 }
 

@@ -455,8 +455,13 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(CombineArgs a) {
   int flag = (valid ? 1 : 0) | (bad ? 4 : 0);
   if (METRICS) {
     if (a.predictions) a.predictions[n] = (int64_t)ai;
-    if (valid && !bad && ai == tv) flag |= 2;
+    if (valid && !foreign && !bad && ai == tv) flag |= 2;
     a.row_ent[n] = valid ? logS - U / S : 0.f;
+    if (a.shard) {
+      a.shard_max[n] = av;
+      a.shard_argmax[n] = (int64_t)ai + a.voff;
+      a.shard_ent[n] = logS - U / S;
+    }
   }
   a.row_flag[n] = flag;
 }
@@ -533,7 +538,29 @@ __global__ __launch_bounds__(256) void shard_combine_kernel(ShardCombineArgs a) 
   if (a.lse_out) a.lse_out[n] = lse;
   if (a.loss_rows) a.loss_rows[n] = row;
   a.row_loss[n] = row;
-  a.row_flag[n] = (valid ? 1 : 0) | (bad ? 4 : 0);
+  int flag = (valid ? 1 : 0) | (bad ? 4 : 0);
+  if (a.shard_max) {
+    // The argmax: the first shard holding the largest value (shards in id
+    // order keep the first index on ties).  The entropy: with q_k the
+    // shard's softmax and w_k = e^{lse_k - lse} its share of the whole,
+    // E_p[z] = sum_k w_k (lse_k - H_k), so H = lse - sum_k w_k (lse_k - H_k).
+    float best = -INFINITY, ez = 0.f;
+    int64_t id = 0;
+    for (int k = 0; k < a.n_shards; ++k) {
+      const int64_t o = (int64_t)k * a.N + n;
+      const float mk = a.shard_max[o];
+      if (k == 0 || mk > best) {
+        best = mk;
+        id = a.shard_argmax[o];
+      }
+      const float lk = a.shard_lse[o];
+      if (lk != -INFINITY) ez = ez + fast_exp2((lk - lse) * LOG2E) * (lk - a.shard_ent[o]);
+    }
+    if (a.predictions) a.predictions[n] = id;
+    if (valid && !bad && id == tv) flag |= 2;
+    a.row_ent[n] = valid ? lse - ez : 0.f;
+  }
+  a.row_flag[n] = flag;
 }
 
 // ------------------------------------------------------------------ backward helpers

@@ -132,8 +132,13 @@ struct CombineArgs {
   // Vocabulary shard: loss_rows receives each row's target logit when the
   // target code is a local id, 0 for ignored rows and for code `foreign`
   // (another shard's id), NaN for a bad id (flagged as for the whole vocabulary).
+  // With metrics, per row: the largest logit, its first id (plus voff, an id
+  // of the whole vocabulary) and the entropy of the shard's softmax.
   int shard;
-  int64_t foreign;
+  int64_t foreign, voff;
+  float* shard_max;
+  int64_t* shard_argmax;
+  float* shard_ent;
 };
 
 // The loss of a vocabulary split into shards, from each shard's per-row
@@ -145,9 +150,15 @@ struct ShardCombineArgs {
   float* lse_out;             // [N] or null
   float* loss_rows;           // [N] for reduction "none", else null
   float* row_loss;            // workspace [N]
-  int* row_flag;              // workspace [N]: bit0 valid, bit2 bad target
+  int* row_flag;              // workspace [N]: bit0 valid, bit1 hit, bit2 bad target
   int64_t N, V, ignore_index; // V: the whole vocabulary
   int n_shards;
+  // metrics (all null without): each shard's row max, its id and its entropy
+  const float* shard_max;        // [n_shards][N]
+  const int64_t* shard_argmax;   // [n_shards][N]
+  const float* shard_ent;        // [n_shards][N]
+  float* row_ent;                // workspace [N]: the row's entropy (0 if ignored)
+  int64_t* predictions;          // [N] the row's first-index argmax, or null
 };
 
 struct ReduceArgs {

@@ -148,8 +148,11 @@ static void run_shards(flce_problem_t whole, const int64_t* bounds, int n_shards
     const void* bias = p.has_bias ? BIA : nullptr;
     const size_t fs = flce_forward_workspace_size(&p), bs = flce_backward_workspace_size(&p);
     hoststub::begin(WSP, fs);
+    float* smax = p.return_metrics ? reinterpret_cast<float*>(OUT + (9ull << 36)) + k * p.n_tokens : nullptr;
+    int64_t* sarg = p.return_metrics ? reinterpret_cast<int64_t*>(OUT + (10ull << 36)) + k * p.n_tokens : nullptr;
+    float* sent = p.return_metrics ? reinterpret_cast<float*>(OUT + (11ull << 36)) + k * p.n_tokens : nullptr;
     expect(flce_forward_shard(&p, HID, WGT, reinterpret_cast<const int64_t*>(TGT), bias, slse + k * p.n_tokens,
-                              stl + k * p.n_tokens, WSP, fs, nullptr),
+                              stl + k * p.n_tokens, smax, sarg, sent, WSP, fs, nullptr),
            FLCE_OK, "forward shard", p);
     hoststub::end();
     hoststub::begin(WSP, bs);
@@ -171,9 +174,13 @@ static void run_shards(flce_problem_t whole, const int64_t* bounds, int n_shards
     }
   }
   const size_t cs = flce_combine_shards_workspace_size(&whole);
+  const bool m = whole.return_metrics != 0;
   hoststub::begin(WSP, cs);
-  expect(flce_combine_shards(&whole, n_shards, slse, stl, reinterpret_cast<const int64_t*>(TGT), loss, lse, WSP, cs,
-                             nullptr),
+  expect(flce_combine_shards(&whole, n_shards, slse, stl, m ? reinterpret_cast<float*>(OUT + (9ull << 36)) : nullptr,
+                             m ? reinterpret_cast<int64_t*>(OUT + (10ull << 36)) : nullptr,
+                             m ? reinterpret_cast<float*>(OUT + (11ull << 36)) : nullptr,
+                             reinterpret_cast<const int64_t*>(TGT), loss, lse,
+                             m ? reinterpret_cast<float*>(OUT + (2ull << 36)) : nullptr, WSP, cs, nullptr),
          FLCE_OK, "combine shards", whole);
   hoststub::end();
 }
@@ -291,6 +298,7 @@ int main() {
         p.reduction = r;
         p.has_bias = r == 1;
         p.softcap = r == 2 ? 30.f : 0.f;
+        p.return_metrics = r != 1;
         run_shards(p, b2, 2);
         run_shards(p, b3, 3);
         run_shards(p, b3, 3, true);
@@ -305,29 +313,40 @@ int main() {
     p.vocab_offset = 1700;
     p.vocab_total = 2600;
     float l;
-    expect(flce_forward_shard(&p, HID, WGT, reinterpret_cast<const int64_t*>(TGT), nullptr, &l, &l, WSP, 1 << 30,
-                              nullptr),
+    expect(flce_forward_shard(&p, HID, WGT, reinterpret_cast<const int64_t*>(TGT), nullptr, &l, &l, nullptr, nullptr,
+                              nullptr, WSP, 1 << 30, nullptr),
            FLCE_ERR_INVALID_ARGUMENT, "shard past the vocabulary", p);
     p.vocab_offset = 1600;
+    p.z_loss = 1e-3f;
+    expect(flce_forward_shard(&p, HID, WGT, reinterpret_cast<const int64_t*>(TGT), nullptr, &l, &l, nullptr, nullptr,
+                              nullptr, WSP, 1 << 30, nullptr),
+           FLCE_ERR_UNSUPPORTED, "shard with z-loss", p);
+    p.z_loss = 0.f;
     p.return_metrics = 1;
-    expect(flce_forward_shard(&p, HID, WGT, reinterpret_cast<const int64_t*>(TGT), nullptr, &l, &l, WSP, 1 << 30,
-                              nullptr),
-           FLCE_ERR_UNSUPPORTED, "shard with metrics", p);
+    expect(flce_forward_shard(&p, HID, WGT, reinterpret_cast<const int64_t*>(TGT), nullptr, &l, &l, nullptr, nullptr,
+                              nullptr, WSP, 1 << 30, nullptr),
+           FLCE_ERR_INVALID_ARGUMENT, "shard metrics without their outputs", p);
     p.return_metrics = 0;
     p.vocab_total = 0;
-    expect(flce_forward_shard(&p, HID, WGT, reinterpret_cast<const int64_t*>(TGT), nullptr, &l, &l, WSP, 1 << 30,
-                              nullptr),
+    expect(flce_forward_shard(&p, HID, WGT, reinterpret_cast<const int64_t*>(TGT), nullptr, &l, &l, nullptr, nullptr,
+                              nullptr, WSP, 1 << 30, nullptr),
            FLCE_ERR_INVALID_ARGUMENT, "offset without a vocabulary total", p);
     p.vocab_offset = 0;
-    expect(flce_forward_shard(&p, HID, WGT, reinterpret_cast<const int64_t*>(TGT), nullptr, &l, &l, WSP, 1 << 30,
-                              nullptr),
+    expect(flce_forward_shard(&p, HID, WGT, reinterpret_cast<const int64_t*>(TGT), nullptr, &l, &l, nullptr, nullptr,
+                              nullptr, WSP, 1 << 30, nullptr),
            FLCE_ERR_INVALID_ARGUMENT, "forward shard without a shard", p);
     p.vocab_total = 2600;
-    expect(flce_combine_shards(&p, 2, &l, &l, reinterpret_cast<const int64_t*>(TGT), &l, &l, WSP, 1 << 30, nullptr),
+    expect(flce_combine_shards(&p, 2, &l, &l, nullptr, nullptr, nullptr, reinterpret_cast<const int64_t*>(TGT), &l, &l,
+                               nullptr, WSP, 1 << 30, nullptr),
            FLCE_ERR_INVALID_ARGUMENT, "combine of a shard problem", p);
     p.vocab_total = 0;
-    expect(flce_combine_shards(&p, 0, &l, &l, reinterpret_cast<const int64_t*>(TGT), &l, &l, WSP, 1 << 30, nullptr),
+    expect(flce_combine_shards(&p, 0, &l, &l, nullptr, nullptr, nullptr, reinterpret_cast<const int64_t*>(TGT), &l, &l,
+                               nullptr, WSP, 1 << 30, nullptr),
            FLCE_ERR_INVALID_ARGUMENT, "combine of no shards", p);
+    p.return_metrics = 1;
+    expect(flce_combine_shards(&p, 2, &l, &l, nullptr, nullptr, nullptr, reinterpret_cast<const int64_t*>(TGT), &l, &l,
+                               &l, WSP, 1 << 30, nullptr),
+           FLCE_ERR_INVALID_ARGUMENT, "combine metrics without the shard arrays", p);
     if (hoststub::launches != before) {
       ++failures;
       fprintf(stderr, "FAIL: a refused shard description launched something\n");

@@ -147,6 +147,7 @@ hipError_t launch_shard_combine(const ShardCombineArgs& a, hipStream_t) {
   maybe_ws("shard_combine", "tgt", a.targets, (size_t)a.N * 8);
   ws("shard_combine", "rowloss", a.row_loss, (size_t)a.N * 4);
   ws("shard_combine", "rowflag", a.row_flag, (size_t)a.N * 4);
+  ws("shard_combine", "rowent", a.row_ent, (size_t)a.N * 4);
   return hipSuccess;
 }
 hipError_t launch_backward_prep(const PrepArgs& a, hipStream_t) {

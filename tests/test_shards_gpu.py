@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import flce_inputs as fi
-from flce_testutil import TOL, gpu_inputs, log_case, maxnorm_rel, oracle_inputs, rel_err, to_np
+from flce_testutil import TIE, TOL, gpu_inputs, log_case, maxnorm_rel, oracle_inputs, rel_err, to_np
 from oracle import flce_reference
 
 pytestmark = pytest.mark.gpu
@@ -16,9 +16,11 @@ pytestmark = pytest.mark.gpu
 W = fi.WORKLOADS
 
 
-def shard_pass(w, g, bounds, *, grad_output=None, bwd_vocab_chunk=0, fwd_tiles_per_split=0, backward=True):
+def shard_pass(w, g, bounds, *, grad_output=None, bwd_vocab_chunk=0, fwd_tiles_per_split=0, backward=True,
+               predictions=None):
     """Every shard's forward, the combine, then every shard's backward with the
-    combined lse; grad_hidden summed over the shards in fp32, in shard order."""
+    combined lse; grad_hidden summed over the shards in fp32, in shard order.
+    Returns (shard_lse, target_logit, loss, lse, grads, metrics or None)."""
     import linear_cross_entropy_fwd_amd as flce
     kw = dict(ignore_index=w.ignore_index, logit_scale=w.logit_scale, softcap=w.softcap)
     V = w.v
@@ -26,11 +28,13 @@ def shard_pass(w, g, bounds, *, grad_output=None, bwd_vocab_chunk=0, fwd_tiles_p
     for a, b in zip(bounds[:-1], bounds[1:]):
         bias = None if g["bias"] is None else g["bias"][a:b]
         parts.append(flce.flce_forward_shard(g["hidden"], g["weight"][a:b], g["targets"], bias, vocab_offset=a,
-                                             vocab_total=V, fwd_tiles_per_split=fwd_tiles_per_split, **kw))
+                                             vocab_total=V, fwd_tiles_per_split=fwd_tiles_per_split,
+                                             return_metrics=w.return_metrics, **kw))
     slse = torch.stack([p[0] for p in parts])
     stl = torch.stack([p[1] for p in parts])
-    loss, lse = flce.flce_combine_shards(slse, stl, g["targets"], V, ignore_index=w.ignore_index,
-                                         reduction=w.reduction)
+    sm = tuple(torch.stack([p[i] for p in parts]) for i in (2, 3, 4)) if w.return_metrics else None
+    loss, lse, metrics = flce.flce_combine_shards(slse, stl, g["targets"], V, ignore_index=w.ignore_index,
+                                                  reduction=w.reduction, shard_metrics=sm, predictions=predictions)
     grads = None
     if backward:
         go = None if grad_output is None else torch.as_tensor(grad_output, dtype=torch.float32)
@@ -44,7 +48,7 @@ def shard_pass(w, g, bounds, *, grad_output=None, bwd_vocab_chunk=0, fwd_tiles_p
             gws.append(gw_k)
             gbs.append(gb_k)
         grads = (gh, torch.cat(gws), None if g["bias"] is None else torch.cat(gbs))
-    return slse, stl, loss, lse, grads
+    return slse, stl, loss, lse, grads, metrics
 
 
 def run_shards(w, bounds, *, grad_output=None, bwd_vocab_chunk=0, fwd_tiles_per_split=0, d=None):
@@ -54,9 +58,11 @@ def run_shards(w, bounds, *, grad_output=None, bwd_vocab_chunk=0, fwd_tiles_per_
     if d is None:
         d = fi.generate(w)
     g = gpu_inputs(d)
-    slse, stl, loss, lse, (gh, gw, gb) = shard_pass(w, g, bounds, grad_output=grad_output,
-                                                    bwd_vocab_chunk=bwd_vocab_chunk,
-                                                    fwd_tiles_per_split=fwd_tiles_per_split)
+    pred = torch.empty(w.n, dtype=torch.int64, device="cuda") if w.return_metrics else None
+    slse, stl, loss, lse, (gh, gw, gb), metrics = shard_pass(w, g, bounds, grad_output=grad_output,
+                                                             bwd_vocab_chunk=bwd_vocab_chunk,
+                                                             fwd_tiles_per_split=fwd_tiles_per_split,
+                                                             predictions=pred)
     torch.cuda.synchronize()
     h, wt, t, bb = oracle_inputs(d)
     okw = dict(ignore_index=w.ignore_index, logit_scale=w.logit_scale, softcap=w.softcap)
@@ -84,6 +90,17 @@ def run_shards(w, bounds, *, grad_output=None, bwd_vocab_chunk=0, fwd_tiles_per_
         errs["loss"] = rel_err(loss.item(), ref["loss"])
     errs["lse"] = maxnorm_rel(to_np(lse), ref["lse"])
     assert errs["loss"] <= tol["loss"] and errs["lse"] <= tol["loss"], errs
+    if w.return_metrics:
+        # metrics as the unsharded path is checked: entropy at the loss tolerance,
+        # hits and predicted ids exact away from near-ties of the top two logits
+        m = to_np(metrics)
+        ties = ref["gap"] <= TIE[w.dtype] * np.maximum(1.0, np.abs(ref["lse"]))
+        errs["entropy"] = rel_err(m[1], ref["entropy"])
+        assert errs["entropy"] <= tol["loss"], errs
+        gpu_hits, ref_hits = int(round(float(m[0]) * ref["n_valid"])), int(ref["hit"].sum())
+        assert abs(gpu_hits - ref_hits) <= int((ties & valid).sum()), (gpu_hits, ref_hits)
+        got_pred = to_np(pred)
+        assert np.all((got_pred == ref["argmax"]) | ties), np.nonzero((got_pred != ref["argmax"]) & ~ties)
     for name, got, r in (("grad_hidden", gh, ref["grad_hidden"]), ("grad_weight", gw, ref["grad_weight"]),
                          ("grad_bias", gb, ref["grad_bias"])):
         if r is None:
@@ -122,17 +139,18 @@ def test_shards_with_unequal_sizes_and_ragged_tokens():
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_one_shard_is_the_unsharded_path_bit_for_bit(dtype):
     """A single shard of the whole vocabulary runs the same kernels on the
-    same ids: its lse, loss and gradients equal flce_forward / flce_backward's
-    bits (grad_hidden in fp32 rounds to the unsharded dtype output)."""
+    same ids: its lse, loss, accuracy and gradients equal flce_forward /
+    flce_backward's bits (grad_hidden in fp32 rounds to the unsharded dtype
+    output)."""
     import linear_cross_entropy_fwd_amd as flce
     w = W["transforms_bf16"].resized(n=300, h=256, v=2600, dtype=dtype, reduction="mean")
     log_case(f"one shard against the unsharded path, {dtype}")
     d = fi.generate(w)
     g = gpu_inputs(d)
     kw = dict(ignore_index=w.ignore_index, logit_scale=w.logit_scale, softcap=w.softcap)
-    slse, stl, loss_s, lse_s, (gh_s, gw_s, gb_s) = shard_pass(w, g, [0, w.v])
-    loss, lse, _ = flce.flce_forward(g["hidden"], g["weight"], g["targets"], g["bias"], reduction=w.reduction,
-                                     **kw)
+    slse, stl, loss_s, lse_s, (gh_s, gw_s, gb_s), metrics_s = shard_pass(w, g, [0, w.v])
+    loss, lse, metrics = flce.flce_forward(g["hidden"], g["weight"], g["targets"], g["bias"],
+                                           reduction=w.reduction, return_metrics=True, **kw)
     gh, gw, gb = flce.flce_backward(g["hidden"], g["weight"], g["targets"], g["bias"], lse, reduction=w.reduction,
                                     **kw)
     torch.cuda.synchronize()
@@ -140,6 +158,10 @@ def test_one_shard_is_the_unsharded_path_bit_for_bit(dtype):
     assert torch.equal(loss_s, loss)
     assert torch.equal(gw_s, gw) and torch.equal(gb_s, gb)
     assert gh_s.dtype == torch.float32 and torch.equal(gh_s.to(gh.dtype), gh)
+    # the same argmax, so the same accuracy; the entropy formed as lse - (lse_0 - H_0)
+    # rounds differently from the unsharded log S - U/S
+    assert metrics_s[0].item() == metrics[0].item()
+    assert rel_err(metrics_s[1].item(), metrics[1].item()) <= 1e-5
 
 
 def test_grad_hidden_fp32_rounds_to_the_dtype_output():
@@ -179,6 +201,7 @@ def test_strided_tokens_with_shards_match_contiguous():
     torch.cuda.synchronize()
     for x, y in ((a[0], b[0]), (a[1], b[1]), (a[2], b[2]), (a[3], b[3])):
         assert torch.equal(x, y)
+    assert a[5] is None and b[5] is None
     for x, y in zip(a[4], b[4]):
         if x is not None:
             assert torch.equal(x.reshape(y.shape), y)
@@ -196,7 +219,7 @@ def test_out_of_range_target_with_shards():
     g = gpu_inputs(d)
     g["targets"][5] = w.v + 3
     g["targets"][6] = 999
-    slse, stl, loss, lse, _ = shard_pass(w, g, [0, 500, 1000], backward=False)
+    slse, stl, loss, lse, _, _ = shard_pass(w, g, [0, 500, 1000], backward=False)
     torch.cuda.synchronize()
     assert torch.isnan(stl[:, 5]).all() and torch.isnan(loss[5])
     assert stl[0, 6].item() == 0.0 and torch.isfinite(stl[1, 6]) and torch.isfinite(loss[6])
@@ -208,8 +231,8 @@ def test_out_of_range_target_with_shards():
     ws = torch.empty(_abi.flce_combine_shards_workspace_size(p), dtype=torch.uint8, device="cuda")
     loss2 = torch.empty(w.n, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
-    _abi.check(_abi.flce_combine_shards(p, 2, slse.data_ptr(), stl.data_ptr(), g["targets"].data_ptr(),
-                                        loss2.data_ptr(), 0, ws.data_ptr(), ws.numel(), stream))
+    _abi.check(_abi.flce_combine_shards(p, 2, slse.data_ptr(), stl.data_ptr(), 0, 0, 0, g["targets"].data_ptr(),
+                                        loss2.data_ptr(), 0, 0, ws.data_ptr(), ws.numel(), stream))
     assert _abi.flce_forward_status(p, ws.data_ptr(), stream) == 1
     assert torch.equal(loss2.nan_to_num(), loss.nan_to_num())
 
