@@ -210,9 +210,13 @@ def main():
                     help="time one device's share of a vocabulary split into this many equal shards "
                          "(flce_forward_shard + flce_combine_shards + the shard's flce_backward; not the headline)")
     ap.add_argument("--shard", type=int, default=0, help="which shard --vocab-shards times")
+    ap.add_argument("--bwd-vocab-chunk", type=int, default=0,
+                    help="plan override: vocabulary ids per backward chunk (not the headline)")
+    ap.add_argument("--fwd-tiles-per-split", type=int, default=0,
+                    help="plan override: vocabulary tiles per forward split (not the headline)")
     args = ap.parse_args()
     variants = bool(args.label_smoothing or args.z_loss or args.class_weights or args.grad_weight_fp32
-                    or args.vocab_shards > 1)
+                    or args.vocab_shards > 1 or args.bwd_vocab_chunk or args.fwd_tiles_per_split)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no "
               f"multi-GPU path.", file=sys.stderr)
@@ -253,9 +257,10 @@ def main():
     if args.class_weights:
         gen = torch.Generator().manual_seed(7)
         cw = (torch.rand(w.v, generator=gen, dtype=torch.float32) + 0.5).to(dev)
+    plan = dict(bwd_vocab_chunk=args.bwd_vocab_chunk, fwd_tiles_per_split=args.fwd_tiles_per_split)
     p = flce.problem_for(hidden, weight, bias, w.ignore_index, w.logit_scale, w.softcap,
                          w.reduction, w.return_metrics, label_smoothing=args.label_smoothing,
-                         z_loss=args.z_loss, class_weight=cw, grad_weight_fp32=args.grad_weight_fp32)
+                         z_loss=args.z_loss, class_weight=cw, grad_weight_fp32=args.grad_weight_fp32, **plan)
     n_shards = args.vocab_shards
     v_eff = w.v  # the vocabulary ids one step sweeps
     shard = None
@@ -278,7 +283,7 @@ def main():
         bias = None if bias is None else bias[a0:a1]
         p = flce.problem_for(hidden, weight, bias, w.ignore_index, w.logit_scale, w.softcap, w.reduction,
                              False, grad_weight_fp32=args.grad_weight_fp32, vocab_offset=a0, vocab_total=w.v,
-                             grad_hidden_fp32=True)
+                             grad_hidden_fp32=True, **plan)
         pc = _abi.make_problem(w.n, 8, w.v, _abi.BF16, w.reduction, w.ignore_index)
         shard = dict(a0=a0, a1=a1, pc=pc,
                      lse_all=torch.empty(n_shards, w.n, dtype=torch.float32, device=dev),
@@ -418,6 +423,7 @@ def main():
                    **({"label_smoothing": args.label_smoothing, "z_loss": args.z_loss,
                        "class_weights": bool(args.class_weights),
                        "grad_weight_fp32": bool(args.grad_weight_fp32),
+                       "bwd_vocab_chunk": chunk, "fwd_tiles_per_split": args.fwd_tiles_per_split or "default",
                        "cold_cache": bool(args.cold)} if variants else {})},
         "mfma_util": round(tflops / PEAK_TFLOPS[w.dtype], 4),
         "step_ms": {"p50": round(step_times[len(step_times) // 2], 4), "min": round(step_times[0], 4),
