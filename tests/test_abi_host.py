@@ -79,6 +79,12 @@ def base(**kw):
     (dict(targets_stride=-1), INVALID),
     (dict(seq_len=16, hidden_seq_stride=2049), INVALID),
     (dict(targets_seq_stride=1 << 40), INVALID),
+    (dict(vocab_offset=10), INVALID),                             # an offset without a vocabulary total
+    (dict(vocab_offset=-1, vocab_total=2000), INVALID),
+    (dict(vocab_offset=1500, vocab_total=2000), INVALID),         # the shard runs past the vocabulary
+    (dict(vocab_total=1 << 31), UNSUPPORTED),
+    (dict(vocab_offset=500, vocab_total=2000, z_loss=1e-3), UNSUPPORTED),   # no loss variants with a shard
+    (dict(grad_hidden_fp32=2), INVALID),
 ])
 def test_invalid_problems(kw, status):
     p = base(**kw)
@@ -87,6 +93,29 @@ def test_invalid_problems(kw, status):
     st = _abi.flce_forward(p, FAKE, FAKE, FAKE, 0, FAKE, FAKE, 0, FAKE, 1 << 30, 0)
     assert st == status, _abi.last_error()
     assert _abi.last_error()
+
+
+def test_shard_problems_take_their_own_entry_points():
+    """A valid vocabulary shard has workspaces, but flce_forward and
+    flce_forward_backward refuse it (the shard forward and the combine are
+    its path), and the combine refuses a shard problem."""
+    import ctypes
+    p = base(vocab_offset=500, vocab_total=2000, dtype=BF16)
+    assert _abi.flce_forward_workspace_size(p) > 0 and _abi.flce_backward_workspace_size(p) > 0
+    assert _abi.flce_forward(p, FAKE, FAKE, FAKE, 0, FAKE, FAKE, 0, FAKE, 1 << 30, 0) == INVALID
+    assert "flce_forward_shard" in _abi.last_error()
+    assert _abi.flce_forward_backward(p, FAKE, FAKE, FAKE, 0, FAKE, FAKE, 0, 0, FAKE, FAKE, 0, FAKE,
+                                      1 << 40, 0) == INVALID
+    assert _abi.flce_combine_shards_workspace_size(p) == 0
+    whole = base(v=2000, dtype=BF16)
+    assert _abi.flce_combine_shards_workspace_size(whole) > 0
+    assert _abi.flce_combine_shards(whole, 0, FAKE, FAKE, 0, 0, 0, FAKE, FAKE, FAKE, 0, FAKE, 1 << 30, 0) == INVALID
+    # metrics in the combine need the three per-shard metric arrays
+    wm = base(v=2000, dtype=BF16, return_metrics=True)
+    assert _abi.flce_combine_shards(wm, 2, FAKE, FAKE, 0, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, 0) == INVALID
+    # the shard's own metric outputs: all three or none
+    sm = base(vocab_offset=500, vocab_total=2000, dtype=BF16, return_metrics=True)
+    assert _abi.flce_forward_shard(sm, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, 0, FAKE, FAKE, 1 << 30, 0) == INVALID
 
 
 def test_problem_null():
