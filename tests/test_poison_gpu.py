@@ -120,3 +120,68 @@ def test_workspace_poison_and_output_canaries(case):
     for k in a:
         assert torch.equal(a[k], b[k]), f"{case['name']}: {k} depends on stale workspace bytes"
     assert a["gh"].numel() > 0 and bool(torch.any(a["gh"] != 0))
+
+
+def _run_shards(g, w, bounds, fill):
+    """Two-level vocabulary-shard pass through the C ABI (each shard's forward
+    with metrics, the combine, each shard's backward with fp32 grad_hidden),
+    workspaces full of `fill`, every output between guards; returns the bytes."""
+    from linear_cross_entropy_fwd_amd import _abi
+    n, h, V = w.n, w.h, w.v
+    eb = g["hidden"].element_size()
+    dt = _abi.BF16 if g["hidden"].dtype == torch.bfloat16 else _abi.F16
+    P = len(bounds) - 1
+    st = torch.cuda.current_stream().cuda_stream
+    sizes = {"slse": 4 * P * n, "stl": 4 * P * n, "smax": 4 * P * n, "sarg": 8 * P * n, "sent": 4 * P * n,
+             "loss": 4, "lse": 4 * n, "metrics": 8, "pred": 8 * n}
+    for k, (a, b) in enumerate(zip(bounds[:-1], bounds[1:])):
+        sizes[f"gh{k}"] = 4 * n * h
+        sizes[f"gw{k}"] = (b - a) * h * eb
+        sizes[f"gb{k}"] = (b - a) * eb
+    bufs = {k: _padded(s) for k, s in sizes.items()}
+    ptr = lambda k: bufs[k][1]
+    for k, (a, b) in enumerate(zip(bounds[:-1], bounds[1:])):
+        p = _abi.make_problem(n, h, b - a, dt, w.reduction, w.ignore_index, w.logit_scale, w.softcap, True, True,
+                              vocab_offset=a, vocab_total=V, grad_hidden_fp32=True)
+        ws = torch.full((_abi.flce_forward_workspace_size(p),), fill, dtype=torch.uint8, device="cuda")
+        _abi.check(_abi.flce_forward_shard(p, g["hidden"].data_ptr(), g["weight"][a:b].data_ptr(),
+                                           g["targets"].data_ptr(), g["bias"][a:b].data_ptr(),
+                                           ptr("slse") + 4 * k * n, ptr("stl") + 4 * k * n, ptr("smax") + 4 * k * n,
+                                           ptr("sarg") + 8 * k * n, ptr("sent") + 4 * k * n, ws.data_ptr(),
+                                           ws.numel(), st))
+    pc = _abi.make_problem(n, 8, V, _abi.BF16, w.reduction, w.ignore_index, return_metrics=True,
+                           predictions=ptr("pred"))
+    ws = torch.full((_abi.flce_combine_shards_workspace_size(pc),), fill, dtype=torch.uint8, device="cuda")
+    _abi.check(_abi.flce_combine_shards(pc, P, ptr("slse"), ptr("stl"), ptr("smax"), ptr("sarg"), ptr("sent"),
+                                        g["targets"].data_ptr(), ptr("loss"), ptr("lse"), ptr("metrics"),
+                                        ws.data_ptr(), ws.numel(), st))
+    for k, (a, b) in enumerate(zip(bounds[:-1], bounds[1:])):
+        p = _abi.make_problem(n, h, b - a, dt, w.reduction, w.ignore_index, w.logit_scale, w.softcap, False, True,
+                              vocab_offset=a, vocab_total=V, grad_hidden_fp32=True, bwd_vocab_chunk=512)
+        ws = torch.full((_abi.flce_backward_workspace_size(p),), fill, dtype=torch.uint8, device="cuda")
+        _abi.check(_abi.flce_backward(p, g["hidden"].data_ptr(), g["weight"][a:b].data_ptr(), g["targets"].data_ptr(),
+                                      g["bias"][a:b].data_ptr(), ptr("lse"), 0, ptr(f"gh{k}"), ptr(f"gw{k}"),
+                                      ptr(f"gb{k}"), ws.data_ptr(), ws.numel(), st))
+    torch.cuda.synchronize()
+    out = {}
+    for k, (buf, _) in bufs.items():
+        host = buf.cpu()
+        s = sizes[k]
+        assert torch.all(host[:PAD] == GUARD), f"shards: write before {k}"
+        assert torch.all(host[PAD + s:] == GUARD), f"shards: write past {k}"
+        out[k] = host[PAD:PAD + s].clone()
+    return out
+
+
+def test_shard_workspace_poison_and_output_canaries():
+    """The vocabulary-shard path (target codes gathered into the workspace,
+    shard metrics, the combine's workspace, fp32 grad_hidden parts) under the
+    same poison and canary checks."""
+    w = W["transforms_bf16"].resized(n=700, h=256, v=2600)
+    log_case("poison/canary: bf16 shards [0, 1111, 2600] with metrics")
+    g = gpu_inputs(fi.generate(w))
+    a = _run_shards(g, w, [0, 1111, 2600], 0x00)
+    b = _run_shards(g, w, [0, 1111, 2600], 0xFF)
+    for k in a:
+        assert torch.equal(a[k], b[k]), f"shards: {k} depends on stale workspace bytes"
+    assert bool(torch.any(a["gh0"] != 0)) and bool(torch.any(a["gh1"] != 0))
