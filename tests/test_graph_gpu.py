@@ -118,3 +118,57 @@ def test_graph_one_call_with_shifted_views():
         want = eager2 if rep % 2 else eager1
         for got, ref in zip(outs, want):
             assert torch.equal(got, ref), f"replay {rep}"
+
+
+def test_graph_vocabulary_shards():
+    """Two vocabulary shards with metrics (their forwards, the combine and
+    their backwards with fp32 grad_hidden parts) captured in one graph:
+    every replay equals the eager pass bit for bit."""
+    import linear_cross_entropy_fwd_amd as flce
+    w = W["transforms_bf16"].resized(n=700, h=256, v=2600)
+    log_case(f"graph capture, vocabulary shards of {w.name}")
+    d1, d2 = fi.generate(w), fi.generate(w.resized(seed=w.seed + 100))
+    g = gpu_inputs(d1)
+    kw = dict(ignore_index=w.ignore_index, logit_scale=w.logit_scale, softcap=w.softcap)
+    bounds = [0, 1111, 2600]
+
+    def run():
+        parts = [flce.flce_forward_shard(g["hidden"], g["weight"][a:b], g["targets"], g["bias"][a:b],
+                                         vocab_offset=a, vocab_total=w.v, return_metrics=True, **kw)
+                 for a, b in zip(bounds[:-1], bounds[1:])]
+        st = [torch.stack([p[i] for p in parts]) for i in range(5)]
+        loss, lse, metrics = flce.flce_combine_shards(st[0], st[1], g["targets"], w.v, ignore_index=w.ignore_index,
+                                                      reduction=w.reduction, shard_metrics=st[2:])
+        outs = [loss, lse, metrics]
+        for a, b in zip(bounds[:-1], bounds[1:]):
+            outs += list(flce.flce_backward(g["hidden"], g["weight"][a:b], g["targets"], g["bias"][a:b], lse,
+                                            reduction=w.reduction, vocab_offset=a, vocab_total=w.v,
+                                            grad_hidden_fp32=True, **kw))
+        return outs
+
+    def load(d):
+        for k in ("hidden", "weight", "bias"):
+            g[k].copy_(d[k].cuda())
+
+    eager1 = [x.clone() for x in run()]
+    load(d2)
+    eager2 = [x.clone() for x in run()]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = run()
+    for rep in range(4):
+        x = torch.randn(256, 256, device="cuda")
+        (x @ x).sum().item()
+        load(d2 if rep % 2 else d1)
+        graph.replay()
+        torch.cuda.synchronize()
+        want = eager2 if rep % 2 else eager1
+        for got, ref in zip(outs, want):
+            assert torch.equal(got, ref), f"replay {rep}"
