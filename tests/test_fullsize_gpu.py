@@ -14,8 +14,9 @@ boundary, of one tile inside the second chunk (the second of a pair where
 grad_hidden runs per pair of chunks) and of the last tile; grad_bias on the
 same ids.  The chunk boundaries are the library's own default plan
 (flce_backward_plan).  Each output is compared element by element at the
-bf16 tolerance (relative max-norm); the achieved errors are written to
-gpurun_out/parity_margins_fullsize.txt.
+bf16 tolerance (relative max-norm); the achieved errors are appended to
+test_output/parity_margins_fullsize.txt (or to the file FLCE_PARITY_MARGINS
+names).
 
 The inputs are drawn on the GPU; the test first checks that they are
 bit-identical to the CPU draw the oracle saw (hidden in full, a band of
@@ -33,7 +34,7 @@ pytestmark = pytest.mark.gpu
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 GOLDEN = os.path.join(ROOT, "tests", "golden")
-MARGINS = os.path.join(ROOT, "gpurun_out", "parity_margins_fullsize.txt")
+MARGINS = os.environ.get("FLCE_PARITY_MARGINS", os.path.join(ROOT, "test_output", "parity_margins_fullsize.txt"))
 NAMES = ["midvocab_bf16", "headvocab_bf16", "transforms_bf16", "peaked_bf16"]
 T = 256
 

@@ -69,7 +69,7 @@ def run_shards(w, bounds, *, grad_output=None, bwd_vocab_chunk=0, fwd_tiles_per_
     ref = flce_reference(h, wt, t, bb, reduction=w.reduction, grad_output=grad_output, **okw)
     tol = TOL[w.dtype]
     valid = t != w.ignore_index
-    # the plain loss of a valid row is lse - z_t, so a target logit is judged
+    # the plain loss of a valid row is lse - z_t, so a target logit is compared
     # at the scale of the row losses it enters with weight 1
     zt = ref["lse"] - ref["row_loss"]
     zt_scale = max(float(np.max(np.abs(ref["row_loss"][valid]))) if valid.any() else 0.0, 1e-30)
