@@ -372,8 +372,8 @@ BwdLayout bwd_layout(const flce_problem_t& p) {
   const int64_t acc_elems = L.dk ? (int64_t)L.n_tok_tiles * L.n_h_tiles * kTile * kTile : N * H;
   L.off_dh = take(L.n_chunks > L.dh_pair || L.dh_split > 1 ? (size_t)L.dh_split * acc_elems * 4 : 0);
   L.off_db = take(p.has_bias ? (size_t)flce::kBiasParts * L.n_tok_tiles * V * 4 : 0);
-  // Caching hints (results are the same bits either way), from A/B runs of
-  // one box session each.  G buffers larger than the last-level cache: G
+  // Caching hints (results are the same bits either way), from alternated
+  // A/B runs on one device each.  G buffers larger than the last-level cache: G
   // leaves with streaming stores (1.5-1.7 % off the backward at N = 16384,
   // H = 2048, V = 262144, 0.2-0.7 % at N = 8192, H = 3584, V = 152064; at
   // N = 4096, H = 4096, V = 128256, whose two buffers fit, plain stores are
