@@ -257,3 +257,33 @@ def test_head_shape_shard_lse_matches_the_plain_forward_on_its_rows():
     assert torch.equal(slse, lse)
     assert torch.equal(stl[~own], torch.zeros_like(stl[~own]))
     assert torch.equal((slse - stl)[own], loss[own])  # the plain row loss is lse - z_t, rounded once
+
+
+def _random_shard_configs(count, seed=20261204):
+    """Seeded draws over sizes, dtypes, options and shard bounds (1 to 5
+    shards of random, unequal sizes, one-id shards included)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for k in range(count):
+        dtype = ["bf16", "f16", "f32"][k % 3]
+        step = 4 if dtype == "f32" else 8
+        n = int(rng.integers(1, 600))
+        h = int(step * rng.integers(1, 50))
+        v = int(rng.integers(2, 4000))
+        n_sh = int(rng.integers(1, 6))
+        cuts = sorted(set(int(c) for c in rng.integers(1, v, size=n_sh - 1))) if n_sh > 1 else []
+        bounds = [0] + cuts + [v]
+        w = W["transforms_bf16"].resized(
+            n=n, h=h, v=v, dtype=dtype, softcap=[None, 5.0, 30.0][int(rng.integers(0, 3))],
+            bias_std=None if rng.random() < 0.5 else 0.1, logit_scale=[1.0, 0.5, 2.0][int(rng.integers(0, 3))],
+            reduction=["mean", "sum", "none"][int(rng.integers(0, 3))], return_metrics=bool(rng.random() < 0.5),
+            ignore_frac=[0.0, 0.1][int(rng.integers(0, 2))], seed=3000 + k)
+        go = rng.standard_normal(n).astype(np.float32) if w.reduction == "none" else None
+        out.append(pytest.param(w, bounds, go, id=f"{k}-{dtype}-n{n}-h{h}-v{v}-s{len(bounds) - 1}"))
+    return out
+
+
+@pytest.mark.parametrize("w,bounds,go", _random_shard_configs(10))
+def test_random_shard_configurations(w, bounds, go):
+    """Shards of random shapes and options against the oracle."""
+    run_shards(w, bounds, grad_output=go)
